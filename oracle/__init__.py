@@ -1,0 +1,164 @@
+"""CPU float64 oracle for causal linear attention with a fixed d_k x d_v state.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check in
+``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` may import this
+package.  The HIP library never loads it, and it shares no code with the HIP
+library: the arithmetic lives in ``oracle.c`` (plain C, float64, one token at a
+time), built into ``liboracle.so`` beside this file.
+
+Functions (both follow the article "From GPT-2 to Kimi K3, explained"):
+
+``la_recurrent``     section "Linear Attention": ELU+1 feature map, running
+                     state S and normaliser z, o_t = phi(q_t) S_t / phi(q_t).z_t.
+``delta_recurrent``  section "DeltaNet (Parallelizing Linear Transformers with
+                     Delta Rule)", sequential prefill loop; with ``g`` given,
+                     the per-key-channel decay of sections "Gated Delta Net" and
+                     "KDA / Kimi Linear" applied to S before each read.
+
+Inputs may be torch CPU tensors (float32, bfloat16, float64) or numpy arrays
+(float32, float64); all inputs of one call share a dtype.  They are read in
+their stored precision and widened to float64 inside the C code, so the oracle
+sees exactly the rounded values the GPU sees.  Results are numpy float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_F32, _BF16, _F64 = 0, 1, 2
+
+
+def build(out_path: str = _LIB_PATH, src: str = _SRC, extra_flags=()) -> str:
+    """Compile oracle.c with gcc into a shared library (portable flags: the
+    library may run on another host than the one that built it)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+           *extra_flags, src, "-o", out_path, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out_path
+
+
+def _bind(lib):
+    d = ctypes.c_void_p
+    i = ctypes.c_int
+    lib.orc_la_recurrent.argtypes = [i, i, i, i, i, d, d, d, i, d, d, d, d, d, i]
+    lib.orc_la_recurrent.restype = i
+    lib.orc_delta_recurrent.argtypes = [i, i, i, i, i, d, d, d, d, d, i, d, d, d, i]
+    lib.orc_delta_recurrent.restype = i
+    lib.orc_max_threads.argtypes = []
+    lib.orc_max_threads.restype = i
+    return lib
+
+
+def load(path: str | None = None):
+    """Load liboracle.so (building it first if it is absent).  With ``path``
+    given, load that library instead (used to test planted mistakes)."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def max_threads() -> int:
+    return int(load().orc_max_threads())
+
+
+def _as_buffer(x):
+    """Return (keepalive, pointer, dtype-code) for a CPU tensor or array,
+    without changing its stored precision."""
+    try:
+        import torch
+    except ImportError:  # pragma: no cover
+        torch = None
+    if torch is not None and isinstance(x, torch.Tensor):
+        if x.device.type != "cpu":
+            raise ValueError("oracle inputs must be CPU tensors")
+        x = x.contiguous()
+        if x.dtype == torch.bfloat16:
+            return x, x.data_ptr(), _BF16
+        if x.dtype == torch.float32:
+            return x, x.data_ptr(), _F32
+        if x.dtype == torch.float64:
+            return x, x.data_ptr(), _F64
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    a = np.ascontiguousarray(x)
+    if a.dtype == np.float32:
+        return a, a.ctypes.data, _F32
+    if a.dtype == np.float64:
+        return a, a.ctypes.data, _F64
+    raise ValueError(f"unsupported dtype {a.dtype}")
+
+
+def _state64(x, shape):
+    if x is None:
+        return None, None
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().double().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64)).reshape(shape)
+    return a, a.ctypes.data
+
+
+def la_recurrent(q, k, v, S0=None, z0=None, nthreads: int = 0, lib=None):
+    """ELU+1 linear attention with normaliser, token by token.
+    q, k [B,H,T,dk]; v [B,H,T,dv]; S0 [B,H,dk,dv] and z0 [B,H,dk] optional
+    (float64-convertible).  Returns (o [B,H,T,dv], S [B,H,dk,dv], z [B,H,dk])."""
+    lib = lib or load()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    bufs = [_as_buffer(t) for t in (q, k, v)]
+    dts = {b[2] for b in bufs}
+    if len(dts) != 1:
+        raise ValueError("q, k, v must share a dtype")
+    s0, s0p = _state64(S0, (B, H, dk, dv))
+    z0a, z0p = _state64(z0, (B, H, dk))
+    o = np.empty((B, H, T, dv), np.float64)
+    S = np.empty((B, H, dk, dv), np.float64)
+    z = np.empty((B, H, dk), np.float64)
+    rc = lib.orc_la_recurrent(B, H, T, dk, dv, bufs[0][1], bufs[1][1], bufs[2][1],
+                              dts.pop(), s0p, z0p, o.ctypes.data, S.ctypes.data,
+                              z.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise MemoryError("oracle allocation failed")
+    return o, S, z
+
+
+def delta_recurrent(q, k, v, beta, g=None, S0=None, nthreads: int = 0, lib=None,
+                    want_o: bool = True):
+    """Delta rule (g None) or per-key-channel gated delta rule, token by token.
+    q, k [B,H,T,dk]; v [B,H,T,dv]; beta [B,H,T]; g [B,H,T,dk] log-decay or
+    None; S0 [B,H,dk,dv] or None.  Returns (o [B,H,T,dv] or None,
+    S [B,H,dk,dv])."""
+    lib = lib or load()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    tensors = [q, k, v, beta] + ([g] if g is not None else [])
+    bufs = [_as_buffer(t) for t in tensors]
+    dts = {b[2] for b in bufs}
+    if len(dts) != 1:
+        raise ValueError("q, k, v, beta (and g) must share a dtype")
+    gp = bufs[4][1] if g is not None else None
+    s0, s0p = _state64(S0, (B, H, dk, dv))
+    o = np.empty((B, H, T, dv), np.float64) if want_o else None
+    S = np.empty((B, H, dk, dv), np.float64)
+    rc = lib.orc_delta_recurrent(B, H, T, dk, dv, bufs[0][1], bufs[1][1], bufs[2][1],
+                                 bufs[3][1], gp, dts.pop(), s0p,
+                                 o.ctypes.data if want_o else None, S.ctypes.data,
+                                 int(nthreads))
+    if rc != 0:
+        raise MemoryError("oracle allocation failed")
+    return o, S

@@ -1,0 +1,228 @@
+/*
+ * oracle.c -- plain CPU float64 reference for causal linear attention with a
+ * fixed d_k x d_v state: ELU+1 linear attention with a running normaliser,
+ * the DeltaNet delta rule, and the per-key-channel gated delta rule.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or helper with
+ * the HIP library.
+ *
+ * Every function here is the per-token recurrence itself, written out one
+ * token at a time with no chunking, blocking or reordering, so that it can be
+ * checked against the article by eye.  Sources (all in the article "From GPT-2
+ * to Kimi K3, explained", mirrored in Chinese on transcrab.onev.cat and in
+ * German on youmind.com):
+ *   - section "Linear Attention": the cached forward with the ELU+1 feature
+ *     map, the running state S and normaliser z, and the division of q@S by
+ *     q@z; plus the three-step description (non-negative scores, divide by
+ *     their sum, weighted mean of v).
+ *   - section "DeltaNet (Parallelizing Linear Transformers with Delta Rule)":
+ *     the sequential prefill loop (read v_old = k S, u = beta (v - v_old),
+ *     write S += k^T u, then read the output with q from the updated S).
+ *   - section "Gated Delta Net" and "KDA / Kimi Linear": the state decays by a
+ *     data-dependent factor before the delta step; for KDA the factor is a
+ *     separate value per key channel.  Reading used here: the decay a_t
+ *     multiplies row i (key channel i) of S before the read at step t, i.e.
+ *     S_t = diag(a_t) S_{t-1} + beta_t k_t (v_t - (diag(a_t) S_{t-1})^T k_t)^T.
+ *
+ * Conventions: row-vector form of the article's code, S is d_k x d_v stored
+ * row-major, a read is k S (= S^T k), a write adds k^T u.  Tensors are
+ * row-major: q, k [B,H,T,d_k]; v [B,H,T,d_v]; beta [B,H,T]; g [B,H,T,d_k]
+ * holds the log-decay g = log a; S [B,H,d_k,d_v]; z [B,H,d_k].
+ *
+ * Inputs are read in their stored precision (fp32, bf16 bit patterns, or
+ * fp64) and widened to float64 element by element; all arithmetic is float64.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2 };
+
+/* Read element i of buffer p stored as dtype dt, widened to double. */
+static double rd(const void *p, size_t i, int dt)
+{
+    if (dt == ORC_F32)
+        return (double)((const float *)p)[i];
+    if (dt == ORC_BF16) {
+        /* bf16 is the top half of an IEEE binary32 */
+        uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    return ((const double *)p)[i];
+}
+
+/* phi(x) = elu(x) + 1 with the default elu constant 1:
+ * x + 1 for x > 0, exp(x) otherwise.  Always positive. */
+static double elu_plus_one(double x)
+{
+    return x > 0.0 ? x + 1.0 : exp(x);
+}
+
+static void set_threads(int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+int orc_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Causal ELU+1 linear attention with normaliser, one token at a time:
+ *   S_t = S_{t-1} + phi(k_t)^T v_t        (d_k x d_v)
+ *   z_t = z_{t-1} + phi(k_t)              (d_k)
+ *   o_t = (phi(q_t) S_t) / (phi(q_t) . z_t)
+ * Both the numerator and the denominator include token t itself.
+ * S0/z0 may be NULL (zero initial state).  o [B,H,T,dv], S_out, z_out may be
+ * NULL if not wanted.  S0 may alias S_out and z0 may alias z_out.
+ * Returns 0, or -1 on allocation failure.
+ */
+int orc_la_recurrent(int B, int H, int T, int dk, int dv,
+                     const void *q, const void *k, const void *v, int dt,
+                     const double *S0, const double *z0,
+                     double *o, double *S_out, double *z_out, int nthreads)
+{
+    int fail = 0;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < B * H; bh++) {
+        double *S = malloc(sizeof(double) * (size_t)dk * dv);
+        double *z = malloc(sizeof(double) * (size_t)dk);
+        double *fq = malloc(sizeof(double) * (size_t)dk);
+        double *fk = malloc(sizeof(double) * (size_t)dk);
+        if (!S || !z || !fq || !fk) {
+#pragma omp atomic write
+            fail = 1;
+            free(S); free(z); free(fq); free(fk);
+            continue;
+        }
+        const size_t sbase = (size_t)bh * dk * dv;
+        for (size_t i = 0; i < (size_t)dk * dv; i++)
+            S[i] = S0 ? S0[sbase + i] : 0.0;
+        for (int i = 0; i < dk; i++)
+            z[i] = z0 ? z0[(size_t)bh * dk + i] : 0.0;
+
+        for (int t = 0; t < T; t++) {
+            const size_t qk_row = ((size_t)bh * T + t) * dk;
+            const size_t v_row = ((size_t)bh * T + t) * dv;
+            for (int i = 0; i < dk; i++) {
+                fq[i] = elu_plus_one(rd(q, qk_row + i, dt));
+                fk[i] = elu_plus_one(rd(k, qk_row + i, dt));
+            }
+            /* write: S += phi(k)^T v, z += phi(k) */
+            for (int i = 0; i < dk; i++) {
+                for (int j = 0; j < dv; j++)
+                    S[(size_t)i * dv + j] += fk[i] * rd(v, v_row + j, dt);
+                z[i] += fk[i];
+            }
+            /* read with the updated state */
+            if (o) {
+                double den = 0.0;
+                for (int i = 0; i < dk; i++)
+                    den += fq[i] * z[i];
+                for (int j = 0; j < dv; j++) {
+                    double num = 0.0;
+                    for (int i = 0; i < dk; i++)
+                        num += fq[i] * S[(size_t)i * dv + j];
+                    o[v_row + j] = num / den;
+                }
+            }
+        }
+        if (S_out)
+            memcpy(S_out + sbase, S, sizeof(double) * (size_t)dk * dv);
+        if (z_out)
+            memcpy(z_out + (size_t)bh * dk, z, sizeof(double) * (size_t)dk);
+        free(S); free(z); free(fq); free(fk);
+    }
+    return fail ? -1 : 0;
+}
+
+/*
+ * Delta rule, optionally with a per-key-channel decay, one token at a time:
+ *   (gated only)  S <- diag(exp(g_t)) S        row i scaled by exp(g_t[i])
+ *   r   = k_t S                                 (what the key reads now)
+ *   u   = beta_t (v_t - r)                      (only what is new)
+ *   S  <- S + k_t^T u                           (outer-product write)
+ *   o_t = q_t S                                 (read after the write)
+ * g may be NULL (ungated, decay 1).  S0 may be NULL (zero state) and may alias
+ * S_out.  o and S_out may be NULL if not wanted.  A decode step is this loop
+ * with T = 1 and S0 = the carried state.
+ */
+int orc_delta_recurrent(int B, int H, int T, int dk, int dv,
+                        const void *q, const void *k, const void *v,
+                        const void *beta, const void *g, int dt,
+                        const double *S0, double *o, double *S_out,
+                        int nthreads)
+{
+    int fail = 0;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < B * H; bh++) {
+        double *S = malloc(sizeof(double) * (size_t)dk * dv);
+        double *kt = malloc(sizeof(double) * (size_t)dk);
+        double *u = malloc(sizeof(double) * (size_t)dv);
+        if (!S || !kt || !u) {
+#pragma omp atomic write
+            fail = 1;
+            free(S); free(kt); free(u);
+            continue;
+        }
+        const size_t sbase = (size_t)bh * dk * dv;
+        for (size_t i = 0; i < (size_t)dk * dv; i++)
+            S[i] = S0 ? S0[sbase + i] : 0.0;
+
+        for (int t = 0; t < T; t++) {
+            const size_t qk_row = ((size_t)bh * T + t) * dk;
+            const size_t v_row = ((size_t)bh * T + t) * dv;
+            const double b = rd(beta, (size_t)bh * T + t, dt);
+            if (g) {
+                for (int i = 0; i < dk; i++) {
+                    const double a = exp(rd(g, qk_row + i, dt));
+                    for (int j = 0; j < dv; j++)
+                        S[(size_t)i * dv + j] *= a;
+                }
+            }
+            for (int i = 0; i < dk; i++)
+                kt[i] = rd(k, qk_row + i, dt);
+            for (int j = 0; j < dv; j++) {
+                double r = 0.0;
+                for (int i = 0; i < dk; i++)
+                    r += kt[i] * S[(size_t)i * dv + j];
+                u[j] = b * (rd(v, v_row + j, dt) - r);
+            }
+            for (int i = 0; i < dk; i++)
+                for (int j = 0; j < dv; j++)
+                    S[(size_t)i * dv + j] += kt[i] * u[j];
+            if (o) {
+                for (int j = 0; j < dv; j++) {
+                    double acc = 0.0;
+                    for (int i = 0; i < dk; i++)
+                        acc += rd(q, qk_row + i, dt) * S[(size_t)i * dv + j];
+                    o[v_row + j] = acc;
+                }
+            }
+        }
+        if (S_out)
+            memcpy(S_out + sbase, S, sizeof(double) * (size_t)dk * dv);
+        free(S); free(kt); free(u);
+    }
+    return fail ? -1 : 0;
+}

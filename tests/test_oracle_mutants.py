@@ -1,0 +1,82 @@
+"""The pins catch plausible mistakes in the oracle (CPU only).
+
+Each case plants one mistake in a copy of ``oracle/oracle.c`` (a dropped term,
+a wrong sign, a wrong operand or index, a read before the write, a decay on the
+wrong step), builds it with gcc into a temporary directory, and runs every pin
+against it in a subprocess.  At least one pin must fail; the unmodified source
+must pass them all.  The copy is made on the CPU only; nothing here touches a
+GPU.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+RUNNER = os.path.join(ROOT, "tests", "oracle_pins.py")
+
+MUTANTS = {
+    "la_feature_map_drops_plus_one": (
+        "return x > 0.0 ? x + 1.0 : exp(x);", "return x > 0.0 ? x : exp(x);"),
+    "la_key_feature_from_query": (
+        "fk[i] = elu_plus_one(rd(k, qk_row + i, dt));",
+        "fk[i] = elu_plus_one(rd(q, qk_row + i, dt));"),
+    "la_normaliser_not_accumulated": ("z[i] += fk[i];", "z[i] += 0.0 * fk[i];"),
+    "la_reads_state_before_write": (
+        "den += fq[i] * z[i];", "den += fq[i] * (z[i] - fk[i]) + 1e-300;"),
+    "delta_sign_of_correction": (
+        "u[j] = b * (rd(v, v_row + j, dt) - r);",
+        "u[j] = b * (rd(v, v_row + j, dt) + r);"),
+    "delta_beta_applied_twice": (
+        "S[(size_t)i * dv + j] += kt[i] * u[j];",
+        "S[(size_t)i * dv + j] += kt[i] * u[j] * b;"),
+    "delta_read_with_query": (
+        "r += kt[i] * S[(size_t)i * dv + j];",
+        "r += rd(q, qk_row + i, dt) * S[(size_t)i * dv + j];"),
+    "delta_output_with_key": (
+        "acc += rd(q, qk_row + i, dt) * S[(size_t)i * dv + j];",
+        "acc += kt[i] * S[(size_t)i * dv + j];"),
+    "gate_sign": (
+        "const double a = exp(rd(g, qk_row + i, dt));",
+        "const double a = exp(-rd(g, qk_row + i, dt));"),
+    "gate_uses_previous_token": (
+        "const double a = exp(rd(g, qk_row + i, dt));",
+        "const double a = exp(rd(g, (t > 0 ? qk_row - dk : qk_row) + i, dt));"),
+    "gate_same_for_all_channels": (
+        "const double a = exp(rd(g, qk_row + i, dt));",
+        "const double a = exp(rd(g, qk_row, dt));"),
+    "bf16_widening_wrong_shift": (
+        "uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;",
+        "uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 15;"),
+}
+
+
+def _build_and_run(tmp_path, name, text):
+    src = tmp_path / f"{name}.c"
+    src.write_text(text)
+    lib = tmp_path / f"lib{name}.so"
+    oracle.build(out_path=str(lib), src=str(src))
+    env = dict(os.environ, OMP_NUM_THREADS="2",
+               PYTHONPATH=os.pathsep.join([ROOT, os.path.join(ROOT, "tests")]))
+    return subprocess.run([sys.executable, RUNNER, str(lib)], capture_output=True,
+                          text=True, timeout=300, env=env, cwd=ROOT)
+
+
+def test_unmodified_oracle_passes_all_pins(tmp_path):
+    r = _build_and_run(tmp_path, "original", open(SRC).read())
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(tmp_path, name):
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"pattern for {name} must occur exactly once"
+    r = _build_and_run(tmp_path, name, text.replace(old, new))
+    assert r.returncode != 0, f"no pin caught {name}: {r.stdout}"
+    # a crash would also be non-zero; require that a pin reported the failure
+    assert "FAILED:" in r.stdout and r.stdout.strip() != "FAILED:", r.stdout + r.stderr
