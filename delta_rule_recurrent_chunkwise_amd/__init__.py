@@ -1,0 +1,201 @@
+"""Causal linear attention with a fixed d_k x d_v state on AMD MI355X (gfx950).
+
+A thin ctypes binding over ``liblinattn.so``, the HIP library whose C ABI is
+declared in ``include/linattn.h``.  The functions below carry the same names
+as the C entry points and only marshal arguments: check devices, dtypes,
+shapes and contiguity, allocate outputs the caller did not pass, and hand raw
+device pointers plus the current HIP stream to the library.  Every step of
+the computation runs in the library's kernels; there is no fallback.
+
+Build the library with ``python -m delta_rule_recurrent_chunkwise_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "la_prefill", "la_decode_step", "deltanet_prefill", "deltanet_decode_step",
+    "la_strerror", "library", "LIB_PATH", "EXPORTED_SYMBOLS", "LinAttnError",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblinattn.so")
+EXPORTED_SYMBOLS = ("la_prefill", "la_decode_step", "deltanet_prefill",
+                    "deltanet_decode_step", "la_strerror")
+
+LA_DTYPE_F32, LA_DTYPE_BF16 = 0, 1
+_DTYPES = {torch.float32: LA_DTYPE_F32, torch.bfloat16: LA_DTYPE_BF16}
+
+_lib = None
+
+
+class LinAttnError(RuntimeError):
+    """A negative return code from liblinattn.so."""
+
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn}: {msg} (code {code})")
+        self.code = code
+
+
+def library():
+    """Load liblinattn.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m delta_rule_recurrent_chunkwise_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I = ctypes.c_void_p, ctypes.c_int
+        lib.la_prefill.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+        lib.la_decode_step.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
+        lib.deltanet_prefill.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+        lib.deltanet_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
+        for fn in ("la_prefill", "la_decode_step", "deltanet_prefill",
+                   "deltanet_decode_step"):
+            getattr(lib, fn).restype = I
+        lib.la_strerror.argtypes = [I]
+        lib.la_strerror.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def la_strerror(code: int) -> str:
+    return library().la_strerror(int(code)).decode()
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise LinAttnError(fn, rc, la_strerror(rc))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _inputs(fn, tensors, shapes):
+    """All given tensors on one GPU, contiguous, one dtype in _DTYPES, with the
+    expected shapes."""
+    dev = None
+    dtype = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{fn}: {name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{fn}: {name} must be contiguous")
+        if dev is None:
+            dev, dtype = t.device, t.dtype
+        if t.device != dev:
+            raise ValueError(f"{fn}: all tensors must be on one device")
+        if t.dtype != dtype:
+            raise ValueError(f"{fn}: {name} has dtype {t.dtype}, expected {dtype}")
+        if tuple(t.shape) != tuple(shapes[name]):
+            raise ValueError(f"{fn}: {name} has shape {tuple(t.shape)}, "
+                             f"expected {tuple(shapes[name])}")
+    if dtype not in _DTYPES:
+        raise ValueError(f"{fn}: dtype must be float32 or bfloat16, got {dtype}")
+    return dev, dtype
+
+
+def _state(fn, name, t, shape, dev):
+    if t is None:
+        return torch.empty(shape, device=dev, dtype=torch.float32)
+    if (not t.is_cuda or t.device != dev or t.dtype != torch.float32
+            or not t.is_contiguous() or tuple(t.shape) != tuple(shape)):
+        raise ValueError(f"{fn}: {name} must be a contiguous float32 tensor of shape "
+                         f"{tuple(shape)} on {dev}")
+    return t
+
+
+def _out(fn, o, shape, dev, dtype):
+    if o is None:
+        return torch.empty(shape, device=dev, dtype=dtype)
+    if (not o.is_cuda or o.device != dev or o.dtype != dtype or not o.is_contiguous()
+            or tuple(o.shape) != tuple(shape)):
+        raise ValueError(f"{fn}: o must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+    return o
+
+
+def la_prefill(q, k, v, S=None, z=None, use_initial_state=False, o=None, stream=None):
+    """ELU+1 linear attention with normaliser over q, k [B,H,T,dk], v [B,H,T,dv].
+    Returns (o [B,H,T,dv], S [B,H,dk,dv] fp32, z [B,H,dk] fp32).  With
+    use_initial_state the given S, z are the initial state; they are
+    overwritten with the final state."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev, dtype = _inputs("la_prefill", dict(q=q, k=k, v=v),
+                         dict(q=(B, H, T, dk), k=(B, H, T, dk), v=(B, H, T, dv)))
+    if use_initial_state and (S is None or z is None):
+        raise ValueError("la_prefill: use_initial_state needs S and z")
+    S = _state("la_prefill", "S", S, (B, H, dk, dv), dev)
+    z = _state("la_prefill", "z", z, (B, H, dk), dev)
+    o = _out("la_prefill", o, (B, H, T, dv), dev, dtype)
+    rc = library().la_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(S), _ptr(z),
+                              int(bool(use_initial_state)), B, H, T, dk, dv,
+                              _DTYPES[dtype], _stream(dev, stream))
+    _check("la_prefill", rc)
+    return o, S, z
+
+
+def la_decode_step(q, k, v, S, z, o=None, stream=None):
+    """One token per sequence: q, k [N,H,dk], v [N,H,dv]; S [N,H,dk,dv] and
+    z [N,H,dk] (fp32) updated in place.  Returns o [N,H,dv]."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dtype = _inputs("la_decode_step", dict(q=q, k=k, v=v),
+                         dict(q=(N, H, dk), k=(N, H, dk), v=(N, H, dv)))
+    S = _state("la_decode_step", "S", S, (N, H, dk, dv), dev)
+    z = _state("la_decode_step", "z", z, (N, H, dk), dev)
+    o = _out("la_decode_step", o, (N, H, dv), dev, dtype)
+    rc = library().la_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(S), _ptr(z),
+                                  N, H, dk, dv, _DTYPES[dtype], _stream(dev, stream))
+    _check("la_decode_step", rc)
+    return o
+
+
+def deltanet_prefill(q, k, v, beta, g=None, S=None, use_initial_state=False, o=None,
+                     stream=None):
+    """Delta rule (g None) or per-key-channel gated delta rule (g = log-decay
+    [B,H,T,dk]) over q, k [B,H,T,dk], v [B,H,T,dv], beta [B,H,T].
+    Returns (o [B,H,T,dv], S [B,H,dk,dv] fp32)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev, dtype = _inputs("deltanet_prefill", dict(q=q, k=k, v=v, beta=beta, g=g),
+                         dict(q=(B, H, T, dk), k=(B, H, T, dk), v=(B, H, T, dv),
+                              beta=(B, H, T), g=(B, H, T, dk)))
+    if use_initial_state and S is None:
+        raise ValueError("deltanet_prefill: use_initial_state needs S")
+    S = _state("deltanet_prefill", "S", S, (B, H, dk, dv), dev)
+    o = _out("deltanet_prefill", o, (B, H, T, dv), dev, dtype)
+    rc = library().deltanet_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                                    _ptr(o), _ptr(S), int(bool(use_initial_state)),
+                                    B, H, T, dk, dv, _DTYPES[dtype], _stream(dev, stream))
+    _check("deltanet_prefill", rc)
+    return o, S
+
+
+def deltanet_decode_step(q, k, v, beta, S, g=None, o=None, stream=None):
+    """One token per sequence: q, k [N,H,dk], v [N,H,dv], beta [N,H],
+    g [N,H,dk] or None; S [N,H,dk,dv] fp32 updated in place.  Returns o."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dtype = _inputs("deltanet_decode_step", dict(q=q, k=k, v=v, beta=beta, g=g),
+                         dict(q=(N, H, dk), k=(N, H, dk), v=(N, H, dv), beta=(N, H),
+                              g=(N, H, dk)))
+    S = _state("deltanet_decode_step", "S", S, (N, H, dk, dv), dev)
+    o = _out("deltanet_decode_step", o, (N, H, dv), dev, dtype)
+    rc = library().deltanet_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                                        _ptr(o), _ptr(S), N, H, dk, dv, _DTYPES[dtype],
+                                        _stream(dev, stream))
+    _check("deltanet_decode_step", rc)
+    return o

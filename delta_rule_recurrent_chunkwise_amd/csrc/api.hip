@@ -1,0 +1,103 @@
+// api.hip -- the extern "C" entry points of liblinattn.so.  Each validates
+// its arguments on the host (no HIP call happens before validation passes),
+// then enqueues one kernel on the caller's stream.  Declarations, argument
+// meaning and layouts are documented in include/linattn.h.
+#include <limits.h>
+#include <stdint.h>
+
+#include "../../include/linattn.h"
+#include "launch.hpp"
+
+namespace {
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+bool dtype_ok(int dt) { return dt == LA_DTYPE_F32 || dt == LA_DTYPE_BF16; }
+
+// Element counts must stay addressable and the grid within one dimension.
+bool sizes_ok(long long b, long long h, long long t, int dk, int dv) {
+  const long long mx = (dk > dv ? dk : dv);
+  if (b <= 0 || h <= 0 || t <= 0) return false;
+  if (b * h > INT_MAX) return false;
+  const long long elems = b * h * t * mx;
+  const long long state = b * h * (long long)dk * dv;
+  return elems / mx / t == b * h && elems < (1LL << 50) && state < (1LL << 50);
+}
+
+int launch_rc(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* la_strerror(int code) {
+  switch (code) {
+    case LA_OK: return "success";
+    case LA_ERR_NULL: return "a required pointer argument is NULL";
+    case LA_ERR_SHAPE:
+      return "invalid shape: B, H, N, T must be positive, T a multiple of 64 for prefill, "
+             "and sizes within range";
+    case LA_ERR_DTYPE: return "dtype must be LA_DTYPE_F32 (0) or LA_DTYPE_BF16 (1)";
+    case LA_ERR_UNSUPPORTED_DIM:
+      return "unsupported head dimension: dk and dv must each be 16, 32, 64 or 128 "
+             "(float32 gated prefill: dk <= 64)";
+    case LA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case LA_ERR_ALIGN:
+      return "q, k and v (prefill) and S (decode) must be 16-byte aligned";
+    default: return "unknown error code";
+  }
+}
+
+int la_prefill(const void* q, const void* k, const void* v, void* o, float* S, float* z,
+               int use_initial_state, int B, int H, int T, int dk, int dv, int dtype,
+               void* stream) {
+  if (!q || !k || !v || !o || !S || !z) return LA_ERR_NULL;
+  if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
+  if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1) || T % 64 != 0) return LA_ERR_SHAPE;
+  if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return LA_ERR_ALIGN;
+  linattn::PrefillArgs a{q, k, v, nullptr, nullptr, o, S, z, B, H, T, dv, use_initial_state ? 1 : 0};
+  return launch_rc(linattn::launch_prefill(linattn::PF_LA, dtype == LA_DTYPE_BF16, dk, a,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int la_decode_step(const void* q, const void* k, const void* v, void* o, float* S, float* z,
+                   int N, int H, int dk, int dv, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !S || !z) return LA_ERR_NULL;
+  if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
+  if (!sizes_ok(N, H, 1, dk > 0 ? dk : 1, dv > 0 ? dv : 1)) return LA_ERR_SHAPE;
+  if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
+  if (!aligned16(S)) return LA_ERR_ALIGN;
+  linattn::DecodeArgs a{q, k, v, nullptr, nullptr, o, S, z, N * H};
+  return launch_rc(linattn::launch_decode(linattn::DEC_LA, dtype == LA_DTYPE_BF16, dk, dv, a,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int deltanet_prefill(const void* q, const void* k, const void* v, const void* beta,
+                     const void* g, void* o, float* S, int use_initial_state, int B, int H,
+                     int T, int dk, int dv, int dtype, void* stream) {
+  if (!q || !k || !v || !beta || !o || !S) return LA_ERR_NULL;
+  if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
+  if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1) || T % 64 != 0) return LA_ERR_SHAPE;
+  if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
+  if (g && dtype == LA_DTYPE_F32 && dk > 64) return LA_ERR_UNSUPPORTED_DIM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return LA_ERR_ALIGN;
+  linattn::PrefillArgs a{q, k, v, beta, g, o, S, nullptr, B, H, T, dv, use_initial_state ? 1 : 0};
+  return launch_rc(linattn::launch_prefill(g ? linattn::PF_GATED : linattn::PF_DELTA, dtype == LA_DTYPE_BF16, dk, a,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int deltanet_decode_step(const void* q, const void* k, const void* v, const void* beta,
+                         const void* g, void* o, float* S, int N, int H, int dk, int dv,
+                         int dtype, void* stream) {
+  if (!q || !k || !v || !beta || !o || !S) return LA_ERR_NULL;
+  if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
+  if (!sizes_ok(N, H, 1, dk > 0 ? dk : 1, dv > 0 ? dv : 1)) return LA_ERR_SHAPE;
+  if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
+  if (!aligned16(S)) return LA_ERR_ALIGN;
+  linattn::DecodeArgs a{q, k, v, beta, g, o, S, nullptr, N * H};
+  return launch_rc(linattn::launch_decode(g ? linattn::DEC_GATED : linattn::DEC_DELTA, dtype == LA_DTYPE_BF16, dk, dv, a,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// launch.hpp -- internal interface between the C-ABI entry points (api.hip)
+// and the kernel launchers (decode.hip, prefill.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace linattn {
+
+enum DecodeKind { DEC_DELTA = 0, DEC_GATED = 1, DEC_LA = 2 };
+enum PrefillMode { PF_LA = 0, PF_DELTA = 1, PF_GATED = 2 };
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* beta;  // delta / gated only
+  const void* g;     // gated only
+  void* o;
+  float* S;
+  float* z;          // linear attention only
+  int nheads;        // N * H
+};
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* beta;  // delta / gated only
+  const void* g;     // gated only
+  void* o;
+  float* S;
+  float* z;          // linear attention only
+  int B, H, T, dv, use_init;
+};
+
+// Enqueue one kernel on `st`; returns hipGetLastError() of the launch, or
+// hipErrorInvalidValue for a combination with no kernel.
+hipError_t launch_decode(int kind, int bf16, int dk, int dv, const DecodeArgs& a,
+                         hipStream_t st);
+hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, hipStream_t st);
+
+}  // namespace linattn

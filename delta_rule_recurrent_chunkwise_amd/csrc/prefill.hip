@@ -1,0 +1,446 @@
+// prefill.hip -- chunkwise prefill of causal linear attention with a fixed
+// dk x dv fp32 state: ELU+1 linear attention with normaliser, the delta rule,
+// and the per-key-channel gated delta rule.
+//
+// Method (article "From GPT-2 to Kimi K3, explained"):
+//  * section "DeltaNet (Parallelizing Linear Transformers with Delta Rule)":
+//    the sequence is cut into chunks of C = 64 tokens; inside a chunk the
+//    masked product tril(Q K^T) is formed directly, across chunks everything
+//    is folded into the state S.  For the delta rule the chunk's corrections
+//    come from the UT/WY form: with L = tril(diag(beta) K K^T, -1) and
+//    T = (I + L)^{-1},  u = T diag(beta) (V - K S),  O = Q S + tril(Q K^T) u,
+//    S <- S + K^T u.  (The article forms W = T diag(beta) K and U = T diag(beta) V
+//    first; u = U - W S is the same quantity.)
+//  * section "Linear Attention": phi(x) = elu(x) + 1 on q and k, and the
+//    output divided by phi(q).z; chunkwise the denominator is
+//    phi(Q) z + rowsum(tril(phi(Q) phi(K)^T)), and z += sum of phi(k).
+//  * sections "Gated Delta Net" and "KDA / Kimi Linear": a decay per key
+//    channel applied to S before each read.  Within a chunk, with the
+//    cumulative decay Gam_t = prod_{s<=t} a_s (per channel, from the chunk
+//    start) -- the article's gamma^r / gamma^i ratios -- the same UT/WY form
+//    holds with K~ = Gam*K, K^ = K/Gam, Q~ = Gam*Q:
+//      L = tril(diag(beta) K~ K^^T, -1), u = T diag(beta) (V - K~ S),
+//      O = Q~ S + tril(Q~ K^^T) u,  S <- diag(Gam_C) S + (K*Gam_C/Gam)^T u.
+//
+// Mapping to gfx950.  One workgroup (4 waves) owns one (batch, head) and a
+// slice of DVS value columns (32, or 16 when dv = 16): the value columns of
+// the state evolve independently given T and the chunk's keys, so slicing dv
+// multiplies the number of independent serial chains.  Inside the workgroup
+// NCW = DVS/16 "chain" waves each keep S[:, 16 columns] in MFMA accumulator
+// registers for the whole sequence (fp32); the other waves form the
+// S-independent products of the chunk.  The chain never moves S through LDS:
+// an accumulator tile is used directly as the B operand of the next product
+// (see device_common.hpp), so the serial work per chunk is five small MFMA
+// contractions per chain wave.  Per chunk the whole 64-token tile of q, k and
+// the slice of v are staged in LDS once.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace linattn {
+
+constexpr int kC = 64;         // chunk length in tokens
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kWaves = kThreads / 64;
+
+template <int DK, class E, int MODE, int DVS>
+struct PrefillLayout {
+  typedef typename E::T T;
+  static constexpr int PAD = 16 / (int)sizeof(T);  // one 16-byte vector of padding
+  static constexpr int LQ = DK + PAD;               // row stride: sQ, sK, sKh
+  static constexpr int LKT = kC + PAD;              // row stride: sKt, sVt, sA
+  static constexpr int LTL = kC + 4;                // row stride: sTL (fp32)
+  static constexpr int oQ = 0;
+  static constexpr int oK = oQ + kC * LQ * (int)sizeof(T);
+  static constexpr int oKh = oK + kC * LQ * (int)sizeof(T);
+  static constexpr int oKt = oKh + (MODE == PF_GATED ? kC * LQ * (int)sizeof(T) : 0);
+  static constexpr int oVt = oKt + DK * LKT * (int)sizeof(T);
+  static constexpr int oA = oVt + DVS * LKT * (int)sizeof(T);
+  static constexpr int oTL = oA + kC * LKT * (int)sizeof(T);
+  static constexpr int oRow = oTL + (MODE == PF_LA ? 0 : kC * LTL * 4);  // beta or den
+  static constexpr int oVec = oRow + kC * 4;                            // Gam_C or z
+  static constexpr int oPart = oVec + DK * 4;                           // scan partials
+  static constexpr int total = oPart + (MODE == PF_GATED ? kThreads * 4 : 0);
+};
+
+// Workgroup i runs on XCD i % 8.  Give consecutive logical indices (the dv
+// slices of one head, which read the same q and k) to one XCD so they share
+// its L2.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  if (n % 8 != 0) return bid;
+  return (bid % 8) * (n / 8) + bid / 8;
+}
+
+__device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+template <class E>
+union VecU {
+  Vec16 v;
+  typename E::T e[E::kVec];
+};
+
+template <int DK, class E, int MODE, int DVS>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
+  typedef PrefillLayout<DK, E, MODE, DVS> L;
+  typedef typename E::T T;
+  constexpr bool kBf16 = sizeof(T) == 2;
+  constexpr int kVec = E::kVec;
+  constexpr int NCW = DVS / 16;  // chain waves
+  constexpr int NKT = DK / 16;   // 16-row tiles of S per chain wave
+  constexpr int LQ = L::LQ, LKT = L::LKT, LTL = L::LTL;
+
+  __shared__ __attribute__((aligned(16))) char smem[L::total];
+  T* sQ = reinterpret_cast<T*>(smem + L::oQ);
+  T* sK = reinterpret_cast<T*>(smem + L::oK);
+  T* sKh = MODE == PF_GATED ? reinterpret_cast<T*>(smem + L::oKh) : sK;
+  T* sKt = reinterpret_cast<T*>(smem + L::oKt);
+  T* sVt = reinterpret_cast<T*>(smem + L::oVt);
+  T* sA = reinterpret_cast<T*>(smem + L::oA);
+  float* sTL = reinterpret_cast<float*>(smem + L::oTL);
+  float* sRow = reinterpret_cast<float*>(smem + L::oRow);  // beta (delta) / den (LA)
+  float* sVec = reinterpret_cast<float*>(smem + L::oVec);  // Gam_C (gated) / z (LA)
+  float* sPart = reinterpret_cast<float*>(smem + L::oPart);
+
+  const int nsl = a.dv / DVS;
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = w / nsl;
+  const int sl = w - bh * nsl;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int lc = lane & 15;
+  const int lg = lane >> 4;
+  const int Tn = a.T;
+  const int dv = a.dv;
+
+  const T* qh = reinterpret_cast<const T*>(a.q) + (size_t)bh * Tn * DK;
+  const T* kh = reinterpret_cast<const T*>(a.k) + (size_t)bh * Tn * DK;
+  const T* vh = reinterpret_cast<const T*>(a.v) + (size_t)bh * Tn * dv + sl * DVS;
+  const T* bth = reinterpret_cast<const T*>(a.beta) + (size_t)bh * Tn;
+  const T* gh = reinterpret_cast<const T*>(a.g) + (size_t)bh * Tn * DK;
+  T* oh = reinterpret_cast<T*>(a.o) + (size_t)bh * Tn * dv + sl * DVS;
+  float* Sh = a.S + (size_t)bh * DK * dv + sl * DVS;
+
+  for (int i = tid; i < kC * LKT; i += kThreads) sA[i] = E::cvt(0.f);
+  if (MODE == PF_LA) {
+    for (int d = tid; d < DK; d += kThreads) sVec[d] = a.use_init ? a.z[(size_t)bh * DK + d] : 0.f;
+  }
+
+  const bool chain = wave < NCW;
+  const int cw = wave;
+  floatx4 st[NKT];
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt) {
+    st[kt] = zero4();
+    if (chain && a.use_init) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[kt][i] = Sh[(size_t)(16 * kt + 4 * lg + i) * dv + 16 * cw + lc];
+    }
+  }
+
+  const int nchunks = Tn / kC;
+  for (int c = 0; c < nchunks; ++c) {
+    const int t0 = c * kC;
+    __syncthreads();  // the previous chunk's readers of LDS are done
+
+    // ---------------- stage the chunk in LDS ----------------
+    if (MODE != PF_GATED) {
+      constexpr int VPR = DK / kVec;
+      for (int i = tid; i < kC * VPR; i += kThreads) {
+        const int r = i / VPR, cv = i - (i / VPR) * VPR;
+        VecU<E> qv, kv;
+        qv.v = *reinterpret_cast<const Vec16*>(qh + (size_t)(t0 + r) * DK + cv * kVec);
+        kv.v = *reinterpret_cast<const Vec16*>(kh + (size_t)(t0 + r) * DK + cv * kVec);
+        if (MODE == PF_LA) {
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) {
+            qv.e[e] = E::cvt(phi_elu1(E::tof(qv.e[e])));
+            kv.e[e] = E::cvt(phi_elu1(E::tof(kv.e[e])));
+          }
+        }
+        *reinterpret_cast<Vec16*>(sQ + r * LQ + cv * kVec) = qv.v;
+        *reinterpret_cast<Vec16*>(sK + r * LQ + cv * kVec) = kv.v;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) sKt[(cv * kVec + e) * LKT + r] = kv.e[e];
+      }
+    } else {
+      // cumulative log-decay per key channel over the chunk, then the scaled
+      // operands Q~ = Gam Q, K~ = Gam K, K^ = K / Gam, (K Gam_C / Gam)^T
+      constexpr int NP = kThreads / DK;  // token parts
+      constexpr int TPP = kC / NP;       // tokens per part
+      const int d = tid % DK;
+      const int part = tid / DK;
+      float gl[TPP];
+      float run = 0.f;
+#pragma unroll
+      for (int j = 0; j < TPP; ++j) {
+        run += E::ld(gh + (size_t)(t0 + part * TPP + j) * DK + d);
+        gl[j] = run;
+      }
+      sPart[part * DK + d] = run;
+      __syncthreads();
+      float off = 0.f, tot = 0.f;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const float x = sPart[p * DK + d];
+        if (p < part) off += x;
+        tot += x;
+      }
+      if (part == 0) sVec[d] = __expf(tot);
+#pragma unroll
+      for (int j = 0; j < TPP; ++j) {
+        const int r = part * TPP + j;
+        const float G = off + gl[j];
+        const float eg = __expf(G), emg = __expf(-G), dec = __expf(tot - G);
+        const float qv = E::ld(qh + (size_t)(t0 + r) * DK + d);
+        const float kv = E::ld(kh + (size_t)(t0 + r) * DK + d);
+        sQ[r * LQ + d] = E::cvt(qv * eg);
+        sK[r * LQ + d] = E::cvt(kv * eg);
+        sKh[r * LQ + d] = E::cvt(kv * emg);
+        sKt[d * LKT + r] = E::cvt(kv * dec);
+      }
+    }
+    {
+      constexpr int VPRV = DVS / kVec;
+      for (int i = tid; i < kC * VPRV; i += kThreads) {
+        const int r = i / VPRV, cv = i - (i / VPRV) * VPRV;
+        VecU<E> vv;
+        vv.v = *reinterpret_cast<const Vec16*>(vh + (size_t)(t0 + r) * dv + cv * kVec);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) sVt[(cv * kVec + e) * LKT + r] = vv.e[e];
+      }
+      if (MODE != PF_LA && tid < kC) sRow[tid] = E::ld(bth + t0 + tid);
+    }
+    __syncthreads();
+
+    // -------- chain waves: products with the incoming state; others: the
+    // -------- chunk's pairwise products
+    floatx4 ox[4], xx[4];
+    if (chain) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const T* qrow = sQ + (16 * mt + lc) * LQ;
+        if constexpr (kBf16) ox[mt] = mm_accB_bf16(zero4(), qrow, st, NKT, lane);
+        else ox[mt] = mm_accB_f32(zero4(), qrow, st, NKT, lane);
+        const T* vp = sVt + (16 * cw + lc) * LKT + 16 * mt + 4 * lg;
+        floatx4 vv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vv[i] = E::tof(vp[i]);
+        if (MODE == PF_LA) {
+          xx[mt] = vv;
+        } else {
+          const T* krow = sK + (16 * mt + lc) * LQ;
+          floatx4 y;
+          if constexpr (kBf16) y = mm_accB_bf16(zero4(), krow, st, NKT, lane);
+          else y = mm_accB_f32(zero4(), krow, st, NKT, lane);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xx[mt][i] = sRow[16 * mt + 4 * lg + i] * (vv[i] - y[i]);
+        }
+      }
+    } else {
+      // jobs 0..9: tiles (i, j<=i) of tril(Q K^^T) -> sA
+      // jobs 10..19: tiles (i, j<=i) of K~ K^^T -> L = beta_row * (.) strictly
+      //              below the diagonal, stored transposed in sTL's upper part
+      const int njobs = MODE == PF_LA ? 10 : 20;
+      for (int jb = wave - NCW; jb < njobs; jb += kWaves - NCW) {
+        const bool isA = jb < 10;
+        const int t = isA ? jb : jb - 10;
+        const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
+        const int tj = t - ti * (ti + 1) / 2;
+        const T* left = (isA ? sQ : sK) + (16 * ti + lc) * LQ;
+        const T* right = sKh + (16 * tj + lc) * LQ;
+        floatx4 acc;
+        if constexpr (kBf16) acc = mm_rowrow_bf16(zero4(), left, right, DK, lane);
+        else acc = mm_rowrow_f32(zero4(), left, right, DK, lane);
+        const int cc = 16 * tj + lc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * ti + 4 * lg + i;
+          if (isA) sA[r * LKT + cc] = E::cvt(cc <= r ? acc[i] : 0.f);
+          else if (cc < r) sTL[cc * LTL + r] = sRow[r] * acc[i];
+        }
+      }
+    }
+    __syncthreads();
+
+    if (MODE == PF_LA) {
+      // denominators phi(Q) z + rowsum(tril(phi(Q) phi(K)^T)), then z += sum phi(k)
+      if (wave == NCW) {
+        float den = 0.f;
+        for (int d = 0; d < DK; ++d) den += E::tof(sQ[lane * LQ + d]) * sVec[d];
+        for (int cidx = 0; cidx < kC; ++cidx) den += E::tof(sA[lane * LKT + cidx]);
+        sRow[lane] = den;
+        for (int d = lane; d < DK; d += 64) {
+          float zs = 0.f;
+          for (int r = 0; r < kC; ++r) zs += E::tof(sK[r * LQ + d]);
+          sVec[d] += zs;
+        }
+      }
+      __syncthreads();
+    } else {
+      // T = (I + L)^{-1}.  Diagonal 16x16 blocks by forward substitution (one
+      // lane per column), then off-diagonal blocks block-row by block-row:
+      // T[bi][bj] = -T[bi][bi] * sum_{bj<=m<bi} L[bi][m] T[m][bj].
+      // T is stored row-major in the lower triangle of sTL (diagonal included).
+      if (wave == kWaves - 1) {
+        const int b0 = 16 * lg;
+        float tv[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) tv[m] = m == lc ? 1.f : 0.f;
+#pragma unroll
+        for (int i = 1; i < 16; ++i) {
+          float s = 0.f;
+#pragma unroll
+          for (int m = 0; m < i; ++m) s += sTL[(b0 + m) * LTL + b0 + i] * tv[m];
+          if (i > lc) tv[i] = -s;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (i >= lc) sTL[(b0 + i) * LTL + b0 + lc] = tv[i];
+      }
+      __syncthreads();
+      for (int bi = 1; bi < 4; ++bi) {
+        if (wave < bi) {
+          const int bj = wave;
+          floatx4 R = zero4();
+          for (int m = bj; m < bi; ++m) {
+            float av[4], bv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int kk = 4 * lg + e;
+              av[e] = sTL[(16 * m + kk) * LTL + 16 * bi + lc];  // L[16bi+lc][16m+kk]
+              bv[e] = (m > bj || kk >= lc) ? sTL[(16 * m + kk) * LTL + 16 * bj + lc] : 0.f;
+            }
+            if constexpr (kBf16) {
+              R = mfma_k16(words_to_shortx4(pack2(av[0], av[1]), pack2(av[2], av[3])),
+                           words_to_shortx4(pack2(bv[0], bv[1]), pack2(bv[2], bv[3])), R);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) R = mfma_f32(av[e], bv[e], R);
+            }
+          }
+          float tv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int kk = 4 * lg + e;
+            tv[e] = kk <= lc ? sTL[(16 * bi + lc) * LTL + 16 * bi + kk] : 0.f;  // T[16bi+lc][16bi+kk]
+          }
+          floatx4 Y = zero4();
+          if constexpr (kBf16) {
+            Y = mfma_k16(words_to_shortx4(pack2(tv[0], tv[1]), pack2(tv[2], tv[3])),
+                         acc_to_b16(R), Y);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Y = mfma_f32(tv[e], R[e], Y);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sTL[(16 * bi + 4 * lg + i) * LTL + 16 * bj + lc] = -Y[i];
+        }
+        __syncthreads();
+      }
+      // clear the strictly upper triangle (it held L) so rows read as T
+      for (int i = tid; i < kC * kC; i += kThreads) {
+        const int r = i >> 6, cidx = i & 63;
+        if (cidx > r) sTL[r * LTL + cidx] = 0.f;
+      }
+      __syncthreads();
+    }
+
+    // ---------------- chain waves: finish the chunk ----------------
+    if (chain) {
+      floatx4 ut[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        if (MODE == PF_LA) {
+          ut[mt] = xx[mt];
+        } else {
+          // T is lower triangular: row tile mt needs column tiles 0..mt.  The
+          // bf16 path rounds that up to an even count (the extra tile of T is
+          // exactly zero) so one accumulation chain never mixes the 32-deep
+          // and 16-deep MFMA opcodes.
+          const float* trow = sTL + (16 * mt + lc) * LTL;
+          if constexpr (kBf16) ut[mt] = mm_accB_bf16(zero4(), trow, xx, (mt | 1) + 1, lane);
+          else ut[mt] = mm_accB_f32(zero4(), trow, xx, mt + 1, lane);
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const T* arow = sA + (16 * mt + lc) * LKT;  // tiles above the diagonal are zero
+        if constexpr (kBf16) ox[mt] = mm_accB_bf16(ox[mt], arow, ut, (mt | 1) + 1, lane);
+        else ox[mt] = mm_accB_f32(ox[mt], arow, ut, mt + 1, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * mt + 4 * lg + i;
+          float val = ox[mt][i];
+          if (MODE == PF_LA) val = val / sRow[r];
+          oh[(size_t)(t0 + r) * dv + 16 * cw + lc] = E::cvt(val);
+        }
+      }
+      if (MODE == PF_GATED) {
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st[kt][i] *= sVec[16 * kt + 4 * lg + i];
+      }
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+        const T* krow = sKt + (16 * kt + lc) * LKT;
+        if constexpr (kBf16) st[kt] = mm_accB_bf16(st[kt], krow, ut, 4, lane);
+        else st[kt] = mm_accB_f32(st[kt], krow, ut, 4, lane);
+      }
+    }
+  }
+
+  if (chain) {
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Sh[(size_t)(16 * kt + 4 * lg + i) * dv + 16 * cw + lc] = st[kt][i];
+  }
+  if (MODE == PF_LA && sl == 0) {
+    __syncthreads();
+    for (int d = tid; d < DK; d += kThreads) a.z[(size_t)bh * DK + d] = sVec[d];
+  }
+}
+
+template <int DK, class E, int MODE, int DVS>
+static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
+  const long blocks = (long)a.B * a.H * (a.dv / DVS);
+  hipLaunchKernelGGL((prefill_kernel<DK, E, MODE, DVS>), dim3((unsigned)blocks),
+                     dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int DK, class E, int MODE>
+static hipError_t launch_prefill_dk(const PrefillArgs& a, hipStream_t st) {
+  if (a.dv % 32 == 0) return launch_prefill_t<DK, E, MODE, 32>(a, st);
+  return launch_prefill_t<DK, E, MODE, 16>(a, st);
+}
+
+template <class E, int MODE>
+static hipError_t launch_prefill_e(int dk, const PrefillArgs& a, hipStream_t st) {
+  switch (dk) {
+    case 16: return launch_prefill_dk<16, E, MODE>(a, st);
+    case 32: return launch_prefill_dk<32, E, MODE>(a, st);
+    case 64: return launch_prefill_dk<64, E, MODE>(a, st);
+    case 128:
+      if constexpr (MODE == PF_GATED && sizeof(typename E::T) == 4) {
+        return hipErrorInvalidValue;  // LDS footprint exceeds one CU
+      } else {
+        return launch_prefill_dk<128, E, MODE>(a, st);
+      }
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, hipStream_t st) {
+  if (bf16) {
+    if (mode == PF_LA) return launch_prefill_e<BF16, PF_LA>(dk, a, st);
+    if (mode == PF_DELTA) return launch_prefill_e<BF16, PF_DELTA>(dk, a, st);
+    return launch_prefill_e<BF16, PF_GATED>(dk, a, st);
+  }
+  if (mode == PF_LA) return launch_prefill_e<F32, PF_LA>(dk, a, st);
+  if (mode == PF_DELTA) return launch_prefill_e<F32, PF_DELTA>(dk, a, st);
+  return launch_prefill_e<F32, PF_GATED>(dk, a, st);
+}
+
+}  // namespace linattn

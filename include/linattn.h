@@ -1,0 +1,135 @@
+/*
+ * linattn.h -- C ABI of liblinattn.so: causal linear attention with a fixed
+ * d_k x d_v state on one AMD Instinct MI355X (gfx950).
+ *
+ * The operations are those of the article "From GPT-2 to Kimi K3, explained"
+ * (Chinese mirror on transcrab.onev.cat, German mirror on youmind.com):
+ *   - ELU+1 linear attention with a running normaliser (section "Linear
+ *     Attention", cached forward: S += phi(k)^T v, z += phi(k),
+ *     o = phi(q) S / phi(q).z);
+ *   - the DeltaNet delta rule (sections "DeltaNet (Fast Weight Programmers)"
+ *     and "DeltaNet (Parallelizing Linear Transformers with Delta Rule)":
+ *     read r = k S, u = beta (v - r), write S += k^T u, output o = q S), whose
+ *     prefill runs in the chunkwise UT/WY form of the latter section;
+ *   - its per-key-channel gated variant (sections "Gated Delta Net" and "KDA /
+ *     Kimi Linear"): before each read the state decays,
+ *     S <- diag(a_t) S, with a separate decay a_t[i] per key channel i.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.   All tensors are dense, row-major, last index fastest:
+ *           q, k [B,H,T,dk]; v, o [B,H,T,dv]; beta [B,H,T]; g [B,H,T,dk];
+ *           S [B,H,dk,dv] (row i = key channel i); z [B,H,dk].
+ *           Decode entry points use the same layout with T = 1 dropped:
+ *           q, k, g [N,H,dk]; v, o [N,H,dv]; beta [N,H].
+ * Output.   o_t is read from the state AFTER token t has been written (the
+ *           article's code reads q S after S += ...), and the normaliser of
+ *           linear attention includes token t as well.
+ * dtype.    LA_DTYPE_F32 (0) or LA_DTYPE_BF16 (1); it applies to q, k, v,
+ *           beta, g and o.  The state S and normaliser z are always float32.
+ *           bf16 outputs are rounded to nearest even.
+ * Pointers. Device pointers (hipMalloc'd or equivalent), owned by the caller.
+ *           q, k, v of the prefill entry points and S of the decode entry
+ *           points must be 16-byte aligned (they are read in 16-byte
+ *           vectors).  o must not alias any input.  S (and z) are read and written.  The
+ *           library allocates no device memory and keeps no state between
+ *           calls; calls are re-entrant.
+ * Sizes.    B, H (or N, H) >= 1; T >= 1 and T a multiple of 64 for prefill;
+ *           dk and dv each one of 16, 32, 64, 128.  The per-channel gated
+ *           prefill with LA_DTYPE_F32 supports dk <= 64.
+ * Stream.   stream is a hipStream_t passed as void*; NULL is the null stream.
+ *           Work is enqueued asynchronously; nothing synchronises the host.
+ * Errors.   0 (LA_OK) or a negative code.  Arguments are validated before
+ *           any HIP call, so a bad call has no effect on the device.  A
+ *           kernel-launch failure returns LA_ERR_LAUNCH.  Numerical problems
+ *           (NaN/Inf inputs) are not errors: they propagate to the outputs.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_OK 0
+#define LA_ERR_NULL (-1)            /* a required pointer is NULL            */
+#define LA_ERR_SHAPE (-2)           /* B/H/N/T not positive, or T % 64 != 0  */
+#define LA_ERR_DTYPE (-3)           /* dtype not LA_DTYPE_F32/LA_DTYPE_BF16  */
+#define LA_ERR_UNSUPPORTED_DIM (-4) /* dk or dv not in {16, 32, 64, 128}     */
+#define LA_ERR_LAUNCH (-5)          /* the HIP runtime rejected a launch     */
+#define LA_ERR_ALIGN (-6)           /* a vector-accessed pointer is not      */
+                                    /* 16-byte aligned                       */
+
+#define LA_DTYPE_F32 0
+#define LA_DTYPE_BF16 1
+
+/*
+ * la_prefill -- causal ELU+1 linear attention over T tokens, chunkwise.
+ * Article section "Linear Attention" (cached forward, feature map
+ * phi(x) = elu(x) + 1 with the default constant 1, i.e. x + 1 for x > 0 and
+ * exp(x) otherwise) and the chunked form of section "DeltaNet (Parallelizing
+ * Linear Transformers with Delta Rule)" (intra-chunk masked attention plus an
+ * inter-chunk state read), extended with the normaliser:
+ *   S_t = S_{t-1} + phi(k_t)^T v_t,  z_t = z_{t-1} + phi(k_t),
+ *   o_t = phi(q_t) S_t / (phi(q_t) . z_t).
+ * q, k [B,H,T,dk], v [B,H,T,dv] in:    dtype.
+ * o [B,H,T,dv] out:                    dtype.
+ * S [B,H,dk,dv], z [B,H,dk] in/out:   float32.  use_initial_state = 0: the
+ *   incoming contents are ignored and the state starts at zero; otherwise
+ *   they are the initial state.  On completion they hold the final state.
+ */
+int la_prefill(const void *q, const void *k, const void *v, void *o, float *S,
+               float *z, int use_initial_state, int B, int H, int T, int dk,
+               int dv, int dtype, void *stream);
+
+/*
+ * la_decode_step -- one new token per sequence, state updated in place.
+ * Article section "Linear Attention", the cached forward at t = 1:
+ *   S <- S + phi(k)^T v,  z <- z + phi(k),  o = phi(q) S / (phi(q) . z).
+ * q, k [N,H,dk], v [N,H,dv] in; o [N,H,dv] out (dtype).
+ * S [N,H,dk,dv], z [N,H,dk] float32, read and written in place.
+ */
+int la_decode_step(const void *q, const void *k, const void *v, void *o,
+                   float *S, float *z, int N, int H, int dk, int dv, int dtype,
+                   void *stream);
+
+/*
+ * deltanet_prefill -- delta rule over T tokens in the chunkwise UT/WY form
+ * (64-token chunks).  Article section "DeltaNet (Parallelizing Linear
+ * Transformers with Delta Rule)": per token r = k_t S, u_t = beta_t (v_t - r),
+ * S += k_t^T u_t, o_t = q_t S; computed per chunk as
+ * T = (I + tril(diag(beta) K K^T, -1))^{-1}, u = T diag(beta) (V - K S),
+ * O = Q S + tril(Q K^T) u, S += K^T u.
+ * With g != NULL the per-key-channel gated rule of sections "Gated Delta Net"
+ * and "KDA / Kimi Linear" is used instead:
+ *   S_t = diag(a_t) S_{t-1} + beta_t k_t^T (v_t - k_t diag(a_t) S_{t-1}),
+ * where g = log a (the log-decay, <= 0) is given per token and key channel.
+ * q and k are used as given: no feature map, normalisation or scale.
+ * q, k [B,H,T,dk], v [B,H,T,dv], beta [B,H,T], g [B,H,T,dk] or NULL (dtype).
+ * o [B,H,T,dv] out (dtype).  S [B,H,dk,dv] float32 in/out as in la_prefill.
+ */
+int deltanet_prefill(const void *q, const void *k, const void *v,
+                     const void *beta, const void *g, void *o, float *S,
+                     int use_initial_state, int B, int H, int T, int dk,
+                     int dv, int dtype, void *stream);
+
+/*
+ * deltanet_decode_step -- one new token per sequence, state updated in
+ * place.  Article section "DeltaNet (Fast Weight Programmers)" (the layer
+ * forward at t = 1): optional decay S <- diag(exp(g)) S, then r = k S,
+ * u = beta (v - r), S <- S + k^T u, o = q S.
+ * q, k [N,H,dk], v [N,H,dv], beta [N,H], g [N,H,dk] or NULL in (dtype);
+ * o [N,H,dv] out (dtype); S [N,H,dk,dv] float32 in place.
+ */
+int deltanet_decode_step(const void *q, const void *k, const void *v,
+                         const void *beta, const void *g, void *o, float *S,
+                         int N, int H, int dk, int dv, int dtype,
+                         void *stream);
+
+/* la_strerror -- a static, NUL-terminated description of an error code. */
+const char *la_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LINATTN_H */

@@ -108,10 +108,11 @@ int orc_la_recurrent(int B, int H, int T, int dk, int dv,
         double *z = malloc(sizeof(double) * (size_t)dk);
         double *fq = malloc(sizeof(double) * (size_t)dk);
         double *fk = malloc(sizeof(double) * (size_t)dk);
-        if (!S || !z || !fq || !fk) {
+        double *num = malloc(sizeof(double) * (size_t)dv);
+        if (!S || !z || !fq || !fk || !num) {
 #pragma omp atomic write
             fail = 1;
-            free(S); free(z); free(fq); free(fk);
+            free(S); free(z); free(fq); free(fk); free(num);
             continue;
         }
         const size_t sbase = (size_t)bh * dk * dv;
@@ -133,24 +134,25 @@ int orc_la_recurrent(int B, int H, int T, int dk, int dv,
                     S[(size_t)i * dv + j] += fk[i] * rd(v, v_row + j, dt);
                 z[i] += fk[i];
             }
-            /* read with the updated state */
+            /* read with the updated state: o = phi(q) S / phi(q).z */
             if (o) {
                 double den = 0.0;
                 for (int i = 0; i < dk; i++)
                     den += fq[i] * z[i];
-                for (int j = 0; j < dv; j++) {
-                    double num = 0.0;
-                    for (int i = 0; i < dk; i++)
-                        num += fq[i] * S[(size_t)i * dv + j];
-                    o[v_row + j] = num / den;
-                }
+                for (int j = 0; j < dv; j++)
+                    num[j] = 0.0;
+                for (int i = 0; i < dk; i++)
+                    for (int j = 0; j < dv; j++)
+                        num[j] += fq[i] * S[(size_t)i * dv + j];
+                for (int j = 0; j < dv; j++)
+                    o[v_row + j] = num[j] / den;
             }
         }
         if (S_out)
             memcpy(S_out + sbase, S, sizeof(double) * (size_t)dk * dv);
         if (z_out)
             memcpy(z_out + (size_t)bh * dk, z, sizeof(double) * (size_t)dk);
-        free(S); free(z); free(fq); free(fk);
+        free(S); free(z); free(fq); free(fk); free(num);
     }
     return fail ? -1 : 0;
 }
@@ -178,11 +180,13 @@ int orc_delta_recurrent(int B, int H, int T, int dk, int dv,
     for (int bh = 0; bh < B * H; bh++) {
         double *S = malloc(sizeof(double) * (size_t)dk * dv);
         double *kt = malloc(sizeof(double) * (size_t)dk);
+        double *qt = malloc(sizeof(double) * (size_t)dk);
+        double *r = malloc(sizeof(double) * (size_t)dv);
         double *u = malloc(sizeof(double) * (size_t)dv);
-        if (!S || !kt || !u) {
+        if (!S || !kt || !qt || !r || !u) {
 #pragma omp atomic write
             fail = 1;
-            free(S); free(kt); free(u);
+            free(S); free(kt); free(qt); free(r); free(u);
             continue;
         }
         const size_t sbase = (size_t)bh * dk * dv;
@@ -200,29 +204,33 @@ int orc_delta_recurrent(int B, int H, int T, int dk, int dv,
                         S[(size_t)i * dv + j] *= a;
                 }
             }
-            for (int i = 0; i < dk; i++)
+            for (int i = 0; i < dk; i++) {
                 kt[i] = rd(k, qk_row + i, dt);
-            for (int j = 0; j < dv; j++) {
-                double r = 0.0;
-                for (int i = 0; i < dk; i++)
-                    r += kt[i] * S[(size_t)i * dv + j];
-                u[j] = b * (rd(v, v_row + j, dt) - r);
+                qt[i] = rd(q, qk_row + i, dt);
             }
+            /* r = k S (sum over key rows i, in order) */
+            for (int j = 0; j < dv; j++)
+                r[j] = 0.0;
+            for (int i = 0; i < dk; i++)
+                for (int j = 0; j < dv; j++)
+                    r[j] += kt[i] * S[(size_t)i * dv + j];
+            for (int j = 0; j < dv; j++)
+                u[j] = b * (rd(v, v_row + j, dt) - r[j]);
             for (int i = 0; i < dk; i++)
                 for (int j = 0; j < dv; j++)
                     S[(size_t)i * dv + j] += kt[i] * u[j];
+            /* o = q S with the updated state */
             if (o) {
-                for (int j = 0; j < dv; j++) {
-                    double acc = 0.0;
-                    for (int i = 0; i < dk; i++)
-                        acc += rd(q, qk_row + i, dt) * S[(size_t)i * dv + j];
-                    o[v_row + j] = acc;
-                }
+                for (int j = 0; j < dv; j++)
+                    o[v_row + j] = 0.0;
+                for (int i = 0; i < dk; i++)
+                    for (int j = 0; j < dv; j++)
+                        o[v_row + j] += qt[i] * S[(size_t)i * dv + j];
             }
         }
         if (S_out)
             memcpy(S_out + sbase, S, sizeof(double) * (size_t)dk * dv);
-        free(S); free(kt); free(u);
+        free(S); free(kt); free(qt); free(r); free(u);
     }
     return fail ? -1 : 0;
 }

@@ -1,0 +1,135 @@
+"""The C ABI of liblinattn.so without a GPU: the library loads, exports every
+function include/linattn.h declares, and rejects bad arguments with the
+documented codes before making any HIP call (the pointers passed here are
+never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import delta_rule_recurrent_chunkwise_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linattn.h")
+
+OK, NULL, SHAPE, DTYPE, DIM, LAUNCH, ALIGN = 0, -1, -2, -3, -4, -5, -6
+P = ctypes.c_void_p
+FAKE = P(0x1000)          # 16-byte aligned, never dereferenced
+MISALIGNED = P(0x1002)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def _codes():
+    text = open(HEADER).read()
+    return {m[0]: int(m[1]) for m in re.findall(r"#define\s+(LA_\w+)\s+\(?(-?\d+)\)?", text)}
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = la.library()
+    declared = _declared_functions()
+    assert set(declared) == set(la.EXPORTED_SYMBOLS), declared
+    for name in declared:
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_error_codes_match_header():
+    codes = _codes()
+    assert codes["LA_OK"] == OK and codes["LA_ERR_NULL"] == NULL
+    assert codes["LA_ERR_SHAPE"] == SHAPE and codes["LA_ERR_DTYPE"] == DTYPE
+    assert codes["LA_ERR_UNSUPPORTED_DIM"] == DIM and codes["LA_ERR_LAUNCH"] == LAUNCH
+    assert codes["LA_ERR_ALIGN"] == ALIGN
+    assert codes["LA_DTYPE_F32"] == 0 and codes["LA_DTYPE_BF16"] == 1
+
+
+def test_strerror_is_static_text_for_every_code():
+    for code in (OK, NULL, SHAPE, DTYPE, DIM, LAUNCH, ALIGN, -99, 7):
+        msg = la.la_strerror(code)
+        assert isinstance(msg, str) and msg
+    assert la.la_strerror(-99) == "unknown error code"
+
+
+def _la_prefill(q=FAKE, k=FAKE, v=FAKE, o=FAKE, S=FAKE, z=FAKE, init=0, B=1, H=1, T=64,
+                dk=64, dv=64, dt=1):
+    return la.library().la_prefill(q, k, v, o, S, z, init, B, H, T, dk, dv, dt, None)
+
+
+def _la_decode(q=FAKE, k=FAKE, v=FAKE, o=FAKE, S=FAKE, z=FAKE, N=1, H=1, dk=64, dv=64, dt=1):
+    return la.library().la_decode_step(q, k, v, o, S, z, N, H, dk, dv, dt, None)
+
+
+def _dn_prefill(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=None, o=FAKE, S=FAKE, init=0, B=1, H=1,
+                T=64, dk=64, dv=64, dt=1):
+    return la.library().deltanet_prefill(q, k, v, beta, g, o, S, init, B, H, T, dk, dv, dt,
+                                         None)
+
+
+def _dn_decode(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=None, o=FAKE, S=FAKE, N=1, H=1, dk=64,
+               dv=64, dt=1):
+    return la.library().deltanet_decode_step(q, k, v, beta, g, o, S, N, H, dk, dv, dt, None)
+
+
+@pytest.mark.parametrize("missing", ["q", "k", "v", "o", "S", "z"])
+def test_la_null_pointers(missing):
+    assert _la_prefill(**{missing: None}) == NULL
+    assert _la_decode(**{missing: None}) == NULL
+
+
+@pytest.mark.parametrize("missing", ["q", "k", "v", "beta", "o", "S"])
+def test_deltanet_null_pointers(missing):
+    assert _dn_prefill(**{missing: None}) == NULL
+    assert _dn_decode(**{missing: None}) == NULL
+
+
+@pytest.mark.parametrize("dt", [-1, 2, 7])
+def test_bad_dtype(dt):
+    assert _la_prefill(dt=dt) == DTYPE
+    assert _la_decode(dt=dt) == DTYPE
+    assert _dn_prefill(dt=dt) == DTYPE
+    assert _dn_decode(dt=dt) == DTYPE
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(T=0), dict(B=-3), dict(T=63),
+                                dict(T=100), dict(T=-64)])
+def test_bad_prefill_shape(kw):
+    assert _la_prefill(**kw) == SHAPE
+    assert _dn_prefill(**kw) == SHAPE
+
+
+@pytest.mark.parametrize("kw", [dict(N=0), dict(H=0), dict(N=-1), dict(N=1 << 20, H=1 << 12)])
+def test_bad_decode_shape(kw):
+    assert _la_decode(**kw) == SHAPE
+    assert _dn_decode(**kw) == SHAPE
+
+
+@pytest.mark.parametrize("kw", [dict(dk=8), dict(dv=8), dict(dk=96), dict(dv=256),
+                                dict(dk=0), dict(dv=-16)])
+def test_unsupported_dims(kw):
+    expected = SHAPE if min(kw.values()) <= 0 else DIM
+    got = {_la_prefill(**kw), _la_decode(**kw), _dn_prefill(**kw), _dn_decode(**kw)}
+    assert got <= {DIM, SHAPE} and (DIM in got if expected == DIM else True)
+
+
+def test_float32_gated_prefill_limited_to_dk_64():
+    assert _dn_prefill(g=FAKE, dt=0, dk=128, dv=64) == DIM
+
+
+def test_misaligned_vector_pointers():
+    assert _la_prefill(q=MISALIGNED) == ALIGN
+    assert _dn_prefill(v=MISALIGNED) == ALIGN
+    assert _la_decode(S=MISALIGNED) == ALIGN
+    assert _dn_decode(S=MISALIGNED) == ALIGN
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 64, 16)
+    with pytest.raises(ValueError):
+        la.deltanet_prefill(q, q, q, torch.zeros(1, 1, 64))
+    with pytest.raises(ValueError):
+        la.la_prefill(q, q, q)

@@ -1,0 +1,250 @@
+"""Chunkwise prefill on the GPU against the float64 oracle, through the C ABI,
+at sizes the oracle finishes in seconds that still span several 64-token
+chunks, plus the method's special cases and cross-entry-point checks."""
+import numpy as np
+import pytest
+import torch
+
+import delta_rule_recurrent_chunkwise_amd as la
+import oracle
+import workloads
+from gpu_common import TOL, assert_close, rel_err, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+DIMS = [(16, 16), (32, 64), (64, 32), (64, 64), (128, 128), (128, 16), (16, 128)]
+DTYPES = [torch.float32, torch.bfloat16]
+IDS = ["f32", "bf16"]
+
+
+def _dev(d, dev):
+    return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
+def _run_delta(inp, dev, gated, init):
+    d = _dev(inp, dev)
+    S = d["S0"].clone() if init else None
+    o, S = la.deltanet_prefill(d["q"], d["k"], d["v"], d["beta"], g=d.get("g"), S=S,
+                               use_initial_state=init)
+    torch.cuda.synchronize()
+    return o, S
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=IDS)
+@pytest.mark.parametrize("dk,dv", DIMS)
+@pytest.mark.parametrize("gated", [False, True], ids=["delta", "gated"])
+@pytest.mark.parametrize("init", [False, True], ids=["zero", "init"])
+def test_deltanet_prefill(dtype, dk, dv, gated, init):
+    dev = require_gpu()
+    if gated and dtype == torch.float32 and dk > 64:
+        pytest.skip("float32 gated prefill supports dk <= 64 (LDS footprint)")
+    B, H, T = 2, 3, 192
+    inp = workloads.make_delta(B, H, T, dk, dv, dtype, seed=100 + dk + 3 * dv,
+                               gated=gated, init_state=init, state_std=0.5)
+    o, S = _run_delta(inp, dev, gated, init)
+    o_ref, S_ref = oracle.delta_recurrent(inp["q"], inp["k"], inp["v"], inp["beta"],
+                                          inp.get("g"), S0=inp["S0"] if init else None)
+    assert_close(o, o_ref, TOL[dtype], "o")
+    assert_close(S, S_ref, TOL[dtype], "S")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=IDS)
+@pytest.mark.parametrize("dk,dv", DIMS)
+@pytest.mark.parametrize("init", [False, True], ids=["zero", "init"])
+def test_la_prefill(dtype, dk, dv, init):
+    dev = require_gpu()
+    B, H, T = 2, 3, 192
+    inp = workloads.make_la(B, H, T, dk, dv, dtype, seed=200 + dk + 3 * dv, init_state=init)
+    d = _dev(inp, dev)
+    S = d["S0"].clone() if init else None
+    z = d["z0"].clone() if init else None
+    o, S, z = la.la_prefill(d["q"], d["k"], d["v"], S=S, z=z, use_initial_state=init)
+    torch.cuda.synchronize()
+    o_ref, S_ref, z_ref = oracle.la_recurrent(inp["q"], inp["k"], inp["v"],
+                                              inp["S0"] if init else None,
+                                              inp["z0"] if init else None)
+    assert_close(o, o_ref, TOL[dtype], "o")
+    assert_close(S, S_ref, TOL[dtype], "S")
+    assert_close(z, z_ref, TOL[dtype], "z")
+
+
+def test_float32_gated_dk128_is_rejected():
+    dev = require_gpu()
+    inp = workloads.make_delta(1, 1, 64, 128, 64, torch.float32, seed=1, gated=True)
+    d = _dev(inp, dev)
+    with pytest.raises(la.LinAttnError) as e:
+        la.deltanet_prefill(d["q"], d["k"], d["v"], d["beta"], g=d["g"])
+    assert e.value.code == -4
+
+
+def test_single_chunk_and_long_sequence():
+    """T = 64 (one chunk) and T = 1024 (sixteen chunks), bf16, d = 128."""
+    dev = require_gpu()
+    for T in (64, 1024):
+        inp = workloads.make_delta(1, 2, T, 128, 128, torch.bfloat16, seed=T, gated=True)
+        o, S = _run_delta(inp, dev, True, False)
+        o_ref, S_ref = oracle.delta_recurrent(inp["q"], inp["k"], inp["v"], inp["beta"],
+                                              inp["g"])
+        assert_close(o, o_ref, 2e-2, f"o T={T}")
+        assert_close(S, S_ref, 2e-2, f"S T={T}")
+
+
+def test_beta_zero_keeps_state_and_reads_it():
+    dev = require_gpu()
+    inp = workloads.make_delta(1, 2, 128, 64, 64, torch.float32, seed=3, init_state=True,
+                               state_std=1.0)
+    inp["beta"] = torch.zeros_like(inp["beta"])
+    o, S = _run_delta(inp, dev, False, True)
+    assert_close(S, inp["S0"], 1e-6, "S unchanged")
+    ref = torch.einsum("bhtd,bhde->bhte", inp["q"].double(), inp["S0"].double())
+    assert_close(o, ref, 1e-5, "o = q S0")
+
+
+def test_exact_retrieval_with_orthonormal_keys():
+    """beta = 1, orthonormal keys, zero state: K S_T = V and a query equal to an
+    earlier key reads back that key's value (fp32 inputs)."""
+    dev = require_gpu()
+    d, T = 128, 128
+    gen = torch.Generator().manual_seed(9)
+    Qm, _ = torch.linalg.qr(torch.randn(d, d, generator=gen, dtype=torch.float64))
+    keys = Qm.T[:T // 2].float()                    # 64 orthonormal rows
+    k = torch.cat([keys, keys.flip(0)])[None, None].contiguous()   # rewrite in reverse
+    v = torch.randn(1, 1, T, d, generator=gen)
+    q = k.clone()
+    beta = torch.ones(1, 1, T)
+    o, S = la.deltanet_prefill(q.to(dev), k.to(dev), v.to(dev), beta.to(dev))
+    torch.cuda.synchronize()
+    # the second half rewrites every key: it must read back the newest value
+    assert_close(o[0, 0], v[0, 0], 1e-4, "o_t = v_t")
+    newest = v[0, 0, T // 2:].flip(0)               # value now stored at keys[i]
+    assert_close(keys.to(dev) @ S[0, 0], newest, 1e-4, "K S = newest V")
+
+
+def test_gate_limits():
+    """g = 0 equals the ungated rule; a strong uniform decay (a = e^-1.2 per
+    token, a cumulative log-decay of -76.8 over a 64-token chunk, near the
+    range the chunk form supports) still matches the oracle."""
+    dev = require_gpu()
+    inp = workloads.make_delta(1, 2, 128, 64, 64, torch.bfloat16, seed=4, gated=True,
+                               init_state=True)
+    o1, S1 = _run_delta(dict(inp, g=torch.zeros_like(inp["g"])), dev, True, True)
+    plain = {k: v for k, v in inp.items() if k != "g"}
+    o2, S2 = _run_delta(plain, dev, False, True)
+    assert_close(o1, o2.float(), 1e-6, "g=0 vs ungated o")
+    assert_close(S1, S2, 1e-6, "g=0 vs ungated S")
+    strong = dict(inp, g=torch.full_like(inp["g"], -1.2))
+    o3, S3 = _run_delta(strong, dev, True, True)
+    o_ref, S_ref = oracle.delta_recurrent(strong["q"], strong["k"], strong["v"],
+                                          strong["beta"], strong["g"], S0=strong["S0"])
+    assert_close(o3, o_ref, 2e-2, "strong decay o")
+    assert_close(S3, S_ref, 2e-2, "strong decay S")
+
+
+def test_decode_gate_clears_memory():
+    """Decode with a very negative log-decay: the state is cleared before the
+    write, so S = beta k^T v and o = beta (q.k) v."""
+    dev = require_gpu()
+    inp = workloads.make_decode(3, 2, 64, 32, torch.float32, seed=6, gated=True, ring=1)
+    S = inp["S0"].to(dev)
+    g = torch.full_like(inp["g"][0], -200.0)
+    q, k, v, beta = (inp[n][0] for n in ("q", "k", "v", "beta"))
+    o = la.deltanet_decode_step(q.to(dev), k.to(dev), v.to(dev), beta.to(dev), S, g=g.to(dev))
+    torch.cuda.synchronize()
+    ref_S = beta.double()[..., None, None] * k.double()[..., :, None] * v.double()[..., None, :]
+    ref_o = (beta.double() * (q.double() * k.double()).sum(-1))[..., None] * v.double()
+    assert_close(S, ref_S, 1e-5, "cleared S")
+    assert_close(o, ref_o, 1e-4, "cleared o")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=IDS)
+def test_split_prefill_equals_full(dtype):
+    """prefill(T1) then prefill(T2) from the returned state equals prefill(T1+T2)
+    exactly (same chunks, fp32 state carried through memory)."""
+    dev = require_gpu()
+    inp = workloads.make_delta(2, 2, 256, 64, 128, dtype, seed=12, gated=True)
+    if dtype == torch.float32:
+        inp = workloads.make_delta(2, 2, 256, 64, 64, dtype, seed=12, gated=True)
+    d = _dev(inp, dev)
+    o, S = la.deltanet_prefill(d["q"], d["k"], d["v"], d["beta"], g=d["g"])
+    cut = 128
+    part = {n: d[n][:, :, :cut].contiguous() for n in ("q", "k", "v", "beta", "g")}
+    rest = {n: d[n][:, :, cut:].contiguous() for n in ("q", "k", "v", "beta", "g")}
+    o1, S1 = la.deltanet_prefill(part["q"], part["k"], part["v"], part["beta"], g=part["g"])
+    o2, S2 = la.deltanet_prefill(rest["q"], rest["k"], rest["v"], rest["beta"], g=rest["g"],
+                                 S=S1, use_initial_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([o1, o2], dim=2), o)
+    assert torch.equal(S2, S)
+    la_inp = _dev(workloads.make_la(1, 2, 192, 32, 32, dtype, seed=13), dev)
+    oa, Sa, za = la.la_prefill(la_inp["q"], la_inp["k"], la_inp["v"])
+    c = {n: la_inp[n][:, :, :64].contiguous() for n in ("q", "k", "v")}
+    r = {n: la_inp[n][:, :, 64:].contiguous() for n in ("q", "k", "v")}
+    ob1, Sb1, zb1 = la.la_prefill(c["q"], c["k"], c["v"])
+    ob2, Sb2, zb2 = la.la_prefill(r["q"], r["k"], r["v"], S=Sb1, z=zb1, use_initial_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([ob1, ob2], dim=2), oa)
+    assert torch.equal(Sb2, Sa) and torch.equal(zb2, za)
+
+
+@pytest.mark.parametrize("gated", [False, True], ids=["delta", "gated"])
+def test_prefill_equals_decode_steps(gated):
+    """The chunkwise prefill and T one-token decode steps compute the same
+    recurrence (GPU against GPU, fp32)."""
+    dev = require_gpu()
+    B, H, T, dk, dv = 1, 3, 128, 32, 64
+    inp = _dev(workloads.make_delta(B, H, T, dk, dv, torch.float32, seed=21, gated=gated,
+                                    init_state=True, state_std=0.3), dev)
+    o, S = la.deltanet_prefill(inp["q"], inp["k"], inp["v"], inp["beta"], g=inp.get("g"),
+                               S=inp["S0"].clone(), use_initial_state=True)
+    Sd = inp["S0"].clone()
+    outs = []
+    for t in range(T):
+        sl = {n: inp[n][:, :, t].contiguous() for n in ("q", "k", "v", "beta")}
+        g = inp["g"][:, :, t].contiguous() if gated else None
+        outs.append(la.deltanet_decode_step(sl["q"], sl["k"], sl["v"], sl["beta"], Sd, g=g))
+    torch.cuda.synchronize()
+    assert_close(o, torch.stack(outs, dim=2), 1e-4, "prefill vs decode o")
+    assert_close(S, Sd, 1e-4, "prefill vs decode S")
+
+
+def test_la_prefill_equals_decode_steps():
+    dev = require_gpu()
+    B, H, T, d = 1, 2, 128, 32
+    inp = _dev(workloads.make_la(B, H, T, d, d, torch.float32, seed=22, init_state=True), dev)
+    o, S, z = la.la_prefill(inp["q"], inp["k"], inp["v"], S=inp["S0"].clone(),
+                            z=inp["z0"].clone(), use_initial_state=True)
+    Sd, zd = inp["S0"].clone(), inp["z0"].clone()
+    outs = [la.la_decode_step(inp["q"][:, :, t].contiguous(), inp["k"][:, :, t].contiguous(),
+                              inp["v"][:, :, t].contiguous(), Sd, zd) for t in range(T)]
+    torch.cuda.synchronize()
+    assert_close(o, torch.stack(outs, dim=2), 1e-4, "la prefill vs decode o")
+    assert_close(S, Sd, 1e-4, "la prefill vs decode S")
+    assert_close(z, zd, 1e-5, "la prefill vs decode z")
+
+
+def test_deterministic():
+    dev = require_gpu()
+    inp = _dev(workloads.make_delta(2, 4, 512, 128, 128, torch.bfloat16, seed=31,
+                                    gated=True), dev)
+    a = la.deltanet_prefill(inp["q"], inp["k"], inp["v"], inp["beta"], g=inp["g"])
+    b = la.deltanet_prefill(inp["q"], inp["k"], inp["v"], inp["beta"], g=inp["g"])
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_nan_stays_in_its_head():
+    """A NaN in one token of one head poisons that head from the token's chunk
+    on; every other head still matches the oracle."""
+    dev = require_gpu()
+    B, H, T, d = 1, 4, 192, 64
+    inp = workloads.make_delta(B, H, T, d, d, torch.bfloat16, seed=41)
+    inp["v"][0, 2, 100, 5] = float("nan")
+    o, S = _run_delta(inp, dev, False, False)
+    o_ref, S_ref = oracle.delta_recurrent(inp["q"], inp["k"], inp["v"], inp["beta"])
+    ok = [0, 1, 3]
+    assert_close(o[:, ok], o_ref[:, ok], 2e-2, "clean heads o")
+    assert_close(S[:, ok], S_ref[:, ok], 2e-2, "clean heads S")
+    oc = o[0, 2].float().cpu()
+    assert torch.isfinite(oc[:64]).all(), "chunks before the NaN stay finite"
+    assert torch.isnan(oc[128:]).any(axis=1).all(), "NaN reaches every later token"
+    assert torch.isnan(S[0, 2]).any()

@@ -1,0 +1,104 @@
+"""The five workloads at full size, in the launch configuration bench.py
+times, against the float64 oracle.  Where the oracle over the whole workload
+would take minutes, outputs are compared on sampled heads, which the oracle
+recomputes independently (heads never interact)."""
+import numpy as np
+import pytest
+import torch
+
+import delta_rule_recurrent_chunkwise_amd as la
+import oracle
+import workloads
+from gpu_common import TOL, assert_close, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+W = workloads.WORKLOADS
+
+
+def _to(d, dev):
+    return {k: v.to(dev) for k, v in d.items()}
+
+
+@pytest.mark.parametrize("w", [W[0], W[1]], ids=lambda w: w.name)
+def test_la_workload_full(w):
+    dev = require_gpu()
+    print(f"workload {w.name}", flush=True)
+    inp = workloads.make_workload(w)
+    d = _to(inp, dev)
+    o, S, z = la.la_prefill(d["q"], d["k"], d["v"])
+    torch.cuda.synchronize()
+    o_ref, S_ref, z_ref = oracle.la_recurrent(inp["q"], inp["k"], inp["v"])
+    tol = TOL[w.dtype]
+    assert_close(o, o_ref, tol, "o")
+    assert_close(S, S_ref, tol, "S")
+    assert_close(z, z_ref, tol, "z")
+
+
+def test_deltanet_workload_full():
+    dev = require_gpu()
+    w = W[2]
+    print(f"workload {w.name}", flush=True)
+    inp = workloads.make_workload(w)
+    d = _to(inp, dev)
+    o, S = la.deltanet_prefill(d["q"], d["k"], d["v"], d["beta"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.delta_recurrent(inp["q"], inp["k"], inp["v"], inp["beta"])
+    assert_close(o, o_ref, TOL[w.dtype], "o")
+    assert_close(S, S_ref, TOL[w.dtype], "S")
+
+
+def test_gated_workload_sampled_heads():
+    dev = require_gpu()
+    w = W[3]
+    print(f"workload {w.name}", flush=True)
+    inp = workloads.make_workload(w)
+    d = _to(inp, dev)
+    o, S = la.deltanet_prefill(d["q"], d["k"], d["v"], d["beta"], g=d["g"])
+    torch.cuda.synchronize()
+    heads = [0, 5, 11, 18, 24, 31]
+    sub = {n: inp[n][:, heads].contiguous() for n in ("q", "k", "v", "beta", "g")}
+    o_ref, S_ref = oracle.delta_recurrent(sub["q"], sub["k"], sub["v"], sub["beta"], sub["g"])
+    assert_close(o[:, heads], o_ref, TOL[w.dtype], "o (sampled heads)")
+    assert_close(S[:, heads], S_ref, TOL[w.dtype], "S (sampled heads)")
+
+
+def test_decode_workload():
+    """Step 1 on the full 512 MiB state; then 10 + 1000 consecutive steps (the
+    bench's warm-up and timed steps, ring slot i mod 16) compared on 64 sampled
+    (sequence, head) pairs replayed by the oracle."""
+    dev = require_gpu()
+    w = W[4]
+    print(f"workload {w.name}", flush=True)
+    inp = workloads.make_workload(w)
+    ring = inp["q"].shape[0]
+    d = _to(inp, dev)
+    S = d["S0"].clone()
+    o = la.deltanet_decode_step(d["q"][0], d["k"][0], d["v"][0], d["beta"][0], S)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.delta_recurrent(inp["q"][0][:, :, None], inp["k"][0][:, :, None],
+                                          inp["v"][0][:, :, None],
+                                          inp["beta"][0][:, :, None], None, S0=inp["S0"])
+    assert_close(o, o_ref[:, :, 0], TOL[w.dtype], "o step 1")
+    assert_close(S, S_ref, TOL[w.dtype], "S step 1 (full state)")
+    del S_ref
+    steps = 1010
+    for i in range(1, steps):
+        s = i % ring
+        o = la.deltanet_decode_step(d["q"][s], d["k"][s], d["v"][s], d["beta"][s], S)
+    torch.cuda.synchronize()
+    gen = np.random.default_rng(0)
+    pairs = sorted(set(zip(gen.integers(0, w.B, 64).tolist(), gen.integers(0, w.H, 64).tolist())))
+    n_idx = torch.tensor([p[0] for p in pairs])
+    h_idx = torch.tensor([p[1] for p in pairs])
+    slots = torch.arange(steps) % ring
+
+    def seq(x):   # [ring, N, H, d] -> [1, P, steps, d]
+        return x[slots][:, n_idx, h_idx].permute(1, 0, 2).unsqueeze(0).contiguous()
+
+    q, k, v = seq(inp["q"]), seq(inp["k"]), seq(inp["v"])
+    beta = inp["beta"][slots][:, n_idx, h_idx].T.unsqueeze(0).contiguous()
+    S0 = inp["S0"][n_idx, h_idx].unsqueeze(0)
+    o_ref, S_ref = oracle.delta_recurrent(q, k, v, beta, None, S0=S0)
+    assert_close(S[n_idx, h_idx], S_ref[0], TOL[w.dtype], "S after 1010 steps (sampled)")
+    assert_close(o[n_idx, h_idx], o_ref[0, :, -1], TOL[w.dtype], "o of step 1010 (sampled)")

@@ -28,18 +28,23 @@ MUTANTS = {
     "la_normaliser_not_accumulated": ("z[i] += fk[i];", "z[i] += 0.0 * fk[i];"),
     "la_reads_state_before_write": (
         "den += fq[i] * z[i];", "den += fq[i] * (z[i] - fk[i]) + 1e-300;"),
+    "la_numerator_with_key_feature": (
+        "num[j] += fq[i] * S[(size_t)i * dv + j];", "num[j] += fk[i] * S[(size_t)i * dv + j];"),
     "delta_sign_of_correction": (
-        "u[j] = b * (rd(v, v_row + j, dt) - r);",
-        "u[j] = b * (rd(v, v_row + j, dt) + r);"),
+        "u[j] = b * (rd(v, v_row + j, dt) - r[j]);",
+        "u[j] = b * (rd(v, v_row + j, dt) + r[j]);"),
     "delta_beta_applied_twice": (
         "S[(size_t)i * dv + j] += kt[i] * u[j];",
         "S[(size_t)i * dv + j] += kt[i] * u[j] * b;"),
     "delta_read_with_query": (
-        "r += kt[i] * S[(size_t)i * dv + j];",
-        "r += rd(q, qk_row + i, dt) * S[(size_t)i * dv + j];"),
+        "r[j] += kt[i] * S[(size_t)i * dv + j];",
+        "r[j] += qt[i] * S[(size_t)i * dv + j];"),
     "delta_output_with_key": (
-        "acc += rd(q, qk_row + i, dt) * S[(size_t)i * dv + j];",
-        "acc += kt[i] * S[(size_t)i * dv + j];"),
+        "o[v_row + j] += qt[i] * S[(size_t)i * dv + j];",
+        "o[v_row + j] += kt[i] * S[(size_t)i * dv + j];"),
+    "delta_state_transposed_write": (
+        "S[(size_t)i * dv + j] += kt[i] * u[j];",
+        "S[(size_t)i * dv + j] += kt[j % dk] * u[i % dv];"),
     "gate_sign": (
         "const double a = exp(rd(g, qk_row + i, dt));",
         "const double a = exp(-rd(g, qk_row + i, dt));"),
