@@ -37,5 +37,7 @@ struct PrefillArgs {
 hipError_t launch_decode(int kind, int bf16, int dk, int dv, const DecodeArgs& a,
                          hipStream_t st);
 hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, hipStream_t st);
+// The software-pipelined delta-rule prefill: bf16, dk = 128, dv % 32 == 0.
+hipError_t launch_prefill_pipe(const PrefillArgs& a, hipStream_t st);
 
 }  // namespace linattn

@@ -433,6 +433,7 @@ static hipError_t launch_prefill_e(int dk, const PrefillArgs& a, hipStream_t st)
 }
 
 hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, hipStream_t st) {
+  if (bf16 && mode == PF_DELTA && dk == 128 && a.dv % 32 == 0) return launch_prefill_pipe(a, st);
   if (bf16) {
     if (mode == PF_LA) return launch_prefill_e<BF16, PF_LA>(dk, a, st);
     if (mode == PF_DELTA) return launch_prefill_e<BF16, PF_DELTA>(dk, a, st);

@@ -1,0 +1,464 @@
+// prefill_pipe.hip -- software-pipelined chunkwise delta-rule prefill for
+// bf16 inputs with dk = 128 and dv a multiple of 32 (the throughput path).
+//
+// The arithmetic is that of the article "From GPT-2 to Kimi K3, explained",
+// section "DeltaNet (Parallelizing Linear Transformers with Delta Rule)":
+// per 64-token chunk, with L = tril(diag(beta) K K^T, -1) and T = (I + L)^-1,
+//   u = T diag(beta) (V - K S),   O = Q S + tril(Q K^T) u,   S <- S + K^T u.
+// It is the same computation as prefill.hip; this kernel only organises it
+// for throughput on one CU.
+//
+// Work split inside a workgroup (8 waves; one (batch, head) and 32 value
+// columns per workgroup):
+//   waves 0-1  "chain": each keeps S[:, 16 columns] in MFMA accumulators and
+//              runs only the S-dependent products of chunk c.
+//   waves 2,3,7 products of chunk c+1: K K^T (giving L) in phase 1 and
+//              tril(Q K^T) in phase 2.
+//   wave 6     T = (I + L)^-1 of chunk c+1: the four 16x16 diagonal blocks by
+//              fp32 forward substitution in phase 2 (one lane per column),
+//              the off-diagonal blocks by MFMA block products in phase 1 of
+//              the next iteration, straight from registers.
+//   waves 4-5  the transposed copy K^T of chunk c+1 (phase 2).
+//   all waves  a share of the global loads of q and k, issued two chunks
+//              ahead into registers and written to LDS one iteration later.
+// Each iteration has two phases separated by LDS-only barriers, so global
+// loads stay in flight across them.
+//
+// Index conventions.  K and Q are stored row-major in natural column order.
+// The chain's 32-deep MFMA pairs two accumulator tiles; the k-index order
+// that pairing implies is absorbed by a fixed permutation of S's rows: the
+// accumulator row rho = 32b + 16h + 4g + i of a chain wave holds logical key
+// channel d = 32b + 8g + 4h + i (perm32 below).  Matrices used as A operands
+// against such paired tiles over tokens (T, tril(Q K^T), K^T) store their
+// token columns permuted the same way, so every operand fragment is one
+// 16-byte LDS read.
+#include <type_traits>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace linattn {
+namespace {
+
+constexpr int kC = 64;
+constexpr int kDK = 128;
+constexpr int kDVS = 32;
+constexpr int kThreads = 512;
+
+constexpr int kLQ = kDK + 8;  // bf16 row stride of q, k (16-byte aligned, conflict-free)
+constexpr int kLT = kC + 8;   // bf16 row stride of K^T, tril(QK^T), T
+constexpr int kLL = kC + 4;   // fp32 row stride of L / D
+
+struct __attribute__((aligned(16))) Smem {
+  bf16_t q[2][kC][kLQ];
+  bf16_t k[2][kC][kLQ];
+  bf16_t kt[2][kDK][kLT];
+  bf16_t a[2][kC][kLT];
+  bf16_t t[kC][kLT];
+  float l[kC][kLL];
+  float beta[2][kC];
+};
+
+// 32b + 16h + 4g + i  ->  32b + 8g + 4h + i
+__device__ __forceinline__ int perm32(int x) {
+  return (x & ~31) | (((x >> 2) & 3) << 3) | (((x >> 4) & 1) << 2) | (x & 3);
+}
+// inverse: 32b + 8g + 4h + i  ->  32b + 16h + 4g + i
+__device__ __forceinline__ int perm32_inv(int x) {
+  return (x & ~31) | (((x >> 2) & 1) << 4) | (((x >> 3) & 3) << 2) | (x & 3);
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  if (n % 8 != 0) return bid;
+  return (bid % 8) * (n / 8) + bid / 8;
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 ld_frag(const bf16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// 16x16 fp32 accumulator tile used as a 16-deep bf16 MFMA operand.  As B it
+// is the tile itself; as A it is the tile's transpose.
+__device__ __forceinline__ floatx4 mm16(floatx4 a_acc, floatx4 b_acc, floatx4 c) {
+  return mfma_k16(acc_to_b16(a_acc), acc_to_b16(b_acc), c);
+}
+__device__ __forceinline__ floatx4 neg4(floatx4 x) { return floatx4{-x[0], -x[1], -x[2], -x[3]}; }
+
+// Registers a wave keeps from the diagonal inverses of one chunk (phase 2)
+// to the block merges (phase 1 of the next iteration).  "n" tiles hold a
+// matrix in accumulator layout, "t" tiles its transpose.
+struct TCarry {
+  floatx4 d0n, d1n, d2n;
+  floatx4 d0t, d1t, d2t, d3t;
+  floatx4 l10t, l32t, l20t, l21t, l30t, l31t;
+};
+
+// Product tile lists: row block i with column blocks j <= i.
+__device__ __forceinline__ int prod_rows(int wave, int& i0, int& i1) {
+  // wave 2: row 3 (4 tiles); wave 3: row 2 (3 tiles); wave 7: rows 0, 1 (3 tiles)
+  if (wave == 2) { i0 = 3; i1 = 3; }
+  else if (wave == 3) { i0 = 2; i1 = 2; }
+  else { i0 = 0; i1 = 1; }
+  return 0;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
+  __shared__ Smem sm;
+
+  const int nsl = a.dv / kDVS;
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = w / nsl;
+  const int sl = w - bh * nsl;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lc = lane & 15;
+  const int lg = lane >> 4;
+  const int Tn = a.T;
+  const int dv = a.dv;
+  const int nch = Tn / kC;
+
+  const bf16_t* qh = reinterpret_cast<const bf16_t*>(a.q) + (size_t)bh * Tn * kDK;
+  const bf16_t* kh = reinterpret_cast<const bf16_t*>(a.k) + (size_t)bh * Tn * kDK;
+  const bf16_t* vh = reinterpret_cast<const bf16_t*>(a.v) + (size_t)bh * Tn * dv + sl * kDVS;
+  const bf16_t* bth = reinterpret_cast<const bf16_t*>(a.beta) + (size_t)bh * Tn;
+  bf16_t* oh = reinterpret_cast<bf16_t*>(a.o) + (size_t)bh * Tn * dv + sl * kDVS;
+  float* Sh = a.S + (size_t)bh * kDK * dv + sl * kDVS;
+
+  // Tiles above the diagonal of tril(QK^T) and T are read as zeros.
+  {
+    uint32_t* z = reinterpret_cast<uint32_t*>(&sm.a[0][0][0]);
+    for (int i = tid; i < (int)(sizeof(sm.a) / 4); i += kThreads) z[i] = 0u;
+    uint32_t* zt = reinterpret_cast<uint32_t*>(&sm.t[0][0]);
+    for (int i = tid; i < (int)(sizeof(sm.t) / 4); i += kThreads) zt[i] = 0u;
+  }
+
+  // ---- register prefetch of q and k by waves 2..7 (the chain waves keep
+  // their registers for the state): thread u = tid - 128 owns the 16-byte
+  // vectors u + 384 j of a chunk (vectors 0..1023 are q, 1024..2047 k);
+  // beta is loaded by wave 4.
+  constexpr int kLoaders = kThreads - 128;
+  constexpr int kPerLoader = (2048 + kLoaders - 1) / kLoaders;  // 6
+  const int lu = tid - 128;
+  auto issue_loads = [&](int chunk, u32x4 (&dst)[kPerLoader], float& bdst) {
+#pragma unroll
+    for (int j = 0; j < kPerLoader; ++j) {
+      const int v = lu + kLoaders * j;
+      if (v < 2048) {
+        const int vv = v & 1023;
+        const int r = vv >> 4, cv = vv & 15;
+        const bf16_t* src = (v < 1024 ? qh : kh) + (size_t)(chunk * kC + r) * kDK + cv * 8;
+        dst[j] = *reinterpret_cast<const u32x4*>(src);
+      }
+    }
+    if (wave == 4) bdst = bf2f(bth[chunk * kC + lane]);
+  };
+  auto store_loads = [&](int buf, const u32x4 (&src)[kPerLoader], float bsrc) {
+#pragma unroll
+    for (int j = 0; j < kPerLoader; ++j) {
+      const int v = lu + kLoaders * j;
+      if (v < 2048) {
+        const int vv = v & 1023;
+        const int r = vv >> 4, cv = vv & 15;
+        bf16_t* dstp = (v < 1024 ? &sm.q[buf][r][cv * 8] : &sm.k[buf][r][cv * 8]);
+        *reinterpret_cast<u32x4*>(dstp) = src[j];
+      }
+    }
+    if (wave == 4) sm.beta[buf][lane] = bsrc;
+  };
+
+  // Every role below runs its own copy of the chunk loop: iteration c
+  // (c = -1 .. nch-1) has two phases, each closed by one LDS barrier, so all
+  // waves meet at the same barriers while each role keeps only its own state
+  // live.  In iteration c the chain works on chunk c, products and T on
+  // chunk c+1; every wave writes its share of chunk c+2 to LDS (loaded one
+  // iteration earlier) and issues its global loads of chunk c+3.
+  // `body(c, P, phase1, phase2)` runs one iteration with P = c & 1 known at
+  // compile time, so every buffer and register-slot index is static.
+  auto run = [&](auto phase1, auto phase2) {
+    const bool loader = wave >= 2;
+    u32x4 pf[2][kPerLoader];
+    float pfb[2] = {0.f, 0.f};
+    if (loader) {
+      issue_loads(0, pf[0], pfb[0]);
+      store_loads(0, pf[0], pfb[0]);
+      if (nch > 1) issue_loads(1, pf[1], pfb[1]);
+    }
+    lds_barrier();
+    auto body = [&](const int c, auto parity) {
+      constexpr int P = decltype(parity)::value;
+      phase1(c, parity);
+      if (loader && c + 3 < nch) issue_loads(c + 3, pf[1 - P], pfb[1 - P]);
+      lds_barrier();
+      phase2(c, parity);
+      if (loader && c + 2 < nch) store_loads(P, pf[P], pfb[P]);
+      lds_barrier();
+    };
+    for (int c = -1; c < nch; c += 2) {
+      body(c, std::integral_constant<int, 1>{});
+      if (c + 1 < nch) body(c + 1, std::integral_constant<int, 0>{});
+    }
+  };
+
+  if (wave < 2) {
+    // ======================= chain waves =======================
+    const int col = 16 * wave + lc;  // value column within the slice
+    floatx4 st[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      st[t] = zero4();
+      if (a.use_init) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[t][i] = Sh[(size_t)perm32(16 * t + 4 * lg + i) * dv + col];
+      }
+    }
+    // V of a chunk in accumulator layout, two chunks in flight
+    floatx4 vbuf[2][4];
+    auto load_v = [&](int chunk, floatx4 (&dst)[4]) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dst[mt][i] = bf2f(vh[(size_t)(chunk * kC + 16 * mt + 4 * lg + i) * dv + col]);
+    };
+    load_v(0, vbuf[0]);
+    if (nch > 1) load_v(1, vbuf[1]);
+    floatx4 xx[4], ox[4];
+    run(
+        [&](const int c, auto parity) {
+          constexpr int P = decltype(parity)::value;
+          if (c < 0) return;
+          // Y = K S and O = Q S (shared S fragments), X = beta (V - Y)
+          floatx4 y[4];
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) { y[mt] = zero4(); ox[mt] = zero4(); }
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const bf16x8 b = acc_pair_to_b(st[2 * kb], st[2 * kb + 1]);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+              y[mt] = mfma_k32(ld_frag(&sm.k[P][16 * mt + lc][32 * kb + 8 * lg]), b, y[mt]);
+              ox[mt] = mfma_k32(ld_frag(&sm.q[P][16 * mt + lc][32 * kb + 8 * lg]), b, ox[mt]);
+            }
+          }
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              xx[mt][i] = sm.beta[P][16 * mt + 4 * lg + i] * (vbuf[P][mt][i] - y[mt][i]);
+          if (c + 2 < nch) load_v(c + 2, vbuf[P]);
+        },
+        [&](const int c, auto parity) {
+          constexpr int P = decltype(parity)::value;
+          if (c < 0) return;
+          // u = T X (T lower triangular; above-diagonal tiles are zero)
+          floatx4 ut[4];
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            ut[mt] = zero4();
+#pragma unroll
+            for (int kb = 0; kb <= mt / 2; ++kb)
+              ut[mt] = mfma_k32(ld_frag(&sm.t[16 * mt + lc][32 * kb + 8 * lg]),
+                                acc_pair_to_b(xx[2 * kb], xx[2 * kb + 1]), ut[mt]);
+          }
+          const bf16x8 u01 = acc_pair_to_b(ut[0], ut[1]);
+          const bf16x8 u23 = acc_pair_to_b(ut[2], ut[3]);
+          // O += tril(Q K^T) u
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            ox[mt] = mfma_k32(ld_frag(&sm.a[P][16 * mt + lc][8 * lg]), u01, ox[mt]);
+            if (mt >= 2) ox[mt] = mfma_k32(ld_frag(&sm.a[P][16 * mt + lc][32 + 8 * lg]), u23, ox[mt]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              oh[(size_t)(c * kC + 16 * mt + 4 * lg + i) * dv + col] = f2bf(ox[mt][i]);
+          }
+          // S += K^T u
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            st[t] = mfma_k32(ld_frag(&sm.kt[P][16 * t + lc][8 * lg]), u01, st[t]);
+            st[t] = mfma_k32(ld_frag(&sm.kt[P][16 * t + lc][32 + 8 * lg]), u23, st[t]);
+          }
+        });
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Sh[(size_t)perm32(16 * t + 4 * lg + i) * dv + col] = st[t][i];
+  } else if (wave == 6) {
+    // ======================= T wave =======================
+    TCarry tc;
+    run(
+        [&](const int c, auto parity) {
+          if (c < 0) return;
+          // off-diagonal blocks of T(c) from the carried diagonal inverses
+          const floatx4 r10 = mm16(tc.l10t, tc.d0n, zero4());
+          const floatx4 t10n = neg4(mm16(tc.d1t, r10, zero4()));
+          const floatx4 t10t = neg4(mm16(r10, tc.d1t, zero4()));
+          const floatx4 r32 = mm16(tc.l32t, tc.d2n, zero4());
+          const floatx4 t32t = neg4(mm16(r32, tc.d3t, zero4()));
+          const floatx4 r20 = mm16(tc.l21t, t10n, mm16(tc.l20t, tc.d0n, zero4()));
+          const floatx4 r21 = mm16(tc.l21t, tc.d1n, zero4());
+          const floatx4 r30 = mm16(tc.l31t, t10n, mm16(tc.l30t, tc.d0n, zero4()));
+          const floatx4 r31 = mm16(tc.l31t, tc.d1n, zero4());
+          const floatx4 t20t = neg4(mm16(r20, tc.d2t, zero4()));
+          const floatx4 t21t = neg4(mm16(r21, tc.d2t, zero4()));
+          const floatx4 t30t = neg4(mm16(r30, tc.d3t, mm16(r20, t32t, zero4())));
+          const floatx4 t31t = neg4(mm16(r31, tc.d3t, mm16(r21, t32t, zero4())));
+          // T row-major with token columns permuted: a transposed tile gives
+          // row 16i + lc, columns 16j + 4lg .. +3, contiguous after the permutation
+          auto put = [&](int i, int j, floatx4 xt) {
+            uint2 wv;
+            wv.x = pack2(xt[0], xt[1]);
+            wv.y = pack2(xt[2], xt[3]);
+            *reinterpret_cast<uint2*>(&sm.t[16 * i + lc][perm32(16 * j + 4 * lg)]) = wv;
+          };
+          put(0, 0, tc.d0t); put(1, 1, tc.d1t); put(2, 2, tc.d2t); put(3, 3, tc.d3t);
+          put(1, 0, t10t); put(3, 2, t32t);
+          put(2, 0, t20t); put(2, 1, t21t); put(3, 0, t30t); put(3, 1, t31t);
+        },
+        [&](const int c, auto parity) {
+          if (c + 1 >= nch) return;
+          // diagonal 16x16 blocks of T(c+1): lane (block lg, column lc) solves
+          // (I + L_bb) t = e_lc by forward substitution in fp32
+          const int b0 = 16 * lg;
+          float tv[16];
+#pragma unroll
+          for (int m = 0; m < 16; ++m) tv[m] = m == lc ? 1.f : 0.f;
+#pragma unroll
+          for (int i = 1; i < 16; ++i) {
+            float s = 0.f;
+#pragma unroll
+            for (int m4 = 0; m4 < i; m4 += 4) {
+              const float4 lr = *reinterpret_cast<const float4*>(&sm.l[b0 + i][b0 + m4]);
+              s += lr.x * tv[m4];
+              if (m4 + 1 < i) s += lr.y * tv[m4 + 1];
+              if (m4 + 2 < i) s += lr.z * tv[m4 + 2];
+              if (m4 + 3 < i) s += lr.w * tv[m4 + 3];
+            }
+            if (i > lc) tv[i] = -s;
+          }
+          // D_b (lower triangular, unit diagonal) over L's diagonal block; the
+          // reads below see these writes (one wave, LDS in program order)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sm.l[b0 + i][b0 + lc] = tv[i];
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+          // accumulator-layout copies for the merges: "n" holds X[4lg+r][lc],
+          // "t" holds X[lc][4lg+r] (the transpose)
+          auto accn = [&](int r0, int c0) {
+            floatx4 x;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] = sm.l[r0 + 4 * lg + r][c0 + lc];
+            return x;
+          };
+          auto acct = [&](int r0, int c0) {
+            const float4 v = *reinterpret_cast<const float4*>(&sm.l[r0 + lc][c0 + 4 * lg]);
+            return floatx4{v.x, v.y, v.z, v.w};
+          };
+          tc.d0n = accn(0, 0); tc.d1n = accn(16, 16); tc.d2n = accn(32, 32);
+          tc.d0t = acct(0, 0); tc.d1t = acct(16, 16); tc.d2t = acct(32, 32); tc.d3t = acct(48, 48);
+          tc.l10t = acct(16, 0); tc.l32t = acct(48, 32); tc.l20t = acct(32, 0);
+          tc.l21t = acct(32, 16); tc.l30t = acct(48, 0); tc.l31t = acct(48, 16);
+        });
+  } else if (wave == 2 || wave == 3 || wave == 7) {
+    // ======================= product waves =======================
+    int i0, i1;
+    prod_rows(wave, i0, i1);
+    run(
+        [&](const int c, auto parity) {
+          constexpr int nb = 1 - decltype(parity)::value;  // buffer of chunk c+1
+          if (c + 1 >= nch) return;
+          // K K^T of chunk c+1 -> L = diag(beta) (.) strictly below the diagonal
+          for (int i = i0; i <= i1; ++i) {
+            floatx4 acc[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+              const bf16x8 af = ld_frag(&sm.k[nb][16 * i + lc][32 * kb + 8 * lg]);
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                if (j <= i) acc[j] = mfma_k32(af, ld_frag(&sm.k[nb][16 * j + lc][32 * kb + 8 * lg]), acc[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              if (j > i) continue;
+#pragma unroll
+              for (int ii = 0; ii < 4; ++ii) {
+                const int r = 16 * i + 4 * lg + ii, cc = 16 * j + lc;
+                if (cc < r) sm.l[r][cc] = sm.beta[nb][r] * acc[j][ii];
+              }
+            }
+          }
+        },
+        [&](const int c, auto parity) {
+          constexpr int nb = 1 - decltype(parity)::value;
+          if (c + 1 >= nch) return;
+          // tril(Q K^T) of chunk c+1, token columns permuted
+          for (int i = i0; i <= i1; ++i) {
+            floatx4 acc[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+              const bf16x8 af = ld_frag(&sm.q[nb][16 * i + lc][32 * kb + 8 * lg]);
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                if (j <= i) acc[j] = mfma_k32(af, ld_frag(&sm.k[nb][16 * j + lc][32 * kb + 8 * lg]), acc[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              if (j > i) continue;
+#pragma unroll
+              for (int ii = 0; ii < 4; ++ii) {
+                const int r = 16 * i + 4 * lg + ii, cc = 16 * j + lc;
+                sm.a[nb][r][perm32(cc)] = f2bf(cc <= r ? acc[j][ii] : 0.f);
+              }
+            }
+          }
+        });
+  } else {
+    // ======================= K^T waves (4, 5) =======================
+    // K^T of chunk c+1 with key channels in chain-row order (row rho holds
+    // channel perm32(rho)) and token columns permuted
+    const int sw = tid - 256;  // 0..127
+    const int p = sw & 31;     // token pair
+    const int cvo = sw >> 5;   // 0..3
+    run([&](const int c, auto parity) {},
+        [&](const int c, auto parity) {
+          constexpr int nb = 1 - decltype(parity)::value;
+          if (c + 1 >= nch) return;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int cv = cvo + 4 * jj;  // group of 8 key channels
+            const u32x4 r0 = *reinterpret_cast<const u32x4*>(&sm.k[nb][2 * p][cv * 8]);
+            const u32x4 r1 = *reinterpret_cast<const u32x4*>(&sm.k[nb][2 * p + 1][cv * 8]);
+            const int pos = perm32(2 * p);  // even: the token pair is one aligned word
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t lo = (r0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+              const uint32_t hi = (r1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+              *reinterpret_cast<uint32_t*>(&sm.kt[nb][perm32_inv(cv * 8 + e)][pos]) = lo | (hi << 16);
+            }
+          }
+        });
+  }
+}
+
+hipError_t launch_prefill_pipe(const PrefillArgs& a, hipStream_t st) {
+  const long blocks = (long)a.B * a.H * (a.dv / kDVS);
+  hipLaunchKernelGGL(prefill_delta_pipe, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace linattn
