@@ -46,18 +46,28 @@ constexpr int kDVS = 32;
 constexpr int kThreads = 512;
 
 constexpr int kLQ = kDK + 8;  // bf16 row stride of q, k (16-byte aligned, conflict-free)
-constexpr int kLT = kC + 8;   // bf16 row stride of K^T, tril(QK^T), T
+constexpr int kLT = kC + 8;   // bf16 row stride of tril(QK^T), T, V^T
 constexpr int kLL = kC + 4;   // fp32 row stride of L / D
+constexpr int kLO = kDVS + 8; // bf16 row stride of the output tile
 
 struct __attribute__((aligned(16))) Smem {
   bf16_t q[2][kC][kLQ];
   bf16_t k[2][kC][kLQ];
-  bf16_t kt[2][kDK][kLT];
+  bf16_t kt[2][kDK][kC];   // unpadded; 16-byte groups XOR-swizzled (kt_col)
   bf16_t a[2][kC][kLT];
   bf16_t t[kC][kLT];
+  bf16_t vt[2][kDVS][kLT]; // V^T of the slice
+  bf16_t o[kC][kLO];       // output tile of one chunk
   float l[kC][kLL];
   float beta[2][kC];
 };
+
+// Column of K^T row `row` holding (permuted) token position `pos`: the eight
+// 16-byte groups of a 64-token row are XOR-swizzled so that the 16 rows a
+// fragment read touches fall in distinct banks.
+__device__ __forceinline__ int kt_col(int row, int pos) {
+  return (((pos >> 3) ^ ((row >> 1) & 7)) << 3) | (pos & 7);
+}
 
 // 32b + 16h + 4g + i  ->  32b + 8g + 4h + i
 __device__ __forceinline__ int perm32(int x) {
@@ -101,15 +111,6 @@ struct TCarry {
   floatx4 l10t, l32t, l20t, l21t, l30t, l31t;
 };
 
-// Product tile lists: row block i with column blocks j <= i.
-__device__ __forceinline__ int prod_rows(int wave, int& i0, int& i1) {
-  // wave 2: row 3 (4 tiles); wave 3: row 2 (3 tiles); wave 7: rows 0, 1 (3 tiles)
-  if (wave == 2) { i0 = 3; i1 = 3; }
-  else if (wave == 3) { i0 = 2; i1 = 2; }
-  else { i0 = 0; i1 = 1; }
-  return 0;
-}
-
 }  // namespace
 
 __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
@@ -143,23 +144,26 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
     for (int i = tid; i < (int)(sizeof(sm.t) / 4); i += kThreads) zt[i] = 0u;
   }
 
-  // ---- register prefetch of q and k by waves 2..7 (the chain waves keep
-  // their registers for the state): thread u = tid - 128 owns the 16-byte
-  // vectors u + 384 j of a chunk (vectors 0..1023 are q, 1024..2047 k);
-  // beta is loaded by wave 4.
+  // ---- register prefetch by waves 2..7 (the chain waves keep their
+  // registers for the state).  A chunk is 2304 16-byte vectors: 0..1023 q,
+  // 1024..2047 k, 2048..2303 the 64 x 32 slice of v; loader thread
+  // u = tid - 128 owns vectors u + 384 j.  beta is loaded by wave 4.
   constexpr int kLoaders = kThreads - 128;
-  constexpr int kPerLoader = (2048 + kLoaders - 1) / kLoaders;  // 6
+  constexpr int kPerLoader = 2304 / kLoaders;  // 6
   const int lu = tid - 128;
   auto issue_loads = [&](int chunk, u32x4 (&dst)[kPerLoader], float& bdst) {
 #pragma unroll
     for (int j = 0; j < kPerLoader; ++j) {
       const int v = lu + kLoaders * j;
+      const bf16_t* src;
       if (v < 2048) {
         const int vv = v & 1023;
-        const int r = vv >> 4, cv = vv & 15;
-        const bf16_t* src = (v < 1024 ? qh : kh) + (size_t)(chunk * kC + r) * kDK + cv * 8;
-        dst[j] = *reinterpret_cast<const u32x4*>(src);
+        src = (v < 1024 ? qh : kh) + (size_t)(chunk * kC + (vv >> 4)) * kDK + (vv & 15) * 8;
+      } else {
+        const int vv = v - 2048;
+        src = vh + (size_t)(chunk * kC + (vv >> 2)) * dv + (vv & 3) * 8;
       }
+      dst[j] = *reinterpret_cast<const u32x4*>(src);
     }
     if (wave == 4) bdst = bf2f(bth[chunk * kC + lane]);
   };
@@ -169,9 +173,14 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
       const int v = lu + kLoaders * j;
       if (v < 2048) {
         const int vv = v & 1023;
-        const int r = vv >> 4, cv = vv & 15;
-        bf16_t* dstp = (v < 1024 ? &sm.q[buf][r][cv * 8] : &sm.k[buf][r][cv * 8]);
+        bf16_t* dstp = (v < 1024 ? &sm.q[buf][vv >> 4][(vv & 15) * 8] : &sm.k[buf][vv >> 4][(vv & 15) * 8]);
         *reinterpret_cast<u32x4*>(dstp) = src[j];
+      } else {
+        const int vv = v - 2048;
+        const int r = vv >> 2, c0 = (vv & 3) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          sm.vt[buf][c0 + e][r] = (bf16_t)((src[j][e >> 1] >> (16 * (e & 1))) & 0xffffu);
       }
     }
     if (wave == 4) sm.beta[buf][lane] = bsrc;
@@ -222,72 +231,94 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
         for (int i = 0; i < 4; ++i) st[t][i] = Sh[(size_t)perm32(16 * t + 4 * lg + i) * dv + col];
       }
     }
-    // V of a chunk in accumulator layout, two chunks in flight
-    floatx4 vbuf[2][4];
-    auto load_v = [&](int chunk, floatx4 (&dst)[4]) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          dst[mt][i] = bf2f(vh[(size_t)(chunk * kC + 16 * mt + 4 * lg + i) * dv + col]);
-    };
-    load_v(0, vbuf[0]);
-    if (nch > 1) load_v(1, vbuf[1]);
     floatx4 xx[4], ox[4];
     run(
         [&](const int c, auto parity) {
           constexpr int P = decltype(parity)::value;
           if (c < 0) return;
-          // Y = K S and O = Q S (shared S fragments), X = beta (V - Y)
+          // Y = K S and O = Q S (shared S fragments), X = beta (V - Y).
+          // The fragments of k-step kb+1 are loaded while kb computes.
           floatx4 y[4];
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) { y[mt] = zero4(); ox[mt] = zero4(); }
+          bf16x8 fk[2][4], fq[2][4];
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            fk[0][mt] = ld_frag(&sm.k[P][16 * mt + lc][8 * lg]);
+            fq[0][mt] = ld_frag(&sm.q[P][16 * mt + lc][8 * lg]);
+          }
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
+            if (kb < 3) {
+#pragma unroll
+              for (int mt = 0; mt < 4; ++mt) {
+                fk[(kb + 1) & 1][mt] = ld_frag(&sm.k[P][16 * mt + lc][32 * (kb + 1) + 8 * lg]);
+                fq[(kb + 1) & 1][mt] = ld_frag(&sm.q[P][16 * mt + lc][32 * (kb + 1) + 8 * lg]);
+              }
+            }
             const bf16x8 b = acc_pair_to_b(st[2 * kb], st[2 * kb + 1]);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-              y[mt] = mfma_k32(ld_frag(&sm.k[P][16 * mt + lc][32 * kb + 8 * lg]), b, y[mt]);
-              ox[mt] = mfma_k32(ld_frag(&sm.q[P][16 * mt + lc][32 * kb + 8 * lg]), b, ox[mt]);
+              y[mt] = mfma_k32(fk[kb & 1][mt], b, y[mt]);
+              ox[mt] = mfma_k32(fq[kb & 1][mt], b, ox[mt]);
             }
           }
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              xx[mt][i] = sm.beta[P][16 * mt + 4 * lg + i] * (vbuf[P][mt][i] - y[mt][i]);
-          if (c + 2 < nch) load_v(c + 2, vbuf[P]);
+          for (int mt = 0; mt < 4; ++mt) {
+            const uint2 vw = *reinterpret_cast<const uint2*>(&sm.vt[P][col][16 * mt + 4 * lg]);
+            const float4 bt = *reinterpret_cast<const float4*>(&sm.beta[P][16 * mt + 4 * lg]);
+            xx[mt][0] = bt.x * (__uint_as_float(vw.x << 16) - y[mt][0]);
+            xx[mt][1] = bt.y * (__uint_as_float(vw.x & 0xffff0000u) - y[mt][1]);
+            xx[mt][2] = bt.z * (__uint_as_float(vw.y << 16) - y[mt][2]);
+            xx[mt][3] = bt.w * (__uint_as_float(vw.y & 0xffff0000u) - y[mt][3]);
+          }
         },
         [&](const int c, auto parity) {
           constexpr int P = decltype(parity)::value;
           if (c < 0) return;
-          // u = T X (T lower triangular; above-diagonal tiles are zero)
+          // u = T X (T lower triangular; above-diagonal tiles are zero).
+          // All T and tril(QK^T) fragments are requested up front.
+          bf16x8 ft[6], fa[6];
+          ft[0] = ld_frag(&sm.t[lc][8 * lg]);
+          ft[1] = ld_frag(&sm.t[16 + lc][8 * lg]);
+          ft[2] = ld_frag(&sm.t[32 + lc][8 * lg]);
+          ft[3] = ld_frag(&sm.t[32 + lc][32 + 8 * lg]);
+          ft[4] = ld_frag(&sm.t[48 + lc][8 * lg]);
+          ft[5] = ld_frag(&sm.t[48 + lc][32 + 8 * lg]);
+          fa[0] = ld_frag(&sm.a[P][lc][8 * lg]);
+          fa[1] = ld_frag(&sm.a[P][16 + lc][8 * lg]);
+          fa[2] = ld_frag(&sm.a[P][32 + lc][8 * lg]);
+          fa[3] = ld_frag(&sm.a[P][32 + lc][32 + 8 * lg]);
+          fa[4] = ld_frag(&sm.a[P][48 + lc][8 * lg]);
+          fa[5] = ld_frag(&sm.a[P][48 + lc][32 + 8 * lg]);
+          const bf16x8 x01 = acc_pair_to_b(xx[0], xx[1]);
+          const bf16x8 x23 = acc_pair_to_b(xx[2], xx[3]);
           floatx4 ut[4];
+          ut[0] = mfma_k32(ft[0], x01, zero4());
+          ut[1] = mfma_k32(ft[1], x01, zero4());
+          ut[2] = mfma_k32(ft[3], x23, mfma_k32(ft[2], x01, zero4()));
+          ut[3] = mfma_k32(ft[5], x23, mfma_k32(ft[4], x01, zero4()));
+          bf16x8 fkt[2][8];
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
-            ut[mt] = zero4();
-#pragma unroll
-            for (int kb = 0; kb <= mt / 2; ++kb)
-              ut[mt] = mfma_k32(ld_frag(&sm.t[16 * mt + lc][32 * kb + 8 * lg]),
-                                acc_pair_to_b(xx[2 * kb], xx[2 * kb + 1]), ut[mt]);
-          }
+          for (int t = 0; t < 8; ++t) fkt[0][t] = ld_frag(&sm.kt[P][16 * t + lc][kt_col(16 * t + lc, 8 * lg)]);
           const bf16x8 u01 = acc_pair_to_b(ut[0], ut[1]);
           const bf16x8 u23 = acc_pair_to_b(ut[2], ut[3]);
           // O += tril(Q K^T) u
+          ox[0] = mfma_k32(fa[0], u01, ox[0]);
+          ox[1] = mfma_k32(fa[1], u01, ox[1]);
+          ox[2] = mfma_k32(fa[3], u23, mfma_k32(fa[2], u01, ox[2]));
+          ox[3] = mfma_k32(fa[5], u23, mfma_k32(fa[4], u01, ox[3]));
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
-            ox[mt] = mfma_k32(ld_frag(&sm.a[P][16 * mt + lc][8 * lg]), u01, ox[mt]);
-            if (mt >= 2) ox[mt] = mfma_k32(ld_frag(&sm.a[P][16 * mt + lc][32 + 8 * lg]), u23, ox[mt]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              oh[(size_t)(c * kC + 16 * mt + 4 * lg + i) * dv + col] = f2bf(ox[mt][i]);
-          }
+          for (int t = 0; t < 8; ++t) fkt[1][t] = ld_frag(&sm.kt[P][16 * t + lc][kt_col(16 * t + lc, 32 + 8 * lg)]);
           // S += K^T u
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            st[t] = mfma_k32(ld_frag(&sm.kt[P][16 * t + lc][8 * lg]), u01, st[t]);
-            st[t] = mfma_k32(ld_frag(&sm.kt[P][16 * t + lc][32 + 8 * lg]), u23, st[t]);
-          }
+          for (int t = 0; t < 8; ++t) st[t] = mfma_k32(fkt[0][t], u01, st[t]);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) st[t] = mfma_k32(fkt[1][t], u23, st[t]);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.o[16 * mt + 4 * lg + i][col] = f2bf(ox[mt][i]);
         });
 #pragma unroll
     for (int t = 0; t < 8; ++t)
@@ -330,21 +361,26 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
           // diagonal 16x16 blocks of T(c+1): lane (block lg, column lc) solves
           // (I + L_bb) t = e_lc by forward substitution in fp32
           const int b0 = 16 * lg;
+          float4 lr[16][4];  // strictly-lower rows of L_bb, requested up front
+#pragma unroll
+          for (int i = 1; i < 16; ++i)
+#pragma unroll
+            for (int m4 = 0; m4 < i; m4 += 4)
+              lr[i][m4 >> 2] = *reinterpret_cast<const float4*>(&sm.l[b0 + i][b0 + m4]);
           float tv[16];
 #pragma unroll
           for (int m = 0; m < 16; ++m) tv[m] = m == lc ? 1.f : 0.f;
 #pragma unroll
           for (int i = 1; i < 16; ++i) {
-            float s = 0.f;
+            float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-            for (int m4 = 0; m4 < i; m4 += 4) {
-              const float4 lr = *reinterpret_cast<const float4*>(&sm.l[b0 + i][b0 + m4]);
-              s += lr.x * tv[m4];
-              if (m4 + 1 < i) s += lr.y * tv[m4 + 1];
-              if (m4 + 2 < i) s += lr.z * tv[m4 + 2];
-              if (m4 + 3 < i) s += lr.w * tv[m4 + 3];
+            for (int m = 0; m < i; ++m) {
+              const float4 q4 = lr[i][m >> 2];
+              const float lv = (m & 3) == 0 ? q4.x : (m & 3) == 1 ? q4.y : (m & 3) == 2 ? q4.z : q4.w;
+              if (m & 1) s1 += lv * tv[m];
+              else s0 += lv * tv[m];
             }
-            if (i > lc) tv[i] = -s;
+            if (i > lc) tv[i] = -(s0 + s1);
           }
           // D_b (lower triangular, unit diagonal) over L's diagonal block; the
           // reads below see these writes (one wave, LDS in program order)
@@ -372,61 +408,73 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
         });
   } else if (wave == 2 || wave == 3 || wave == 7) {
     // ======================= product waves =======================
-    int i0, i1;
-    prod_rows(wave, i0, i1);
-    run(
-        [&](const int c, auto parity) {
-          constexpr int nb = 1 - decltype(parity)::value;  // buffer of chunk c+1
-          if (c + 1 >= nch) return;
-          // K K^T of chunk c+1 -> L = diag(beta) (.) strictly below the diagonal
-          for (int i = i0; i <= i1; ++i) {
-            floatx4 acc[4];
+    // Row blocks I0..I1 of K K^T (phase 1) and tril(Q K^T) (phase 2) of
+    // chunk c+1, tile lists fixed at compile time: wave 2 row 3, wave 3
+    // row 2, wave 7 rows 0 and 1.  All fragments of a row block are
+    // requested before its MFMAs.
+    auto prod = [&](auto i0c, auto i1c) {
+      constexpr int I0 = decltype(i0c)::value, I1 = decltype(i1c)::value;
+      run(
+          [&](const int c, auto parity) {
+            constexpr int nb = 1 - decltype(parity)::value;  // buffer of chunk c+1
+            if (c + 1 >= nch) return;
+            // K K^T -> L = diag(beta) (.) strictly below the diagonal
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j] = zero4();
+            for (int i = I0; i <= I1; ++i) {
+              bf16x8 fb[4][4];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-              const bf16x8 af = ld_frag(&sm.k[nb][16 * i + lc][32 * kb + 8 * lg]);
+              for (int j = 0; j <= i; ++j)
 #pragma unroll
-              for (int j = 0; j < 4; ++j)
-                if (j <= i) acc[j] = mfma_k32(af, ld_frag(&sm.k[nb][16 * j + lc][32 * kb + 8 * lg]), acc[j]);
-            }
+                for (int kb = 0; kb < 4; ++kb) fb[j][kb] = ld_frag(&sm.k[nb][16 * j + lc][32 * kb + 8 * lg]);
+              floatx4 acc[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              if (j > i) continue;
+              for (int j = 0; j <= i; ++j) {
+                acc[j] = zero4();
 #pragma unroll
-              for (int ii = 0; ii < 4; ++ii) {
-                const int r = 16 * i + 4 * lg + ii, cc = 16 * j + lc;
-                if (cc < r) sm.l[r][cc] = sm.beta[nb][r] * acc[j][ii];
+                for (int kb = 0; kb < 4; ++kb) acc[j] = mfma_k32(fb[i][kb], fb[j][kb], acc[j]);
               }
+#pragma unroll
+              for (int j = 0; j <= i; ++j)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                  const int r = 16 * i + 4 * lg + ii, cc = 16 * j + lc;
+                  if (cc < r) sm.l[r][cc] = sm.beta[nb][r] * acc[j][ii];
+                }
             }
-          }
-        },
-        [&](const int c, auto parity) {
-          constexpr int nb = 1 - decltype(parity)::value;
-          if (c + 1 >= nch) return;
-          // tril(Q K^T) of chunk c+1, token columns permuted
-          for (int i = i0; i <= i1; ++i) {
-            floatx4 acc[4];
+          },
+          [&](const int c, auto parity) {
+            constexpr int nb = 1 - decltype(parity)::value;
+            if (c + 1 >= nch) return;
+            // tril(Q K^T), token columns permuted
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j] = zero4();
+            for (int i = I0; i <= I1; ++i) {
+              bf16x8 fq[4], fb[4][4];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-              const bf16x8 af = ld_frag(&sm.q[nb][16 * i + lc][32 * kb + 8 * lg]);
+              for (int kb = 0; kb < 4; ++kb) fq[kb] = ld_frag(&sm.q[nb][16 * i + lc][32 * kb + 8 * lg]);
 #pragma unroll
-              for (int j = 0; j < 4; ++j)
-                if (j <= i) acc[j] = mfma_k32(af, ld_frag(&sm.k[nb][16 * j + lc][32 * kb + 8 * lg]), acc[j]);
-            }
+              for (int j = 0; j <= i; ++j)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              if (j > i) continue;
+                for (int kb = 0; kb < 4; ++kb) fb[j][kb] = ld_frag(&sm.k[nb][16 * j + lc][32 * kb + 8 * lg]);
+              floatx4 acc[4];
 #pragma unroll
-              for (int ii = 0; ii < 4; ++ii) {
-                const int r = 16 * i + 4 * lg + ii, cc = 16 * j + lc;
-                sm.a[nb][r][perm32(cc)] = f2bf(cc <= r ? acc[j][ii] : 0.f);
+              for (int j = 0; j <= i; ++j) {
+                acc[j] = zero4();
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) acc[j] = mfma_k32(fq[kb], fb[j][kb], acc[j]);
               }
+#pragma unroll
+              for (int j = 0; j <= i; ++j)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                  const int r = 16 * i + 4 * lg + ii, cc = 16 * j + lc;
+                  sm.a[nb][r][perm32(cc)] = f2bf(cc <= r ? acc[j][ii] : 0.f);
+                }
             }
-          }
-        });
+          });
+    };
+    if (wave == 2) prod(std::integral_constant<int, 3>{}, std::integral_constant<int, 3>{});
+    else if (wave == 3) prod(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
+    else prod(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
   } else {
     // ======================= K^T waves (4, 5) =======================
     // K^T of chunk c+1 with key channels in chain-row order (row rho holds
@@ -434,7 +482,20 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
     const int sw = tid - 256;  // 0..127
     const int p = sw & 31;     // token pair
     const int cvo = sw >> 5;   // 0..3
-    run([&](const int c, auto parity) {},
+    // They also write the output tile of chunk c-1 (left in LDS by the
+    // chain waves) to memory with 16-byte stores.
+    auto store_o = [&](int chunk) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int v = sw + 128 * j;
+        const int r = v >> 2, c8 = (v & 3) * 8;
+        *reinterpret_cast<u32x4*>(oh + (size_t)(chunk * kC + r) * dv + c8) =
+            *reinterpret_cast<const u32x4*>(&sm.o[r][c8]);
+      }
+    };
+    run([&](const int c, auto parity) {
+          if (c >= 1) store_o(c - 1);
+        },
         [&](const int c, auto parity) {
           constexpr int nb = 1 - decltype(parity)::value;
           if (c + 1 >= nch) return;
@@ -448,10 +509,12 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
             for (int e = 0; e < 8; ++e) {
               const uint32_t lo = (r0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
               const uint32_t hi = (r1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-              *reinterpret_cast<uint32_t*>(&sm.kt[nb][perm32_inv(cv * 8 + e)][pos]) = lo | (hi << 16);
+              const int row = perm32_inv(cv * 8 + e);
+              *reinterpret_cast<uint32_t*>(&sm.kt[nb][row][kt_col(row, pos)]) = lo | (hi << 16);
             }
           }
         });
+    store_o(nch - 1);
   }
 }
 
