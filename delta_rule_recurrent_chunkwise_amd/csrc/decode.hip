@@ -23,23 +23,49 @@
 
 namespace linattn {
 
-template <int DK, int DV>
+// RPTT: target rows per thread.  Fewer rows per thread means more threads
+// per head and fewer bytes per thread in flight between the load and the
+// store of the state, which streams better.
+template <int DK, int DV, int RPTT>
 struct DecodeShape {
-  static constexpr int CQ = DV / 4;               // float4 column groups
-  static constexpr int RPT = DK < 16 ? DK : 16;  // rows per thread
-  static constexpr int RG = DK / RPT;             // row groups
-  static constexpr int TPH = CQ * RG;             // threads per head
-  static constexpr int HPB = 256 / TPH;           // heads per block
-  static_assert(TPH <= 256 && 256 % TPH == 0, "bad decode shape");
+  static constexpr int CQ = DV / 4;                    // float4 column groups
+  static constexpr int RPT = DK < RPTT ? DK : RPTT;    // rows per thread
+  static constexpr int RG = DK / RPT;                  // row groups
+  static constexpr int TPH = CQ * RG;                  // threads per head
+  static constexpr int NTB = TPH > 256 ? TPH : 256;    // threads per block
+  static constexpr int HPB = NTB / TPH;                // heads per block
+  static_assert(TPH <= 1024 && NTB % TPH == 0, "bad decode shape");
 };
+
+template <bool NT>
+__device__ __forceinline__ float4 ld_state(const float4* p) {
+  if constexpr (NT) {
+    typedef float fx4 __attribute__((ext_vector_type(4)));
+    const fx4 v = __builtin_nontemporal_load(reinterpret_cast<const fx4*>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    return *p;
+  }
+}
+template <bool NT>
+__device__ __forceinline__ void st_state(float4* p, float4 x) {
+  if constexpr (NT) {
+    typedef float fx4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(fx4{x.x, x.y, x.z, x.w}, reinterpret_cast<fx4*>(p));
+  } else {
+    *p = x;
+  }
+}
 
 __device__ __forceinline__ float elu_plus_one(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
-template <int DK, int DV, class E, int KIND>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
-  typedef DecodeShape<DK, DV> Sh;
+template <int DK, int DV, class E, int KIND, int RPTT, bool NT, int WPE>
+__global__ __launch_bounds__((DecodeShape<DK, DV, RPTT>::NTB))
+__attribute__((amdgpu_waves_per_eu(WPE))) void decode_kernel(DecodeArgs a) {
+  typedef DecodeShape<DK, DV, RPTT> Sh;
   typedef typename E::T T;
   constexpr int CQ = Sh::CQ, RPT = Sh::RPT, RG = Sh::RG, TPH = Sh::TPH, HPB = Sh::HPB;
+  constexpr int NTB = Sh::NTB;
 
   __shared__ float s_q[HPB][DK];
   __shared__ float s_k[HPB][DK];
@@ -48,6 +74,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   __shared__ float4 s_red0[HPB][RG][CQ];
   __shared__ float4 s_red1[HPB][RG][CQ];
   __shared__ float2 s_red2[HPB][RG][CQ];
+  __shared__ float4 s_u[HPB][CQ];
 
   const int hb = threadIdx.x / TPH;
   const int tl = threadIdx.x % TPH;
@@ -63,13 +90,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   float4 s[RPT];
 #pragma unroll
   for (int j = 0; j < RPT; ++j) {
-    s[j] = active ? S4[(rg + RG * j) * CQ + cq] : make_float4(0.f, 0.f, 0.f, 0.f);
+    s[j] = ld_state<NT>(&S4[(rg + RG * j) * CQ + cq]);  // hc is clamped: always in bounds
   }
 
   // Stage this block's per-row vectors (q, k, decay, z) in LDS as fp32.
   const T* qg = reinterpret_cast<const T*>(a.q);
   const T* kg = reinterpret_cast<const T*>(a.k);
-  for (int i = threadIdx.x; i < HPB * DK; i += 256) {
+  for (int i = threadIdx.x; i < HPB * DK; i += NTB) {
     const int h = i / DK, d = i % DK;
     const long hh = (long)blockIdx.x * HPB + h;
     float qv = 0.f, kv = 0.f;
@@ -114,56 +141,65 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       if (KIND == DEC_LA) sz += qr * s_z[hb][row];
     }
   }
-  if (RG > 1) {
-    s_red0[hb][rg][cq] = r4;
-    s_red1[hb][rg][cq] = s4;
-    s_red2[hb][rg][cq] = make_float2(sc, sz);
-    __syncthreads();
+  // Cross-row-group reduction: every thread posts its partial sums; the
+  // threads of row group 0 add them up, form u and o, and hand u back to the
+  // other row groups through LDS.
+  s_red0[hb][rg][cq] = r4;
+  s_red1[hb][rg][cq] = s4;
+  s_red2[hb][rg][cq] = make_float2(sc, sz);
+  __syncthreads();
+  float4 u4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (rg == 0) {
     r4 = make_float4(0.f, 0.f, 0.f, 0.f);
     s4 = make_float4(0.f, 0.f, 0.f, 0.f);
     sc = 0.f;
     sz = 0.f;
-#pragma unroll
+#pragma unroll 4
     for (int i = 0; i < RG; ++i) {
       const float4 x = s_red0[hb][i][cq];
       const float4 y = s_red1[hb][i][cq];
+      const float2 w = s_red2[hb][i][0];  // scalar sums live in the cq == 0 threads
       r4.x += x.x; r4.y += x.y; r4.z += x.z; r4.w += x.w;
       s4.x += y.x; s4.y += y.y; s4.z += y.z; s4.w += y.w;
-      sc += s_red2[hb][i][0].x;
-      sz += s_red2[hb][i][0].y;
+      sc += w.x;
+      sz += w.y;
     }
-  } else {
-    // a single row group: every thread of the head already holds the full
-    // column sums; the scalar sum lives in the cq == 0 thread.
-    s_red2[hb][0][cq] = make_float2(sc, sz);
+    if (active) {
+      const T* vg = reinterpret_cast<const T*>(a.v) + hc * DV + 4 * cq;
+      const float4 v4 = make_float4(E::ld(vg), E::ld(vg + 1), E::ld(vg + 2), E::ld(vg + 3));
+      float4 o4;
+      if (KIND == DEC_LA) {
+        u4 = v4;
+        const float inv = 1.f / (sz + sc);
+        o4 = make_float4((s4.x + sc * v4.x) * inv, (s4.y + sc * v4.y) * inv,
+                         (s4.z + sc * v4.z) * inv, (s4.w + sc * v4.w) * inv);
+      } else {
+        const float b = E::ld(reinterpret_cast<const T*>(a.beta) + hc);
+        u4 = make_float4(b * (v4.x - r4.x), b * (v4.y - r4.y), b * (v4.z - r4.z),
+                         b * (v4.w - r4.w));
+        o4 = make_float4(s4.x + sc * u4.x, s4.y + sc * u4.y, s4.z + sc * u4.z,
+                         s4.w + sc * u4.w);
+      }
+      T* og = reinterpret_cast<T*>(a.o) + hc * DV + 4 * cq;
+      og[0] = E::cvt(o4.x);
+      og[1] = E::cvt(o4.y);
+      og[2] = E::cvt(o4.z);
+      og[3] = E::cvt(o4.w);
+      if (RG > 1) s_u[hb][cq] = u4;
+    }
+  }
+  if (RG > 1) {
     __syncthreads();
-    sc = s_red2[hb][0][0].x;
-    sz = s_red2[hb][0][0].y;
+    u4 = s_u[hb][cq];
   }
   if (!active) return;
-
-  const T* vg = reinterpret_cast<const T*>(a.v) + hc * DV + 4 * cq;
-  const float4 v4 = make_float4(E::ld(vg), E::ld(vg + 1), E::ld(vg + 2), E::ld(vg + 3));
-  float4 u4, o4;
-  if (KIND == DEC_LA) {
-    u4 = v4;
-    const float inv = 1.f / (sz + sc);
-    o4 = make_float4((s4.x + sc * v4.x) * inv, (s4.y + sc * v4.y) * inv,
-                     (s4.z + sc * v4.z) * inv, (s4.w + sc * v4.w) * inv);
-  } else {
-    const float b = E::ld(reinterpret_cast<const T*>(a.beta) + hc);
-    u4 = make_float4(b * (v4.x - r4.x), b * (v4.y - r4.y), b * (v4.z - r4.z),
-                     b * (v4.w - r4.w));
-    o4 = make_float4(s4.x + sc * u4.x, s4.y + sc * u4.y, s4.z + sc * u4.z,
-                     s4.w + sc * u4.w);
-  }
 
 #pragma unroll
   for (int j = 0; j < RPT; ++j) {
     const int row = rg + RG * j;
     const float kr = s_k[hb][row];
     s[j].x += kr * u4.x; s[j].y += kr * u4.y; s[j].z += kr * u4.z; s[j].w += kr * u4.w;
-    S4[row * CQ + cq] = s[j];
+    st_state<NT>(&S4[row * CQ + cq], s[j]);
   }
   if (KIND == DEC_LA && cq == 0) {
 #pragma unroll
@@ -172,20 +208,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       a.z[hc * DK + row] = s_z[hb][row] + s_k[hb][row];
     }
   }
-  if (rg == 0) {
-    T* og = reinterpret_cast<T*>(a.o) + hc * DV + 4 * cq;
-    og[0] = E::cvt(o4.x);
-    og[1] = E::cvt(o4.y);
-    og[2] = E::cvt(o4.z);
-    og[3] = E::cvt(o4.w);
-  }
 }
 
-template <int DK, int DV, class E, int KIND>
+template <int DK, int DV, class E, int KIND, int RPTT = 4, bool NT = true, int WPE = 8>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
-  typedef DecodeShape<DK, DV> Sh;
+  typedef DecodeShape<DK, DV, RPTT> Sh;
   const int blocks = (a.nheads + Sh::HPB - 1) / Sh::HPB;
-  hipLaunchKernelGGL((decode_kernel<DK, DV, E, KIND>), dim3(blocks), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((decode_kernel<DK, DV, E, KIND, RPTT, NT, WPE>), dim3(blocks), dim3(Sh::NTB), 0,
+                     st, a);
   return hipGetLastError();
 }
 
