@@ -35,10 +35,16 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 METRIC = "prefill tokens/s (delta rule, H=16,d=128,T=4K); decode state-update GB/s"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["delta_rule_recurrent_chunkwise_amd/csrc/prefill.hip",
-                  "delta_rule_recurrent_chunkwise_amd/csrc/device_common.hpp"]
-DECODE_SOURCES = ["delta_rule_recurrent_chunkwise_amd/csrc/decode.hip",
-                  "delta_rule_recurrent_chunkwise_amd/csrc/device_common.hpp"]
+_CSRC = "delta_rule_recurrent_chunkwise_amd/csrc/"
+PREFILL_SOURCES = [_CSRC + "prefill_pipe.hip", _CSRC + "device_common.hpp", _CSRC + "launch.hpp"]
+DECODE_SOURCES = [_CSRC + "decode.hip", _CSRC + "device_common.hpp", _CSRC + "launch.hpp"]
+# Symbol substrings of the two timed kernels (as rocprofv3 lists them) and the
+# profile summaries that record their counters.
+PREFILL_KERNEL = "prefill_delta_pipe"
+DECODE_KERNEL = "decode_kernel<128, 128, linattn::BF16, 0"
+PREFILL_PROFILE = "prefill_delta_pipe_B4_H16_T4096_d128.txt"
+DECODE_PROFILE = "decode_kernel_delta_N256_H32_d128.txt"
+COPY_KERNEL = "copyBuffer"
 
 
 def prefill_algorithmic(B, H, T, dk, dv, in_bytes=2):
@@ -69,17 +75,110 @@ def sources_digest(paths):
 
 
 def recorded_traffic(name, digest):
-    """HBM bytes per launch measured with rocprofv3 counters, if they were
-    taken on the current kernel source; otherwise None."""
-    path = os.path.join(PROFILES, name)
+    """HBM bytes per launch measured with rocprofv3 counters, if the summary
+    in profiles/ was taken on the current kernel source; otherwise None."""
+    rec = {}
     try:
+        with open(os.path.join(PROFILES, name)) as f:
+            for ln in f:
+                key, sep, val = ln.partition(":")
+                if sep:
+                    rec[key.strip()] = val.strip()
+    except OSError:
+        return None
+    if rec.get("kernel_sources_sha256") != digest or "hbm_bytes_per_launch" not in rec:
+        return None
+    return float(rec["hbm_bytes_per_launch"])
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True)):
         with open(path) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if rec.get("kernel_sources_sha256") != digest:
-        return None
-    return rec.get("hbm_bytes_per_launch")
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _counter_mean(directory, counter, kernel):
+    vals = [float(r["Counter_Value"]) for r in _csv_rows(directory, "counter_collection.csv")
+            if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernel '{kernel}' under {directory}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize(prof_dir):
+    """Write the rocprofv3 summaries in profiles/ from the raw output of the
+    profiling commands listed in each summary (run from /tmp, repo at $R):
+      trace:  rocprofv3 --kernel-trace --stats -f csv -d $R/<dir>/trace -o trace
+                -- python3 $R/bench.py --no-cpu-baseline
+      counters, one run per counter C in FETCH_SIZE, WRITE_SIZE and mode M in
+      prefill, decode, copy:
+              rocprofv3 --pmc C -f csv -d $R/<dir>/pmc_C_M -o pmc
+                -- python3 $R/bench.py --only M --steps 5 --warmup 1 --decode-steps 20
+    FETCH_SIZE and WRITE_SIZE are in KiB per dispatch; each is scaled by the
+    ratio of the true size of a 1 GiB device copy to what the same counter
+    reads for it."""
+    stats = _csv_rows(os.path.join(prof_dir, "trace"), "kernel_stats.csv")
+    copy_bytes = 1 << 30
+    cal = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        kib, _ = _counter_mean(os.path.join(prof_dir, f"pmc_{c}_copy"), c, COPY_KERNEL)
+        cal[c] = (kib, copy_bytes / (kib * 1024.0))
+    trace_cmd = ("cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/prof/trace "
+                 "-o trace -- python3 $R/bench.py --no-cpu-baseline")
+    pmc_cmd = ("cd /tmp && rocprofv3 --pmc {c} -f csv -d $R/gpurun_out/prof/pmc_{c}_{m} -o pmc "
+               "-- python3 $R/bench.py --only {m} --steps 5 --warmup 1 --decode-steps 20")
+    jobs = [("prefill", PREFILL_KERNEL, PREFILL_PROFILE, PREFILL_SOURCES,
+             "deltanet_prefill B=4 H=16 T=4096 dk=dv=128, bf16 q/k/v/beta/o, fp32 state",
+             prefill_algorithmic(4, 16, 4096, 128, 128)[0]),
+            ("decode", DECODE_KERNEL, DECODE_PROFILE, DECODE_SOURCES,
+             "deltanet_decode_step N=256 H=32 dk=dv=128, fp32 state in place, bf16 token inputs",
+             decode_algorithmic(256, 32, 128, 128))]
+    for mode, kname, fname, srcs, wl, alg in jobs:
+        row = [r for r in stats if kname in r["Name"]]
+        if len(row) != 1:
+            raise SystemExit(f"expected one kernel-trace row for '{kname}', found {len(row)}")
+        row = row[0]
+        meas = {}
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            meas[c] = _counter_mean(os.path.join(prof_dir, f"pmc_{c}_{mode}"), c, kname)
+        fetch = meas["FETCH_SIZE"][0] * 1024.0 * cal["FETCH_SIZE"][1]
+        write = meas["WRITE_SIZE"][0] * 1024.0 * cal["WRITE_SIZE"][1]
+        lines = [
+            f"# rocprofv3 summary: {row['Name']}",
+            f"# workload: {wl}",
+            "# $R is the repository root; every command runs committed files only.",
+            f"kernel_sources: {' '.join(srcs)}",
+            f"kernel_sources_sha256: {sources_digest(srcs)}",
+            "",
+            f"## kernel trace  ({trace_cmd})",
+            f"calls: {row['Calls']}",
+            f"average_ns: {float(row['AverageNs']):.0f}",
+            f"min_ns: {float(row['MinNs']):.0f}",
+            f"max_ns: {float(row['MaxNs']):.0f}",
+            f"stddev_ns: {float(row['StdDev']):.0f}",
+            "",
+            "## HBM counters, one run per counter",
+            f"#   {pmc_cmd.format(c='FETCH_SIZE', m=mode)}",
+            f"#   {pmc_cmd.format(c='WRITE_SIZE', m=mode)}",
+            f"#   calibration: the same two commands with --only copy ({COPY_KERNEL}, 1 GiB)",
+            f"fetch_kib_per_dispatch: {meas['FETCH_SIZE'][0]:.1f}   (dispatches {meas['FETCH_SIZE'][1]})",
+            f"write_kib_per_dispatch: {meas['WRITE_SIZE'][0]:.1f}   (dispatches {meas['WRITE_SIZE'][1]})",
+            f"copy_fetch_kib: {cal['FETCH_SIZE'][0]:.1f}   scale {cal['FETCH_SIZE'][1]:.4f}",
+            f"copy_write_kib: {cal['WRITE_SIZE'][0]:.1f}   scale {cal['WRITE_SIZE'][1]:.4f}",
+            f"hbm_read_bytes_per_launch: {fetch:.0f}",
+            f"hbm_write_bytes_per_launch: {write:.0f}",
+            f"hbm_bytes_per_launch: {fetch + write:.0f}",
+            f"algorithmic_bytes_per_launch: {alg}",
+            f"traffic_over_algorithmic: {(fetch + write) / alg:.3f}",
+        ]
+        os.makedirs(PROFILES, exist_ok=True)
+        with open(os.path.join(PROFILES, fname), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print(f"wrote profiles/{fname}")
 
 
 def bench_prefill(la, workloads, torch, steps, warmup, copies=3):
@@ -154,31 +253,43 @@ def copy_probe(torch, nbytes=1 << 30, reps=5):
     return nbytes
 
 
-def cpu_baseline(workloads, oracle, torch, prefill_inp, w, decode_inp, wd, budget_s=8.0):
+def cpu_baseline(workloads, oracle, torch, prefill_inp, w, decode_inp, wd, budget_s=10.0,
+                 decode_budget_s=3.0):
+    """The float64 oracle (as written, untuned) timed on the host cores: whole
+    passes over the prefill workload, repeated until about `budget_s` seconds
+    of work are done, and whole decode steps over all heads for about
+    `decode_budget_s` seconds."""
     cores = min(len(os.sched_getaffinity(0)), 16)
-    done_rows = 0
+    x = {n: prefill_inp[n].contiguous() for n in ("q", "k", "v", "beta")}
+    passes = 0
     t0 = time.perf_counter()
-    for b in range(w.B):
-        sub = {n: prefill_inp[n][b:b + 1].contiguous() for n in ("q", "k", "v", "beta")}
-        oracle.delta_recurrent(sub["q"], sub["k"], sub["v"], sub["beta"], nthreads=cores)
-        done_rows += 1
-        if time.perf_counter() - t0 > budget_s:
+    while True:
+        oracle.delta_recurrent(x["q"], x["k"], x["v"], x["beta"], nthreads=cores)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el > budget_s:
             break
-    el = time.perf_counter() - t0
-    tok_s = done_rows * w.T / el
+    tok_s = passes * w.B * w.T / el
     q = decode_inp
+    dq = {n: q[n][0][:, :, None].contiguous() for n in ("q", "k", "v", "beta")}
+    steps = 0
     t1 = time.perf_counter()
-    oracle.delta_recurrent(q["q"][0][:, :, None], q["k"][0][:, :, None], q["v"][0][:, :, None],
-                           q["beta"][0][:, :, None], None, S0=q["S0"], nthreads=cores)
-    el_d = time.perf_counter() - t1
+    while True:
+        oracle.delta_recurrent(dq["q"], dq["k"], dq["v"], dq["beta"], None, S0=q["S0"],
+                               nthreads=cores)
+        steps += 1
+        el_d = time.perf_counter() - t1
+        if el_d > decode_budget_s:
+            break
     dec_bytes = decode_algorithmic(wd.B, wd.H, wd.dk, wd.dv)
     return {
         "value": tok_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-        "sample": (f"float64 per-token recurrence over {done_rows} of {w.B} batch rows "
-                   f"(H={w.H}, T={w.T}, d={w.dk}) of the prefill workload, "
-                   f"{el:.1f} s wall on {cores} threads"),
-        "decode": {"value": dec_bytes / el_d / 1e9, "unit": "GB/s",
-                   "sample": f"one decode step over all {wd.B * wd.H} heads, {el_d:.2f} s"},
+        "sample": (f"float64 per-token recurrence, {passes} whole passes over the prefill "
+                   f"workload (B={w.B}, H={w.H}, T={w.T}, d={w.dk}) in {el:.1f} s "
+                   f"on {cores} threads"),
+        "decode": {"value": dec_bytes * steps / el_d / 1e9, "unit": "GB/s",
+                   "sample": (f"{steps} decode steps over all {wd.B * wd.H} heads "
+                              f"(float64 state) in {el_d:.1f} s")},
     }
 
 
@@ -191,7 +302,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
                     help="run one part only (for profiler runs)")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="write profiles/*.txt from rocprofv3 output under DIR and exit")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
@@ -223,7 +339,7 @@ def main():
     avg_kernel_s = sum(kms) / len(kms) / 1e3
     pbytes, pflops = prefill_algorithmic(B, H, T, dk, dv)
     achieved = pbytes / avg_kernel_s / 1e9
-    traffic = recorded_traffic("deltanet_prefill_traffic.json", sources_digest(KERNEL_SOURCES))
+    traffic = recorded_traffic(PREFILL_PROFILE, sources_digest(PREFILL_SOURCES))
     line = {
         "metric": METRIC,
         "value": B * T / (wall / args.steps),
@@ -242,7 +358,7 @@ def main():
                    "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": 64},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "prefill_kernel<128, BF16, PF_DELTA, 32>",
+                     "kernel": PREFILL_KERNEL,
                      "algorithmic_bytes_per_launch": pbytes,
                      "avg_launch_us": avg_kernel_s * 1e6,
                      "median_launch_us": kms[len(kms) // 2] * 1e3},
@@ -255,7 +371,7 @@ def main():
         wd, dinp, el = bench_decode(la, workloads, torch, args.decode_steps)
         dbytes = decode_algorithmic(wd.B, wd.H, wd.dk, wd.dv)
         gbs = dbytes * args.decode_steps / el / 1e9
-        dtraffic = recorded_traffic("deltanet_decode_traffic.json", sources_digest(DECODE_SOURCES))
+        dtraffic = recorded_traffic(DECODE_PROFILE, sources_digest(DECODE_SOURCES))
         line["decode"] = {
             "value": gbs, "unit": "GB/s", "steps": args.decode_steps, "warmup": 10,
             "us_per_step": el / args.decode_steps * 1e6,
@@ -264,6 +380,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": dtraffic,
                          "kernel": "decode_kernel<128, 128, BF16, DEC_DELTA>",
+                         "avg_launch_us": el / args.decode_steps * 1e6,
                          "algorithmic_bytes_per_launch": dbytes},
         }
         if not args.no_cpu_baseline:
