@@ -18,20 +18,28 @@
 //              fp32 forward substitution in phase 2 (one lane per column),
 //              the off-diagonal blocks by MFMA block products in phase 1 of
 //              the next iteration, straight from registers.
-//   waves 4-5  the transposed copy K^T of chunk c+1 (phase 2).
-//   all waves  a share of the global loads of q and k, issued two chunks
-//              ahead into registers and written to LDS one iteration later.
+//   wave 4     writes the output tile of chunk c-1 to memory (phase 1).
+//   waves 2-7  the global loads of q, k and the v slice, issued three
+//              chunks ahead into registers and written to LDS two chunks
+//              ahead.
 // Each iteration has two phases separated by LDS-only barriers, so global
 // loads stay in flight across them.
 //
-// Index conventions.  K and Q are stored row-major in natural column order.
-// The chain's 32-deep MFMA pairs two accumulator tiles; the k-index order
-// that pairing implies is absorbed by a fixed permutation of S's rows: the
-// accumulator row rho = 32b + 16h + 4g + i of a chain wave holds logical key
-// channel d = 32b + 8g + 4h + i (perm32 below).  Matrices used as A operands
-// against such paired tiles over tokens (T, tril(Q K^T), K^T) store their
-// token columns permuted the same way, so every operand fragment is one
-// 16-byte LDS read.
+// Index conventions.  K, Q and the v slice are stored row-major (tokens x
+// channels) in natural column order.  The chain's 32-deep MFMA pairs two
+// accumulator tiles; the k-index order that pairing implies is absorbed by a
+// fixed permutation of S's rows: the accumulator row rho = 32b + 16h + 4g + i
+// of a chain wave holds logical key channel d = 32b + 8g + 4h + i (perm32
+// below).  T and tril(Q K^T), used as A operands against paired tiles over
+// tokens, store their token columns permuted the same way, so each of their
+// fragments is one 16-byte LDS read.  The transposed operands K^T (for
+// S += K^T u) and the accumulator-layout V are read straight from the
+// row-major tiles with the LDS transpose read (ds_read_b64_tr_b16): lane
+// 16G + 4a + b receives element b of the 8-byte runs addressed by lanes
+// 16G + a + 4e, e = 0..3.
+//
+// Row strides are 8 (mod 32) dwords: 16-byte fragment reads of 16 rows and
+// transpose reads of 4-8 rows then fall in distinct LDS banks.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -45,29 +53,22 @@ constexpr int kDK = 128;
 constexpr int kDVS = 32;
 constexpr int kThreads = 512;
 
-constexpr int kLQ = kDK + 8;  // bf16 row stride of q, k (16-byte aligned, conflict-free)
-constexpr int kLT = kC + 8;   // bf16 row stride of tril(QK^T), T, V^T
-constexpr int kLL = kC + 4;   // fp32 row stride of L / D
-constexpr int kLO = kDVS + 8; // bf16 row stride of the output tile
+constexpr int kLQ = kDK + 16;  // bf16 row stride of q, k (72 dwords)
+constexpr int kLT = kC + 16;   // bf16 row stride of tril(QK^T), T (40 dwords)
+constexpr int kLV = kDVS + 16; // bf16 row stride of the v slice (24 dwords)
+constexpr int kLL = kC + 4;    // fp32 row stride of L / D
+constexpr int kLO = kDVS + 8;  // bf16 row stride of the output tile
 
 struct __attribute__((aligned(16))) Smem {
   bf16_t q[2][kC][kLQ];
-  bf16_t k[2][kC][kLQ];
-  bf16_t kt[2][kDK][kC];   // unpadded; 16-byte groups XOR-swizzled (kt_col)
+  bf16_t k[3][kC][kLQ];    // chunk x in buffer x mod 3: K(c) is read in both phases
   bf16_t a[2][kC][kLT];
   bf16_t t[kC][kLT];
-  bf16_t vt[2][kDVS][kLT]; // V^T of the slice
+  bf16_t v[2][kC][kLV];    // the v slice, row-major
   bf16_t o[kC][kLO];       // output tile of one chunk
   float l[kC][kLL];
   float beta[2][kC];
 };
-
-// Column of K^T row `row` holding (permuted) token position `pos`: the eight
-// 16-byte groups of a 64-token row are XOR-swizzled so that the 16 rows a
-// fragment read touches fall in distinct banks.
-__device__ __forceinline__ int kt_col(int row, int pos) {
-  return (((pos >> 3) ^ ((row >> 1) & 7)) << 3) | (pos & 7);
-}
 
 // 32b + 16h + 4g + i  ->  32b + 8g + 4h + i
 __device__ __forceinline__ int perm32(int x) {
@@ -84,6 +85,8 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+__device__ __forceinline__ int mod3(int x) { return (x + 3) % 3; }  // x >= -3
+
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
   if (n % 8 != 0) return bid;
   return (bid % 8) * (n / 8) + bid / 8;
@@ -93,6 +96,19 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8 ld_frag(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
+}
+
+typedef short shortx4_t __attribute__((ext_vector_type(4)));
+// LDS transpose read of four bf16 (see the index conventions above).
+__device__ __forceinline__ shortx4_t ld_tr(const bf16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4_t*)(
+          (__attribute__((address_space(3))) bf16_t*)(p)));
+}
+__device__ __forceinline__ bf16x8 cat_tr(shortx4_t lo, shortx4_t hi) {
+  typedef short shortx8_t __attribute__((ext_vector_type(8)));
+  const shortx8_t x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, x);
 }
 
 // 16x16 fp32 accumulator tile used as a 16-deep bf16 MFMA operand.  As B it
@@ -151,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
   constexpr int kLoaders = kThreads - 128;
   constexpr int kPerLoader = 2304 / kLoaders;  // 6
   const int lu = tid - 128;
-  auto issue_loads = [&](int chunk, u32x4 (&dst)[kPerLoader], float& bdst) {
+  auto issue_loads = [&](int chunk, u32x4 (&dst)[kPerLoader], uint32_t& bdst) {
 #pragma unroll
     for (int j = 0; j < kPerLoader; ++j) {
       const int v = lu + kLoaders * j;
@@ -165,25 +181,22 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
       }
       dst[j] = *reinterpret_cast<const u32x4*>(src);
     }
-    if (wave == 4) bdst = bf2f(bth[chunk * kC + lane]);
+    if (wave == 4) bdst = bth[chunk * kC + lane];  // converted when stored
   };
-  auto store_loads = [&](int buf, const u32x4 (&src)[kPerLoader], float bsrc) {
+  auto store_loads = [&](int buf, int kbuf, const u32x4 (&src)[kPerLoader], uint32_t bsrc) {
 #pragma unroll
     for (int j = 0; j < kPerLoader; ++j) {
       const int v = lu + kLoaders * j;
       if (v < 2048) {
         const int vv = v & 1023;
-        bf16_t* dstp = (v < 1024 ? &sm.q[buf][vv >> 4][(vv & 15) * 8] : &sm.k[buf][vv >> 4][(vv & 15) * 8]);
+        bf16_t* dstp = (v < 1024 ? &sm.q[buf][vv >> 4][(vv & 15) * 8] : &sm.k[kbuf][vv >> 4][(vv & 15) * 8]);
         *reinterpret_cast<u32x4*>(dstp) = src[j];
       } else {
         const int vv = v - 2048;
-        const int r = vv >> 2, c0 = (vv & 3) * 8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          sm.vt[buf][c0 + e][r] = (bf16_t)((src[j][e >> 1] >> (16 * (e & 1))) & 0xffffu);
+        *reinterpret_cast<u32x4*>(&sm.v[buf][vv >> 2][(vv & 3) * 8]) = src[j];
       }
     }
-    if (wave == 4) sm.beta[buf][lane] = bsrc;
+    if (wave == 4) sm.beta[buf][lane] = bf2f((bf16_t)bsrc);
   };
 
   // Every role below runs its own copy of the chunk loop: iteration c
@@ -197,10 +210,10 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
   auto run = [&](auto phase1, auto phase2) {
     const bool loader = wave >= 2;
     u32x4 pf[2][kPerLoader];
-    float pfb[2] = {0.f, 0.f};
+    uint32_t pfb[2] = {0u, 0u};
     if (loader) {
       issue_loads(0, pf[0], pfb[0]);
-      store_loads(0, pf[0], pfb[0]);
+      store_loads(0, 0, pf[0], pfb[0]);
       if (nch > 1) issue_loads(1, pf[1], pfb[1]);
     }
     lds_barrier();
@@ -210,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
       if (loader && c + 3 < nch) issue_loads(c + 3, pf[1 - P], pfb[1 - P]);
       lds_barrier();
       phase2(c, parity);
-      if (loader && c + 2 < nch) store_loads(P, pf[P], pfb[P]);
+      if (loader && c + 2 < nch) store_loads(P, mod3(c + 2), pf[P], pfb[P]);
       lds_barrier();
     };
     for (int c = -1; c < nch; c += 2) {
@@ -236,6 +249,7 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
         [&](const int c, auto parity) {
           constexpr int P = decltype(parity)::value;
           if (c < 0) return;
+          const int kc = mod3(c);
           // Y = K S and O = Q S (shared S fragments), X = beta (V - Y).
           // The fragments of k-step kb+1 are loaded while kb computes.
           floatx4 y[4];
@@ -244,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
           bf16x8 fk[2][4], fq[2][4];
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) {
-            fk[0][mt] = ld_frag(&sm.k[P][16 * mt + lc][8 * lg]);
+            fk[0][mt] = ld_frag(&sm.k[kc][16 * mt + lc][8 * lg]);
             fq[0][mt] = ld_frag(&sm.q[P][16 * mt + lc][8 * lg]);
           }
 #pragma unroll
@@ -252,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
             if (kb < 3) {
 #pragma unroll
               for (int mt = 0; mt < 4; ++mt) {
-                fk[(kb + 1) & 1][mt] = ld_frag(&sm.k[P][16 * mt + lc][32 * (kb + 1) + 8 * lg]);
+                fk[(kb + 1) & 1][mt] = ld_frag(&sm.k[kc][16 * mt + lc][32 * (kb + 1) + 8 * lg]);
                 fq[(kb + 1) & 1][mt] = ld_frag(&sm.q[P][16 * mt + lc][32 * (kb + 1) + 8 * lg]);
               }
             }
@@ -265,17 +279,19 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
           }
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) {
-            const uint2 vw = *reinterpret_cast<const uint2*>(&sm.vt[P][col][16 * mt + 4 * lg]);
+            // lane (lg, lc) gets V[16 mt + 4 lg + i][col], i = 0..3
+            const shortx4_t vw = ld_tr(&sm.v[P][16 * mt + 4 * lg + ((lane >> 2) & 3)][16 * wave + 4 * (lane & 3)]);
             const float4 bt = *reinterpret_cast<const float4*>(&sm.beta[P][16 * mt + 4 * lg]);
-            xx[mt][0] = bt.x * (__uint_as_float(vw.x << 16) - y[mt][0]);
-            xx[mt][1] = bt.y * (__uint_as_float(vw.x & 0xffff0000u) - y[mt][1]);
-            xx[mt][2] = bt.z * (__uint_as_float(vw.y << 16) - y[mt][2]);
-            xx[mt][3] = bt.w * (__uint_as_float(vw.y & 0xffff0000u) - y[mt][3]);
+            xx[mt][0] = bt.x * (bf2f((bf16_t)vw[0]) - y[mt][0]);
+            xx[mt][1] = bt.y * (bf2f((bf16_t)vw[1]) - y[mt][1]);
+            xx[mt][2] = bt.z * (bf2f((bf16_t)vw[2]) - y[mt][2]);
+            xx[mt][3] = bt.w * (bf2f((bf16_t)vw[3]) - y[mt][3]);
           }
         },
         [&](const int c, auto parity) {
           constexpr int P = decltype(parity)::value;
           if (c < 0) return;
+          const int kc = mod3(c);
           // u = T X (T lower triangular; above-diagonal tiles are zero).
           // All T and tril(QK^T) fragments are requested up front.
           bf16x8 ft[6], fa[6];
@@ -298,9 +314,16 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
           ut[1] = mfma_k32(ft[1], x01, zero4());
           ut[2] = mfma_k32(ft[3], x23, mfma_k32(ft[2], x01, zero4()));
           ut[3] = mfma_k32(ft[5], x23, mfma_k32(ft[4], x01, zero4()));
+          // K^T fragments: row 16t + c of the A operand is key channel
+          // perm32(16t + c); its k-elements are the tokens of u's pairing.
+          const int trow = 4 * lg + ((lane >> 2) & 3);
+          auto kt_frag = [&](int t, int tok0) {
+            const int col = 32 * (t >> 1) + 4 * (t & 1) + 8 * (lane & 3);
+            return cat_tr(ld_tr(&sm.k[kc][tok0 + trow][col]), ld_tr(&sm.k[kc][tok0 + 16 + trow][col]));
+          };
           bf16x8 fkt[2][8];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) fkt[0][t] = ld_frag(&sm.kt[P][16 * t + lc][kt_col(16 * t + lc, 8 * lg)]);
+          for (int t = 0; t < 8; ++t) fkt[0][t] = kt_frag(t, 0);
           const bf16x8 u01 = acc_pair_to_b(ut[0], ut[1]);
           const bf16x8 u23 = acc_pair_to_b(ut[2], ut[3]);
           // O += tril(Q K^T) u
@@ -309,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
           ox[2] = mfma_k32(fa[3], u23, mfma_k32(fa[2], u01, ox[2]));
           ox[3] = mfma_k32(fa[5], u23, mfma_k32(fa[4], u01, ox[3]));
 #pragma unroll
-          for (int t = 0; t < 8; ++t) fkt[1][t] = ld_frag(&sm.kt[P][16 * t + lc][kt_col(16 * t + lc, 32 + 8 * lg)]);
+          for (int t = 0; t < 8; ++t) fkt[1][t] = kt_frag(t, 32);
           // S += K^T u
 #pragma unroll
           for (int t = 0; t < 8; ++t) st[t] = mfma_k32(fkt[0][t], u01, st[t]);
@@ -418,6 +441,7 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
           [&](const int c, auto parity) {
             constexpr int nb = 1 - decltype(parity)::value;  // buffer of chunk c+1
             if (c + 1 >= nch) return;
+            const int kn = mod3(c + 1);
             // K K^T -> L = diag(beta) (.) strictly below the diagonal
 #pragma unroll
             for (int i = I0; i <= I1; ++i) {
@@ -425,7 +449,7 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
 #pragma unroll
               for (int j = 0; j <= i; ++j)
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) fb[j][kb] = ld_frag(&sm.k[nb][16 * j + lc][32 * kb + 8 * lg]);
+                for (int kb = 0; kb < 4; ++kb) fb[j][kb] = ld_frag(&sm.k[kn][16 * j + lc][32 * kb + 8 * lg]);
               floatx4 acc[4];
 #pragma unroll
               for (int j = 0; j <= i; ++j) {
@@ -445,6 +469,7 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
           [&](const int c, auto parity) {
             constexpr int nb = 1 - decltype(parity)::value;
             if (c + 1 >= nch) return;
+            const int kn = mod3(c + 1);
             // tril(Q K^T), token columns permuted
 #pragma unroll
             for (int i = I0; i <= I1; ++i) {
@@ -454,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
 #pragma unroll
               for (int j = 0; j <= i; ++j)
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) fb[j][kb] = ld_frag(&sm.k[nb][16 * j + lc][32 * kb + 8 * lg]);
+                for (int kb = 0; kb < 4; ++kb) fb[j][kb] = ld_frag(&sm.k[kn][16 * j + lc][32 * kb + 8 * lg]);
               floatx4 acc[4];
 #pragma unroll
               for (int j = 0; j <= i; ++j) {
@@ -476,45 +501,24 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
     else if (wave == 3) prod(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
     else prod(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
   } else {
-    // ======================= K^T waves (4, 5) =======================
-    // K^T of chunk c+1 with key channels in chain-row order (row rho holds
-    // channel perm32(rho)) and token columns permuted
+    // ======================= output waves (4, 5) =======================
+    // Wave 4 writes the output tile of chunk c-1 (left in LDS by the chain
+    // waves) to memory with 16-byte stores; both waves also load.
     const int sw = tid - 256;  // 0..127
-    const int p = sw & 31;     // token pair
-    const int cvo = sw >> 5;   // 0..3
-    // They also write the output tile of chunk c-1 (left in LDS by the
-    // chain waves) to memory with 16-byte stores.
     auto store_o = [&](int chunk) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int v = sw + 128 * j;
+      for (int j = 0; j < 4; ++j) {
+        const int v = sw + 64 * j;
         const int r = v >> 2, c8 = (v & 3) * 8;
         *reinterpret_cast<u32x4*>(oh + (size_t)(chunk * kC + r) * dv + c8) =
             *reinterpret_cast<const u32x4*>(&sm.o[r][c8]);
       }
     };
     run([&](const int c, auto parity) {
-          if (c >= 1) store_o(c - 1);
+          if (wave == 4 && c >= 1) store_o(c - 1);
         },
-        [&](const int c, auto parity) {
-          constexpr int nb = 1 - decltype(parity)::value;
-          if (c + 1 >= nch) return;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int cv = cvo + 4 * jj;  // group of 8 key channels
-            const u32x4 r0 = *reinterpret_cast<const u32x4*>(&sm.k[nb][2 * p][cv * 8]);
-            const u32x4 r1 = *reinterpret_cast<const u32x4*>(&sm.k[nb][2 * p + 1][cv * 8]);
-            const int pos = perm32(2 * p);  // even: the token pair is one aligned word
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t lo = (r0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-              const uint32_t hi = (r1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-              const int row = perm32_inv(cv * 8 + e);
-              *reinterpret_cast<uint32_t*>(&sm.kt[nb][row][kt_col(row, pos)]) = lo | (hi << 16);
-            }
-          }
-        });
-    store_o(nch - 1);
+        [&](const int c, auto parity) {});
+    if (wave == 4) store_o(nch - 1);
   }
 }
 
