@@ -6,7 +6,10 @@
 // per 64-token chunk, with L = tril(diag(beta) K K^T, -1) and T = (I + L)^-1,
 //   u = T diag(beta) (V - K S),   O = Q S + tril(Q K^T) u,   S <- S + K^T u.
 // It is the same computation as prefill.hip; this kernel only organises it
-// for throughput on one CU.
+// for throughput on one CU.  T is never formed: with I + L split into 16x16
+// token blocks, u is obtained by block forward substitution,
+//   u_b = D_b (X_b - sum_{j<b} L_bj u_j),   D_b = (I + L_bb)^-1,
+// where X = diag(beta) (V - K S).
 //
 // Work split inside a workgroup (8 waves; one (batch, head) and 32 value
 // columns per workgroup):
@@ -14,10 +17,8 @@
 //              runs only the S-dependent products of chunk c.
 //   waves 2,3,7 products of chunk c+1: K K^T (giving L) in phase 1 and
 //              tril(Q K^T) in phase 2.
-//   wave 6     T = (I + L)^-1 of chunk c+1: the four 16x16 diagonal blocks by
-//              fp32 forward substitution in phase 2 (one lane per column),
-//              the off-diagonal blocks by MFMA block products in phase 1 of
-//              the next iteration, straight from registers.
+//   wave 6     the diagonal-block inverses D_b of chunk c+1 by fp32 forward
+//              substitution (one lane per column; phase 2).
 //   wave 4     writes the output tile of chunk c-1 to memory (phase 1).
 //   waves 2-7  the global loads of q, k and the v slice, issued three
 //              chunks ahead into registers and written to LDS two chunks
@@ -30,13 +31,15 @@
 // accumulator tiles; the k-index order that pairing implies is absorbed by a
 // fixed permutation of S's rows: the accumulator row rho = 32b + 16h + 4g + i
 // of a chain wave holds logical key channel d = 32b + 8g + 4h + i (perm32
-// below).  T and tril(Q K^T), used as A operands against paired tiles over
-// tokens, store their token columns permuted the same way, so each of their
+// below).  tril(Q K^T), used as an A operand against paired tiles over
+// tokens, stores its token columns permuted the same way, so each of its
 // fragments is one 16-byte LDS read.  The transposed operands K^T (for
 // S += K^T u) and the accumulator-layout V are read straight from the
 // row-major tiles with the LDS transpose read (ds_read_b64_tr_b16): lane
 // 16G + 4a + b receives element b of the 8-byte runs addressed by lanes
-// 16G + a + 4e, e = 0..3.
+// 16G + a + 4e, e = 0..3.  The 16x16 blocks D_b and L_bj are stored
+// transposed (16 bf16 per row, unpadded) and read the same way as the A
+// operands of the 16-deep MFMA.
 //
 // Row strides are 8 (mod 32) dwords: 16-byte fragment reads of 16 rows and
 // transpose reads of 4-8 rows then fall in distinct LDS banks.
@@ -54,16 +57,17 @@ constexpr int kDVS = 32;
 constexpr int kThreads = 512;
 
 constexpr int kLQ = kDK + 16;  // bf16 row stride of q, k (72 dwords)
-constexpr int kLT = kC + 16;   // bf16 row stride of tril(QK^T), T (40 dwords)
+constexpr int kLT = kC + 16;   // bf16 row stride of tril(QK^T) (40 dwords)
 constexpr int kLV = kDVS + 16; // bf16 row stride of the v slice (24 dwords)
-constexpr int kLL = kC + 4;    // fp32 row stride of L / D
+constexpr int kLL = kC + 4;    // fp32 row stride of L (diagonal blocks)
 constexpr int kLO = kDVS + 8;  // bf16 row stride of the output tile
 
 struct __attribute__((aligned(16))) Smem {
   bf16_t q[2][kC][kLQ];
   bf16_t k[3][kC][kLQ];    // chunk x in buffer x mod 3: K(c) is read in both phases
   bf16_t a[2][kC][kLT];
-  bf16_t t[kC][kLT];
+  bf16_t lb[2][6][16][16]; // off-diagonal blocks L_bj (b > j), transposed
+  bf16_t d[2][4][16][16];  // diagonal-block inverses D_b, transposed
   bf16_t v[2][kC][kLV];    // the v slice, row-major
   bf16_t o[kC][kLO];       // output tile of one chunk
   float l[kC][kLL];
@@ -113,20 +117,6 @@ __device__ __forceinline__ bf16x8 cat_tr(shortx4_t lo, shortx4_t hi) {
 
 // 16x16 fp32 accumulator tile used as a 16-deep bf16 MFMA operand.  As B it
 // is the tile itself; as A it is the tile's transpose.
-__device__ __forceinline__ floatx4 mm16(floatx4 a_acc, floatx4 b_acc, floatx4 c) {
-  return mfma_k16(acc_to_b16(a_acc), acc_to_b16(b_acc), c);
-}
-__device__ __forceinline__ floatx4 neg4(floatx4 x) { return floatx4{-x[0], -x[1], -x[2], -x[3]}; }
-
-// Registers a wave keeps from the diagonal inverses of one chunk (phase 2)
-// to the block merges (phase 1 of the next iteration).  "n" tiles hold a
-// matrix in accumulator layout, "t" tiles its transpose.
-struct TCarry {
-  floatx4 d0n, d1n, d2n;
-  floatx4 d0t, d1t, d2t, d3t;
-  floatx4 l10t, l32t, l20t, l21t, l30t, l31t;
-};
-
 }  // namespace
 
 __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
@@ -152,12 +142,10 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
   bf16_t* oh = reinterpret_cast<bf16_t*>(a.o) + (size_t)bh * Tn * dv + sl * kDVS;
   float* Sh = a.S + (size_t)bh * kDK * dv + sl * kDVS;
 
-  // Tiles above the diagonal of tril(QK^T) and T are read as zeros.
+  // Tiles above the diagonal of tril(QK^T) are read as zeros.
   {
     uint32_t* z = reinterpret_cast<uint32_t*>(&sm.a[0][0][0]);
     for (int i = tid; i < (int)(sizeof(sm.a) / 4); i += kThreads) z[i] = 0u;
-    uint32_t* zt = reinterpret_cast<uint32_t*>(&sm.t[0][0]);
-    for (int i = tid; i < (int)(sizeof(sm.t) / 4); i += kThreads) zt[i] = 0u;
   }
 
   // ---- register prefetch by waves 2..7 (the chain waves keep their
@@ -292,28 +280,34 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
           constexpr int P = decltype(parity)::value;
           if (c < 0) return;
           const int kc = mod3(c);
-          // u = T X (T lower triangular; above-diagonal tiles are zero).
-          // All T and tril(QK^T) fragments are requested up front.
-          bf16x8 ft[6], fa[6];
-          ft[0] = ld_frag(&sm.t[lc][8 * lg]);
-          ft[1] = ld_frag(&sm.t[16 + lc][8 * lg]);
-          ft[2] = ld_frag(&sm.t[32 + lc][8 * lg]);
-          ft[3] = ld_frag(&sm.t[32 + lc][32 + 8 * lg]);
-          ft[4] = ld_frag(&sm.t[48 + lc][8 * lg]);
-          ft[5] = ld_frag(&sm.t[48 + lc][32 + 8 * lg]);
+          // u by block forward substitution; the D_b, L_bj and tril(Q K^T)
+          // fragments are requested up front.
+          auto fr16 = [&](const bf16_t* blk) {  // A operand of a transposed 16x16 block
+            return ld_tr(blk + (4 * lg + ((lane >> 2) & 3)) * 16 + 4 * (lane & 3));
+          };
+          shortx4_t fd[4], fl[6];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) fd[b] = fr16(&sm.d[P][b][0][0]);
+#pragma unroll
+          for (int x = 0; x < 6; ++x) fl[x] = fr16(&sm.lb[P][x][0][0]);
+          bf16x8 fa[6];
           fa[0] = ld_frag(&sm.a[P][lc][8 * lg]);
           fa[1] = ld_frag(&sm.a[P][16 + lc][8 * lg]);
           fa[2] = ld_frag(&sm.a[P][32 + lc][8 * lg]);
           fa[3] = ld_frag(&sm.a[P][32 + lc][32 + 8 * lg]);
           fa[4] = ld_frag(&sm.a[P][48 + lc][8 * lg]);
           fa[5] = ld_frag(&sm.a[P][48 + lc][32 + 8 * lg]);
-          const bf16x8 x01 = acc_pair_to_b(xx[0], xx[1]);
-          const bf16x8 x23 = acc_pair_to_b(xx[2], xx[3]);
+          // blocks L_bj stored in the order (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
           floatx4 ut[4];
-          ut[0] = mfma_k32(ft[0], x01, zero4());
-          ut[1] = mfma_k32(ft[1], x01, zero4());
-          ut[2] = mfma_k32(ft[3], x23, mfma_k32(ft[2], x01, zero4()));
-          ut[3] = mfma_k32(ft[5], x23, mfma_k32(ft[4], x01, zero4()));
+          ut[0] = mfma_k16(fd[0], acc_to_b16(xx[0]), zero4());
+          const shortx4_t u0 = acc_to_b16(ut[0]);
+          ut[1] = mfma_k16(fd[1], acc_to_b16(xx[1] - mfma_k16(fl[0], u0, zero4())), zero4());
+          const shortx4_t u1 = acc_to_b16(ut[1]);
+          ut[2] = mfma_k16(fd[2], acc_to_b16(xx[2] - mfma_k16(fl[2], u1, mfma_k16(fl[1], u0, zero4()))),
+                           zero4());
+          const shortx4_t u2 = acc_to_b16(ut[2]);
+          ut[3] = mfma_k16(fd[3], acc_to_b16(xx[3] - mfma_k16(fl[5], u2, mfma_k16(fl[4], u1, mfma_k16(fl[3], u0, zero4())))),
+                           zero4());
           // K^T fragments: row 16t + c of the A operand is key channel
           // perm32(16t + c); its k-elements are the tokens of u's pairing.
           const int trow = 4 * lg + ((lane >> 2) & 3);
@@ -348,41 +342,14 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) Sh[(size_t)perm32(16 * t + 4 * lg + i) * dv + col] = st[t][i];
   } else if (wave == 6) {
-    // ======================= T wave =======================
-    TCarry tc;
-    run(
+    // ======================= D wave =======================
+    // Diagonal 16x16 blocks of I + L for chunk c+1 (phase 2): lane (block lg,
+    // column lc) solves (I + L_bb) x = e_lc by forward substitution in fp32;
+    // x is column lc of D_b = (I + L_bb)^-1, stored as row lc of D_b^T.
+    run([&](const int c, auto parity) {},
         [&](const int c, auto parity) {
-          if (c < 0) return;
-          // off-diagonal blocks of T(c) from the carried diagonal inverses
-          const floatx4 r10 = mm16(tc.l10t, tc.d0n, zero4());
-          const floatx4 t10n = neg4(mm16(tc.d1t, r10, zero4()));
-          const floatx4 t10t = neg4(mm16(r10, tc.d1t, zero4()));
-          const floatx4 r32 = mm16(tc.l32t, tc.d2n, zero4());
-          const floatx4 t32t = neg4(mm16(r32, tc.d3t, zero4()));
-          const floatx4 r20 = mm16(tc.l21t, t10n, mm16(tc.l20t, tc.d0n, zero4()));
-          const floatx4 r21 = mm16(tc.l21t, tc.d1n, zero4());
-          const floatx4 r30 = mm16(tc.l31t, t10n, mm16(tc.l30t, tc.d0n, zero4()));
-          const floatx4 r31 = mm16(tc.l31t, tc.d1n, zero4());
-          const floatx4 t20t = neg4(mm16(r20, tc.d2t, zero4()));
-          const floatx4 t21t = neg4(mm16(r21, tc.d2t, zero4()));
-          const floatx4 t30t = neg4(mm16(r30, tc.d3t, mm16(r20, t32t, zero4())));
-          const floatx4 t31t = neg4(mm16(r31, tc.d3t, mm16(r21, t32t, zero4())));
-          // T row-major with token columns permuted: a transposed tile gives
-          // row 16i + lc, columns 16j + 4lg .. +3, contiguous after the permutation
-          auto put = [&](int i, int j, floatx4 xt) {
-            uint2 wv;
-            wv.x = pack2(xt[0], xt[1]);
-            wv.y = pack2(xt[2], xt[3]);
-            *reinterpret_cast<uint2*>(&sm.t[16 * i + lc][perm32(16 * j + 4 * lg)]) = wv;
-          };
-          put(0, 0, tc.d0t); put(1, 1, tc.d1t); put(2, 2, tc.d2t); put(3, 3, tc.d3t);
-          put(1, 0, t10t); put(3, 2, t32t);
-          put(2, 0, t20t); put(2, 1, t21t); put(3, 0, t30t); put(3, 1, t31t);
-        },
-        [&](const int c, auto parity) {
+          constexpr int nb = 1 - decltype(parity)::value;
           if (c + 1 >= nch) return;
-          // diagonal 16x16 blocks of T(c+1): lane (block lg, column lc) solves
-          // (I + L_bb) t = e_lc by forward substitution in fp32
           const int b0 = 16 * lg;
           float4 lr[16][4];  // strictly-lower rows of L_bb, requested up front
 #pragma unroll
@@ -405,29 +372,14 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
             }
             if (i > lc) tv[i] = -(s0 + s1);
           }
-          // D_b (lower triangular, unit diagonal) over L's diagonal block; the
-          // reads below see these writes (one wave, LDS in program order)
+          u32x4 w0, w1;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sm.l[b0 + i][b0 + lc] = tv[i];
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-          // accumulator-layout copies for the merges: "n" holds X[4lg+r][lc],
-          // "t" holds X[lc][4lg+r] (the transpose)
-          auto accn = [&](int r0, int c0) {
-            floatx4 x;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) x[r] = sm.l[r0 + 4 * lg + r][c0 + lc];
-            return x;
-          };
-          auto acct = [&](int r0, int c0) {
-            const float4 v = *reinterpret_cast<const float4*>(&sm.l[r0 + lc][c0 + 4 * lg]);
-            return floatx4{v.x, v.y, v.z, v.w};
-          };
-          tc.d0n = accn(0, 0); tc.d1n = accn(16, 16); tc.d2n = accn(32, 32);
-          tc.d0t = acct(0, 0); tc.d1t = acct(16, 16); tc.d2t = acct(32, 32); tc.d3t = acct(48, 48);
-          tc.l10t = acct(16, 0); tc.l32t = acct(48, 32); tc.l20t = acct(32, 0);
-          tc.l21t = acct(32, 16); tc.l30t = acct(48, 0); tc.l31t = acct(48, 16);
+          for (int e = 0; e < 4; ++e) {
+            w0[e] = pack2(tv[2 * e], tv[2 * e + 1]);
+            w1[e] = pack2(tv[8 + 2 * e], tv[9 + 2 * e]);
+          }
+          *reinterpret_cast<u32x4*>(&sm.d[nb][lg][lc][0]) = w0;
+          *reinterpret_cast<u32x4*>(&sm.d[nb][lg][lc][8]) = w1;
         });
   } else if (wave == 2 || wave == 3 || wave == 7) {
     // ======================= product waves =======================
@@ -457,13 +409,22 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) acc[j] = mfma_k32(fb[i][kb], fb[j][kb], acc[j]);
               }
+              // diagonal tile: fp32 strictly-lower part for the D wave;
+              // off-diagonal tiles: bf16, transposed (lane writes row lc,
+              // columns 4 lg .. 4 lg + 3 of L_ij^T)
+              const float4 bt = *reinterpret_cast<const float4*>(&sm.beta[nb][16 * i + 4 * lg]);
 #pragma unroll
-              for (int j = 0; j <= i; ++j)
+              for (int j = 0; j < i; ++j) {
+                uint2 w;
+                w.x = pack2(bt.x * acc[j][0], bt.y * acc[j][1]);
+                w.y = pack2(bt.z * acc[j][2], bt.w * acc[j][3]);
+                *reinterpret_cast<uint2*>(&sm.lb[nb][i * (i - 1) / 2 + j][lc][4 * lg]) = w;
+              }
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                  const int r = 16 * i + 4 * lg + ii, cc = 16 * j + lc;
-                  if (cc < r) sm.l[r][cc] = sm.beta[nb][r] * acc[j][ii];
-                }
+              for (int ii = 0; ii < 4; ++ii) {
+                const int r = 16 * i + 4 * lg + ii, cc = 16 * i + lc;
+                if (cc < r) sm.l[r][cc] = (ii == 0 ? bt.x : ii == 1 ? bt.y : ii == 2 ? bt.z : bt.w) * acc[i][ii];
+              }
             }
           },
           [&](const int c, auto parity) {
