@@ -433,7 +433,19 @@ static hipError_t launch_prefill_e(int dk, const PrefillArgs& a, hipStream_t st)
 }
 
 hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, hipStream_t st) {
-  if (bf16 && mode == PF_DELTA && dk == 128 && a.dv % 32 == 0) return launch_prefill_pipe(a, st);
+  if (bf16 && dk == 128 && a.dv % 32 == 0) {
+    if (mode == PF_DELTA) return launch_prefill_pipe(a, st);
+    if (mode == PF_GATED) {
+      // the gate pre-pass writes Gam Q, Gam K, K / Gam and Gam_C to a
+      // stream-ordered workspace that is released after the main kernel
+      void* ws = nullptr;
+      hipError_t e = hipMallocAsync(&ws, gated_pipe_workspace_bytes(a), st);
+      if (e != hipSuccess) return e;
+      e = launch_prefill_pipe2(a, ws, st);
+      const hipError_t f = hipFreeAsync(ws, st);
+      return e != hipSuccess ? e : f;
+    }
+  }
   if (bf16) {
     if (mode == PF_LA) return launch_prefill_e<BF16, PF_LA>(dk, a, st);
     if (mode == PF_DELTA) return launch_prefill_e<BF16, PF_DELTA>(dk, a, st);

@@ -1,0 +1,634 @@
+// prefill_pipe2.hip -- software-pipelined chunkwise delta-rule prefill, plain
+// and with a per-key-channel gate, for bf16 inputs with dk = 128 and dv a
+// multiple of 32.
+//
+// Arithmetic (article "From GPT-2 to Kimi K3, explained"):
+//  * section "DeltaNet (Parallelizing Linear Transformers with Delta Rule)":
+//    per 64-token chunk, with L = tril(diag(beta) K K^T, -1),
+//      u = (I + L)^-1 diag(beta) (V - K S),  O = Q S + tril(Q K^T) u,
+//      S <- S + K^T u.
+//  * sections "Gated Delta Net" and "KDA / Kimi Linear": a decay a_t[i] per
+//    key channel scales row i of S before each read.  With the decay
+//    accumulated from the chunk start, Gam_t = prod_{s<=t} a_s, the same
+//    form holds with K~ = Gam K, K^ = K / Gam, Q~ = Gam Q (row-wise):
+//      L = tril(diag(beta) K~ K^^T, -1),  u = (I + L)^-1 diag(beta) (V - K~ S),
+//      O = Q~ S + tril(Q~ K^^T) u,  S <- diag(Gam_C) (S + K^^T u),
+//    since (K Gam_C / Gam)^T u = diag(Gam_C) K^^T u.  A pre-pass (gate_prep
+//    below) forms K~, K^, Q~ and Gam_C for every chunk; the main kernel is
+//    the plain one with K~ in place of K on the left of every product, K^ on
+//    the right, and the row scaling by Gam_C.
+//
+// (I + L)^-1 is never formed: with I + L cut into 16x16 token blocks, u is
+// obtained by block forward substitution,
+//   u_b = D_b (X_b - sum_{j<b} L_bj u_j),   D_b = (I + L_bb)^-1.
+//
+// Work split inside a workgroup (8 waves; one (batch, head) and 32 value
+// columns per workgroup).  Iteration x has two phases, each closed by an
+// LDS-only barrier:
+//   waves 0-1    "chain": each keeps S[:, 16 columns] in MFMA accumulators.
+//                Phase 1: Y = K S, O = Q S, X = beta (V - Y) for chunk x.
+//                Phase 2: u, O += tril(Q K^T) u, S += K^T u for chunk x.
+//   waves 2,3,7  products.  Phase 1: tril(Q K^T) of chunk x.  Phase 2: L of
+//                chunk x+1 (diagonal blocks fp32, the others bf16).
+//   wave 6       D_b of chunk x from L's diagonal blocks (phase 1).
+//   wave 4       writes the output tile of chunk x-1 to memory (phase 1).
+//   loaders      write chunk x+1 to LDS in phase 1 of iteration x and issue
+//                the global loads of chunk x+3 into the freed registers.
+// Chunk y lives in LDS buffer y & 1: it is written in phase 1 of iteration
+// y-1 and last read in phase 2 of iteration y.
+//
+// Index conventions.  Q, K (and K^) and the v slice are stored row-major
+// (tokens x channels).  The chain's 32-deep MFMA pairs two accumulator
+// tiles; the k-index order of that pairing is absorbed by a fixed
+// permutation of S's rows: accumulator row rho = 32b + 16h + 4g + i of a
+// chain wave holds key channel perm32(rho) = 32b + 8g + 4h + i.
+// tril(Q K^T), an A operand against paired tiles over tokens, stores its
+// token columns permuted the same way.  K^T (for S += K^T u), V in
+// accumulator layout, and the 16x16 blocks D_b, L_bj (stored transposed) are
+// read with the LDS transpose read ds_read_b64_tr_b16: lane 16G + 4a + b
+// receives element b of the 8-byte runs addressed by lanes 16G + a + 4e,
+// e = 0..3.  Row strides are 8 (mod 32) dwords, which keeps 16-byte fragment
+// reads of 16 rows and transpose reads of 4-8 rows in distinct LDS banks.
+#include <type_traits>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace linattn {
+namespace {
+
+constexpr int kC = 64;
+constexpr int kDK = 128;
+constexpr int kDVS = 32;
+constexpr int kThreads = 512;
+
+constexpr int kLQ = kDK + 16;   // bf16 row stride of q, k, k^ (72 dwords)
+constexpr int kLT = kC + 16;    // bf16 row stride of tril(QK^T) (40 dwords)
+constexpr int kLV = kDVS + 16;  // bf16 row stride of the v slice (24 dwords)
+constexpr int kLO = kDVS + 8;   // bf16 row stride of the output tile
+constexpr int kLR = 20;         // fp32 row stride inside a diagonal block of L
+constexpr int kLB = 16 * kLR + 16;  // fp32 stride between diagonal blocks
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short shortx4_t __attribute__((ext_vector_type(4)));
+
+template <bool GATED>
+struct __attribute__((aligned(16))) Smem2 {
+  static constexpr int NKH = GATED ? 2 : 1;
+  static constexpr int RKH = GATED ? kC : 1;
+  bf16_t q[2][kC][kLQ];       // Q (gated: Gam Q)
+  bf16_t k[2][kC][kLQ];       // K (gated: Gam K)
+  bf16_t kh[NKH][RKH][kLQ];   // gated: K / Gam
+  bf16_t a[kC][kLT];          // tril(Q K^T), token columns permuted
+  bf16_t lb[2][6][16][16];    // L_bj (b > j), transposed
+  bf16_t d[4][16][16];        // D_b, transposed
+  bf16_t v[2][kC][kLV];       // v slice
+  bf16_t o[kC][kLO];          // output tile
+  float l[4 * kLB];           // diagonal blocks of L (strictly lower parts)
+  float beta[2][kC];
+  float gc[NKH][kDK];         // gated: Gam_C per key channel
+};
+
+// 32b + 16h + 4g + i  ->  32b + 8g + 4h + i
+__device__ __forceinline__ int perm32(int x) {
+  return (x & ~31) | (((x >> 2) & 3) << 3) | (((x >> 4) & 1) << 2) | (x & 3);
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Consecutive logical workgroups (the dv slices of one head, which read the
+// same q and k) go to one XCD, so they share its L2.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  if (n % 8 != 0) return bid;
+  return (bid % 8) * (n / 8) + bid / 8;
+}
+
+__device__ __forceinline__ bf16x8 ld_frag(const bf16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ shortx4_t ld_tr(const bf16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4_t*)((__attribute__((address_space(3))) bf16_t*)(p)));
+}
+__device__ __forceinline__ bf16x8 cat_tr(shortx4_t lo, shortx4_t hi) {
+  typedef short shortx8_t __attribute__((ext_vector_type(8)));
+  const shortx8_t x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, x);
+}
+
+struct PipeArgs {
+  const bf16_t* q;     // Q, or Gam Q
+  const bf16_t* k;     // K, or Gam K
+  const bf16_t* kh;    // gated: K / Gam
+  const float* gc;     // gated: Gam_C, [B*H][T/64][dk]
+  const bf16_t* v;
+  const bf16_t* beta;
+  bf16_t* o;
+  float* S;
+  int T, dv, use_init;
+};
+
+// Loads.  Waves 4 and 5 carry the q, k (and k^) tiles: lane u = 64 (wave-4)
+// + lane owns 16-byte vector u + 128 j, j < NT (tile j / 8).  Wave 7 carries
+// the v slice (4 vectors per lane), beta (one value per lane) and, gated,
+// Gam_C (lanes 0..31).  Every lane issues every load of its slots (a
+// per-lane condition around a load would make the compiler wait for all
+// outstanding loads), so lanes 32..63 re-read Gam_C's first vectors.
+template <bool GATED>
+struct LoadPlan {
+  static constexpr int NT = GATED ? 24 : 16;  // tile vectors per lane (waves 4, 5)
+  static constexpr int NS = NT;               // registers (16-byte vectors) per slot
+  // Register slots: with two, the loads of chunk y are issued in iteration
+  // y-3 and stored in iteration y-1; with one (the gated tiles need 96
+  // registers a slot), issued in iteration y-2.
+  static constexpr int NSLOT = GATED ? 1 : 2;
+};
+
+template <bool GATED>
+__global__ __launch_bounds__(kThreads) void prefill_pipe2(PipeArgs a) {
+  typedef Smem2<GATED> Sm;
+  typedef LoadPlan<GATED> LP;
+  __shared__ Sm sm;
+
+  const int nsl = a.dv / kDVS;
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = w / nsl;
+  const int sl = w - bh * nsl;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lc = lane & 15;
+  const int lg = lane >> 4;
+  const int Tn = a.T;
+  const int dv = a.dv;
+  const int nch = Tn / kC;
+
+  const bf16_t* qh = a.q + (size_t)bh * Tn * kDK;
+  const bf16_t* kh = a.k + (size_t)bh * Tn * kDK;
+  const bf16_t* khh = GATED ? a.kh + (size_t)bh * Tn * kDK : nullptr;
+  const float* gch = GATED ? a.gc + (size_t)bh * nch * kDK : nullptr;
+  const bf16_t* vh = a.v + (size_t)bh * Tn * dv + sl * kDVS;
+  const bf16_t* bth = a.beta + (size_t)bh * Tn;
+  bf16_t* oh = a.o + (size_t)bh * Tn * dv + sl * kDVS;
+  float* Sh = a.S + (size_t)bh * kDK * dv + sl * kDVS;
+
+  // Tiles above the diagonal of tril(QK^T) are read as zeros.
+  {
+    uint32_t* z = reinterpret_cast<uint32_t*>(&sm.a[0][0]);
+    for (int i = tid; i < (int)(sizeof(sm.a) / 4); i += kThreads) z[i] = 0u;
+  }
+
+  auto issue_loads = [&](int chunk, u32x4 (&dst)[LP::NS], uint32_t& bdst) {
+    if (wave == 4 || wave == 5) {
+      const int u = 64 * (wave - 4) + lane;
+#pragma unroll
+      for (int j = 0; j < LP::NT; ++j) {
+        const bf16_t* base = j < 8 ? qh : (j < 16 ? kh : khh);
+        const int vv = u + 128 * (j & 7);  // 0..1023 within the tile
+        dst[j] = *reinterpret_cast<const u32x4*>(base + (size_t)(chunk * kC + (vv >> 4)) * kDK + (vv & 15) * 8);
+      }
+    } else {  // wave 7
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int vv = lane + 64 * j;  // 0..255: row vv / 4, eight columns
+        dst[j] = *reinterpret_cast<const u32x4*>(vh + (size_t)(chunk * kC + (vv >> 2)) * dv + (vv & 3) * 8);
+      }
+      if constexpr (GATED) dst[4] = *reinterpret_cast<const u32x4*>(gch + (size_t)chunk * kDK + 4 * (lane & 31));
+      bdst = bth[chunk * kC + lane];  // converted when stored
+    }
+  };
+  auto store_loads = [&](int buf, const u32x4 (&src)[LP::NS], uint32_t bsrc) {
+    if (wave == 4 || wave == 5) {
+      const int u = 64 * (wave - 4) + lane;
+#pragma unroll
+      for (int j = 0; j < LP::NT; ++j) {
+        bf16_t(*tile)[kLQ] = j < 8 ? sm.q[buf] : (j < 16 ? sm.k[buf] : sm.kh[GATED ? buf : 0]);
+        const int vv = u + 128 * (j & 7);
+        *reinterpret_cast<u32x4*>(&tile[vv >> 4][(vv & 15) * 8]) = src[j];
+      }
+    } else {  // wave 7
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int vv = lane + 64 * j;
+        *reinterpret_cast<u32x4*>(&sm.v[buf][vv >> 2][(vv & 3) * 8]) = src[j];
+      }
+      if constexpr (GATED) {
+        if (lane < 32) *reinterpret_cast<u32x4*>(&sm.gc[GATED ? buf : 0][4 * lane]) = src[4];
+      }
+      sm.beta[buf][lane] = bf2f((bf16_t)bsrc);
+    }
+  };
+
+  // Every role runs its own copy of the chunk loop (the same barriers, only
+  // its own registers live).  body(x, parity) runs iteration x with
+  // parity = x & 1 known at compile time, so buffer and register-slot
+  // indices are static.
+  auto run = [&](auto phase1, auto phase2) {
+    const bool loader = wave == 4 || wave == 5 || wave == 7;
+    constexpr int NSL = LP::NSLOT;
+    u32x4 pf[NSL][LP::NS];
+    uint32_t pfb[NSL] = {};
+    if (loader) {
+      issue_loads(0, pf[0], pfb[0]);
+      if (NSL == 2 && nch > 1) issue_loads(1, pf[NSL - 1], pfb[NSL - 1]);
+    }
+    auto body = [&](const int x, auto parity) {
+      constexpr int P = decltype(parity)::value;
+      constexpr int SL = NSL == 2 ? 1 - P : 0;  // slot holding chunk x+1
+      phase1(x, parity);
+      if (loader && x + 1 < nch) {
+        store_loads(1 - P, pf[SL], pfb[SL]);
+        if (x + 1 + NSL < nch) issue_loads(x + 1 + NSL, pf[SL], pfb[SL]);
+      }
+      lds_barrier();
+      phase2(x, parity);
+      lds_barrier();
+    };
+    for (int x = -1; x < nch; x += 2) {
+      body(x, std::integral_constant<int, 1>{});
+      if (x + 1 < nch) body(x + 1, std::integral_constant<int, 0>{});
+    }
+  };
+
+  if (wave < 2) {
+    // ======================= chain waves =======================
+    const int col = 16 * wave + lc;  // value column within the slice
+    floatx4 st[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      st[t] = zero4();
+      if (a.use_init) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[t][i] = Sh[(size_t)perm32(16 * t + 4 * lg + i) * dv + col];
+      }
+    }
+    floatx4 xx[4], ox[4];
+    run(
+        [&](const int x, auto parity) {
+          constexpr int P = decltype(parity)::value;
+          if (x < 0) return;
+          // Y = K S and O = Q S (shared S fragments), X = beta (V - Y); the
+          // fragments of k-step kb+1 are loaded while kb computes.
+          floatx4 y[4];
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) { y[mt] = zero4(); ox[mt] = zero4(); }
+          bf16x8 fk[2][4], fq[2][4];
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            fk[0][mt] = ld_frag(&sm.k[P][16 * mt + lc][8 * lg]);
+            fq[0][mt] = ld_frag(&sm.q[P][16 * mt + lc][8 * lg]);
+          }
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            if (kb < 3) {
+#pragma unroll
+              for (int mt = 0; mt < 4; ++mt) {
+                fk[(kb + 1) & 1][mt] = ld_frag(&sm.k[P][16 * mt + lc][32 * (kb + 1) + 8 * lg]);
+                fq[(kb + 1) & 1][mt] = ld_frag(&sm.q[P][16 * mt + lc][32 * (kb + 1) + 8 * lg]);
+              }
+            }
+            const bf16x8 b = acc_pair_to_b(st[2 * kb], st[2 * kb + 1]);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+              y[mt] = mfma_k32(fk[kb & 1][mt], b, y[mt]);
+              ox[mt] = mfma_k32(fq[kb & 1][mt], b, ox[mt]);
+            }
+          }
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            // lane (lg, lc) gets V[16 mt + 4 lg + i][col], i = 0..3
+            const shortx4_t vw =
+                ld_tr(&sm.v[P][16 * mt + 4 * lg + ((lane >> 2) & 3)][16 * wave + 4 * (lane & 3)]);
+            const float4 bt = *reinterpret_cast<const float4*>(&sm.beta[P][16 * mt + 4 * lg]);
+            xx[mt][0] = bt.x * (bf2f((bf16_t)vw[0]) - y[mt][0]);
+            xx[mt][1] = bt.y * (bf2f((bf16_t)vw[1]) - y[mt][1]);
+            xx[mt][2] = bt.z * (bf2f((bf16_t)vw[2]) - y[mt][2]);
+            xx[mt][3] = bt.w * (bf2f((bf16_t)vw[3]) - y[mt][3]);
+          }
+        },
+        [&](const int x, auto parity) {
+          constexpr int P = decltype(parity)::value;
+          if (x < 0) return;
+          auto fr16 = [&](const bf16_t* blk) {  // A operand of a transposed 16x16 block
+            return ld_tr(blk + (4 * lg + ((lane >> 2) & 3)) * 16 + 4 * (lane & 3));
+          };
+          shortx4_t fd[4], fl[6];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) fd[b] = fr16(&sm.d[b][0][0]);
+#pragma unroll
+          for (int i = 0; i < 6; ++i) fl[i] = fr16(&sm.lb[P][i][0][0]);
+          bf16x8 fa[6];
+          fa[0] = ld_frag(&sm.a[lc][8 * lg]);
+          fa[1] = ld_frag(&sm.a[16 + lc][8 * lg]);
+          fa[2] = ld_frag(&sm.a[32 + lc][8 * lg]);
+          fa[3] = ld_frag(&sm.a[32 + lc][32 + 8 * lg]);
+          fa[4] = ld_frag(&sm.a[48 + lc][8 * lg]);
+          fa[5] = ld_frag(&sm.a[48 + lc][32 + 8 * lg]);
+          // blocks L_bj stored in the order (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+          floatx4 ut[4];
+          ut[0] = mfma_k16(fd[0], acc_to_b16(xx[0]), zero4());
+          const shortx4_t u0 = acc_to_b16(ut[0]);
+          ut[1] = mfma_k16(fd[1], acc_to_b16(xx[1] - mfma_k16(fl[0], u0, zero4())), zero4());
+          const shortx4_t u1 = acc_to_b16(ut[1]);
+          ut[2] = mfma_k16(fd[2], acc_to_b16(xx[2] - mfma_k16(fl[2], u1, mfma_k16(fl[1], u0, zero4()))),
+                           zero4());
+          const shortx4_t u2 = acc_to_b16(ut[2]);
+          ut[3] = mfma_k16(
+              fd[3], acc_to_b16(xx[3] - mfma_k16(fl[5], u2, mfma_k16(fl[4], u1, mfma_k16(fl[3], u0, zero4())))),
+              zero4());
+          // K^T fragments (K^ when gated): row 16t + c of the A operand is key
+          // channel perm32(16t + c); its k-elements are the tokens of u's pairing.
+          const bf16_t(*kt)[kLQ] = GATED ? sm.kh[GATED ? P : 0] : sm.k[P];
+          const int trow = 4 * lg + ((lane >> 2) & 3);
+          auto kt_frag = [&](int t, int tok0) {
+            const int cc = 32 * (t >> 1) + 4 * (t & 1) + 8 * (lane & 3);
+            return cat_tr(ld_tr(&kt[tok0 + trow][cc]), ld_tr(&kt[tok0 + 16 + trow][cc]));
+          };
+          bf16x8 fkt[2][8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) fkt[0][t] = kt_frag(t, 0);
+          const bf16x8 u01 = acc_pair_to_b(ut[0], ut[1]);
+          const bf16x8 u23 = acc_pair_to_b(ut[2], ut[3]);
+          // O += tril(Q K^T) u
+          ox[0] = mfma_k32(fa[0], u01, ox[0]);
+          ox[1] = mfma_k32(fa[1], u01, ox[1]);
+          ox[2] = mfma_k32(fa[3], u23, mfma_k32(fa[2], u01, ox[2]));
+          ox[3] = mfma_k32(fa[5], u23, mfma_k32(fa[4], u01, ox[3]));
+#pragma unroll
+          for (int t = 0; t < 8; ++t) fkt[1][t] = kt_frag(t, 32);
+          // S += K^T u
+#pragma unroll
+          for (int t = 0; t < 8; ++t) st[t] = mfma_k32(fkt[0][t], u01, st[t]);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) st[t] = mfma_k32(fkt[1][t], u23, st[t]);
+          if constexpr (GATED) {
+            // S <- diag(Gam_C) S; accumulator rows 16t + 4lg + i are the
+            // consecutive channels perm32(16t + 4lg) + i
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              const float4 gv = *reinterpret_cast<const float4*>(&sm.gc[P][perm32(16 * t + 4 * lg)]);
+              st[t][0] *= gv.x;
+              st[t][1] *= gv.y;
+              st[t][2] *= gv.z;
+              st[t][3] *= gv.w;
+            }
+          }
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.o[16 * mt + 4 * lg + i][col] = f2bf(ox[mt][i]);
+        });
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Sh[(size_t)perm32(16 * t + 4 * lg + i) * dv + col] = st[t][i];
+  } else if (wave == 6) {
+    // ======================= D wave =======================
+    // D_b = (I + L_bb)^-1 of chunk x (phase 1): lane (block lg, column lc)
+    // solves (I + L_bb) x = e_lc by forward substitution in fp32; x is column
+    // lc of D_b, stored as row lc of D_b^T.
+    run(
+        [&](const int x, auto parity) {
+          if (x < 0) return;
+          const float* lbk = &sm.l[lg * kLB];
+          float4 lr[16][4];  // strictly-lower rows of L_bb, requested up front
+#pragma unroll
+          for (int i = 1; i < 16; ++i)
+#pragma unroll
+            for (int m4 = 0; m4 < i; m4 += 4)
+              lr[i][m4 >> 2] = *reinterpret_cast<const float4*>(lbk + i * kLR + m4);
+          float tv[16];
+#pragma unroll
+          for (int m = 0; m < 16; ++m) tv[m] = m == lc ? 1.f : 0.f;
+#pragma unroll
+          for (int i = 1; i < 16; ++i) {
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+            for (int m = 0; m < i; ++m) {
+              const float4 q4 = lr[i][m >> 2];
+              const float lv = (m & 3) == 0 ? q4.x : (m & 3) == 1 ? q4.y : (m & 3) == 2 ? q4.z : q4.w;
+              if (m & 1) s1 += lv * tv[m];
+              else s0 += lv * tv[m];
+            }
+            if (i > lc) tv[i] = -(s0 + s1);
+          }
+          u32x4 w0, w1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            w0[e] = pack2(tv[2 * e], tv[2 * e + 1]);
+            w1[e] = pack2(tv[8 + 2 * e], tv[9 + 2 * e]);
+          }
+          *reinterpret_cast<u32x4*>(&sm.d[lg][lc][0]) = w0;
+          *reinterpret_cast<u32x4*>(&sm.d[lg][lc][8]) = w1;
+        },
+        [&](const int x, auto parity) {});
+  } else if (wave == 2 || wave == 3 || wave == 7) {
+    // ======================= product waves =======================
+    // Row blocks I0..I1: tril(Q K^T) of chunk x in phase 1, L of chunk x+1
+    // in phase 2 (K^ on the right when gated).  Wave 2 row 3, wave 3 row 2,
+    // wave 7 rows 0 and 1.  All fragments of a row block are requested
+    // before its MFMAs.
+    auto prod = [&](auto i0c, auto i1c) {
+      constexpr int I0 = decltype(i0c)::value, I1 = decltype(i1c)::value;
+      run(
+          [&](const int x, auto parity) {
+            constexpr int P = decltype(parity)::value;
+            if (x < 0) return;
+            const bf16_t(*rt)[kLQ] = GATED ? sm.kh[GATED ? P : 0] : sm.k[P];
+#pragma unroll
+            for (int i = I0; i <= I1; ++i) {
+              bf16x8 fq[4], fb[4][4];
+#pragma unroll
+              for (int kb = 0; kb < 4; ++kb) fq[kb] = ld_frag(&sm.q[P][16 * i + lc][32 * kb + 8 * lg]);
+#pragma unroll
+              for (int j = 0; j <= i; ++j)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) fb[j][kb] = ld_frag(&rt[16 * j + lc][32 * kb + 8 * lg]);
+              floatx4 acc[4];
+#pragma unroll
+              for (int j = 0; j <= i; ++j) {
+                acc[j] = zero4();
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) acc[j] = mfma_k32(fq[kb], fb[j][kb], acc[j]);
+              }
+              // token columns permuted for the chain's pairing
+#pragma unroll
+              for (int j = 0; j <= i; ++j)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                  const int r = 16 * i + 4 * lg + ii, cc = 16 * j + lc;
+                  sm.a[r][perm32(cc)] = f2bf(cc <= r ? acc[j][ii] : 0.f);
+                }
+            }
+          },
+          [&](const int x, auto parity) {
+            constexpr int nb = 1 - decltype(parity)::value;  // buffer of chunk x+1
+            if (x + 1 >= nch) return;
+            const bf16_t(*rt)[kLQ] = GATED ? sm.kh[GATED ? nb : 0] : sm.k[nb];
+#pragma unroll
+            for (int i = I0; i <= I1; ++i) {
+              bf16x8 fl[4], fb[4][4];
+#pragma unroll
+              for (int j = 0; j <= i; ++j)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) fb[j][kb] = ld_frag(&rt[16 * j + lc][32 * kb + 8 * lg]);
+#pragma unroll
+              for (int kb = 0; kb < 4; ++kb)  // left operand: K (gated: Gam K)
+                fl[kb] = GATED ? ld_frag(&sm.k[nb][16 * i + lc][32 * kb + 8 * lg]) : fb[i][kb];
+              floatx4 acc[4];
+#pragma unroll
+              for (int j = 0; j <= i; ++j) {
+                acc[j] = zero4();
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) acc[j] = mfma_k32(fl[kb], fb[j][kb], acc[j]);
+              }
+              // L = diag(beta) (.): the diagonal tile's strictly-lower part in
+              // fp32 for the D wave; off-diagonal tiles bf16, transposed (the
+              // lane writes row lc, columns 4lg .. 4lg+3 of L_ij^T)
+              const float4 bt = *reinterpret_cast<const float4*>(&sm.beta[nb][16 * i + 4 * lg]);
+#pragma unroll
+              for (int j = 0; j < i; ++j) {
+                uint2 wv;
+                wv.x = pack2(bt.x * acc[j][0], bt.y * acc[j][1]);
+                wv.y = pack2(bt.z * acc[j][2], bt.w * acc[j][3]);
+                *reinterpret_cast<uint2*>(&sm.lb[nb][i * (i - 1) / 2 + j][lc][4 * lg]) = wv;
+              }
+              float* lbk = &sm.l[i * kLB];
+#pragma unroll
+              for (int ii = 0; ii < 4; ++ii) {
+                const int r = 4 * lg + ii;
+                const float bv = ii == 0 ? bt.x : ii == 1 ? bt.y : ii == 2 ? bt.z : bt.w;
+                if (lc < r) lbk[r * kLR + lc] = bv * acc[i][ii];
+              }
+            }
+          });
+    };
+    if (wave == 2) prod(std::integral_constant<int, 3>{}, std::integral_constant<int, 3>{});
+    else if (wave == 3) prod(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
+    else prod(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+  } else {
+    // ======================= output / load waves (4, 5) =======================
+    // Wave 4 writes the output tile of chunk x-1 (left in LDS by the chain
+    // waves) to memory with 16-byte stores.
+    const int sw = tid - 256;  // 0..63 on wave 4
+    auto store_o = [&](int chunk) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int vi = sw + 64 * j;
+        const int r = vi >> 2, c8 = (vi & 3) * 8;
+        *reinterpret_cast<u32x4*>(oh + (size_t)(chunk * kC + r) * dv + c8) =
+            *reinterpret_cast<const u32x4*>(&sm.o[r][c8]);
+      }
+    };
+    run([&](const int x, auto parity) {
+          if (wave == 4 && x >= 1) store_o(x - 1);
+        },
+        [&](const int x, auto parity) {});
+    if (wave == 4) store_o(nch - 1);
+  }
+}
+
+// Gate pre-pass: for each (batch, head, chunk) and key channel d, the
+// cumulative log-decay G_t = sum_{s<=t} g_s over the chunk (fp32), then
+// Gam Q, Gam K, K / Gam in bf16 and Gam_C = e^{G_63}.  One workgroup of 256
+// threads per chunk: thread (w, l) holds channels 2l, 2l+1 of tokens
+// 16w .. 16w+15; the four waves' partial sums are combined through LDS.
+__global__ __launch_bounds__(256) void gate_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                 const bf16_t* __restrict__ g, bf16_t* __restrict__ qt,
+                                                 bf16_t* __restrict__ kt, bf16_t* __restrict__ kht,
+                                                 float* __restrict__ gcum, int nch) {
+  __shared__ float2 part[4][64];
+  const int chunk = blockIdx.x;  // over B*H*nch
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const size_t base = (size_t)chunk * kC * kDK;
+  const uint32_t* g2 = reinterpret_cast<const uint32_t*>(g + base);
+  uint32_t gw[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) gw[t] = g2[(16 * w + t) * (kDK / 2) + l];
+  float2 run = make_float2(0.f, 0.f);
+  float2 gl[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    run.x += bf2f((bf16_t)(gw[t] & 0xffffu));
+    run.y += bf2f((bf16_t)(gw[t] >> 16));
+    gl[t] = run;
+  }
+  part[w][l] = run;
+  __syncthreads();
+  float2 off = make_float2(0.f, 0.f), tot = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float2 x = part[p][l];
+    if (p < w) { off.x += x.x; off.y += x.y; }
+    tot.x += x.x;
+    tot.y += x.y;
+  }
+  if (w == 0) reinterpret_cast<float2*>(gcum + (size_t)chunk * kDK)[l] = make_float2(__expf(tot.x), __expf(tot.y));
+  const uint32_t* q2 = reinterpret_cast<const uint32_t*>(q + base);
+  const uint32_t* k2 = reinterpret_cast<const uint32_t*>(k + base);
+  uint32_t* qt2 = reinterpret_cast<uint32_t*>(qt + base);
+  uint32_t* kt2 = reinterpret_cast<uint32_t*>(kt + base);
+  uint32_t* kh2 = reinterpret_cast<uint32_t*>(kht + base);
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int idx = (16 * w + t) * (kDK / 2) + l;
+    const uint32_t qw = q2[idx], kw = k2[idx];
+    const float G0 = off.x + gl[t].x, G1 = off.y + gl[t].y;
+    const float e0 = __expf(G0), e1 = __expf(G1), r0 = __expf(-G0), r1 = __expf(-G1);
+    const float q0 = bf2f((bf16_t)(qw & 0xffffu)), q1 = bf2f((bf16_t)(qw >> 16));
+    const float k0 = bf2f((bf16_t)(kw & 0xffffu)), k1 = bf2f((bf16_t)(kw >> 16));
+    qt2[idx] = pack2(q0 * e0, q1 * e1);
+    kt2[idx] = pack2(k0 * e0, k1 * e1);
+    kh2[idx] = pack2(k0 * r0, k1 * r1);
+  }
+}
+
+}  // namespace
+
+size_t gated_pipe_workspace_bytes(const PrefillArgs& a) {
+  const size_t n = (size_t)a.B * a.H * a.T * kDK;
+  return 3 * n * sizeof(bf16_t) + (size_t)a.B * a.H * (a.T / kC) * kDK * sizeof(float);
+}
+
+hipError_t launch_prefill_pipe2(const PrefillArgs& a, void* workspace, hipStream_t st) {
+  const long blocks = (long)a.B * a.H * (a.dv / kDVS);
+  PipeArgs p;
+  p.v = reinterpret_cast<const bf16_t*>(a.v);
+  p.beta = reinterpret_cast<const bf16_t*>(a.beta);
+  p.o = reinterpret_cast<bf16_t*>(a.o);
+  p.S = a.S;
+  p.T = a.T;
+  p.dv = a.dv;
+  p.use_init = a.use_init;
+  if (a.g == nullptr) {
+    p.q = reinterpret_cast<const bf16_t*>(a.q);
+    p.k = reinterpret_cast<const bf16_t*>(a.k);
+    p.kh = nullptr;
+    p.gc = nullptr;
+    hipLaunchKernelGGL(prefill_pipe2<false>, dim3((unsigned)blocks), dim3(kThreads), 0, st, p);
+    return hipGetLastError();
+  }
+  const size_t n = (size_t)a.B * a.H * a.T * kDK;
+  bf16_t* qt = reinterpret_cast<bf16_t*>(workspace);
+  bf16_t* kt = qt + n;
+  bf16_t* kht = kt + n;
+  float* gcum = reinterpret_cast<float*>(kht + n);
+  const int nch = a.T / kC;
+  hipLaunchKernelGGL(gate_prep, dim3((unsigned)(a.B * a.H * nch)), dim3(256), 0, st,
+                     reinterpret_cast<const bf16_t*>(a.q), reinterpret_cast<const bf16_t*>(a.k),
+                     reinterpret_cast<const bf16_t*>(a.g), qt, kt, kht, gcum, nch);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  p.q = qt;
+  p.k = kt;
+  p.kh = kht;
+  p.gc = gcum;
+  hipLaunchKernelGGL(prefill_pipe2<true>, dim3((unsigned)blocks), dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace linattn
