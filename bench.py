@@ -242,6 +242,117 @@ def bench_decode(la, workloads, torch, steps=1000, warmup=10):
     return w, inp, ev0.elapsed_time(ev1) / 1e3
 
 
+def _time_launches(torch, stream, run, sets, n, warmup=3):
+    """Average and median duration of `n` launches of run(set), each between
+    its own pair of HIP events on `stream`; the input sets are cycled."""
+    for i in range(warmup):
+        run(sets[i % len(sets)])
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        run(sets[i % len(sets)])
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return sum(ms) / n * 1e3, ms[n // 2] * 1e3
+
+
+def _row(name, workload, us, med_us, nbytes, note=None):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    r = {"workload": workload, "avg_launch_us": us, "median_launch_us": med_us,
+         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes}}
+    if note:
+        r["note"] = note
+    return name, r
+
+
+def bench_rows(la, workloads, torch, launches=20):
+    """The remaining rows of the path, each timed on its own workload: linear
+    attention prefill (fp32 and bf16), the gated delta-rule prefill, and the
+    linear-attention and gated decode steps at the decode workload's shape."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    rows = {}
+    W = workloads.WORKLOADS
+    for w in (W[0], W[1]):
+        inp = workloads.make_workload(w)
+        per = w.B * w.H * (w.T * 2 * (w.dk + w.dv) * (4 if w.dtype == torch.float32 else 2)
+                           + (w.dk * w.dv + w.dk) * 4)
+        copies = max(1, min(8, -(-600_000_000 // per)))
+        sets = []
+        for _ in range(copies):
+            d = {k: v.to(dev) for k, v in inp.items()}
+            d["o"] = torch.empty_like(d["v"])
+            d["S"] = torch.empty(w.B, w.H, w.dk, w.dv, device=dev, dtype=torch.float32)
+            d["z"] = torch.empty(w.B, w.H, w.dk, device=dev, dtype=torch.float32)
+            sets.append(d)
+
+        def run(d):
+            la.la_prefill(d["q"], d["k"], d["v"], S=d["S"], z=d["z"], o=d["o"], stream=stream)
+
+        us, med = _time_launches(torch, stream, run, sets, launches)
+        name, r = _row("la_prefill", f"la_prefill {w.name}, {copies} input copies cycled",
+                       us, med, per,
+                       "latency-bound: one 64-token chunk" if w.T == 64 else None)
+        rows[f"{name}_{w.name}"] = r
+        del sets
+    w = W[3]
+    inp = workloads.make_workload(w)
+    d = {k: v.to(dev) for k, v in inp.items()}
+    d["o"] = torch.empty_like(d["v"])
+    d["S"] = torch.empty(w.B, w.H, w.dk, w.dv, device=dev, dtype=torch.float32)
+    del inp
+
+    def run_g(d):
+        la.deltanet_prefill(d["q"], d["k"], d["v"], d["beta"], g=d["g"], S=d["S"], o=d["o"],
+                            stream=stream)
+
+    us, med = _time_launches(torch, stream, run_g, [d], max(3, launches // 4), warmup=1)
+    per = w.B * w.H * (w.T * 2 * (3 * w.dk + 2 * w.dv + 1) + w.dk * w.dv * 4)
+    name, r = _row("deltanet_prefill_gated", f"deltanet_prefill (gated) {w.name}", us, med, per,
+                   "serial chain over 512 chunks; 32 heads x 4 value slices = 128 workgroups")
+    rows[name] = r
+    del d
+    wd = W[4]
+    N, H, dk, dv = wd.B, wd.H, wd.dk, wd.dv
+    li = workloads.make_la_decode(N, H, dk, dv, wd.dtype, seed=77)
+    d = {k: v.to(dev) for k, v in li.items()}
+    o = torch.empty(N, H, dv, device=dev, dtype=wd.dtype)
+    ring = d["q"].shape[0]
+    cnt = [0]
+
+    def run_ld(_):
+        s = cnt[0] % ring
+        cnt[0] += 1
+        la.la_decode_step(d["q"][s], d["k"][s], d["v"][s], d["S0"], d["z0"], o=o, stream=stream)
+
+    us, med = _time_launches(torch, stream, run_ld, [None], 200, warmup=10)
+    per = N * H * (2 * (dk * dv + dk) * 4 + 2 * (2 * dk + 2 * dv))
+    name, r = _row("la_decode_step", f"la_decode_step N={N} H={H} dk=dv={dk}, fp32 S and z "
+                   "in place", us, med, per)
+    rows[name] = r
+    del d, li
+    gi = workloads.make_decode(N, H, dk, dv, wd.dtype, seed=78, gated=True)
+    d = {k: v.to(dev) for k, v in gi.items()}
+    cnt[0] = 0
+
+    def run_gd(_):
+        s = cnt[0] % ring
+        cnt[0] += 1
+        la.deltanet_decode_step(d["q"][s], d["k"][s], d["v"][s], d["beta"][s], d["S0"],
+                                g=d["g"][s], o=o, stream=stream)
+
+    us, med = _time_launches(torch, stream, run_gd, [None], 200, warmup=10)
+    per = N * H * (2 * dk * dv * 4 + 2 * (3 * dk + 2 * dv + 1))
+    name, r = _row("deltanet_decode_step_gated", f"deltanet_decode_step (gated) N={N} H={H} "
+                   f"dk=dv={dk}, fp32 state in place", us, med, per)
+    rows[name] = r
+    return rows
+
+
 def copy_probe(torch, nbytes=1 << 30, reps=5):
     """A plain device copy of known size (used to calibrate HBM counters)."""
     dev = torch.device("cuda:0")
@@ -300,7 +411,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the other rows (LA prefill, gated prefill, LA/gated decode)")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy", "rows"], default="all",
                     help="run one part only (for profiler runs)")
     ap.add_argument("--summarize", metavar="DIR",
                     help="write profiles/*.txt from rocprofv3 output under DIR and exit")
@@ -327,6 +440,9 @@ def main():
     if args.only == "copy":
         n = copy_probe(torch)
         print(json.dumps({"copy_probe_bytes": n}))
+        return
+    if args.only == "rows":
+        print(json.dumps(bench_rows(la, workloads, torch)))
         return
     if args.only == "decode":
         wd, _, el = bench_decode(la, workloads, torch, args.decode_steps)
@@ -383,6 +499,8 @@ def main():
                          "avg_launch_us": el / args.decode_steps * 1e6,
                          "algorithmic_bytes_per_launch": dbytes},
         }
+        if not args.no_rows:
+            line["rows"] = bench_rows(la, workloads, torch)
         if not args.no_cpu_baseline:
             import oracle
             line["cpu_baseline"] = cpu_baseline(workloads, oracle, torch, pinp, w, dinp, wd)
