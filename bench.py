@@ -40,11 +40,25 @@ PREFILL_SOURCES = [_CSRC + "prefill_pipe.hip", _CSRC + "device_common.hpp", _CSR
 DECODE_SOURCES = [_CSRC + "decode.hip", _CSRC + "device_common.hpp", _CSRC + "launch.hpp"]
 # Symbol substrings of the two timed kernels (as rocprofv3 lists them) and the
 # profile summaries that record their counters.
-PREFILL_KERNEL = "prefill_delta_pipe"
+PREFILL_KERNEL = "prefill_pipe<false, 32>"
 DECODE_KERNEL = "decode_kernel<128, 128, linattn::BF16, 0"
-PREFILL_PROFILE = "prefill_delta_pipe_B4_H16_T4096_d128.txt"
+PREFILL_PROFILE = "prefill_pipe_delta_B4_H16_T4096_d128.txt"
 DECODE_PROFILE = "decode_kernel_delta_N256_H32_d128.txt"
 COPY_KERNEL = "copyBuffer"
+# (summary file, workload, kernel-name substrings) of the rows timed by bench_rows
+ROW_PROFILES = [
+    ("prefill_pipe_gated_B1_H32_T32768_d128.txt",
+     "gated deltanet_prefill B=1 H=32 T=32768 dk=dv=128 bf16: gate pre-pass + pipelined kernel",
+     ["gate_prep", "prefill_pipe<true, 16>"]),
+    ("prefill_kernel_la_B8_H12_T1024_d64.txt", "la_prefill B=8 H=12 T=1024 dk=dv=64 bf16",
+     ["prefill_kernel<64, linattn::BF16, 0, 32>"]),
+    ("prefill_kernel_la_fp32_B1_H2_T64_d16.txt", "la_prefill B=1 H=2 T=64 dk=dv=16 fp32",
+     ["prefill_kernel<16, linattn::F32, 0, 16>"]),
+    ("decode_kernel_la_N256_H32_d128.txt", "la_decode_step N=256 H=32 dk=dv=128, fp32 S and z",
+     ["decode_kernel<128, 128, linattn::BF16, 2"]),
+    ("decode_kernel_gated_N256_H32_d128.txt", "gated deltanet_decode_step N=256 H=32 dk=dv=128",
+     ["decode_kernel<128, 128, linattn::BF16, 1"]),
+]
 
 
 def prefill_algorithmic(B, H, T, dk, dv, in_bytes=2):
@@ -178,6 +192,22 @@ def summarize(prof_dir):
         os.makedirs(PROFILES, exist_ok=True)
         with open(os.path.join(PROFILES, fname), "w") as f:
             f.write("\n".join(lines) + "\n")
+        print(f"wrote profiles/{fname}")
+    # the other rows: kernel-trace figures only (same trace run)
+    for fname, wl, kernels in ROW_PROFILES:
+        lines = [f"# rocprofv3 kernel-trace summary: {wl}",
+                 "# $R is the repository root; the command runs committed files only.",
+                 f"# command: {trace_cmd}", ""]
+        for kname in kernels:
+            row = [r for r in stats if kname in r["Name"]]
+            if len(row) != 1:
+                raise SystemExit(f"expected one kernel-trace row for '{kname}', found {len(row)}")
+            row = row[0]
+            lines += [f"kernel: {row['Name']}", f"calls: {row['Calls']}",
+                      f"average_ns: {float(row['AverageNs']):.0f}",
+                      f"min_ns: {float(row['MinNs']):.0f}", f"max_ns: {float(row['MaxNs']):.0f}", ""]
+        with open(os.path.join(PROFILES, fname), "w") as f:
+            f.write("\n".join(lines))
         print(f"wrote profiles/{fname}")
 
 

@@ -41,7 +41,7 @@ const char* la_strerror(int code) {
     case LA_ERR_UNSUPPORTED_DIM:
       return "unsupported head dimension: dk and dv must each be 16, 32, 64 or 128 "
              "(float32 gated prefill: dk <= 64)";
-    case LA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case LA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch or a workspace allocation";
     case LA_ERR_ALIGN:
       return "q, k and v (prefill) and S (decode) must be 16-byte aligned";
     default: return "unknown error code";

@@ -37,11 +37,10 @@ struct PrefillArgs {
 hipError_t launch_decode(int kind, int bf16, int dk, int dv, const DecodeArgs& a,
                          hipStream_t st);
 hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, hipStream_t st);
-// The software-pipelined delta-rule prefill: bf16, dk = 128, dv % 32 == 0.
-hipError_t launch_prefill_pipe(const PrefillArgs& a, hipStream_t st);
-// The pipelined prefill with the gate (a.g != NULL; needs a workspace of
-// gated_pipe_workspace_bytes(a) bytes) or without it (no workspace).
+// The software-pipelined delta-rule prefill for bf16, dk = 128, dv % 32 == 0:
+// plain (a.g == NULL, no workspace) or gated (needs a workspace of
+// gated_pipe_workspace_bytes(a) bytes).
 size_t gated_pipe_workspace_bytes(const PrefillArgs& a);
-hipError_t launch_prefill_pipe2(const PrefillArgs& a, void* workspace, hipStream_t st);
+hipError_t launch_prefill_pipe(const PrefillArgs& a, void* workspace, hipStream_t st);
 
 }  // namespace linattn

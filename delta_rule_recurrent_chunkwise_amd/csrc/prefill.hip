@@ -138,31 +138,84 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   }
 
   const int nchunks = Tn / kC;
+
+  // Non-gated modes: the chunk's q, k and v-slice vectors (and beta) are
+  // loaded into registers one chunk ahead, so their latency overlaps the
+  // previous chunk's work.  Thread tid owns vectors tid + kThreads j of the
+  // chunk (q, then k, then v); every thread issues every load (a vector past
+  // the end re-reads vector 0 and is not stored).
+  constexpr int VPRQ = DK / kVec;          // 16-byte vectors per q/k row
+  constexpr int NQV = kC * VPRQ;
+  constexpr int VPRS = DVS / kVec;         // per row of the v slice
+  constexpr int NTOT = 2 * NQV + kC * VPRS;
+  constexpr int NPT = (NTOT + kThreads - 1) / kThreads;
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));  // a register array of
+  u32x4v pre[MODE == PF_GATED ? 1 : NPT];                        // structs would go to memory
+  float preb = 0.f;
+  auto prefetch = [&](int c) {
+    if constexpr (MODE != PF_GATED) {
+      const T* const pq = qh;
+      const T* const pk = kh;
+      const T* const pv = vh;
+#pragma unroll
+      for (int j = 0; j < NPT; ++j) {
+        const int i0 = tid + kThreads * j;
+        const int i = i0 < NTOT ? i0 : 0;
+        const T* src;
+        if (i < 2 * NQV) {
+          const int ii = i < NQV ? i : i - NQV;
+          src = (i < NQV ? pq : pk) + (size_t)(c * kC + ii / VPRQ) * DK + (ii % VPRQ) * kVec;
+        } else {
+          const int ii = i - 2 * NQV;
+          src = pv + (size_t)(c * kC + ii / VPRS) * dv + (ii % VPRS) * kVec;
+        }
+        pre[j] = *reinterpret_cast<const u32x4v*>(src);
+      }
+      if (MODE != PF_LA && tid < kC) preb = E::ld(bth + c * kC + tid);
+    }
+  };
+  prefetch(0);
+
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = c * kC;
     __syncthreads();  // the previous chunk's readers of LDS are done
 
     // ---------------- stage the chunk in LDS ----------------
     if (MODE != PF_GATED) {
-      constexpr int VPR = DK / kVec;
-      for (int i = tid; i < kC * VPR; i += kThreads) {
-        const int r = i / VPR, cv = i - (i / VPR) * VPR;
-        VecU<E> qv, kv;
-        qv.v = *reinterpret_cast<const Vec16*>(qh + (size_t)(t0 + r) * DK + cv * kVec);
-        kv.v = *reinterpret_cast<const Vec16*>(kh + (size_t)(t0 + r) * DK + cv * kVec);
+#pragma unroll
+      for (int j = 0; j < NPT; ++j) {
+        const int i = tid + kThreads * j;
+        if (i >= NTOT) continue;
+        if (i >= 2 * NQV) {  // v slice, stored transposed
+          const int ii = i - 2 * NQV;
+          const int r = ii / VPRS, cv = ii % VPRS;
+          VecU<E> vv;
+          vv.v = __builtin_bit_cast(Vec16, pre[j]);
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) sVt[(cv * kVec + e) * LKT + r] = vv.e[e];
+          continue;
+        }
+        const bool isq = i < NQV;
+        const int ii = isq ? i : i - NQV;
+        const int r = ii / VPRQ, cv = ii % VPRQ;
+        VecU<E> xv;
+        xv.v = __builtin_bit_cast(Vec16, pre[j]);
         if (MODE == PF_LA) {
 #pragma unroll
-          for (int e = 0; e < kVec; ++e) {
-            qv.e[e] = E::cvt(phi_elu1(E::tof(qv.e[e])));
-            kv.e[e] = E::cvt(phi_elu1(E::tof(kv.e[e])));
-          }
+          for (int e = 0; e < kVec; ++e) xv.e[e] = E::cvt(phi_elu1(E::tof(xv.e[e])));
         }
-        *reinterpret_cast<Vec16*>(sQ + r * LQ + cv * kVec) = qv.v;
-        *reinterpret_cast<Vec16*>(sK + r * LQ + cv * kVec) = kv.v;
+        if (isq) {
+          *reinterpret_cast<Vec16*>(sQ + r * LQ + cv * kVec) = xv.v;
+        } else {
+          *reinterpret_cast<Vec16*>(sK + r * LQ + cv * kVec) = xv.v;
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) sKt[(cv * kVec + e) * LKT + r] = kv.e[e];
+          for (int e = 0; e < kVec; ++e) sKt[(cv * kVec + e) * LKT + r] = xv.e[e];
+        }
       }
-    } else {
+      if (MODE != PF_LA && tid < kC) sRow[tid] = preb;
+      if (c + 1 < nchunks) prefetch(c + 1);
+    }
+    if (MODE == PF_GATED) {
       // cumulative log-decay per key channel over the chunk, then the scaled
       // operands Q~ = Gam Q, K~ = Gam K, K^ = K / Gam, (K Gam_C / Gam)^T
       constexpr int NP = kThreads / DK;  // token parts
@@ -199,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         sKt[d * LKT + r] = E::cvt(kv * dec);
       }
     }
-    {
+    if (MODE == PF_GATED) {
       constexpr int VPRV = DVS / kVec;
       for (int i = tid; i < kC * VPRV; i += kThreads) {
         const int r = i / VPRV, cv = i - (i / VPRV) * VPRV;
@@ -264,16 +317,45 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 
     if (MODE == PF_LA) {
       // denominators phi(Q) z + rowsum(tril(phi(Q) phi(K)^T)), then z += sum phi(k)
+      // (lane = row r; 16-byte row reads of phi(Q), tril(.) and phi(K)^T)
       if (wave == NCW) {
-        float den = 0.f;
-        for (int d = 0; d < DK; ++d) den += E::tof(sQ[lane * LQ + d]) * sVec[d];
-        for (int cidx = 0; cidx < kC; ++cidx) den += E::tof(sA[lane * LKT + cidx]);
-        sRow[lane] = den;
-        for (int d = lane; d < DK; d += 64) {
-          float zs = 0.f;
-          for (int r = 0; r < kC; ++r) zs += E::tof(sK[r * LQ + d]);
-          sVec[d] += zs;
+        float den0 = 0.f, den1 = 0.f;
+#pragma unroll
+        for (int d8 = 0; d8 < DK; d8 += kVec) {
+          VecU<E> x;
+          x.v = *reinterpret_cast<const Vec16*>(sQ + lane * LQ + d8);
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) den0 += E::tof(x.e[e]) * sVec[d8 + e];
         }
+#pragma unroll
+        for (int c8 = 0; c8 < kC; c8 += kVec) {
+          VecU<E> x;
+          x.v = *reinterpret_cast<const Vec16*>(sA + lane * LKT + c8);
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) den1 += E::tof(x.e[e]);
+        }
+        float zs[DK > 64 ? 2 : 1];
+#pragma unroll
+        for (int h = 0; h * 64 < DK; ++h) {
+          const int d = lane + 64 * h;
+          float acc = 0.f;
+          if (d < DK) {
+#pragma unroll
+            for (int r8 = 0; r8 < kC; r8 += kVec) {
+              VecU<E> x;
+              x.v = *reinterpret_cast<const Vec16*>(sKt + d * LKT + r8);
+#pragma unroll
+              for (int e = 0; e < kVec; ++e) acc += E::tof(x.e[e]);
+            }
+          }
+          zs[h] = acc;
+        }
+        // every lane has read z (sVec) before it is updated: one wave, LDS
+        // operations in program order
+        sRow[lane] = den0 + den1;
+#pragma unroll
+        for (int h = 0; h * 64 < DK; ++h)
+          if (lane + 64 * h < DK) sVec[lane + 64 * h] += zs[h];
       }
       __syncthreads();
     } else {
@@ -434,14 +516,14 @@ static hipError_t launch_prefill_e(int dk, const PrefillArgs& a, hipStream_t st)
 
 hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, hipStream_t st) {
   if (bf16 && dk == 128 && a.dv % 32 == 0) {
-    if (mode == PF_DELTA) return launch_prefill_pipe(a, st);
+    if (mode == PF_DELTA) return launch_prefill_pipe(a, nullptr, st);
     if (mode == PF_GATED) {
       // the gate pre-pass writes Gam Q, Gam K, K / Gam and Gam_C to a
       // stream-ordered workspace that is released after the main kernel
       void* ws = nullptr;
       hipError_t e = hipMallocAsync(&ws, gated_pipe_workspace_bytes(a), st);
       if (e != hipSuccess) return e;
-      e = launch_prefill_pipe2(a, ws, st);
+      e = launch_prefill_pipe(a, ws, st);
       const hipError_t f = hipFreeAsync(ws, st);
       return e != hipSuccess ? e : f;
     }

@@ -1,48 +1,54 @@
-// prefill_pipe.hip -- software-pipelined chunkwise delta-rule prefill for
-// bf16 inputs with dk = 128 and dv a multiple of 32 (the throughput path).
+// prefill_pipe.hip -- software-pipelined chunkwise delta-rule prefill, plain
+// and with a per-key-channel gate, for bf16 inputs with dk = 128 and dv a
+// multiple of 32.
 //
-// The arithmetic is that of the article "From GPT-2 to Kimi K3, explained",
-// section "DeltaNet (Parallelizing Linear Transformers with Delta Rule)":
-// per 64-token chunk, with L = tril(diag(beta) K K^T, -1) and T = (I + L)^-1,
-//   u = T diag(beta) (V - K S),   O = Q S + tril(Q K^T) u,   S <- S + K^T u.
-// It is the same computation as prefill.hip; this kernel only organises it
-// for throughput on one CU.  T is never formed: with I + L split into 16x16
-// token blocks, u is obtained by block forward substitution,
-//   u_b = D_b (X_b - sum_{j<b} L_bj u_j),   D_b = (I + L_bb)^-1,
-// where X = diag(beta) (V - K S).
+// Arithmetic (article "From GPT-2 to Kimi K3, explained"):
+//  * section "DeltaNet (Parallelizing Linear Transformers with Delta Rule)":
+//    per 64-token chunk, with L = tril(diag(beta) K K^T, -1),
+//      u = (I + L)^-1 diag(beta) (V - K S),  O = Q S + tril(Q K^T) u,
+//      S <- S + K^T u.
+//  * sections "Gated Delta Net" and "KDA / Kimi Linear": a decay a_t[i] per
+//    key channel scales row i of S before each read.  With the decay
+//    accumulated from the chunk start, Gam_t = prod_{s<=t} a_s, the same
+//    form holds with K~ = Gam K, K^ = K / Gam, Q~ = Gam Q (row-wise):
+//      L = tril(diag(beta) K~ K^^T, -1),  u = (I + L)^-1 diag(beta) (V - K~ S),
+//      O = Q~ S + tril(Q~ K^^T) u,  S <- diag(Gam_C) (S + K^^T u),
+//    since (K Gam_C / Gam)^T u = diag(Gam_C) K^^T u.  A pre-pass (gate_prep
+//    below) forms K~, K^, Q~ and Gam_C for every chunk; the main kernel is
+//    the plain one with K~ in place of K on the left of every product, K^ on
+//    the right, and the row scaling by Gam_C.
+//
+// (I + L)^-1 is never formed: with I + L cut into 16x16 token blocks, u is
+// obtained by block forward substitution,
+//   u_b = D_b (X_b - sum_{j<b} L_bj u_j),   D_b = (I + L_bb)^-1.
 //
 // Work split inside a workgroup (8 waves; one (batch, head) and 32 value
-// columns per workgroup):
-//   waves 0-1  "chain": each keeps S[:, 16 columns] in MFMA accumulators and
-//              runs only the S-dependent products of chunk c.
-//   waves 2,3,7 products of chunk c+1: K K^T (giving L) in phase 1 and
-//              tril(Q K^T) in phase 2.
-//   wave 6     the diagonal-block inverses D_b of chunk c+1 by fp32 forward
-//              substitution (one lane per column; phase 2).
-//   wave 4     writes the output tile of chunk c-1 to memory (phase 1).
-//   waves 2-7  the global loads of q, k and the v slice, issued three
-//              chunks ahead into registers and written to LDS two chunks
-//              ahead.
-// Each iteration has two phases separated by LDS-only barriers, so global
-// loads stay in flight across them.
+// columns per workgroup).  Iteration x has two phases, each closed by an
+// LDS-only barrier:
+//   waves 0-1    "chain": each keeps S[:, 16 columns] in MFMA accumulators.
+//                Phase 1: Y = K S, O = Q S, X = beta (V - Y) for chunk x.
+//                Phase 2: u, O += tril(Q K^T) u, S += K^T u for chunk x.
+//   waves 2,3,7  products.  Phase 1: tril(Q K^T) of chunk x.  Phase 2: L of
+//                chunk x+1 (diagonal blocks fp32, the others bf16).
+//   wave 6       D_b of chunk x from L's diagonal blocks (phase 1).
+//   wave 4       writes the output tile of chunk x-1 to memory (phase 1).
+//   loaders      write chunk x+1 to LDS in phase 1 of iteration x and issue
+//                the global loads of chunk x+3 into the freed registers.
+// Chunk y lives in LDS buffer y & 1: it is written in phase 1 of iteration
+// y-1 and last read in phase 2 of iteration y.
 //
-// Index conventions.  K, Q and the v slice are stored row-major (tokens x
-// channels) in natural column order.  The chain's 32-deep MFMA pairs two
-// accumulator tiles; the k-index order that pairing implies is absorbed by a
-// fixed permutation of S's rows: the accumulator row rho = 32b + 16h + 4g + i
-// of a chain wave holds logical key channel d = 32b + 8g + 4h + i (perm32
-// below).  tril(Q K^T), used as an A operand against paired tiles over
-// tokens, stores its token columns permuted the same way, so each of its
-// fragments is one 16-byte LDS read.  The transposed operands K^T (for
-// S += K^T u) and the accumulator-layout V are read straight from the
-// row-major tiles with the LDS transpose read (ds_read_b64_tr_b16): lane
-// 16G + 4a + b receives element b of the 8-byte runs addressed by lanes
-// 16G + a + 4e, e = 0..3.  The 16x16 blocks D_b and L_bj are stored
-// transposed (16 bf16 per row, unpadded) and read the same way as the A
-// operands of the 16-deep MFMA.
-//
-// Row strides are 8 (mod 32) dwords: 16-byte fragment reads of 16 rows and
-// transpose reads of 4-8 rows then fall in distinct LDS banks.
+// Index conventions.  Q, K (and K^) and the v slice are stored row-major
+// (tokens x channels).  The chain's 32-deep MFMA pairs two accumulator
+// tiles; the k-index order of that pairing is absorbed by a fixed
+// permutation of S's rows: accumulator row rho = 32b + 16h + 4g + i of a
+// chain wave holds key channel perm32(rho) = 32b + 8g + 4h + i.
+// tril(Q K^T), an A operand against paired tiles over tokens, stores its
+// token columns permuted the same way.  K^T (for S += K^T u), V in
+// accumulator layout, and the 16x16 blocks D_b, L_bj (stored transposed) are
+// read with the LDS transpose read ds_read_b64_tr_b16: lane 16G + 4a + b
+// receives element b of the 8-byte runs addressed by lanes 16G + a + 4e,
+// e = 0..3.  Row strides are 8 (mod 32) dwords, which keeps 16-byte fragment
+// reads of 16 rows and transpose reads of 4-8 rows in distinct LDS banks.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -53,34 +59,40 @@ namespace {
 
 constexpr int kC = 64;
 constexpr int kDK = 128;
-constexpr int kDVS = 32;
 constexpr int kThreads = 512;
 
-constexpr int kLQ = kDK + 16;  // bf16 row stride of q, k (72 dwords)
-constexpr int kLT = kC + 16;   // bf16 row stride of tril(QK^T) (40 dwords)
-constexpr int kLV = kDVS + 16; // bf16 row stride of the v slice (24 dwords)
-constexpr int kLL = kC + 4;    // fp32 row stride of L (diagonal blocks)
-constexpr int kLO = kDVS + 8;  // bf16 row stride of the output tile
+constexpr int kLQ = kDK + 16;   // bf16 row stride of q, k, k^ (72 dwords)
+constexpr int kLT = kC + 16;    // bf16 row stride of tril(QK^T) (40 dwords)
+constexpr int kLR = 20;         // fp32 row stride inside a diagonal block of L
+constexpr int kLB = 16 * kLR + 16;  // fp32 stride between diagonal blocks
 
-struct __attribute__((aligned(16))) Smem {
-  bf16_t q[2][kC][kLQ];
-  bf16_t k[3][kC][kLQ];    // chunk x in buffer x mod 3: K(c) is read in both phases
-  bf16_t a[2][kC][kLT];
-  bf16_t lb[2][6][16][16]; // off-diagonal blocks L_bj (b > j), transposed
-  bf16_t d[2][4][16][16];  // diagonal-block inverses D_b, transposed
-  bf16_t v[2][kC][kLV];    // the v slice, row-major
-  bf16_t o[kC][kLO];       // output tile of one chunk
-  float l[kC][kLL];
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short shortx4_t __attribute__((ext_vector_type(4)));
+
+// DVS: value columns per workgroup (32, or 16 when there are too few
+// (batch, head) pairs to fill the GPU with 32-column slices).
+template <bool GATED, int DVS>
+struct __attribute__((aligned(16))) Smem2 {
+  static constexpr int kLV = DVS + 16;  // bf16 row stride of the v slice
+  static constexpr int kLO = DVS + 8;   // bf16 row stride of the output tile
+  static constexpr int NKH = GATED ? 2 : 1;
+  static constexpr int RKH = GATED ? kC : 1;
+  bf16_t q[2][kC][kLQ];       // Q (gated: Gam Q)
+  bf16_t k[2][kC][kLQ];       // K (gated: Gam K)
+  bf16_t kh[NKH][RKH][kLQ];   // gated: K / Gam
+  bf16_t a[kC][kLT];          // tril(Q K^T), token columns permuted
+  bf16_t lb[2][6][16][16];    // L_bj (b > j), transposed
+  bf16_t d[4][16][16];        // D_b, transposed
+  bf16_t v[2][kC][kLV];       // v slice
+  bf16_t o[kC][kLO];          // output tile
+  float l[4 * kLB];           // diagonal blocks of L (strictly lower parts)
   float beta[2][kC];
+  float gc[NKH][kDK];         // gated: Gam_C per key channel
 };
 
 // 32b + 16h + 4g + i  ->  32b + 8g + 4h + i
 __device__ __forceinline__ int perm32(int x) {
   return (x & ~31) | (((x >> 2) & 3) << 3) | (((x >> 4) & 1) << 2) | (x & 3);
-}
-// inverse: 32b + 8g + 4h + i  ->  32b + 16h + 4g + i
-__device__ __forceinline__ int perm32_inv(int x) {
-  return (x & ~31) | (((x >> 2) & 1) << 4) | (((x >> 3) & 3) << 2) | (x & 3);
 }
 
 __device__ __forceinline__ void lds_barrier() {
@@ -89,25 +101,19 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__device__ __forceinline__ int mod3(int x) { return (x + 3) % 3; }  // x >= -3
-
+// Consecutive logical workgroups (the dv slices of one head, which read the
+// same q and k) go to one XCD, so they share its L2.
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
   if (n % 8 != 0) return bid;
   return (bid % 8) * (n / 8) + bid / 8;
 }
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ bf16x8 ld_frag(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
-
-typedef short shortx4_t __attribute__((ext_vector_type(4)));
-// LDS transpose read of four bf16 (see the index conventions above).
 __device__ __forceinline__ shortx4_t ld_tr(const bf16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) shortx4_t*)(
-          (__attribute__((address_space(3))) bf16_t*)(p)));
+      (__attribute__((address_space(3))) shortx4_t*)((__attribute__((address_space(3))) bf16_t*)(p)));
 }
 __device__ __forceinline__ bf16x8 cat_tr(shortx4_t lo, shortx4_t hi) {
   typedef short shortx8_t __attribute__((ext_vector_type(8)));
@@ -115,12 +121,57 @@ __device__ __forceinline__ bf16x8 cat_tr(shortx4_t lo, shortx4_t hi) {
   return __builtin_bit_cast(bf16x8, x);
 }
 
-// 16x16 fp32 accumulator tile used as a 16-deep bf16 MFMA operand.  As B it
-// is the tile itself; as A it is the tile's transpose.
-}  // namespace
+struct PipeArgs {
+  const bf16_t* q;     // Q, or Gam Q
+  const bf16_t* k;     // K, or Gam K
+  const bf16_t* kh;    // gated: K / Gam
+  const float* gc;     // gated: Gam_C, [B*H][T/64][dk]
+  const bf16_t* v;
+  const bf16_t* beta;
+  bf16_t* o;
+  float* S;
+  int T, dv, use_init;
+};
 
-__global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
-  __shared__ Smem sm;
+// Loads.  Each tile-loader wave owns whole tiles (Q, K, and, gated, K^) and
+// lane `lane` of it loads 16-byte vectors lane + 64 j of a tile (rows 4j +
+// lane/16, 8 columns each).  Wave 7 loads the v slice, beta and (gated)
+// Gam_C.  Every lane issues every load of its slots: a per-lane condition
+// around a load would make the compiler wait for all outstanding loads.
+//   plain:            wave 4 Q, wave 5 K; two register slots.
+//   gated, 16 cols:   wave 1 (no chain work) Q, wave 4 K, wave 5 K^; two slots.
+//   gated, 32 cols:   wave 4 Q + half of K^, wave 5 K + the other half; one
+//                     slot (96 registers).
+// With two slots the loads of chunk y are issued in iteration y-3 and stored
+// in iteration y-1; with one, issued in iteration y-2.
+template <bool GATED, int DVS>
+struct LoadPlan {
+  static constexpr bool kThree = GATED && DVS == 16;           // three tile waves
+  static constexpr int NT = (GATED && !kThree) ? 24 : 16;      // tile vectors per lane
+  static constexpr int NSLOT = NT > 16 ? 1 : 2;
+  static constexpr int NS = NT;                                // registers per slot
+  __device__ static bool is_tile_wave(int wave) { return wave == 4 || wave == 5 || (kThree && wave == 1); }
+  // tile (0 Q, 1 K, 2 K^) and vector index within it of slot j
+  __device__ static int tile_of(int wave, int j) {
+    if (kThree) return wave == 1 ? 0 : (wave == 4 ? 1 : 2);
+    if (GATED && j >= 16) return 2;
+    return wave == 4 ? 0 : 1;
+  }
+  __device__ static int vec_of(int wave, int lane, int j) {
+    if (GATED && !kThree && j >= 16) return 512 * (wave - 4) + lane + 64 * (j - 16);
+    return lane + 64 * j;
+  }
+};
+
+template <bool GATED, int DVS>
+__global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
+  typedef Smem2<GATED, DVS> Sm;
+  constexpr int kDVS = DVS;
+  constexpr int NCW = DVS / 16;        // chain waves
+  constexpr int VPRV = DVS / 8;        // 16-byte vectors per row of the v slice
+  constexpr int NVL = kC * VPRV / 64;  // v-slice vectors per lane of wave 7
+  typedef LoadPlan<GATED, DVS> LP;
+  __shared__ Sm sm;
 
   const int nsl = a.dv / kDVS;
   const int w = xcd_remap(blockIdx.x, gridDim.x);
@@ -135,92 +186,104 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
   const int dv = a.dv;
   const int nch = Tn / kC;
 
-  const bf16_t* qh = reinterpret_cast<const bf16_t*>(a.q) + (size_t)bh * Tn * kDK;
-  const bf16_t* kh = reinterpret_cast<const bf16_t*>(a.k) + (size_t)bh * Tn * kDK;
-  const bf16_t* vh = reinterpret_cast<const bf16_t*>(a.v) + (size_t)bh * Tn * dv + sl * kDVS;
-  const bf16_t* bth = reinterpret_cast<const bf16_t*>(a.beta) + (size_t)bh * Tn;
-  bf16_t* oh = reinterpret_cast<bf16_t*>(a.o) + (size_t)bh * Tn * dv + sl * kDVS;
+  const bf16_t* qh = a.q + (size_t)bh * Tn * kDK;
+  const bf16_t* kh = a.k + (size_t)bh * Tn * kDK;
+  const bf16_t* khh = GATED ? a.kh + (size_t)bh * Tn * kDK : nullptr;
+  const float* gch = GATED ? a.gc + (size_t)bh * nch * kDK : nullptr;
+  const bf16_t* vh = a.v + (size_t)bh * Tn * dv + sl * kDVS;
+  const bf16_t* bth = a.beta + (size_t)bh * Tn;
+  bf16_t* oh = a.o + (size_t)bh * Tn * dv + sl * kDVS;
   float* Sh = a.S + (size_t)bh * kDK * dv + sl * kDVS;
 
   // Tiles above the diagonal of tril(QK^T) are read as zeros.
   {
-    uint32_t* z = reinterpret_cast<uint32_t*>(&sm.a[0][0][0]);
+    uint32_t* z = reinterpret_cast<uint32_t*>(&sm.a[0][0]);
     for (int i = tid; i < (int)(sizeof(sm.a) / 4); i += kThreads) z[i] = 0u;
   }
 
-  // ---- register prefetch by waves 2..7 (the chain waves keep their
-  // registers for the state).  A chunk is 2304 16-byte vectors: 0..1023 q,
-  // 1024..2047 k, 2048..2303 the 64 x 32 slice of v; loader thread
-  // u = tid - 128 owns vectors u + 384 j.  beta is loaded by wave 4.
-  constexpr int kLoaders = kThreads - 128;
-  constexpr int kPerLoader = 2304 / kLoaders;  // 6
-  const int lu = tid - 128;
-  auto issue_loads = [&](int chunk, u32x4 (&dst)[kPerLoader], uint32_t& bdst) {
+  // load kind of a role, fixed at compile time: 0 none, 1 tiles (q, k, k^),
+  // 2 wave 7's v slice, beta and Gam_C
+  constexpr int NSMALL = NVL + (GATED ? 1 : 0);
+  auto issue_loads = [&](auto kindc, int chunk, auto& dst, uint32_t& bdst) {
+    constexpr int KIND = decltype(kindc)::value;
+    if constexpr (KIND == 1) {
+      const bf16_t* const pq = qh;  // register copies: a select among captured
+      const bf16_t* const pk = kh;  // references would go through memory
+      const bf16_t* const pkh = khh;
 #pragma unroll
-    for (int j = 0; j < kPerLoader; ++j) {
-      const int v = lu + kLoaders * j;
-      const bf16_t* src;
-      if (v < 2048) {
-        const int vv = v & 1023;
-        src = (v < 1024 ? qh : kh) + (size_t)(chunk * kC + (vv >> 4)) * kDK + (vv & 15) * 8;
-      } else {
-        const int vv = v - 2048;
-        src = vh + (size_t)(chunk * kC + (vv >> 2)) * dv + (vv & 3) * 8;
+      for (int j = 0; j < LP::NT; ++j) {
+        const int t = LP::tile_of(wave, j);
+        const bf16_t* base = t == 0 ? pq : (t == 1 ? pk : pkh);
+        const int vv = LP::vec_of(wave, lane, j);
+        dst[j] = *reinterpret_cast<const u32x4*>(base + (size_t)(chunk * kC + (vv >> 4)) * kDK + (vv & 15) * 8);
       }
-      dst[j] = *reinterpret_cast<const u32x4*>(src);
+    } else if constexpr (KIND == 2) {  // wave 7
+#pragma unroll
+      for (int j = 0; j < NVL; ++j) {
+        const int vv = lane + 64 * j;  // row vv / VPRV, eight columns
+        dst[j] = *reinterpret_cast<const u32x4*>(vh + (size_t)(chunk * kC + vv / VPRV) * dv + (vv % VPRV) * 8);
+      }
+      if constexpr (GATED) dst[NVL] = *reinterpret_cast<const u32x4*>(gch + (size_t)chunk * kDK + 4 * (lane & 31));
+      bdst = bth[chunk * kC + lane];  // converted when stored
     }
-    if (wave == 4) bdst = bth[chunk * kC + lane];  // converted when stored
   };
-  auto store_loads = [&](int buf, int kbuf, const u32x4 (&src)[kPerLoader], uint32_t bsrc) {
+  auto store_loads = [&](auto kindc, int buf, const auto& src, uint32_t bsrc) {
+    constexpr int KIND = decltype(kindc)::value;
+    if constexpr (KIND == 1) {
 #pragma unroll
-    for (int j = 0; j < kPerLoader; ++j) {
-      const int v = lu + kLoaders * j;
-      if (v < 2048) {
-        const int vv = v & 1023;
-        bf16_t* dstp = (v < 1024 ? &sm.q[buf][vv >> 4][(vv & 15) * 8] : &sm.k[kbuf][vv >> 4][(vv & 15) * 8]);
-        *reinterpret_cast<u32x4*>(dstp) = src[j];
-      } else {
-        const int vv = v - 2048;
-        *reinterpret_cast<u32x4*>(&sm.v[buf][vv >> 2][(vv & 3) * 8]) = src[j];
+      for (int j = 0; j < LP::NT; ++j) {
+        const int t = LP::tile_of(wave, j);
+        bf16_t(*tile)[kLQ] = t == 0 ? sm.q[buf] : (t == 1 ? sm.k[buf] : sm.kh[GATED ? buf : 0]);
+        const int vv = LP::vec_of(wave, lane, j);
+        *reinterpret_cast<u32x4*>(&tile[vv >> 4][(vv & 15) * 8]) = src[j];
       }
+    } else if constexpr (KIND == 2) {  // wave 7
+#pragma unroll
+      for (int j = 0; j < NVL; ++j) {
+        const int vv = lane + 64 * j;
+        *reinterpret_cast<u32x4*>(&sm.v[buf][vv / VPRV][(vv % VPRV) * 8]) = src[j];
+      }
+      if constexpr (GATED) {
+        if (lane < 32) *reinterpret_cast<u32x4*>(&sm.gc[GATED ? buf : 0][4 * lane]) = src[NVL];
+      }
+      sm.beta[buf][lane] = bf2f((bf16_t)bsrc);
     }
-    if (wave == 4) sm.beta[buf][lane] = bf2f((bf16_t)bsrc);
   };
 
-  // Every role below runs its own copy of the chunk loop: iteration c
-  // (c = -1 .. nch-1) has two phases, each closed by one LDS barrier, so all
-  // waves meet at the same barriers while each role keeps only its own state
-  // live.  In iteration c the chain works on chunk c, products and T on
-  // chunk c+1; every wave writes its share of chunk c+2 to LDS (loaded one
-  // iteration earlier) and issues its global loads of chunk c+3.
-  // `body(c, P, phase1, phase2)` runs one iteration with P = c & 1 known at
-  // compile time, so every buffer and register-slot index is static.
-  auto run = [&](auto phase1, auto phase2) {
-    const bool loader = wave >= 2;
-    u32x4 pf[2][kPerLoader];
-    uint32_t pfb[2] = {0u, 0u};
+  // Every role runs its own copy of the chunk loop (the same barriers, only
+  // its own registers live).  body(x, parity) runs iteration x with
+  // parity = x & 1 known at compile time, so buffer and register-slot
+  // indices are static.
+  auto run = [&](auto phase1, auto phase2, auto kindc) {
+    constexpr int KIND = decltype(kindc)::value;
+    constexpr bool loader = KIND != 0;
+    constexpr int NSL = KIND == 1 ? LP::NSLOT : 2;
+    constexpr int NREG = KIND == 1 ? LP::NT : (KIND == 2 ? NSMALL : 1);
+    u32x4 pf[NSL][NREG];
+    uint32_t pfb[NSL] = {};
     if (loader) {
-      issue_loads(0, pf[0], pfb[0]);
-      store_loads(0, 0, pf[0], pfb[0]);
-      if (nch > 1) issue_loads(1, pf[1], pfb[1]);
+      issue_loads(kindc, 0, pf[0], pfb[0]);
+      if (NSL == 2 && nch > 1) issue_loads(kindc, 1, pf[NSL - 1], pfb[NSL - 1]);
     }
-    lds_barrier();
-    auto body = [&](const int c, auto parity) {
+    auto body = [&](const int x, auto parity) {
       constexpr int P = decltype(parity)::value;
-      phase1(c, parity);
-      if (loader && c + 3 < nch) issue_loads(c + 3, pf[1 - P], pfb[1 - P]);
+      constexpr int SL = NSL == 2 ? 1 - P : 0;  // slot holding chunk x+1
+      phase1(x, parity);
+      if (loader && x + 1 < nch) {
+        store_loads(kindc, 1 - P, pf[SL], pfb[SL]);
+        if (x + 1 + NSL < nch) issue_loads(kindc, x + 1 + NSL, pf[SL], pfb[SL]);
+      }
       lds_barrier();
-      phase2(c, parity);
-      if (loader && c + 2 < nch) store_loads(P, mod3(c + 2), pf[P], pfb[P]);
+      phase2(x, parity);
       lds_barrier();
     };
-    for (int c = -1; c < nch; c += 2) {
-      body(c, std::integral_constant<int, 1>{});
-      if (c + 1 < nch) body(c + 1, std::integral_constant<int, 0>{});
+    for (int x = -1; x < nch; x += 2) {
+      body(x, std::integral_constant<int, 1>{});
+      if (x + 1 < nch) body(x + 1, std::integral_constant<int, 0>{});
     }
   };
 
-  if (wave < 2) {
+  if (wave < NCW) {
     // ======================= chain waves =======================
     const int col = 16 * wave + lc;  // value column within the slice
     floatx4 st[8];
@@ -234,19 +297,18 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
     }
     floatx4 xx[4], ox[4];
     run(
-        [&](const int c, auto parity) {
+        [&](const int x, auto parity) {
           constexpr int P = decltype(parity)::value;
-          if (c < 0) return;
-          const int kc = mod3(c);
-          // Y = K S and O = Q S (shared S fragments), X = beta (V - Y).
-          // The fragments of k-step kb+1 are loaded while kb computes.
+          if (x < 0) return;
+          // Y = K S and O = Q S (shared S fragments), X = beta (V - Y); the
+          // fragments of k-step kb+1 are loaded while kb computes.
           floatx4 y[4];
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) { y[mt] = zero4(); ox[mt] = zero4(); }
           bf16x8 fk[2][4], fq[2][4];
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) {
-            fk[0][mt] = ld_frag(&sm.k[kc][16 * mt + lc][8 * lg]);
+            fk[0][mt] = ld_frag(&sm.k[P][16 * mt + lc][8 * lg]);
             fq[0][mt] = ld_frag(&sm.q[P][16 * mt + lc][8 * lg]);
           }
 #pragma unroll
@@ -254,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
             if (kb < 3) {
 #pragma unroll
               for (int mt = 0; mt < 4; ++mt) {
-                fk[(kb + 1) & 1][mt] = ld_frag(&sm.k[kc][16 * mt + lc][32 * (kb + 1) + 8 * lg]);
+                fk[(kb + 1) & 1][mt] = ld_frag(&sm.k[P][16 * mt + lc][32 * (kb + 1) + 8 * lg]);
                 fq[(kb + 1) & 1][mt] = ld_frag(&sm.q[P][16 * mt + lc][32 * (kb + 1) + 8 * lg]);
               }
             }
@@ -268,7 +330,8 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) {
             // lane (lg, lc) gets V[16 mt + 4 lg + i][col], i = 0..3
-            const shortx4_t vw = ld_tr(&sm.v[P][16 * mt + 4 * lg + ((lane >> 2) & 3)][16 * wave + 4 * (lane & 3)]);
+            const shortx4_t vw =
+                ld_tr(&sm.v[P][16 * mt + 4 * lg + ((lane >> 2) & 3)][16 * wave + 4 * (lane & 3)]);
             const float4 bt = *reinterpret_cast<const float4*>(&sm.beta[P][16 * mt + 4 * lg]);
             xx[mt][0] = bt.x * (bf2f((bf16_t)vw[0]) - y[mt][0]);
             xx[mt][1] = bt.y * (bf2f((bf16_t)vw[1]) - y[mt][1]);
@@ -276,27 +339,24 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
             xx[mt][3] = bt.w * (bf2f((bf16_t)vw[3]) - y[mt][3]);
           }
         },
-        [&](const int c, auto parity) {
+        [&](const int x, auto parity) {
           constexpr int P = decltype(parity)::value;
-          if (c < 0) return;
-          const int kc = mod3(c);
-          // u by block forward substitution; the D_b, L_bj and tril(Q K^T)
-          // fragments are requested up front.
+          if (x < 0) return;
           auto fr16 = [&](const bf16_t* blk) {  // A operand of a transposed 16x16 block
             return ld_tr(blk + (4 * lg + ((lane >> 2) & 3)) * 16 + 4 * (lane & 3));
           };
           shortx4_t fd[4], fl[6];
 #pragma unroll
-          for (int b = 0; b < 4; ++b) fd[b] = fr16(&sm.d[P][b][0][0]);
+          for (int b = 0; b < 4; ++b) fd[b] = fr16(&sm.d[b][0][0]);
 #pragma unroll
-          for (int x = 0; x < 6; ++x) fl[x] = fr16(&sm.lb[P][x][0][0]);
+          for (int i = 0; i < 6; ++i) fl[i] = fr16(&sm.lb[P][i][0][0]);
           bf16x8 fa[6];
-          fa[0] = ld_frag(&sm.a[P][lc][8 * lg]);
-          fa[1] = ld_frag(&sm.a[P][16 + lc][8 * lg]);
-          fa[2] = ld_frag(&sm.a[P][32 + lc][8 * lg]);
-          fa[3] = ld_frag(&sm.a[P][32 + lc][32 + 8 * lg]);
-          fa[4] = ld_frag(&sm.a[P][48 + lc][8 * lg]);
-          fa[5] = ld_frag(&sm.a[P][48 + lc][32 + 8 * lg]);
+          fa[0] = ld_frag(&sm.a[lc][8 * lg]);
+          fa[1] = ld_frag(&sm.a[16 + lc][8 * lg]);
+          fa[2] = ld_frag(&sm.a[32 + lc][8 * lg]);
+          fa[3] = ld_frag(&sm.a[32 + lc][32 + 8 * lg]);
+          fa[4] = ld_frag(&sm.a[48 + lc][8 * lg]);
+          fa[5] = ld_frag(&sm.a[48 + lc][32 + 8 * lg]);
           // blocks L_bj stored in the order (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
           floatx4 ut[4];
           ut[0] = mfma_k16(fd[0], acc_to_b16(xx[0]), zero4());
@@ -306,14 +366,16 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
           ut[2] = mfma_k16(fd[2], acc_to_b16(xx[2] - mfma_k16(fl[2], u1, mfma_k16(fl[1], u0, zero4()))),
                            zero4());
           const shortx4_t u2 = acc_to_b16(ut[2]);
-          ut[3] = mfma_k16(fd[3], acc_to_b16(xx[3] - mfma_k16(fl[5], u2, mfma_k16(fl[4], u1, mfma_k16(fl[3], u0, zero4())))),
-                           zero4());
-          // K^T fragments: row 16t + c of the A operand is key channel
-          // perm32(16t + c); its k-elements are the tokens of u's pairing.
+          ut[3] = mfma_k16(
+              fd[3], acc_to_b16(xx[3] - mfma_k16(fl[5], u2, mfma_k16(fl[4], u1, mfma_k16(fl[3], u0, zero4())))),
+              zero4());
+          // K^T fragments (K^ when gated): row 16t + c of the A operand is key
+          // channel perm32(16t + c); its k-elements are the tokens of u's pairing.
+          const bf16_t(*kt)[kLQ] = GATED ? sm.kh[GATED ? P : 0] : sm.k[P];
           const int trow = 4 * lg + ((lane >> 2) & 3);
           auto kt_frag = [&](int t, int tok0) {
-            const int col = 32 * (t >> 1) + 4 * (t & 1) + 8 * (lane & 3);
-            return cat_tr(ld_tr(&sm.k[kc][tok0 + trow][col]), ld_tr(&sm.k[kc][tok0 + 16 + trow][col]));
+            const int cc = 32 * (t >> 1) + 4 * (t & 1) + 8 * (lane & 3);
+            return cat_tr(ld_tr(&kt[tok0 + trow][cc]), ld_tr(&kt[tok0 + 16 + trow][cc]));
           };
           bf16x8 fkt[2][8];
 #pragma unroll
@@ -332,31 +394,43 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
           for (int t = 0; t < 8; ++t) st[t] = mfma_k32(fkt[0][t], u01, st[t]);
 #pragma unroll
           for (int t = 0; t < 8; ++t) st[t] = mfma_k32(fkt[1][t], u23, st[t]);
+          if constexpr (GATED) {
+            // S <- diag(Gam_C) S; accumulator rows 16t + 4lg + i are the
+            // consecutive channels perm32(16t + 4lg) + i
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              const float4 gv = *reinterpret_cast<const float4*>(&sm.gc[P][perm32(16 * t + 4 * lg)]);
+              st[t][0] *= gv.x;
+              st[t][1] *= gv.y;
+              st[t][2] *= gv.z;
+              st[t][3] *= gv.w;
+            }
+          }
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) sm.o[16 * mt + 4 * lg + i][col] = f2bf(ox[mt][i]);
-        });
+        },
+        std::integral_constant<int, 0>{});
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) Sh[(size_t)perm32(16 * t + 4 * lg + i) * dv + col] = st[t][i];
   } else if (wave == 6) {
     // ======================= D wave =======================
-    // Diagonal 16x16 blocks of I + L for chunk c+1 (phase 2): lane (block lg,
-    // column lc) solves (I + L_bb) x = e_lc by forward substitution in fp32;
-    // x is column lc of D_b = (I + L_bb)^-1, stored as row lc of D_b^T.
-    run([&](const int c, auto parity) {},
-        [&](const int c, auto parity) {
-          constexpr int nb = 1 - decltype(parity)::value;
-          if (c + 1 >= nch) return;
-          const int b0 = 16 * lg;
+    // D_b = (I + L_bb)^-1 of chunk x (phase 1): lane (block lg, column lc)
+    // solves (I + L_bb) x = e_lc by forward substitution in fp32; x is column
+    // lc of D_b, stored as row lc of D_b^T.
+    run(
+        [&](const int x, auto parity) {
+          if (x < 0) return;
+          const float* lbk = &sm.l[lg * kLB];
           float4 lr[16][4];  // strictly-lower rows of L_bb, requested up front
 #pragma unroll
           for (int i = 1; i < 16; ++i)
 #pragma unroll
             for (int m4 = 0; m4 < i; m4 += 4)
-              lr[i][m4 >> 2] = *reinterpret_cast<const float4*>(&sm.l[b0 + i][b0 + m4]);
+              lr[i][m4 >> 2] = *reinterpret_cast<const float4*>(lbk + i * kLR + m4);
           float tv[16];
 #pragma unroll
           for (int m = 0; m < 16; ++m) tv[m] = m == lc ? 1.f : 0.f;
@@ -378,69 +452,32 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
             w0[e] = pack2(tv[2 * e], tv[2 * e + 1]);
             w1[e] = pack2(tv[8 + 2 * e], tv[9 + 2 * e]);
           }
-          *reinterpret_cast<u32x4*>(&sm.d[nb][lg][lc][0]) = w0;
-          *reinterpret_cast<u32x4*>(&sm.d[nb][lg][lc][8]) = w1;
-        });
+          *reinterpret_cast<u32x4*>(&sm.d[lg][lc][0]) = w0;
+          *reinterpret_cast<u32x4*>(&sm.d[lg][lc][8]) = w1;
+        },
+        [&](const int x, auto parity) {}, std::integral_constant<int, 0>{});
   } else if (wave == 2 || wave == 3 || wave == 7) {
     // ======================= product waves =======================
-    // Row blocks I0..I1 of K K^T (phase 1) and tril(Q K^T) (phase 2) of
-    // chunk c+1, tile lists fixed at compile time: wave 2 row 3, wave 3
-    // row 2, wave 7 rows 0 and 1.  All fragments of a row block are
-    // requested before its MFMAs.
+    // Row blocks I0..I1: tril(Q K^T) of chunk x in phase 1, L of chunk x+1
+    // in phase 2 (K^ on the right when gated).  Wave 2 row 3, wave 3 row 2,
+    // wave 7 rows 0 and 1.  All fragments of a row block are requested
+    // before its MFMAs.
     auto prod = [&](auto i0c, auto i1c) {
       constexpr int I0 = decltype(i0c)::value, I1 = decltype(i1c)::value;
       run(
-          [&](const int c, auto parity) {
-            constexpr int nb = 1 - decltype(parity)::value;  // buffer of chunk c+1
-            if (c + 1 >= nch) return;
-            const int kn = mod3(c + 1);
-            // K K^T -> L = diag(beta) (.) strictly below the diagonal
-#pragma unroll
-            for (int i = I0; i <= I1; ++i) {
-              bf16x8 fb[4][4];
-#pragma unroll
-              for (int j = 0; j <= i; ++j)
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) fb[j][kb] = ld_frag(&sm.k[kn][16 * j + lc][32 * kb + 8 * lg]);
-              floatx4 acc[4];
-#pragma unroll
-              for (int j = 0; j <= i; ++j) {
-                acc[j] = zero4();
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) acc[j] = mfma_k32(fb[i][kb], fb[j][kb], acc[j]);
-              }
-              // diagonal tile: fp32 strictly-lower part for the D wave;
-              // off-diagonal tiles: bf16, transposed (lane writes row lc,
-              // columns 4 lg .. 4 lg + 3 of L_ij^T)
-              const float4 bt = *reinterpret_cast<const float4*>(&sm.beta[nb][16 * i + 4 * lg]);
-#pragma unroll
-              for (int j = 0; j < i; ++j) {
-                uint2 w;
-                w.x = pack2(bt.x * acc[j][0], bt.y * acc[j][1]);
-                w.y = pack2(bt.z * acc[j][2], bt.w * acc[j][3]);
-                *reinterpret_cast<uint2*>(&sm.lb[nb][i * (i - 1) / 2 + j][lc][4 * lg]) = w;
-              }
-#pragma unroll
-              for (int ii = 0; ii < 4; ++ii) {
-                const int r = 16 * i + 4 * lg + ii, cc = 16 * i + lc;
-                if (cc < r) sm.l[r][cc] = (ii == 0 ? bt.x : ii == 1 ? bt.y : ii == 2 ? bt.z : bt.w) * acc[i][ii];
-              }
-            }
-          },
-          [&](const int c, auto parity) {
-            constexpr int nb = 1 - decltype(parity)::value;
-            if (c + 1 >= nch) return;
-            const int kn = mod3(c + 1);
-            // tril(Q K^T), token columns permuted
+          [&](const int x, auto parity) {
+            constexpr int P = decltype(parity)::value;
+            if (x < 0) return;
+            const bf16_t(*rt)[kLQ] = GATED ? sm.kh[GATED ? P : 0] : sm.k[P];
 #pragma unroll
             for (int i = I0; i <= I1; ++i) {
               bf16x8 fq[4], fb[4][4];
 #pragma unroll
-              for (int kb = 0; kb < 4; ++kb) fq[kb] = ld_frag(&sm.q[nb][16 * i + lc][32 * kb + 8 * lg]);
+              for (int kb = 0; kb < 4; ++kb) fq[kb] = ld_frag(&sm.q[P][16 * i + lc][32 * kb + 8 * lg]);
 #pragma unroll
               for (int j = 0; j <= i; ++j)
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) fb[j][kb] = ld_frag(&sm.k[kn][16 * j + lc][32 * kb + 8 * lg]);
+                for (int kb = 0; kb < 4; ++kb) fb[j][kb] = ld_frag(&rt[16 * j + lc][32 * kb + 8 * lg]);
               floatx4 acc[4];
 #pragma unroll
               for (int j = 0; j <= i; ++j) {
@@ -448,45 +485,199 @@ __global__ __launch_bounds__(kThreads) void prefill_delta_pipe(PrefillArgs a) {
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) acc[j] = mfma_k32(fq[kb], fb[j][kb], acc[j]);
               }
+              // token columns permuted for the chain's pairing
 #pragma unroll
               for (int j = 0; j <= i; ++j)
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
                   const int r = 16 * i + 4 * lg + ii, cc = 16 * j + lc;
-                  sm.a[nb][r][perm32(cc)] = f2bf(cc <= r ? acc[j][ii] : 0.f);
+                  sm.a[r][perm32(cc)] = f2bf(cc <= r ? acc[j][ii] : 0.f);
                 }
             }
-          });
+          },
+          [&](const int x, auto parity) {
+            constexpr int nb = 1 - decltype(parity)::value;  // buffer of chunk x+1
+            if (x + 1 >= nch) return;
+            const bf16_t(*rt)[kLQ] = GATED ? sm.kh[GATED ? nb : 0] : sm.k[nb];
+#pragma unroll
+            for (int i = I0; i <= I1; ++i) {
+              bf16x8 fl[4], fb[4][4];
+#pragma unroll
+              for (int j = 0; j <= i; ++j)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) fb[j][kb] = ld_frag(&rt[16 * j + lc][32 * kb + 8 * lg]);
+#pragma unroll
+              for (int kb = 0; kb < 4; ++kb)  // left operand: K (gated: Gam K)
+                fl[kb] = GATED ? ld_frag(&sm.k[nb][16 * i + lc][32 * kb + 8 * lg]) : fb[i][kb];
+              floatx4 acc[4];
+#pragma unroll
+              for (int j = 0; j <= i; ++j) {
+                acc[j] = zero4();
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) acc[j] = mfma_k32(fl[kb], fb[j][kb], acc[j]);
+              }
+              // L = diag(beta) (.): the diagonal tile's strictly-lower part in
+              // fp32 for the D wave; off-diagonal tiles bf16, transposed (the
+              // lane writes row lc, columns 4lg .. 4lg+3 of L_ij^T)
+              const float4 bt = *reinterpret_cast<const float4*>(&sm.beta[nb][16 * i + 4 * lg]);
+#pragma unroll
+              for (int j = 0; j < i; ++j) {
+                uint2 wv;
+                wv.x = pack2(bt.x * acc[j][0], bt.y * acc[j][1]);
+                wv.y = pack2(bt.z * acc[j][2], bt.w * acc[j][3]);
+                *reinterpret_cast<uint2*>(&sm.lb[nb][i * (i - 1) / 2 + j][lc][4 * lg]) = wv;
+              }
+              float* lbk = &sm.l[i * kLB];
+#pragma unroll
+              for (int ii = 0; ii < 4; ++ii) {
+                const int r = 4 * lg + ii;
+                const float bv = ii == 0 ? bt.x : ii == 1 ? bt.y : ii == 2 ? bt.z : bt.w;
+                if (lc < r) lbk[r * kLR + lc] = bv * acc[i][ii];
+              }
+            }
+          },
+          std::integral_constant<int, (I0 == 0 && I1 == 1) ? 2 : 0>{});  // wave 7 loads v, beta
     };
     if (wave == 2) prod(std::integral_constant<int, 3>{}, std::integral_constant<int, 3>{});
     else if (wave == 3) prod(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
     else prod(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
   } else {
-    // ======================= output waves (4, 5) =======================
-    // Wave 4 writes the output tile of chunk c-1 (left in LDS by the chain
-    // waves) to memory with 16-byte stores; both waves also load.
-    const int sw = tid - 256;  // 0..127
+    // ============ output / load waves (4, 5; wave 1 idles when NCW = 1) ============
+    // Wave 4 writes the output tile of chunk x-1 (left in LDS by the chain
+    // waves) to memory with 16-byte stores.
+    const int sw = tid - 256;  // 0..63 on wave 4
     auto store_o = [&](int chunk) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int v = sw + 64 * j;
-        const int r = v >> 2, c8 = (v & 3) * 8;
+      for (int j = 0; j < kC * VPRV / 64; ++j) {
+        const int vi = sw + 64 * j;
+        const int r = vi / VPRV, c8 = (vi % VPRV) * 8;
         *reinterpret_cast<u32x4*>(oh + (size_t)(chunk * kC + r) * dv + c8) =
             *reinterpret_cast<const u32x4*>(&sm.o[r][c8]);
       }
     };
-    run([&](const int c, auto parity) {
-          if (wave == 4 && c >= 1) store_o(c - 1);
-        },
-        [&](const int c, auto parity) {});
+    auto ph1 = [&](const int x, auto parity) {
+      if (wave == 4 && x >= 1) store_o(x - 1);
+    };
+    auto ph2 = [&](const int x, auto parity) {};
+    if (LP::is_tile_wave(wave)) run(ph1, ph2, std::integral_constant<int, 1>{});
+    else run(ph1, ph2, std::integral_constant<int, 0>{});
     if (wave == 4) store_o(nch - 1);
   }
 }
 
-hipError_t launch_prefill_pipe(const PrefillArgs& a, hipStream_t st) {
-  const long blocks = (long)a.B * a.H * (a.dv / kDVS);
-  hipLaunchKernelGGL(prefill_delta_pipe, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+// Gate pre-pass: for each (batch, head, chunk) and key channel d, the
+// cumulative log-decay G_t = sum_{s<=t} g_s over the chunk (fp32), then
+// Gam Q, Gam K, K / Gam in bf16 and Gam_C = e^{G_63}.  One workgroup of 256
+// threads per chunk: thread (w, l) holds channels 2l, 2l+1 of tokens
+// 16w .. 16w+15; the four waves' partial sums are combined through LDS.
+__global__ __launch_bounds__(256) void gate_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                 const bf16_t* __restrict__ g, bf16_t* __restrict__ qt,
+                                                 bf16_t* __restrict__ kt, bf16_t* __restrict__ kht,
+                                                 float* __restrict__ gcum, int nch) {
+  __shared__ float2 part[4][64];
+  const int chunk = blockIdx.x;  // over B*H*nch
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const size_t base = (size_t)chunk * kC * kDK;
+  const uint32_t* g2 = reinterpret_cast<const uint32_t*>(g + base);
+  uint32_t gw[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) gw[t] = g2[(16 * w + t) * (kDK / 2) + l];
+  float2 run = make_float2(0.f, 0.f);
+  float2 gl[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    run.x += bf2f((bf16_t)(gw[t] & 0xffffu));
+    run.y += bf2f((bf16_t)(gw[t] >> 16));
+    gl[t] = run;
+  }
+  part[w][l] = run;
+  __syncthreads();
+  float2 off = make_float2(0.f, 0.f), tot = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float2 x = part[p][l];
+    if (p < w) { off.x += x.x; off.y += x.y; }
+    tot.x += x.x;
+    tot.y += x.y;
+  }
+  if (w == 0) reinterpret_cast<float2*>(gcum + (size_t)chunk * kDK)[l] = make_float2(__expf(tot.x), __expf(tot.y));
+  const uint32_t* q2 = reinterpret_cast<const uint32_t*>(q + base);
+  const uint32_t* k2 = reinterpret_cast<const uint32_t*>(k + base);
+  uint32_t* qt2 = reinterpret_cast<uint32_t*>(qt + base);
+  uint32_t* kt2 = reinterpret_cast<uint32_t*>(kt + base);
+  uint32_t* kh2 = reinterpret_cast<uint32_t*>(kht + base);
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int idx = (16 * w + t) * (kDK / 2) + l;
+    const uint32_t qw = q2[idx], kw = k2[idx];
+    const float G0 = off.x + gl[t].x, G1 = off.y + gl[t].y;
+    const float e0 = __expf(G0), e1 = __expf(G1), r0 = __expf(-G0), r1 = __expf(-G1);
+    const float q0 = bf2f((bf16_t)(qw & 0xffffu)), q1 = bf2f((bf16_t)(qw >> 16));
+    const float k0 = bf2f((bf16_t)(kw & 0xffffu)), k1 = bf2f((bf16_t)(kw >> 16));
+    qt2[idx] = pack2(q0 * e0, q1 * e1);
+    kt2[idx] = pack2(k0 * e0, k1 * e1);
+    kh2[idx] = pack2(k0 * r0, k1 * r1);
+  }
+}
+
+}  // namespace
+
+size_t gated_pipe_workspace_bytes(const PrefillArgs& a) {
+  const size_t n = (size_t)a.B * a.H * a.T * kDK;
+  return 3 * n * sizeof(bf16_t) + (size_t)a.B * a.H * (a.T / kC) * kDK * sizeof(float);
+}
+
+namespace {
+
+template <bool GATED>
+hipError_t launch_pipe_t(const PipeArgs& p, long bh, int dv, hipStream_t st) {
+  // 32 value columns per workgroup, or 16 when 32-column slices would leave
+  // compute units idle (few (batch, head) pairs, as with long sequences)
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (bh * (dv / 32) < cus && dv % 16 == 0) {
+    hipLaunchKernelGGL((prefill_pipe<GATED, 16>), dim3((unsigned)(bh * (dv / 16))), dim3(kThreads), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((prefill_pipe<GATED, 32>), dim3((unsigned)(bh * (dv / 32))), dim3(kThreads), 0, st, p);
+  }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_pipe(const PrefillArgs& a, void* workspace, hipStream_t st) {
+  const long bh = (long)a.B * a.H;
+  PipeArgs p;
+  p.v = reinterpret_cast<const bf16_t*>(a.v);
+  p.beta = reinterpret_cast<const bf16_t*>(a.beta);
+  p.o = reinterpret_cast<bf16_t*>(a.o);
+  p.S = a.S;
+  p.T = a.T;
+  p.dv = a.dv;
+  p.use_init = a.use_init;
+  if (a.g == nullptr) {
+    p.q = reinterpret_cast<const bf16_t*>(a.q);
+    p.k = reinterpret_cast<const bf16_t*>(a.k);
+    p.kh = nullptr;
+    p.gc = nullptr;
+    return launch_pipe_t<false>(p, bh, a.dv, st);
+  }
+  const size_t n = (size_t)a.B * a.H * a.T * kDK;
+  bf16_t* qt = reinterpret_cast<bf16_t*>(workspace);
+  bf16_t* kt = qt + n;
+  bf16_t* kht = kt + n;
+  float* gcum = reinterpret_cast<float*>(kht + n);
+  const int nch = a.T / kC;
+  hipLaunchKernelGGL(gate_prep, dim3((unsigned)(a.B * a.H * nch)), dim3(256), 0, st,
+                     reinterpret_cast<const bf16_t*>(a.q), reinterpret_cast<const bf16_t*>(a.k),
+                     reinterpret_cast<const bf16_t*>(a.g), qt, kt, kht, gcum, nch);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  p.q = qt;
+  p.k = kt;
+  p.kh = kht;
+  p.gc = gcum;
+  return launch_pipe_t<true>(p, bh, a.dv, st);
 }
 
 }  // namespace linattn

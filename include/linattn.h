@@ -32,8 +32,13 @@
  *           q, k, v of the prefill entry points and S of the decode entry
  *           points must be 16-byte aligned (they are read in 16-byte
  *           vectors).  o must not alias any input.  S (and z) are read and written.  The
- *           library allocates no device memory and keeps no state between
- *           calls; calls are re-entrant.
+ *           library keeps no state between calls; calls are re-entrant.  It
+ *           allocates device memory in one case only: the gated
+ *           deltanet_prefill with bf16 inputs, dk = 128 and dv % 32 == 0
+ *           takes a stream-ordered workspace (hipMallocAsync on `stream`,
+ *           released with hipFreeAsync after its kernels) of
+ *           6 B*H*T*dk + 4 B*H*(T/64)*dk bytes for the decay-scaled q and k;
+ *           a failed allocation returns LA_ERR_LAUNCH.
  * Sizes.    B, H (or N, H) >= 1; T >= 1 and T a multiple of 64 for prefill;
  *           dk and dv each one of 16, 32, 64, 128.  The per-channel gated
  *           prefill with LA_DTYPE_F32 supports dk <= 64.

@@ -68,6 +68,21 @@ def test_la_prefill(dtype, dk, dv, init):
     assert_close(z, z_ref, TOL[dtype], "z")
 
 
+@pytest.mark.parametrize("gated", [False, True], ids=["delta", "gated"])
+def test_many_heads_bf16_dk128(gated):
+    """Enough (batch, head) pairs that the bf16 dk = 128 kernels take their
+    32-column value slices (few pairs select 16-column slices)."""
+    dev = require_gpu()
+    B, H, T = 8, 32, 128
+    inp = workloads.make_delta(B, H, T, 128, 128, torch.bfloat16, seed=321, gated=gated,
+                               init_state=True, state_std=0.5)
+    o, S = _run_delta(inp, dev, gated, True)
+    o_ref, S_ref = oracle.delta_recurrent(inp["q"], inp["k"], inp["v"], inp["beta"],
+                                          inp.get("g"), S0=inp["S0"])
+    assert_close(o, o_ref, TOL[torch.bfloat16], "o")
+    assert_close(S, S_ref, TOL[torch.bfloat16], "S")
+
+
 def test_float32_gated_dk128_is_rejected():
     dev = require_gpu()
     inp = workloads.make_delta(1, 1, 64, 128, 64, torch.float32, seed=1, gated=True)
