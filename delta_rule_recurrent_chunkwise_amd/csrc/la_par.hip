@@ -1,0 +1,331 @@
+// la_par.hip -- chunk-parallel pieces of the linear-attention prefill.
+//
+// Article "From GPT-2 to Kimi K3, explained", section "Linear Attention":
+// the state is S_t = S_{t-1} + phi(k_t) v_t^T and the normaliser
+// z_t = z_{t-1} + phi(k_t), phi = elu + 1.  Neither update depends on the
+// state, so with 64-token chunks the state entering chunk c is
+//   S_c = S_0 + sum_{c' < c} phi(K_c')^T V_c',   z_c = z_0 + sum_{c' < c} colsum phi(K_c').
+// la_chunk_state forms every chunk's phi(K)^T V and colsum phi(K) in
+// parallel; la_state_scan turns them, in place, into S_c and z_c (and
+// writes the final state); the chunk outputs are then independent.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace linattn {
+namespace {
+
+constexpr int kC = 64;
+typedef short shortx4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+__device__ __forceinline__ shortx4_t ld_tr(const bf16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4_t*)((__attribute__((address_space(3))) bf16_t*)(p)));
+}
+__device__ __forceinline__ bf16x8 cat_tr(shortx4_t lo, shortx4_t hi) {
+  typedef short shortx8_t __attribute__((ext_vector_type(8)));
+  const shortx8_t x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, x);
+}
+
+// One workgroup (4 waves) per (batch, head, chunk): dS[chunk] = phi(K)^T V
+// (dk x dv, fp32) and dz[chunk] = colsum phi(K) (dk), bf16 inputs.  Output
+// tile (16 key channels x 16 value columns) = sum over the 64 tokens, two
+// 32-deep MFMAs; both operands are read from the row-major LDS tiles with
+// the transpose read (lane 16G + 4a + b receives element b of the 8-byte runs
+// addressed by lanes 16G + a + 4e), so that the k-index of element (g, e) is
+// token 4g + e (e < 4) or 16 + 4g + e - 4.  The column sums are the same
+// product with V replaced by ones.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void la_chunk_state(const bf16_t* __restrict__ k,
+                                                      const bf16_t* __restrict__ v,
+                                                      float* __restrict__ dS, float* __restrict__ dz) {
+  constexpr int LK = DK + 16, LV = DV + 16;  // row strides (bf16)
+  __shared__ __attribute__((aligned(16))) bf16_t sk[kC][LK];
+  __shared__ __attribute__((aligned(16))) bf16_t sv[kC][LV];
+  const size_t chunk = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bf16_t* kc = k + chunk * kC * DK;
+  const bf16_t* vc = v + chunk * kC * DV;
+  for (int i = tid; i < kC * DK / 8; i += 256) {
+    const int r = i / (DK / 8), c8 = (i % (DK / 8)) * 8;
+    u32x4 w = *reinterpret_cast<const u32x4*>(kc + (size_t)r * DK + c8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = phi_elu1(bf2f((bf16_t)(w[e] & 0xffffu)));
+      const float hi = phi_elu1(bf2f((bf16_t)(w[e] >> 16)));
+      w[e] = pack2(lo, hi);
+    }
+    *reinterpret_cast<u32x4*>(&sk[r][c8]) = w;
+  }
+  for (int i = tid; i < kC * DV / 8; i += 256) {
+    const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
+    *reinterpret_cast<u32x4*>(&sv[r][c8]) = *reinterpret_cast<const u32x4*>(vc + (size_t)r * DV + c8);
+  }
+  __syncthreads();
+  constexpr int NDT = DK / 16, NJT = DV / 16 + 1;  // the extra column tile gives dz
+  const int trow = 4 * (lane >> 4) + ((lane >> 2) & 3);
+  const int tcol = 4 * (lane & 3);
+  const int lc = lane & 15, lg = lane >> 4;
+  const bf16_t one = f2bf(1.f);
+  const bf16x8 ones = {__builtin_bit_cast(__bf16, one), __builtin_bit_cast(__bf16, one),
+                       __builtin_bit_cast(__bf16, one), __builtin_bit_cast(__bf16, one),
+                       __builtin_bit_cast(__bf16, one), __builtin_bit_cast(__bf16, one),
+                       __builtin_bit_cast(__bf16, one), __builtin_bit_cast(__bf16, one)};
+  for (int tile = wave; tile < NDT * NJT; tile += 4) {
+    const int dt = tile / NJT, jt = tile % NJT;
+    floatx4 acc = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int t0 = 32 * kb;
+      const bf16x8 a = cat_tr(ld_tr(&sk[t0 + trow][16 * dt + tcol]), ld_tr(&sk[t0 + 16 + trow][16 * dt + tcol]));
+      const bf16x8 b = jt < NJT - 1
+                           ? cat_tr(ld_tr(&sv[t0 + trow][16 * jt + tcol]), ld_tr(&sv[t0 + 16 + trow][16 * jt + tcol]))
+                           : ones;
+      acc = mfma_k32(a, b, acc);
+    }
+    // lane (lc, lg) holds rows 16dt + 4lg + i, column 16jt + lc
+    if (jt < NJT - 1) {
+      float* out = dS + chunk * DK * DV;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[(size_t)(16 * dt + 4 * lg + i) * DV + 16 * jt + lc] = acc[i];
+    } else if (lc == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dz[chunk * DK + 16 * dt + 4 * lg + i] = acc[i];
+    }
+  }
+}
+
+// In place, per (batch, head) and state element: the exclusive prefix over
+// chunks, starting from the initial state (or zero); the total is the final
+// state.  Thread e of a (batch, head) owns element e of [S (dk*dv), z (dk)].
+__global__ __launch_bounds__(256) void la_state_scan(float* __restrict__ dS, float* __restrict__ dz,
+                                                     float* S, float* z, int nch, int dkdv, int dk,
+                                                     int use_init) {
+  const long bh = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= dkdv + dk) return;
+  const bool isz = e >= dkdv;
+  const int idx = isz ? e - dkdv : e;
+  const int stride = isz ? dk : dkdv;
+  float* base = isz ? dz + (size_t)bh * nch * dk + idx : dS + (size_t)bh * nch * dkdv + idx;
+  float* fin = isz ? z + (size_t)bh * dk + idx : S + (size_t)bh * dkdv + idx;
+  float run = use_init ? *fin : 0.f;
+  int c = 0;
+  for (; c + 8 <= nch; c += 8) {  // eight loads in flight
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = base[(size_t)(c + i) * stride];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      base[(size_t)(c + i) * stride] = run;
+      run += t[i];
+    }
+  }
+  for (; c < nch; ++c) {
+    const float t = base[(size_t)c * stride];
+    base[(size_t)c * stride] = run;
+    run += t;
+  }
+  *fin = run;
+}
+
+// One workgroup (4 waves) per (batch, head, chunk): with S_c, z_c the state
+// entering the chunk (from la_state_scan),
+//   O = (phi(Q) S_c + tril(phi(Q) phi(K)^T) V) / (phi(Q) z_c + rowsum tril(...)).
+// Wave w owns tokens 16w .. 16w+15.  A operands (phi(Q) rows, rows of the
+// masked score block) are 16-byte LDS reads in natural k order; B operands
+// over tokens or key channels (V, S_c) are LDS transpose reads addressing
+// rows 8G + e and 8G + 4 + e, which gives the same natural order.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void la_chunk_out(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                    const bf16_t* __restrict__ v, const float* __restrict__ Sc,
+                                                    const float* __restrict__ zc, bf16_t* __restrict__ o) {
+  constexpr int LQ = DK + 16, LV = DV + 16, LA = kC + 16;
+  __shared__ __attribute__((aligned(16))) bf16_t sq[kC][LQ];
+  __shared__ __attribute__((aligned(16))) bf16_t sk[kC][LQ];
+  __shared__ __attribute__((aligned(16))) bf16_t sv[kC][LV];
+  __shared__ __attribute__((aligned(16))) bf16_t ss[DK][LV];   // S_c in bf16
+  __shared__ __attribute__((aligned(16))) bf16_t sa[kC][LA];   // masked scores, bf16
+  __shared__ float sz[DK];
+  __shared__ float sden[kC];
+  const size_t chunk = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lc = lane & 15, lg = lane >> 4;
+  const bf16_t* qc = q + chunk * kC * DK;
+  const bf16_t* kc = k + chunk * kC * DK;
+  const bf16_t* vc = v + chunk * kC * DV;
+  for (int i = tid; i < 2 * kC * DK / 8; i += 256) {
+    const bool isq = i < kC * DK / 8;
+    const int ii = isq ? i : i - kC * DK / 8;
+    const int r = ii / (DK / 8), c8 = (ii % (DK / 8)) * 8;
+    u32x4 w = *reinterpret_cast<const u32x4*>((isq ? qc : kc) + (size_t)r * DK + c8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = pack2(phi_elu1(bf2f((bf16_t)(w[e] & 0xffffu))), phi_elu1(bf2f((bf16_t)(w[e] >> 16))));
+    *reinterpret_cast<u32x4*>(isq ? &sq[r][c8] : &sk[r][c8]) = w;
+  }
+  for (int i = tid; i < kC * DV / 8; i += 256) {
+    const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
+    *reinterpret_cast<u32x4*>(&sv[r][c8]) = *reinterpret_cast<const u32x4*>(vc + (size_t)r * DV + c8);
+  }
+  const float* sc = Sc + chunk * DK * DV;
+  for (int i = tid; i < DK * DV / 4; i += 256) {
+    const int r = i / (DV / 4), c4 = (i % (DV / 4)) * 4;
+    const float4 x = *reinterpret_cast<const float4*>(sc + (size_t)r * DV + c4);
+    *reinterpret_cast<uint2*>(&ss[r][c4]) = make_uint2(pack2(x.x, x.y), pack2(x.z, x.w));
+  }
+  for (int i = tid; i < DK; i += 256) sz[i] = zc[chunk * DK + i];
+  __syncthreads();
+
+  const int mt = wave;  // token row block
+  // masked scores of the row block: tiles j <= mt; rowsum on the way
+  float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (j > mt) break;
+    floatx4 acc = zero4();
+    if constexpr (DK == 16) {  // one 16-deep product
+      acc = mfma_k16(*reinterpret_cast<const shortx4_t*>(&sq[16 * mt + lc][4 * lg]),
+                     *reinterpret_cast<const shortx4_t*>(&sk[16 * j + lc][4 * lg]), acc);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb)
+        acc = mfma_k32(*reinterpret_cast<const bf16x8*>(&sq[16 * mt + lc][32 * kb + 8 * lg]),
+                       *reinterpret_cast<const bf16x8*>(&sk[16 * j + lc][32 * kb + 8 * lg]), acc);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * mt + 4 * lg + i, cc = 16 * j + lc;
+      const float x = cc <= r ? acc[i] : 0.f;
+      sa[r][cc] = f2bf(x);
+      rs[i] += x;
+    }
+  }
+  for (int j = mt + 1; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sa[16 * mt + 4 * lg + i][16 * j + lc] = 0;
+  // denominators: phi(q_r).z_c (lane lc takes channels lc, lc + 16, ...)
+  // plus the row sum, summed over the 16 lanes of a lane group
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * mt + 4 * lg + i;
+    float x = rs[i];
+#pragma unroll
+    for (int c = lc; c < DK; c += 16) x += bf2f(sq[r][c]) * sz[c];
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 16);
+    if (lc == 0) sden[r] = x;
+  }
+  // one wave wrote its own score rows and denominators: wave-local ordering
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  const int trow = 8 * lg + ((lane >> 2) & 3);
+  const int tcol = 4 * (lane & 3);
+  bf16_t* oc = o + chunk * kC * DV;
+#pragma unroll
+  for (int jt = 0; jt < DV / 16; ++jt) {
+    // phi(Q) S_c (a separate accumulator: the 16-deep and 32-deep opcodes
+    // must not share one accumulation chain)
+    floatx4 aqs = zero4();
+    if constexpr (DK == 16) {
+      aqs = mfma_k16(*reinterpret_cast<const shortx4_t*>(&sq[16 * mt + lc][4 * lg]),
+                     ld_tr(&ss[4 * lg + ((lane >> 2) & 3)][16 * jt + tcol]), aqs);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) {
+        const bf16x8 b = cat_tr(ld_tr(&ss[32 * kb + trow][16 * jt + tcol]), ld_tr(&ss[32 * kb + 4 + trow][16 * jt + tcol]));
+        aqs = mfma_k32(*reinterpret_cast<const bf16x8*>(&sq[16 * mt + lc][32 * kb + 8 * lg]), b, aqs);
+      }
+    }
+    // tril(.) V over tokens 0 .. 16 mt + 15
+    floatx4 acc = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (32 * kb > 16 * mt + 15) break;
+      const bf16x8 b = cat_tr(ld_tr(&sv[32 * kb + trow][16 * jt + tcol]), ld_tr(&sv[32 * kb + 4 + trow][16 * jt + tcol]));
+      acc = mfma_k32(*reinterpret_cast<const bf16x8*>(&sa[16 * mt + lc][32 * kb + 8 * lg]), b, acc);
+    }
+    acc += aqs;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * mt + 4 * lg + i;
+      oc[(size_t)r * DV + 16 * jt + lc] = f2bf(acc[i] / sden[r]);
+    }
+  }
+}
+
+template <int DK>
+hipError_t launch_state_dk(int dv, const bf16_t* k, const bf16_t* v, float* dS, float* dz, long nchunks,
+                           hipStream_t st) {
+  switch (dv) {
+    case 16: hipLaunchKernelGGL((la_chunk_state<DK, 16>), dim3((unsigned)nchunks), dim3(256), 0, st, k, v, dS, dz); break;
+    case 32: hipLaunchKernelGGL((la_chunk_state<DK, 32>), dim3((unsigned)nchunks), dim3(256), 0, st, k, v, dS, dz); break;
+    case 64: hipLaunchKernelGGL((la_chunk_state<DK, 64>), dim3((unsigned)nchunks), dim3(256), 0, st, k, v, dS, dz); break;
+    case 128: hipLaunchKernelGGL((la_chunk_state<DK, 128>), dim3((unsigned)nchunks), dim3(256), 0, st, k, v, dS, dz); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+
+template <int DK>
+hipError_t launch_out_dk(int dv, const PrefillArgs& a, const float* Sc, const float* zc, long nchunks, hipStream_t st) {
+  const bf16_t* q = reinterpret_cast<const bf16_t*>(a.q);
+  const bf16_t* k = reinterpret_cast<const bf16_t*>(a.k);
+  const bf16_t* v = reinterpret_cast<const bf16_t*>(a.v);
+  bf16_t* o = reinterpret_cast<bf16_t*>(a.o);
+  switch (dv) {
+    case 16: hipLaunchKernelGGL((la_chunk_out<DK, 16>), dim3((unsigned)nchunks), dim3(256), 0, st, q, k, v, Sc, zc, o); break;
+    case 32: hipLaunchKernelGGL((la_chunk_out<DK, 32>), dim3((unsigned)nchunks), dim3(256), 0, st, q, k, v, Sc, zc, o); break;
+    case 64: hipLaunchKernelGGL((la_chunk_out<DK, 64>), dim3((unsigned)nchunks), dim3(256), 0, st, q, k, v, Sc, zc, o); break;
+    case 128: hipLaunchKernelGGL((la_chunk_out<DK, 128>), dim3((unsigned)nchunks), dim3(256), 0, st, q, k, v, Sc, zc, o); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_la_par_outputs(int dk, const PrefillArgs& a, void* workspace, hipStream_t st) {
+  const long nchunks = (long)a.B * a.H * (a.T / kC);
+  const float* Sc = reinterpret_cast<const float*>(workspace);
+  const float* zc = Sc + (size_t)nchunks * dk * a.dv;
+  switch (dk) {
+    case 16: return launch_out_dk<16>(a.dv, a, Sc, zc, nchunks, st);
+    case 32: return launch_out_dk<32>(a.dv, a, Sc, zc, nchunks, st);
+    case 64: return launch_out_dk<64>(a.dv, a, Sc, zc, nchunks, st);
+    case 128: return launch_out_dk<128>(a.dv, a, Sc, zc, nchunks, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+size_t la_par_workspace_bytes(int dk, const PrefillArgs& a) {
+  return (size_t)a.B * a.H * (a.T / kC) * ((size_t)dk * a.dv + dk) * sizeof(float);
+}
+
+hipError_t launch_la_par_states(int dk, const PrefillArgs& a, void* workspace, hipStream_t st) {
+  const long nchunks = (long)a.B * a.H * (a.T / kC);
+  float* dS = reinterpret_cast<float*>(workspace);
+  float* dz = dS + (size_t)nchunks * dk * a.dv;
+  const bf16_t* k = reinterpret_cast<const bf16_t*>(a.k);
+  const bf16_t* v = reinterpret_cast<const bf16_t*>(a.v);
+  hipError_t e;
+  switch (dk) {
+    case 16: e = launch_state_dk<16>(a.dv, k, v, dS, dz, nchunks, st); break;
+    case 32: e = launch_state_dk<32>(a.dv, k, v, dS, dz, nchunks, st); break;
+    case 64: e = launch_state_dk<64>(a.dv, k, v, dS, dz, nchunks, st); break;
+    case 128: e = launch_state_dk<128>(a.dv, k, v, dS, dz, nchunks, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  const int n = dk * a.dv + dk;
+  hipLaunchKernelGGL(la_state_scan, dim3((unsigned)((n + 255) / 256), (unsigned)(a.B * a.H)), dim3(256), 0, st,
+                     dS, dz, a.S, a.z, a.T / kC, dk * a.dv, dk, a.use_init);
+  return hipGetLastError();
+}
+
+}  // namespace linattn

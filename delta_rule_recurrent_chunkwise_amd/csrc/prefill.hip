@@ -515,6 +515,18 @@ static hipError_t launch_prefill_e(int dk, const PrefillArgs& a, hipStream_t st)
 }
 
 hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, hipStream_t st) {
+  if (bf16 && mode == PF_LA) {
+    // Linear attention, chunk-parallel: the chunk-start states come from a
+    // prefix over per-chunk phi(K)^T V; then every chunk's output is formed
+    // independently from its own start state.
+    void* ws = nullptr;
+    hipError_t e = hipMallocAsync(&ws, la_par_workspace_bytes(dk, a), st);
+    if (e != hipSuccess) return e;
+    e = launch_la_par_states(dk, a, ws, st);
+    if (e == hipSuccess) e = launch_la_par_outputs(dk, a, ws, st);
+    const hipError_t f = hipFreeAsync(ws, st);
+    return e != hipSuccess ? e : f;
+  }
   if (bf16 && dk == 128 && a.dv % 32 == 0) {
     if (mode == PF_DELTA) return launch_prefill_pipe(a, nullptr, st);
     if (mode == PF_GATED) {
