@@ -77,8 +77,11 @@ struct __attribute__((aligned(16))) Smem2 {
   static constexpr int kLO = DVS + 8;   // bf16 row stride of the output tile
   static constexpr int NKH = GATED ? 2 : 1;
   static constexpr int RKH = GATED ? kC : 1;
+  static constexpr int NKB = GATED ? 2 : 3;  // K buffers (see the loader schedule)
+  // K first: its buffer is chosen at run time, and fragment offsets from one
+  // base register stay within the 16-bit immediate of the LDS instructions
+  bf16_t k[NKB][kC][kLQ];     // K (gated: Gam K)
   bf16_t q[2][kC][kLQ];       // Q (gated: Gam Q)
-  bf16_t k[2][kC][kLQ];       // K (gated: Gam K)
   bf16_t kh[NKH][RKH][kLQ];   // gated: K / Gam
   bf16_t a[kC][kLT];          // tril(Q K^T), token columns permuted
   bf16_t lb[2][6][16][16];    // L_bj (b > j), transposed
@@ -227,13 +230,13 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
       bdst = bth[chunk * kC + lane];  // converted when stored
     }
   };
-  auto store_loads = [&](auto kindc, int buf, const auto& src, uint32_t bsrc) {
+  auto store_loads = [&](auto kindc, int buf, int kbi, const auto& src, uint32_t bsrc) {
     constexpr int KIND = decltype(kindc)::value;
     if constexpr (KIND == 1) {
 #pragma unroll
       for (int j = 0; j < LP::NT; ++j) {
         const int t = LP::tile_of(wave, j);
-        bf16_t(*tile)[kLQ] = t == 0 ? sm.q[buf] : (t == 1 ? sm.k[buf] : sm.kh[GATED ? buf : 0]);
+        bf16_t(*tile)[kLQ] = t == 0 ? sm.q[buf] : (t == 1 ? sm.k[kbi] : sm.kh[GATED ? buf : 0]);
         const int vv = LP::vec_of(wave, lane, j);
         *reinterpret_cast<u32x4*>(&tile[vv >> 4][(vv & 15) * 8]) = src[j];
       }
@@ -250,37 +253,64 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
     }
   };
 
+  // K buffer of chunk c: three in rotation (plain), two by parity (gated)
+  auto kidx = [&](int c) { return GATED ? (c & 1) : (c % 3); };
+
   // Every role runs its own copy of the chunk loop (the same barriers, only
   // its own registers live).  body(x, parity) runs iteration x with
   // parity = x & 1 known at compile time, so buffer and register-slot
-  // indices are static.
-  auto run = [&](auto phase1, auto phase2, auto kindc) {
+  // indices are static.  A loader's schedule SCH: 0 stores chunk x+1 in
+  // phase 1 of iteration x; 1 stores it in phase 2; 2 stores chunk x+2 in
+  // phase 2 (chunk 0 goes to LDS before the loop).  Phase 1 carries most of
+  // the LDS reads, so stores moved out of it wait less.
+  auto run = [&](auto phase1, auto phase2, auto kindc, auto schc) {
     constexpr int KIND = decltype(kindc)::value;
+    constexpr int SCH = decltype(schc)::value;
+    constexpr int LEAD = SCH == 2 ? 2 : 1;
     constexpr bool loader = KIND != 0;
     constexpr int NSL = KIND == 1 ? LP::NSLOT : 2;
     constexpr int NREG = KIND == 1 ? LP::NT : (KIND == 2 ? NSMALL : 1);
+    static_assert(LEAD == 1 || NSL == 2, "a two-chunk lead needs two register slots");
     u32x4 pf[NSL][NREG];
     uint32_t pfb[NSL] = {};
     if (loader) {
       issue_loads(kindc, 0, pf[0], pfb[0]);
-      if (NSL == 2 && nch > 1) issue_loads(kindc, 1, pf[NSL - 1], pfb[NSL - 1]);
+      if constexpr (LEAD == 2) {
+        store_loads(kindc, 0, 0, pf[0], pfb[0]);
+        issue_loads(kindc, nch > 1 ? 1 : 0, pf[1], pfb[1]);
+        issue_loads(kindc, nch > 2 ? 2 : nch - 1, pf[0], pfb[0]);
+      } else if (NSL == 2) {
+        issue_loads(kindc, nch > 1 ? 1 : 0, pf[NSL - 1], pfb[NSL - 1]);
+      }
     }
+    // The loads are issued on every path (past the last chunk they re-read
+    // it and the registers are not stored): a path without them would make
+    // the compiler assume the slot being stored holds the newest loads and
+    // wait for every outstanding load and store of the wave.
     auto body = [&](const int x, auto parity) {
       constexpr int P = decltype(parity)::value;
-      constexpr int SL = NSL == 2 ? 1 - P : 0;  // slot holding chunk x+1
+      constexpr int PC = (P + LEAD) & 1;             // parity of chunk x + LEAD
+      constexpr int SL = NSL == 2 ? PC : 0;          // its register slot
+      auto move = [&] {
+        const int c = x + LEAD;
+        if (c < nch) store_loads(kindc, PC, kidx(c), pf[SL], pfb[SL]);
+        issue_loads(kindc, c + NSL < nch ? c + NSL : nch - 1, pf[SL], pfb[SL]);
+      };
       phase1(x, parity);
-      if (loader && x + 1 < nch) {
-        store_loads(kindc, 1 - P, pf[SL], pfb[SL]);
-        if (x + 1 + NSL < nch) issue_loads(kindc, x + 1 + NSL, pf[SL], pfb[SL]);
-      }
+      if (loader && SCH == 0) move();
       lds_barrier();
       phase2(x, parity);
+      if (loader && SCH != 0) move();
       lds_barrier();
     };
-    for (int x = -1; x < nch; x += 2) {
+    // Both bodies run on every trip (no path back to the loop head skips
+    // the second one's loads); an odd chunk left over runs after the loop.
+    int x = -1;
+    for (; x + 1 < nch; x += 2) {
       body(x, std::integral_constant<int, 1>{});
-      if (x + 1 < nch) body(x + 1, std::integral_constant<int, 0>{});
+      body(x + 1, std::integral_constant<int, 0>{});
     }
+    if (x < nch) body(x, std::integral_constant<int, 1>{});
   };
 
   if (wave < NCW) {
@@ -305,10 +335,11 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
           floatx4 y[4];
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) { y[mt] = zero4(); ox[mt] = zero4(); }
+          const bf16_t(*kx)[kLQ] = sm.k[GATED ? P : kidx(x)];
           bf16x8 fk[2][4], fq[2][4];
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) {
-            fk[0][mt] = ld_frag(&sm.k[P][16 * mt + lc][8 * lg]);
+            fk[0][mt] = ld_frag(&kx[16 * mt + lc][8 * lg]);
             fq[0][mt] = ld_frag(&sm.q[P][16 * mt + lc][8 * lg]);
           }
 #pragma unroll
@@ -316,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
             if (kb < 3) {
 #pragma unroll
               for (int mt = 0; mt < 4; ++mt) {
-                fk[(kb + 1) & 1][mt] = ld_frag(&sm.k[P][16 * mt + lc][32 * (kb + 1) + 8 * lg]);
+                fk[(kb + 1) & 1][mt] = ld_frag(&kx[16 * mt + lc][32 * (kb + 1) + 8 * lg]);
                 fq[(kb + 1) & 1][mt] = ld_frag(&sm.q[P][16 * mt + lc][32 * (kb + 1) + 8 * lg]);
               }
             }
@@ -371,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
               zero4());
           // K^T fragments (K^ when gated): row 16t + c of the A operand is key
           // channel perm32(16t + c); its k-elements are the tokens of u's pairing.
-          const bf16_t(*kt)[kLQ] = GATED ? sm.kh[GATED ? P : 0] : sm.k[P];
+          const bf16_t(*kt)[kLQ] = GATED ? sm.kh[GATED ? P : 0] : sm.k[kidx(x)];
           const int trow = 4 * lg + ((lane >> 2) & 3);
           auto kt_frag = [&](int t, int tok0) {
             const int cc = 32 * (t >> 1) + 4 * (t & 1) + 8 * (lane & 3);
@@ -411,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) sm.o[16 * mt + 4 * lg + i][col] = f2bf(ox[mt][i]);
         },
-        std::integral_constant<int, 0>{});
+        std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
@@ -455,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
           *reinterpret_cast<u32x4*>(&sm.d[lg][lc][0]) = w0;
           *reinterpret_cast<u32x4*>(&sm.d[lg][lc][8]) = w1;
         },
-        [&](const int x, auto parity) {}, std::integral_constant<int, 0>{});
+        [&](const int x, auto parity) {}, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
   } else if (wave == 2 || wave == 3 || wave == 7) {
     // ======================= product waves =======================
     // Row blocks I0..I1: tril(Q K^T) of chunk x in phase 1, L of chunk x+1
@@ -468,7 +499,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
           [&](const int x, auto parity) {
             constexpr int P = decltype(parity)::value;
             if (x < 0) return;
-            const bf16_t(*rt)[kLQ] = GATED ? sm.kh[GATED ? P : 0] : sm.k[P];
+            const bf16_t(*rt)[kLQ] = GATED ? sm.kh[GATED ? P : 0] : sm.k[kidx(x)];
 #pragma unroll
             for (int i = I0; i <= I1; ++i) {
               bf16x8 fq[4], fb[4][4];
@@ -498,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
           [&](const int x, auto parity) {
             constexpr int nb = 1 - decltype(parity)::value;  // buffer of chunk x+1
             if (x + 1 >= nch) return;
-            const bf16_t(*rt)[kLQ] = GATED ? sm.kh[GATED ? nb : 0] : sm.k[nb];
+            const bf16_t(*rt)[kLQ] = GATED ? sm.kh[GATED ? nb : 0] : sm.k[kidx(x + 1)];
 #pragma unroll
             for (int i = I0; i <= I1; ++i) {
               bf16x8 fl[4], fb[4][4];
@@ -508,7 +539,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
                 for (int kb = 0; kb < 4; ++kb) fb[j][kb] = ld_frag(&rt[16 * j + lc][32 * kb + 8 * lg]);
 #pragma unroll
               for (int kb = 0; kb < 4; ++kb)  // left operand: K (gated: Gam K)
-                fl[kb] = GATED ? ld_frag(&sm.k[nb][16 * i + lc][32 * kb + 8 * lg]) : fb[i][kb];
+                fl[kb] = GATED ? ld_frag(&sm.k[GATED ? nb : 0][16 * i + lc][32 * kb + 8 * lg]) : fb[i][kb];
               floatx4 acc[4];
 #pragma unroll
               for (int j = 0; j <= i; ++j) {
@@ -536,7 +567,8 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
               }
             }
           },
-          std::integral_constant<int, (I0 == 0 && I1 == 1) ? 2 : 0>{});  // wave 7 loads v, beta
+          std::integral_constant<int, (I0 == 0 && I1 == 1) ? 2 : 0>{},  // wave 7 loads v, beta
+          std::integral_constant<int, 0>{});
     };
     if (wave == 2) prod(std::integral_constant<int, 3>{}, std::integral_constant<int, 3>{});
     else if (wave == 3) prod(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
@@ -559,8 +591,12 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
       if (wave == 4 && x >= 1) store_o(x - 1);
     };
     auto ph2 = [&](const int x, auto parity) {};
-    if (LP::is_tile_wave(wave)) run(ph1, ph2, std::integral_constant<int, 1>{});
-    else run(ph1, ph2, std::integral_constant<int, 0>{});
+    // plain: Q of chunk x+1 and K of chunk x+2 are stored in phase 2 of x
+    // (K(x+1) is read then, for L(x+1)); gated: both in phase 1
+    if (!GATED && wave == 4) run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, GATED ? 0 : 1>{});
+    else if (!GATED && wave == 5) run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, GATED ? 0 : 2>{});
+    else if (LP::is_tile_wave(wave)) run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+    else run(ph1, ph2, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
     if (wave == 4) store_o(nch - 1);
   }
 }
@@ -634,7 +670,9 @@ hipError_t launch_pipe_t(const PipeArgs& p, long bh, int dv, hipStream_t st) {
   // 32 value columns per workgroup, or 16 when 32-column slices would leave
   // compute units idle (few (batch, head) pairs, as with long sequences)
   int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
   if (bh * (dv / 32) < cus && dv % 16 == 0) {
     hipLaunchKernelGGL((prefill_pipe<GATED, 16>), dim3((unsigned)(bh * (dv / 16))), dim3(kThreads), 0, st, p);
   } else {
