@@ -50,8 +50,9 @@ ROW_PROFILES = [
     ("prefill_pipe_gated_B1_H32_T32768_d128.txt",
      "gated deltanet_prefill B=1 H=32 T=32768 dk=dv=128 bf16: gate pre-pass + pipelined kernel",
      ["gate_prep", "prefill_pipe<true, 16>"]),
-    ("prefill_kernel_la_B8_H12_T1024_d64.txt", "la_prefill B=8 H=12 T=1024 dk=dv=64 bf16",
-     ["prefill_kernel<64, linattn::BF16, 0, 32>"]),
+    ("la_par_B8_H12_T1024_d64.txt",
+     "la_prefill B=8 H=12 T=1024 dk=dv=64 bf16: chunk states, state scan, chunk outputs",
+     ["la_chunk_state<64, 64>", "la_state_scan", "la_chunk_out<64, 64>"]),
     ("prefill_kernel_la_fp32_B1_H2_T64_d16.txt", "la_prefill B=1 H=2 T=64 dk=dv=16 fp32",
      ["prefill_kernel<16, linattn::F32, 0, 16>"]),
     ("decode_kernel_la_N256_H32_d128.txt", "la_decode_step N=256 H=32 dk=dv=128, fp32 S and z",
@@ -343,7 +344,8 @@ def bench_rows(la, workloads, torch, launches=20):
     us, med = _time_launches(torch, stream, run_g, [d], max(3, launches // 4), warmup=1)
     per = w.B * w.H * (w.T * 2 * (3 * w.dk + 2 * w.dv + 1) + w.dk * w.dv * 4)
     name, r = _row("deltanet_prefill_gated", f"deltanet_prefill (gated) {w.name}", us, med, per,
-                   "serial chain over 512 chunks; 32 heads x 4 value slices = 128 workgroups")
+                   "gate pre-pass, then a serial chain over 512 chunks; 32 heads x 8 value "
+                   "slices of 16 = 256 workgroups")
     rows[name] = r
     del d
     wd = W[4]
