@@ -33,12 +33,15 @@
  *           points must be 16-byte aligned (they are read in 16-byte
  *           vectors).  o must not alias any input.  S (and z) are read and written.  The
  *           library keeps no state between calls; calls are re-entrant.  It
- *           allocates device memory in one case only: the gated
- *           deltanet_prefill with bf16 inputs, dk = 128 and dv % 32 == 0
- *           takes a stream-ordered workspace (hipMallocAsync on `stream`,
- *           released with hipFreeAsync after its kernels) of
- *           6 B*H*T*dk + 4 B*H*(T/64)*dk bytes for the decay-scaled q and k;
- *           a failed allocation returns LA_ERR_LAUNCH.
+ *           allocates device memory in two cases, each a stream-ordered
+ *           workspace (hipMallocAsync on `stream`, released with
+ *           hipFreeAsync after its kernels):
+ *             - the gated deltanet_prefill with bf16 inputs, dk = 128 and
+ *               dv % 32 == 0: 6 B*H*T*dk + 4 B*H*(T/64)*dk bytes for the
+ *               decay-scaled q and k;
+ *             - la_prefill with bf16 inputs: 4 B*H*(T/64)*(dk*dv + dk)
+ *               bytes for the state and normaliser entering each chunk.
+ *           A failed allocation returns LA_ERR_LAUNCH.
  * Sizes.    B, H (or N, H) >= 1; T >= 1 and T a multiple of 64 for prefill;
  *           dk and dv each one of 16, 32, 64, 128.  The per-channel gated
  *           prefill with LA_DTYPE_F32 supports dk <= 64.
