@@ -106,6 +106,25 @@ def recorded_traffic(name, digest):
     return float(rec["hbm_bytes_per_launch"])
 
 
+def recorded_counters(name, digest):
+    """MFMA and LDS figures per launch from the counter section of a summary
+    in profiles/, if it was taken on the current kernel source; else None."""
+    rec = {}
+    try:
+        with open(os.path.join(PROFILES, name)) as f:
+            for ln in f:
+                key, sep, val = ln.partition(":")
+                if sep:
+                    rec[key.strip()] = val.split()[0] if val.split() else ""
+    except OSError:
+        return None
+    keys = ("mfma_bf16_flops_per_launch", "mfma_busy_frac", "lds_active_frac",
+            "lds_bank_conflict_frac", "effective_clock_ghz")
+    if rec.get("kernel_sources_sha256") != digest or any(k not in rec for k in keys):
+        return None
+    return {k: float(rec[k]) for k in keys}
+
+
 def _csv_rows(directory, suffix):
     import csv
     import glob
@@ -122,6 +141,44 @@ def _counter_mean(directory, counter, kernel):
     if not vals:
         raise SystemExit(f"no {counter} rows for kernel '{kernel}' under {directory}")
     return sum(vals) / len(vals), len(vals)
+
+
+PREFILL_SQ_SETS = {
+    # one rocprofv3 run each (at most 8 SQ and 2 GRBM counters per run)
+    "mfma": ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"],
+    "lds": ["SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", "SQ_WAVE_CYCLES"],
+}
+
+
+def _prefill_counter_lines(prof_dir, kname, avg_ns):
+    """MFMA and LDS activity of the prefill kernel from two counter runs.
+    Counter values are summed over the GPU per dispatch: MFMA busy cycles
+    over the 1024 SIMDs, LDS cycles over the 256 CUs, GRBM_GUI_ACTIVE over
+    the 8 XCDs (so GRBM / 8 is the kernel's length in cycles)."""
+    m = {}
+    for tag, counters in PREFILL_SQ_SETS.items():
+        for c in counters:
+            m[c] = _counter_mean(os.path.join(prof_dir, f"pmc_{tag}_prefill"), c, kname)[0]
+    cycles = m["GRBM_GUI_ACTIVE"] / 8.0
+    flops = m["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0
+    alg_flops = prefill_algorithmic(4, 16, 4096, 128, 128)[1]
+    cmd = ("cd /tmp && rocprofv3 --pmc {cs} -f csv -d $R/gpurun_out/prof/pmc_{t}_prefill -o pmc "
+           "-- python3 $R/bench.py --only prefill --steps 5 --warmup 1 --decode-steps 20")
+    out = ["", "## MFMA and LDS counters, one run per set"]
+    out += [f"#   {cmd.format(cs=' '.join(cs), t=t)}" for t, cs in PREFILL_SQ_SETS.items()]
+    out += [f"{c.lower()}_per_dispatch: {m[c]:.0f}" for cs in PREFILL_SQ_SETS.values() for c in cs]
+    out += [
+        f"kernel_cycles (GRBM_GUI_ACTIVE / 8): {cycles:.0f}",
+        f"effective_clock_ghz: {cycles / avg_ns:.3f}   (cycles / traced average ns)",
+        f"mfma_bf16_flops_per_launch: {flops:.4g}   (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)",
+        f"algorithmic_flops_per_launch: {alg_flops:.4g}",
+        f"executed_over_algorithmic_flops: {flops / alg_flops:.3f}",
+        f"mfma_busy_frac: {m['SQ_VALU_MFMA_BUSY_CYCLES'] / (cycles * 1024):.4f}   "
+        "(MFMA busy cycles / (kernel cycles x 1024 SIMDs))",
+        f"lds_active_frac: {m['SQ_LDS_IDX_ACTIVE'] / (cycles * 256):.4f}   (LDS active cycles / (kernel cycles x 256 CUs))",
+        f"lds_bank_conflict_frac: {m['SQ_LDS_BANK_CONFLICT'] / (cycles * 256):.4f}   (of the same)",
+    ]
+    return out
 
 
 def summarize(prof_dir):
@@ -190,6 +247,8 @@ def summarize(prof_dir):
             f"algorithmic_bytes_per_launch: {alg}",
             f"traffic_over_algorithmic: {(fetch + write) / alg:.3f}",
         ]
+        if mode == "prefill":
+            lines += _prefill_counter_lines(prof_dir, kname, float(row["AverageNs"]))
         os.makedirs(PROFILES, exist_ok=True)
         with open(os.path.join(PROFILES, fname), "w") as f:
             f.write("\n".join(lines) + "\n")
@@ -385,6 +444,67 @@ def bench_rows(la, workloads, torch, launches=20):
     return rows
 
 
+def measured_peaks(torch, reps=5):
+    """Rates this GPU sustains in the same run, from libpeak_probe.so (built
+    with the library): a copy between two buffers (the prefill's pattern:
+    inputs read, outputs written elsewhere) and an in-place update (the
+    decode's pattern), both averaged over back-to-back launches, and a dense
+    bf16 MFMA loop (32x32x16 tiles; random operands draw more power than
+    zeros, and the clock follows), best of `reps` launches."""
+    import ctypes
+    path = os.path.join(ROOT, "delta_rule_recurrent_chunkwise_amd", "libpeak_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m delta_rule_recurrent_chunkwise_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    lib.peak_probe_mfma_bf16.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp]
+    lib.peak_probe_stream.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = vp(stream.cuda_stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def best_ms(launch):
+        best = None
+        for _ in range(reps + 1):  # the first launch is a warm-up
+            ev[0].record(stream)
+            rc = launch()
+            ev[1].record(stream)
+            ev[1].synchronize()
+            if rc != 0:
+                raise RuntimeError(f"peak probe returned {rc}")
+            ms = ev[0].elapsed_time(ev[1])
+            best = ms if best is None else min(best, ms)
+        return best
+
+    def avg_ms(launch, n=20):
+        for _ in range(3):
+            launch()
+        ev[0].record(stream)
+        for _ in range(n):
+            if launch() != 0:
+                raise RuntimeError("peak probe launch failed")
+        ev[1].record(stream)
+        ev[1].synchronize()
+        return ev[0].elapsed_time(ev[1]) / n
+
+    nbytes = 512 << 20  # the decode state's size, above the 256 MB Infinity Cache
+    src = torch.ones(nbytes // 4, device=dev, dtype=torch.float32)
+    dst = torch.empty_like(src)
+    copy_gbs = 2 * nbytes / (avg_ms(lambda: lib.peak_probe_stream(src.data_ptr(), dst.data_ptr(), nbytes, 0, sp)) * 1e-3) / 1e9
+    rmw_gbs = 2 * nbytes / (avg_ms(lambda: lib.peak_probe_stream(src.data_ptr(), None, nbytes, 1, sp)) * 1e-3) / 1e9
+    del src, dst
+    blocks, iters = 256 * 4, 4000
+    seed = torch.rand(64, device=dev, dtype=torch.float32)
+    sink = torch.empty(blocks * 256, device=dev, dtype=torch.float32)
+    ms = best_ms(lambda: lib.peak_probe_mfma_bf16(seed.data_ptr(), sink.data_ptr(), blocks, iters, sp))
+    mfma_tflops = blocks * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12
+    return {"copy_gbs": copy_gbs, "in_place_gbs": rmw_gbs, "mfma_bf16_tflops": mfma_tflops,
+            "note": "measured before the timed work (libpeak_probe.so): a 512 MiB copy between two "
+                    "buffers and a 512 MiB in-place update, 20 back-to-back launches each (read + "
+                    "write bytes); a dense 32x32x16 bf16 MFMA loop on random operands, best of 5"}
+
+
 def copy_probe(torch, nbytes=1 << 30, reps=5):
     """A plain device copy of known size (used to calibrate HBM counters)."""
     dev = torch.device("cuda:0")
@@ -481,6 +601,9 @@ def main():
         print(json.dumps({"decode_us_per_step": el / args.decode_steps * 1e6}))
         return
 
+    # peak rates first, while the GPU is still cool (clocks drop under the
+    # sustained load that follows)
+    peaks = measured_peaks(torch) if args.only == "all" else None
     w, pinp, wall, kms = bench_prefill(la, workloads, torch, args.steps, args.warmup)
     B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
     ms_per_step = wall / args.steps * 1e3
@@ -512,8 +635,13 @@ def main():
                      "median_launch_us": kms[len(kms) // 2] * 1e3},
         "mfma": {"achieved": pflops / avg_kernel_s / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
                  "unit": "TFLOP/s", "frac": pflops / avg_kernel_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                 "algorithmic_flops_per_launch": pflops},
+                 "algorithmic_flops_per_launch": pflops,
+                 "counters": recorded_counters(PREFILL_PROFILE, sources_digest(PREFILL_SOURCES))},
     }
+    if peaks is not None:
+        line["measured_peaks"] = peaks
+        line["roofline"]["frac_of_measured_copy"] = achieved / peaks["copy_gbs"]
+        line["mfma"]["frac_of_measured_peak"] = line["mfma"]["achieved"] / peaks["mfma_bf16_tflops"]
     dinp = None
     if args.only == "all":
         wd, dinp, el = bench_decode(la, workloads, torch, args.decode_steps)
@@ -527,6 +655,7 @@ def main():
                                    "fp32 state in place, bf16 token inputs (ring of 16)"},
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": dtraffic,
+                         "frac_of_measured_in_place": gbs / peaks["in_place_gbs"],
                          "kernel": "decode_kernel<128, 128, BF16, DEC_DELTA>",
                          "avg_launch_us": el / args.decode_steps * 1e6,
                          "algorithmic_bytes_per_launch": dbytes},

@@ -19,6 +19,9 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "liblinattn.so")
 SOURCES = ["api.hip", "decode.hip", "prefill.hip", "prefill_pipe.hip", "la_par.hip"]
+# the measurement harness's MFMA peak probe, a library of its own
+PROBE_PATH = os.path.join(HERE, "libpeak_probe.so")
+PROBE_SOURCE = "peak_probe.hip"
 
 ARCH = "gfx950"
 FLAGS = [
@@ -46,18 +49,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path):
+    tmp = path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"linking liblinattn.so failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+        raise RuntimeError(f"linking {os.path.basename(path)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        objs = list(ex.map(_compile, SOURCES + [PROBE_SOURCE]))
+    _link(objs[:-1], LIB_PATH)
+    _link(objs[-1:], PROBE_PATH)
     if verbose:
         print(f"built {LIB_PATH}")
+        print(f"built {PROBE_PATH}")
     return LIB_PATH
 
 

@@ -133,3 +133,21 @@ def test_python_binding_rejects_cpu_tensors():
         la.deltanet_prefill(q, q, q, torch.zeros(1, 1, 64))
     with pytest.raises(ValueError):
         la.la_prefill(q, q, q)
+
+
+def test_peak_probe_library_loads_and_rejects_bad_arguments():
+    """The measurement harness's peak probes (libpeak_probe.so, not part of the
+    linattn ABI) check their arguments before any launch."""
+    path = os.path.join(ROOT, "delta_rule_recurrent_chunkwise_amd", "libpeak_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("libpeak_probe.so not built")
+    lib = ctypes.CDLL(path)
+    lib.peak_probe_mfma_bf16.argtypes = [P, P, ctypes.c_int, ctypes.c_int, P]
+    lib.peak_probe_stream.argtypes = [P, P, ctypes.c_size_t, ctypes.c_int, P]
+    assert lib.peak_probe_mfma_bf16(None, FAKE, 1, 1, None) == -1
+    assert lib.peak_probe_mfma_bf16(FAKE, FAKE, 0, 1, None) == -1
+    assert lib.peak_probe_mfma_bf16(FAKE, FAKE, 1, 0, None) == -1
+    assert lib.peak_probe_stream(None, FAKE, 1 << 15, 0, None) == -1
+    assert lib.peak_probe_stream(FAKE, None, 1 << 15, 0, None) == -1      # copy needs dst
+    assert lib.peak_probe_stream(FAKE, FAKE, (1 << 15) + 16, 0, None) == -1  # not whole tiles
+    assert lib.peak_probe_stream(MISALIGNED, FAKE, 1 << 15, 1, None) == -1
