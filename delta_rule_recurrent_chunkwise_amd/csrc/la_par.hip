@@ -6,8 +6,9 @@
 // state, so with 64-token chunks the state entering chunk c is
 //   S_c = S_0 + sum_{c' < c} phi(K_c')^T V_c',   z_c = z_0 + sum_{c' < c} colsum phi(K_c').
 // la_chunk_state forms every chunk's phi(K)^T V and colsum phi(K) in
-// parallel; la_state_scan turns them, in place, into S_c and z_c (and
-// writes the final state); the chunk outputs are then independent.
+// parallel; la_state_scan turns them into S_c (bf16, the precision the
+// output products read it in) and z_c (fp32, in place) and writes the final
+// state; the chunk outputs are then independent.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -98,21 +99,29 @@ __global__ __launch_bounds__(256) void la_chunk_state(const bf16_t* __restrict__
   }
 }
 
-// In place, per (batch, head) and state element: the exclusive prefix over
-// chunks, starting from the initial state (or zero); the total is the final
-// state.  Thread e of a (batch, head) owns element e of [S (dk*dv), z (dk)].
-__global__ __launch_bounds__(256) void la_state_scan(float* __restrict__ dS, float* __restrict__ dz,
-                                                     float* S, float* z, int nch, int dkdv, int dk,
-                                                     int use_init) {
+// Per (batch, head) and state element: the exclusive prefix over chunks,
+// starting from the initial state (or zero); the total is the final state.
+// Thread e of a (batch, head) owns element e of [S (dk*dv), z (dk)].  The
+// prefix of S goes to Sb in bf16 (rounded to nearest even); that of z
+// replaces dz in place.
+__global__ __launch_bounds__(256) void la_state_scan(const float* __restrict__ dS, float* __restrict__ dz,
+                                                     bf16_t* __restrict__ Sb, float* S, float* z, int nch,
+                                                     int dkdv, int dk, int use_init) {
   const long bh = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= dkdv + dk) return;
   const bool isz = e >= dkdv;
   const int idx = isz ? e - dkdv : e;
   const int stride = isz ? dk : dkdv;
-  float* base = isz ? dz + (size_t)bh * nch * dk + idx : dS + (size_t)bh * nch * dkdv + idx;
+  const float* base = isz ? dz + (size_t)bh * nch * dk + idx : dS + (size_t)bh * nch * dkdv + idx;
+  float* zout = dz + (size_t)bh * nch * dk + idx;
+  bf16_t* sout = Sb + (size_t)bh * nch * dkdv + idx;
   float* fin = isz ? z + (size_t)bh * dk + idx : S + (size_t)bh * dkdv + idx;
   float run = use_init ? *fin : 0.f;
+  auto put = [&](int c, float val) {
+    if (isz) zout[(size_t)c * stride] = val;
+    else sout[(size_t)c * stride] = f2bf(val);
+  };
   int c = 0;
   for (; c + 8 <= nch; c += 8) {  // eight loads in flight
     float t[8];
@@ -120,20 +129,20 @@ __global__ __launch_bounds__(256) void la_state_scan(float* __restrict__ dS, flo
     for (int i = 0; i < 8; ++i) t[i] = base[(size_t)(c + i) * stride];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      base[(size_t)(c + i) * stride] = run;
+      put(c + i, run);
       run += t[i];
     }
   }
   for (; c < nch; ++c) {
     const float t = base[(size_t)c * stride];
-    base[(size_t)c * stride] = run;
+    put(c, run);
     run += t;
   }
   *fin = run;
 }
 
-// One workgroup (4 waves) per (batch, head, chunk): with S_c, z_c the state
-// entering the chunk (from la_state_scan),
+// One workgroup (4 waves) per (batch, head, chunk): with S_c (bf16), z_c the
+// state entering the chunk (from la_state_scan),
 //   O = (phi(Q) S_c + tril(phi(Q) phi(K)^T) V) / (phi(Q) z_c + rowsum tril(...)).
 // Wave w owns tokens 16w .. 16w+15.  A operands (phi(Q) rows, rows of the
 // masked score block) are 16-byte LDS reads in natural k order; B operands
@@ -141,7 +150,7 @@ __global__ __launch_bounds__(256) void la_state_scan(float* __restrict__ dS, flo
 // rows 8G + e and 8G + 4 + e, which gives the same natural order.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void la_chunk_out(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                                                    const bf16_t* __restrict__ v, const float* __restrict__ Sc,
+                                                    const bf16_t* __restrict__ v, const bf16_t* __restrict__ Sc,
                                                     const float* __restrict__ zc, bf16_t* __restrict__ o) {
   constexpr int LQ = DK + 16, LV = DV + 16, LA = kC + 16;
   __shared__ __attribute__((aligned(16))) bf16_t sq[kC][LQ];
@@ -171,11 +180,10 @@ __global__ __launch_bounds__(256) void la_chunk_out(const bf16_t* __restrict__ q
     const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
     *reinterpret_cast<u32x4*>(&sv[r][c8]) = *reinterpret_cast<const u32x4*>(vc + (size_t)r * DV + c8);
   }
-  const float* sc = Sc + chunk * DK * DV;
-  for (int i = tid; i < DK * DV / 4; i += 256) {
-    const int r = i / (DV / 4), c4 = (i % (DV / 4)) * 4;
-    const float4 x = *reinterpret_cast<const float4*>(sc + (size_t)r * DV + c4);
-    *reinterpret_cast<uint2*>(&ss[r][c4]) = make_uint2(pack2(x.x, x.y), pack2(x.z, x.w));
+  const bf16_t* sc = Sc + chunk * DK * DV;
+  for (int i = tid; i < DK * DV / 8; i += 256) {
+    const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
+    *reinterpret_cast<u32x4*>(&ss[r][c8]) = *reinterpret_cast<const u32x4*>(sc + (size_t)r * DV + c8);
   }
   for (int i = tid; i < DK; i += 256) sz[i] = zc[chunk * DK + i];
   __syncthreads();
@@ -273,7 +281,7 @@ hipError_t launch_state_dk(int dv, const bf16_t* k, const bf16_t* v, float* dS, 
 
 
 template <int DK>
-hipError_t launch_out_dk(int dv, const PrefillArgs& a, const float* Sc, const float* zc, long nchunks, hipStream_t st) {
+hipError_t launch_out_dk(int dv, const PrefillArgs& a, const bf16_t* Sc, const float* zc, long nchunks, hipStream_t st) {
   const bf16_t* q = reinterpret_cast<const bf16_t*>(a.q);
   const bf16_t* k = reinterpret_cast<const bf16_t*>(a.k);
   const bf16_t* v = reinterpret_cast<const bf16_t*>(a.v);
@@ -292,8 +300,9 @@ hipError_t launch_out_dk(int dv, const PrefillArgs& a, const float* Sc, const fl
 
 hipError_t launch_la_par_outputs(int dk, const PrefillArgs& a, void* workspace, hipStream_t st) {
   const long nchunks = (long)a.B * a.H * (a.T / kC);
-  const float* Sc = reinterpret_cast<const float*>(workspace);
-  const float* zc = Sc + (size_t)nchunks * dk * a.dv;
+  const float* dS = reinterpret_cast<const float*>(workspace);
+  const float* zc = dS + (size_t)nchunks * dk * a.dv;
+  const bf16_t* Sc = reinterpret_cast<const bf16_t*>(zc + (size_t)nchunks * dk);
   switch (dk) {
     case 16: return launch_out_dk<16>(a.dv, a, Sc, zc, nchunks, st);
     case 32: return launch_out_dk<32>(a.dv, a, Sc, zc, nchunks, st);
@@ -303,8 +312,10 @@ hipError_t launch_la_par_outputs(int dk, const PrefillArgs& a, void* workspace, 
   }
 }
 
+// [dS: fp32 nchunks x dk x dv][dz, then z_c: fp32 nchunks x dk][S_c: bf16 nchunks x dk x dv]
 size_t la_par_workspace_bytes(int dk, const PrefillArgs& a) {
-  return (size_t)a.B * a.H * (a.T / kC) * ((size_t)dk * a.dv + dk) * sizeof(float);
+  const size_t nchunks = (size_t)a.B * a.H * (a.T / kC);
+  return nchunks * ((size_t)dk * a.dv + dk) * sizeof(float) + nchunks * dk * a.dv * sizeof(bf16_t);
 }
 
 hipError_t launch_la_par_states(int dk, const PrefillArgs& a, void* workspace, hipStream_t st) {
@@ -323,8 +334,9 @@ hipError_t launch_la_par_states(int dk, const PrefillArgs& a, void* workspace, h
   }
   if (e != hipSuccess) return e;
   const int n = dk * a.dv + dk;
+  bf16_t* Sb = reinterpret_cast<bf16_t*>(dz + (size_t)nchunks * dk);
   hipLaunchKernelGGL(la_state_scan, dim3((unsigned)((n + 255) / 256), (unsigned)(a.B * a.H)), dim3(256), 0, st,
-                     dS, dz, a.S, a.z, a.T / kC, dk * a.dv, dk, a.use_init);
+                     dS, dz, Sb, a.S, a.z, a.T / kC, dk * a.dv, dk, a.use_init);
   return hipGetLastError();
 }
 

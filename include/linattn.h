@@ -39,8 +39,10 @@
  *             - the gated deltanet_prefill with bf16 inputs, dk = 128 and
  *               dv % 32 == 0: 6 B*H*T*dk + 4 B*H*(T/64)*dk bytes for the
  *               decay-scaled q and k;
- *             - la_prefill with bf16 inputs: 4 B*H*(T/64)*(dk*dv + dk)
- *               bytes for the state and normaliser entering each chunk.
+ *             - la_prefill with bf16 inputs: 6 B*H*(T/64)*dk*dv +
+ *               4 B*H*(T/64)*dk bytes for the per-chunk state increments
+ *               (fp32), the state entering each chunk (bf16) and the
+ *               normaliser entering each chunk (fp32).
  *           A failed allocation returns LA_ERR_LAUNCH.
  * Sizes.    B, H (or N, H) >= 1; T >= 1 and T a multiple of 64 for prefill;
  *           dk and dv each one of 16, 32, 64, 128.  The per-channel gated
