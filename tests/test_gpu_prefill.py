@@ -92,14 +92,17 @@ def test_float32_gated_dk128_is_rejected():
     assert e.value.code == -4
 
 
-def test_single_chunk_and_long_sequence():
-    """T = 64 (one chunk) and T = 1024 (sixteen chunks), bf16, d = 128."""
+@pytest.mark.parametrize("gated", [False, True], ids=["delta", "gated"])
+def test_short_and_long_sequences(gated):
+    """T = 64, 128, 320 and 1024 (1, 2, 5 and 16 chunks), bf16, d = 128: the
+    pipelined kernel's loop runs its bodies in pairs with an odd one after,
+    and its loaders start one or two chunks ahead."""
     dev = require_gpu()
-    for T in (64, 1024):
-        inp = workloads.make_delta(1, 2, T, 128, 128, torch.bfloat16, seed=T, gated=True)
-        o, S = _run_delta(inp, dev, True, False)
+    for T in (64, 128, 320, 1024):
+        inp = workloads.make_delta(1, 2, T, 128, 128, torch.bfloat16, seed=T + gated, gated=gated)
+        o, S = _run_delta(inp, dev, gated, False)
         o_ref, S_ref = oracle.delta_recurrent(inp["q"], inp["k"], inp["v"], inp["beta"],
-                                              inp["g"])
+                                              inp.get("g"))
         assert_close(o, o_ref, 2e-2, f"o T={T}")
         assert_close(S, S_ref, 2e-2, f"S T={T}")
 
