@@ -77,8 +77,14 @@ __device__ __forceinline__ floatx4 mfma_f32(float a, float b, floatx4 c) {
 // ---------------------------------------------------------------------------
 // Operand packing
 // ---------------------------------------------------------------------------
+// two floats -> two bf16 (round to nearest even) in one word; written as a
+// vector conversion so that it is one two-source convert instruction (a pair
+// of scalar conversions became two converts plus a shift and an or)
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  typedef float float2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const float2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 __device__ __forceinline__ bf16x8 words_to_bf16x8(uint32_t w0, uint32_t w1, uint32_t w2,
                                                    uint32_t w3) {

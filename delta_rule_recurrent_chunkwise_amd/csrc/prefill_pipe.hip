@@ -462,20 +462,21 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
 #pragma unroll
             for (int m4 = 0; m4 < i; m4 += 4)
               lr[i][m4 >> 2] = *reinterpret_cast<const float4*>(lbk + i * kLR + m4);
-          float tv[16];
+          // right-looking: once x_m is known it is folded into the partial
+          // sums of every later row, so one multiply-add separates x_m from
+          // x_{m+1} (x_m = 0 for m < lc, x_lc = 1)
+          float tv[16], ps[16];
 #pragma unroll
-          for (int m = 0; m < 16; ++m) tv[m] = m == lc ? 1.f : 0.f;
+          for (int i = 0; i < 16; ++i) ps[i] = 0.f;
 #pragma unroll
-          for (int i = 1; i < 16; ++i) {
-            float s0 = 0.f, s1 = 0.f;
+          for (int m = 0; m < 16; ++m) {
+            tv[m] = m < lc ? 0.f : (m == lc ? 1.f : -ps[m]);
 #pragma unroll
-            for (int m = 0; m < i; ++m) {
+            for (int i = m + 1; i < 16; ++i) {
               const float4 q4 = lr[i][m >> 2];
               const float lv = (m & 3) == 0 ? q4.x : (m & 3) == 1 ? q4.y : (m & 3) == 2 ? q4.z : q4.w;
-              if (m & 1) s1 += lv * tv[m];
-              else s0 += lv * tv[m];
+              ps[i] += lv * tv[m];
             }
-            if (i > lc) tv[i] = -(s0 + s1);
           }
           u32x4 w0, w1;
 #pragma unroll
