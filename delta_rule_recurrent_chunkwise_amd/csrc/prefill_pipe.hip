@@ -510,21 +510,23 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
               for (int j = 0; j <= i; ++j)
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) fb[j][kb] = ld_frag(&rt[16 * j + lc][32 * kb + 8 * lg]);
+              // the transposed product K Q^T: lane (lc, lg) gets row 16i + lc,
+              // columns 16j + 4lg .. +3, which the token-column permutation
+              // for the chain's pairing keeps contiguous: one 8-byte store
               floatx4 acc[4];
 #pragma unroll
               for (int j = 0; j <= i; ++j) {
                 acc[j] = zero4();
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) acc[j] = mfma_k32(fq[kb], fb[j][kb], acc[j]);
+                for (int kb = 0; kb < 4; ++kb) acc[j] = mfma_k32(fb[j][kb], fq[kb], acc[j]);
               }
-              // token columns permuted for the chain's pairing
 #pragma unroll
-              for (int j = 0; j <= i; ++j)
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                  const int r = 16 * i + 4 * lg + ii, cc = 16 * j + lc;
-                  sm.a[r][perm32(cc)] = f2bf(cc <= r ? acc[j][ii] : 0.f);
-                }
+              for (int j = 0; j <= i; ++j) {
+                const int r = 16 * i + lc, c0 = 16 * j + 4 * lg;
+                const float e0 = c0 <= r ? acc[j][0] : 0.f, e1 = c0 + 1 <= r ? acc[j][1] : 0.f;
+                const float e2 = c0 + 2 <= r ? acc[j][2] : 0.f, e3 = c0 + 3 <= r ? acc[j][3] : 0.f;
+                *reinterpret_cast<uint2*>(&sm.a[r][perm32(c0)]) = make_uint2(pack2(e0, e1), pack2(e2, e3));
+              }
             }
           },
           [&](const int x, auto parity) {
@@ -541,12 +543,16 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
 #pragma unroll
               for (int kb = 0; kb < 4; ++kb)  // left operand: K (gated: Gam K)
                 fl[kb] = GATED ? ld_frag(&sm.k[GATED ? nb : 0][16 * i + lc][32 * kb + 8 * lg]) : fb[i][kb];
+              // off-diagonal blocks as L (stored transposed below); the
+              // diagonal block as the transposed product, so that a lane holds
+              // four consecutive columns of one row (one 16-byte store)
               floatx4 acc[4];
 #pragma unroll
               for (int j = 0; j <= i; ++j) {
                 acc[j] = zero4();
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) acc[j] = mfma_k32(fl[kb], fb[j][kb], acc[j]);
+                for (int kb = 0; kb < 4; ++kb)
+                  acc[j] = j < i ? mfma_k32(fl[kb], fb[j][kb], acc[j]) : mfma_k32(fb[j][kb], fl[kb], acc[j]);
               }
               // L = diag(beta) (.): the diagonal tile's strictly-lower part in
               // fp32 for the D wave; off-diagonal tiles bf16, transposed (the
@@ -559,13 +565,11 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
                 wv.y = pack2(bt.z * acc[j][2], bt.w * acc[j][3]);
                 *reinterpret_cast<uint2*>(&sm.lb[nb][i * (i - 1) / 2 + j][lc][4 * lg]) = wv;
               }
-              float* lbk = &sm.l[i * kLB];
-#pragma unroll
-              for (int ii = 0; ii < 4; ++ii) {
-                const int r = 4 * lg + ii;
-                const float bv = ii == 0 ? bt.x : ii == 1 ? bt.y : ii == 2 ? bt.z : bt.w;
-                if (lc < r) lbk[r * kLR + lc] = bv * acc[i][ii];
-              }
+              // lane (lc, lg): row lc, columns 4lg .. 4lg+3 of the diagonal
+              // block; entries on and above the diagonal are not read
+              const float bl = sm.beta[nb][16 * i + lc];
+              *reinterpret_cast<float4*>(&sm.l[i * kLB + lc * kLR + 4 * lg]) =
+                  make_float4(bl * acc[i][0], bl * acc[i][1], bl * acc[i][2], bl * acc[i][3]);
             }
           },
           std::integral_constant<int, (I0 == 0 && I1 == 1) ? 2 : 0>{},  // wave 7 loads v, beta
