@@ -87,7 +87,7 @@ struct __attribute__((aligned(16))) Smem2 {
   bf16_t lb[2][6][16][16];    // L_bj (b > j), transposed
   bf16_t d[4][16][16];        // D_b, transposed
   bf16_t v[2][kC][kLV];       // v slice
-  bf16_t o[kC][kLO];          // output tile
+  bf16_t o[2][kC][kLO];       // output tile of chunk c in buffer c & 1
   float l[4 * kLB];           // diagonal blocks of L (strictly lower parts)
   float beta[2][kC];
   float gc[NKH][kDK];         // gated: Gam_C per key channel
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sm.o[16 * mt + 4 * lg + i][col] = f2bf(ox[mt][i]);
+            for (int i = 0; i < 4; ++i) sm.o[P][16 * mt + 4 * lg + i][col] = f2bf(ox[mt][i]);
         },
         std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
 #pragma unroll
@@ -581,7 +581,8 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
   } else {
     // ============ output / load waves (4, 5; wave 1 idles when NCW = 1) ============
     // Wave 4 writes the output tile of chunk x-1 (left in LDS by the chain
-    // waves) to memory with 16-byte stores.
+    // waves) to memory with 16-byte stores, in phase 2 of iteration x, while
+    // the chain waves fill the other buffer with chunk x.
     const int sw = tid - 256;  // 0..63 on wave 4
     auto store_o = [&](int chunk) {
 #pragma unroll
@@ -589,17 +590,20 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
         const int vi = sw + 64 * j;
         const int r = vi / VPRV, c8 = (vi % VPRV) * 8;
         *reinterpret_cast<u32x4*>(oh + (size_t)(chunk * kC + r) * dv + c8) =
-            *reinterpret_cast<const u32x4*>(&sm.o[r][c8]);
+            *reinterpret_cast<const u32x4*>(&sm.o[chunk & 1][r][c8]);
       }
     };
-    auto ph1 = [&](const int x, auto parity) {
+    auto ph1 = [&](const int x, auto parity) {};
+    auto ph2 = [&](const int x, auto parity) {
       if (wave == 4 && x >= 1) store_o(x - 1);
     };
-    auto ph2 = [&](const int x, auto parity) {};
     // plain: Q of chunk x+1 and K of chunk x+2 are stored in phase 2 of x
-    // (K(x+1) is read then, for L(x+1)); gated: both in phase 1
+    // (K(x+1) is read then, for L(x+1)); gated: K and K^ in phase 1, and
+    // Q of chunk x+1 in phase 2 where a wave of its own loads it (16-column
+    // slices)
     if (!GATED && wave == 4) run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, GATED ? 0 : 1>{});
     else if (!GATED && wave == 5) run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, GATED ? 0 : 2>{});
+    else if (LP::kThree && wave == 1) run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, LP::kThree ? 1 : 0>{});
     else if (LP::is_tile_wave(wave)) run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
     else run(ph1, ph2, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
     if (wave == 4) store_o(nch - 1);
