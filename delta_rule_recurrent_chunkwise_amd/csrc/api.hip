@@ -15,13 +15,17 @@ bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0
 bool dtype_ok(int dt) { return dt == LA_DTYPE_F32 || dt == LA_DTYPE_BF16; }
 
 // Element counts must stay addressable and the grid within one dimension.
-bool sizes_ok(long long b, long long h, long long t, int dk, int dv) {
+// t = 0 is allowed where the caller says so (a prefill over no tokens).
+bool sizes_ok(long long b, long long h, long long t, int dk, int dv, bool allow_empty = false) {
   const long long mx = (dk > dv ? dk : dv);
-  if (b <= 0 || h <= 0 || t <= 0) return false;
+  if (b <= 0 || h <= 0 || t < (allow_empty ? 0 : 1)) return false;
   if (b * h > INT_MAX) return false;
-  const long long elems = b * h * t * mx;
+  if (t > INT_MAX - 64) return false;  // the chunk count rounds t up to 64
+  const long long tp = ((t + 63) / 64) * 64;
+  const long long elems = b * h * tp * mx;
   const long long state = b * h * (long long)dk * dv;
-  return elems / mx / t == b * h && elems < (1LL << 50) && state < (1LL << 50);
+  if (b * h * (tp / 64) > INT_MAX) return false;  // one workgroup per chunk in some kernels
+  return (tp == 0 || elems / mx / tp == b * h) && elems < (1LL << 50) && state < (1LL << 50);
 }
 
 int launch_rc(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH; }
@@ -35,7 +39,7 @@ const char* la_strerror(int code) {
     case LA_OK: return "success";
     case LA_ERR_NULL: return "a required pointer argument is NULL";
     case LA_ERR_SHAPE:
-      return "invalid shape: B, H, N, T must be positive, T a multiple of 64 for prefill, "
+      return "invalid shape: B, H, N must be positive, T >= 0 for prefill, "
              "and sizes within range";
     case LA_ERR_DTYPE: return "dtype must be LA_DTYPE_F32 (0) or LA_DTYPE_BF16 (1)";
     case LA_ERR_UNSUPPORTED_DIM:
@@ -51,9 +55,9 @@ const char* la_strerror(int code) {
 int la_prefill(const void* q, const void* k, const void* v, void* o, float* S, float* z,
                int use_initial_state, int B, int H, int T, int dk, int dv, int dtype,
                void* stream) {
-  if (!q || !k || !v || !o || !S || !z) return LA_ERR_NULL;
+  if (!S || !z || (T != 0 && (!q || !k || !v || !o))) return LA_ERR_NULL;
   if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
-  if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1) || T % 64 != 0) return LA_ERR_SHAPE;
+  if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1, true)) return LA_ERR_SHAPE;
   if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return LA_ERR_ALIGN;
   linattn::PrefillArgs a{q, k, v, nullptr, nullptr, o, S, z, B, H, T, dv, use_initial_state ? 1 : 0};
@@ -76,9 +80,9 @@ int la_decode_step(const void* q, const void* k, const void* v, void* o, float* 
 int deltanet_prefill(const void* q, const void* k, const void* v, const void* beta,
                      const void* g, void* o, float* S, int use_initial_state, int B, int H,
                      int T, int dk, int dv, int dtype, void* stream) {
-  if (!q || !k || !v || !beta || !o || !S) return LA_ERR_NULL;
+  if (!S || (T != 0 && (!q || !k || !v || !beta || !o))) return LA_ERR_NULL;
   if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
-  if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1) || T % 64 != 0) return LA_ERR_SHAPE;
+  if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1, true)) return LA_ERR_SHAPE;
   if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
   if (g && dtype == LA_DTYPE_F32 && dk > 64) return LA_ERR_UNSUPPORTED_DIM;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return LA_ERR_ALIGN;

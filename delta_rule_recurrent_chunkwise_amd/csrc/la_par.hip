@@ -9,6 +9,11 @@
 // parallel; la_state_scan turns them into S_c (bf16, the precision the
 // output products read it in) and z_c (fp32, in place) and writes the final
 // state; the chunk outputs are then independent.
+//
+// Chunks are numbered over (batch, head, chunk) with nch = ceil(T / 64)
+// chunks per head; inputs have T rows per head.  A partial last chunk is
+// staged with zero rows past the end (phi(k) = 0 there: no contribution to
+// the state or the normaliser), and its missing outputs are not stored.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -42,28 +47,33 @@ __device__ __forceinline__ bf16x8 cat_tr(shortx4_t lo, shortx4_t hi) {
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void la_chunk_state(const bf16_t* __restrict__ k,
                                                       const bf16_t* __restrict__ v,
-                                                      float* __restrict__ dS, float* __restrict__ dz) {
+                                                      float* __restrict__ dS, float* __restrict__ dz, int T,
+                                                      int nch) {
   constexpr int LK = DK + 16, LV = DV + 16;  // row strides (bf16)
   __shared__ __attribute__((aligned(16))) bf16_t sk[kC][LK];
   __shared__ __attribute__((aligned(16))) bf16_t sv[kC][LV];
   const size_t chunk = blockIdx.x;
+  const int bh = (int)(chunk / nch), t0 = (int)(chunk - (size_t)bh * nch) * kC;
+  const int nrow = min(kC, T - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bf16_t* kc = k + chunk * kC * DK;
-  const bf16_t* vc = v + chunk * kC * DV;
+  const bf16_t* kc = k + ((size_t)bh * T + t0) * DK;
+  const bf16_t* vc = v + ((size_t)bh * T + t0) * DV;
   for (int i = tid; i < kC * DK / 8; i += 256) {
     const int r = i / (DK / 8), c8 = (i % (DK / 8)) * 8;
-    u32x4 w = *reinterpret_cast<const u32x4*>(kc + (size_t)r * DK + c8);
+    // rows past the end re-read the last row and are zeroed after phi
+    u32x4 w = *reinterpret_cast<const u32x4*>(kc + (size_t)min(r, nrow - 1) * DK + c8);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float lo = phi_elu1(bf2f((bf16_t)(w[e] & 0xffffu)));
       const float hi = phi_elu1(bf2f((bf16_t)(w[e] >> 16)));
-      w[e] = pack2(lo, hi);
+      w[e] = r < nrow ? pack2(lo, hi) : 0u;
     }
     *reinterpret_cast<u32x4*>(&sk[r][c8]) = w;
   }
   for (int i = tid; i < kC * DV / 8; i += 256) {
     const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
-    *reinterpret_cast<u32x4*>(&sv[r][c8]) = *reinterpret_cast<const u32x4*>(vc + (size_t)r * DV + c8);
+    const u32x4 x = *reinterpret_cast<const u32x4*>(vc + (size_t)min(r, nrow - 1) * DV + c8);
+    *reinterpret_cast<u32x4*>(&sv[r][c8]) = r < nrow ? x : u32x4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
   constexpr int NDT = DK / 16, NJT = DV / 16 + 1;  // the extra column tile gives dz
@@ -151,7 +161,8 @@ __global__ __launch_bounds__(256) void la_state_scan(const float* __restrict__ d
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void la_chunk_out(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                     const bf16_t* __restrict__ v, const bf16_t* __restrict__ Sc,
-                                                    const float* __restrict__ zc, bf16_t* __restrict__ o) {
+                                                    const float* __restrict__ zc, bf16_t* __restrict__ o, int T,
+                                                    int nch) {
   constexpr int LQ = DK + 16, LV = DV + 16, LA = kC + 16;
   __shared__ __attribute__((aligned(16))) bf16_t sq[kC][LQ];
   __shared__ __attribute__((aligned(16))) bf16_t sk[kC][LQ];
@@ -161,24 +172,28 @@ __global__ __launch_bounds__(256) void la_chunk_out(const bf16_t* __restrict__ q
   __shared__ float sz[DK];
   __shared__ float sden[kC];
   const size_t chunk = blockIdx.x;
+  const int bh = (int)(chunk / nch), t0 = (int)(chunk - (size_t)bh * nch) * kC;
+  const int nrow = min(kC, T - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lc = lane & 15, lg = lane >> 4;
-  const bf16_t* qc = q + chunk * kC * DK;
-  const bf16_t* kc = k + chunk * kC * DK;
-  const bf16_t* vc = v + chunk * kC * DV;
+  const bf16_t* qc = q + ((size_t)bh * T + t0) * DK;
+  const bf16_t* kc = k + ((size_t)bh * T + t0) * DK;
+  const bf16_t* vc = v + ((size_t)bh * T + t0) * DV;
   for (int i = tid; i < 2 * kC * DK / 8; i += 256) {
     const bool isq = i < kC * DK / 8;
     const int ii = isq ? i : i - kC * DK / 8;
     const int r = ii / (DK / 8), c8 = (ii % (DK / 8)) * 8;
-    u32x4 w = *reinterpret_cast<const u32x4*>((isq ? qc : kc) + (size_t)r * DK + c8);
+    // rows past the end re-read the last row; phi(q) = phi(k) = 0 there
+    u32x4 w = *reinterpret_cast<const u32x4*>((isq ? qc : kc) + (size_t)min(r, nrow - 1) * DK + c8);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      w[e] = pack2(phi_elu1(bf2f((bf16_t)(w[e] & 0xffffu))), phi_elu1(bf2f((bf16_t)(w[e] >> 16))));
+      w[e] = r < nrow ? pack2(phi_elu1(bf2f((bf16_t)(w[e] & 0xffffu))), phi_elu1(bf2f((bf16_t)(w[e] >> 16)))) : 0u;
     *reinterpret_cast<u32x4*>(isq ? &sq[r][c8] : &sk[r][c8]) = w;
   }
   for (int i = tid; i < kC * DV / 8; i += 256) {
     const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
-    *reinterpret_cast<u32x4*>(&sv[r][c8]) = *reinterpret_cast<const u32x4*>(vc + (size_t)r * DV + c8);
+    const u32x4 x = *reinterpret_cast<const u32x4*>(vc + (size_t)min(r, nrow - 1) * DV + c8);
+    *reinterpret_cast<u32x4*>(&sv[r][c8]) = r < nrow ? x : u32x4{0u, 0u, 0u, 0u};
   }
   const bf16_t* sc = Sc + chunk * DK * DV;
   for (int i = tid; i < DK * DV / 8; i += 256) {
@@ -233,7 +248,7 @@ __global__ __launch_bounds__(256) void la_chunk_out(const bf16_t* __restrict__ q
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
   const int trow = 8 * lg + ((lane >> 2) & 3);
   const int tcol = 4 * (lane & 3);
-  bf16_t* oc = o + chunk * kC * DV;
+  bf16_t* oc = o + ((size_t)bh * T + t0) * DV;
 #pragma unroll
   for (int jt = 0; jt < DV / 16; ++jt) {
     // phi(Q) S_c (a separate accumulator: the 16-deep and 32-deep opcodes
@@ -261,19 +276,19 @@ __global__ __launch_bounds__(256) void la_chunk_out(const bf16_t* __restrict__ q
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * mt + 4 * lg + i;
-      oc[(size_t)r * DV + 16 * jt + lc] = f2bf(acc[i] / sden[r]);
+      if (r < nrow) oc[(size_t)r * DV + 16 * jt + lc] = f2bf(acc[i] / sden[r]);
     }
   }
 }
 
 template <int DK>
 hipError_t launch_state_dk(int dv, const bf16_t* k, const bf16_t* v, float* dS, float* dz, long nchunks,
-                           hipStream_t st) {
+                           int T, int nch, hipStream_t st) {
   switch (dv) {
-    case 16: hipLaunchKernelGGL((la_chunk_state<DK, 16>), dim3((unsigned)nchunks), dim3(256), 0, st, k, v, dS, dz); break;
-    case 32: hipLaunchKernelGGL((la_chunk_state<DK, 32>), dim3((unsigned)nchunks), dim3(256), 0, st, k, v, dS, dz); break;
-    case 64: hipLaunchKernelGGL((la_chunk_state<DK, 64>), dim3((unsigned)nchunks), dim3(256), 0, st, k, v, dS, dz); break;
-    case 128: hipLaunchKernelGGL((la_chunk_state<DK, 128>), dim3((unsigned)nchunks), dim3(256), 0, st, k, v, dS, dz); break;
+    case 16: hipLaunchKernelGGL((la_chunk_state<DK, 16>), dim3((unsigned)nchunks), dim3(256), 0, st, k, v, dS, dz, T, nch); break;
+    case 32: hipLaunchKernelGGL((la_chunk_state<DK, 32>), dim3((unsigned)nchunks), dim3(256), 0, st, k, v, dS, dz, T, nch); break;
+    case 64: hipLaunchKernelGGL((la_chunk_state<DK, 64>), dim3((unsigned)nchunks), dim3(256), 0, st, k, v, dS, dz, T, nch); break;
+    case 128: hipLaunchKernelGGL((la_chunk_state<DK, 128>), dim3((unsigned)nchunks), dim3(256), 0, st, k, v, dS, dz, T, nch); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -281,16 +296,17 @@ hipError_t launch_state_dk(int dv, const bf16_t* k, const bf16_t* v, float* dS, 
 
 
 template <int DK>
-hipError_t launch_out_dk(int dv, const PrefillArgs& a, const bf16_t* Sc, const float* zc, long nchunks, hipStream_t st) {
+hipError_t launch_out_dk(int dv, const PrefillArgs& a, const bf16_t* Sc, const float* zc, long nchunks, int nch,
+                         hipStream_t st) {
   const bf16_t* q = reinterpret_cast<const bf16_t*>(a.q);
   const bf16_t* k = reinterpret_cast<const bf16_t*>(a.k);
   const bf16_t* v = reinterpret_cast<const bf16_t*>(a.v);
   bf16_t* o = reinterpret_cast<bf16_t*>(a.o);
   switch (dv) {
-    case 16: hipLaunchKernelGGL((la_chunk_out<DK, 16>), dim3((unsigned)nchunks), dim3(256), 0, st, q, k, v, Sc, zc, o); break;
-    case 32: hipLaunchKernelGGL((la_chunk_out<DK, 32>), dim3((unsigned)nchunks), dim3(256), 0, st, q, k, v, Sc, zc, o); break;
-    case 64: hipLaunchKernelGGL((la_chunk_out<DK, 64>), dim3((unsigned)nchunks), dim3(256), 0, st, q, k, v, Sc, zc, o); break;
-    case 128: hipLaunchKernelGGL((la_chunk_out<DK, 128>), dim3((unsigned)nchunks), dim3(256), 0, st, q, k, v, Sc, zc, o); break;
+    case 16: hipLaunchKernelGGL((la_chunk_out<DK, 16>), dim3((unsigned)nchunks), dim3(256), 0, st, q, k, v, Sc, zc, o, a.T, nch); break;
+    case 32: hipLaunchKernelGGL((la_chunk_out<DK, 32>), dim3((unsigned)nchunks), dim3(256), 0, st, q, k, v, Sc, zc, o, a.T, nch); break;
+    case 64: hipLaunchKernelGGL((la_chunk_out<DK, 64>), dim3((unsigned)nchunks), dim3(256), 0, st, q, k, v, Sc, zc, o, a.T, nch); break;
+    case 128: hipLaunchKernelGGL((la_chunk_out<DK, 128>), dim3((unsigned)nchunks), dim3(256), 0, st, q, k, v, Sc, zc, o, a.T, nch); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -299,44 +315,46 @@ hipError_t launch_out_dk(int dv, const PrefillArgs& a, const bf16_t* Sc, const f
 }  // namespace
 
 hipError_t launch_la_par_outputs(int dk, const PrefillArgs& a, void* workspace, hipStream_t st) {
-  const long nchunks = (long)a.B * a.H * (a.T / kC);
+  const int nch = (a.T + kC - 1) / kC;
+  const long nchunks = (long)a.B * a.H * nch;
   const float* dS = reinterpret_cast<const float*>(workspace);
   const float* zc = dS + (size_t)nchunks * dk * a.dv;
   const bf16_t* Sc = reinterpret_cast<const bf16_t*>(zc + (size_t)nchunks * dk);
   switch (dk) {
-    case 16: return launch_out_dk<16>(a.dv, a, Sc, zc, nchunks, st);
-    case 32: return launch_out_dk<32>(a.dv, a, Sc, zc, nchunks, st);
-    case 64: return launch_out_dk<64>(a.dv, a, Sc, zc, nchunks, st);
-    case 128: return launch_out_dk<128>(a.dv, a, Sc, zc, nchunks, st);
+    case 16: return launch_out_dk<16>(a.dv, a, Sc, zc, nchunks, nch, st);
+    case 32: return launch_out_dk<32>(a.dv, a, Sc, zc, nchunks, nch, st);
+    case 64: return launch_out_dk<64>(a.dv, a, Sc, zc, nchunks, nch, st);
+    case 128: return launch_out_dk<128>(a.dv, a, Sc, zc, nchunks, nch, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 // [dS: fp32 nchunks x dk x dv][dz, then z_c: fp32 nchunks x dk][S_c: bf16 nchunks x dk x dv]
 size_t la_par_workspace_bytes(int dk, const PrefillArgs& a) {
-  const size_t nchunks = (size_t)a.B * a.H * (a.T / kC);
+  const size_t nchunks = (size_t)a.B * a.H * ((a.T + kC - 1) / kC);
   return nchunks * ((size_t)dk * a.dv + dk) * sizeof(float) + nchunks * dk * a.dv * sizeof(bf16_t);
 }
 
 hipError_t launch_la_par_states(int dk, const PrefillArgs& a, void* workspace, hipStream_t st) {
-  const long nchunks = (long)a.B * a.H * (a.T / kC);
+  const int nch = (a.T + kC - 1) / kC;
+  const long nchunks = (long)a.B * a.H * nch;
   float* dS = reinterpret_cast<float*>(workspace);
   float* dz = dS + (size_t)nchunks * dk * a.dv;
   const bf16_t* k = reinterpret_cast<const bf16_t*>(a.k);
   const bf16_t* v = reinterpret_cast<const bf16_t*>(a.v);
   hipError_t e;
   switch (dk) {
-    case 16: e = launch_state_dk<16>(a.dv, k, v, dS, dz, nchunks, st); break;
-    case 32: e = launch_state_dk<32>(a.dv, k, v, dS, dz, nchunks, st); break;
-    case 64: e = launch_state_dk<64>(a.dv, k, v, dS, dz, nchunks, st); break;
-    case 128: e = launch_state_dk<128>(a.dv, k, v, dS, dz, nchunks, st); break;
+    case 16: e = launch_state_dk<16>(a.dv, k, v, dS, dz, nchunks, a.T, nch, st); break;
+    case 32: e = launch_state_dk<32>(a.dv, k, v, dS, dz, nchunks, a.T, nch, st); break;
+    case 64: e = launch_state_dk<64>(a.dv, k, v, dS, dz, nchunks, a.T, nch, st); break;
+    case 128: e = launch_state_dk<128>(a.dv, k, v, dS, dz, nchunks, a.T, nch, st); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
   const int n = dk * a.dv + dk;
   bf16_t* Sb = reinterpret_cast<bf16_t*>(dz + (size_t)nchunks * dk);
   hipLaunchKernelGGL(la_state_scan, dim3((unsigned)((n + 255) / 256), (unsigned)(a.B * a.H)), dim3(256), 0, st,
-                     dS, dz, Sb, a.S, a.z, a.T / kC, dk * a.dv, dk, a.use_init);
+                     dS, dz, Sb, a.S, a.z, nch, dk * a.dv, dk, a.use_init);
   return hipGetLastError();
 }
 

@@ -137,7 +137,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  const int nchunks = Tn / kC;
+  // A partial last chunk: loads past the last token re-read it, and the
+  // staged rows past the end get k = 0, v = 0, beta = 0 and (gated) g = 0,
+  // so they add nothing to the state, the normaliser or the outputs of the
+  // tokens that exist; their own outputs are not stored.
+  const int nchunks = (Tn + kC - 1) / kC;
+  const int tlast = Tn - 1;
 
   // Non-gated modes: the chunk's q, k and v-slice vectors (and beta) are
   // loaded into registers one chunk ahead, so their latency overlaps the
@@ -164,14 +169,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         const T* src;
         if (i < 2 * NQV) {
           const int ii = i < NQV ? i : i - NQV;
-          src = (i < NQV ? pq : pk) + (size_t)(c * kC + ii / VPRQ) * DK + (ii % VPRQ) * kVec;
+          src = (i < NQV ? pq : pk) + (size_t)min(c * kC + ii / VPRQ, tlast) * DK + (ii % VPRQ) * kVec;
         } else {
           const int ii = i - 2 * NQV;
-          src = pv + (size_t)(c * kC + ii / VPRS) * dv + (ii % VPRS) * kVec;
+          src = pv + (size_t)min(c * kC + ii / VPRS, tlast) * dv + (ii % VPRS) * kVec;
         }
         pre[j] = *reinterpret_cast<const u32x4v*>(src);
       }
-      if (MODE != PF_LA && tid < kC) preb = E::ld(bth + c * kC + tid);
+      if (MODE != PF_LA && tid < kC) preb = E::ld(bth + min(c * kC + tid, tlast));
     }
   };
   prefetch(0);
@@ -191,6 +196,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
           const int r = ii / VPRS, cv = ii % VPRS;
           VecU<E> vv;
           vv.v = __builtin_bit_cast(Vec16, pre[j]);
+          if (t0 + r > tlast) vv.v = Vec16{};
 #pragma unroll
           for (int e = 0; e < kVec; ++e) sVt[(cv * kVec + e) * LKT + r] = vv.e[e];
           continue;
@@ -207,12 +213,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         if (isq) {
           *reinterpret_cast<Vec16*>(sQ + r * LQ + cv * kVec) = xv.v;
         } else {
+          if (t0 + r > tlast) xv.v = Vec16{};  // after the feature map: phi(0) = 1
           *reinterpret_cast<Vec16*>(sK + r * LQ + cv * kVec) = xv.v;
 #pragma unroll
           for (int e = 0; e < kVec; ++e) sKt[(cv * kVec + e) * LKT + r] = xv.e[e];
         }
       }
-      if (MODE != PF_LA && tid < kC) sRow[tid] = preb;
+      if (MODE != PF_LA && tid < kC) sRow[tid] = t0 + tid <= tlast ? preb : 0.f;
       if (c + 1 < nchunks) prefetch(c + 1);
     }
     if (MODE == PF_GATED) {
@@ -226,7 +233,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
       float run = 0.f;
 #pragma unroll
       for (int j = 0; j < TPP; ++j) {
-        run += E::ld(gh + (size_t)(t0 + part * TPP + j) * DK + d);
+        const int t = t0 + part * TPP + j;
+        run += t <= tlast ? E::ld(gh + (size_t)t * DK + d) : 0.f;
         gl[j] = run;
       }
       sPart[part * DK + d] = run;
@@ -244,8 +252,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         const int r = part * TPP + j;
         const float G = off + gl[j];
         const float eg = __expf(G), emg = __expf(-G), dec = __expf(tot - G);
-        const float qv = E::ld(qh + (size_t)(t0 + r) * DK + d);
-        const float kv = E::ld(kh + (size_t)(t0 + r) * DK + d);
+        const bool in = t0 + r <= tlast;
+        const float qv = in ? E::ld(qh + (size_t)(t0 + r) * DK + d) : 0.f;
+        const float kv = in ? E::ld(kh + (size_t)(t0 + r) * DK + d) : 0.f;
         sQ[r * LQ + d] = E::cvt(qv * eg);
         sK[r * LQ + d] = E::cvt(kv * eg);
         sKh[r * LQ + d] = E::cvt(kv * emg);
@@ -257,11 +266,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
       for (int i = tid; i < kC * VPRV; i += kThreads) {
         const int r = i / VPRV, cv = i - (i / VPRV) * VPRV;
         VecU<E> vv;
-        vv.v = *reinterpret_cast<const Vec16*>(vh + (size_t)(t0 + r) * dv + cv * kVec);
+        vv.v = t0 + r <= tlast ? *reinterpret_cast<const Vec16*>(vh + (size_t)(t0 + r) * dv + cv * kVec) : Vec16{};
 #pragma unroll
         for (int e = 0; e < kVec; ++e) sVt[(cv * kVec + e) * LKT + r] = vv.e[e];
       }
-      if (MODE != PF_LA && tid < kC) sRow[tid] = E::ld(bth + t0 + tid);
+      if (MODE != PF_LA && tid < kC) sRow[tid] = t0 + tid <= tlast ? E::ld(bth + t0 + tid) : 0.f;
     }
     __syncthreads();
 
@@ -454,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
           const int r = 16 * mt + 4 * lg + i;
           float val = ox[mt][i];
           if (MODE == PF_LA) val = val / sRow[r];
-          oh[(size_t)(t0 + r) * dv + 16 * cw + lc] = E::cvt(val);
+          if (t0 + r <= tlast) oh[(size_t)(t0 + r) * dv + 16 * cw + lc] = E::cvt(val);
         }
       }
       if (MODE == PF_GATED) {
@@ -482,6 +491,19 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     __syncthreads();
     for (int d = tid; d < DK; d += kThreads) a.z[(size_t)bh * DK + d] = sVec[d];
   }
+}
+
+// T = 0 without an initial state: the final state is zero.  A kernel rather
+// than a memset, so the call can be captured in a graph.
+__global__ __launch_bounds__(256) void zero_fill(float* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0.f;
+}
+
+static hipError_t zero_floats(float* p, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+  hipLaunchKernelGGL(zero_fill, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
+  return hipGetLastError();
 }
 
 template <int DK, class E, int MODE, int DVS>
@@ -515,6 +537,13 @@ static hipError_t launch_prefill_e(int dk, const PrefillArgs& a, hipStream_t st)
 }
 
 hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, hipStream_t st) {
+  if (a.T == 0) {  // no tokens: the state passes through unchanged
+    if (a.use_init) return hipSuccess;
+    const size_t nbh = (size_t)a.B * a.H;
+    hipError_t e = zero_floats(a.S, nbh * dk * a.dv, st);
+    if (e == hipSuccess && mode == PF_LA) e = zero_floats(a.z, nbh * dk, st);
+    return e;
+  }
   if (bf16 && mode == PF_LA) {
     // Linear attention, chunk-parallel: the chunk-start states come from a
     // prefix over per-chunk phi(K)^T V; then every chunk's output is formed

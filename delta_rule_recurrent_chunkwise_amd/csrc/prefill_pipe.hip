@@ -128,12 +128,13 @@ struct PipeArgs {
   const bf16_t* q;     // Q, or Gam Q
   const bf16_t* k;     // K, or Gam K
   const bf16_t* kh;    // gated: K / Gam
-  const float* gc;     // gated: Gam_C, [B*H][T/64][dk]
+  const float* gc;     // gated: Gam_C, [B*H][ceil(T/64)][dk]
   const bf16_t* v;
   const bf16_t* beta;
   bf16_t* o;
   float* S;
   int T, dv, use_init;
+  int Tq;              // rows per head of q, k, k^: T, or T rounded up to 64 (gated)
 };
 
 // Loads.  Each tile-loader wave owns whole tiles (Q, K, and, gated, K^) and
@@ -187,11 +188,18 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
   const int lg = lane >> 4;
   const int Tn = a.T;
   const int dv = a.dv;
-  const int nch = Tn / kC;
+  const int nch = (Tn + kC - 1) / kC;
+  // A last chunk with fewer than 64 tokens: loads of rows past the end
+  // re-read the last row (every lane still issues every load), and those
+  // rows get beta = 0 where they are staged in LDS.  Then their rows of L
+  // and of X = beta (V - K S) vanish, so their u rows are zero and they
+  // change neither S nor the outputs of earlier tokens; their own outputs
+  // are not stored.  (The gate pre-pass gives them zero log-decay.)
+  const int qlast = a.Tq - 1, tlast = Tn - 1;
 
-  const bf16_t* qh = a.q + (size_t)bh * Tn * kDK;
-  const bf16_t* kh = a.k + (size_t)bh * Tn * kDK;
-  const bf16_t* khh = GATED ? a.kh + (size_t)bh * Tn * kDK : nullptr;
+  const bf16_t* qh = a.q + (size_t)bh * a.Tq * kDK;
+  const bf16_t* kh = a.k + (size_t)bh * a.Tq * kDK;
+  const bf16_t* khh = GATED ? a.kh + (size_t)bh * a.Tq * kDK : nullptr;
   const float* gch = GATED ? a.gc + (size_t)bh * nch * kDK : nullptr;
   const bf16_t* vh = a.v + (size_t)bh * Tn * dv + sl * kDVS;
   const bf16_t* bth = a.beta + (size_t)bh * Tn;
@@ -218,19 +226,21 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
         const int t = LP::tile_of(wave, j);
         const bf16_t* base = t == 0 ? pq : (t == 1 ? pk : pkh);
         const int vv = LP::vec_of(wave, lane, j);
-        dst[j] = *reinterpret_cast<const u32x4*>(base + (size_t)(chunk * kC + (vv >> 4)) * kDK + (vv & 15) * 8);
+        const int row = min(chunk * kC + (vv >> 4), qlast);
+        dst[j] = *reinterpret_cast<const u32x4*>(base + (size_t)row * kDK + (vv & 15) * 8);
       }
     } else if constexpr (KIND == 2) {  // wave 7
 #pragma unroll
       for (int j = 0; j < NVL; ++j) {
         const int vv = lane + 64 * j;  // row vv / VPRV, eight columns
-        dst[j] = *reinterpret_cast<const u32x4*>(vh + (size_t)(chunk * kC + vv / VPRV) * dv + (vv % VPRV) * 8);
+        const int row = min(chunk * kC + vv / VPRV, tlast);
+        dst[j] = *reinterpret_cast<const u32x4*>(vh + (size_t)row * dv + (vv % VPRV) * 8);
       }
       if constexpr (GATED) dst[NVL] = *reinterpret_cast<const u32x4*>(gch + (size_t)chunk * kDK + 4 * (lane & 31));
-      bdst = bth[chunk * kC + lane];  // converted when stored
+      bdst = bth[min(chunk * kC + lane, tlast)];  // converted when stored
     }
   };
-  auto store_loads = [&](auto kindc, int buf, int kbi, const auto& src, uint32_t bsrc) {
+  auto store_loads = [&](auto kindc, int chunk, int buf, int kbi, const auto& src, uint32_t bsrc) {
     constexpr int KIND = decltype(kindc)::value;
     if constexpr (KIND == 1) {
 #pragma unroll
@@ -249,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
       if constexpr (GATED) {
         if (lane < 32) *reinterpret_cast<u32x4*>(&sm.gc[GATED ? buf : 0][4 * lane]) = src[NVL];
       }
-      sm.beta[buf][lane] = bf2f((bf16_t)bsrc);
+      sm.beta[buf][lane] = chunk * kC + lane <= tlast ? bf2f((bf16_t)bsrc) : 0.f;
     }
   };
 
@@ -276,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
     if (loader) {
       issue_loads(kindc, 0, pf[0], pfb[0]);
       if constexpr (LEAD == 2) {
-        store_loads(kindc, 0, 0, pf[0], pfb[0]);
+        store_loads(kindc, 0, 0, 0, pf[0], pfb[0]);
         issue_loads(kindc, nch > 1 ? 1 : 0, pf[1], pfb[1]);
         issue_loads(kindc, nch > 2 ? 2 : nch - 1, pf[0], pfb[0]);
       } else if (NSL == 2) {
@@ -293,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
       constexpr int SL = NSL == 2 ? PC : 0;          // its register slot
       auto move = [&] {
         const int c = x + LEAD;
-        if (c < nch) store_loads(kindc, PC, kidx(c), pf[SL], pfb[SL]);
+        if (c < nch) store_loads(kindc, c, PC, kidx(c), pf[SL], pfb[SL]);
         issue_loads(kindc, c + NSL < nch ? c + NSL : nch - 1, pf[SL], pfb[SL]);
       };
       phase1(x, parity);
@@ -583,19 +593,22 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
     // Wave 4 writes the output tile of chunk x-1 (left in LDS by the chain
     // waves) to memory with 16-byte stores, in phase 2 of iteration x, while
     // the chain waves fill the other buffer with chunk x.
+    // Only the last chunk can be partial: it is stored after the loop, the
+    // one place where rows past the end are skipped.
     const int sw = tid - 256;  // 0..63 on wave 4
-    auto store_o = [&](int chunk) {
+    auto store_o = [&](int chunk, auto tailc) {
 #pragma unroll
       for (int j = 0; j < kC * VPRV / 64; ++j) {
         const int vi = sw + 64 * j;
         const int r = vi / VPRV, c8 = (vi % VPRV) * 8;
+        if (decltype(tailc)::value && chunk * kC + r > tlast) continue;
         *reinterpret_cast<u32x4*>(oh + (size_t)(chunk * kC + r) * dv + c8) =
             *reinterpret_cast<const u32x4*>(&sm.o[chunk & 1][r][c8]);
       }
     };
     auto ph1 = [&](const int x, auto parity) {};
     auto ph2 = [&](const int x, auto parity) {
-      if (wave == 4 && x >= 1) store_o(x - 1);
+      if (wave == 4 && x >= 1) store_o(x - 1, std::false_type{});
     };
     // plain: Q of chunk x+1 and K of chunk x+2 are stored in phase 2 of x
     // (K(x+1) is read then, for L(x+1)); gated: K and K^ in phase 1, and
@@ -606,7 +619,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
     else if (LP::kThree && wave == 1) run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, LP::kThree ? 1 : 0>{});
     else if (LP::is_tile_wave(wave)) run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
     else run(ph1, ph2, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-    if (wave == 4) store_o(nch - 1);
+    if (wave == 4) store_o(nch - 1, std::true_type{});
   }
 }
 
@@ -615,24 +628,31 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
 // Gam Q, Gam K, K / Gam in bf16 and Gam_C = e^{G_63}.  One workgroup of 256
 // threads per chunk: thread (w, l) holds channels 2l, 2l+1 of tokens
 // 16w .. 16w+15; the four waves' partial sums are combined through LDS.
+// Inputs have T rows per head; the outputs have nch * 64, and rows past T
+// (a partial last chunk) get g = 0 and q = k = 0, so Gam_C is the decay
+// over the tokens that exist.
 __global__ __launch_bounds__(256) void gate_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                  const bf16_t* __restrict__ g, bf16_t* __restrict__ qt,
                                                  bf16_t* __restrict__ kt, bf16_t* __restrict__ kht,
-                                                 float* __restrict__ gcum, int nch) {
+                                                 float* __restrict__ gcum, int T, int nch) {
   __shared__ float2 part[4][64];
   const int chunk = blockIdx.x;  // over B*H*nch
+  const int bh = chunk / nch, t0 = (chunk - bh * nch) * kC;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const size_t base = (size_t)chunk * kC * kDK;
-  const uint32_t* g2 = reinterpret_cast<const uint32_t*>(g + base);
+  const size_t base = (size_t)chunk * kC * kDK;                 // outputs
+  const size_t ibase = ((size_t)bh * T + t0) * kDK;             // inputs
+  const int nrow = min(kC, T - t0);                             // rows that exist
+  const uint32_t* g2 = reinterpret_cast<const uint32_t*>(g + ibase);
   uint32_t gw[16];
 #pragma unroll
-  for (int t = 0; t < 16; ++t) gw[t] = g2[(16 * w + t) * (kDK / 2) + l];
+  for (int t = 0; t < 16; ++t) gw[t] = g2[min(16 * w + t, nrow - 1) * (kDK / 2) + l];  // masked below
   float2 run = make_float2(0.f, 0.f);
   float2 gl[16];
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
-    run.x += bf2f((bf16_t)(gw[t] & 0xffffu));
-    run.y += bf2f((bf16_t)(gw[t] >> 16));
+    const uint32_t gv = 16 * w + t < nrow ? gw[t] : 0u;
+    run.x += bf2f((bf16_t)(gv & 0xffffu));
+    run.y += bf2f((bf16_t)(gv >> 16));
     gl[t] = run;
   }
   part[w][l] = run;
@@ -646,15 +666,18 @@ __global__ __launch_bounds__(256) void gate_prep(const bf16_t* __restrict__ q, c
     tot.y += x.y;
   }
   if (w == 0) reinterpret_cast<float2*>(gcum + (size_t)chunk * kDK)[l] = make_float2(__expf(tot.x), __expf(tot.y));
-  const uint32_t* q2 = reinterpret_cast<const uint32_t*>(q + base);
-  const uint32_t* k2 = reinterpret_cast<const uint32_t*>(k + base);
+  const uint32_t* q2 = reinterpret_cast<const uint32_t*>(q + ibase);
+  const uint32_t* k2 = reinterpret_cast<const uint32_t*>(k + ibase);
   uint32_t* qt2 = reinterpret_cast<uint32_t*>(qt + base);
   uint32_t* kt2 = reinterpret_cast<uint32_t*>(kt + base);
   uint32_t* kh2 = reinterpret_cast<uint32_t*>(kht + base);
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
     const int idx = (16 * w + t) * (kDK / 2) + l;
-    const uint32_t qw = q2[idx], kw = k2[idx];
+    const int iidx = min(16 * w + t, nrow - 1) * (kDK / 2) + l;
+    const bool in = 16 * w + t < nrow;
+    const uint32_t qr = q2[iidx], kr = k2[iidx];  // in bounds for every lane
+    const uint32_t qw = in ? qr : 0u, kw = in ? kr : 0u;
     const float G0 = off.x + gl[t].x, G1 = off.y + gl[t].y;
     const float e0 = __expf(G0), e1 = __expf(G1), r0 = __expf(-G0), r1 = __expf(-G1);
     const float q0 = bf2f((bf16_t)(qw & 0xffffu)), q1 = bf2f((bf16_t)(qw >> 16));
@@ -668,8 +691,9 @@ __global__ __launch_bounds__(256) void gate_prep(const bf16_t* __restrict__ q, c
 }  // namespace
 
 size_t gated_pipe_workspace_bytes(const PrefillArgs& a) {
-  const size_t n = (size_t)a.B * a.H * a.T * kDK;
-  return 3 * n * sizeof(bf16_t) + (size_t)a.B * a.H * (a.T / kC) * kDK * sizeof(float);
+  const size_t nch = (size_t)(a.T + kC - 1) / kC;
+  const size_t n = (size_t)a.B * a.H * nch * kC * kDK;
+  return 3 * n * sizeof(bf16_t) + (size_t)a.B * a.H * nch * kDK * sizeof(float);
 }
 
 namespace {
@@ -702,6 +726,7 @@ hipError_t launch_prefill_pipe(const PrefillArgs& a, void* workspace, hipStream_
   p.T = a.T;
   p.dv = a.dv;
   p.use_init = a.use_init;
+  p.Tq = a.T;
   if (a.g == nullptr) {
     p.q = reinterpret_cast<const bf16_t*>(a.q);
     p.k = reinterpret_cast<const bf16_t*>(a.k);
@@ -709,21 +734,22 @@ hipError_t launch_prefill_pipe(const PrefillArgs& a, void* workspace, hipStream_
     p.gc = nullptr;
     return launch_pipe_t<false>(p, bh, a.dv, st);
   }
-  const size_t n = (size_t)a.B * a.H * a.T * kDK;
+  const int nch = (a.T + kC - 1) / kC;
+  const size_t n = (size_t)a.B * a.H * nch * kC * kDK;
   bf16_t* qt = reinterpret_cast<bf16_t*>(workspace);
   bf16_t* kt = qt + n;
   bf16_t* kht = kt + n;
   float* gcum = reinterpret_cast<float*>(kht + n);
-  const int nch = a.T / kC;
   hipLaunchKernelGGL(gate_prep, dim3((unsigned)(a.B * a.H * nch)), dim3(256), 0, st,
                      reinterpret_cast<const bf16_t*>(a.q), reinterpret_cast<const bf16_t*>(a.k),
-                     reinterpret_cast<const bf16_t*>(a.g), qt, kt, kht, gcum, nch);
+                     reinterpret_cast<const bf16_t*>(a.g), qt, kt, kht, gcum, a.T, nch);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   p.q = qt;
   p.k = kt;
   p.kh = kht;
   p.gc = gcum;
+  p.Tq = nch * kC;
   return launch_pipe_t<true>(p, bh, a.dv, st);
 }
 

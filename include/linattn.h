@@ -37,14 +37,18 @@
  *           workspace (hipMallocAsync on `stream`, released with
  *           hipFreeAsync after its kernels):
  *             - the gated deltanet_prefill with bf16 inputs, dk = 128 and
- *               dv % 32 == 0: 6 B*H*T*dk + 4 B*H*(T/64)*dk bytes for the
- *               decay-scaled q and k;
- *             - la_prefill with bf16 inputs: 6 B*H*(T/64)*dk*dv +
- *               4 B*H*(T/64)*dk bytes for the per-chunk state increments
- *               (fp32), the state entering each chunk (bf16) and the
- *               normaliser entering each chunk (fp32).
+ *               dv % 32 == 0: 384 B*H*C*dk + 4 B*H*C*dk bytes for the
+ *               decay-scaled q and k, where C = ceil(T/64) is the number
+ *               of 64-token chunks;
+ *             - la_prefill with bf16 inputs: 6 B*H*C*dk*dv + 4 B*H*C*dk
+ *               bytes for the per-chunk state increments (fp32), the state
+ *               entering each chunk (bf16) and the normaliser entering each
+ *               chunk (fp32).
  *           A failed allocation returns LA_ERR_LAUNCH.
- * Sizes.    B, H (or N, H) >= 1; T >= 1 and T a multiple of 64 for prefill;
+ * Sizes.    B, H (or N, H) >= 1; T >= 0 for prefill, any length (the last
+ *           64-token chunk may be partial).  T = 0 enqueues no work when
+ *           use_initial_state is set and otherwise zero-fills S (and z);
+ *           the token arrays may then be NULL.
  *           dk and dv each one of 16, 32, 64, 128.  The per-channel gated
  *           prefill with LA_DTYPE_F32 supports dk <= 64.
  * Stream.   stream is a hipStream_t passed as void*; NULL is the null stream.
@@ -63,7 +67,7 @@ extern "C" {
 
 #define LA_OK 0
 #define LA_ERR_NULL (-1)            /* a required pointer is NULL            */
-#define LA_ERR_SHAPE (-2)           /* B/H/N/T not positive, or T % 64 != 0  */
+#define LA_ERR_SHAPE (-2)           /* B/H/N not positive, T < 0, too large  */
 #define LA_ERR_DTYPE (-3)           /* dtype not LA_DTYPE_F32/LA_DTYPE_BF16  */
 #define LA_ERR_UNSUPPORTED_DIM (-4) /* dk or dv not in {16, 32, 64, 128}     */
 #define LA_ERR_LAUNCH (-5)          /* the HIP runtime rejected a launch     */

@@ -94,11 +94,22 @@ def test_bad_dtype(dt):
     assert _dn_decode(dt=dt) == DTYPE
 
 
-@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(T=0), dict(B=-3), dict(T=63),
-                                dict(T=100), dict(T=-64)])
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(B=-3), dict(T=-1), dict(T=-64),
+                                dict(T=2**31 - 1), dict(B=1 << 16, H=1 << 10, T=1 << 14)])
 def test_bad_prefill_shape(kw):
     assert _la_prefill(**kw) == SHAPE
     assert _dn_prefill(**kw) == SHAPE
+
+
+def test_empty_prefill_with_initial_state_is_a_no_op():
+    """T = 0 with the initial state kept enqueues nothing (no HIP call, so it
+    runs here) and accepts NULL token arrays; S and z are required."""
+    none = dict(q=None, k=None, v=None, o=None)
+    assert _la_prefill(T=0, init=1, **none) == OK
+    assert _dn_prefill(T=0, init=1, beta=None, **none) == OK
+    assert _la_prefill(T=0, init=1, S=None) == NULL
+    assert _la_prefill(T=0, init=1, z=None) == NULL
+    assert _dn_prefill(T=0, init=1, S=None) == NULL
 
 
 @pytest.mark.parametrize("kw", [dict(N=0), dict(H=0), dict(N=-1), dict(N=1 << 20, H=1 << 12)])

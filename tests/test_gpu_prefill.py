@@ -107,6 +107,104 @@ def test_short_and_long_sequences(gated):
         assert_close(S, S_ref, 2e-2, f"S T={T}")
 
 
+RAGGED_T = (1, 63, 65, 100, 130)
+
+
+@pytest.mark.parametrize("mode", ["la", "delta", "gated"])
+@pytest.mark.parametrize("dtype,dk,dv", [(torch.bfloat16, 128, 128), (torch.bfloat16, 64, 32),
+                                         (torch.float32, 64, 64)],
+                         ids=["bf16-128x128", "bf16-64x32", "f32-64x64"])
+def test_ragged_lengths(mode, dtype, dk, dv):
+    """T not a multiple of 64 (a partial last chunk, or one chunk of one
+    token) in every prefill kernel: bf16 d = 128 takes the pipelined delta
+    kernels and the chunk-parallel linear attention, the others the generic
+    kernel.  Odd T starts from an initial state."""
+    dev = require_gpu()
+    for T in RAGGED_T:
+        init = T % 2 == 1
+        seed = 1000 + T + 7 * dk + dv
+        print(f"  mode={mode} T={T} init={init}", flush=True)
+        if mode == "la":
+            inp = workloads.make_la(2, 3, T, dk, dv, dtype, seed=seed, init_state=init)
+            d = _dev(inp, dev)
+            o, S, z = la.la_prefill(d["q"], d["k"], d["v"], S=d["S0"].clone() if init else None,
+                                    z=d["z0"].clone() if init else None, use_initial_state=init)
+            torch.cuda.synchronize()
+            o_ref, S_ref, z_ref = oracle.la_recurrent(inp["q"], inp["k"], inp["v"],
+                                                      inp["S0"] if init else None,
+                                                      inp["z0"] if init else None)
+            assert_close(z, z_ref, TOL[dtype], f"z T={T}")
+        else:
+            inp = workloads.make_delta(2, 3, T, dk, dv, dtype, seed=seed, gated=mode == "gated",
+                                       init_state=init, state_std=0.5)
+            o, S = _run_delta(inp, dev, mode == "gated", init)
+            o_ref, S_ref = oracle.delta_recurrent(inp["q"], inp["k"], inp["v"], inp["beta"],
+                                                  inp.get("g"), S0=inp["S0"] if init else None)
+        assert tuple(o.shape) == (2, 3, T, dv)
+        assert_close(o, o_ref, TOL[dtype], f"o T={T}")
+        assert_close(S, S_ref, TOL[dtype], f"S T={T}")
+
+
+@pytest.mark.parametrize("gated", [False, True], ids=["delta", "gated"])
+def test_ragged_many_heads_bf16_dk128(gated):
+    """A partial last chunk with 32-column value slices (many (batch, head)
+    pairs), where the output tile of the last chunk is written by the store
+    after the loop."""
+    dev = require_gpu()
+    inp = workloads.make_delta(8, 32, 100, 128, 128, torch.bfloat16, seed=77, gated=gated,
+                               init_state=True, state_std=0.5)
+    o, S = _run_delta(inp, dev, gated, True)
+    o_ref, S_ref = oracle.delta_recurrent(inp["q"], inp["k"], inp["v"], inp["beta"],
+                                          inp.get("g"), S0=inp["S0"])
+    assert_close(o, o_ref, TOL[torch.bfloat16], "o")
+    assert_close(S, S_ref, TOL[torch.bfloat16], "S")
+
+
+def test_partial_chunk_leaves_memory_past_the_end_alone():
+    """The output rows of a partial chunk that do not exist are never
+    written: o is a view into a larger buffer whose next row holds a
+    sentinel."""
+    dev = require_gpu()
+    T, dv = 100, 128
+    inp = workloads.make_delta(1, 1, T, 128, dv, torch.bfloat16, seed=5)
+    d = _dev(inp, dev)
+    buf = torch.full((T + 28, dv), 7.0, device=dev, dtype=torch.bfloat16)
+    o = buf[:T].view(1, 1, T, dv)
+    la.deltanet_prefill(d["q"], d["k"], d["v"], d["beta"], o=o)
+    torch.cuda.synchronize()
+    assert torch.all(buf[T:] == 7.0)
+    o_ref, _ = oracle.delta_recurrent(inp["q"], inp["k"], inp["v"], inp["beta"])
+    assert_close(o, o_ref, TOL[torch.bfloat16], "o")
+
+
+@pytest.mark.parametrize("mode", ["la", "delta", "gated"])
+@pytest.mark.parametrize("dtype", DTYPES, ids=IDS)
+def test_empty_sequence(mode, dtype):
+    """T = 0: the final state is the initial state when one is given, and
+    zero otherwise (the sum over no tokens); the output is empty."""
+    dev = require_gpu()
+    B, H, dk, dv = 2, 3, 64, 32
+    gen = torch.Generator().manual_seed(9)
+    S0 = torch.randn(B, H, dk, dv, generator=gen).to(dev)
+    z0 = torch.rand(B, H, dk, generator=gen).to(dev) + 1.0
+    e = torch.empty(B, H, 0, dk, device=dev, dtype=dtype)
+    ev = torch.empty(B, H, 0, dv, device=dev, dtype=dtype)
+    eb = torch.empty(B, H, 0, device=dev, dtype=dtype)
+    for init in (True, False):
+        S = S0.clone()
+        if mode == "la":
+            z = z0.clone()
+            o, S, z = la.la_prefill(e, e, ev, S=S, z=z, use_initial_state=init)
+            torch.cuda.synchronize()
+            assert torch.equal(z, z0 if init else torch.zeros_like(z0))
+        else:
+            o, S = la.deltanet_prefill(e, e, ev, eb, g=e if mode == "gated" else None, S=S,
+                                       use_initial_state=init)
+            torch.cuda.synchronize()
+        assert tuple(o.shape) == (B, H, 0, dv)
+        assert torch.equal(S, S0 if init else torch.zeros_like(S0))
+
+
 def test_beta_zero_keeps_state_and_reads_it():
     dev = require_gpu()
     inp = workloads.make_delta(1, 2, 128, 64, 64, torch.float32, seed=3, init_state=True,
