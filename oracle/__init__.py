@@ -12,8 +12,11 @@ Functions (both follow the article "From GPT-2 to Kimi K3, explained"):
                      state S and normaliser z, o_t = phi(q_t) S_t / phi(q_t).z_t.
 ``delta_recurrent``  section "DeltaNet (Parallelizing Linear Transformers with
                      Delta Rule)", sequential prefill loop; with ``g`` given,
-                     the per-key-channel decay of sections "Gated Delta Net" and
-                     "KDA / Kimi Linear" applied to S before each read.
+                     the decay of sections "Gated Delta Net" (one scalar per
+                     token, g [B,H,T]) and "KDA / Kimi Linear" (per key
+                     channel, g [B,H,T,dk]) applied to S before each read.
+``gla_recurrent``    section "Gated Delta Net", the additive cache with a
+                     forgetting factor: S <- a_t S + k_t^T v_t, o_t = q_t S.
 
 Inputs may be torch CPU tensors (float32, bfloat16, float64) or numpy arrays
 (float32, float64); all inputs of one call share a dtype.  They are read in
@@ -50,8 +53,10 @@ def _bind(lib):
     i = ctypes.c_int
     lib.orc_la_recurrent.argtypes = [i, i, i, i, i, d, d, d, i, d, d, d, d, d, i]
     lib.orc_la_recurrent.restype = i
-    lib.orc_delta_recurrent.argtypes = [i, i, i, i, i, d, d, d, d, d, i, d, d, d, i]
+    lib.orc_delta_recurrent.argtypes = [i, i, i, i, i, d, d, d, d, d, i, i, d, d, d, i]
     lib.orc_delta_recurrent.restype = i
+    lib.orc_gla_recurrent.argtypes = [i, i, i, i, i, d, d, d, d, i, d, d, d, i]
+    lib.orc_gla_recurrent.restype = i
     lib.orc_max_threads.argtypes = []
     lib.orc_max_threads.restype = i
     return lib
@@ -139,10 +144,10 @@ def la_recurrent(q, k, v, S0=None, z0=None, nthreads: int = 0, lib=None):
 
 def delta_recurrent(q, k, v, beta, g=None, S0=None, nthreads: int = 0, lib=None,
                     want_o: bool = True):
-    """Delta rule (g None) or per-key-channel gated delta rule, token by token.
-    q, k [B,H,T,dk]; v [B,H,T,dv]; beta [B,H,T]; g [B,H,T,dk] log-decay or
-    None; S0 [B,H,dk,dv] or None.  Returns (o [B,H,T,dv] or None,
-    S [B,H,dk,dv])."""
+    """Delta rule (g None) or gated delta rule, token by token.
+    q, k [B,H,T,dk]; v [B,H,T,dv]; beta [B,H,T]; g log-decay, [B,H,T,dk] per
+    key channel or [B,H,T] per token, or None; S0 [B,H,dk,dv] or None.
+    Returns (o [B,H,T,dv] or None, S [B,H,dk,dv])."""
     lib = lib or load()
     B, H, T, dk = q.shape
     dv = v.shape[-1]
@@ -152,13 +157,45 @@ def delta_recurrent(q, k, v, beta, g=None, S0=None, nthreads: int = 0, lib=None,
     if len(dts) != 1:
         raise ValueError("q, k, v, beta (and g) must share a dtype")
     gp = bufs[4][1] if g is not None else None
+    per_channel = 1
+    if g is not None:
+        if tuple(g.shape) == (B, H, T):
+            per_channel = 0
+        elif tuple(g.shape) != (B, H, T, dk):
+            raise ValueError(f"g must be [B,H,T] or [B,H,T,dk], got {tuple(g.shape)}")
     s0, s0p = _state64(S0, (B, H, dk, dv))
     o = np.empty((B, H, T, dv), np.float64) if want_o else None
     S = np.empty((B, H, dk, dv), np.float64)
     rc = lib.orc_delta_recurrent(B, H, T, dk, dv, bufs[0][1], bufs[1][1], bufs[2][1],
-                                 bufs[3][1], gp, dts.pop(), s0p,
+                                 bufs[3][1], gp, per_channel, dts.pop(), s0p,
                                  o.ctypes.data if want_o else None, S.ctypes.data,
                                  int(nthreads))
+    if rc != 0:
+        raise MemoryError("oracle allocation failed")
+    return o, S
+
+
+def gla_recurrent(q, k, v, g=None, S0=None, nthreads: int = 0, lib=None):
+    """Gated linear attention without a normaliser, token by token:
+    S <- exp(g_t) S + k_t^T v_t, o_t = q_t S.  q, k [B,H,T,dk]; v [B,H,T,dv];
+    g [B,H,T] log-decay or None; S0 [B,H,dk,dv] or None.
+    Returns (o [B,H,T,dv], S [B,H,dk,dv])."""
+    lib = lib or load()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    tensors = [q, k, v] + ([g] if g is not None else [])
+    bufs = [_as_buffer(t) for t in tensors]
+    dts = {b[2] for b in bufs}
+    if len(dts) != 1:
+        raise ValueError("q, k, v (and g) must share a dtype")
+    if g is not None and tuple(g.shape) != (B, H, T):
+        raise ValueError(f"g must be [B,H,T], got {tuple(g.shape)}")
+    gp = bufs[3][1] if g is not None else None
+    s0, s0p = _state64(S0, (B, H, dk, dv))
+    o = np.empty((B, H, T, dv), np.float64)
+    S = np.empty((B, H, dk, dv), np.float64)
+    rc = lib.orc_gla_recurrent(B, H, T, dk, dv, bufs[0][1], bufs[1][1], bufs[2][1], gp,
+                               dts.pop(), s0p, o.ctypes.data, S.ctypes.data, int(nthreads))
     if rc != 0:
         raise MemoryError("oracle allocation failed")
     return o, S

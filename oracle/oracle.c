@@ -1,7 +1,8 @@
 /*
  * oracle.c -- plain CPU float64 reference for causal linear attention with a
  * fixed d_k x d_v state: ELU+1 linear attention with a running normaliser,
- * the DeltaNet delta rule, and the per-key-channel gated delta rule.
+ * the DeltaNet delta rule with its scalar and per-key-channel gated forms,
+ * and decayed (gated) linear attention without a normaliser.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
  * call this file: only the test suite, the smoke check and the benchmark's
@@ -21,15 +22,20 @@
  *     the sequential prefill loop (read v_old = k S, u = beta (v - v_old),
  *     write S += k^T u, then read the output with q from the updated S).
  *   - section "Gated Delta Net" and "KDA / Kimi Linear": the state decays by a
- *     data-dependent factor before the delta step; for KDA the factor is a
- *     separate value per key channel.  Reading used here: the decay a_t
- *     multiplies row i (key channel i) of S before the read at step t, i.e.
+ *     data-dependent factor before the delta step; for Gated DeltaNet the
+ *     factor is one scalar per token, for KDA a separate value per key
+ *     channel.  Reading used here: the decay a_t multiplies row i (key
+ *     channel i) of S before the read at step t, i.e.
  *     S_t = diag(a_t) S_{t-1} + beta_t k_t (v_t - (diag(a_t) S_{t-1})^T k_t)^T.
+ *   - section "Gated Delta Net", its first step (the additive cache with a
+ *     forgetting factor, credited to Mamba-2): cache = alpha * S_old + k^T v,
+ *     read with q, with q and k used as given (no feature map, no normaliser).
  *
  * Conventions: row-vector form of the article's code, S is d_k x d_v stored
  * row-major, a read is k S (= S^T k), a write adds k^T u.  Tensors are
- * row-major: q, k [B,H,T,d_k]; v [B,H,T,d_v]; beta [B,H,T]; g [B,H,T,d_k]
- * holds the log-decay g = log a; S [B,H,d_k,d_v]; z [B,H,d_k].
+ * row-major: q, k [B,H,T,d_k]; v [B,H,T,d_v]; beta [B,H,T]; g holds the
+ * log-decay g = log a, [B,H,T,d_k] per key channel or [B,H,T] per token;
+ * S [B,H,d_k,d_v]; z [B,H,d_k].
  *
  * Inputs are read in their stored precision (fp32, bf16 bit patterns, or
  * fp64) and widened to float64 element by element; all arithmetic is float64.
@@ -158,8 +164,10 @@ int orc_la_recurrent(int B, int H, int T, int dk, int dv,
 }
 
 /*
- * Delta rule, optionally with a per-key-channel decay, one token at a time:
- *   (gated only)  S <- diag(exp(g_t)) S        row i scaled by exp(g_t[i])
+ * Delta rule, optionally with a decay, one token at a time:
+ *   (gated only)  S <- diag(exp(g_t)) S        row i scaled by exp(g_t[i]);
+ *                                              g_per_channel = 0: every row
+ *                                              by the one exp(g_t)
  *   r   = k_t S                                 (what the key reads now)
  *   u   = beta_t (v_t - r)                      (only what is new)
  *   S  <- S + k_t^T u                           (outer-product write)
@@ -170,8 +178,8 @@ int orc_la_recurrent(int B, int H, int T, int dk, int dv,
  */
 int orc_delta_recurrent(int B, int H, int T, int dk, int dv,
                         const void *q, const void *k, const void *v,
-                        const void *beta, const void *g, int dt,
-                        const double *S0, double *o, double *S_out,
+                        const void *beta, const void *g, int g_per_channel,
+                        int dt, const double *S0, double *o, double *S_out,
                         int nthreads)
 {
     int fail = 0;
@@ -199,7 +207,8 @@ int orc_delta_recurrent(int B, int H, int T, int dk, int dv,
             const double b = rd(beta, (size_t)bh * T + t, dt);
             if (g) {
                 for (int i = 0; i < dk; i++) {
-                    const double a = exp(rd(g, qk_row + i, dt));
+                    const double a = g_per_channel ? exp(rd(g, qk_row + i, dt))
+                                                   : exp(rd(g, (size_t)bh * T + t, dt));
                     for (int j = 0; j < dv; j++)
                         S[(size_t)i * dv + j] *= a;
                 }
@@ -231,6 +240,69 @@ int orc_delta_recurrent(int B, int H, int T, int dk, int dv,
         if (S_out)
             memcpy(S_out + sbase, S, sizeof(double) * (size_t)dk * dv);
         free(S); free(kt); free(qt); free(r); free(u);
+    }
+    return fail ? -1 : 0;
+}
+
+/*
+ * Gated linear attention (the additive cache with a forgetting factor), one
+ * token at a time:
+ *   (gated only)  S <- exp(g_t) S              one scalar per token
+ *   S   <- S + k_t^T v_t                        (outer-product write)
+ *   o_t = q_t S                                 (read after the write)
+ * q and k are used as given.  g [B,H,T] may be NULL (no decay).  S0 may be
+ * NULL (zero state) and may alias S_out; o and S_out may be NULL.
+ */
+int orc_gla_recurrent(int B, int H, int T, int dk, int dv,
+                      const void *q, const void *k, const void *v,
+                      const void *g, int dt, const double *S0, double *o,
+                      double *S_out, int nthreads)
+{
+    int fail = 0;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < B * H; bh++) {
+        double *S = malloc(sizeof(double) * (size_t)dk * dv);
+        double *kt = malloc(sizeof(double) * (size_t)dk);
+        double *vt = malloc(sizeof(double) * (size_t)dv);
+        if (!S || !kt || !vt) {
+#pragma omp atomic write
+            fail = 1;
+            free(S); free(kt); free(vt);
+            continue;
+        }
+        const size_t sbase = (size_t)bh * dk * dv;
+        for (size_t i = 0; i < (size_t)dk * dv; i++)
+            S[i] = S0 ? S0[sbase + i] : 0.0;
+
+        for (int t = 0; t < T; t++) {
+            const size_t qk_row = ((size_t)bh * T + t) * dk;
+            const size_t v_row = ((size_t)bh * T + t) * dv;
+            if (g) {
+                const double a = exp(rd(g, (size_t)bh * T + t, dt));
+                for (size_t i = 0; i < (size_t)dk * dv; i++)
+                    S[i] *= a;
+            }
+            for (int i = 0; i < dk; i++)
+                kt[i] = rd(k, qk_row + i, dt);
+            for (int j = 0; j < dv; j++)
+                vt[j] = rd(v, v_row + j, dt);
+            for (int i = 0; i < dk; i++)
+                for (int j = 0; j < dv; j++)
+                    S[(size_t)i * dv + j] += kt[i] * vt[j];
+            if (o) {
+                for (int j = 0; j < dv; j++)
+                    o[v_row + j] = 0.0;
+                for (int i = 0; i < dk; i++) {
+                    const double qi = rd(q, qk_row + i, dt);
+                    for (int j = 0; j < dv; j++)
+                        o[v_row + j] += qi * S[(size_t)i * dv + j];
+                }
+            }
+        }
+        if (S_out)
+            memcpy(S_out + sbase, S, sizeof(double) * (size_t)dk * dv);
+        free(S); free(kt); free(vt);
     }
     return fail ? -1 : 0;
 }

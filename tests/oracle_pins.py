@@ -25,7 +25,11 @@ Independent evaluations used:
   again replaces the old association);
 * gate limits (section "Gated Delta Net": decay 1 is the plain delta rule,
   decay 0 clears the memory), the scalar-gated Householder form, closed forms
-  of pure decay, and the per-channel gated UT form.
+  of pure decay, and the per-channel gated UT form;
+* for the additive cache with a forgetting factor (section "Gated Delta Net",
+  first step): its unrolled sum, i.e. the decayed masked quadratic form
+  (tril(Q K^T) * e^{G_t - G_j}) V, and the limits a = 1 (plain additive
+  linear attention, closed-form state) and a = 0 (only the newest write).
 """
 from __future__ import annotations
 
@@ -321,22 +325,28 @@ def pin_gated_limits(lib):
 
 
 def pin_gated_scalar_householder(lib):
-    """A decay equal across channels is the scalar-gated delta rule:
+    """The scalar-gated delta rule (one decay per token, given either as
+    g [B,H,T] or equal across the channels of g [B,H,T,dk]) is
     M_t = a_t M_{t-1} (I - b k k^T) + b v k^T (transposed convention)."""
     rng = _rng(11)
     B, H, T, dk, dv = 1, 1, 30, 5, 6
     q, k, v, beta, _ = _delta_inputs(rng, B, H, T, dk, dv)
     alpha = np.exp(-np.abs(rng.standard_normal(T)) * 0.3)
-    g = np.broadcast_to(np.log(alpha)[None, None, :, None], (B, H, T, dk)).copy()
+    g_tok = np.log(alpha)[None, None, :].copy()
+    g_chan = np.broadcast_to(g_tok[..., None], (B, H, T, dk)).copy()
     S0 = rng.standard_normal((B, H, dk, dv))
-    o, S = oracle.delta_recurrent(q, k, v, beta, g, S0, lib=lib)
     M = S0[0, 0].T.copy()
+    Ms = []
     for t in range(T):
         kt = k[0, 0, t][:, None]
         M = alpha[t] * M @ (np.eye(dk) - beta[0, 0, t] * (kt @ kt.T)) \
             + beta[0, 0, t] * (v[0, 0, t][:, None] @ kt.T)
-        _close(o[0, 0, t], M @ q[0, 0, t], what="scalar gate o")
-    _close(S[0, 0], M.T, what="scalar gate S")
+        Ms.append(M.copy())
+    for g in (g_chan, g_tok):
+        o, S = oracle.delta_recurrent(q, k, v, beta, g, S0, lib=lib)
+        for t in range(T):
+            _close(o[0, 0, t], Ms[t] @ q[0, 0, t], what=f"scalar gate o {g.ndim}")
+        _close(S[0, 0], Ms[-1].T, what=f"scalar gate S {g.ndim}")
 
 
 def pin_gated_pure_decay_closed_forms(lib):
@@ -380,6 +390,64 @@ def pin_gated_ut_form(lib):
 
 
 # --------------------------------------------------------------------------
+# Gated linear attention (scalar decay, no normaliser)
+# --------------------------------------------------------------------------
+
+def _gla_inputs(rng, B, H, T, dk, dv, scale=0.3):
+    q = rng.standard_normal((B, H, T, dk))
+    k = rng.standard_normal((B, H, T, dk))
+    v = rng.standard_normal((B, H, T, dv))
+    g = -np.abs(rng.standard_normal((B, H, T))) * scale
+    return q, k, v, g
+
+
+def pin_gla_decayed_quadratic_form(lib):
+    """Unrolling S_t = a_t S_{t-1} + k_t^T v_t with G_t = sum_{s<=t} log a_s:
+    S_t = e^{G_t} S_0 + sum_{j<=t} e^{G_t - G_j} k_j^T v_j, so
+    O = diag(e^G) Q S_0 + (tril(Q K^T) * M) V with M_tj = e^{G_t - G_j}, and
+    S_T = e^{G_T} S_0 + (K * e^{G_T - G})^T V."""
+    rng = _rng(20)
+    B, H, T, dk, dv = 1, 2, 25, 6, 5
+    q, k, v, g = _gla_inputs(rng, B, H, T, dk, dv)
+    S0 = rng.standard_normal((B, H, dk, dv))
+    o, S = oracle.gla_recurrent(q, k, v, g, S0, lib=lib)
+    for h in range(H):
+        G = np.cumsum(g[0, h])
+        M = np.tril(np.exp(G[:, None] - G[None, :]))
+        Q, K, V = q[0, h], k[0, h], v[0, h]
+        O = np.exp(G)[:, None] * (Q @ S0[0, h]) + (np.tril(Q @ K.T) * M) @ V
+        ST = np.exp(G[-1]) * S0[0, h] + (K * np.exp(G[-1] - G)[:, None]).T @ V
+        _close(o[0, h], O, tol=1e-10, what="gla quadratic o")
+        _close(S[0, h], ST, tol=1e-10, what="gla quadratic S")
+
+
+def pin_gla_limits(lib):
+    """No decay (g None, or g = 0) is additive linear attention without a
+    normaliser: S_T = S_0 + sum_j k_j^T v_j (in any order), o_t = q_t S_t.
+    Decay 0 (g = -inf) keeps only the newest write: S_t = k_t^T v_t,
+    o_t = (q_t . k_t) v_t."""
+    rng = _rng(21)
+    B, H, T, dk, dv = 1, 2, 18, 5, 4
+    q, k, v, _ = _gla_inputs(rng, B, H, T, dk, dv)
+    S0 = rng.standard_normal((B, H, dk, dv))
+    o1, S1 = oracle.gla_recurrent(q, k, v, None, S0, lib=lib)
+    o2, S2 = oracle.gla_recurrent(q, k, v, np.zeros((B, H, T)), S0, lib=lib)
+    _close(o1, o2, tol=0, what="g=0 o")
+    _close(S1, S2, tol=0, what="g=0 S")
+    for h in range(H):
+        K, V = k[0, h], v[0, h]
+        perm = rng.permutation(T)
+        _close(S1[0, h], S0[0, h] + K[perm].T @ V[perm], what="additive closed form")
+        Sc = S0[0, h] + np.cumsum(K[:, :, None] * V[:, None, :], axis=0)
+        _close(o1[0, h], np.einsum("td,tde->te", q[0, h], Sc), what="additive read")
+    o3, S3 = oracle.gla_recurrent(q, k, v, np.full((B, H, T), -np.inf), S0, lib=lib)
+    for h in range(H):
+        _close(S3[0, h], np.outer(k[0, h, -1], v[0, h, -1]), what="a=0 state")
+        qk = np.sum(q[0, h] * k[0, h], axis=1)
+        _close(o3[0, h], qk[:, None] * v[0, h], what="a=0 out")
+
+
+# --------------------------------------------------------------------------
 # Input handling and state carry
 # --------------------------------------------------------------------------
 
@@ -400,6 +468,11 @@ def pin_stored_precision_widening(lib):
         la2 = oracle.la_recurrent(*[t.double() for t in args[:3]], lib=lib)
         for a, b in zip(la1, la2):
             _close(a, b, tol=0, what="widening la")
+        gs = args[4][..., 0].contiguous()
+        gl1 = oracle.gla_recurrent(*args[:3], gs, lib=lib)
+        gl2 = oracle.gla_recurrent(*[t.double() for t in args[:3]], gs.double(), lib=lib)
+        for a, b in zip(gl1, gl2):
+            _close(a, b, tol=0, what="widening gla")
 
 
 def pin_state_carry(lib):
@@ -430,6 +503,14 @@ def pin_state_carry(lib):
     _close(np.concatenate([ob1, ob2], axis=2), oa, what="la carry o")
     _close(Sb2, Sa, what="la carry S")
     _close(zb2, za, what="la carry z")
+    gg = -np.abs(rng.standard_normal((B, H, T))) * 0.2
+    oc, Sc = oracle.gla_recurrent(qa, ka, va, gg, lib=lib)
+    oc1, Sc1 = oracle.gla_recurrent(qa[:, :, :9], ka[:, :, :9], va[:, :, :9], gg[:, :, :9],
+                                    lib=lib)
+    oc2, Sc2 = oracle.gla_recurrent(qa[:, :, 9:], ka[:, :, 9:], va[:, :, 9:], gg[:, :, 9:],
+                                    Sc1, lib=lib)
+    _close(np.concatenate([oc1, oc2], axis=2), oc, what="gla carry o")
+    _close(Sc2, Sc, what="gla carry S")
 
 
 ALL_PINS = [
@@ -447,6 +528,8 @@ ALL_PINS = [
     pin_gated_scalar_householder,
     pin_gated_pure_decay_closed_forms,
     pin_gated_ut_form,
+    pin_gla_decayed_quadratic_form,
+    pin_gla_limits,
     pin_stored_precision_widening,
     pin_state_carry,
 ]

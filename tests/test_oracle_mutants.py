@@ -46,14 +46,25 @@ MUTANTS = {
         "S[(size_t)i * dv + j] += kt[i] * u[j];",
         "S[(size_t)i * dv + j] += kt[j % dk] * u[i % dv];"),
     "gate_sign": (
-        "const double a = exp(rd(g, qk_row + i, dt));",
-        "const double a = exp(-rd(g, qk_row + i, dt));"),
+        "? exp(rd(g, qk_row + i, dt))", "? exp(-rd(g, qk_row + i, dt))"),
     "gate_uses_previous_token": (
-        "const double a = exp(rd(g, qk_row + i, dt));",
-        "const double a = exp(rd(g, (t > 0 ? qk_row - dk : qk_row) + i, dt));"),
+        "? exp(rd(g, qk_row + i, dt))",
+        "? exp(rd(g, (t > 0 ? qk_row - dk : qk_row) + i, dt))"),
     "gate_same_for_all_channels": (
-        "const double a = exp(rd(g, qk_row + i, dt));",
-        "const double a = exp(rd(g, qk_row, dt));"),
+        "? exp(rd(g, qk_row + i, dt))", "? exp(rd(g, qk_row, dt))"),
+    "scalar_gate_sign": (
+        ": exp(rd(g, (size_t)bh * T + t, dt));", ": exp(-rd(g, (size_t)bh * T + t, dt));"),
+    "scalar_gate_uses_previous_token": (
+        ": exp(rd(g, (size_t)bh * T + t, dt));",
+        ": exp(rd(g, (size_t)bh * T + (t > 0 ? t - 1 : t), dt));"),
+    "gla_decay_applied_twice": ("S[i] *= a;", "S[i] *= a * a;"),
+    "gla_decay_uses_next_token": (
+        "const double a = exp(rd(g, (size_t)bh * T + t, dt));",
+        "const double a = exp(rd(g, (size_t)bh * T + (t + 1 < T ? t + 1 : t), dt));"),
+    "gla_write_with_wrong_value_column": (
+        "vt[j] = rd(v, v_row + j, dt);", "vt[j] = rd(v, v_row + (j + 1) % dv, dt);"),
+    "gla_read_with_key": (
+        "const double qi = rd(q, qk_row + i, dt);", "const double qi = rd(k, qk_row + i, dt);"),
     "bf16_widening_wrong_shift": (
         "uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;",
         "uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 15;"),
