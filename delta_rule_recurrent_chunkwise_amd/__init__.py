@@ -18,12 +18,16 @@ import torch
 
 __all__ = [
     "la_prefill", "la_decode_step", "deltanet_prefill", "deltanet_decode_step",
-    "la_strerror", "library", "LIB_PATH", "EXPORTED_SYMBOLS", "LinAttnError",
+    "gated_deltanet_prefill", "gated_deltanet_decode_step", "gla_prefill",
+    "gla_decode_step", "la_strerror", "library", "LIB_PATH", "EXPORTED_SYMBOLS",
+    "LinAttnError",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblinattn.so")
 EXPORTED_SYMBOLS = ("la_prefill", "la_decode_step", "deltanet_prefill",
-                    "deltanet_decode_step", "la_strerror")
+                    "deltanet_decode_step", "gated_deltanet_prefill",
+                    "gated_deltanet_decode_step", "gla_prefill", "gla_decode_step",
+                    "la_strerror")
 
 LA_DTYPE_F32, LA_DTYPE_BF16 = 0, 1
 _DTYPES = {torch.float32: LA_DTYPE_F32, torch.bfloat16: LA_DTYPE_BF16}
@@ -53,8 +57,11 @@ def library():
         lib.la_decode_step.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
         lib.deltanet_prefill.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
         lib.deltanet_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
-        for fn in ("la_prefill", "la_decode_step", "deltanet_prefill",
-                   "deltanet_decode_step"):
+        lib.gated_deltanet_prefill.argtypes = lib.deltanet_prefill.argtypes
+        lib.gated_deltanet_decode_step.argtypes = lib.deltanet_decode_step.argtypes
+        lib.gla_prefill.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+        lib.gla_decode_step.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
+        for fn in EXPORTED_SYMBOLS[:-1]:
             getattr(lib, fn).restype = I
         lib.la_strerror.argtypes = [I]
         lib.la_strerror.restype = ctypes.c_char_p
@@ -198,4 +205,83 @@ def deltanet_decode_step(q, k, v, beta, S, g=None, o=None, stream=None):
                                         _ptr(o), _ptr(S), N, H, dk, dv, _DTYPES[dtype],
                                         _stream(dev, stream))
     _check("deltanet_decode_step", rc)
+    return o
+
+
+def gated_deltanet_prefill(q, k, v, beta, g, S=None, use_initial_state=False, o=None,
+                           stream=None):
+    """Delta rule with one decay per token (g = log-decay [B,H,T]) over
+    q, k [B,H,T,dk], v [B,H,T,dv], beta [B,H,T].
+    Returns (o [B,H,T,dv], S [B,H,dk,dv] fp32)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if g is None:
+        raise ValueError("gated_deltanet_prefill: g is required")
+    dev, dtype = _inputs("gated_deltanet_prefill", dict(q=q, k=k, v=v, beta=beta, g=g),
+                         dict(q=(B, H, T, dk), k=(B, H, T, dk), v=(B, H, T, dv),
+                              beta=(B, H, T), g=(B, H, T)))
+    if use_initial_state and S is None:
+        raise ValueError("gated_deltanet_prefill: use_initial_state needs S")
+    S = _state("gated_deltanet_prefill", "S", S, (B, H, dk, dv), dev)
+    o = _out("gated_deltanet_prefill", o, (B, H, T, dv), dev, dtype)
+    rc = library().gated_deltanet_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                                          _ptr(o), _ptr(S), int(bool(use_initial_state)),
+                                          B, H, T, dk, dv, _DTYPES[dtype],
+                                          _stream(dev, stream))
+    _check("gated_deltanet_prefill", rc)
+    return o, S
+
+
+def gated_deltanet_decode_step(q, k, v, beta, g, S, o=None, stream=None):
+    """One token per sequence of gated_deltanet_prefill: q, k [N,H,dk],
+    v [N,H,dv], beta [N,H], g [N,H]; S [N,H,dk,dv] fp32 updated in place.
+    Returns o [N,H,dv]."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if g is None:
+        raise ValueError("gated_deltanet_decode_step: g is required")
+    dev, dtype = _inputs("gated_deltanet_decode_step", dict(q=q, k=k, v=v, beta=beta, g=g),
+                         dict(q=(N, H, dk), k=(N, H, dk), v=(N, H, dv), beta=(N, H),
+                              g=(N, H)))
+    S = _state("gated_deltanet_decode_step", "S", S, (N, H, dk, dv), dev)
+    o = _out("gated_deltanet_decode_step", o, (N, H, dv), dev, dtype)
+    rc = library().gated_deltanet_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                              _ptr(g), _ptr(o), _ptr(S), N, H, dk, dv,
+                                              _DTYPES[dtype], _stream(dev, stream))
+    _check("gated_deltanet_decode_step", rc)
+    return o
+
+
+def gla_prefill(q, k, v, g=None, S=None, use_initial_state=False, o=None, stream=None):
+    """Gated linear attention S <- a S + k^T v, o = q S over q, k [B,H,T,dk],
+    v [B,H,T,dv], g = log-decay [B,H,T] or None.
+    Returns (o [B,H,T,dv], S [B,H,dk,dv] fp32)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev, dtype = _inputs("gla_prefill", dict(q=q, k=k, v=v, g=g),
+                         dict(q=(B, H, T, dk), k=(B, H, T, dk), v=(B, H, T, dv),
+                              g=(B, H, T)))
+    if use_initial_state and S is None:
+        raise ValueError("gla_prefill: use_initial_state needs S")
+    S = _state("gla_prefill", "S", S, (B, H, dk, dv), dev)
+    o = _out("gla_prefill", o, (B, H, T, dv), dev, dtype)
+    rc = library().gla_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(o), _ptr(S),
+                               int(bool(use_initial_state)), B, H, T, dk, dv,
+                               _DTYPES[dtype], _stream(dev, stream))
+    _check("gla_prefill", rc)
+    return o, S
+
+
+def gla_decode_step(q, k, v, S, g=None, o=None, stream=None):
+    """One token per sequence of gla_prefill: q, k [N,H,dk], v [N,H,dv],
+    g [N,H] or None; S [N,H,dk,dv] fp32 updated in place.  Returns o."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dtype = _inputs("gla_decode_step", dict(q=q, k=k, v=v, g=g),
+                         dict(q=(N, H, dk), k=(N, H, dk), v=(N, H, dv), g=(N, H)))
+    S = _state("gla_decode_step", "S", S, (N, H, dk, dv), dev)
+    o = _out("gla_decode_step", o, (N, H, dv), dev, dtype)
+    rc = library().gla_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(o), _ptr(S),
+                                   N, H, dk, dv, _DTYPES[dtype], _stream(dev, stream))
+    _check("gla_decode_step", rc)
     return o

@@ -44,7 +44,7 @@ const char* la_strerror(int code) {
     case LA_ERR_DTYPE: return "dtype must be LA_DTYPE_F32 (0) or LA_DTYPE_BF16 (1)";
     case LA_ERR_UNSUPPORTED_DIM:
       return "unsupported head dimension: dk and dv must each be 16, 32, 64 or 128 "
-             "(float32 gated prefill: dk <= 64)";
+             "(float32 deltanet_prefill with a per-channel gate: dk <= 64)";
     case LA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch or a workspace allocation";
     case LA_ERR_ALIGN:
       return "q, k and v (prefill) and S (decode) must be 16-byte aligned";
@@ -101,6 +101,57 @@ int deltanet_decode_step(const void* q, const void* k, const void* v, const void
   if (!aligned16(S)) return LA_ERR_ALIGN;
   linattn::DecodeArgs a{q, k, v, beta, g, o, S, nullptr, N * H};
   return launch_rc(linattn::launch_decode(g ? linattn::DEC_GATED : linattn::DEC_DELTA, dtype == LA_DTYPE_BF16, dk, dv, a,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int gated_deltanet_prefill(const void* q, const void* k, const void* v, const void* beta,
+                           const void* g, void* o, float* S, int use_initial_state, int B,
+                           int H, int T, int dk, int dv, int dtype, void* stream) {
+  if (!S || (T != 0 && (!q || !k || !v || !beta || !g || !o))) return LA_ERR_NULL;
+  if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
+  if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1, true)) return LA_ERR_SHAPE;
+  if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return LA_ERR_ALIGN;
+  linattn::PrefillArgs a{q, k, v, beta, g, o, S, nullptr, B, H, T, dv, use_initial_state ? 1 : 0};
+  return launch_rc(linattn::launch_prefill(linattn::PF_SGATED, dtype == LA_DTYPE_BF16, dk, a,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int gated_deltanet_decode_step(const void* q, const void* k, const void* v, const void* beta,
+                               const void* g, void* o, float* S, int N, int H, int dk, int dv,
+                               int dtype, void* stream) {
+  if (!q || !k || !v || !beta || !g || !o || !S) return LA_ERR_NULL;
+  if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
+  if (!sizes_ok(N, H, 1, dk > 0 ? dk : 1, dv > 0 ? dv : 1)) return LA_ERR_SHAPE;
+  if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
+  if (!aligned16(S)) return LA_ERR_ALIGN;
+  linattn::DecodeArgs a{q, k, v, beta, g, o, S, nullptr, N * H};
+  return launch_rc(linattn::launch_decode(linattn::DEC_SGATED, dtype == LA_DTYPE_BF16, dk, dv, a,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int gla_prefill(const void* q, const void* k, const void* v, const void* g, void* o, float* S,
+                int use_initial_state, int B, int H, int T, int dk, int dv, int dtype,
+                void* stream) {
+  if (!S || (T != 0 && (!q || !k || !v || !o))) return LA_ERR_NULL;
+  if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
+  if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1, true)) return LA_ERR_SHAPE;
+  if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return LA_ERR_ALIGN;
+  linattn::PrefillArgs a{q, k, v, nullptr, g, o, S, nullptr, B, H, T, dv, use_initial_state ? 1 : 0};
+  return launch_rc(linattn::launch_prefill(linattn::PF_GLA, dtype == LA_DTYPE_BF16, dk, a,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int gla_decode_step(const void* q, const void* k, const void* v, const void* g, void* o,
+                    float* S, int N, int H, int dk, int dv, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !S) return LA_ERR_NULL;
+  if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
+  if (!sizes_ok(N, H, 1, dk > 0 ? dk : 1, dv > 0 ? dv : 1)) return LA_ERR_SHAPE;
+  if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
+  if (!aligned16(S)) return LA_ERR_ALIGN;
+  linattn::DecodeArgs a{q, k, v, nullptr, g, o, S, nullptr, N * H};
+  return launch_rc(linattn::launch_decode(linattn::DEC_GLA, dtype == LA_DTYPE_BF16, dk, dv, a,
                                           static_cast<hipStream_t>(stream)));
 }
 

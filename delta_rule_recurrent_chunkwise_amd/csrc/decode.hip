@@ -1,6 +1,7 @@
 // decode.hip -- one-token decode steps that update each head's fp32 state in
-// place: the delta rule (optionally with a per-key-channel decay) and ELU+1
-// linear attention with its normaliser.
+// place: the delta rule (optionally with a decay per key channel or per
+// token), ELU+1 linear attention with its normaliser, and gated linear
+// attention.
 //
 // Delta rule, from the layer forward of the article "From GPT-2 to Kimi K3,
 // explained", section "DeltaNet (Fast Weight Programmers)", at one token:
@@ -10,6 +11,8 @@
 //   S <- S + phi(k)^T v, z <- z + phi(k),
 //   o = phi(q) S / phi(q).z = (phi(q) S_old + (phi(q).phi(k)) v)
 //                             / (phi(q).z_old + phi(q).phi(k)).
+// Gated linear attention, section "Gated Delta Net" (the additive cache with
+// a forgetting factor): S' = a S, S <- S' + k^T v, o = q S' + (q.k) v.
 // Writing the output through the old state lets each state element be read
 // once and written once: the step is a pure streaming read-modify-write of
 // the state, so the kernel is bound by HBM bandwidth.
@@ -66,10 +69,12 @@ __attribute__((amdgpu_waves_per_eu(WPE))) void decode_kernel(DecodeArgs a) {
   typedef typename E::T T;
   constexpr int CQ = Sh::CQ, RPT = Sh::RPT, RG = Sh::RG, TPH = Sh::TPH, HPB = Sh::HPB;
   constexpr int NTB = Sh::NTB;
+  constexpr bool kDecay = KIND == DEC_GATED || KIND == DEC_SGATED || KIND == DEC_GLA;
+  constexpr bool kDelta = KIND == DEC_DELTA || KIND == DEC_GATED || KIND == DEC_SGATED;
 
   __shared__ float s_q[HPB][DK];
   __shared__ float s_k[HPB][DK];
-  __shared__ float s_a[KIND == DEC_GATED ? HPB : 1][KIND == DEC_GATED ? DK : 1];
+  __shared__ float s_a[kDecay ? HPB : 1][kDecay ? DK : 1];
   __shared__ float s_z[KIND == DEC_LA ? HPB : 1][KIND == DEC_LA ? DK : 1];
   __shared__ float4 s_red0[HPB][RG][CQ];
   __shared__ float4 s_red1[HPB][RG][CQ];
@@ -109,9 +114,10 @@ __attribute__((amdgpu_waves_per_eu(WPE))) void decode_kernel(DecodeArgs a) {
       kv = elu_plus_one(kv);
       s_z[h][d] = hh < a.nheads ? a.z[hh * DK + d] : 0.f;
     }
-    if (KIND == DEC_GATED) {
+    if (kDecay) {  // per key channel, or one value per head (and none: a = 1)
       const T* gg = reinterpret_cast<const T*>(a.g);
-      s_a[h][d] = hh < a.nheads ? __expf(E::ld(gg + hh * DK + d)) : 1.f;
+      const long gi = KIND == DEC_GATED ? hh * DK + d : hh;
+      s_a[h][d] = hh < a.nheads && gg ? __expf(E::ld(gg + gi)) : 1.f;
     }
     s_q[h][d] = qv;
     s_k[h][d] = kv;
@@ -128,11 +134,11 @@ __attribute__((amdgpu_waves_per_eu(WPE))) void decode_kernel(DecodeArgs a) {
     const int row = rg + RG * j;
     const float kr = s_k[hb][row];
     const float qr = s_q[hb][row];
-    if (KIND == DEC_GATED) {
+    if (kDecay) {
       const float ar = s_a[hb][row];
       s[j].x *= ar; s[j].y *= ar; s[j].z *= ar; s[j].w *= ar;
     }
-    if (KIND != DEC_LA) {
+    if (kDelta) {
       r4.x += kr * s[j].x; r4.y += kr * s[j].y; r4.z += kr * s[j].z; r4.w += kr * s[j].w;
     }
     s4.x += qr * s[j].x; s4.y += qr * s[j].y; s4.z += qr * s[j].z; s4.w += qr * s[j].w;
@@ -173,6 +179,9 @@ __attribute__((amdgpu_waves_per_eu(WPE))) void decode_kernel(DecodeArgs a) {
         const float inv = 1.f / (sz + sc);
         o4 = make_float4((s4.x + sc * v4.x) * inv, (s4.y + sc * v4.y) * inv,
                          (s4.z + sc * v4.z) * inv, (s4.w + sc * v4.w) * inv);
+      } else if (KIND == DEC_GLA) {
+        u4 = v4;
+        o4 = make_float4(s4.x + sc * v4.x, s4.y + sc * v4.y, s4.z + sc * v4.z, s4.w + sc * v4.w);
       } else {
         const float b = E::ld(reinterpret_cast<const T*>(a.beta) + hc);
         u4 = make_float4(b * (v4.x - r4.x), b * (v4.y - r4.y), b * (v4.z - r4.z),
@@ -239,16 +248,21 @@ static hipError_t launch_decode_e(int dk, int dv, const DecodeArgs& a, hipStream
 #undef LINATTN_DV
 }
 
+template <class E>
+static hipError_t launch_decode_kind(int kind, int dk, int dv, const DecodeArgs& a, hipStream_t st) {
+  switch (kind) {
+    case DEC_DELTA: return launch_decode_e<E, DEC_DELTA>(dk, dv, a, st);
+    case DEC_GATED: return launch_decode_e<E, DEC_GATED>(dk, dv, a, st);
+    case DEC_LA: return launch_decode_e<E, DEC_LA>(dk, dv, a, st);
+    case DEC_SGATED: return launch_decode_e<E, DEC_SGATED>(dk, dv, a, st);
+    case DEC_GLA: return launch_decode_e<E, DEC_GLA>(dk, dv, a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_decode(int kind, int bf16, int dk, int dv, const DecodeArgs& a,
                          hipStream_t st) {
-  if (bf16) {
-    if (kind == DEC_DELTA) return launch_decode_e<BF16, DEC_DELTA>(dk, dv, a, st);
-    if (kind == DEC_GATED) return launch_decode_e<BF16, DEC_GATED>(dk, dv, a, st);
-    return launch_decode_e<BF16, DEC_LA>(dk, dv, a, st);
-  }
-  if (kind == DEC_DELTA) return launch_decode_e<F32, DEC_DELTA>(dk, dv, a, st);
-  if (kind == DEC_GATED) return launch_decode_e<F32, DEC_GATED>(dk, dv, a, st);
-  return launch_decode_e<F32, DEC_LA>(dk, dv, a, st);
+  return bf16 ? launch_decode_kind<BF16>(kind, dk, dv, a, st) : launch_decode_kind<F32>(kind, dk, dv, a, st);
 }
 
 }  // namespace linattn

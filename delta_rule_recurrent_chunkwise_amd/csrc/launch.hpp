@@ -5,15 +5,19 @@
 
 namespace linattn {
 
-enum DecodeKind { DEC_DELTA = 0, DEC_GATED = 1, DEC_LA = 2 };
-enum PrefillMode { PF_LA = 0, PF_DELTA = 1, PF_GATED = 2 };
+// DEC_GATED: decay per key channel; DEC_SGATED: one decay per token (Gated
+// DeltaNet); DEC_GLA: gated linear attention, S <- a S + k^T v, o = q S.
+enum DecodeKind { DEC_DELTA = 0, DEC_GATED = 1, DEC_LA = 2, DEC_SGATED = 3, DEC_GLA = 4 };
+// PF_GATED: gated delta rule, decay per key channel; PF_SGATED: one decay per
+// token (Gated DeltaNet); PF_GLA: gated linear attention (one decay per token).
+enum PrefillMode { PF_LA = 0, PF_DELTA = 1, PF_GATED = 2, PF_GLA = 3, PF_SGATED = 4 };
 
 struct DecodeArgs {
   const void* q;
   const void* k;
   const void* v;
   const void* beta;  // delta / gated only
-  const void* g;     // gated only
+  const void* g;     // gated only: [N*H][dk]; [N*H] for DEC_SGATED, DEC_GLA (may be NULL)
   void* o;
   float* S;
   float* z;          // linear attention only
@@ -25,7 +29,7 @@ struct PrefillArgs {
   const void* k;
   const void* v;
   const void* beta;  // delta / gated only
-  const void* g;     // gated only
+  const void* g;     // gated only: log-decay [B,H,T,dk] (PF_GATED) or [B,H,T]
   void* o;
   float* S;
   float* z;          // linear attention only

@@ -1,6 +1,7 @@
 // prefill.hip -- chunkwise prefill of causal linear attention with a fixed
 // dk x dv fp32 state: ELU+1 linear attention with normaliser, the delta rule,
-// and the per-key-channel gated delta rule.
+// the gated delta rule (decay per key channel or per token), and gated
+// linear attention (additive cache with a per-token forgetting factor).
 //
 // Method (article "From GPT-2 to Kimi K3, explained"):
 //  * section "DeltaNet (Parallelizing Linear Transformers with Delta Rule)":
@@ -21,6 +22,15 @@
 //    holds with K~ = Gam*K, K^ = K/Gam, Q~ = Gam*Q:
 //      L = tril(diag(beta) K~ K^^T, -1), u = T diag(beta) (V - K~ S),
 //      O = Q~ S + tril(Q~ K^^T) u,  S <- diag(Gam_C) S + (K*Gam_C/Gam)^T u.
+//  * one decay per token (section "Gated Delta Net"): with G_t the summed
+//    log-decay from the chunk start, the same products are formed from the
+//    plain Q and K, and each entry (r, c) of tril(Q K^T) and L is scaled by
+//    exp(G_r - G_c) <= 1; the rows of Q S and K S by exp(G_r); the state by
+//    exp(G_C) and the rows of u by exp(G_C - G_r) before S += K^T u.  No
+//    factor exceeds 1, so any decay is representable.
+//  * section "Gated Delta Net", first step: the additive cache with a
+//    forgetting factor, S <- a_t S + k^T v, o = q S (q, k as given).  It is
+//    the per-token gated form with u = V: no beta, no L, no normaliser.
 //
 // Mapping to gfx950.  One workgroup (4 waves) owns one (batch, head) and a
 // slice of DVS value columns (32, or 16 when dv = 16): the value columns of
@@ -42,9 +52,20 @@ constexpr int kC = 64;         // chunk length in tokens
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kWaves = kThreads / 64;
 
+// kGate: decay per key channel, decayed operands (K~, K^, Q~) staged;
+// kScal: one decay per token, applied to the products' entries and rows;
+// kSolve: beta, L and T = (I + L)^-1 (the delta-rule modes).
+template <int MODE>
+struct ModeTraits {
+  static constexpr bool kGate = MODE == PF_GATED;
+  static constexpr bool kScal = MODE == PF_SGATED || MODE == PF_GLA;
+  static constexpr bool kSolve = MODE == PF_DELTA || MODE == PF_GATED || MODE == PF_SGATED;
+};
+
 template <int DK, class E, int MODE, int DVS>
 struct PrefillLayout {
   typedef typename E::T T;
+  static constexpr bool kGate = ModeTraits<MODE>::kGate;
   static constexpr int PAD = 16 / (int)sizeof(T);  // one 16-byte vector of padding
   static constexpr int LQ = DK + PAD;               // row stride: sQ, sK, sKh
   static constexpr int LKT = kC + PAD;              // row stride: sKt, sVt, sA
@@ -52,14 +73,15 @@ struct PrefillLayout {
   static constexpr int oQ = 0;
   static constexpr int oK = oQ + kC * LQ * (int)sizeof(T);
   static constexpr int oKh = oK + kC * LQ * (int)sizeof(T);
-  static constexpr int oKt = oKh + (MODE == PF_GATED ? kC * LQ * (int)sizeof(T) : 0);
+  static constexpr int oKt = oKh + (kGate ? kC * LQ * (int)sizeof(T) : 0);
   static constexpr int oVt = oKt + DK * LKT * (int)sizeof(T);
   static constexpr int oA = oVt + DVS * LKT * (int)sizeof(T);
   static constexpr int oTL = oA + kC * LKT * (int)sizeof(T);
-  static constexpr int oRow = oTL + (MODE == PF_LA ? 0 : kC * LTL * 4);  // beta or den
+  static constexpr int oRow = oTL + (ModeTraits<MODE>::kSolve ? kC * LTL * 4 : 0);  // beta or den
   static constexpr int oVec = oRow + kC * 4;                            // Gam_C or z
   static constexpr int oPart = oVec + DK * 4;                           // scan partials
-  static constexpr int total = oPart + (MODE == PF_GATED ? kThreads * 4 : 0);
+  static constexpr int oG = oPart + (kGate ? kThreads * 4 : 0);         // per-token G_t
+  static constexpr int total = oG + (ModeTraits<MODE>::kScal ? kC * 4 : 0);
 };
 
 // Workgroup i runs on XCD i % 8.  Give consecutive logical indices (the dv
@@ -87,11 +109,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   constexpr int NCW = DVS / 16;  // chain waves
   constexpr int NKT = DK / 16;   // 16-row tiles of S per chain wave
   constexpr int LQ = L::LQ, LKT = L::LKT, LTL = L::LTL;
+  constexpr bool kGate = ModeTraits<MODE>::kGate;
+  constexpr bool kScal = ModeTraits<MODE>::kScal;
+  constexpr bool kSolve = ModeTraits<MODE>::kSolve;
 
   __shared__ __attribute__((aligned(16))) char smem[L::total];
   T* sQ = reinterpret_cast<T*>(smem + L::oQ);
   T* sK = reinterpret_cast<T*>(smem + L::oK);
-  T* sKh = MODE == PF_GATED ? reinterpret_cast<T*>(smem + L::oKh) : sK;
+  T* sKh = kGate ? reinterpret_cast<T*>(smem + L::oKh) : sK;
   T* sKt = reinterpret_cast<T*>(smem + L::oKt);
   T* sVt = reinterpret_cast<T*>(smem + L::oVt);
   T* sA = reinterpret_cast<T*>(smem + L::oA);
@@ -99,6 +124,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   float* sRow = reinterpret_cast<float*>(smem + L::oRow);  // beta (delta) / den (LA)
   float* sVec = reinterpret_cast<float*>(smem + L::oVec);  // Gam_C (gated) / z (LA)
   float* sPart = reinterpret_cast<float*>(smem + L::oPart);
+  float* sG = reinterpret_cast<float*>(smem + L::oG);  // per-token modes: G_t
 
   const int nsl = a.dv / DVS;
   const int w = xcd_remap(blockIdx.x, gridDim.x);
@@ -116,7 +142,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   const T* kh = reinterpret_cast<const T*>(a.k) + (size_t)bh * Tn * DK;
   const T* vh = reinterpret_cast<const T*>(a.v) + (size_t)bh * Tn * dv + sl * DVS;
   const T* bth = reinterpret_cast<const T*>(a.beta) + (size_t)bh * Tn;
-  const T* gh = reinterpret_cast<const T*>(a.g) + (size_t)bh * Tn * DK;
+  // log-decay: [T][DK] per key channel, [T] per token, or none (gated
+  // linear attention without a decay)
+  const T* gh = a.g ? reinterpret_cast<const T*>(a.g) + (size_t)bh * Tn * (kGate ? DK : 1) : nullptr;
   T* oh = reinterpret_cast<T*>(a.o) + (size_t)bh * Tn * dv + sl * DVS;
   float* Sh = a.S + (size_t)bh * DK * dv + sl * DVS;
 
@@ -155,10 +183,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   constexpr int NTOT = 2 * NQV + kC * VPRS;
   constexpr int NPT = (NTOT + kThreads - 1) / kThreads;
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));  // a register array of
-  u32x4v pre[MODE == PF_GATED ? 1 : NPT];                        // structs would go to memory
-  float preb = 0.f;
+  u32x4v pre[kGate ? 1 : NPT];                        // structs would go to memory
+  float preb = 0.f, preg = 0.f;
   auto prefetch = [&](int c) {
-    if constexpr (MODE != PF_GATED) {
+    if constexpr (!kGate) {
       const T* const pq = qh;
       const T* const pk = kh;
       const T* const pv = vh;
@@ -176,7 +204,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         }
         pre[j] = *reinterpret_cast<const u32x4v*>(src);
       }
-      if (MODE != PF_LA && tid < kC) preb = E::ld(bth + min(c * kC + tid, tlast));
+      if (kSolve && tid < kC) preb = E::ld(bth + min(c * kC + tid, tlast));
+      if (kScal && tid < kC) preg = gh ? E::ld(gh + min(c * kC + tid, tlast)) : 0.f;
     }
   };
   prefetch(0);
@@ -186,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     __syncthreads();  // the previous chunk's readers of LDS are done
 
     // ---------------- stage the chunk in LDS ----------------
-    if (MODE != PF_GATED) {
+    if (!kGate) {
 #pragma unroll
       for (int j = 0; j < NPT; ++j) {
         const int i = tid + kThreads * j;
@@ -219,10 +248,20 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
           for (int e = 0; e < kVec; ++e) sKt[(cv * kVec + e) * LKT + r] = xv.e[e];
         }
       }
-      if (MODE != PF_LA && tid < kC) sRow[tid] = t0 + tid <= tlast ? preb : 0.f;
+      if (kSolve && tid < kC) sRow[tid] = t0 + tid <= tlast ? preb : 0.f;
+      if (kScal && tid < kC) {
+        // wave 0 (one lane per token): G_t = sum_{s<=t} g_s over the chunk
+        float x = t0 + tid <= tlast ? preg : 0.f;
+#pragma unroll
+        for (int off = 1; off < kC; off <<= 1) {
+          const float y = __shfl_up(x, off, kC);
+          if (lane >= off) x += y;
+        }
+        sG[tid] = x;
+      }
       if (c + 1 < nchunks) prefetch(c + 1);
     }
-    if (MODE == PF_GATED) {
+    if (kGate) {
       // cumulative log-decay per key channel over the chunk, then the scaled
       // operands Q~ = Gam Q, K~ = Gam K, K^ = K / Gam, (K Gam_C / Gam)^T
       constexpr int NP = kThreads / DK;  // token parts
@@ -234,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int j = 0; j < TPP; ++j) {
         const int t = t0 + part * TPP + j;
-        run += t <= tlast ? E::ld(gh + (size_t)t * DK + d) : 0.f;
+        if (t <= tlast) run += E::ld(gh + (size_t)t * DK + d);
         gl[j] = run;
       }
       sPart[part * DK + d] = run;
@@ -261,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         sKt[d * LKT + r] = E::cvt(kv * dec);
       }
     }
-    if (MODE == PF_GATED) {
+    if (kGate) {
       constexpr int VPRV = DVS / kVec;
       for (int i = tid; i < kC * VPRV; i += kThreads) {
         const int r = i / VPRV, cv = i - (i / VPRV) * VPRV;
@@ -270,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int e = 0; e < kVec; ++e) sVt[(cv * kVec + e) * LKT + r] = vv.e[e];
       }
-      if (MODE != PF_LA && tid < kC) sRow[tid] = t0 + tid <= tlast ? E::ld(bth + t0 + tid) : 0.f;
+      if (kSolve && tid < kC) sRow[tid] = t0 + tid <= tlast ? E::ld(bth + t0 + tid) : 0.f;
     }
     __syncthreads();
 
@@ -287,7 +326,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         floatx4 vv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) vv[i] = E::tof(vp[i]);
-        if (MODE == PF_LA) {
+        floatx4 dec = {1.f, 1.f, 1.f, 1.f};  // per-token decay exp(G_r) of rows r
+        if constexpr (kScal) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dec[i] = __expf(sG[16 * mt + 4 * lg + i]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ox[mt][i] *= dec[i];
+        }
+        if (!kSolve) {
           xx[mt] = vv;
         } else {
           const T* krow = sK + (16 * mt + lc) * LQ;
@@ -295,14 +341,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
           if constexpr (kBf16) y = mm_accB_bf16(zero4(), krow, st, NKT, lane);
           else y = mm_accB_f32(zero4(), krow, st, NKT, lane);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) xx[mt][i] = sRow[16 * mt + 4 * lg + i] * (vv[i] - y[i]);
+          for (int i = 0; i < 4; ++i) xx[mt][i] = sRow[16 * mt + 4 * lg + i] * (vv[i] - dec[i] * y[i]);
         }
       }
     } else {
       // jobs 0..9: tiles (i, j<=i) of tril(Q K^^T) -> sA
       // jobs 10..19: tiles (i, j<=i) of K~ K^^T -> L = beta_row * (.) strictly
       //              below the diagonal, stored transposed in sTL's upper part
-      const int njobs = MODE == PF_LA ? 10 : 20;
+      const int njobs = kSolve ? 20 : 10;
       for (int jb = wave - NCW; jb < njobs; jb += kWaves - NCW) {
         const bool isA = jb < 10;
         const int t = isA ? jb : jb - 10;
@@ -317,8 +363,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * ti + 4 * lg + i;
-          if (isA) sA[r * LKT + cc] = E::cvt(cc <= r ? acc[i] : 0.f);
-          else if (cc < r) sTL[cc * LTL + r] = sRow[r] * acc[i];
+          float x = acc[i];
+          if constexpr (kScal) x *= cc <= r ? __expf(sG[r] - sG[cc]) : 0.f;  // decay from c to r
+          if (isA) sA[r * LKT + cc] = E::cvt(cc <= r ? x : 0.f);
+          else if (cc < r) sTL[cc * LTL + r] = sRow[r] * x;
         }
       }
     }
@@ -367,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
           if (lane + 64 * h < DK) sVec[lane + 64 * h] += zs[h];
       }
       __syncthreads();
-    } else {
+    } else if constexpr (kSolve) {
       // T = (I + L)^{-1}.  Diagonal 16x16 blocks by forward substitution (one
       // lane per column), then off-diagonal blocks block-row by block-row:
       // T[bi][bj] = -T[bi][bi] * sum_{bj<=m<bi} L[bi][m] T[m][bj].
@@ -441,7 +489,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
       floatx4 ut[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        if (MODE == PF_LA) {
+        if (!kSolve) {
           ut[mt] = xx[mt];
         } else {
           // T is lower triangular: row tile mt needs column tiles 0..mt.  The
@@ -466,11 +514,25 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
           if (t0 + r <= tlast) oh[(size_t)(t0 + r) * dv + 16 * cw + lc] = E::cvt(val);
         }
       }
-      if (MODE == PF_GATED) {
+      if (kGate) {
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) st[kt][i] *= sVec[16 * kt + 4 * lg + i];
+      }
+      if constexpr (kScal) {
+        // S <- exp(G_C) S + K^T (u * exp(G_C - G_r)): row r of u decays from
+        // token r to the chunk end
+        const float gC = sG[kC - 1];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ut[mt][i] *= __expf(gC - sG[16 * mt + 4 * lg + i]);
+        const float eC = __expf(gC);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st[kt][i] *= eC;
       }
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt) {
@@ -527,7 +589,7 @@ static hipError_t launch_prefill_e(int dk, const PrefillArgs& a, hipStream_t st)
     case 32: return launch_prefill_dk<32, E, MODE>(a, st);
     case 64: return launch_prefill_dk<64, E, MODE>(a, st);
     case 128:
-      if constexpr (MODE == PF_GATED && sizeof(typename E::T) == 4) {
+      if constexpr (ModeTraits<MODE>::kGate && sizeof(typename E::T) == 4) {
         return hipErrorInvalidValue;  // LDS footprint exceeds one CU
       } else {
         return launch_prefill_dk<128, E, MODE>(a, st);
@@ -570,13 +632,23 @@ hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, hipS
     }
   }
   if (bf16) {
-    if (mode == PF_LA) return launch_prefill_e<BF16, PF_LA>(dk, a, st);
-    if (mode == PF_DELTA) return launch_prefill_e<BF16, PF_DELTA>(dk, a, st);
-    return launch_prefill_e<BF16, PF_GATED>(dk, a, st);
+    switch (mode) {
+      case PF_LA: return launch_prefill_e<BF16, PF_LA>(dk, a, st);
+      case PF_DELTA: return launch_prefill_e<BF16, PF_DELTA>(dk, a, st);
+      case PF_GATED: return launch_prefill_e<BF16, PF_GATED>(dk, a, st);
+      case PF_GLA: return launch_prefill_e<BF16, PF_GLA>(dk, a, st);
+      case PF_SGATED: return launch_prefill_e<BF16, PF_SGATED>(dk, a, st);
+      default: return hipErrorInvalidValue;
+    }
   }
-  if (mode == PF_LA) return launch_prefill_e<F32, PF_LA>(dk, a, st);
-  if (mode == PF_DELTA) return launch_prefill_e<F32, PF_DELTA>(dk, a, st);
-  return launch_prefill_e<F32, PF_GATED>(dk, a, st);
+  switch (mode) {
+    case PF_LA: return launch_prefill_e<F32, PF_LA>(dk, a, st);
+    case PF_DELTA: return launch_prefill_e<F32, PF_DELTA>(dk, a, st);
+    case PF_GATED: return launch_prefill_e<F32, PF_GATED>(dk, a, st);
+    case PF_GLA: return launch_prefill_e<F32, PF_GLA>(dk, a, st);
+    case PF_SGATED: return launch_prefill_e<F32, PF_SGATED>(dk, a, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace linattn

@@ -11,17 +11,22 @@
  *     and "DeltaNet (Parallelizing Linear Transformers with Delta Rule)":
  *     read r = k S, u = beta (v - r), write S += k^T u, output o = q S), whose
  *     prefill runs in the chunkwise UT/WY form of the latter section;
- *   - its per-key-channel gated variant (sections "Gated Delta Net" and "KDA /
- *     Kimi Linear"): before each read the state decays,
- *     S <- diag(a_t) S, with a separate decay a_t[i] per key channel i.
+ *   - its gated variants (sections "Gated Delta Net" and "KDA / Kimi
+ *     Linear"): before each read the state decays, S <- diag(a_t) S, with a
+ *     separate decay a_t[i] per key channel i (KDA), or one scalar a_t per
+ *     token (Gated DeltaNet);
+ *   - gated linear attention, the first step of section "Gated Delta Net"
+ *     (the additive cache with a forgetting factor credited to Mamba-2):
+ *     S <- a_t S + k^T v, o = q S.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
  * Layout.   All tensors are dense, row-major, last index fastest:
- *           q, k [B,H,T,dk]; v, o [B,H,T,dv]; beta [B,H,T]; g [B,H,T,dk];
+ *           q, k [B,H,T,dk]; v, o [B,H,T,dv]; beta [B,H,T];
+ *           g [B,H,T,dk] (per key channel) or [B,H,T] (per token);
  *           S [B,H,dk,dv] (row i = key channel i); z [B,H,dk].
  *           Decode entry points use the same layout with T = 1 dropped:
- *           q, k, g [N,H,dk]; v, o [N,H,dv]; beta [N,H].
+ *           q, k [N,H,dk]; v, o [N,H,dv]; beta [N,H]; g [N,H,dk] or [N,H].
  * Output.   o_t is read from the state AFTER token t has been written (the
  *           article's code reads q S after S += ...), and the normaliser of
  *           linear attention includes token t as well.
@@ -49,8 +54,8 @@
  *           64-token chunk may be partial).  T = 0 enqueues no work when
  *           use_initial_state is set and otherwise zero-fills S (and z);
  *           the token arrays may then be NULL.
- *           dk and dv each one of 16, 32, 64, 128.  The per-channel gated
- *           prefill with LA_DTYPE_F32 supports dk <= 64.
+ *           dk and dv each one of 16, 32, 64, 128.  deltanet_prefill with
+ *           a per-channel gate and LA_DTYPE_F32 supports dk <= 64.
  * Stream.   stream is a hipStream_t passed as void*; NULL is the null stream.
  *           Work is enqueued asynchronously; nothing synchronises the host.
  * Errors.   0 (LA_OK) or a negative code.  Arguments are validated before
@@ -118,6 +123,11 @@ int la_decode_step(const void *q, const void *k, const void *v, void *o,
  * and "KDA / Kimi Linear" is used instead:
  *   S_t = diag(a_t) S_{t-1} + beta_t k_t^T (v_t - k_t diag(a_t) S_{t-1}),
  * where g = log a (the log-decay, <= 0) is given per token and key channel.
+ * The chunked gated form divides keys by the decay accumulated from the
+ * start of their 64-token chunk, so the summed log-decay of any key channel
+ * over one chunk must stay above about -87 (the float exponent range);
+ * stronger decays overflow to Inf/NaN.  gated_deltanet_prefill has no such
+ * limit.
  * q and k are used as given: no feature map, normalisation or scale.
  * q, k [B,H,T,dk], v [B,H,T,dv], beta [B,H,T], g [B,H,T,dk] or NULL (dtype).
  * o [B,H,T,dv] out (dtype).  S [B,H,dk,dv] float32 in/out as in la_prefill.
@@ -139,6 +149,57 @@ int deltanet_decode_step(const void *q, const void *k, const void *v,
                          const void *beta, const void *g, void *o, float *S,
                          int N, int H, int dk, int dv, int dtype,
                          void *stream);
+
+/*
+ * gated_deltanet_prefill -- the delta rule with one decay per token and head
+ * (Gated DeltaNet, section "Gated Delta Net": a data-dependent scalar in
+ * (0, 1] decays the previous state):
+ *   S_t = a_t S_{t-1} + beta_t k_t^T (v_t - k_t a_t S_{t-1}),  o_t = q_t S_t,
+ * computed in the chunkwise form with per-token decay ratios exp(G_r - G_c)
+ * (G the summed log-decay), which are never above 1, so any g <= 0 is
+ * supported.  g [B,H,T] = log a (dtype, required).  Everything else as
+ * deltanet_prefill.  The result equals deltanet_prefill with g broadcast
+ * over the key channels.
+ */
+int gated_deltanet_prefill(const void *q, const void *k, const void *v,
+                           const void *beta, const void *g, void *o, float *S,
+                           int use_initial_state, int B, int H, int T, int dk,
+                           int dv, int dtype, void *stream);
+
+/*
+ * gated_deltanet_decode_step -- one token of gated_deltanet_prefill, state
+ * updated in place: S <- a S, r = k S, u = beta (v - r), S <- S + k^T u,
+ * o = q S.  g [N,H] = log a (required); the rest as deltanet_decode_step.
+ */
+int gated_deltanet_decode_step(const void *q, const void *k, const void *v,
+                               const void *beta, const void *g, void *o,
+                               float *S, int N, int H, int dk, int dv,
+                               int dtype, void *stream);
+
+/*
+ * gla_prefill -- gated linear attention: the additive cache of section
+ * "Linear Attention" with the forgetting factor of section "Gated Delta Net"
+ * (credited there to Mamba-2), with q and k used as given (no feature map,
+ * no normaliser):
+ *   S_t = a_t S_{t-1} + k_t^T v_t,  o_t = q_t S_t.
+ * Chunkwise: O = diag(Gam) Q S + (tril(Q K^T) * exp(G_r - G_c)) V and
+ * S <- Gam_C S + (K * Gam_C / Gam)^T V, with G the log-decay summed from the
+ * chunk start and Gam = exp(G).
+ * q, k [B,H,T,dk], v [B,H,T,dv], g [B,H,T] = log a or NULL (no decay), in
+ * dtype; o [B,H,T,dv] out; S [B,H,dk,dv] float32 in/out as in la_prefill.
+ */
+int gla_prefill(const void *q, const void *k, const void *v, const void *g,
+                void *o, float *S, int use_initial_state, int B, int H, int T,
+                int dk, int dv, int dtype, void *stream);
+
+/*
+ * gla_decode_step -- one token of gla_prefill, state updated in place:
+ * S <- a S + k^T v, o = q S.  q, k [N,H,dk], v [N,H,dv], g [N,H] or NULL
+ * (dtype); o [N,H,dv] out; S [N,H,dk,dv] float32 in place.
+ */
+int gla_decode_step(const void *q, const void *k, const void *v, const void *g,
+                    void *o, float *S, int N, int H, int dk, int dv, int dtype,
+                    void *stream);
 
 /* la_strerror -- a static, NUL-terminated description of an error code. */
 const char *la_strerror(int code);

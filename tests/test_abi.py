@@ -74,6 +74,57 @@ def _dn_decode(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=None, o=FAKE, S=FAKE, N=1, H
     return la.library().deltanet_decode_step(q, k, v, beta, g, o, S, N, H, dk, dv, dt, None)
 
 
+def _gdn_prefill(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, o=FAKE, S=FAKE, init=0, B=1, H=1,
+                 T=64, dk=64, dv=64, dt=1):
+    return la.library().gated_deltanet_prefill(q, k, v, beta, g, o, S, init, B, H, T, dk, dv,
+                                               dt, None)
+
+
+def _gdn_decode(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, o=FAKE, S=FAKE, N=1, H=1, dk=64,
+                dv=64, dt=1):
+    return la.library().gated_deltanet_decode_step(q, k, v, beta, g, o, S, N, H, dk, dv, dt,
+                                                   None)
+
+
+def _gla_prefill(q=FAKE, k=FAKE, v=FAKE, g=FAKE, o=FAKE, S=FAKE, init=0, B=1, H=1, T=64,
+                 dk=64, dv=64, dt=1):
+    return la.library().gla_prefill(q, k, v, g, o, S, init, B, H, T, dk, dv, dt, None)
+
+
+def _gla_decode(q=FAKE, k=FAKE, v=FAKE, g=FAKE, o=FAKE, S=FAKE, N=1, H=1, dk=64, dv=64, dt=1):
+    return la.library().gla_decode_step(q, k, v, g, o, S, N, H, dk, dv, dt, None)
+
+
+@pytest.mark.parametrize("missing", ["q", "k", "v", "beta", "g", "o", "S"])
+def test_gated_deltanet_null_pointers(missing):
+    assert _gdn_prefill(**{missing: None}) == NULL
+    assert _gdn_decode(**{missing: None}) == NULL
+
+
+@pytest.mark.parametrize("missing", ["q", "k", "v", "o", "S"])
+def test_gla_null_pointers(missing):
+    """g may be NULL (no decay); everything else is required."""
+    assert _gla_prefill(**{missing: None}) == NULL
+    assert _gla_decode(**{missing: None}) == NULL
+
+
+def test_scalar_gated_entry_points_validate_like_the_others():
+    for fn in (_gdn_prefill, _gla_prefill):
+        assert fn(dt=5) == DTYPE
+        assert fn(T=-1) == SHAPE
+        assert fn(B=0) == SHAPE
+        assert fn(dk=96) == DIM
+        assert fn(q=MISALIGNED) == ALIGN
+    for fn in (_gdn_decode, _gla_decode):
+        assert fn(dt=5) == DTYPE
+        assert fn(N=0) == SHAPE
+        assert fn(dv=8) == DIM
+        assert fn(S=MISALIGNED) == ALIGN
+    none = dict(q=None, k=None, v=None, o=None)
+    assert _gdn_prefill(T=0, init=1, beta=None, g=None, **none) == OK
+    assert _gla_prefill(T=0, init=1, g=None, **none) == OK
+
+
 @pytest.mark.parametrize("missing", ["q", "k", "v", "o", "S", "z"])
 def test_la_null_pointers(missing):
     assert _la_prefill(**{missing: None}) == NULL

@@ -16,7 +16,10 @@ dtype with round-to-nearest-even):
   beta = sigmoid(N(0, 1)) per (batch, head, token).
 * gated delta rule: as the delta rule, plus gate logits x ~ N(0, 1) per
   (batch, head, token, key channel); the decay is a = exp(-softplus(x)/16) and
-  the kernel receives its logarithm g = -softplus(x)/16.
+  the kernel receives its logarithm g = -softplus(x)/16.  With one decay per
+  token (Gated DeltaNet) the logits are drawn per (batch, head, token).
+* gated linear attention: q, k, v as the delta rule (no beta), plus one gate
+  logit per (batch, head, token) turned into g = -softplus(x)/16 as above.
 * decode: state S0 = 0.02 * N(0, 1) (float32), plus a ring of 16 one-token
   inputs drawn as for the delta rule; step i uses ring slot i mod 16.
 """
@@ -85,7 +88,8 @@ def make_la(B, H, T, dk, dv, dtype, seed, init_state=False):
 
 def make_delta(B, H, T, dk, dv, dtype, seed, gated=False, init_state=False,
                state_std=0.02):
-    """Delta-rule inputs per the recipe above.  g is the log-decay."""
+    """Delta-rule inputs per the recipe above.  g is the log-decay: per key
+    channel [B,H,T,dk] with gated=True, per token [B,H,T] with gated="token"."""
     gen = generator(seed)
     q = F.normalize(_normal(gen, (B, H, T, dk)), dim=-1) / math.sqrt(dk)
     k = F.normalize(_normal(gen, (B, H, T, dk)), dim=-1)
@@ -93,8 +97,23 @@ def make_delta(B, H, T, dk, dv, dtype, seed, gated=False, init_state=False,
     beta = torch.sigmoid(_normal(gen, (B, H, T)))
     out = dict(q=q.to(dtype), k=k.to(dtype), v=v.to(dtype), beta=beta.to(dtype))
     if gated:
-        x = _normal(gen, (B, H, T, dk))
+        x = _normal(gen, (B, H, T) if gated == "token" else (B, H, T, dk))
         out["g"] = (-F.softplus(x) / 16.0).to(dtype)
+    if init_state:
+        out["S0"] = state_std * _normal(gen, (B, H, dk, dv))
+    return out
+
+
+def make_gla(B, H, T, dk, dv, dtype, seed, init_state=False, state_std=0.5):
+    """Gated linear attention inputs: q, k, v as for the delta rule and the
+    per-token log-decay g [B,H,T] = -softplus(x)/16."""
+    gen = generator(seed)
+    q = F.normalize(_normal(gen, (B, H, T, dk)), dim=-1) / math.sqrt(dk)
+    k = F.normalize(_normal(gen, (B, H, T, dk)), dim=-1)
+    v = _normal(gen, (B, H, T, dv))
+    x = _normal(gen, (B, H, T))
+    out = dict(q=q.to(dtype), k=k.to(dtype), v=v.to(dtype),
+               g=(-F.softplus(x) / 16.0).to(dtype))
     if init_state:
         out["S0"] = state_std * _normal(gen, (B, H, dk, dv))
     return out
@@ -111,7 +130,7 @@ def make_decode(N, H, dk, dv, dtype, seed, gated=False, ring=DECODE_RING):
     beta = torch.sigmoid(_normal(gen, (ring, N, H)))
     out = dict(q=q.to(dtype), k=k.to(dtype), v=v.to(dtype), beta=beta.to(dtype))
     if gated:
-        x = _normal(gen, (ring, N, H, dk))
+        x = _normal(gen, (ring, N, H) if gated == "token" else (ring, N, H, dk))
         out["g"] = (-F.softplus(x) / 16.0).to(dtype)
     out["S0"] = 0.02 * _normal(gen, (N, H, dk, dv))
     return out
