@@ -441,6 +441,85 @@ def bench_rows(la, workloads, torch, launches=20):
     name, r = _row("deltanet_decode_step_gated", f"deltanet_decode_step (gated) N={N} H={H} "
                    f"dk=dv={dk}, fp32 state in place", us, med, per)
     rows[name] = r
+    del d, gi
+    rows.update(bench_token_gated_rows(la, workloads, torch, launches))
+    return rows
+
+
+def bench_token_gated_rows(la, workloads, torch, launches=20):
+    """The per-token gated entry points: the Gated DeltaNet prefill at the
+    delta-rule and gated workloads' shapes, gated linear attention at the
+    bf16 linear-attention workload's shape, and both decode steps at the
+    decode workload's shape."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    rows = {}
+    W = workloads.WORKLOADS
+    for w in (W[2], W[3]):
+        inp = workloads.make_delta(w.B, w.H, w.T, w.dk, w.dv, w.dtype, seed=90 + w.index,
+                                   gated="token")
+        d = {k: v.to(dev) for k, v in inp.items()}
+        d["o"] = torch.empty_like(d["v"])
+        d["S"] = torch.empty(w.B, w.H, w.dk, w.dv, device=dev, dtype=torch.float32)
+        del inp
+
+        def run(d):
+            la.gated_deltanet_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], S=d["S"],
+                                      o=d["o"], stream=stream)
+
+        us, med = _time_launches(torch, stream, run, [d], max(5, launches // 2), warmup=2)
+        per = w.B * w.H * (w.T * 2 * (2 * w.dk + 2 * w.dv + 2) + w.dk * w.dv * 4)
+        name, r = _row("gated_deltanet_prefill", f"gated_deltanet_prefill (one decay per token) "
+                       f"B={w.B} H={w.H} T={w.T} dk=dv={w.dk} bf16", us, med, per)
+        rows[f"{name}_T{w.T}"] = r
+        del d
+    w = W[1]
+    inp = workloads.make_gla(w.B, w.H, w.T, w.dk, w.dv, w.dtype, seed=92)
+    d = {k: v.to(dev) for k, v in inp.items()}
+    d["o"] = torch.empty_like(d["v"])
+    d["S"] = torch.empty(w.B, w.H, w.dk, w.dv, device=dev, dtype=torch.float32)
+
+    def run_gla(d):
+        la.gla_prefill(d["q"], d["k"], d["v"], d["g"], S=d["S"], o=d["o"], stream=stream)
+
+    us, med = _time_launches(torch, stream, run_gla, [d], launches)
+    per = w.B * w.H * (w.T * 2 * (2 * w.dk + 2 * w.dv + 1) + w.dk * w.dv * 4)
+    name, r = _row("gla_prefill", f"gla_prefill B={w.B} H={w.H} T={w.T} dk=dv={w.dk} bf16",
+                   us, med, per)
+    rows[name] = r
+    del d, inp
+    wd = W[4]
+    N, H, dk, dv = wd.B, wd.H, wd.dk, wd.dv
+    gi = workloads.make_decode(N, H, dk, dv, wd.dtype, seed=93, gated="token")
+    d = {k: v.to(dev) for k, v in gi.items()}
+    o = torch.empty(N, H, dv, device=dev, dtype=wd.dtype)
+    ring = d["q"].shape[0]
+    cnt = [0]
+
+    def run_gd(_):
+        s = cnt[0] % ring
+        cnt[0] += 1
+        la.gated_deltanet_decode_step(d["q"][s], d["k"][s], d["v"][s], d["beta"][s], d["g"][s],
+                                      d["S0"], o=o, stream=stream)
+
+    us, med = _time_launches(torch, stream, run_gd, [None], 200, warmup=10)
+    per = N * H * (2 * dk * dv * 4 + 2 * (2 * dk + 2 * dv + 2))
+    name, r = _row("gated_deltanet_decode_step", f"gated_deltanet_decode_step N={N} H={H} "
+                   f"dk=dv={dk}, fp32 state in place", us, med, per)
+    rows[name] = r
+    cnt[0] = 0
+
+    def run_gld(_):
+        s = cnt[0] % ring
+        cnt[0] += 1
+        la.gla_decode_step(d["q"][s], d["k"][s], d["v"][s], d["S0"], g=d["g"][s], o=o,
+                           stream=stream)
+
+    us, med = _time_launches(torch, stream, run_gld, [None], 200, warmup=10)
+    per = N * H * (2 * dk * dv * 4 + 2 * (2 * dk + 2 * dv + 1))
+    name, r = _row("gla_decode_step", f"gla_decode_step N={N} H={H} dk=dv={dk}, fp32 state "
+                   "in place", us, med, per)
+    rows[name] = r
     return rows
 
 
@@ -565,7 +644,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the other rows (LA prefill, gated prefill, LA/gated decode)")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy", "rows"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy", "rows", "token-rows"],
+                    default="all",
                     help="run one part only (for profiler runs)")
     ap.add_argument("--summarize", metavar="DIR",
                     help="write profiles/*.txt from rocprofv3 output under DIR and exit")
@@ -595,6 +675,9 @@ def main():
         return
     if args.only == "rows":
         print(json.dumps(bench_rows(la, workloads, torch)))
+        return
+    if args.only == "token-rows":
+        print(json.dumps(bench_token_gated_rows(la, workloads, torch)))
         return
     if args.only == "decode":
         wd, _, el = bench_decode(la, workloads, torch, args.decode_steps)

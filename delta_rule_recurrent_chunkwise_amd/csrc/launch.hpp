@@ -46,6 +46,8 @@ hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, hipS
 // gated_pipe_workspace_bytes(a) bytes).
 size_t gated_pipe_workspace_bytes(const PrefillArgs& a);
 hipError_t launch_prefill_pipe(const PrefillArgs& a, void* workspace, hipStream_t st);
+// ... and with one decay per token (a.g [B,H,T]; no workspace).
+hipError_t launch_prefill_pipe_token(const PrefillArgs& a, hipStream_t st);
 
 // Chunk-parallel linear attention (bf16): every chunk's phi(K)^T V and
 // colsum phi(K) into a workspace of la_par_workspace_bytes bytes, then their

@@ -620,6 +620,7 @@ hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, hipS
   }
   if (bf16 && dk == 128 && a.dv % 32 == 0) {
     if (mode == PF_DELTA) return launch_prefill_pipe(a, nullptr, st);
+    if (mode == PF_SGATED) return launch_prefill_pipe_token(a, st);
     if (mode == PF_GATED) {
       // the gate pre-pass writes Gam Q, Gam K, K / Gam and Gam_C to a
       // stream-ordered workspace that is released after the main kernel

@@ -17,6 +17,13 @@
 //    below) forms K~, K^, Q~ and Gam_C for every chunk; the main kernel is
 //    the plain one with K~ in place of K on the left of every product, K^ on
 //    the right, and the row scaling by Gam_C.
+//  * one decay per token (Gated DeltaNet): the same identity with scalar
+//    Gam_t = exp(G_t), G_t the log-decay summed from the chunk start, is
+//    applied to the products' entries instead of the operands: entry (r, c)
+//    of tril(Q K^T) and of L is scaled by exp(G_r - G_c), the rows of Q S and
+//    K S by exp(G_r), the state by exp(G_C) and the rows of u by
+//    exp(G_C - G_r) before S += K^T u.  No factor exceeds 1, there is no
+//    pre-pass, and the kernel is otherwise the plain one.
 //
 // (I + L)^-1 is never formed: with I + L cut into 16x16 token blocks, u is
 // obtained by block forward substitution,
@@ -71,8 +78,12 @@ typedef short shortx4_t __attribute__((ext_vector_type(4)));
 
 // DVS: value columns per workgroup (32, or 16 when there are too few
 // (batch, head) pairs to fill the GPU with 32-column slices).
-template <bool GATED, int DVS>
+// GM: 0 plain, 1 decay per key channel (operands from the pre-pass), 2 one
+// decay per token.
+template <int GM, int DVS>
 struct __attribute__((aligned(16))) Smem2 {
+  static constexpr bool GATED = GM == 1;
+  static constexpr bool TOKG = GM == 2;
   static constexpr int kLV = DVS + 16;  // bf16 row stride of the v slice
   static constexpr int kLO = DVS + 8;   // bf16 row stride of the output tile
   static constexpr int NKH = GATED ? 2 : 1;
@@ -91,6 +102,8 @@ struct __attribute__((aligned(16))) Smem2 {
   float l[4 * kLB];           // diagonal blocks of L (strictly lower parts)
   float beta[2][kC];
   float gc[NKH][kDK];         // gated: Gam_C per key channel
+  // per-token decay of chunk c in buffer c & 1: G_t, exp(G_t), exp(G_63 - G_t)
+  float gs[TOKG ? 2 : 1][3][TOKG ? kC : 1];
 };
 
 // 32b + 16h + 4g + i  ->  32b + 8g + 4h + i
@@ -129,6 +142,7 @@ struct PipeArgs {
   const bf16_t* k;     // K, or Gam K
   const bf16_t* kh;    // gated: K / Gam
   const float* gc;     // gated: Gam_C, [B*H][ceil(T/64)][dk]
+  const bf16_t* g;     // per-token gate: log-decay [B*H][T]
   const bf16_t* v;
   const bf16_t* beta;
   bf16_t* o;
@@ -167,9 +181,11 @@ struct LoadPlan {
   }
 };
 
-template <bool GATED, int DVS>
+template <int GM, int DVS>
 __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
-  typedef Smem2<GATED, DVS> Sm;
+  constexpr bool GATED = GM == 1;  // per key channel, operands from the pre-pass
+  constexpr bool TOKG = GM == 2;   // one decay per token
+  typedef Smem2<GM, DVS> Sm;
   constexpr int kDVS = DVS;
   constexpr int NCW = DVS / 16;        // chain waves
   constexpr int VPRV = DVS / 8;        // 16-byte vectors per row of the v slice
@@ -203,6 +219,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
   const float* gch = GATED ? a.gc + (size_t)bh * nch * kDK : nullptr;
   const bf16_t* vh = a.v + (size_t)bh * Tn * dv + sl * kDVS;
   const bf16_t* bth = a.beta + (size_t)bh * Tn;
+  const bf16_t* gth = TOKG ? a.g + (size_t)bh * Tn : nullptr;
   bf16_t* oh = a.o + (size_t)bh * Tn * dv + sl * kDVS;
   float* Sh = a.S + (size_t)bh * kDK * dv + sl * kDVS;
 
@@ -215,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
   // load kind of a role, fixed at compile time: 0 none, 1 tiles (q, k, k^),
   // 2 wave 7's v slice, beta and Gam_C
   constexpr int NSMALL = NVL + (GATED ? 1 : 0);
-  auto issue_loads = [&](auto kindc, int chunk, auto& dst, uint32_t& bdst) {
+  auto issue_loads = [&](auto kindc, int chunk, auto& dst, uint32_t* bdst) {
     constexpr int KIND = decltype(kindc)::value;
     if constexpr (KIND == 1) {
       const bf16_t* const pq = qh;  // register copies: a select among captured
@@ -237,10 +254,12 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
         dst[j] = *reinterpret_cast<const u32x4*>(vh + (size_t)row * dv + (vv % VPRV) * 8);
       }
       if constexpr (GATED) dst[NVL] = *reinterpret_cast<const u32x4*>(gch + (size_t)chunk * kDK + 4 * (lane & 31));
-      bdst = bth[min(chunk * kC + lane, tlast)];  // converted when stored
+      const int row = min(chunk * kC + lane, tlast);
+      bdst[0] = bth[row];  // converted when stored
+      if constexpr (TOKG) bdst[1] = gth[row];
     }
   };
-  auto store_loads = [&](auto kindc, int chunk, int buf, int kbi, const auto& src, uint32_t bsrc) {
+  auto store_loads = [&](auto kindc, int chunk, int buf, int kbi, const auto& src, const uint32_t* bsrc) {
     constexpr int KIND = decltype(kindc)::value;
     if constexpr (KIND == 1) {
 #pragma unroll
@@ -259,7 +278,22 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
       if constexpr (GATED) {
         if (lane < 32) *reinterpret_cast<u32x4*>(&sm.gc[GATED ? buf : 0][4 * lane]) = src[NVL];
       }
-      sm.beta[buf][lane] = chunk * kC + lane <= tlast ? bf2f((bf16_t)bsrc) : 0.f;
+      const bool in = chunk * kC + lane <= tlast;
+      sm.beta[buf][lane] = in ? bf2f((bf16_t)bsrc[0]) : 0.f;
+      if constexpr (TOKG) {
+        // G_t = sum_{s<=t} g_s over the chunk (lane = token), then the
+        // factors exp(G_t) and exp(G_63 - G_t), both at most 1
+        float x = in ? bf2f((bf16_t)bsrc[1]) : 0.f;
+#pragma unroll
+        for (int off = 1; off < kC; off <<= 1) {
+          const float y = __shfl_up(x, off, kC);
+          if (lane >= off) x += y;
+        }
+        const float gC = __shfl(x, kC - 1, kC);
+        sm.gs[TOKG ? buf : 0][0][lane] = x;
+        sm.gs[TOKG ? buf : 0][1][lane] = __expf(x);
+        sm.gs[TOKG ? buf : 0][2][lane] = __expf(gC - x);
+      }
     }
   };
 
@@ -282,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
     constexpr int NREG = KIND == 1 ? LP::NT : (KIND == 2 ? NSMALL : 1);
     static_assert(LEAD == 1 || NSL == 2, "a two-chunk lead needs two register slots");
     u32x4 pf[NSL][NREG];
-    uint32_t pfb[NSL] = {};
+    uint32_t pfb[NSL][2] = {};  // beta and (per-token gate) g of each slot
     if (loader) {
       issue_loads(kindc, 0, pf[0], pfb[0]);
       if constexpr (LEAD == 2) {
@@ -374,6 +408,11 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
             const shortx4_t vw =
                 ld_tr(&sm.v[P][16 * mt + 4 * lg + ((lane >> 2) & 3)][16 * wave + 4 * (lane & 3)]);
             const float4 bt = *reinterpret_cast<const float4*>(&sm.beta[P][16 * mt + 4 * lg]);
+            if constexpr (TOKG) {  // rows of K S and Q S decay by exp(G_r)
+              const float4 dc = *reinterpret_cast<const float4*>(&sm.gs[TOKG ? P : 0][1][16 * mt + 4 * lg]);
+              y[mt][0] *= dc.x; y[mt][1] *= dc.y; y[mt][2] *= dc.z; y[mt][3] *= dc.w;
+              ox[mt][0] *= dc.x; ox[mt][1] *= dc.y; ox[mt][2] *= dc.z; ox[mt][3] *= dc.w;
+            }
             xx[mt][0] = bt.x * (bf2f((bf16_t)vw[0]) - y[mt][0]);
             xx[mt][1] = bt.y * (bf2f((bf16_t)vw[1]) - y[mt][1]);
             xx[mt][2] = bt.z * (bf2f((bf16_t)vw[2]) - y[mt][2]);
@@ -398,6 +437,11 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
           fa[3] = ld_frag(&sm.a[32 + lc][32 + 8 * lg]);
           fa[4] = ld_frag(&sm.a[48 + lc][8 * lg]);
           fa[5] = ld_frag(&sm.a[48 + lc][32 + 8 * lg]);
+          if constexpr (TOKG) {  // S <- exp(G_C) S before K^T u is added
+            const float eC = sm.gs[TOKG ? P : 0][1][kC - 1];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) st[t] *= eC;
+          }
           // blocks L_bj stored in the order (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
           floatx4 ut[4];
           ut[0] = mfma_k16(fd[0], acc_to_b16(xx[0]), zero4());
@@ -430,11 +474,23 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
           ox[3] = mfma_k32(fa[5], u23, mfma_k32(fa[4], u01, ox[3]));
 #pragma unroll
           for (int t = 0; t < 8; ++t) fkt[1][t] = kt_frag(t, 32);
-          // S += K^T u
+          // S += K^T u (per-token gate: rows of u decay by exp(G_C - G_r))
+          bf16x8 s01 = u01, s23 = u23;
+          if constexpr (TOKG) {
+            floatx4 us[4];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) st[t] = mfma_k32(fkt[0][t], u01, st[t]);
+            for (int mt = 0; mt < 4; ++mt) {
+              const float4 rm = *reinterpret_cast<const float4*>(&sm.gs[TOKG ? P : 0][2][16 * mt + 4 * lg]);
+              us[mt][0] = ut[mt][0] * rm.x; us[mt][1] = ut[mt][1] * rm.y;
+              us[mt][2] = ut[mt][2] * rm.z; us[mt][3] = ut[mt][3] * rm.w;
+            }
+            s01 = acc_pair_to_b(us[0], us[1]);
+            s23 = acc_pair_to_b(us[2], us[3]);
+          }
 #pragma unroll
-          for (int t = 0; t < 8; ++t) st[t] = mfma_k32(fkt[1][t], u23, st[t]);
+          for (int t = 0; t < 8; ++t) st[t] = mfma_k32(fkt[0][t], s01, st[t]);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) st[t] = mfma_k32(fkt[1][t], s23, st[t]);
           if constexpr (GATED) {
             // S <- diag(Gam_C) S; accumulator rows 16t + 4lg + i are the
             // consecutive channels perm32(16t + 4lg) + i
@@ -533,6 +589,14 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
 #pragma unroll
               for (int j = 0; j <= i; ++j) {
                 const int r = 16 * i + lc, c0 = 16 * j + 4 * lg;
+                if constexpr (TOKG) {  // decay from token c to token r (c <= r)
+                  const float gr = sm.gs[TOKG ? P : 0][0][r];
+                  const float4 gcl = *reinterpret_cast<const float4*>(&sm.gs[TOKG ? P : 0][0][c0]);
+                  acc[j][0] *= c0 <= r ? __expf(gr - gcl.x) : 0.f;
+                  acc[j][1] *= c0 + 1 <= r ? __expf(gr - gcl.y) : 0.f;
+                  acc[j][2] *= c0 + 2 <= r ? __expf(gr - gcl.z) : 0.f;
+                  acc[j][3] *= c0 + 3 <= r ? __expf(gr - gcl.w) : 0.f;
+                }
                 const float e0 = c0 <= r ? acc[j][0] : 0.f, e1 = c0 + 1 <= r ? acc[j][1] : 0.f;
                 const float e2 = c0 + 2 <= r ? acc[j][2] : 0.f, e3 = c0 + 3 <= r ? acc[j][3] : 0.f;
                 *reinterpret_cast<uint2*>(&sm.a[r][perm32(c0)]) = make_uint2(pack2(e0, e1), pack2(e2, e3));
@@ -568,6 +632,25 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
               // fp32 for the D wave; off-diagonal tiles bf16, transposed (the
               // lane writes row lc, columns 4lg .. 4lg+3 of L_ij^T)
               const float4 bt = *reinterpret_cast<const float4*>(&sm.beta[nb][16 * i + 4 * lg]);
+              if constexpr (TOKG) {  // decay from token c to token r
+                const float4 grw = *reinterpret_cast<const float4*>(&sm.gs[TOKG ? nb : 0][0][16 * i + 4 * lg]);
+#pragma unroll
+                for (int j = 0; j < i; ++j) {  // rows 16i + 4lg + n, column 16j + lc
+                  const float gcl = sm.gs[TOKG ? nb : 0][0][16 * j + lc];
+                  acc[j][0] *= __expf(grw.x - gcl);
+                  acc[j][1] *= __expf(grw.y - gcl);
+                  acc[j][2] *= __expf(grw.z - gcl);
+                  acc[j][3] *= __expf(grw.w - gcl);
+                }
+                // diagonal block: row 16i + lc, columns 16i + 4lg + n; only
+                // the strictly lower entries are read
+                const float gr = sm.gs[TOKG ? nb : 0][0][16 * i + lc];
+                const float4 gcd = *reinterpret_cast<const float4*>(&sm.gs[TOKG ? nb : 0][0][16 * i + 4 * lg]);
+                acc[i][0] *= 4 * lg < lc ? __expf(gr - gcd.x) : 0.f;
+                acc[i][1] *= 4 * lg + 1 < lc ? __expf(gr - gcd.y) : 0.f;
+                acc[i][2] *= 4 * lg + 2 < lc ? __expf(gr - gcd.z) : 0.f;
+                acc[i][3] *= 4 * lg + 3 < lc ? __expf(gr - gcd.w) : 0.f;
+              }
 #pragma unroll
               for (int j = 0; j < i; ++j) {
                 uint2 wv;
@@ -698,7 +781,7 @@ size_t gated_pipe_workspace_bytes(const PrefillArgs& a) {
 
 namespace {
 
-template <bool GATED>
+template <int GM>
 hipError_t launch_pipe_t(const PipeArgs& p, long bh, int dv, hipStream_t st) {
   // 32 value columns per workgroup, or 16 when 32-column slices would leave
   // compute units idle (few (batch, head) pairs, as with long sequences)
@@ -707,9 +790,9 @@ hipError_t launch_pipe_t(const PipeArgs& p, long bh, int dv, hipStream_t st) {
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
   if (bh * (dv / 32) < cus && dv % 16 == 0) {
-    hipLaunchKernelGGL((prefill_pipe<GATED, 16>), dim3((unsigned)(bh * (dv / 16))), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((prefill_pipe<GM, 16>), dim3((unsigned)(bh * (dv / 16))), dim3(kThreads), 0, st, p);
   } else {
-    hipLaunchKernelGGL((prefill_pipe<GATED, 32>), dim3((unsigned)(bh * (dv / 32))), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((prefill_pipe<GM, 32>), dim3((unsigned)(bh * (dv / 32))), dim3(kThreads), 0, st, p);
   }
   return hipGetLastError();
 }
@@ -718,7 +801,7 @@ hipError_t launch_pipe_t(const PipeArgs& p, long bh, int dv, hipStream_t st) {
 
 hipError_t launch_prefill_pipe(const PrefillArgs& a, void* workspace, hipStream_t st) {
   const long bh = (long)a.B * a.H;
-  PipeArgs p;
+  PipeArgs p{};
   p.v = reinterpret_cast<const bf16_t*>(a.v);
   p.beta = reinterpret_cast<const bf16_t*>(a.beta);
   p.o = reinterpret_cast<bf16_t*>(a.o);
@@ -732,7 +815,7 @@ hipError_t launch_prefill_pipe(const PrefillArgs& a, void* workspace, hipStream_
     p.k = reinterpret_cast<const bf16_t*>(a.k);
     p.kh = nullptr;
     p.gc = nullptr;
-    return launch_pipe_t<false>(p, bh, a.dv, st);
+    return launch_pipe_t<0>(p, bh, a.dv, st);
   }
   const int nch = (a.T + kC - 1) / kC;
   const size_t n = (size_t)a.B * a.H * nch * kC * kDK;
@@ -750,7 +833,23 @@ hipError_t launch_prefill_pipe(const PrefillArgs& a, void* workspace, hipStream_
   p.kh = kht;
   p.gc = gcum;
   p.Tq = nch * kC;
-  return launch_pipe_t<true>(p, bh, a.dv, st);
+  return launch_pipe_t<1>(p, bh, a.dv, st);
+}
+
+hipError_t launch_prefill_pipe_token(const PrefillArgs& a, hipStream_t st) {
+  PipeArgs p{};
+  p.q = reinterpret_cast<const bf16_t*>(a.q);
+  p.k = reinterpret_cast<const bf16_t*>(a.k);
+  p.g = reinterpret_cast<const bf16_t*>(a.g);
+  p.v = reinterpret_cast<const bf16_t*>(a.v);
+  p.beta = reinterpret_cast<const bf16_t*>(a.beta);
+  p.o = reinterpret_cast<bf16_t*>(a.o);
+  p.S = a.S;
+  p.T = a.T;
+  p.dv = a.dv;
+  p.use_init = a.use_init;
+  p.Tq = a.T;
+  return launch_pipe_t<2>(p, (long)a.B * a.H, a.dv, st);
 }
 
 }  // namespace linattn
