@@ -10,6 +10,14 @@
 // output products read it in) and z_c (fp32, in place) and writes the final
 // state; the chunk outputs are then independent.
 //
+// Gated linear attention (section "Gated Delta Net", the additive cache with
+// a forgetting factor; q and k as given, no normaliser) has the same
+// structure with a decay per token: with G_t the log-decay summed from the
+// chunk start and Gam_C = exp(G_63),
+//   dS_c = (K * exp(G_63 - G_t))^T V,   S_{c+1} = Gam_C S_c + dS_c,
+//   O = diag(exp(G_t)) Q S_c + (tril(Q K^T) * exp(G_r - G_c)) V,
+// every factor at most 1.  The kernels take it as the template flag GLA.
+//
 // Chunks are numbered over (batch, head, chunk) with nch = ceil(T / 64)
 // chunks per head; inputs have T rows per head.  A partial last chunk is
 // staged with zero rows past the end (phi(k) = 0 there: no contribution to
@@ -25,6 +33,18 @@ typedef short shortx4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+// Wave 0 of a chunk's workgroup: G_t = sum_{s<=t} g_s over the chunk (lane =
+// token; tokens past the end and a missing gate count as 0).
+__device__ __forceinline__ float chunk_log_decay(const bf16_t* gc, int lane, int nrow) {
+  float x = (gc && lane < nrow) ? bf2f(gc[min(lane, nrow - 1)]) : 0.f;
+#pragma unroll
+  for (int off = 1; off < kC; off <<= 1) {
+    const float y = __shfl_up(x, off, kC);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
 
 __device__ __forceinline__ shortx4_t ld_tr(const bf16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -44,28 +64,43 @@ __device__ __forceinline__ bf16x8 cat_tr(shortx4_t lo, shortx4_t hi) {
 // addressed by lanes 16G + a + 4e), so that the k-index of element (g, e) is
 // token 4g + e (e < 4) or 16 + 4g + e - 4.  The column sums are the same
 // product with V replaced by ones.
-template <int DK, int DV>
+// GLA: K rows are scaled by exp(G_63 - G_t) instead of phi, there is no
+// column sum, and dz[chunk] receives Gam_C = exp(G_63) instead.
+template <int DK, int DV, bool GLA>
 __global__ __launch_bounds__(256) void la_chunk_state(const bf16_t* __restrict__ k,
                                                       const bf16_t* __restrict__ v,
+                                                      const bf16_t* __restrict__ g,
                                                       float* __restrict__ dS, float* __restrict__ dz, int T,
                                                       int nch) {
   constexpr int LK = DK + 16, LV = DV + 16;  // row strides (bf16)
   __shared__ __attribute__((aligned(16))) bf16_t sk[kC][LK];
   __shared__ __attribute__((aligned(16))) bf16_t sv[kC][LV];
+  __shared__ float sw[GLA ? kC : 1];
   const size_t chunk = blockIdx.x;
   const int bh = (int)(chunk / nch), t0 = (int)(chunk - (size_t)bh * nch) * kC;
   const int nrow = min(kC, T - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bf16_t* kc = k + ((size_t)bh * T + t0) * DK;
   const bf16_t* vc = v + ((size_t)bh * T + t0) * DV;
+  if constexpr (GLA) {
+    if (wave == 0) {
+      const float G = chunk_log_decay(g ? g + (size_t)bh * T + t0 : nullptr, lane, nrow);
+      const float gC = __shfl(G, kC - 1, kC);
+      sw[lane] = __expf(gC - G);
+      if (lane == 0) dz[chunk] = __expf(gC);
+    }
+    __syncthreads();
+  }
   for (int i = tid; i < kC * DK / 8; i += 256) {
     const int r = i / (DK / 8), c8 = (i % (DK / 8)) * 8;
     // rows past the end re-read the last row and are zeroed after phi
     u32x4 w = *reinterpret_cast<const u32x4*>(kc + (size_t)min(r, nrow - 1) * DK + c8);
+    const float wr = GLA ? sw[GLA ? r : 0] : 1.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float lo = phi_elu1(bf2f((bf16_t)(w[e] & 0xffffu)));
-      const float hi = phi_elu1(bf2f((bf16_t)(w[e] >> 16)));
+      const float x0 = bf2f((bf16_t)(w[e] & 0xffffu)), x1 = bf2f((bf16_t)(w[e] >> 16));
+      const float lo = GLA ? x0 * wr : phi_elu1(x0);
+      const float hi = GLA ? x1 * wr : phi_elu1(x1);
       w[e] = r < nrow ? pack2(lo, hi) : 0u;
     }
     *reinterpret_cast<u32x4*>(&sk[r][c8]) = w;
@@ -76,7 +111,7 @@ __global__ __launch_bounds__(256) void la_chunk_state(const bf16_t* __restrict__
     *reinterpret_cast<u32x4*>(&sv[r][c8]) = r < nrow ? x : u32x4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
-  constexpr int NDT = DK / 16, NJT = DV / 16 + 1;  // the extra column tile gives dz
+  constexpr int NDT = DK / 16, NJT = DV / 16 + (GLA ? 0 : 1);  // the extra column tile gives dz
   const int trow = 4 * (lane >> 4) + ((lane >> 2) & 3);
   const int tcol = 4 * (lane & 3);
   const int lc = lane & 15, lg = lane >> 4;
@@ -92,13 +127,13 @@ __global__ __launch_bounds__(256) void la_chunk_state(const bf16_t* __restrict__
     for (int kb = 0; kb < 2; ++kb) {
       const int t0 = 32 * kb;
       const bf16x8 a = cat_tr(ld_tr(&sk[t0 + trow][16 * dt + tcol]), ld_tr(&sk[t0 + 16 + trow][16 * dt + tcol]));
-      const bf16x8 b = jt < NJT - 1
+      const bf16x8 b = (GLA || jt < NJT - 1)
                            ? cat_tr(ld_tr(&sv[t0 + trow][16 * jt + tcol]), ld_tr(&sv[t0 + 16 + trow][16 * jt + tcol]))
                            : ones;
       acc = mfma_k32(a, b, acc);
     }
     // lane (lc, lg) holds rows 16dt + 4lg + i, column 16jt + lc
-    if (jt < NJT - 1) {
+    if (GLA || jt < NJT - 1) {
       float* out = dS + chunk * DK * DV;
 #pragma unroll
       for (int i = 0; i < 4; ++i) out[(size_t)(16 * dt + 4 * lg + i) * DV + 16 * jt + lc] = acc[i];
@@ -114,12 +149,16 @@ __global__ __launch_bounds__(256) void la_chunk_state(const bf16_t* __restrict__
 // Thread e of a (batch, head) owns element e of [S (dk*dv), z (dk)].  The
 // prefix of S goes to Sb in bf16 (rounded to nearest even); that of z
 // replaces dz in place.
+// GLA: S only (dk = 0 here), and each step first decays the running state
+// by the chunk's Gam_C, held in dz[chunk]: S_{c+1} = Gam_C S_c + dS_c.
+template <bool GLA>
 __global__ __launch_bounds__(256) void la_state_scan(const float* __restrict__ dS, float* __restrict__ dz,
                                                      bf16_t* __restrict__ Sb, float* S, float* z, int nch,
                                                      int dkdv, int dk, int use_init) {
   const long bh = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= dkdv + dk) return;
+  const float* gam = GLA ? dz + (size_t)bh * nch : nullptr;
   const bool isz = e >= dkdv;
   const int idx = isz ? e - dkdv : e;
   const int stride = isz ? dk : dkdv;
@@ -140,13 +179,13 @@ __global__ __launch_bounds__(256) void la_state_scan(const float* __restrict__ d
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       put(c + i, run);
-      run += t[i];
+      run = GLA ? run * gam[c + i] + t[i] : run + t[i];
     }
   }
   for (; c < nch; ++c) {
     const float t = base[(size_t)c * stride];
     put(c, run);
-    run += t;
+    run = GLA ? run * gam[c] + t : run + t;
   }
   *fin = run;
 }
@@ -158,9 +197,12 @@ __global__ __launch_bounds__(256) void la_state_scan(const float* __restrict__ d
 // masked score block) are 16-byte LDS reads in natural k order; B operands
 // over tokens or key channels (V, S_c) are LDS transpose reads addressing
 // rows 8G + e and 8G + 4 + e, which gives the same natural order.
-template <int DK, int DV>
+// GLA: q and k as given, no denominator; scores scaled by exp(G_r - G_c)
+// and the rows of phi(Q) S_c -> Q S_c by exp(G_r).
+template <int DK, int DV, bool GLA>
 __global__ __launch_bounds__(256) void la_chunk_out(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                                                    const bf16_t* __restrict__ v, const bf16_t* __restrict__ Sc,
+                                                    const bf16_t* __restrict__ v, const bf16_t* __restrict__ g,
+                                                    const bf16_t* __restrict__ Sc,
                                                     const float* __restrict__ zc, bf16_t* __restrict__ o, int T,
                                                     int nch) {
   constexpr int LQ = DK + 16, LV = DV + 16, LA = kC + 16;
@@ -171,6 +213,7 @@ __global__ __launch_bounds__(256) void la_chunk_out(const bf16_t* __restrict__ q
   __shared__ __attribute__((aligned(16))) bf16_t sa[kC][LA];   // masked scores, bf16
   __shared__ float sz[DK];
   __shared__ float sden[kC];
+  __shared__ float sg[GLA ? kC : 1];
   const size_t chunk = blockIdx.x;
   const int bh = (int)(chunk / nch), t0 = (int)(chunk - (size_t)bh * nch) * kC;
   const int nrow = min(kC, T - t0);
@@ -185,9 +228,12 @@ __global__ __launch_bounds__(256) void la_chunk_out(const bf16_t* __restrict__ q
     const int r = ii / (DK / 8), c8 = (ii % (DK / 8)) * 8;
     // rows past the end re-read the last row; phi(q) = phi(k) = 0 there
     u32x4 w = *reinterpret_cast<const u32x4*>((isq ? qc : kc) + (size_t)min(r, nrow - 1) * DK + c8);
+    if constexpr (!GLA) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = r < nrow ? pack2(phi_elu1(bf2f((bf16_t)(w[e] & 0xffffu))), phi_elu1(bf2f((bf16_t)(w[e] >> 16)))) : 0u;
+      for (int e = 0; e < 4; ++e)
+        w[e] = pack2(phi_elu1(bf2f((bf16_t)(w[e] & 0xffffu))), phi_elu1(bf2f((bf16_t)(w[e] >> 16))));
+    }
+    if (r >= nrow) w = u32x4{0u, 0u, 0u, 0u};
     *reinterpret_cast<u32x4*>(isq ? &sq[r][c8] : &sk[r][c8]) = w;
   }
   for (int i = tid; i < kC * DV / 8; i += 256) {
@@ -200,7 +246,11 @@ __global__ __launch_bounds__(256) void la_chunk_out(const bf16_t* __restrict__ q
     const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
     *reinterpret_cast<u32x4*>(&ss[r][c8]) = *reinterpret_cast<const u32x4*>(sc + (size_t)r * DV + c8);
   }
-  for (int i = tid; i < DK; i += 256) sz[i] = zc[chunk * DK + i];
+  if constexpr (GLA) {
+    if (wave == 0) sg[lane] = chunk_log_decay(g ? g + (size_t)bh * T + t0 : nullptr, lane, nrow);
+  } else {
+    for (int i = tid; i < DK; i += 256) sz[i] = zc[chunk * DK + i];
+  }
   __syncthreads();
 
   const int mt = wave;  // token row block
@@ -222,7 +272,9 @@ __global__ __launch_bounds__(256) void la_chunk_out(const bf16_t* __restrict__ q
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * mt + 4 * lg + i, cc = 16 * j + lc;
-      const float x = cc <= r ? acc[i] : 0.f;
+      float x = acc[i];
+      if constexpr (GLA) x *= cc <= r ? __expf(sg[GLA ? r : 0] - sg[GLA ? cc : 0]) : 0.f;
+      x = cc <= r ? x : 0.f;
       sa[r][cc] = f2bf(x);
       rs[i] += x;
     }
@@ -233,7 +285,7 @@ __global__ __launch_bounds__(256) void la_chunk_out(const bf16_t* __restrict__ q
   // denominators: phi(q_r).z_c (lane lc takes channels lc, lc + 16, ...)
   // plus the row sum, summed over the 16 lanes of a lane group
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < (GLA ? 0 : 4); ++i) {
     const int r = 16 * mt + 4 * lg + i;
     float x = rs[i];
 #pragma unroll
@@ -272,90 +324,104 @@ __global__ __launch_bounds__(256) void la_chunk_out(const bf16_t* __restrict__ q
       const bf16x8 b = cat_tr(ld_tr(&sv[32 * kb + trow][16 * jt + tcol]), ld_tr(&sv[32 * kb + 4 + trow][16 * jt + tcol]));
       acc = mfma_k32(*reinterpret_cast<const bf16x8*>(&sa[16 * mt + lc][32 * kb + 8 * lg]), b, acc);
     }
-    acc += aqs;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * mt + 4 * lg + i;
-      if (r < nrow) oc[(size_t)r * DV + 16 * jt + lc] = f2bf(acc[i] / sden[r]);
+      const float val = GLA ? acc[i] + aqs[i] * __expf(sg[GLA ? r : 0]) : (acc[i] + aqs[i]) / sden[r];
+      if (r < nrow) oc[(size_t)r * DV + 16 * jt + lc] = f2bf(val);
     }
   }
 }
 
-template <int DK>
-hipError_t launch_state_dk(int dv, const bf16_t* k, const bf16_t* v, float* dS, float* dz, long nchunks,
-                           int T, int nch, hipStream_t st) {
+template <int DK, bool GLA>
+hipError_t launch_state_dk(int dv, const PrefillArgs& a, float* dS, float* dz, long nchunks, int nch,
+                           hipStream_t st) {
+  const bf16_t* k = reinterpret_cast<const bf16_t*>(a.k);
+  const bf16_t* v = reinterpret_cast<const bf16_t*>(a.v);
+  const bf16_t* g = reinterpret_cast<const bf16_t*>(a.g);
+  const dim3 grid((unsigned)nchunks), block(256);
   switch (dv) {
-    case 16: hipLaunchKernelGGL((la_chunk_state<DK, 16>), dim3((unsigned)nchunks), dim3(256), 0, st, k, v, dS, dz, T, nch); break;
-    case 32: hipLaunchKernelGGL((la_chunk_state<DK, 32>), dim3((unsigned)nchunks), dim3(256), 0, st, k, v, dS, dz, T, nch); break;
-    case 64: hipLaunchKernelGGL((la_chunk_state<DK, 64>), dim3((unsigned)nchunks), dim3(256), 0, st, k, v, dS, dz, T, nch); break;
-    case 128: hipLaunchKernelGGL((la_chunk_state<DK, 128>), dim3((unsigned)nchunks), dim3(256), 0, st, k, v, dS, dz, T, nch); break;
+    case 16: hipLaunchKernelGGL((la_chunk_state<DK, 16, GLA>), grid, block, 0, st, k, v, g, dS, dz, a.T, nch); break;
+    case 32: hipLaunchKernelGGL((la_chunk_state<DK, 32, GLA>), grid, block, 0, st, k, v, g, dS, dz, a.T, nch); break;
+    case 64: hipLaunchKernelGGL((la_chunk_state<DK, 64, GLA>), grid, block, 0, st, k, v, g, dS, dz, a.T, nch); break;
+    case 128: hipLaunchKernelGGL((la_chunk_state<DK, 128, GLA>), grid, block, 0, st, k, v, g, dS, dz, a.T, nch); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-
-template <int DK>
+template <int DK, bool GLA>
 hipError_t launch_out_dk(int dv, const PrefillArgs& a, const bf16_t* Sc, const float* zc, long nchunks, int nch,
                          hipStream_t st) {
   const bf16_t* q = reinterpret_cast<const bf16_t*>(a.q);
   const bf16_t* k = reinterpret_cast<const bf16_t*>(a.k);
   const bf16_t* v = reinterpret_cast<const bf16_t*>(a.v);
+  const bf16_t* g = reinterpret_cast<const bf16_t*>(a.g);
   bf16_t* o = reinterpret_cast<bf16_t*>(a.o);
+  const dim3 grid((unsigned)nchunks), block(256);
   switch (dv) {
-    case 16: hipLaunchKernelGGL((la_chunk_out<DK, 16>), dim3((unsigned)nchunks), dim3(256), 0, st, q, k, v, Sc, zc, o, a.T, nch); break;
-    case 32: hipLaunchKernelGGL((la_chunk_out<DK, 32>), dim3((unsigned)nchunks), dim3(256), 0, st, q, k, v, Sc, zc, o, a.T, nch); break;
-    case 64: hipLaunchKernelGGL((la_chunk_out<DK, 64>), dim3((unsigned)nchunks), dim3(256), 0, st, q, k, v, Sc, zc, o, a.T, nch); break;
-    case 128: hipLaunchKernelGGL((la_chunk_out<DK, 128>), dim3((unsigned)nchunks), dim3(256), 0, st, q, k, v, Sc, zc, o, a.T, nch); break;
+    case 16: hipLaunchKernelGGL((la_chunk_out<DK, 16, GLA>), grid, block, 0, st, q, k, v, g, Sc, zc, o, a.T, nch); break;
+    case 32: hipLaunchKernelGGL((la_chunk_out<DK, 32, GLA>), grid, block, 0, st, q, k, v, g, Sc, zc, o, a.T, nch); break;
+    case 64: hipLaunchKernelGGL((la_chunk_out<DK, 64, GLA>), grid, block, 0, st, q, k, v, g, Sc, zc, o, a.T, nch); break;
+    case 128: hipLaunchKernelGGL((la_chunk_out<DK, 128, GLA>), grid, block, 0, st, q, k, v, g, Sc, zc, o, a.T, nch); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_la_par_outputs(int dk, const PrefillArgs& a, void* workspace, hipStream_t st) {
+template <bool GLA>
+hipError_t launch_outputs(int dk, const PrefillArgs& a, void* workspace, hipStream_t st) {
   const int nch = (a.T + kC - 1) / kC;
   const long nchunks = (long)a.B * a.H * nch;
   const float* dS = reinterpret_cast<const float*>(workspace);
   const float* zc = dS + (size_t)nchunks * dk * a.dv;
   const bf16_t* Sc = reinterpret_cast<const bf16_t*>(zc + (size_t)nchunks * dk);
   switch (dk) {
-    case 16: return launch_out_dk<16>(a.dv, a, Sc, zc, nchunks, nch, st);
-    case 32: return launch_out_dk<32>(a.dv, a, Sc, zc, nchunks, nch, st);
-    case 64: return launch_out_dk<64>(a.dv, a, Sc, zc, nchunks, nch, st);
-    case 128: return launch_out_dk<128>(a.dv, a, Sc, zc, nchunks, nch, st);
+    case 16: return launch_out_dk<16, GLA>(a.dv, a, Sc, zc, nchunks, nch, st);
+    case 32: return launch_out_dk<32, GLA>(a.dv, a, Sc, zc, nchunks, nch, st);
+    case 64: return launch_out_dk<64, GLA>(a.dv, a, Sc, zc, nchunks, nch, st);
+    case 128: return launch_out_dk<128, GLA>(a.dv, a, Sc, zc, nchunks, nch, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-// [dS: fp32 nchunks x dk x dv][dz, then z_c: fp32 nchunks x dk][S_c: bf16 nchunks x dk x dv]
+template <bool GLA>
+hipError_t launch_states(int dk, const PrefillArgs& a, void* workspace, hipStream_t st) {
+  const int nch = (a.T + kC - 1) / kC;
+  const long nchunks = (long)a.B * a.H * nch;
+  float* dS = reinterpret_cast<float*>(workspace);
+  float* dz = dS + (size_t)nchunks * dk * a.dv;
+  hipError_t e;
+  switch (dk) {
+    case 16: e = launch_state_dk<16, GLA>(a.dv, a, dS, dz, nchunks, nch, st); break;
+    case 32: e = launch_state_dk<32, GLA>(a.dv, a, dS, dz, nchunks, nch, st); break;
+    case 64: e = launch_state_dk<64, GLA>(a.dv, a, dS, dz, nchunks, nch, st); break;
+    case 128: e = launch_state_dk<128, GLA>(a.dv, a, dS, dz, nchunks, nch, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  const int nz = GLA ? 0 : dk;  // gated linear attention has no normaliser
+  const int n = dk * a.dv + nz;
+  bf16_t* Sb = reinterpret_cast<bf16_t*>(dz + (size_t)nchunks * dk);
+  hipLaunchKernelGGL((la_state_scan<GLA>), dim3((unsigned)((n + 255) / 256), (unsigned)(a.B * a.H)), dim3(256),
+                     0, st, dS, dz, Sb, a.S, a.z, nch, dk * a.dv, nz, a.use_init);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// [dS: fp32 nchunks x dk x dv][dz, then z_c (or Gam_C): fp32 nchunks x dk][S_c: bf16 nchunks x dk x dv]
 size_t la_par_workspace_bytes(int dk, const PrefillArgs& a) {
   const size_t nchunks = (size_t)a.B * a.H * ((a.T + kC - 1) / kC);
   return nchunks * ((size_t)dk * a.dv + dk) * sizeof(float) + nchunks * dk * a.dv * sizeof(bf16_t);
 }
 
-hipError_t launch_la_par_states(int dk, const PrefillArgs& a, void* workspace, hipStream_t st) {
-  const int nch = (a.T + kC - 1) / kC;
-  const long nchunks = (long)a.B * a.H * nch;
-  float* dS = reinterpret_cast<float*>(workspace);
-  float* dz = dS + (size_t)nchunks * dk * a.dv;
-  const bf16_t* k = reinterpret_cast<const bf16_t*>(a.k);
-  const bf16_t* v = reinterpret_cast<const bf16_t*>(a.v);
-  hipError_t e;
-  switch (dk) {
-    case 16: e = launch_state_dk<16>(a.dv, k, v, dS, dz, nchunks, a.T, nch, st); break;
-    case 32: e = launch_state_dk<32>(a.dv, k, v, dS, dz, nchunks, a.T, nch, st); break;
-    case 64: e = launch_state_dk<64>(a.dv, k, v, dS, dz, nchunks, a.T, nch, st); break;
-    case 128: e = launch_state_dk<128>(a.dv, k, v, dS, dz, nchunks, a.T, nch, st); break;
-    default: return hipErrorInvalidValue;
-  }
-  if (e != hipSuccess) return e;
-  const int n = dk * a.dv + dk;
-  bf16_t* Sb = reinterpret_cast<bf16_t*>(dz + (size_t)nchunks * dk);
-  hipLaunchKernelGGL(la_state_scan, dim3((unsigned)((n + 255) / 256), (unsigned)(a.B * a.H)), dim3(256), 0, st,
-                     dS, dz, Sb, a.S, a.z, nch, dk * a.dv, dk, a.use_init);
-  return hipGetLastError();
+hipError_t launch_la_par_states(int dk, const PrefillArgs& a, void* workspace, bool gla, hipStream_t st) {
+  return gla ? launch_states<true>(dk, a, workspace, st) : launch_states<false>(dk, a, workspace, st);
+}
+
+hipError_t launch_la_par_outputs(int dk, const PrefillArgs& a, void* workspace, bool gla, hipStream_t st) {
+  return gla ? launch_outputs<true>(dk, a, workspace, st) : launch_outputs<false>(dk, a, workspace, st);
 }
 
 }  // namespace linattn

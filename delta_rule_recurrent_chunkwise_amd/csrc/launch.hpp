@@ -52,9 +52,11 @@ hipError_t launch_prefill_pipe_token(const PrefillArgs& a, hipStream_t st);
 // Chunk-parallel linear attention (bf16): every chunk's phi(K)^T V and
 // colsum phi(K) into a workspace of la_par_workspace_bytes bytes, then their
 // exclusive prefix in place (the chunk-start states) and the final S, z.
+// gla: gated linear attention instead (no feature map or normaliser; a decay
+// per token).
 size_t la_par_workspace_bytes(int dk, const PrefillArgs& a);
-hipError_t launch_la_par_states(int dk, const PrefillArgs& a, void* workspace, hipStream_t st);
+hipError_t launch_la_par_states(int dk, const PrefillArgs& a, void* workspace, bool gla, hipStream_t st);
 // ... then every chunk's output from its chunk-start state (bf16).
-hipError_t launch_la_par_outputs(int dk, const PrefillArgs& a, void* workspace, hipStream_t st);
+hipError_t launch_la_par_outputs(int dk, const PrefillArgs& a, void* workspace, bool gla, hipStream_t st);
 
 }  // namespace linattn

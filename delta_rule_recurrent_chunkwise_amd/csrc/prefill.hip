@@ -606,15 +606,15 @@ hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, hipS
     if (e == hipSuccess && mode == PF_LA) e = zero_floats(a.z, nbh * dk, st);
     return e;
   }
-  if (bf16 && mode == PF_LA) {
+  if (bf16 && (mode == PF_LA || mode == PF_GLA)) {
     // Linear attention, chunk-parallel: the chunk-start states come from a
-    // prefix over per-chunk phi(K)^T V; then every chunk's output is formed
-    // independently from its own start state.
+    // prefix over per-chunk phi(K)^T V (gated: decayed); then every chunk's
+    // output is formed independently from its own start state.
     void* ws = nullptr;
     hipError_t e = hipMallocAsync(&ws, la_par_workspace_bytes(dk, a), st);
     if (e != hipSuccess) return e;
-    e = launch_la_par_states(dk, a, ws, st);
-    if (e == hipSuccess) e = launch_la_par_outputs(dk, a, ws, st);
+    e = launch_la_par_states(dk, a, ws, mode == PF_GLA, st);
+    if (e == hipSuccess) e = launch_la_par_outputs(dk, a, ws, mode == PF_GLA, st);
     const hipError_t f = hipFreeAsync(ws, st);
     return e != hipSuccess ? e : f;
   }

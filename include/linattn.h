@@ -45,10 +45,11 @@
  *               dv % 32 == 0: 384 B*H*C*dk + 4 B*H*C*dk bytes for the
  *               decay-scaled q and k, where C = ceil(T/64) is the number
  *               of 64-token chunks;
- *             - la_prefill with bf16 inputs: 6 B*H*C*dk*dv + 4 B*H*C*dk
- *               bytes for the per-chunk state increments (fp32), the state
- *               entering each chunk (bf16) and the normaliser entering each
- *               chunk (fp32).
+ *             - la_prefill and gla_prefill with bf16 inputs:
+ *               6 B*H*C*dk*dv + 4 B*H*C*dk bytes for the per-chunk state
+ *               increments (fp32), the state entering each chunk (bf16) and
+ *               the normaliser entering each chunk, or the chunk's decay
+ *               (fp32).
  *           A failed allocation returns LA_ERR_LAUNCH.
  * Sizes.    B, H (or N, H) >= 1; T >= 0 for prefill, any length (the last
  *           64-token chunk may be partial).  T = 0 enqueues no work when
