@@ -17,6 +17,9 @@ Functions (both follow the article "From GPT-2 to Kimi K3, explained"):
                      channel, g [B,H,T,dk]) applied to S before each read.
 ``gla_recurrent``    section "Gated Delta Net", the additive cache with a
                      forgetting factor: S <- a_t S + k_t^T v_t, o_t = q_t S.
+``delta_backward``   reverse-mode gradient of the (ungated) delta rule, token
+                     by token: dq, dk, dv, dbeta and dS0 for the loss
+                     sum do . o + sum dS_T * S_T.
 
 Inputs may be torch CPU tensors (float32, bfloat16, float64) or numpy arrays
 (float32, float64); all inputs of one call share a dtype.  They are read in
@@ -57,6 +60,9 @@ def _bind(lib):
     lib.orc_delta_recurrent.restype = i
     lib.orc_gla_recurrent.argtypes = [i, i, i, i, i, d, d, d, d, i, d, d, d, i]
     lib.orc_gla_recurrent.restype = i
+    lib.orc_delta_backward.argtypes = [i, i, i, i, i, d, d, d, d, i, d, d, d,
+                                       d, d, d, d, d, i]
+    lib.orc_delta_backward.restype = i
     lib.orc_max_threads.argtypes = []
     lib.orc_max_threads.restype = i
     return lib
@@ -199,3 +205,30 @@ def gla_recurrent(q, k, v, g=None, S0=None, nthreads: int = 0, lib=None):
     if rc != 0:
         raise MemoryError("oracle allocation failed")
     return o, S
+
+
+def delta_backward(q, k, v, beta, dO, S0=None, dST=None, nthreads: int = 0, lib=None):
+    """Gradients of the delta rule for the loss sum(dO * o) + sum(dST * S_T).
+    q, k [B,H,T,dk]; v, dO [B,H,T,dv]; beta [B,H,T] (one dtype); S0 and dST
+    [B,H,dk,dv] or None.  Returns (dq, dk, dv, dbeta, dS0) as float64."""
+    lib = lib or load()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    bufs = [_as_buffer(t) for t in (q, k, v, beta, dO)]
+    dts = {b[2] for b in bufs}
+    if len(dts) != 1:
+        raise ValueError("q, k, v, beta and dO must share a dtype")
+    s0, s0p = _state64(S0, (B, H, dk, dv))
+    dst, dstp = _state64(dST, (B, H, dk, dv))
+    dq = np.empty((B, H, T, dk), np.float64)
+    dkk = np.empty((B, H, T, dk), np.float64)
+    dvv = np.empty((B, H, T, dv), np.float64)
+    db = np.empty((B, H, T), np.float64)
+    dS0 = np.empty((B, H, dk, dv), np.float64)
+    rc = lib.orc_delta_backward(B, H, T, dk, dv, bufs[0][1], bufs[1][1], bufs[2][1],
+                                bufs[3][1], dts.pop(), s0p, bufs[4][1], dstp,
+                                dq.ctypes.data, dkk.ctypes.data, dvv.ctypes.data,
+                                db.ctypes.data, dS0.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise MemoryError("oracle allocation failed")
+    return dq, dkk, dvv, db, dS0

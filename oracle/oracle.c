@@ -306,3 +306,134 @@ int orc_gla_recurrent(int B, int H, int T, int dk, int dv,
     }
     return fail ? -1 : 0;
 }
+
+/*
+ * Reverse-mode gradient of the ungated delta rule, one token at a time, for
+ * the loss  sum_t do_t . o_t + sum dS_T * S_T  (do the output gradient, dS_T
+ * the gradient of the final state).  Forward, per token: u = beta (v - S^T k),
+ * S' = S + k u^T, o = S'^T q.  Backward, walking t from T-1 down to 0 with dS
+ * the gradient of the state after token t:
+ *   dS  += q do^T                       (o = S'^T q)
+ *   dq   = S' do
+ *   du   = dS^T k                       (S' = S + k u^T)
+ *   dk   = dS u
+ *   dv   = beta du                      (u = beta (v - S^T k))
+ *   dbeta= du . (v - S^T k)
+ *   dr   = -beta du                     (r = S^T k)
+ *   dk  += S dr ;  dS += k dr^T         (the gradient of the state before t)
+ * The states before every token are kept (recomputed forward), so memory is
+ * T * dk * dv doubles per head: for small cases only.  S0 may be NULL (zero
+ * start), dST may be NULL (no final-state gradient).  dO has the inputs'
+ * dtype.  Outputs (float64): dq, dk [B,H,T,dk], dv [B,H,T,dv], dbeta [B,H,T],
+ * dS0 [B,H,dk,dv] (any may be NULL).  Returns 0, or -1 on allocation failure.
+ */
+int orc_delta_backward(int B, int H, int T, int dk, int dv,
+                       const void *q, const void *k, const void *v,
+                       const void *beta, int dt, const double *S0,
+                       const void *dO, const double *dST,
+                       double *dq, double *dkk, double *dvv, double *dbeta,
+                       double *dS0, int nthreads)
+{
+    int fail = 0;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < B * H; bh++) {
+        const size_t ss = (size_t)dk * dv;
+        double *Sall = malloc(sizeof(double) * ss * ((size_t)T + 1));
+        double *dS = malloc(sizeof(double) * ss);
+        double *kt = malloc(sizeof(double) * (size_t)dk);
+        double *r = malloc(sizeof(double) * (size_t)dv);
+        double *u = malloc(sizeof(double) * (size_t)dv);
+        double *du = malloc(sizeof(double) * (size_t)dv);
+        double *dov = malloc(sizeof(double) * (size_t)dv);
+        if (!Sall || !dS || !kt || !r || !u || !du || !dov) {
+#pragma omp atomic write
+            fail = 1;
+            free(Sall); free(dS); free(kt); free(r); free(u); free(du); free(dov);
+            continue;
+        }
+        const size_t sbase = (size_t)bh * ss;
+        /* forward: Sall[t] is the state before token t, Sall[T] the final one */
+        for (size_t i = 0; i < ss; i++)
+            Sall[i] = S0 ? S0[sbase + i] : 0.0;
+        for (int t = 0; t < T; t++) {
+            const double *S = Sall + (size_t)t * ss;
+            double *Sn = Sall + (size_t)(t + 1) * ss;
+            const size_t qk_row = ((size_t)bh * T + t) * dk;
+            const size_t v_row = ((size_t)bh * T + t) * dv;
+            const double b = rd(beta, (size_t)bh * T + t, dt);
+            for (int i = 0; i < dk; i++)
+                kt[i] = rd(k, qk_row + i, dt);
+            for (int j = 0; j < dv; j++) {
+                r[j] = 0.0;
+                for (int i = 0; i < dk; i++)
+                    r[j] += S[(size_t)i * dv + j] * kt[i];
+                u[j] = (rd(v, v_row + j, dt) - r[j]) * b;
+            }
+            for (int i = 0; i < dk; i++)
+                for (int j = 0; j < dv; j++)
+                    Sn[(size_t)i * dv + j] = S[(size_t)i * dv + j] + kt[i] * u[j];
+        }
+        /* backward */
+        for (size_t i = 0; i < ss; i++)
+            dS[i] = dST ? dST[sbase + i] : 0.0;
+        for (int t = T - 1; t >= 0; t--) {
+            const double *S = Sall + (size_t)t * ss;        /* before token t */
+            const double *Sn = Sall + (size_t)(t + 1) * ss; /* after token t */
+            const size_t qk_row = ((size_t)bh * T + t) * dk;
+            const size_t v_row = ((size_t)bh * T + t) * dv;
+            const double b = rd(beta, (size_t)bh * T + t, dt);
+            for (int i = 0; i < dk; i++)
+                kt[i] = rd(k, qk_row + i, dt);
+            for (int j = 0; j < dv; j++)
+                dov[j] = rd(dO, v_row + j, dt);
+            /* o = S'^T q */
+            for (int i = 0; i < dk; i++) {
+                const double qa = rd(q, qk_row + i, dt);
+                double acc = 0.0;
+                for (int j = 0; j < dv; j++) {
+                    dS[(size_t)i * dv + j] += qa * dov[j];
+                    acc += Sn[(size_t)i * dv + j] * dov[j];
+                }
+                if (dq)
+                    dq[qk_row + i] = acc;
+            }
+            /* recompute r and u of token t */
+            for (int j = 0; j < dv; j++) {
+                r[j] = 0.0;
+                for (int i = 0; i < dk; i++)
+                    r[j] += S[(size_t)i * dv + j] * kt[i];
+                u[j] = (rd(v, v_row + j, dt) - r[j]) * b;
+            }
+            /* S' = S + k u^T */
+            for (int j = 0; j < dv; j++) {
+                du[j] = 0.0;
+                for (int i = 0; i < dk; i++)
+                    du[j] += dS[(size_t)i * dv + j] * kt[i];
+            }
+            double db = 0.0;
+            for (int j = 0; j < dv; j++)
+                db += du[j] * (rd(v, v_row + j, dt) - r[j]);
+            if (dbeta)
+                dbeta[(size_t)bh * T + t] = db;
+            if (dvv)
+                for (int j = 0; j < dv; j++)
+                    dvv[v_row + j] = b * du[j];
+            for (int i = 0; i < dk; i++) {
+                double acc = 0.0;
+                for (int j = 0; j < dv; j++)
+                    acc += dS[(size_t)i * dv + j] * u[j] - b * S[(size_t)i * dv + j] * du[j];
+                if (dkk)
+                    dkk[qk_row + i] = acc;
+            }
+            /* the gradient of the state before token t: dS += k dr^T, dr = -b du */
+            for (int i = 0; i < dk; i++)
+                for (int j = 0; j < dv; j++)
+                    dS[(size_t)i * dv + j] -= b * kt[i] * du[j];
+        }
+        if (dS0)
+            memcpy(dS0 + sbase, dS, sizeof(double) * ss);
+        free(Sall); free(dS); free(kt); free(r); free(u); free(du); free(dov);
+    }
+    return fail ? -1 : 0;
+}

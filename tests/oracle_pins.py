@@ -29,7 +29,10 @@ Independent evaluations used:
 * for the additive cache with a forgetting factor (section "Gated Delta Net",
   first step): its unrolled sum, i.e. the decayed masked quadratic form
   (tril(Q K^T) * e^{G_t - G_j}) V, and the limits a = 1 (plain additive
-  linear attention, closed-form state) and a = 0 (only the newest write).
+  linear attention, closed-form state) and a = 0 (only the newest write);
+* for the delta rule's gradient (the training use the article gives the
+  chunk form for): central finite differences of the forward oracle, and
+  torch autograd through a plain float64 loop of the same recurrence.
 """
 from __future__ import annotations
 
@@ -448,6 +451,70 @@ def pin_gla_limits(lib):
 
 
 # --------------------------------------------------------------------------
+# Gradient of the delta rule
+# --------------------------------------------------------------------------
+
+def _delta_loss(q, k, v, beta, S0, dO, dST, lib):
+    o, S = oracle.delta_recurrent(q, k, v, beta, None, S0, lib=lib)
+    return float(np.sum(o * dO) + np.sum(S * dST))
+
+
+def pin_delta_backward_finite_differences(lib):
+    """Every gradient the backward returns matches central differences of
+    the forward oracle's loss sum(dO * o) + sum(dST * S_T) (float64)."""
+    rng = _rng(30)
+    B, H, T, dk, dv = 1, 2, 6, 3, 4
+    q, k, v, beta, _ = _delta_inputs(rng, B, H, T, dk, dv)
+    S0 = rng.standard_normal((B, H, dk, dv))
+    dO = rng.standard_normal((B, H, T, dv))
+    dST = rng.standard_normal((B, H, dk, dv))
+    grads = oracle.delta_backward(q, k, v, beta, dO, S0, dST, lib=lib)
+    names = ("q", "k", "v", "beta", "S0")
+    args = dict(q=q, k=k, v=v, beta=beta, S0=S0)
+    h = 1e-6
+    for name, g in zip(names, grads):
+        x = args[name]
+        num = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            saved = x[idx]
+            x[idx] = saved + h
+            lp = _delta_loss(args["q"], args["k"], args["v"], args["beta"], args["S0"], dO, dST, lib)
+            x[idx] = saved - h
+            lm = _delta_loss(args["q"], args["k"], args["v"], args["beta"], args["S0"], dO, dST, lib)
+            x[idx] = saved
+            num[idx] = (lp - lm) / (2 * h)
+        _close(g, num, tol=1e-6, what=f"d{name} vs finite differences")
+
+
+def pin_delta_backward_autograd(lib):
+    """The backward equals torch autograd through a plain float64 loop of the
+    recurrence (read with k, correct with beta (v - r), write k^T u, read
+    with q), at a size with several dozen tokens."""
+    rng = _rng(31)
+    B, H, T, dk, dv = 1, 2, 40, 8, 6
+    q, k, v, beta, _ = _delta_inputs(rng, B, H, T, dk, dv)
+    S0 = rng.standard_normal((B, H, dk, dv))
+    dO = rng.standard_normal((B, H, T, dv))
+    dST = rng.standard_normal((B, H, dk, dv))
+    tq, tk, tv, tb, tS0 = (torch.tensor(x, dtype=torch.float64, requires_grad=True)
+                           for x in (q, k, v, beta, S0))
+    S = tS0
+    outs = []
+    for t in range(T):
+        kt = tk[:, :, t]
+        r = torch.einsum("bhi,bhij->bhj", kt, S)
+        u = tb[:, :, t, None] * (tv[:, :, t] - r)
+        S = S + kt[..., :, None] * u[..., None, :]
+        outs.append(torch.einsum("bhi,bhij->bhj", tq[:, :, t], S))
+    o = torch.stack(outs, 2)
+    loss = (o * torch.from_numpy(dO)).sum() + (S * torch.from_numpy(dST)).sum()
+    loss.backward()
+    grads = oracle.delta_backward(q, k, v, beta, dO, S0, dST, lib=lib)
+    for name, g, t in zip(("q", "k", "v", "beta", "S0"), grads, (tq, tk, tv, tb, tS0)):
+        _close(g, t.grad.numpy(), tol=1e-11, what=f"d{name} vs autograd")
+
+
+# --------------------------------------------------------------------------
 # Input handling and state carry
 # --------------------------------------------------------------------------
 
@@ -530,6 +597,8 @@ ALL_PINS = [
     pin_gated_ut_form,
     pin_gla_decayed_quadratic_form,
     pin_gla_limits,
+    pin_delta_backward_finite_differences,
+    pin_delta_backward_autograd,
     pin_stored_precision_widening,
     pin_state_carry,
 ]

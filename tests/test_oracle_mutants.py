@@ -63,6 +63,16 @@ MUTANTS = {
         "const double a = exp(rd(g, (size_t)bh * T + (t + 1 < T ? t + 1 : t), dt));"),
     "gla_write_with_wrong_value_column": (
         "vt[j] = rd(v, v_row + j, dt);", "vt[j] = rd(v, v_row + (j + 1) % dv, dt);"),
+    "bwd_output_gradient_not_added": (
+        "dS[(size_t)i * dv + j] += qa * dov[j];", "dS[(size_t)i * dv + j] += 0.0 * qa * dov[j];"),
+    "bwd_key_gradient_drops_read_term": (
+        "acc += dS[(size_t)i * dv + j] * u[j] - b * S[(size_t)i * dv + j] * du[j];",
+        "acc += dS[(size_t)i * dv + j] * u[j];"),
+    "bwd_beta_gradient_without_read": (
+        "db += du[j] * (rd(v, v_row + j, dt) - r[j]);", "db += du[j] * rd(v, v_row + j, dt);"),
+    "bwd_state_gradient_sign": (
+        "dS[(size_t)i * dv + j] -= b * kt[i] * du[j];", "dS[(size_t)i * dv + j] += b * kt[i] * du[j];"),
+    "bwd_value_gradient_without_beta": ("dvv[v_row + j] = b * du[j];", "dvv[v_row + j] = du[j];"),
     "gla_read_with_key": (
         "const double qi = rd(q, qk_row + i, dt);", "const double qi = rd(k, qk_row + i, dt);"),
     "bf16_widening_wrong_shift": (
