@@ -457,7 +457,34 @@ def bench_rows(la, workloads, torch, launches=20):
     rows[name] = r
     del d, gi
     rows.update(bench_token_gated_rows(la, workloads, torch, launches))
+    rows.update(bench_backward_row(la, workloads, torch))
     return rows
+
+
+def bench_backward_row(la, workloads, torch, launches=5):
+    """The delta rule's gradient at the timed prefill workload's shape: the
+    forward chunk states, the reverse chain and the chunk-parallel gradients."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    w = workloads.WORKLOADS[2]
+    inp = workloads.make_delta(w.B, w.H, w.T, w.dk, w.dv, w.dtype, seed=95)
+    d = {k: v.to(dev) for k, v in inp.items()}
+    gen = workloads.generator(96)
+    d["dO"] = torch.randn(w.B, w.H, w.T, w.dv, generator=gen).to(w.dtype).to(dev)
+    del inp
+
+    def run(d):
+        la.deltanet_prefill_backward(d["q"], d["k"], d["v"], d["beta"], d["dO"], stream=stream)
+
+    us, med = _time_launches(torch, stream, run, [d], launches, warmup=1)
+    th = w.B * w.H * w.T
+    per = th * 2 * (2 * w.dk + 2 * w.dv + 1) + th * 2 * (2 * w.dk + w.dv + 1)
+    name, r = _row("deltanet_prefill_backward", f"deltanet_prefill_backward B={w.B} H={w.H} "
+                   f"T={w.T} dk=dv={w.dk} bf16", us, med, per,
+                   "three passes: forward chunk states (generic kernel), reverse chain over "
+                   "chunks, chunk-parallel gradients; bytes are the inputs (q, k, v, beta, dO) "
+                   "and gradients (dq, dk, dv, dbeta) only")
+    return {name: r}
 
 
 def bench_token_gated_rows(la, workloads, torch, launches=20):
@@ -658,7 +685,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the other rows (LA prefill, gated prefill, LA/gated decode)")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy", "rows", "token-rows"],
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy", "rows", "token-rows",
+                                       "backward-row"],
                     default="all",
                     help="run one part only (for profiler runs)")
     ap.add_argument("--summarize", metavar="DIR",
@@ -692,6 +720,9 @@ def main():
         return
     if args.only == "token-rows":
         print(json.dumps(bench_token_gated_rows(la, workloads, torch)))
+        return
+    if args.only == "backward-row":
+        print(json.dumps(bench_backward_row(la, workloads, torch)))
         return
     if args.only == "decode":
         wd, _, el = bench_decode(la, workloads, torch, args.decode_steps)

@@ -44,7 +44,8 @@ const char* la_strerror(int code) {
     case LA_ERR_DTYPE: return "dtype must be LA_DTYPE_F32 (0) or LA_DTYPE_BF16 (1)";
     case LA_ERR_UNSUPPORTED_DIM:
       return "unsupported head dimension: dk and dv must each be 16, 32, 64 or 128 "
-             "(float32 deltanet_prefill with a per-channel gate: dk <= 64)";
+             "(float32: dk <= 64 for deltanet_prefill with a per-channel gate, "
+             "dk and dv <= 64 for deltanet_prefill_backward)";
     case LA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch or a workspace allocation";
     case LA_ERR_ALIGN:
       return "q, k and v (prefill) and S (decode) must be 16-byte aligned";
@@ -153,6 +154,20 @@ int gla_decode_step(const void* q, const void* k, const void* v, const void* g, 
   linattn::DecodeArgs a{q, k, v, nullptr, g, o, S, nullptr, N * H};
   return launch_rc(linattn::launch_decode(linattn::DEC_GLA, dtype == LA_DTYPE_BF16, dk, dv, a,
                                           static_cast<hipStream_t>(stream)));
+}
+
+int deltanet_prefill_backward(const void* q, const void* k, const void* v, const void* beta,
+                              const float* S0, const void* dO, const float* dST, void* dq, void* dk_out,
+                              void* dv_out, void* dbeta, float* dS0, int B, int H, int T, int dk,
+                              int dv, int dtype, void* stream) {
+  if (T != 0 && (!q || !k || !v || !beta || !dO || !dq || !dk_out || !dv_out || !dbeta)) return LA_ERR_NULL;
+  if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
+  if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1, true)) return LA_ERR_SHAPE;
+  if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
+  if (dtype == LA_DTYPE_F32 && (dk > 64 || dv > 64)) return LA_ERR_UNSUPPORTED_DIM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return LA_ERR_ALIGN;
+  linattn::BackwardArgs a{q, k, v, beta, S0, dO, dST, dq, dk_out, dv_out, dbeta, dS0, B, H, T, dk, dv};
+  return launch_rc(linattn::launch_delta_backward(dtype == LA_DTYPE_BF16, a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

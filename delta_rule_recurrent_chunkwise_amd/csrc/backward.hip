@@ -1,0 +1,676 @@
+// backward.hip -- gradient of the chunkwise delta rule (ungated).
+//
+// The article "From GPT-2 to Kimi K3, explained" gives the chunk form of
+// section "DeltaNet (Parallelizing Linear Transformers with Delta Rule)" as
+// the way to train the delta rule in linear time.  Per 64-token chunk with
+// incoming state S (dk x dv), L = tril(diag(beta) K K^T, -1), T = (I + L)^-1:
+//   X = diag(beta)(V - K S),  u = T X,  A = tril(Q K^T),
+//   O = Q S + A u,            S' = S + K^T u.
+// For the loss sum(dO * O) + sum(dS' * S') the chain rule gives, with
+// dS' the gradient of the state leaving the chunk (dSn below):
+//   du = A^T dO + K dSn            (O through u, and S' through u)
+//   dX = T^T du                    ((I + L) u = X)
+//   dL = -tril(dX u^T, -1),  dA = tril(dO u^T)
+//   dV = diag(beta) dX
+//   dbeta = rowsum((V - K S) * dX) + rowsum(dL * K K^T)
+//   dQ = dO S^T + dA K
+//   dK = dA^T Q + u dSn^T - diag(beta) dX S^T + (diag(beta) dL) K + (diag(beta) dL)^T K
+//   dS = dSn + Q^T dO - K^T diag(beta) dX   (the gradient of the state entering)
+//
+// Three passes:
+//   1. the forward chunk recurrence (the generic prefill kernel) writes the
+//      state entering every chunk to a workspace (fp32);
+//   2. bwd_chain walks the chunks backwards, one workgroup per (batch, head,
+//      slice of value columns) -- the columns of dS are independent, as those
+//      of S are forward -- and writes dSn of every chunk to a workspace;
+//   3. bwd_grads forms every chunk's dQ, dK, dV, dbeta at once, one workgroup
+//      per chunk, from its S and dSn.
+// Inputs and outputs have the input dtype; the products run on bf16 MFMA
+// (fp32 MFMA for fp32 inputs) with fp32 accumulation, like the forward.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace linattn {
+namespace {
+
+constexpr int kC = 64;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int LTL = kC + 4;  // fp32 row stride of T and its transpose
+
+__device__ __forceinline__ int xcd_remap_b(int bid, int n) {
+  if (n % 8 != 0) return bid;
+  return (bid % 8) * (n / 8) + bid / 8;
+}
+
+// T = (I + L)^-1 in the lower triangle (diagonal included) of sTL, from L
+// stored transposed in its strictly upper triangle (sTL[c][r] = L[r][c],
+// c < r).  Diagonal 16 x 16 blocks by forward substitution, one lane per
+// column; then block row by block row, T[bi][bj] = -T[bi][bi] sum_m L[bi][m]
+// T[m][bj].  The strictly upper triangle is cleared.  Every thread calls it.
+template <bool kBf16>
+__device__ void form_T(float* sTL, int tid, int wave, int lane) {
+  const int lc = lane & 15, lg = lane >> 4;
+  if (wave == kWaves - 1) {
+    const int b0 = 16 * lg;
+    float tv[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) tv[m] = m == lc ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) s += sTL[(b0 + m) * LTL + b0 + i] * tv[m];
+      if (i > lc) tv[i] = -s;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i >= lc) sTL[(b0 + i) * LTL + b0 + lc] = tv[i];
+  }
+  __syncthreads();
+  for (int bi = 1; bi < 4; ++bi) {
+    if (wave < bi) {
+      const int bj = wave;
+      floatx4 R = zero4();
+      for (int m = bj; m < bi; ++m) {
+        float av[4], bv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kk = 4 * lg + e;
+          av[e] = sTL[(16 * m + kk) * LTL + 16 * bi + lc];
+          bv[e] = (m > bj || kk >= lc) ? sTL[(16 * m + kk) * LTL + 16 * bj + lc] : 0.f;
+        }
+        if constexpr (kBf16) {
+          R = mfma_k16(words_to_shortx4(pack2(av[0], av[1]), pack2(av[2], av[3])),
+                       words_to_shortx4(pack2(bv[0], bv[1]), pack2(bv[2], bv[3])), R);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) R = mfma_f32(av[e], bv[e], R);
+        }
+      }
+      float tv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kk = 4 * lg + e;
+        tv[e] = kk <= lc ? sTL[(16 * bi + lc) * LTL + 16 * bi + kk] : 0.f;
+      }
+      floatx4 Y = zero4();
+      if constexpr (kBf16) {
+        Y = mfma_k16(words_to_shortx4(pack2(tv[0], tv[1]), pack2(tv[2], tv[3])), acc_to_b16(R), Y);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Y = mfma_f32(tv[e], R[e], Y);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sTL[(16 * bi + 4 * lg + i) * LTL + 16 * bj + lc] = -Y[i];
+    }
+    __syncthreads();
+  }
+  for (int i = tid; i < kC * kC; i += kThreads) {
+    const int r = i >> 6, c = i & 63;
+    if (c > r) sTL[r * LTL + c] = 0.f;
+  }
+  __syncthreads();
+}
+
+// acc (one 16 x 16 tile) += A[r, 0:K] B[c, 0:K]^T, both row-major in LDS
+template <bool kBf16, class T>
+__device__ __forceinline__ floatx4 rowrow(floatx4 acc, const T* arow, const T* brow, int K, int lane) {
+  if constexpr (kBf16) return mm_rowrow_bf16(acc, arow, brow, K, lane);
+  else return mm_rowrow_f32(acc, arow, brow, K, lane);
+}
+// acc += A[r, 0:16 nt] X, X given as nt accumulator tiles (nt even, or 1)
+template <bool kBf16, class EA>
+__device__ __forceinline__ floatx4 accB(floatx4 acc, const EA* arow, const floatx4* xt, int nt, int lane) {
+  if constexpr (kBf16) return mm_accB_bf16(acc, arow, xt, nt, lane);
+  else return mm_accB_f32(acc, reinterpret_cast<const float*>(arow), xt, nt, lane);
+}
+
+// Stage rows [t0, t0 + 64) of a [T][D] tensor (row-major) into LDS, rows
+// past the end as zeros: row-major (dst[r][d], stride ld) and/or transposed
+// (dstT[d][r], stride ldT).
+template <class E, int D>
+__device__ __forceinline__ void stage_rows(const typename E::T* src, int t0, int nrow, typename E::T* dst, int ld,
+                                           typename E::T* dstT, int ldT, int tid) {
+  typedef typename E::T T;
+  for (int i = tid; i < kC * D; i += kThreads) {
+    const int r = i / D, d = i - r * D;
+    const T x = r < nrow ? src[(size_t)(t0 + r) * D + d] : E::cvt(0.f);
+    if (dst) dst[r * ld + d] = x;
+    if (dstT) dstT[d * ldT + r] = x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: the reverse chain.  One workgroup per (batch, head, DVS value
+// columns); NCW = DVS / 16 chain waves hold dS[:, 16 columns] as accumulator
+// tiles.  Per chunk (last to first): write dSn, stage Q, K, dO, beta; the
+// other waves form tril(Q K^T) (stored transposed) and L; all form T and its
+// transpose; the chain forms du = A^T dO + K dSn, dX = T^T du and
+// dS = dSn + Q^T dO - K^T diag(beta) dX.
+// ---------------------------------------------------------------------------
+template <int DK, class E, int DVS>
+struct ChainLayout {
+  typedef typename E::T T;
+  static constexpr int PAD = 16 / (int)sizeof(T);
+  static constexpr int LQ = DK + PAD;   // rows of Q, K
+  static constexpr int LKT = kC + PAD;  // rows of Q^T, K^T, dO^T, A^T
+  static constexpr int oQ = 0;
+  static constexpr int oK = oQ + kC * LQ * (int)sizeof(T);
+  static constexpr int oQt = oK + kC * LQ * (int)sizeof(T);
+  static constexpr int oKt = oQt + DK * LKT * (int)sizeof(T);
+  static constexpr int oDOt = oKt + DK * LKT * (int)sizeof(T);
+  static constexpr int oAt = oDOt + DVS * LKT * (int)sizeof(T);
+  static constexpr int oTL = oAt + kC * LKT * (int)sizeof(T);
+  static constexpr int oTt = oTL + kC * LTL * 4;
+  static constexpr int oB = oTt + kC * LTL * 4;
+  static constexpr int total = oB + kC * 4;
+};
+
+template <int DK, class E, int DVS>
+__global__ __launch_bounds__(kThreads) void bwd_chain(BackwardArgs a, float* __restrict__ dSc) {
+  typedef ChainLayout<DK, E, DVS> L;
+  typedef typename E::T T;
+  constexpr bool kBf16 = sizeof(T) == 2;
+  constexpr int NCW = DVS / 16, NKT = DK / 16;
+  constexpr int LQ = L::LQ, LKT = L::LKT;
+  __shared__ __attribute__((aligned(16))) char smem[L::total];
+  T* sQ = reinterpret_cast<T*>(smem + L::oQ);
+  T* sK = reinterpret_cast<T*>(smem + L::oK);
+  T* sQt = reinterpret_cast<T*>(smem + L::oQt);
+  T* sKt = reinterpret_cast<T*>(smem + L::oKt);
+  T* sDOt = reinterpret_cast<T*>(smem + L::oDOt);
+  T* sAt = reinterpret_cast<T*>(smem + L::oAt);
+  float* sTL = reinterpret_cast<float*>(smem + L::oTL);
+  float* sTt = reinterpret_cast<float*>(smem + L::oTt);
+  float* sB = reinterpret_cast<float*>(smem + L::oB);
+
+  const int dv = a.dv_;
+  const int nsl = dv / DVS;
+  const int w = xcd_remap_b(blockIdx.x, gridDim.x);
+  const int bh = w / nsl, sl = w - bh * nsl;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
+  const int Tn = a.T, nch = (Tn + kC - 1) / kC;
+  const T* qh = reinterpret_cast<const T*>(a.q) + (size_t)bh * Tn * DK;
+  const T* kh = reinterpret_cast<const T*>(a.k) + (size_t)bh * Tn * DK;
+  const T* doh = reinterpret_cast<const T*>(a.dO) + (size_t)bh * Tn * dv + sl * DVS;
+  const T* bth = reinterpret_cast<const T*>(a.beta) + (size_t)bh * Tn;
+  const bool chain = wave < NCW;
+  const int col = sl * DVS + 16 * wave + lc;  // value column of a chain lane
+
+  floatx4 st[NKT];  // dS[:, 16 columns] of a chain wave
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt) {
+    st[kt] = zero4();
+    if (chain && a.dST) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[kt][i] = a.dST[((size_t)bh * DK + 16 * kt + 4 * lg + i) * dv + col];
+    }
+  }
+
+  for (int c = nch - 1; c >= 0; --c) {
+    const int t0 = c * kC, nrow = min(kC, Tn - t0);
+    if (chain) {  // dSn of chunk c
+      float* out = dSc + ((size_t)bh * nch + c) * DK * dv;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[(size_t)(16 * kt + 4 * lg + i) * dv + col] = st[kt][i];
+    }
+    __syncthreads();  // the previous chunk's readers are done
+    stage_rows<E, DK>(qh, t0, nrow, sQ, LQ, sQt, LKT, tid);
+    stage_rows<E, DK>(kh, t0, nrow, sK, LQ, sKt, LKT, tid);
+    for (int i = tid; i < kC * DVS; i += kThreads) {  // the dO slice, transposed
+      const int r = i / DVS, d = i - r * DVS;
+      sDOt[d * LKT + r] = r < nrow ? doh[(size_t)(t0 + r) * dv + d] : E::cvt(0.f);
+    }
+    if (tid < kC) sB[tid] = tid < nrow ? E::tof(bth[t0 + tid]) : 0.f;
+    __syncthreads();
+
+    floatx4 kds[4];
+    if (chain) {  // K dSn while the other waves form the products
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) kds[mt] = accB<kBf16>(zero4(), sK + (16 * mt + lc) * LQ, st, NKT, lane);
+    } else {
+      // jobs 0..9: tiles (i, j <= i) of tril(Q K^T), stored transposed;
+      // jobs 10..19: the same tiles of K K^T -> L (strictly lower, rows
+      // scaled by beta), stored transposed in T's upper triangle
+      for (int jb = wave - NCW; jb < 20; jb += kWaves - NCW) {
+        const bool isA = jb < 10;
+        const int t = isA ? jb : jb - 10;
+        const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
+        const int tj = t - ti * (ti + 1) / 2;
+        const floatx4 acc =
+            rowrow<kBf16>(zero4(), (isA ? sQ : sK) + (16 * ti + lc) * LQ, sK + (16 * tj + lc) * LQ, DK, lane);
+        const int cc = 16 * tj + lc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * ti + 4 * lg + i;
+          if (isA) sAt[cc * LKT + r] = E::cvt(cc <= r ? acc[i] : 0.f);
+          else if (cc < r) sTL[cc * LTL + r] = sB[r] * acc[i];
+        }
+      }
+      // A^T above the diagonal tiles (ti < tj) is never written: zero it
+      for (int i = tid - 64 * NCW; i >= 0 && i < kC * kC; i += kThreads - 64 * NCW) {
+        const int r = i >> 6, cc = i & 63;
+        if ((cc >> 4) > (r >> 4)) sAt[cc * LKT + r] = E::cvt(0.f);
+      }
+    }
+    __syncthreads();
+    form_T<kBf16>(sTL, tid, wave, lane);
+    for (int i = tid; i < kC * kC; i += kThreads) {
+      const int r = i >> 6, cc = i & 63;
+      sTt[cc * LTL + r] = sTL[r * LTL + cc];
+    }
+    __syncthreads();
+    if (chain) {
+      floatx4 dOt[4], du[4], dx[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {  // dO tiles over tokens: lane holds rows 16t + 4lg + i
+        const T* p = sDOt + (16 * wave + lc) * LKT + 16 * t + 4 * lg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dOt[t][i] = E::tof(p[i]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)  // a fresh accumulator: K dSn may come from the 16-deep opcode
+        du[mt] = kds[mt] + accB<kBf16>(zero4(), sAt + (16 * mt + lc) * LKT, dOt, 4, lane);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        dx[mt] = accB<kBf16>(zero4(), sTt + (16 * mt + lc) * LTL, du, 4, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dx[mt][i] *= -sB[16 * mt + 4 * lg + i];  // -diag(beta) dX
+      }
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+        floatx4 g1 = accB<kBf16>(zero4(), sQt + (16 * kt + lc) * LKT, dOt, 4, lane);
+        floatx4 g2 = accB<kBf16>(zero4(), sKt + (16 * kt + lc) * LKT, dx, 4, lane);
+        st[kt] += g1 + g2;
+      }
+    }
+  }
+  if (chain && a.dS0) {
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a.dS0[((size_t)bh * DK + 16 * kt + 4 * lg + i) * dv + col] = st[kt][i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 3: one workgroup per (batch, head, chunk).  Phases (barriers between),
+// with LDS regions reused as operands die:
+//   A  stage Q, K; tril(Q K^T) (transposed) and K K^T -> L, T, T^T
+//   B  per 16-column slice of dv (one wave each): X, u, du, dX from S and
+//      dSn held as accumulator tiles; write dV; rowsum((V - K S) * dX) into
+//      dbeta; u and dX rows to LDS
+//   C  stage dO; dA = tril(dO u^T), dL = -tril(dX u^T, -1) (+ its rowsum
+//      against K K^T into dbeta), both also transposed
+//   D  stage K^T: dQ = dA K and dK = (bL) K + (bL)^T K, bL = diag(beta) dL;
+//      then Q^T over bL: dK += dA^T Q (all kept in registers)
+//   E  stage S, dSn rows; dQ += dO S^T, dK += u dSn^T - diag(beta) dX S^T;
+//      write dQ, dK, dbeta
+// ---------------------------------------------------------------------------
+template <int DK, int DV, class E>
+struct GradLayout {
+  typedef typename E::T T;
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int PAD = 16 / ES;
+  static constexpr int LQ = DK + PAD;   // rows of Q, K
+  static constexpr int LV = DV + PAD;   // rows of u, dX, dO
+  static constexpr int LS = DV + PAD;   // rows of S, dSn (key rows)
+  static constexpr int LKT = kC + PAD;  // rows of A^T, dA, bL and their transposes, K^T, Q^T
+  static constexpr int ROWQ = kC * LQ * ES, ROWV = kC * LV * ES, TRI = kC * LKT * ES;
+  static constexpr int TQ = DK * LKT * ES, ST = DK * LS * ES, FT = kC * LTL * 4;
+  // persistent: u, dX, K K^T (fp32), beta, dbeta
+  static constexpr int oU = 0;
+  static constexpr int oDX = oU + ROWV;
+  static constexpr int oKK = oDX + ROWV;
+  static constexpr int oB = oKK + FT;
+  static constexpr int oDB = oB + kC * 4;
+  static constexpr int oW = oDB + kC * 4;  // phase-dependent work area
+  // phases A, B
+  static constexpr int aQ = oW, aK = aQ + ROWQ, aAt = aK + ROWQ, aTL = aAt + TRI, aTt = aTL + FT;
+  static constexpr int endAB = aTt + FT;
+  // phases C, D: dO, dA, dA^T, bL, bL^T, K^T; then Q^T where bL was
+  static constexpr int cDO = oW, cDA = cDO + ROWV, cDAt = cDA + TRI, cBL = cDAt + TRI, cBLt = cBL + TRI;
+  static constexpr int dKt = cBLt + TRI, dQt = cBL;
+  static_assert(TQ <= 2 * TRI, "Q^T must fit where bL and its transpose were");
+  static constexpr int endCD = dKt + TQ;
+  // phase E: dO (kept), S, dSn
+  static constexpr int eS = cDA, eDS = eS + ST;
+  static constexpr int endE = eDS + ST;
+  static constexpr int total = endAB > endCD ? (endAB > endE ? endAB : endE) : (endCD > endE ? endCD : endE);
+};
+
+template <int DK, int DV, class E>
+__global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const float* __restrict__ Sc,
+                                                     const float* __restrict__ dSc) {
+  typedef GradLayout<DK, DV, E> L;
+  typedef typename E::T T;
+  constexpr bool kBf16 = sizeof(T) == 2;
+  constexpr int NKT = DK / 16;
+  constexpr int NVT = DV / 16;
+  constexpr int LQ = L::LQ, LV = L::LV, LS = L::LS, LKT = L::LKT;
+  __shared__ __attribute__((aligned(16))) char smem[L::total];
+  T* sU = reinterpret_cast<T*>(smem + L::oU);
+  T* sDX = reinterpret_cast<T*>(smem + L::oDX);
+  float* sKK = reinterpret_cast<float*>(smem + L::oKK);
+  float* sB = reinterpret_cast<float*>(smem + L::oB);
+  float* sDB = reinterpret_cast<float*>(smem + L::oDB);
+
+  const int chunk = blockIdx.x;  // over B * H * nch
+  const int Tn = a.T, nch = (Tn + kC - 1) / kC;
+  const int bh = chunk / nch, c = chunk - bh * nch;
+  const int t0 = c * kC, nrow = min(kC, Tn - t0);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
+  const T* qh = reinterpret_cast<const T*>(a.q) + (size_t)bh * Tn * DK;
+  const T* kh = reinterpret_cast<const T*>(a.k) + (size_t)bh * Tn * DK;
+  const T* vh = reinterpret_cast<const T*>(a.v) + (size_t)bh * Tn * DV;
+  const T* doh = reinterpret_cast<const T*>(a.dO) + (size_t)bh * Tn * DV;
+  const T* bth = reinterpret_cast<const T*>(a.beta) + (size_t)bh * Tn;
+  const float* S = Sc + (size_t)chunk * DK * DV;
+  const float* dSn = dSc + (size_t)chunk * DK * DV;
+
+  // ---- phase A ----
+  T* sQ = reinterpret_cast<T*>(smem + L::aQ);
+  T* sK = reinterpret_cast<T*>(smem + L::aK);
+  T* sAt = reinterpret_cast<T*>(smem + L::aAt);
+  float* sTL = reinterpret_cast<float*>(smem + L::aTL);
+  float* sTt = reinterpret_cast<float*>(smem + L::aTt);
+  stage_rows<E, DK>(qh, t0, nrow, sQ, LQ, nullptr, 0, tid);
+  stage_rows<E, DK>(kh, t0, nrow, sK, LQ, nullptr, 0, tid);
+  if (tid < kC) {
+    sB[tid] = tid < nrow ? E::tof(bth[t0 + tid]) : 0.f;
+    sDB[tid] = 0.f;
+  }
+  for (int i = tid; i < kC * kC; i += kThreads) {  // tiles above the diagonal stay zero
+    const int r = i >> 6, cc = i & 63;
+    if ((cc >> 4) > (r >> 4)) sAt[cc * LKT + r] = E::cvt(0.f);
+  }
+  __syncthreads();
+  for (int jb = wave; jb < 20; jb += kWaves) {
+    const bool isA = jb < 10;
+    const int t = isA ? jb : jb - 10;
+    const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
+    const int tj = t - ti * (ti + 1) / 2;
+    const floatx4 acc =
+        rowrow<kBf16>(zero4(), (isA ? sQ : sK) + (16 * ti + lc) * LQ, sK + (16 * tj + lc) * LQ, DK, lane);
+    const int cc = 16 * tj + lc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * ti + 4 * lg + i;
+      if (isA) {
+        sAt[cc * LKT + r] = E::cvt(cc <= r ? acc[i] : 0.f);
+      } else if (cc < r) {
+        sTL[cc * LTL + r] = sB[r] * acc[i];
+        sKK[r * LTL + cc] = acc[i];
+      }
+    }
+  }
+  __syncthreads();
+  form_T<kBf16>(sTL, tid, wave, lane);
+  for (int i = tid; i < kC * kC; i += kThreads) {
+    const int r = i >> 6, cc = i & 63;
+    sTt[cc * LTL + r] = sTL[r * LTL + cc];
+  }
+  __syncthreads();
+
+  // ---- phase B: 16-column slices of dv, one per wave at a time ----
+  for (int s = wave; s < NVT; s += kWaves) {
+    const int col = 16 * s + lc;
+    floatx4 Sv[NKT], dSv[NKT], vt[4], dOt[4];
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        Sv[kt][i] = S[(size_t)(16 * kt + 4 * lg + i) * DV + col];
+        dSv[kt][i] = dSn[(size_t)(16 * kt + 4 * lg + i) * DV + col];
+      }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * lg + i;
+        vt[mt][i] = r < nrow ? E::tof(vh[(size_t)(t0 + r) * DV + col]) : 0.f;
+        dOt[mt][i] = r < nrow ? E::tof(doh[(size_t)(t0 + r) * DV + col]) : 0.f;
+      }
+    floatx4 res[4], xx[4], ut[4], du[4], dx[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const floatx4 y = accB<kBf16>(zero4(), sK + (16 * mt + lc) * LQ, Sv, NKT, lane);
+      res[mt] = vt[mt] - y;  // V - K S
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xx[mt][i] = sB[16 * mt + 4 * lg + i] * res[mt][i];
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      if constexpr (kBf16) ut[mt] = accB<kBf16>(zero4(), sTL + (16 * mt + lc) * LTL, xx, (mt | 1) + 1, lane);
+      else ut[mt] = accB<kBf16>(zero4(), sTL + (16 * mt + lc) * LTL, xx, mt + 1, lane);
+      const floatx4 d1 = accB<kBf16>(zero4(), sAt + (16 * mt + lc) * LKT, dOt, 4, lane);
+      const floatx4 d2 = accB<kBf16>(zero4(), sK + (16 * mt + lc) * LQ, dSv, NKT, lane);
+      du[mt] = d1 + d2;
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      dx[mt] = accB<kBf16>(zero4(), sTt + (16 * mt + lc) * LTL, du, 4, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * lg + i;
+        if (r < nrow) reinterpret_cast<T*>(a.dv)[((size_t)bh * Tn + t0 + r) * DV + col] = E::cvt(sB[r] * dx[mt][i]);
+        sU[r * LV + col] = E::cvt(ut[mt][i]);
+        sDX[r * LV + col] = E::cvt(dx[mt][i]);
+        float p = res[mt][i] * dx[mt][i];  // rowsum over this slice's 16 columns
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) p += __shfl_xor(p, off, 16);
+        if (lc == 0) atomicAdd(&sDB[r], p);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase C ----
+  T* sDO = reinterpret_cast<T*>(smem + L::cDO);
+  T* sDA = reinterpret_cast<T*>(smem + L::cDA);
+  T* sDAt = reinterpret_cast<T*>(smem + L::cDAt);
+  T* sBL = reinterpret_cast<T*>(smem + L::cBL);
+  T* sBLt = reinterpret_cast<T*>(smem + L::cBLt);
+  stage_rows<E, DV>(doh, t0, nrow, sDO, LV, nullptr, 0, tid);
+  for (int i = tid; i < kC * kC; i += kThreads) {  // tiles above the diagonal stay zero
+    const int r = i >> 6, cc = i & 63;
+    if ((cc >> 4) > (r >> 4)) {
+      const T z = E::cvt(0.f);
+      sDA[r * LKT + cc] = z;
+      sDAt[cc * LKT + r] = z;
+      sBL[r * LKT + cc] = z;
+      sBLt[cc * LKT + r] = z;
+    }
+  }
+  __syncthreads();
+  for (int jb = wave; jb < 20; jb += kWaves) {
+    const bool isA = jb < 10;  // dA, else dL
+    const int t = isA ? jb : jb - 10;
+    const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
+    const int tj = t - ti * (ti + 1) / 2;
+    const floatx4 acc =
+        rowrow<kBf16>(zero4(), (isA ? sDO : sDX) + (16 * ti + lc) * LV, sU + (16 * tj + lc) * LV, DV, lane);
+    const int cc = 16 * tj + lc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * ti + 4 * lg + i;
+      if (isA) {
+        const T x = E::cvt(cc <= r ? acc[i] : 0.f);
+        sDA[r * LKT + cc] = x;
+        sDAt[cc * LKT + r] = x;
+      } else {
+        const float dl = cc < r ? -acc[i] : 0.f;
+        float p = cc < r ? dl * sKK[r * LTL + cc] : 0.f;  // rowsum(dL * K K^T)
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) p += __shfl_xor(p, off, 16);
+        if (lc == 0) atomicAdd(&sDB[r], p);
+        const T x = E::cvt(sB[r] * dl);
+        sBL[r * LKT + cc] = x;
+        sBLt[cc * LKT + r] = x;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase D: each wave owns output tiles id = wave + 4 n of the 4 x NKT grid ----
+  T* sKt = reinterpret_cast<T*>(smem + L::dKt);
+  T* sQt = reinterpret_cast<T*>(smem + L::dQt);
+  stage_rows<E, DK>(kh, t0, nrow, nullptr, 0, sKt, LKT, tid);
+  __syncthreads();
+  constexpr int NOWN = NKT;  // 4 * NKT tiles over 4 waves
+  floatx4 gq[NOWN], gk[NOWN];
+#pragma unroll
+  for (int n = 0; n < NOWN; ++n) {
+    const int id = wave + kWaves * n, ti = id / NKT, tk = id - ti * NKT;
+    gq[n] = rowrow<kBf16>(zero4(), sDA + (16 * ti + lc) * LKT, sKt + (16 * tk + lc) * LKT, kC, lane);
+    floatx4 x = rowrow<kBf16>(zero4(), sBL + (16 * ti + lc) * LKT, sKt + (16 * tk + lc) * LKT, kC, lane);
+    x += rowrow<kBf16>(zero4(), sBLt + (16 * ti + lc) * LKT, sKt + (16 * tk + lc) * LKT, kC, lane);
+    gk[n] = x;
+  }
+  __syncthreads();  // bL is dead: Q^T goes in its place
+  stage_rows<E, DK>(qh, t0, nrow, nullptr, 0, sQt, LKT, tid);
+  __syncthreads();
+#pragma unroll
+  for (int n = 0; n < NOWN; ++n) {
+    const int id = wave + kWaves * n, ti = id / NKT, tk = id - ti * NKT;
+    gk[n] += rowrow<kBf16>(zero4(), sDAt + (16 * ti + lc) * LKT, sQt + (16 * tk + lc) * LKT, kC, lane);
+  }
+  __syncthreads();
+
+  // ---- phase E ----
+  T* sS = reinterpret_cast<T*>(smem + L::eS);
+  T* sDS = reinterpret_cast<T*>(smem + L::eDS);
+  for (int i = tid; i < DK * DV; i += kThreads) {
+    const int r = i / DV, d = i - r * DV;
+    sS[r * LS + d] = E::cvt(S[i]);
+    sDS[r * LS + d] = E::cvt(dSn[i]);
+  }
+  __syncthreads();
+  T* dqo = reinterpret_cast<T*>(a.dq) + ((size_t)bh * Tn + t0) * DK;
+  T* dko = reinterpret_cast<T*>(a.dk) + ((size_t)bh * Tn + t0) * DK;
+#pragma unroll
+  for (int n = 0; n < NOWN; ++n) {
+    const int id = wave + kWaves * n, ti = id / NKT, tk = id - ti * NKT;
+    const floatx4 q1 = rowrow<kBf16>(zero4(), sDO + (16 * ti + lc) * LV, sS + (16 * tk + lc) * LS, DV, lane);
+    const floatx4 k1 = rowrow<kBf16>(zero4(), sU + (16 * ti + lc) * LV, sDS + (16 * tk + lc) * LS, DV, lane);
+    const floatx4 k2 = rowrow<kBf16>(zero4(), sDX + (16 * ti + lc) * LV, sS + (16 * tk + lc) * LS, DV, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * ti + 4 * lg + i, d = 16 * tk + lc;
+      if (r < nrow) {
+        dqo[(size_t)r * DK + d] = E::cvt(gq[n][i] + q1[i]);
+        dko[(size_t)r * DK + d] = E::cvt(gk[n][i] + k1[i] - sB[r] * k2[i]);
+      }
+    }
+  }
+  if (tid < nrow) reinterpret_cast<T*>(a.dbeta)[(size_t)bh * Tn + t0 + tid] = E::cvt(sDB[tid]);
+}
+
+template <int DK, int DV, class E>
+hipError_t launch_grads(const BackwardArgs& a, const float* Sc, const float* dSc, long nchunks, hipStream_t st) {
+  static_assert(GradLayout<DK, DV, E>::total <= 160 * 1024, "backward gradient kernel exceeds the LDS of a CU");
+  hipLaunchKernelGGL((bwd_grads<DK, DV, E>), dim3((unsigned)nchunks), dim3(kThreads), 0, st, a, Sc, dSc);
+  return hipGetLastError();
+}
+
+template <int DK, class E>
+hipError_t launch_grads_dk(const BackwardArgs& a, const float* Sc, const float* dSc, long nchunks, hipStream_t st) {
+  switch (a.dv_) {
+    case 16: return launch_grads<DK, 16, E>(a, Sc, dSc, nchunks, st);
+    case 32: return launch_grads<DK, 32, E>(a, Sc, dSc, nchunks, st);
+    case 64: return launch_grads<DK, 64, E>(a, Sc, dSc, nchunks, st);
+    case 128:
+      if constexpr (sizeof(typename E::T) == 2) return launch_grads<DK, 128, E>(a, Sc, dSc, nchunks, st);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DK, class E>
+hipError_t launch_chain_dk(const BackwardArgs& a, float* dSc, hipStream_t st) {
+  const long bh = (long)a.B * a.H;
+  if (a.dv_ % 32 == 0) {
+    hipLaunchKernelGGL((bwd_chain<DK, E, 32>), dim3((unsigned)(bh * (a.dv_ / 32))), dim3(kThreads), 0, st, a, dSc);
+  } else {
+    hipLaunchKernelGGL((bwd_chain<DK, E, 16>), dim3((unsigned)(bh * (a.dv_ / 16))), dim3(kThreads), 0, st, a, dSc);
+  }
+  return hipGetLastError();
+}
+
+template <class E>
+hipError_t launch_backward_e(const BackwardArgs& a, float* Sc, float* dSc, hipStream_t st) {
+  const long nchunks = (long)a.B * a.H * ((a.T + kC - 1) / kC);
+  hipError_t e;
+  switch (a.dk_) {
+    case 16: e = launch_chain_dk<16, E>(a, dSc, st); break;
+    case 32: e = launch_chain_dk<32, E>(a, dSc, st); break;
+    case 64: e = launch_chain_dk<64, E>(a, dSc, st); break;
+    case 128:
+      if constexpr (sizeof(typename E::T) == 2) {
+        e = launch_chain_dk<128, E>(a, dSc, st);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  switch (a.dk_) {
+    case 16: return launch_grads_dk<16, E>(a, Sc, dSc, nchunks, st);
+    case 32: return launch_grads_dk<32, E>(a, Sc, dSc, nchunks, st);
+    case 64: return launch_grads_dk<64, E>(a, Sc, dSc, nchunks, st);
+    case 128:
+      if constexpr (sizeof(typename E::T) == 2) return launch_grads_dk<128, E>(a, Sc, dSc, nchunks, st);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_state(float* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0.f;
+}
+
+size_t delta_backward_workspace_bytes(const BackwardArgs& a) {
+  const size_t nchunks = (size_t)a.B * a.H * ((a.T + kC - 1) / kC);
+  return 2 * nchunks * a.dk_ * a.dv_ * sizeof(float);
+}
+
+}  // namespace
+
+hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, hipStream_t st) {
+  if (a.T == 0) {  // no tokens: the state's gradient passes through
+    if (!a.dS0) return hipSuccess;
+    const size_t n = (size_t)a.B * a.H * a.dk_ * a.dv_;
+    if (a.dST) return hipMemcpyAsync(a.dS0, a.dST, n * sizeof(float), hipMemcpyDeviceToDevice, st);
+    const size_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+    hipLaunchKernelGGL(zero_state, dim3((unsigned)blocks), dim3(256), 0, st, a.dS0, n);
+    return hipGetLastError();
+  }
+  // pass 1: the state entering every chunk, from the generic forward kernel
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, delta_backward_workspace_bytes(a), st);
+  if (e != hipSuccess) return e;
+  float* Sc = reinterpret_cast<float*>(ws);
+  float* dSc = Sc + (size_t)a.B * a.H * ((a.T + kC - 1) / kC) * a.dk_ * a.dv_;
+  PrefillArgs f{};
+  f.q = a.q;
+  f.k = a.k;
+  f.v = a.v;
+  f.beta = a.beta;
+  f.S = const_cast<float*>(a.S0);
+  f.B = a.B;
+  f.H = a.H;
+  f.T = a.T;
+  f.dv = a.dv_;
+  f.use_init = a.S0 != nullptr;
+  f.Sc = Sc;
+  e = launch_prefill_generic(PF_DELTA, bf16, a.dk_, f, st);
+  // passes 2 and 3
+  if (e == hipSuccess) e = bf16 ? launch_backward_e<BF16>(a, Sc, dSc, st) : launch_backward_e<F32>(a, Sc, dSc, st);
+  const hipError_t fr = hipFreeAsync(ws, st);
+  return e != hipSuccess ? e : fr;
+}
+
+}  // namespace linattn

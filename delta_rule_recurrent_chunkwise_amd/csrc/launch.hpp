@@ -34,6 +34,10 @@ struct PrefillArgs {
   float* S;
   float* z;          // linear attention only
   int B, H, T, dv, use_init;
+  // backward pass only (generic kernel): when set, the state entering every
+  // chunk is written to Sc [B*H][ceil(T/64)][dk][dv] and neither o nor the
+  // final state is written
+  float* Sc;
 };
 
 // Enqueue one kernel on `st`; returns hipGetLastError() of the launch, or
@@ -41,6 +45,25 @@ struct PrefillArgs {
 hipError_t launch_decode(int kind, int bf16, int dk, int dv, const DecodeArgs& a,
                          hipStream_t st);
 hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, hipStream_t st);
+// The generic prefill kernel only (used by the backward pass with a.Sc set).
+hipError_t launch_prefill_generic(int mode, int bf16, int dk, const PrefillArgs& a, hipStream_t st);
+// Gradient of the ungated delta rule (backward.hip): see deltanet_prefill_backward.
+struct BackwardArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* beta;
+  const float* S0;   // initial state or NULL
+  const void* dO;
+  const float* dST;  // gradient of the final state or NULL
+  void* dq;
+  void* dk;
+  void* dv;
+  void* dbeta;
+  float* dS0;        // gradient of the initial state or NULL
+  int B, H, T, dk_, dv_;
+};
+hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, hipStream_t st);
 // The software-pipelined delta-rule prefill for bf16, dk = 128, dv % 32 == 0:
 // plain (a.g == NULL, no workspace) or gated (needs a workspace of
 // gated_pipe_workspace_bytes(a) bytes).

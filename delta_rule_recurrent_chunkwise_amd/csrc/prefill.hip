@@ -212,6 +212,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = c * kC;
+    if (a.Sc && chain) {  // the state entering chunk c, for the backward pass
+      float* sc = a.Sc + ((size_t)bh * nchunks + c) * DK * dv + sl * DVS;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[(size_t)(16 * kt + 4 * lg + i) * dv + 16 * cw + lc] = st[kt][i];
+    }
     __syncthreads();  // the previous chunk's readers of LDS are done
 
     // ---------------- stage the chunk in LDS ----------------
@@ -511,7 +518,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
           const int r = 16 * mt + 4 * lg + i;
           float val = ox[mt][i];
           if (MODE == PF_LA) val = val / sRow[r];
-          if (t0 + r <= tlast) oh[(size_t)(t0 + r) * dv + 16 * cw + lc] = E::cvt(val);
+          if (!a.Sc && t0 + r <= tlast) oh[(size_t)(t0 + r) * dv + 16 * cw + lc] = E::cvt(val);
         }
       }
       if (kGate) {
@@ -543,13 +550,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  if (chain) {
+  if (chain && !a.Sc) {
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) Sh[(size_t)(16 * kt + 4 * lg + i) * dv + 16 * cw + lc] = st[kt][i];
   }
-  if (MODE == PF_LA && sl == 0) {
+  if (MODE == PF_LA && sl == 0 && !a.Sc) {
     __syncthreads();
     for (int d = tid; d < DK; d += kThreads) a.z[(size_t)bh * DK + d] = sVec[d];
   }
@@ -632,6 +639,10 @@ hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, hipS
       return e != hipSuccess ? e : f;
     }
   }
+  return launch_prefill_generic(mode, bf16, dk, a, st);
+}
+
+hipError_t launch_prefill_generic(int mode, int bf16, int dk, const PrefillArgs& a, hipStream_t st) {
   if (bf16) {
     switch (mode) {
       case PF_LA: return launch_prefill_e<BF16, PF_LA>(dk, a, st);

@@ -38,7 +38,7 @@
  *           points must be 16-byte aligned (they are read in 16-byte
  *           vectors).  o must not alias any input.  S (and z) are read and written.  The
  *           library keeps no state between calls; calls are re-entrant.  It
- *           allocates device memory in two cases, each a stream-ordered
+ *           allocates device memory in three cases, each a stream-ordered
  *           workspace (hipMallocAsync on `stream`, released with
  *           hipFreeAsync after its kernels):
  *             - the gated deltanet_prefill with bf16 inputs, dk = 128 and
@@ -49,7 +49,9 @@
  *               6 B*H*C*dk*dv + 4 B*H*C*dk bytes for the per-chunk state
  *               increments (fp32), the state entering each chunk (bf16) and
  *               the normaliser entering each chunk, or the chunk's decay
- *               (fp32).
+ *               (fp32);
+ *             - deltanet_prefill_backward: 8 B*H*C*dk*dv bytes for the
+ *               state entering and the gradient leaving every chunk.
  *           A failed allocation returns LA_ERR_LAUNCH.
  * Sizes.    B, H (or N, H) >= 1; T >= 0 for prefill, any length (the last
  *           64-token chunk may be partial).  T = 0 enqueues no work when
@@ -201,6 +203,32 @@ int gla_prefill(const void *q, const void *k, const void *v, const void *g,
 int gla_decode_step(const void *q, const void *k, const void *v, const void *g,
                     void *o, float *S, int N, int H, int dk, int dv, int dtype,
                     void *stream);
+
+/*
+ * deltanet_prefill_backward -- gradients of deltanet_prefill without a gate
+ * (the delta rule), for training: the article gives the chunk form of
+ * section "DeltaNet (Parallelizing Linear Transformers with Delta Rule)" as
+ * the linear-time way to train it.  For the loss
+ *   sum(dO * o) + sum(dST * S_T)
+ * it writes dq, dk [B,H,T,dk], dv [B,H,T,dv], dbeta [B,H,T] (dtype) and,
+ * if dS0 != NULL, the gradient of the initial state dS0 [B,H,dk,dv] (fp32).
+ * Inputs: q, k, v, beta as for deltanet_prefill; S0 [B,H,dk,dv] fp32 or NULL
+ * (zero initial state); dO [B,H,T,dv] (dtype); dST [B,H,dk,dv] fp32 or NULL
+ * (no gradient on the final state).  Chunkwise, per 64-token chunk with
+ * incoming state S and dSn the gradient of the state leaving it:
+ *   du = A^T dO + K dSn, dX = T^T du, dV = diag(beta) dX,
+ *   dQ = dO S^T + tril(dO u^T) K, dS = dSn + Q^T dO - K^T diag(beta) dX, ...
+ * It recomputes the forward chunk states into a stream-ordered workspace of
+ * 8 B*H*C*dk*dv bytes (C = ceil(T/64)); a failed allocation returns
+ * LA_ERR_LAUNCH.  Sizes: dk, dv in {16, 32, 64, 128} for bf16, up to 64 for
+ * float32.  T = 0 copies dST to dS0 (or zero-fills it).
+ */
+int deltanet_prefill_backward(const void *q, const void *k, const void *v,
+                              const void *beta, const float *S0,
+                              const void *dO, const float *dST, void *dq,
+                              void *dk_out, void *dv_out, void *dbeta,
+                              float *dS0, int B, int H, int T, int dk, int dv,
+                              int dtype, void *stream);
 
 /* la_strerror -- a static, NUL-terminated description of an error code. */
 const char *la_strerror(int code);
