@@ -40,7 +40,7 @@ PREFILL_SOURCES = [_CSRC + "prefill_pipe.hip", _CSRC + "device_common.hpp", _CSR
 DECODE_SOURCES = [_CSRC + "decode.hip", _CSRC + "device_common.hpp", _CSRC + "launch.hpp"]
 # Symbol substrings of the two timed kernels (as rocprofv3 lists them) and the
 # profile summaries that record their counters.
-PREFILL_KERNEL = "prefill_pipe<0, 32>"
+PREFILL_KERNEL = "prefill_pipe<0, 32, false>"
 DECODE_KERNEL = "decode_kernel<128, 128, linattn::BF16, 0"
 PREFILL_PROFILE = "prefill_pipe_delta_B4_H16_T4096_d128.txt"
 DECODE_PROFILE = "decode_kernel_delta_N256_H32_d128.txt"
@@ -49,7 +49,7 @@ COPY_KERNEL = "copyBuffer"
 ROW_PROFILES = [
     ("prefill_pipe_gated_B1_H32_T32768_d128.txt",
      "gated deltanet_prefill B=1 H=32 T=32768 dk=dv=128 bf16: gate pre-pass + pipelined kernel",
-     ["gate_prep", "prefill_pipe<1, 16>"]),
+     ["gate_prep", "prefill_pipe<1, 16, false>"]),
     ("la_par_B8_H12_T1024_d64.txt",
      "la_prefill B=8 H=12 T=1024 dk=dv=64 bf16: chunk states, state scan, chunk outputs",
      ["la_chunk_state<64, 64, false>", "la_state_scan<false>", "la_chunk_out<64, 64, false>"]),
@@ -58,10 +58,10 @@ ROW_PROFILES = [
      ["la_chunk_state<64, 64, true>", "la_state_scan<true>", "la_chunk_out<64, 64, true>"]),
     ("prefill_pipe_token_gate_B4_H16_T4096_d128.txt",
      "gated_deltanet_prefill (one decay per token) B=4 H=16 T=4096 dk=dv=128 bf16",
-     ["prefill_pipe<2, 32>"]),
+     ["prefill_pipe<2, 32, false>"]),
     ("prefill_pipe_token_gate_B1_H32_T32768_d128.txt",
      "gated_deltanet_prefill (one decay per token) B=1 H=32 T=32768 dk=dv=128 bf16",
-     ["prefill_pipe<2, 16>"]),
+     ["prefill_pipe<2, 16, false>"]),
     ("prefill_kernel_la_fp32_B1_H2_T64_d16.txt", "la_prefill B=1 H=2 T=64 dk=dv=16 fp32",
      ["prefill_kernel<16, linattn::F32, 0, 16>"]),
     ("decode_kernel_la_N256_H32_d128.txt", "la_decode_step N=256 H=32 dk=dv=128, fp32 S and z",

@@ -48,7 +48,7 @@ const char* la_strerror(int code) {
              "dk and dv <= 64 for deltanet_prefill_backward)";
     case LA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch or a workspace allocation";
     case LA_ERR_ALIGN:
-      return "q, k and v (prefill) and S (decode) must be 16-byte aligned";
+      return "q, k and v (prefill; and dO, backward) and S (decode) must be 16-byte aligned";
     default: return "unknown error code";
   }
 }
@@ -165,7 +165,7 @@ int deltanet_prefill_backward(const void* q, const void* k, const void* v, const
   if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1, true)) return LA_ERR_SHAPE;
   if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
   if (dtype == LA_DTYPE_F32 && (dk > 64 || dv > 64)) return LA_ERR_UNSUPPORTED_DIM;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return LA_ERR_ALIGN;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO)) return LA_ERR_ALIGN;
   linattn::BackwardArgs a{q, k, v, beta, S0, dO, dST, dq, dk_out, dv_out, dbeta, dS0, B, H, T, dk, dv};
   return launch_rc(linattn::launch_delta_backward(dtype == LA_DTYPE_BF16, a, static_cast<hipStream_t>(stream)));
 }

@@ -126,18 +126,42 @@ __device__ __forceinline__ floatx4 accB(floatx4 acc, const EA* arow, const float
   else return mm_accB_f32(acc, reinterpret_cast<const float*>(arow), xt, nt, lane);
 }
 
-// Stage rows [t0, t0 + 64) of a [T][D] tensor (row-major) into LDS, rows
-// past the end as zeros: row-major (dst[r][d], stride ld) and/or transposed
-// (dstT[d][r], stride ldT).
+template <class E>
+union Vec16U {
+  Vec16 v;
+  typename E::T e[E::kVec];
+};
+
+// Stage D columns of rows [t0, t0 + 64) of a row-major tensor (source row
+// stride sld elements, 16-byte aligned rows) into LDS, rows past the end as
+// zeros: row-major (dst[r][d], stride ld, 16-byte aligned rows) and/or
+// transposed (dstT[d][r], stride ldT).  Every thread first issues all of its
+// 16-byte loads (rows past the end re-read the last row), then stores.
 template <class E, int D>
-__device__ __forceinline__ void stage_rows(const typename E::T* src, int t0, int nrow, typename E::T* dst, int ld,
-                                           typename E::T* dstT, int ldT, int tid) {
-  typedef typename E::T T;
-  for (int i = tid; i < kC * D; i += kThreads) {
-    const int r = i / D, d = i - r * D;
-    const T x = r < nrow ? src[(size_t)(t0 + r) * D + d] : E::cvt(0.f);
-    if (dst) dst[r * ld + d] = x;
-    if (dstT) dstT[d * ldT + r] = x;
+__device__ __forceinline__ void stage_rows(const typename E::T* src, int sld, int t0, int nrow, typename E::T* dst,
+                                           int ld, typename E::T* dstT, int ldT, int tid) {
+  constexpr int KV = E::kVec;
+  constexpr int VPR = D / KV;  // 16-byte vectors per row
+  constexpr int NV = kC * VPR;
+  constexpr int NPT = (NV + kThreads - 1) / kThreads;
+  Vec16U<E> buf[NPT];
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) {
+    const int i = min(tid + kThreads * j, NV - 1);
+    const int r = min(i / VPR, nrow - 1);
+    buf[j].v = *reinterpret_cast<const Vec16*>(src + (size_t)(t0 + r) * sld + (i % VPR) * KV);
+  }
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) {
+    const int i = tid + kThreads * j;
+    if (NV % kThreads != 0 && i >= NV) continue;
+    const int r = i / VPR, d = (i % VPR) * KV;
+    if (r >= nrow) buf[j].v = Vec16{};
+    if (dst) *reinterpret_cast<Vec16*>(dst + r * ld + d) = buf[j].v;
+    if (dstT) {
+#pragma unroll
+      for (int e = 0; e < KV; ++e) dstT[(d + e) * ldT + r] = buf[j].e[e];
+    }
   }
 }
 
@@ -218,12 +242,9 @@ __global__ __launch_bounds__(kThreads) void bwd_chain(BackwardArgs a, float* __r
         for (int i = 0; i < 4; ++i) out[(size_t)(16 * kt + 4 * lg + i) * dv + col] = st[kt][i];
     }
     __syncthreads();  // the previous chunk's readers are done
-    stage_rows<E, DK>(qh, t0, nrow, sQ, LQ, sQt, LKT, tid);
-    stage_rows<E, DK>(kh, t0, nrow, sK, LQ, sKt, LKT, tid);
-    for (int i = tid; i < kC * DVS; i += kThreads) {  // the dO slice, transposed
-      const int r = i / DVS, d = i - r * DVS;
-      sDOt[d * LKT + r] = r < nrow ? doh[(size_t)(t0 + r) * dv + d] : E::cvt(0.f);
-    }
+    stage_rows<E, DK>(qh, DK, t0, nrow, sQ, LQ, sQt, LKT, tid);
+    stage_rows<E, DK>(kh, DK, t0, nrow, sK, LQ, sKt, LKT, tid);
+    stage_rows<E, DVS>(doh, dv, t0, nrow, nullptr, 0, sDOt, LKT, tid);  // the dO slice, transposed
     if (tid < kC) sB[tid] = tid < nrow ? E::tof(bth[t0 + tid]) : 0.f;
     __syncthreads();
 
@@ -377,8 +398,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const floa
   T* sAt = reinterpret_cast<T*>(smem + L::aAt);
   float* sTL = reinterpret_cast<float*>(smem + L::aTL);
   float* sTt = reinterpret_cast<float*>(smem + L::aTt);
-  stage_rows<E, DK>(qh, t0, nrow, sQ, LQ, nullptr, 0, tid);
-  stage_rows<E, DK>(kh, t0, nrow, sK, LQ, nullptr, 0, tid);
+  stage_rows<E, DK>(qh, DK, t0, nrow, sQ, LQ, nullptr, 0, tid);
+  stage_rows<E, DK>(kh, DK, t0, nrow, sK, LQ, nullptr, 0, tid);
   if (tid < kC) {
     sB[tid] = tid < nrow ? E::tof(bth[t0 + tid]) : 0.f;
     sDB[tid] = 0.f;
@@ -431,8 +452,11 @@ __global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const floa
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * mt + 4 * lg + i;
-        vt[mt][i] = r < nrow ? E::tof(vh[(size_t)(t0 + r) * DV + col]) : 0.f;
-        dOt[mt][i] = r < nrow ? E::tof(doh[(size_t)(t0 + r) * DV + col]) : 0.f;
+        const int rr = min(r, nrow - 1);  // every lane loads; rows past the end are zeroed
+        const float vx = E::tof(vh[(size_t)(t0 + rr) * DV + col]);
+        const float ox = E::tof(doh[(size_t)(t0 + rr) * DV + col]);
+        vt[mt][i] = r < nrow ? vx : 0.f;
+        dOt[mt][i] = r < nrow ? ox : 0.f;
       }
     floatx4 res[4], xx[4], ut[4], du[4], dx[4];
 #pragma unroll
@@ -474,7 +498,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const floa
   T* sDAt = reinterpret_cast<T*>(smem + L::cDAt);
   T* sBL = reinterpret_cast<T*>(smem + L::cBL);
   T* sBLt = reinterpret_cast<T*>(smem + L::cBLt);
-  stage_rows<E, DV>(doh, t0, nrow, sDO, LV, nullptr, 0, tid);
+  stage_rows<E, DV>(doh, DV, t0, nrow, sDO, LV, nullptr, 0, tid);
   for (int i = tid; i < kC * kC; i += kThreads) {  // tiles above the diagonal stay zero
     const int r = i >> 6, cc = i & 63;
     if ((cc >> 4) > (r >> 4)) {
@@ -518,7 +542,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const floa
   // ---- phase D: each wave owns output tiles id = wave + 4 n of the 4 x NKT grid ----
   T* sKt = reinterpret_cast<T*>(smem + L::dKt);
   T* sQt = reinterpret_cast<T*>(smem + L::dQt);
-  stage_rows<E, DK>(kh, t0, nrow, nullptr, 0, sKt, LKT, tid);
+  stage_rows<E, DK>(kh, DK, t0, nrow, nullptr, 0, sKt, LKT, tid);
   __syncthreads();
   constexpr int NOWN = NKT;  // 4 * NKT tiles over 4 waves
   floatx4 gq[NOWN], gk[NOWN];
@@ -531,7 +555,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const floa
     gk[n] = x;
   }
   __syncthreads();  // bL is dead: Q^T goes in its place
-  stage_rows<E, DK>(qh, t0, nrow, nullptr, 0, sQt, LKT, tid);
+  stage_rows<E, DK>(qh, DK, t0, nrow, nullptr, 0, sQt, LKT, tid);
   __syncthreads();
 #pragma unroll
   for (int n = 0; n < NOWN; ++n) {
@@ -543,10 +567,25 @@ __global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const floa
   // ---- phase E ----
   T* sS = reinterpret_cast<T*>(smem + L::eS);
   T* sDS = reinterpret_cast<T*>(smem + L::eDS);
-  for (int i = tid; i < DK * DV; i += kThreads) {
-    const int r = i / DV, d = i - r * DV;
-    sS[r * LS + d] = E::cvt(S[i]);
-    sDS[r * LS + d] = E::cvt(dSn[i]);
+  {  // S and dSn rows, fp32 -> operand type, 16-byte loads issued first
+    constexpr int NV4 = DK * DV / 4, NPT = NV4 / kThreads > 0 ? NV4 / kThreads : 1;
+    float4 bs[NPT], bd[NPT];
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      const int i = min(tid + kThreads * j, NV4 - 1);
+      bs[j] = reinterpret_cast<const float4*>(S)[i];
+      bd[j] = reinterpret_cast<const float4*>(dSn)[i];
+    }
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      const int i = tid + kThreads * j;
+      if (i >= NV4) continue;
+      const int r = (4 * i) / DV, d = (4 * i) % DV;
+      T* ps = sS + r * LS + d;
+      T* pd = sDS + r * LS + d;
+      ps[0] = E::cvt(bs[j].x); ps[1] = E::cvt(bs[j].y); ps[2] = E::cvt(bs[j].z); ps[3] = E::cvt(bs[j].w);
+      pd[0] = E::cvt(bd[j].x); pd[1] = E::cvt(bd[j].y); pd[2] = E::cvt(bd[j].z); pd[3] = E::cvt(bd[j].w);
+    }
   }
   __syncthreads();
   T* dqo = reinterpret_cast<T*>(a.dq) + ((size_t)bh * Tn + t0) * DK;
@@ -632,9 +671,17 @@ __global__ __launch_bounds__(256) void zero_state(float* __restrict__ p, size_t 
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0.f;
 }
 
-size_t delta_backward_workspace_bytes(const BackwardArgs& a) {
+// The pipelined forward kernel (bf16, dk = 128, dv % 32 == 0) writes an
+// output and a final state it does not skip; they go to scratch at the end
+// of the workspace (the final state where a copy of S0 was put).
+bool pass1_pipelined(int bf16, const BackwardArgs& a) { return bf16 && a.dk_ == 128 && a.dv_ % 32 == 0; }
+
+size_t delta_backward_workspace_bytes(int bf16, const BackwardArgs& a) {
   const size_t nchunks = (size_t)a.B * a.H * ((a.T + kC - 1) / kC);
-  return 2 * nchunks * a.dk_ * a.dv_ * sizeof(float);
+  size_t n = 2 * nchunks * a.dk_ * a.dv_ * sizeof(float);
+  if (pass1_pipelined(bf16, a))
+    n += (size_t)a.B * a.H * a.dk_ * a.dv_ * sizeof(float) + (size_t)a.B * a.H * a.T * a.dv_ * sizeof(bf16_t);
+  return n;
 }
 
 }  // namespace
@@ -648,12 +695,13 @@ hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, hipStream_t st
     hipLaunchKernelGGL(zero_state, dim3((unsigned)blocks), dim3(256), 0, st, a.dS0, n);
     return hipGetLastError();
   }
-  // pass 1: the state entering every chunk, from the generic forward kernel
+  // pass 1: the state entering every chunk, from a forward kernel
   void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, delta_backward_workspace_bytes(a), st);
+  hipError_t e = hipMallocAsync(&ws, delta_backward_workspace_bytes(bf16, a), st);
   if (e != hipSuccess) return e;
+  const size_t nst = (size_t)a.B * a.H * ((a.T + kC - 1) / kC) * a.dk_ * a.dv_;
   float* Sc = reinterpret_cast<float*>(ws);
-  float* dSc = Sc + (size_t)a.B * a.H * ((a.T + kC - 1) / kC) * a.dk_ * a.dv_;
+  float* dSc = Sc + nst;
   PrefillArgs f{};
   f.q = a.q;
   f.k = a.k;
@@ -666,7 +714,18 @@ hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, hipStream_t st
   f.dv = a.dv_;
   f.use_init = a.S0 != nullptr;
   f.Sc = Sc;
-  e = launch_prefill_generic(PF_DELTA, bf16, a.dk_, f, st);
+  if (pass1_pipelined(bf16, a)) {
+    float* s_scratch = dSc + nst;  // the final state lands here
+    bf16_t* o_scratch = reinterpret_cast<bf16_t*>(s_scratch + (size_t)a.B * a.H * a.dk_ * a.dv_);
+    if (a.S0)
+      e = hipMemcpyAsync(s_scratch, a.S0, (size_t)a.B * a.H * a.dk_ * a.dv_ * sizeof(float),
+                         hipMemcpyDeviceToDevice, st);
+    f.S = s_scratch;
+    f.o = o_scratch;
+    if (e == hipSuccess) e = launch_prefill_pipe(f, nullptr, st);
+  } else {
+    e = launch_prefill_generic(PF_DELTA, bf16, a.dk_, f, st);
+  }
   // passes 2 and 3
   if (e == hipSuccess) e = bf16 ? launch_backward_e<BF16>(a, Sc, dSc, st) : launch_backward_e<F32>(a, Sc, dSc, st);
   const hipError_t fr = hipFreeAsync(ws, st);

@@ -149,6 +149,7 @@ struct PipeArgs {
   float* S;
   int T, dv, use_init;
   int Tq;              // rows per head of q, k, k^: T, or T rounded up to 64 (gated)
+  float* Sc;           // if set: the state entering every chunk, [B*H][nch][dk][dv]
 };
 
 // Loads.  Each tile-loader wave owns whole tiles (Q, K, and, gated, K^) and
@@ -181,7 +182,8 @@ struct LoadPlan {
   }
 };
 
-template <int GM, int DVS>
+// CAP: also write the state entering every chunk to a.Sc (backward pass).
+template <int GM, int DVS, bool CAP = false>
 __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
   constexpr bool GATED = GM == 1;  // per key channel, operands from the pre-pass
   constexpr bool TOKG = GM == 2;   // one decay per token
@@ -374,6 +376,15 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
         [&](const int x, auto parity) {
           constexpr int P = decltype(parity)::value;
           if (x < 0) return;
+          if constexpr (CAP) {  // the state entering chunk x, for the backward pass
+            // row perm32(16t + 4lg + i) = 8lg + 32(t / 2) + 4(t % 2) + i: one
+            // lane-dependent base, offsets uniform across the wave
+            float* scl = a.Sc + ((size_t)bh * nch + x) * kDK * dv + sl * kDVS + (size_t)(8 * lg) * dv + col;
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) scl[(size_t)(32 * (t >> 1) + 4 * (t & 1) + i) * dv] = st[t][i];
+          }
           // Y = K S and O = Q S (shared S fragments), X = beta (V - Y); the
           // fragments of k-step kb+1 are loaded while kb computes.
           floatx4 y[4];
@@ -781,7 +792,7 @@ size_t gated_pipe_workspace_bytes(const PrefillArgs& a) {
 
 namespace {
 
-template <int GM>
+template <int GM, bool CAP = false>
 hipError_t launch_pipe_t(const PipeArgs& p, long bh, int dv, hipStream_t st) {
   // 32 value columns per workgroup, or 16 when 32-column slices would leave
   // compute units idle (few (batch, head) pairs, as with long sequences)
@@ -790,9 +801,9 @@ hipError_t launch_pipe_t(const PipeArgs& p, long bh, int dv, hipStream_t st) {
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
   if (bh * (dv / 32) < cus && dv % 16 == 0) {
-    hipLaunchKernelGGL((prefill_pipe<GM, 16>), dim3((unsigned)(bh * (dv / 16))), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((prefill_pipe<GM, 16, CAP>), dim3((unsigned)(bh * (dv / 16))), dim3(kThreads), 0, st, p);
   } else {
-    hipLaunchKernelGGL((prefill_pipe<GM, 32>), dim3((unsigned)(bh * (dv / 32))), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((prefill_pipe<GM, 32, CAP>), dim3((unsigned)(bh * (dv / 32))), dim3(kThreads), 0, st, p);
   }
   return hipGetLastError();
 }
@@ -810,12 +821,13 @@ hipError_t launch_prefill_pipe(const PrefillArgs& a, void* workspace, hipStream_
   p.dv = a.dv;
   p.use_init = a.use_init;
   p.Tq = a.T;
+  p.Sc = a.Sc;
   if (a.g == nullptr) {
     p.q = reinterpret_cast<const bf16_t*>(a.q);
     p.k = reinterpret_cast<const bf16_t*>(a.k);
     p.kh = nullptr;
     p.gc = nullptr;
-    return launch_pipe_t<0>(p, bh, a.dv, st);
+    return a.Sc ? launch_pipe_t<0, true>(p, bh, a.dv, st) : launch_pipe_t<0>(p, bh, a.dv, st);
   }
   const int nch = (a.T + kC - 1) / kC;
   const size_t n = (size_t)a.B * a.H * nch * kC * kDK;
