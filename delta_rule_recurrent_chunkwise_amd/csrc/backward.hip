@@ -126,6 +126,39 @@ __device__ __forceinline__ floatx4 accB(floatx4 acc, const EA* arow, const float
   else return mm_accB_f32(acc, reinterpret_cast<const float*>(arow), xt, nt, lane);
 }
 
+// acc += A X with A's row r (r = lane % 16 of the tile) read as column r of a
+// row-major matrix M (A[r][k] = M[k][r]): col = &M[0][r], ld = M's row
+// stride.  Same k order as mm_accB_bf16 / mm_accB_f32, so X is given as nt
+// accumulator tiles (nt even, or 1, for bf16).  Consecutive lanes read
+// consecutive addresses.
+template <bool kBf16, class EM>
+__device__ __forceinline__ floatx4 accB_col(floatx4 acc, const EM* col, int ld, const floatx4* xt, int nt, int lane) {
+  const int g = lane >> 4;
+  auto ldf = [&](int k) { return (float)(sizeof(EM) == 2 ? bf2f(*reinterpret_cast<const bf16_t*>(col + (size_t)k * ld))
+                                                        : *reinterpret_cast<const float*>(col + (size_t)k * ld)); };
+  if constexpr (kBf16) {
+    int t = 0;
+    for (; t + 1 < nt; t += 2) {
+      const int k0 = 16 * t + 4 * g, k1 = 16 * t + 16 + 4 * g;
+      const bf16x8 a = words_to_bf16x8(pack2(ldf(k0), ldf(k0 + 1)), pack2(ldf(k0 + 2), ldf(k0 + 3)),
+                                       pack2(ldf(k1), ldf(k1 + 1)), pack2(ldf(k1 + 2), ldf(k1 + 3)));
+      acc = mfma_k32(a, acc_pair_to_b(xt[t], xt[t + 1]), acc);
+    }
+    if (t < nt) {
+      const int k0 = 16 * t + 4 * g;
+      acc = mfma_k16(words_to_shortx4(pack2(ldf(k0), ldf(k0 + 1)), pack2(ldf(k0 + 2), ldf(k0 + 3))),
+                     acc_to_b16(xt[t]), acc);
+    }
+  } else {
+    for (int t = 0; t < nt; ++t) {
+      const int k0 = 16 * t + 4 * g;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = mfma_f32(ldf(k0 + e), xt[t][e], acc);
+    }
+  }
+  return acc;
+}
+
 template <class E>
 union Vec16U {
   Vec16 v;
@@ -137,6 +170,9 @@ union Vec16U {
 // zeros: row-major (dst[r][d], stride ld, 16-byte aligned rows) and/or
 // transposed (dstT[d][r], stride ldT).  Every thread first issues all of its
 // 16-byte loads (rows past the end re-read the last row), then stores.
+// With a transposed copy, consecutive lanes take consecutive rows, so the
+// transposed stores of one instruction are consecutive addresses (no bank
+// conflicts); otherwise consecutive lanes take consecutive vectors of a row.
 template <class E, int D>
 __device__ __forceinline__ void stage_rows(const typename E::T* src, int sld, int t0, int nrow, typename E::T* dst,
                                            int ld, typename E::T* dstT, int ldT, int tid) {
@@ -144,18 +180,20 @@ __device__ __forceinline__ void stage_rows(const typename E::T* src, int sld, in
   constexpr int VPR = D / KV;  // 16-byte vectors per row
   constexpr int NV = kC * VPR;
   constexpr int NPT = (NV + kThreads - 1) / kThreads;
+  const bool rows_fast = dstT != nullptr;
   Vec16U<E> buf[NPT];
 #pragma unroll
   for (int j = 0; j < NPT; ++j) {
     const int i = min(tid + kThreads * j, NV - 1);
-    const int r = min(i / VPR, nrow - 1);
-    buf[j].v = *reinterpret_cast<const Vec16*>(src + (size_t)(t0 + r) * sld + (i % VPR) * KV);
+    const int r = min(rows_fast ? i % kC : i / VPR, nrow - 1);
+    const int vc = rows_fast ? i / kC : i % VPR;
+    buf[j].v = *reinterpret_cast<const Vec16*>(src + (size_t)(t0 + r) * sld + vc * KV);
   }
 #pragma unroll
   for (int j = 0; j < NPT; ++j) {
     const int i = tid + kThreads * j;
     if (NV % kThreads != 0 && i >= NV) continue;
-    const int r = i / VPR, d = (i % VPR) * KV;
+    const int r = rows_fast ? i % kC : i / VPR, d = (rows_fast ? i / kC : i % VPR) * KV;
     if (r >= nrow) buf[j].v = Vec16{};
     if (dst) *reinterpret_cast<Vec16*>(dst + r * ld + d) = buf[j].v;
     if (dstT) {
@@ -165,12 +203,46 @@ __device__ __forceinline__ void stage_rows(const typename E::T* src, int sld, in
   }
 }
 
+// The same staging split in two, so that the loads of the next chunk can be
+// in flight while the current one is computed: load() issues the 16-byte
+// loads into registers, store() writes them to LDS.  RF: rows-fast lane
+// mapping (for a transposed copy), as in stage_rows.
+template <class E, int D, bool RF>
+struct RowTile {
+  typedef typename E::T T;
+  static constexpr int KV = E::kVec, VPR = D / KV, NV = kC * VPR, NPT = (NV + kThreads - 1) / kThreads;
+  Vec16U<E> buf[NPT];
+  __device__ __forceinline__ void load(const T* src, int sld, int t0, int nrow, int tid) {
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      const int i = min(tid + kThreads * j, NV - 1);
+      const int r = min(RF ? i % kC : i / VPR, nrow - 1);
+      buf[j].v = *reinterpret_cast<const Vec16*>(src + (size_t)(t0 + r) * sld + (RF ? i / kC : i % VPR) * KV);
+    }
+  }
+  __device__ __forceinline__ void store(int nrow, T* dst, int ld, T* dstT, int ldT, int tid) {
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      const int i = tid + kThreads * j;
+      if (NV % kThreads != 0 && i >= NV) continue;
+      const int r = RF ? i % kC : i / VPR, d = (RF ? i / kC : i % VPR) * KV;
+      Vec16U<E> x = buf[j];
+      if (r >= nrow) x.v = Vec16{};
+      if (dst) *reinterpret_cast<Vec16*>(dst + r * ld + d) = x.v;
+      if (dstT) {
+#pragma unroll
+        for (int e = 0; e < KV; ++e) dstT[(d + e) * ldT + r] = x.e[e];
+      }
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Pass 2: the reverse chain.  One workgroup per (batch, head, DVS value
 // columns); NCW = DVS / 16 chain waves hold dS[:, 16 columns] as accumulator
 // tiles.  Per chunk (last to first): write dSn, stage Q, K, dO, beta; the
-// other waves form tril(Q K^T) (stored transposed) and L; all form T and its
-// transpose; the chain forms du = A^T dO + K dSn, dX = T^T du and
+// other waves form tril(Q K^T) and L; all form T; the chain forms
+// du = A^T dO + K dSn, dX = T^T du (A and T read by columns) and
 // dS = dSn + Q^T dO - K^T diag(beta) dX.
 // ---------------------------------------------------------------------------
 template <int DK, class E, int DVS>
@@ -178,7 +250,7 @@ struct ChainLayout {
   typedef typename E::T T;
   static constexpr int PAD = 16 / (int)sizeof(T);
   static constexpr int LQ = DK + PAD;   // rows of Q, K
-  static constexpr int LKT = kC + PAD;  // rows of Q^T, K^T, dO^T, A^T
+  static constexpr int LKT = kC + PAD;  // rows of Q^T, K^T, dO^T, A
   static constexpr int oQ = 0;
   static constexpr int oK = oQ + kC * LQ * (int)sizeof(T);
   static constexpr int oQt = oK + kC * LQ * (int)sizeof(T);
@@ -186,8 +258,7 @@ struct ChainLayout {
   static constexpr int oDOt = oKt + DK * LKT * (int)sizeof(T);
   static constexpr int oAt = oDOt + DVS * LKT * (int)sizeof(T);
   static constexpr int oTL = oAt + kC * LKT * (int)sizeof(T);
-  static constexpr int oTt = oTL + kC * LTL * 4;
-  static constexpr int oB = oTt + kC * LTL * 4;
+  static constexpr int oB = oTL + kC * LTL * 4;
   static constexpr int total = oB + kC * 4;
 };
 
@@ -204,9 +275,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chain(BackwardArgs a, float* __r
   T* sQt = reinterpret_cast<T*>(smem + L::oQt);
   T* sKt = reinterpret_cast<T*>(smem + L::oKt);
   T* sDOt = reinterpret_cast<T*>(smem + L::oDOt);
-  T* sAt = reinterpret_cast<T*>(smem + L::oAt);
+  T* sA = reinterpret_cast<T*>(smem + L::oAt);  // tril(Q K^T), row-major
   float* sTL = reinterpret_cast<float*>(smem + L::oTL);
-  float* sTt = reinterpret_cast<float*>(smem + L::oTt);
   float* sB = reinterpret_cast<float*>(smem + L::oB);
 
   const int dv = a.dv_;
@@ -232,6 +302,19 @@ __global__ __launch_bounds__(kThreads) void bwd_chain(BackwardArgs a, float* __r
     }
   }
 
+  // chunk c's Q, K, dO slice and beta are loaded into registers while chunk
+  // c + 1 is computed
+  RowTile<E, DK, true> pq, pk;
+  RowTile<E, DVS, true> pdo;
+  float pb = 0.f;
+  auto prefetch = [&](int cc) {
+    const int t0 = cc * kC, nrow = min(kC, Tn - t0);
+    pq.load(qh, DK, t0, nrow, tid);
+    pk.load(kh, DK, t0, nrow, tid);
+    pdo.load(doh, dv, t0, nrow, tid);
+    if (tid < kC) pb = E::tof(bth[t0 + min(tid, nrow - 1)]);
+  };
+  prefetch(nch - 1);
   for (int c = nch - 1; c >= 0; --c) {
     const int t0 = c * kC, nrow = min(kC, Tn - t0);
     if (chain) {  // dSn of chunk c
@@ -242,10 +325,11 @@ __global__ __launch_bounds__(kThreads) void bwd_chain(BackwardArgs a, float* __r
         for (int i = 0; i < 4; ++i) out[(size_t)(16 * kt + 4 * lg + i) * dv + col] = st[kt][i];
     }
     __syncthreads();  // the previous chunk's readers are done
-    stage_rows<E, DK>(qh, DK, t0, nrow, sQ, LQ, sQt, LKT, tid);
-    stage_rows<E, DK>(kh, DK, t0, nrow, sK, LQ, sKt, LKT, tid);
-    stage_rows<E, DVS>(doh, dv, t0, nrow, nullptr, 0, sDOt, LKT, tid);  // the dO slice, transposed
-    if (tid < kC) sB[tid] = tid < nrow ? E::tof(bth[t0 + tid]) : 0.f;
+    pq.store(nrow, sQ, LQ, sQt, LKT, tid);
+    pk.store(nrow, sK, LQ, sKt, LKT, tid);
+    pdo.store(nrow, nullptr, 0, sDOt, LKT, tid);  // the dO slice, transposed
+    if (tid < kC) sB[tid] = tid < nrow ? pb : 0.f;
+    prefetch(c > 0 ? c - 1 : 0);  // issued on every trip (the last one re-reads chunk 0)
     __syncthreads();
 
     floatx4 kds[4];
@@ -253,9 +337,9 @@ __global__ __launch_bounds__(kThreads) void bwd_chain(BackwardArgs a, float* __r
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) kds[mt] = accB<kBf16>(zero4(), sK + (16 * mt + lc) * LQ, st, NKT, lane);
     } else {
-      // jobs 0..9: tiles (i, j <= i) of tril(Q K^T), stored transposed;
-      // jobs 10..19: the same tiles of K K^T -> L (strictly lower, rows
-      // scaled by beta), stored transposed in T's upper triangle
+      // jobs 0..9: tiles (i, j <= i) of tril(Q K^T); jobs 10..19: the same
+      // tiles of K K^T -> L (strictly lower, rows scaled by beta), stored
+      // transposed in T's upper triangle
       for (int jb = wave - NCW; jb < 20; jb += kWaves - NCW) {
         const bool isA = jb < 10;
         const int t = isA ? jb : jb - 10;
@@ -267,23 +351,18 @@ __global__ __launch_bounds__(kThreads) void bwd_chain(BackwardArgs a, float* __r
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * ti + 4 * lg + i;
-          if (isA) sAt[cc * LKT + r] = E::cvt(cc <= r ? acc[i] : 0.f);
+          if (isA) sA[r * LKT + cc] = E::cvt(cc <= r ? acc[i] : 0.f);
           else if (cc < r) sTL[cc * LTL + r] = sB[r] * acc[i];
         }
       }
-      // A^T above the diagonal tiles (ti < tj) is never written: zero it
+      // tiles above the diagonal (ti < tj) are never written: zero them
       for (int i = tid - 64 * NCW; i >= 0 && i < kC * kC; i += kThreads - 64 * NCW) {
         const int r = i >> 6, cc = i & 63;
-        if ((cc >> 4) > (r >> 4)) sAt[cc * LKT + r] = E::cvt(0.f);
+        if ((cc >> 4) > (r >> 4)) sA[r * LKT + cc] = E::cvt(0.f);
       }
     }
     __syncthreads();
     form_T<kBf16>(sTL, tid, wave, lane);
-    for (int i = tid; i < kC * kC; i += kThreads) {
-      const int r = i >> 6, cc = i & 63;
-      sTt[cc * LTL + r] = sTL[r * LTL + cc];
-    }
-    __syncthreads();
     if (chain) {
       floatx4 dOt[4], du[4], dx[4];
 #pragma unroll
@@ -294,10 +373,10 @@ __global__ __launch_bounds__(kThreads) void bwd_chain(BackwardArgs a, float* __r
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)  // a fresh accumulator: K dSn may come from the 16-deep opcode
-        du[mt] = kds[mt] + accB<kBf16>(zero4(), sAt + (16 * mt + lc) * LKT, dOt, 4, lane);
+        du[mt] = kds[mt] + accB_col<kBf16>(zero4(), sA + 16 * mt + lc, LKT, dOt, 4, lane);  // A^T dO
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        dx[mt] = accB<kBf16>(zero4(), sTt + (16 * mt + lc) * LTL, du, 4, lane);
+        dx[mt] = accB_col<kBf16>(zero4(), sTL + 16 * mt + lc, LTL, du, 4, lane);  // T^T du
 #pragma unroll
         for (int i = 0; i < 4; ++i) dx[mt][i] *= -sB[16 * mt + 4 * lg + i];  // -diag(beta) dX
       }
@@ -320,7 +399,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chain(BackwardArgs a, float* __r
 // ---------------------------------------------------------------------------
 // Pass 3: one workgroup per (batch, head, chunk).  Phases (barriers between),
 // with LDS regions reused as operands die:
-//   A  stage Q, K; tril(Q K^T) (transposed) and K K^T -> L, T, T^T
+//   A  stage Q, K; tril(Q K^T) and K K^T -> L, T (A and T are read by
+//      columns where their transposes are needed)
 //   B  per 16-column slice of dv (one wave each): X, u, du, dX from S and
 //      dSn held as accumulator tiles; write dV; rowsum((V - K S) * dX) into
 //      dbeta; u and dX rows to LDS
@@ -339,7 +419,7 @@ struct GradLayout {
   static constexpr int LQ = DK + PAD;   // rows of Q, K
   static constexpr int LV = DV + PAD;   // rows of u, dX, dO
   static constexpr int LS = DV + PAD;   // rows of S, dSn (key rows)
-  static constexpr int LKT = kC + PAD;  // rows of A^T, dA, bL and their transposes, K^T, Q^T
+  static constexpr int LKT = kC + PAD;  // rows of A, dA, bL and their transposes, K^T, Q^T
   static constexpr int ROWQ = kC * LQ * ES, ROWV = kC * LV * ES, TRI = kC * LKT * ES;
   static constexpr int TQ = DK * LKT * ES, ST = DK * LS * ES, FT = kC * LTL * 4;
   // persistent: u, dX, K K^T (fp32), beta, dbeta
@@ -350,8 +430,8 @@ struct GradLayout {
   static constexpr int oDB = oB + kC * 4;
   static constexpr int oW = oDB + kC * 4;  // phase-dependent work area
   // phases A, B
-  static constexpr int aQ = oW, aK = aQ + ROWQ, aAt = aK + ROWQ, aTL = aAt + TRI, aTt = aTL + FT;
-  static constexpr int endAB = aTt + FT;
+  static constexpr int aQ = oW, aK = aQ + ROWQ, aAt = aK + ROWQ, aTL = aAt + TRI;
+  static constexpr int endAB = aTL + FT;
   // phases C, D: dO, dA, dA^T, bL, bL^T, K^T; then Q^T where bL was
   static constexpr int cDO = oW, cDA = cDO + ROWV, cDAt = cDA + TRI, cBL = cDAt + TRI, cBLt = cBL + TRI;
   static constexpr int dKt = cBLt + TRI, dQt = cBL;
@@ -395,9 +475,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const floa
   // ---- phase A ----
   T* sQ = reinterpret_cast<T*>(smem + L::aQ);
   T* sK = reinterpret_cast<T*>(smem + L::aK);
-  T* sAt = reinterpret_cast<T*>(smem + L::aAt);
+  T* sA = reinterpret_cast<T*>(smem + L::aAt);  // tril(Q K^T), row-major
   float* sTL = reinterpret_cast<float*>(smem + L::aTL);
-  float* sTt = reinterpret_cast<float*>(smem + L::aTt);
   stage_rows<E, DK>(qh, DK, t0, nrow, sQ, LQ, nullptr, 0, tid);
   stage_rows<E, DK>(kh, DK, t0, nrow, sK, LQ, nullptr, 0, tid);
   if (tid < kC) {
@@ -406,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const floa
   }
   for (int i = tid; i < kC * kC; i += kThreads) {  // tiles above the diagonal stay zero
     const int r = i >> 6, cc = i & 63;
-    if ((cc >> 4) > (r >> 4)) sAt[cc * LKT + r] = E::cvt(0.f);
+    if ((cc >> 4) > (r >> 4)) sA[r * LKT + cc] = E::cvt(0.f);
   }
   __syncthreads();
   for (int jb = wave; jb < 20; jb += kWaves) {
@@ -421,7 +500,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const floa
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * ti + 4 * lg + i;
       if (isA) {
-        sAt[cc * LKT + r] = E::cvt(cc <= r ? acc[i] : 0.f);
+        sA[r * LKT + cc] = E::cvt(cc <= r ? acc[i] : 0.f);
       } else if (cc < r) {
         sTL[cc * LTL + r] = sB[r] * acc[i];
         sKK[r * LTL + cc] = acc[i];
@@ -430,11 +509,6 @@ __global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const floa
   }
   __syncthreads();
   form_T<kBf16>(sTL, tid, wave, lane);
-  for (int i = tid; i < kC * kC; i += kThreads) {
-    const int r = i >> 6, cc = i & 63;
-    sTt[cc * LTL + r] = sTL[r * LTL + cc];
-  }
-  __syncthreads();
 
   // ---- phase B: 16-column slices of dv, one per wave at a time ----
   for (int s = wave; s < NVT; s += kWaves) {
@@ -470,13 +544,13 @@ __global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const floa
     for (int mt = 0; mt < 4; ++mt) {
       if constexpr (kBf16) ut[mt] = accB<kBf16>(zero4(), sTL + (16 * mt + lc) * LTL, xx, (mt | 1) + 1, lane);
       else ut[mt] = accB<kBf16>(zero4(), sTL + (16 * mt + lc) * LTL, xx, mt + 1, lane);
-      const floatx4 d1 = accB<kBf16>(zero4(), sAt + (16 * mt + lc) * LKT, dOt, 4, lane);
+      const floatx4 d1 = accB_col<kBf16>(zero4(), sA + 16 * mt + lc, LKT, dOt, 4, lane);  // A^T dO
       const floatx4 d2 = accB<kBf16>(zero4(), sK + (16 * mt + lc) * LQ, dSv, NKT, lane);
       du[mt] = d1 + d2;
     }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      dx[mt] = accB<kBf16>(zero4(), sTt + (16 * mt + lc) * LTL, du, 4, lane);
+      dx[mt] = accB_col<kBf16>(zero4(), sTL + 16 * mt + lc, LTL, du, 4, lane);  // T^T du
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * mt + 4 * lg + i;
