@@ -20,6 +20,10 @@ Functions (both follow the article "From GPT-2 to Kimi K3, explained"):
 ``delta_backward``   reverse-mode gradient of the (ungated) delta rule, token
                      by token: dq, dk, dv, dbeta and dS0 for the loss
                      sum do . o + sum dS_T * S_T.
+``qk_prologue``      section "DeltaNet (Fast Weight Programmers)", the layer's
+                     q, k = normalize(silu(.)) (and an optional scale).
+``beta_sigmoid``     the same layer's beta = sigmoid(logits), broadcast over
+                     heads when the logits have one head.
 
 Inputs may be torch CPU tensors (float32, bfloat16, float64) or numpy arrays
 (float32, float64); all inputs of one call share a dtype.  They are read in
@@ -63,6 +67,10 @@ def _bind(lib):
     lib.orc_delta_backward.argtypes = [i, i, i, i, i, d, d, d, d, i, d, d, d,
                                        d, d, d, d, d, i]
     lib.orc_delta_backward.restype = i
+    lib.orc_qk_prologue.argtypes = [ctypes.c_long, i, d, i, i, ctypes.c_double, d]
+    lib.orc_qk_prologue.restype = i
+    lib.orc_beta_sigmoid.argtypes = [i, i, i, i, d, i, d]
+    lib.orc_beta_sigmoid.restype = i
     lib.orc_max_threads.argtypes = []
     lib.orc_max_threads.restype = i
     return lib
@@ -232,3 +240,27 @@ def delta_backward(q, k, v, beta, dO, S0=None, dST=None, nthreads: int = 0, lib=
     if rc != 0:
         raise MemoryError("oracle allocation failed")
     return dq, dkk, dvv, db, dS0
+
+
+def qk_prologue(x, apply_silu: bool = True, scale: float = 1.0, lib=None):
+    """scale * L2-normalise(silu(x)) over the last dimension (silu skipped
+    when apply_silu is False).  x [..., d]; returns float64 of x's shape."""
+    lib = lib or load()
+    buf = _as_buffer(x)
+    d = x.shape[-1]
+    rows = int(np.prod(x.shape[:-1]))
+    out = np.empty(tuple(x.shape), np.float64)
+    lib.orc_qk_prologue(rows, d, buf[1], buf[2], int(bool(apply_silu)), float(scale),
+                        out.ctypes.data)
+    return out
+
+
+def beta_sigmoid(logits, H: int, lib=None):
+    """sigmoid(logits) for logits [B, Hb, T] with Hb = 1 (shared by all H
+    heads) or Hb = H; returns float64 [B, H, T]."""
+    lib = lib or load()
+    buf = _as_buffer(logits)
+    B, Hb, T = logits.shape
+    out = np.empty((B, H, T), np.float64)
+    lib.orc_beta_sigmoid(B, Hb, H, T, buf[1], buf[2], out.ctypes.data)
+    return out

@@ -437,3 +437,47 @@ int orc_delta_backward(int B, int H, int T, int dk, int dv,
     }
     return fail ? -1 : 0;
 }
+
+/*
+ * The steps just before the delta rule in the layer of section "DeltaNet
+ * (Fast Weight Programmers)": q and k are each passed through silu and then
+ * L2-normalised over the head dimension (torch's F.normalize: x divided by
+ * max(|x|_2, 1e-12)), and beta is the sigmoid of its logits, one per token,
+ * shared by every head when the logits have a single head.
+ *   orc_qk_prologue: x [rows, d] -> out = scale * n(s(x)), s = silu if
+ *                    apply_silu else identity, n = the L2 normalisation.
+ *   orc_beta_sigmoid: logits [B, Hb, T] (Hb = 1 or H) -> beta [B, H, T].
+ */
+int orc_qk_prologue(long rows, int d, const void *x, int dt, int apply_silu,
+                    double scale, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < rows; r++) {
+        double ss = 0.0;
+        for (int i = 0; i < d; i++) {
+            const double xi = rd(x, (size_t)r * d + i, dt);
+            const double y = apply_silu ? xi / (1.0 + exp(-xi)) : xi;
+            out[(size_t)r * d + i] = y;
+            ss += y * y;
+        }
+        double nrm = sqrt(ss);
+        if (nrm < 1e-12)
+            nrm = 1e-12;
+        for (int i = 0; i < d; i++)
+            out[(size_t)r * d + i] = scale * out[(size_t)r * d + i] / nrm;
+    }
+    return 0;
+}
+
+int orc_beta_sigmoid(int B, int Hb, int H, int T, const void *logits, int dt,
+                     double *beta)
+{
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < H; h++)
+            for (int t = 0; t < T; t++) {
+                const int hs = Hb == 1 ? 0 : h;
+                const double z = rd(logits, ((size_t)b * Hb + hs) * T + t, dt);
+                beta[((size_t)b * H + h) * T + t] = 1.0 / (1.0 + exp(-z));
+            }
+    return 0;
+}

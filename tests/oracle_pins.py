@@ -515,6 +515,47 @@ def pin_delta_backward_autograd(lib):
 
 
 # --------------------------------------------------------------------------
+# The layer's prologue: q, k = normalize(silu(.)), beta = sigmoid(.)
+# --------------------------------------------------------------------------
+
+def pin_prologue_facts(lib):
+    """Rows come out with norm `scale` and point along silu(x): silu is
+    x * sigmoid(x), so silu(0) = 0, silu(x) -> x for large x and -> 0 for
+    very negative x, and the ratio of two silu values at a, b is the ratio
+    a s(a) / (b s(b)); a zero row stays zero (the 1e-12 floor).  sigmoid(0)
+    = 1/2 and sigmoid(-z) = 1 - sigmoid(z); one-head logits give every head
+    the same beta."""
+    x = np.array([[0.0, 40.0, -40.0, 1.0], [0.5, -0.5, 2.0, -3.0], [0.0, 0.0, 0.0, 0.0]])
+    out = oracle.qk_prologue(x, True, 2.5, lib=lib)
+    _close(np.linalg.norm(out[:2], axis=1), np.array([2.5, 2.5]), tol=1e-14, what="row norms")
+    _close(out[2], np.zeros(4), tol=0, what="zero row")
+    r0 = out[0] / 2.5 * np.linalg.norm([0.0, 40.0, 0.0, 1.0 / (1.0 + np.exp(-1.0))])
+    _close(r0[[0, 2]], np.zeros(2), tol=1e-15, what="silu(0), silu(-40)")
+    _close(r0[1], 40.0, tol=1e-14, what="silu(40)")
+    sg = lambda z: 1.0 / (1.0 + np.exp(-z))  # noqa: E731  (the logistic function's definition)
+    ratio = out[1, 0] / out[1, 2]
+    _close(ratio, (0.5 * sg(0.5)) / (2.0 * sg(2.0)), tol=1e-14, what="silu ratio")
+    plain = oracle.qk_prologue(x[:2], False, 1.0, lib=lib)
+    _close(plain, x[:2] / np.linalg.norm(x[:2], axis=1, keepdims=True), tol=1e-15, what="no silu")
+    lg = np.array([[[0.0, 1.5, -1.5, 30.0]]])
+    be = oracle.beta_sigmoid(lg, 3, lib=lib)
+    _close(be[0, 0, 0], 0.5, tol=0, what="sigmoid(0)")
+    _close(be[0, 0, 1] + be[0, 0, 2], 1.0, tol=1e-15, what="sigmoid symmetry")
+    _close(be[0, 1], be[0, 0], tol=0, what="head broadcast")
+    _close(be[0, 2], be[0, 0], tol=0, what="head broadcast")
+    lg3 = np.random.default_rng(40).standard_normal((2, 3, 5))
+    be3 = oracle.beta_sigmoid(lg3, 3, lib=lib)
+    _close(be3 + oracle.beta_sigmoid(-lg3, 3, lib=lib), np.ones_like(be3), tol=1e-15,
+           what="per-head symmetry")
+    # per-head logits: head h reads its own logit (sigmoid is increasing, and
+    # a zero logit gives exactly 1/2 in the head that holds it)
+    lgh = np.array([[[0.0, -2.0], [1.0, 0.0], [3.0, 2.0]]])
+    bh = oracle.beta_sigmoid(lgh, 3, lib=lib)
+    assert np.all(np.diff(bh[0], axis=0) > 0), "beta must follow each head's own logit"
+    _close(np.array([bh[0, 0, 0], bh[0, 1, 1]]), np.array([0.5, 0.5]), tol=0, what="own head")
+
+
+# --------------------------------------------------------------------------
 # Input handling and state carry
 # --------------------------------------------------------------------------
 
@@ -599,6 +640,7 @@ ALL_PINS = [
     pin_gla_limits,
     pin_delta_backward_finite_differences,
     pin_delta_backward_autograd,
+    pin_prologue_facts,
     pin_stored_precision_widening,
     pin_state_carry,
 ]

@@ -73,6 +73,12 @@ MUTANTS = {
     "bwd_state_gradient_sign": (
         "dS[(size_t)i * dv + j] -= b * kt[i] * du[j];", "dS[(size_t)i * dv + j] += b * kt[i] * du[j];"),
     "bwd_value_gradient_without_beta": ("dvv[v_row + j] = b * du[j];", "dvv[v_row + j] = du[j];"),
+    "prologue_silu_without_gate": (
+        "const double y = apply_silu ? xi / (1.0 + exp(-xi)) : xi;",
+        "const double y = apply_silu ? xi / (1.0 + exp(xi)) : xi;"),
+    "prologue_normalised_by_squared_norm": ("double nrm = sqrt(ss);", "double nrm = ss;"),
+    "beta_broadcast_wrong_head": (
+        "const int hs = Hb == 1 ? 0 : h;", "const int hs = Hb == 1 ? 0 : (h + 1) % Hb;"),
     "gla_read_with_key": (
         "const double qi = rd(q, qk_row + i, dt);", "const double qi = rd(k, qk_row + i, dt);"),
     "bf16_widening_wrong_shift": (
