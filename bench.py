@@ -458,7 +458,31 @@ def bench_rows(la, workloads, torch, launches=20):
     del d, gi
     rows.update(bench_token_gated_rows(la, workloads, torch, launches))
     rows.update(bench_backward_row(la, workloads, torch))
+    rows.update(bench_prologue_row(la, workloads, torch))
     return rows
+
+
+def bench_prologue_row(la, workloads, torch, launches=20):
+    """The layer prologue (q, k = normalize(silu(.)), beta = sigmoid of one
+    logit per token) at the timed prefill workload's shape."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    w = workloads.WORKLOADS[2]
+    gen = workloads.generator(97)
+    q = torch.randn(w.B, w.H, w.T, w.dk, generator=gen).to(w.dtype).to(dev)
+    k = torch.randn(w.B, w.H, w.T, w.dk, generator=gen).to(w.dtype).to(dev)
+    lg = torch.randn(w.B, 1, w.T, generator=gen).to(w.dtype).to(dev)
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+
+    def run(_):
+        la.deltanet_prologue(q, k, lg, out=(qo, ko), stream=stream)
+
+    us, med = _time_launches(torch, stream, run, [None], launches)
+    th = w.B * w.H * w.T
+    per = th * 2 * 2 * w.dk * 2 + w.B * w.T * 2 + th * 2
+    name, r = _row("deltanet_prologue", f"deltanet_prologue B={w.B} H={w.H} T={w.T} dk={w.dk} "
+                   "bf16, beta shared by the heads", us, med, per)
+    return {name: r}
 
 
 def bench_backward_row(la, workloads, torch, launches=5):
@@ -686,7 +710,7 @@ def main():
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the other rows (LA prefill, gated prefill, LA/gated decode)")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "copy", "rows", "token-rows",
-                                       "backward-row"],
+                                       "backward-row", "prologue-row"],
                     default="all",
                     help="run one part only (for profiler runs)")
     ap.add_argument("--summarize", metavar="DIR",
@@ -723,6 +747,9 @@ def main():
         return
     if args.only == "backward-row":
         print(json.dumps(bench_backward_row(la, workloads, torch)))
+        return
+    if args.only == "prologue-row":
+        print(json.dumps(bench_prologue_row(la, workloads, torch)))
         return
     if args.only == "decode":
         wd, _, el = bench_decode(la, workloads, torch, args.decode_steps)

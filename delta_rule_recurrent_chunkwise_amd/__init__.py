@@ -19,7 +19,8 @@ import torch
 __all__ = [
     "la_prefill", "la_decode_step", "deltanet_prefill", "deltanet_decode_step",
     "gated_deltanet_prefill", "gated_deltanet_decode_step", "gla_prefill",
-    "gla_decode_step", "deltanet_prefill_backward", "la_strerror", "library", "LIB_PATH",
+    "gla_decode_step", "deltanet_prefill_backward", "deltanet_prologue", "la_strerror",
+    "library", "LIB_PATH",
     "EXPORTED_SYMBOLS",
     "LinAttnError",
 ]
@@ -28,7 +29,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblinattn.
 EXPORTED_SYMBOLS = ("la_prefill", "la_decode_step", "deltanet_prefill",
                     "deltanet_decode_step", "gated_deltanet_prefill",
                     "gated_deltanet_decode_step", "gla_prefill", "gla_decode_step",
-                    "deltanet_prefill_backward", "la_strerror")
+                    "deltanet_prefill_backward", "deltanet_prologue", "la_strerror")
 
 LA_DTYPE_F32, LA_DTYPE_BF16 = 0, 1
 _DTYPES = {torch.float32: LA_DTYPE_F32, torch.bfloat16: LA_DTYPE_BF16}
@@ -63,6 +64,7 @@ def library():
         lib.gla_prefill.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
         lib.gla_decode_step.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
         lib.deltanet_prefill_backward.argtypes = [P] * 12 + [I] * 6 + [P]
+        lib.deltanet_prologue.argtypes = [P] * 6 + [I] * 6 + [ctypes.c_float, I, P]
         for fn in EXPORTED_SYMBOLS[:-1]:
             getattr(lib, fn).restype = I
         lib.la_strerror.argtypes = [I]
@@ -314,3 +316,28 @@ def deltanet_prefill_backward(q, k, v, beta, dO, S0=None, dST=None, want_dS0=Fal
         _stream(dev, stream))
     _check("deltanet_prefill_backward", rc)
     return dq, dkk, dvv, db, dS0
+
+
+def deltanet_prologue(q, k, beta_logits=None, apply_silu=True, q_scale=1.0, out=None,
+                      stream=None):
+    """q, k [B,H,T,dk] -> (q_scale * normalize(silu(q)), normalize(silu(k)),
+    sigmoid(beta_logits) [B,H,T] or None); beta_logits [B,1,T] (shared by all
+    heads) or [B,H,T].  out = (q_out, k_out) may be given (they may be q, k)."""
+    B, H, T, dk = q.shape
+    dev, dtype = _inputs("deltanet_prologue", dict(q=q, k=k), dict(q=(B, H, T, dk), k=(B, H, T, dk)))
+    bh = 1
+    if beta_logits is not None:
+        if beta_logits.dim() != 3 or beta_logits.shape[0] != B or beta_logits.shape[2] != T:
+            raise ValueError("deltanet_prologue: beta_logits must be [B,1,T] or [B,H,T]")
+        bh = beta_logits.shape[1]
+        _inputs("deltanet_prologue", dict(q=q, beta_logits=beta_logits),
+                dict(q=(B, H, T, dk), beta_logits=(B, bh, T)))
+    qo, ko = out if out is not None else (torch.empty_like(q), torch.empty_like(k))
+    _out("deltanet_prologue", qo, (B, H, T, dk), dev, dtype)
+    _out("deltanet_prologue", ko, (B, H, T, dk), dev, dtype)
+    bo = torch.empty(B, H, T, device=dev, dtype=dtype) if beta_logits is not None else None
+    rc = library().deltanet_prologue(_ptr(q), _ptr(k), _ptr(beta_logits), _ptr(qo), _ptr(ko),
+                                     _ptr(bo), B, H, T, dk, bh, int(bool(apply_silu)),
+                                     float(q_scale), _DTYPES[dtype], _stream(dev, stream))
+    _check("deltanet_prologue", rc)
+    return qo, ko, bo

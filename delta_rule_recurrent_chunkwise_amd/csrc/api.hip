@@ -170,4 +170,19 @@ int deltanet_prefill_backward(const void* q, const void* k, const void* v, const
   return launch_rc(linattn::launch_delta_backward(dtype == LA_DTYPE_BF16, a, static_cast<hipStream_t>(stream)));
 }
 
+int deltanet_prologue(const void* q_in, const void* k_in, const void* beta_logits, void* q_out,
+                      void* k_out, void* beta_out, int B, int H, int T, int dk, int beta_heads,
+                      int apply_silu, float q_scale, int dtype, void* stream) {
+  if (T != 0 && (!q_in || !k_in || !q_out || !k_out)) return LA_ERR_NULL;
+  if (T != 0 && (beta_logits != nullptr) != (beta_out != nullptr)) return LA_ERR_NULL;
+  if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
+  if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, 1, true)) return LA_ERR_SHAPE;
+  if (beta_logits && beta_heads != 1 && beta_heads != H) return LA_ERR_SHAPE;
+  if (!dim_ok(dk)) return LA_ERR_UNSUPPORTED_DIM;
+  if (!aligned16(q_in) || !aligned16(k_in) || !aligned16(q_out) || !aligned16(k_out)) return LA_ERR_ALIGN;
+  linattn::PrologueArgs a{q_in, k_in, beta_logits, q_out, k_out, beta_out, B, H, T, dk,
+                          beta_logits ? beta_heads : H, apply_silu ? 1 : 0, q_scale};
+  return launch_rc(linattn::launch_prologue(dtype == LA_DTYPE_BF16, a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

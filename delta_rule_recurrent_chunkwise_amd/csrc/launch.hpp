@@ -64,6 +64,18 @@ struct BackwardArgs {
   int B, H, T, dk_, dv_;
 };
 hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, hipStream_t st);
+// The layer prologue (prologue.hip): see deltanet_prologue.
+struct PrologueArgs {
+  const void* q_in;
+  const void* k_in;
+  const void* beta_logits;  // [B, beta_heads, T] or NULL
+  void* q_out;
+  void* k_out;
+  void* beta_out;           // [B, H, T]
+  int B, H, T, dk, beta_heads, silu;
+  float q_scale;
+};
+hipError_t launch_prologue(int bf16, const PrologueArgs& a, hipStream_t st);
 // The software-pipelined delta-rule prefill for bf16, dk = 128, dv % 32 == 0:
 // plain (a.g == NULL, no workspace) or gated (needs a workspace of
 // gated_pipe_workspace_bytes(a) bytes).

@@ -230,6 +230,26 @@ int deltanet_prefill_backward(const void *q, const void *k, const void *v,
                               float *dS0, int B, int H, int T, int dk, int dv,
                               int dtype, void *stream);
 
+/*
+ * deltanet_prologue -- the steps just before the delta rule in the layer of
+ * section "DeltaNet (Fast Weight Programmers)":
+ *   q_out = q_scale * normalize(silu(q_in)),  k_out = normalize(silu(k_in)),
+ *   beta_out = sigmoid(beta_logits),
+ * with normalize(x) = x / max(|x|_2, 1e-12) over the head dimension (torch's
+ * F.normalize) and silu(x) = x sigmoid(x), skipped when apply_silu = 0.
+ * q_in, k_in, q_out, k_out [B,H,T,dk] (dtype; 16-byte aligned; outputs may
+ * alias their inputs).  beta_logits [B,beta_heads,T] with beta_heads = 1 (one
+ * logit per token shared by every head, the article's [b,1,t,1] view) or H;
+ * beta_out [B,H,T]; both NULL to skip beta.  q_scale = 1 for the article's
+ * layer (a 1/sqrt(dk) attention-style scale is the caller's choice).  The
+ * outputs feed deltanet_prefill / deltanet_decode_step directly.
+ */
+int deltanet_prologue(const void *q_in, const void *k_in,
+                      const void *beta_logits, void *q_out, void *k_out,
+                      void *beta_out, int B, int H, int T, int dk,
+                      int beta_heads, int apply_silu, float q_scale, int dtype,
+                      void *stream);
+
 /* la_strerror -- a static, NUL-terminated description of an error code. */
 const char *la_strerror(int code);
 

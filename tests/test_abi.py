@@ -125,6 +125,49 @@ def test_scalar_gated_entry_points_validate_like_the_others():
     assert _gla_prefill(T=0, init=1, g=None, **none) == OK
 
 
+def _bwd(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, S0=None, dO=FAKE, dST=None, dq=FAKE, dk_=FAKE,
+         dv_=FAKE, db=FAKE, dS0=None, B=1, H=1, T=64, dk=64, dv=64, dt=1):
+    return la.library().deltanet_prefill_backward(q, k, v, beta, S0, dO, dST, dq, dk_, dv_, db,
+                                                  dS0, B, H, T, dk, dv, dt, None)
+
+
+def _pro(qi=FAKE, ki=FAKE, bl=None, qo=FAKE, ko=FAKE, bo=None, B=1, H=2, T=64, dk=64, bh=1,
+         silu=1, scale=1.0, dt=1):
+    return la.library().deltanet_prologue(qi, ki, bl, qo, ko, bo, B, H, T, dk, bh, silu,
+                                          ctypes.c_float(scale), dt, None)
+
+
+@pytest.mark.parametrize("missing", ["q", "k", "v", "beta", "dO", "dq", "dk_", "dv_", "db"])
+def test_backward_null_pointers(missing):
+    assert _bwd(**{missing: None}) == NULL
+
+
+def test_backward_validation():
+    assert _bwd(dt=3) == DTYPE
+    assert _bwd(T=-1) == SHAPE
+    assert _bwd(dk=96) == DIM
+    assert _bwd(dt=0, dk=128) == DIM    # float32 backward: dk, dv <= 64
+    assert _bwd(dt=0, dv=128) == DIM
+    assert _bwd(dO=MISALIGNED) == ALIGN
+    assert _bwd(q=MISALIGNED) == ALIGN
+
+
+@pytest.mark.parametrize("missing", ["qi", "ki", "qo", "ko"])
+def test_prologue_null_pointers(missing):
+    assert _pro(**{missing: None}) == NULL
+
+
+def test_prologue_validation():
+    assert _pro(bl=FAKE) == NULL             # beta logits without an output
+    assert _pro(bo=FAKE) == NULL
+    assert _pro(bl=FAKE, bo=FAKE, bh=3) == SHAPE   # beta heads must be 1 or H
+    assert _pro(dt=2) == DTYPE
+    assert _pro(B=0) == SHAPE
+    assert _pro(dk=48) == DIM
+    assert _pro(qo=MISALIGNED) == ALIGN
+    assert _pro(T=0, qi=None, ki=None, qo=None, ko=None) == OK   # nothing to do, no HIP call
+
+
 @pytest.mark.parametrize("missing", ["q", "k", "v", "o", "S", "z"])
 def test_la_null_pointers(missing):
     assert _la_prefill(**{missing: None}) == NULL
