@@ -102,3 +102,53 @@ def test_decode_workload():
     o_ref, S_ref = oracle.delta_recurrent(q, k, v, beta, None, S0=S0)
     assert_close(S[n_idx, h_idx], S_ref[0], TOL[w.dtype], "S after 1010 steps (sampled)")
     assert_close(o[n_idx, h_idx], o_ref[0, :, -1], TOL[w.dtype], "o of step 1010 (sampled)")
+
+
+def test_token_gate_at_the_gated_workload_shape_sampled_heads():
+    """gated_deltanet_prefill (one decay per token) at B=1 H=32 T=32768
+    d=128 bf16, the shape and launch its bench row times, on sampled heads."""
+    dev = require_gpu()
+    w = W[3]
+    print("gated_deltanet_prefill at the gated workload's shape", flush=True)
+    inp = workloads.make_delta(w.B, w.H, w.T, w.dk, w.dv, w.dtype, seed=90 + w.index, gated="token")
+    d = _to(inp, dev)
+    o, S = la.gated_deltanet_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"])
+    torch.cuda.synchronize()
+    heads = [3, 17, 30]
+    sub = {n: inp[n][:, heads].contiguous() for n in ("q", "k", "v", "beta", "g")}
+    o_ref, S_ref = oracle.delta_recurrent(sub["q"], sub["k"], sub["v"], sub["beta"], sub["g"])
+    assert_close(o[:, heads], o_ref, TOL[w.dtype], "o (sampled heads)")
+    assert_close(S[:, heads], S_ref, TOL[w.dtype], "S (sampled heads)")
+
+
+def test_gla_at_the_la_workload_shape():
+    """gla_prefill at B=8 H=12 T=1024 d=64 bf16, the shape its bench row times."""
+    dev = require_gpu()
+    w = W[1]
+    inp = workloads.make_gla(w.B, w.H, w.T, w.dk, w.dv, w.dtype, seed=92)
+    d = _to(inp, dev)
+    o, S = la.gla_prefill(d["q"], d["k"], d["v"], d["g"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.gla_recurrent(inp["q"], inp["k"], inp["v"], inp["g"])
+    assert_close(o, o_ref, TOL[w.dtype], "o")
+    assert_close(S, S_ref, TOL[w.dtype], "S")
+
+
+def test_backward_at_the_deltanet_workload_shape_sampled_heads():
+    """deltanet_prefill_backward at B=4 H=16 T=4096 d=128 bf16 (the shape its
+    bench row times); the oracle's reverse recurrence on two sampled heads."""
+    dev = require_gpu()
+    w = W[2]
+    print("deltanet_prefill_backward at the delta-rule workload's shape", flush=True)
+    inp = workloads.make_delta(w.B, w.H, w.T, w.dk, w.dv, w.dtype, seed=95)
+    gen = workloads.generator(96)
+    dO = torch.randn(w.B, w.H, w.T, w.dv, generator=gen).to(w.dtype)
+    d = _to(inp, dev)
+    grads = la.deltanet_prefill_backward(d["q"], d["k"], d["v"], d["beta"], dO.to(dev))
+    torch.cuda.synchronize()
+    bi, heads = 1, [2, 13]
+    sub = {n: inp[n][bi:bi + 1, heads].contiguous() for n in ("q", "k", "v", "beta")}
+    ref = oracle.delta_backward(sub["q"], sub["k"], sub["v"], sub["beta"],
+                                dO[bi:bi + 1, heads].contiguous())
+    for name, g, r in zip(("dq", "dk", "dv", "dbeta"), grads, ref):
+        assert_close(g[bi:bi + 1, heads], r, TOL[w.dtype], f"{name} (sampled heads)")
