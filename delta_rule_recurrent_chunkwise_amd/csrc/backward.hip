@@ -34,8 +34,9 @@ namespace linattn {
 namespace {
 
 constexpr int kC = 64;
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;        // bwd_grads
 constexpr int kWaves = kThreads / 64;
+constexpr int kChainThreads = 512;   // bwd_chain: 8 waves, so the products spread wider
 constexpr int LTL = kC + 4;  // fp32 row stride of T and its transpose
 
 __device__ __forceinline__ int xcd_remap_b(int bid, int n) {
@@ -48,10 +49,10 @@ __device__ __forceinline__ int xcd_remap_b(int bid, int n) {
 // c < r).  Diagonal 16 x 16 blocks by forward substitution, one lane per
 // column; then block row by block row, T[bi][bj] = -T[bi][bi] sum_m L[bi][m]
 // T[m][bj].  The strictly upper triangle is cleared.  Every thread calls it.
-template <bool kBf16>
+template <bool kBf16, int NTH>
 __device__ void form_T(float* sTL, int tid, int wave, int lane) {
   const int lc = lane & 15, lg = lane >> 4;
-  if (wave == kWaves - 1) {
+  if (wave == NTH / 64 - 1) {
     const int b0 = 16 * lg;
     float tv[16];
 #pragma unroll
@@ -106,7 +107,7 @@ __device__ void form_T(float* sTL, int tid, int wave, int lane) {
     }
     __syncthreads();
   }
-  for (int i = tid; i < kC * kC; i += kThreads) {
+  for (int i = tid; i < kC * kC; i += NTH) {
     const int r = i >> 6, c = i & 63;
     if (c > r) sTL[r * LTL + c] = 0.f;
   }
@@ -173,26 +174,26 @@ union Vec16U {
 // With a transposed copy, consecutive lanes take consecutive rows, so the
 // transposed stores of one instruction are consecutive addresses (no bank
 // conflicts); otherwise consecutive lanes take consecutive vectors of a row.
-template <class E, int D>
+template <class E, int D, int NTH = kThreads>
 __device__ __forceinline__ void stage_rows(const typename E::T* src, int sld, int t0, int nrow, typename E::T* dst,
                                            int ld, typename E::T* dstT, int ldT, int tid) {
   constexpr int KV = E::kVec;
   constexpr int VPR = D / KV;  // 16-byte vectors per row
   constexpr int NV = kC * VPR;
-  constexpr int NPT = (NV + kThreads - 1) / kThreads;
+  constexpr int NPT = (NV + NTH - 1) / NTH;
   const bool rows_fast = dstT != nullptr;
   Vec16U<E> buf[NPT];
 #pragma unroll
   for (int j = 0; j < NPT; ++j) {
-    const int i = min(tid + kThreads * j, NV - 1);
+    const int i = min(tid + NTH * j, NV - 1);
     const int r = min(rows_fast ? i % kC : i / VPR, nrow - 1);
     const int vc = rows_fast ? i / kC : i % VPR;
     buf[j].v = *reinterpret_cast<const Vec16*>(src + (size_t)(t0 + r) * sld + vc * KV);
   }
 #pragma unroll
   for (int j = 0; j < NPT; ++j) {
-    const int i = tid + kThreads * j;
-    if (NV % kThreads != 0 && i >= NV) continue;
+    const int i = tid + NTH * j;
+    if (NV % NTH != 0 && i >= NV) continue;
     const int r = rows_fast ? i % kC : i / VPR, d = (rows_fast ? i / kC : i % VPR) * KV;
     if (r >= nrow) buf[j].v = Vec16{};
     if (dst) *reinterpret_cast<Vec16*>(dst + r * ld + d) = buf[j].v;
@@ -207,15 +208,15 @@ __device__ __forceinline__ void stage_rows(const typename E::T* src, int sld, in
 // in flight while the current one is computed: load() issues the 16-byte
 // loads into registers, store() writes them to LDS.  RF: rows-fast lane
 // mapping (for a transposed copy), as in stage_rows.
-template <class E, int D, bool RF>
+template <class E, int D, bool RF, int NTH>
 struct RowTile {
   typedef typename E::T T;
-  static constexpr int KV = E::kVec, VPR = D / KV, NV = kC * VPR, NPT = (NV + kThreads - 1) / kThreads;
+  static constexpr int KV = E::kVec, VPR = D / KV, NV = kC * VPR, NPT = (NV + NTH - 1) / NTH;
   Vec16U<E> buf[NPT];
   __device__ __forceinline__ void load(const T* src, int sld, int t0, int nrow, int tid) {
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
-      const int i = min(tid + kThreads * j, NV - 1);
+      const int i = min(tid + NTH * j, NV - 1);
       const int r = min(RF ? i % kC : i / VPR, nrow - 1);
       buf[j].v = *reinterpret_cast<const Vec16*>(src + (size_t)(t0 + r) * sld + (RF ? i / kC : i % VPR) * KV);
     }
@@ -223,8 +224,8 @@ struct RowTile {
   __device__ __forceinline__ void store(int nrow, T* dst, int ld, T* dstT, int ldT, int tid) {
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
-      const int i = tid + kThreads * j;
-      if (NV % kThreads != 0 && i >= NV) continue;
+      const int i = tid + NTH * j;
+      if (NV % NTH != 0 && i >= NV) continue;
       const int r = RF ? i % kC : i / VPR, d = (RF ? i / kC : i % VPR) * KV;
       Vec16U<E> x = buf[j];
       if (r >= nrow) x.v = Vec16{};
@@ -263,7 +264,8 @@ struct ChainLayout {
 };
 
 template <int DK, class E, int DVS>
-__global__ __launch_bounds__(kThreads) void bwd_chain(BackwardArgs a, float* __restrict__ dSc) {
+__global__ __launch_bounds__(kChainThreads) void bwd_chain(BackwardArgs a, float* __restrict__ dSc) {
+  constexpr int NTH = kChainThreads, NW = NTH / 64;
   typedef ChainLayout<DK, E, DVS> L;
   typedef typename E::T T;
   constexpr bool kBf16 = sizeof(T) == 2;
@@ -304,8 +306,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chain(BackwardArgs a, float* __r
 
   // chunk c's Q, K, dO slice and beta are loaded into registers while chunk
   // c + 1 is computed
-  RowTile<E, DK, true> pq, pk;
-  RowTile<E, DVS, true> pdo;
+  RowTile<E, DK, true, NTH> pq, pk;
+  RowTile<E, DVS, true, NTH> pdo;
   float pb = 0.f;
   auto prefetch = [&](int cc) {
     const int t0 = cc * kC, nrow = min(kC, Tn - t0);
@@ -340,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain(BackwardArgs a, float* __r
       // jobs 0..9: tiles (i, j <= i) of tril(Q K^T); jobs 10..19: the same
       // tiles of K K^T -> L (strictly lower, rows scaled by beta), stored
       // transposed in T's upper triangle
-      for (int jb = wave - NCW; jb < 20; jb += kWaves - NCW) {
+      for (int jb = wave - NCW; jb < 20; jb += NW - NCW) {
         const bool isA = jb < 10;
         const int t = isA ? jb : jb - 10;
         const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
@@ -356,13 +358,13 @@ __global__ __launch_bounds__(kThreads) void bwd_chain(BackwardArgs a, float* __r
         }
       }
       // tiles above the diagonal (ti < tj) are never written: zero them
-      for (int i = tid - 64 * NCW; i >= 0 && i < kC * kC; i += kThreads - 64 * NCW) {
+      for (int i = tid - 64 * NCW; i >= 0 && i < kC * kC; i += NTH - 64 * NCW) {
         const int r = i >> 6, cc = i & 63;
         if ((cc >> 4) > (r >> 4)) sA[r * LKT + cc] = E::cvt(0.f);
       }
     }
     __syncthreads();
-    form_T<kBf16>(sTL, tid, wave, lane);
+    form_T<kBf16, NTH>(sTL, tid, wave, lane);
     if (chain) {
       floatx4 dOt[4], du[4], dx[4];
 #pragma unroll
@@ -508,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const floa
     }
   }
   __syncthreads();
-  form_T<kBf16>(sTL, tid, wave, lane);
+  form_T<kBf16, kThreads>(sTL, tid, wave, lane);
 
   // ---- phase B: 16-column slices of dv, one per wave at a time ----
   for (int s = wave; s < NVT; s += kWaves) {
@@ -706,9 +708,9 @@ template <int DK, class E>
 hipError_t launch_chain_dk(const BackwardArgs& a, float* dSc, hipStream_t st) {
   const long bh = (long)a.B * a.H;
   if (a.dv_ % 32 == 0) {
-    hipLaunchKernelGGL((bwd_chain<DK, E, 32>), dim3((unsigned)(bh * (a.dv_ / 32))), dim3(kThreads), 0, st, a, dSc);
+    hipLaunchKernelGGL((bwd_chain<DK, E, 32>), dim3((unsigned)(bh * (a.dv_ / 32))), dim3(kChainThreads), 0, st, a, dSc);
   } else {
-    hipLaunchKernelGGL((bwd_chain<DK, E, 16>), dim3((unsigned)(bh * (a.dv_ / 16))), dim3(kThreads), 0, st, a, dSc);
+    hipLaunchKernelGGL((bwd_chain<DK, E, 16>), dim3((unsigned)(bh * (a.dv_ / 16))), dim3(kChainThreads), 0, st, a, dSc);
   }
   return hipGetLastError();
 }
