@@ -37,6 +37,7 @@ constexpr int kC = 64;
 constexpr int kThreads = 256;        // bwd_grads
 constexpr int kWaves = kThreads / 64;
 constexpr int kChainThreads = 512;   // bwd_chain: 8 waves, so the products spread wider
+constexpr int kGradThreads = 512;    // bwd_grads: likewise
 constexpr int LTL = kC + 4;  // fp32 row stride of T and its transpose
 
 __device__ __forceinline__ int xcd_remap_b(int bid, int n) {
@@ -446,11 +447,12 @@ struct GradLayout {
 };
 
 template <int DK, int DV, class E>
-__global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const float* __restrict__ Sc,
+__global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const float* __restrict__ Sc,
                                                      const float* __restrict__ dSc) {
   typedef GradLayout<DK, DV, E> L;
   typedef typename E::T T;
   constexpr bool kBf16 = sizeof(T) == 2;
+  constexpr int NTH = kGradThreads, NW = NTH / 64;
   constexpr int NKT = DK / 16;
   constexpr int NVT = DV / 16;
   constexpr int LQ = L::LQ, LV = L::LV, LS = L::LS, LKT = L::LKT;
@@ -479,18 +481,18 @@ __global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const floa
   T* sK = reinterpret_cast<T*>(smem + L::aK);
   T* sA = reinterpret_cast<T*>(smem + L::aAt);  // tril(Q K^T), row-major
   float* sTL = reinterpret_cast<float*>(smem + L::aTL);
-  stage_rows<E, DK>(qh, DK, t0, nrow, sQ, LQ, nullptr, 0, tid);
-  stage_rows<E, DK>(kh, DK, t0, nrow, sK, LQ, nullptr, 0, tid);
+  stage_rows<E, DK, NTH>(qh, DK, t0, nrow, sQ, LQ, nullptr, 0, tid);
+  stage_rows<E, DK, NTH>(kh, DK, t0, nrow, sK, LQ, nullptr, 0, tid);
   if (tid < kC) {
     sB[tid] = tid < nrow ? E::tof(bth[t0 + tid]) : 0.f;
     sDB[tid] = 0.f;
   }
-  for (int i = tid; i < kC * kC; i += kThreads) {  // tiles above the diagonal stay zero
+  for (int i = tid; i < kC * kC; i += NTH) {  // tiles above the diagonal stay zero
     const int r = i >> 6, cc = i & 63;
     if ((cc >> 4) > (r >> 4)) sA[r * LKT + cc] = E::cvt(0.f);
   }
   __syncthreads();
-  for (int jb = wave; jb < 20; jb += kWaves) {
+  for (int jb = wave; jb < 20; jb += NW) {
     const bool isA = jb < 10;
     const int t = isA ? jb : jb - 10;
     const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
@@ -510,10 +512,10 @@ __global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const floa
     }
   }
   __syncthreads();
-  form_T<kBf16, kThreads>(sTL, tid, wave, lane);
+  form_T<kBf16, NTH>(sTL, tid, wave, lane);
 
   // ---- phase B: 16-column slices of dv, one per wave at a time ----
-  for (int s = wave; s < NVT; s += kWaves) {
+  for (int s = wave; s < NVT; s += NW) {
     const int col = 16 * s + lc;
     floatx4 Sv[NKT], dSv[NKT], vt[4], dOt[4];
 #pragma unroll
@@ -574,8 +576,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const floa
   T* sDAt = reinterpret_cast<T*>(smem + L::cDAt);
   T* sBL = reinterpret_cast<T*>(smem + L::cBL);
   T* sBLt = reinterpret_cast<T*>(smem + L::cBLt);
-  stage_rows<E, DV>(doh, DV, t0, nrow, sDO, LV, nullptr, 0, tid);
-  for (int i = tid; i < kC * kC; i += kThreads) {  // tiles above the diagonal stay zero
+  stage_rows<E, DV, NTH>(doh, DV, t0, nrow, sDO, LV, nullptr, 0, tid);
+  for (int i = tid; i < kC * kC; i += NTH) {  // tiles above the diagonal stay zero
     const int r = i >> 6, cc = i & 63;
     if ((cc >> 4) > (r >> 4)) {
       const T z = E::cvt(0.f);
@@ -586,7 +588,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const floa
     }
   }
   __syncthreads();
-  for (int jb = wave; jb < 20; jb += kWaves) {
+  for (int jb = wave; jb < 20; jb += NW) {
     const bool isA = jb < 10;  // dA, else dL
     const int t = isA ? jb : jb - 10;
     const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
@@ -618,24 +620,26 @@ __global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const floa
   // ---- phase D: each wave owns output tiles id = wave + 4 n of the 4 x NKT grid ----
   T* sKt = reinterpret_cast<T*>(smem + L::dKt);
   T* sQt = reinterpret_cast<T*>(smem + L::dQt);
-  stage_rows<E, DK>(kh, DK, t0, nrow, nullptr, 0, sKt, LKT, tid);
+  stage_rows<E, DK, NTH>(kh, DK, t0, nrow, nullptr, 0, sKt, LKT, tid);
   __syncthreads();
-  constexpr int NOWN = NKT;  // 4 * NKT tiles over 4 waves
+  constexpr int NTILE = 4 * NKT, NOWN = (NTILE + NW - 1) / NW;  // output tiles, per wave
   floatx4 gq[NOWN], gk[NOWN];
 #pragma unroll
   for (int n = 0; n < NOWN; ++n) {
-    const int id = wave + kWaves * n, ti = id / NKT, tk = id - ti * NKT;
+    const int id = wave + NW * n, ti = id / NKT, tk = id - ti * NKT;
+    if (NTILE % NW != 0 && id >= NTILE) continue;
     gq[n] = rowrow<kBf16>(zero4(), sDA + (16 * ti + lc) * LKT, sKt + (16 * tk + lc) * LKT, kC, lane);
     floatx4 x = rowrow<kBf16>(zero4(), sBL + (16 * ti + lc) * LKT, sKt + (16 * tk + lc) * LKT, kC, lane);
     x += rowrow<kBf16>(zero4(), sBLt + (16 * ti + lc) * LKT, sKt + (16 * tk + lc) * LKT, kC, lane);
     gk[n] = x;
   }
   __syncthreads();  // bL is dead: Q^T goes in its place
-  stage_rows<E, DK>(qh, DK, t0, nrow, nullptr, 0, sQt, LKT, tid);
+  stage_rows<E, DK, NTH>(qh, DK, t0, nrow, nullptr, 0, sQt, LKT, tid);
   __syncthreads();
 #pragma unroll
   for (int n = 0; n < NOWN; ++n) {
-    const int id = wave + kWaves * n, ti = id / NKT, tk = id - ti * NKT;
+    const int id = wave + NW * n, ti = id / NKT, tk = id - ti * NKT;
+    if (NTILE % NW != 0 && id >= NTILE) continue;
     gk[n] += rowrow<kBf16>(zero4(), sDAt + (16 * ti + lc) * LKT, sQt + (16 * tk + lc) * LKT, kC, lane);
   }
   __syncthreads();
@@ -644,17 +648,17 @@ __global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const floa
   T* sS = reinterpret_cast<T*>(smem + L::eS);
   T* sDS = reinterpret_cast<T*>(smem + L::eDS);
   {  // S and dSn rows, fp32 -> operand type, 16-byte loads issued first
-    constexpr int NV4 = DK * DV / 4, NPT = NV4 / kThreads > 0 ? NV4 / kThreads : 1;
+    constexpr int NV4 = DK * DV / 4, NPT = NV4 / NTH > 0 ? NV4 / NTH : 1;
     float4 bs[NPT], bd[NPT];
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
-      const int i = min(tid + kThreads * j, NV4 - 1);
+      const int i = min(tid + NTH * j, NV4 - 1);
       bs[j] = reinterpret_cast<const float4*>(S)[i];
       bd[j] = reinterpret_cast<const float4*>(dSn)[i];
     }
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
-      const int i = tid + kThreads * j;
+      const int i = tid + NTH * j;
       if (i >= NV4) continue;
       const int r = (4 * i) / DV, d = (4 * i) % DV;
       T* ps = sS + r * LS + d;
@@ -668,7 +672,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const floa
   T* dko = reinterpret_cast<T*>(a.dk) + ((size_t)bh * Tn + t0) * DK;
 #pragma unroll
   for (int n = 0; n < NOWN; ++n) {
-    const int id = wave + kWaves * n, ti = id / NKT, tk = id - ti * NKT;
+    const int id = wave + NW * n, ti = id / NKT, tk = id - ti * NKT;
+    if (NTILE % NW != 0 && id >= NTILE) continue;
     const floatx4 q1 = rowrow<kBf16>(zero4(), sDO + (16 * ti + lc) * LV, sS + (16 * tk + lc) * LS, DV, lane);
     const floatx4 k1 = rowrow<kBf16>(zero4(), sU + (16 * ti + lc) * LV, sDS + (16 * tk + lc) * LS, DV, lane);
     const floatx4 k2 = rowrow<kBf16>(zero4(), sDX + (16 * ti + lc) * LV, sS + (16 * tk + lc) * LS, DV, lane);
@@ -687,7 +692,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads(BackwardArgs a, const floa
 template <int DK, int DV, class E>
 hipError_t launch_grads(const BackwardArgs& a, const float* Sc, const float* dSc, long nchunks, hipStream_t st) {
   static_assert(GradLayout<DK, DV, E>::total <= 160 * 1024, "backward gradient kernel exceeds the LDS of a CU");
-  hipLaunchKernelGGL((bwd_grads<DK, DV, E>), dim3((unsigned)nchunks), dim3(kThreads), 0, st, a, Sc, dSc);
+  hipLaunchKernelGGL((bwd_grads<DK, DV, E>), dim3((unsigned)nchunks), dim3(kGradThreads), 0, st, a, Sc, dSc);
   return hipGetLastError();
 }
 
