@@ -34,6 +34,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
+// Loads of a tile of N 16-byte vectors, all issued before any is used:
+// thread tid takes vectors tid + 256 j; idx(i) gives the element offset of
+// vector i (already clamped to valid rows by the caller).
+template <int N, class F>
+__device__ __forceinline__ void load_vecs(u32x4 (&buf)[(N + 255) / 256], const bf16_t* base, int tid, F idx) {
+#pragma unroll
+  for (int j = 0; j < (N + 255) / 256; ++j) {
+    const int i = min(tid + 256 * j, N - 1);
+    buf[j] = *reinterpret_cast<const u32x4*>(base + idx(i));
+  }
+}
+
 // Wave 0 of a chunk's workgroup: G_t = sum_{s<=t} g_s over the chunk (lane =
 // token; tokens past the end and a missing gate count as 0).
 __device__ __forceinline__ float chunk_log_decay(const bf16_t* gc, int lane, int nrow) {
@@ -91,10 +103,17 @@ __global__ __launch_bounds__(256) void la_chunk_state(const bf16_t* __restrict__
     }
     __syncthreads();
   }
-  for (int i = tid; i < kC * DK / 8; i += 256) {
+  // rows past the end re-read the last row and are zeroed after phi
+  constexpr int NK = kC * DK / 8, NV = kC * DV / 8;
+  u32x4 bk[(NK + 255) / 256], bv[(NV + 255) / 256];
+  load_vecs<NK>(bk, kc, tid, [&](int i) { return (size_t)min(i / (DK / 8), nrow - 1) * DK + (i % (DK / 8)) * 8; });
+  load_vecs<NV>(bv, vc, tid, [&](int i) { return (size_t)min(i / (DV / 8), nrow - 1) * DV + (i % (DV / 8)) * 8; });
+#pragma unroll
+  for (int j = 0; j < (NK + 255) / 256; ++j) {
+    const int i = tid + 256 * j;
+    if (NK % 256 != 0 && i >= NK) continue;
     const int r = i / (DK / 8), c8 = (i % (DK / 8)) * 8;
-    // rows past the end re-read the last row and are zeroed after phi
-    u32x4 w = *reinterpret_cast<const u32x4*>(kc + (size_t)min(r, nrow - 1) * DK + c8);
+    u32x4 w = bk[j];
     const float wr = GLA ? sw[GLA ? r : 0] : 1.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -105,10 +124,12 @@ __global__ __launch_bounds__(256) void la_chunk_state(const bf16_t* __restrict__
     }
     *reinterpret_cast<u32x4*>(&sk[r][c8]) = w;
   }
-  for (int i = tid; i < kC * DV / 8; i += 256) {
+#pragma unroll
+  for (int j = 0; j < (NV + 255) / 256; ++j) {
+    const int i = tid + 256 * j;
+    if (NV % 256 != 0 && i >= NV) continue;
     const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
-    const u32x4 x = *reinterpret_cast<const u32x4*>(vc + (size_t)min(r, nrow - 1) * DV + c8);
-    *reinterpret_cast<u32x4*>(&sv[r][c8]) = r < nrow ? x : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(&sv[r][c8]) = r < nrow ? bv[j] : u32x4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
   constexpr int NDT = DK / 16, NJT = DV / 16 + (GLA ? 0 : 1);  // the extra column tile gives dz
@@ -222,29 +243,46 @@ __global__ __launch_bounds__(256) void la_chunk_out(const bf16_t* __restrict__ q
   const bf16_t* qc = q + ((size_t)bh * T + t0) * DK;
   const bf16_t* kc = k + ((size_t)bh * T + t0) * DK;
   const bf16_t* vc = v + ((size_t)bh * T + t0) * DV;
-  for (int i = tid; i < 2 * kC * DK / 8; i += 256) {
-    const bool isq = i < kC * DK / 8;
-    const int ii = isq ? i : i - kC * DK / 8;
-    const int r = ii / (DK / 8), c8 = (ii % (DK / 8)) * 8;
-    // rows past the end re-read the last row; phi(q) = phi(k) = 0 there
-    u32x4 w = *reinterpret_cast<const u32x4*>((isq ? qc : kc) + (size_t)min(r, nrow - 1) * DK + c8);
+  // every load first (rows past the end re-read the last row; phi(q) =
+  // phi(k) = 0 there), then phi and the LDS stores
+  constexpr int NQ = kC * DK / 8, NV = kC * DV / 8, NS = DK * DV / 8;
+  const bf16_t* sc = Sc + chunk * DK * DV;
+  u32x4 bq[(NQ + 255) / 256], bk[(NQ + 255) / 256], bv[(NV + 255) / 256], bs[(NS + 255) / 256];
+  auto qk_idx = [&](int i) { return (size_t)min(i / (DK / 8), nrow - 1) * DK + (i % (DK / 8)) * 8; };
+  load_vecs<NQ>(bq, qc, tid, qk_idx);
+  load_vecs<NQ>(bk, kc, tid, qk_idx);
+  load_vecs<NV>(bv, vc, tid, [&](int i) { return (size_t)min(i / (DV / 8), nrow - 1) * DV + (i % (DV / 8)) * 8; });
+  load_vecs<NS>(bs, sc, tid, [&](int i) { return (size_t)i * 8; });
+#pragma unroll
+  for (int j = 0; j < (NQ + 255) / 256; ++j) {
+    const int i = tid + 256 * j;
+    if (NQ % 256 != 0 && i >= NQ) continue;
+    const int r = i / (DK / 8), c8 = (i % (DK / 8)) * 8;
+    u32x4 wq = bq[j], wk = bk[j];
     if constexpr (!GLA) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = pack2(phi_elu1(bf2f((bf16_t)(w[e] & 0xffffu))), phi_elu1(bf2f((bf16_t)(w[e] >> 16))));
+      for (int e = 0; e < 4; ++e) {
+        wq[e] = pack2(phi_elu1(bf2f((bf16_t)(wq[e] & 0xffffu))), phi_elu1(bf2f((bf16_t)(wq[e] >> 16))));
+        wk[e] = pack2(phi_elu1(bf2f((bf16_t)(wk[e] & 0xffffu))), phi_elu1(bf2f((bf16_t)(wk[e] >> 16))));
+      }
     }
-    if (r >= nrow) w = u32x4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(isq ? &sq[r][c8] : &sk[r][c8]) = w;
+    if (r >= nrow) wq = wk = u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(&sq[r][c8]) = wq;
+    *reinterpret_cast<u32x4*>(&sk[r][c8]) = wk;
   }
-  for (int i = tid; i < kC * DV / 8; i += 256) {
+#pragma unroll
+  for (int j = 0; j < (NV + 255) / 256; ++j) {
+    const int i = tid + 256 * j;
+    if (NV % 256 != 0 && i >= NV) continue;
     const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
-    const u32x4 x = *reinterpret_cast<const u32x4*>(vc + (size_t)min(r, nrow - 1) * DV + c8);
-    *reinterpret_cast<u32x4*>(&sv[r][c8]) = r < nrow ? x : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(&sv[r][c8]) = r < nrow ? bv[j] : u32x4{0u, 0u, 0u, 0u};
   }
-  const bf16_t* sc = Sc + chunk * DK * DV;
-  for (int i = tid; i < DK * DV / 8; i += 256) {
+#pragma unroll
+  for (int j = 0; j < (NS + 255) / 256; ++j) {
+    const int i = tid + 256 * j;
+    if (NS % 256 != 0 && i >= NS) continue;
     const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
-    *reinterpret_cast<u32x4*>(&ss[r][c8]) = *reinterpret_cast<const u32x4*>(sc + (size_t)r * DV + c8);
+    *reinterpret_cast<u32x4*>(&ss[r][c8]) = bs[j];
   }
   if constexpr (GLA) {
     if (wave == 0) sg[lane] = chunk_log_decay(g ? g + (size_t)bh * T + t0 : nullptr, lane, nrow);
