@@ -27,6 +27,8 @@
 //      per chunk, from its S and dSn.
 // Inputs and outputs have the input dtype; the products run on bf16 MFMA
 // (fp32 MFMA for fp32 inputs) with fp32 accumulation, like the forward.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -400,6 +402,377 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain(BackwardArgs a, float
 }
 
 // ---------------------------------------------------------------------------
+// bf16: the reverse chain as one product per chunk.  With W = T diag(beta) K,
+// i.e. (I + L) W = diag(beta) K, the gradient of the state entering a chunk
+// is
+//   dS = dSn + Q^T dO - W^T (A^T dO + K dSn) = dSn - P dSn + R^T dO,
+//   P = W^T K (dk x dk),  R = Q - A W (64 x dk),
+// and P, R depend on the chunk's inputs only.  bwd_transition forms them for
+// every chunk at once; bwd_chain_mat walks the chunks backwards with
+// dS <- dS - P dS + R^T dO, one barrier per chunk.
+// ---------------------------------------------------------------------------
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 ld_frag(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ shortx4 ld_tr(const bf16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4*)((__attribute__((address_space(3))) bf16_t*)(p)));
+}
+__device__ __forceinline__ bf16x8 cat_tr(shortx4 lo, shortx4 hi) {
+  typedef short shortx8_t __attribute__((ext_vector_type(8)));
+  const shortx8_t x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, x);
+}
+// Operand of a 32-deep product over tokens t0 .. t0 + 31, read with the LDS
+// transpose read from a row-major (token x column) bf16 tile: lane (lc, G)
+// receives column c0 + lc of tokens t0 + 4G + e and t0 + 16 + 4G + e,
+// e = 0..3 (lane 16G + 4a + b receives element b of the 8-byte runs addressed
+// by lanes 16G + a + 4e).  As an A operand its rows are columns c0 .. c0+15;
+// as a B operand, its columns.
+__device__ __forceinline__ bf16x8 tok_frag(const bf16_t* tile, int ld, int t0, int c0, int lane) {
+  const int trow = 4 * (lane >> 4) + ((lane >> 2) & 3), tcol = 4 * (lane & 3);
+  return cat_tr(ld_tr(tile + (t0 + trow) * ld + c0 + tcol), ld_tr(tile + (t0 + 16 + trow) * ld + c0 + tcol));
+}
+// The token order of tok_frag as a column permutation, for tiles read with
+// plain 16-byte fragment reads against it: token 32b + 16h + 4g + i is kept
+// in column 32b + 8g + 4h + i.
+__device__ __forceinline__ int tperm(int x) {
+  return (x & ~31) | (((x >> 2) & 3) << 3) | (((x >> 4) & 1) << 2) | (x & 3);
+}
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+__device__ __forceinline__ void st4_bf16(bf16_t* p, float a0, float a1, float a2, float a3) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack2(a0, a1), pack2(a2, a3));
+}
+
+template <int DK>
+struct TransLayout {
+  static constexpr int LQ = DK + 16;  // rows of Q, K
+  static constexpr int LT = kC + 16;  // rows of A and W^T (token columns permuted by tperm)
+  static constexpr int LD = 20;       // fp32 rows of a diagonal block of L
+  static constexpr int oQ = 0;
+  static constexpr int oK = oQ + kC * LQ * 2;
+  static constexpr int oA = oK + kC * LQ * 2;
+  static constexpr int oWt = oA + kC * LT * 2;
+  static constexpr int oLo = oWt + DK * LT * 2;   // L_bj, b > j: bf16 [6][16][16], row-major
+  static constexpr int oD = oLo + 6 * 256 * 2;    // D_b = (I + L_bb)^-1: bf16 [4][16][16]
+  static constexpr int oLd = oD + 4 * 256 * 2;    // L_bb: fp32 [4][16][LD], strictly lower
+  static constexpr int oB = oLd + 4 * 16 * LD * 4;
+  static constexpr int total = oB + kC * 4;
+};
+
+constexpr int kTransThreads = 512;
+
+// One workgroup (8 waves) per (batch, head, chunk): P = W^T K and R = Q - A W.
+//   1. stage Q, K, beta;
+//   2. tril(Q K^T) -> A (bf16, token columns permuted) and the blocks of
+//      L = tril(diag(beta) K K^T, -1): off the diagonal in bf16, on it fp32;
+//   3. D_b = (I + L_bb)^-1 (one lane per block column, fp32);
+//   4. W by block forward substitution, W_b = D_b (beta K_b - sum_{j<b} L_bj W_j),
+//      one wave per 16-column tile of W, stored as W^T (token columns permuted);
+//   5. P (row-major, dk x dk) and R^T (dk x 64, token columns permuted) to
+//      global memory.
+template <int DK>
+__global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, bf16_t* __restrict__ Pg,
+                                                                bf16_t* __restrict__ Rg) {
+  typedef TransLayout<DK> LY;
+  constexpr int NTH = kTransThreads, NW = NTH / 64, LQ = LY::LQ, LT = LY::LT, LD = LY::LD, NT = DK / 16;
+  __shared__ __attribute__((aligned(16))) char smem[LY::total];
+  bf16_t* sQ = reinterpret_cast<bf16_t*>(smem + LY::oQ);
+  bf16_t* sK = reinterpret_cast<bf16_t*>(smem + LY::oK);
+  bf16_t* sA = reinterpret_cast<bf16_t*>(smem + LY::oA);
+  bf16_t* sWt = reinterpret_cast<bf16_t*>(smem + LY::oWt);
+  bf16_t* sLo = reinterpret_cast<bf16_t*>(smem + LY::oLo);
+  bf16_t* sD = reinterpret_cast<bf16_t*>(smem + LY::oD);
+  float* sLd = reinterpret_cast<float*>(smem + LY::oLd);
+  float* sB = reinterpret_cast<float*>(smem + LY::oB);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
+  const int Tn = a.T, nch = (Tn + kC - 1) / kC;
+  const size_t chunk = blockIdx.x;
+  const int bh = (int)(chunk / nch), c = (int)(chunk - (size_t)bh * nch);
+  const int t0 = c * kC, nrow = min(kC, Tn - t0);
+  const bf16_t* qh = reinterpret_cast<const bf16_t*>(a.q) + (size_t)bh * Tn * DK;
+  const bf16_t* kh = reinterpret_cast<const bf16_t*>(a.k) + (size_t)bh * Tn * DK;
+  const bf16_t* bth = reinterpret_cast<const bf16_t*>(a.beta) + (size_t)bh * Tn;
+
+  // 1. staging (rows past the end as zeros); A starts cleared, as its tiles
+  // above the diagonal are read as zeros
+  constexpr int NV = kC * DK / 8, VPT = (NV + NTH - 1) / NTH;
+  u32x4 bq[VPT], bk[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int v = min(tid + NTH * j, NV - 1);
+    const size_t off = (size_t)(t0 + min(v / (DK / 8), nrow - 1)) * DK + (v % (DK / 8)) * 8;
+    bq[j] = *reinterpret_cast<const u32x4*>(qh + off);
+    bk[j] = *reinterpret_cast<const u32x4*>(kh + off);
+  }
+  const float bt = bf2f(bth[t0 + min(tid & 63, nrow - 1)]);
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  for (int i = tid; i < kC * LT / 8; i += NTH) reinterpret_cast<u32x4*>(sA)[i] = z4;
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int v = tid + NTH * j;
+    if (NV % NTH != 0 && v >= NV) continue;
+    const int r = v / (DK / 8), c8 = (v % (DK / 8)) * 8;
+    *reinterpret_cast<u32x4*>(sQ + r * LQ + c8) = r < nrow ? bq[j] : z4;
+    *reinterpret_cast<u32x4*>(sK + r * LQ + c8) = r < nrow ? bk[j] : z4;
+  }
+  if (tid < kC) sB[tid] = tid < nrow ? bt : 0.f;
+  __syncthreads();
+
+  // 2. jobs 0..9: tiles (ti >= tj) of tril(Q K^T); 10..19: of L.  The
+  // transposed products, so that a lane holds row 16 ti + lc and the four
+  // consecutive columns 16 tj + 4 lg + i.
+  for (int jb = wave; jb < 20; jb += NW) {
+    const bool isA = jb < 10;
+    const int t = isA ? jb : jb - 10;
+    const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
+    const int tj = t - ti * (ti + 1) / 2;
+    const floatx4 acc = mm_rowrow_bf16(zero4(), sK + (16 * tj + lc) * LQ, (isA ? sQ : sK) + (16 * ti + lc) * LQ, DK, lane);
+    const int r = 16 * ti + lc, c0 = 16 * tj + 4 * lg;
+    if (isA) {
+      st4_bf16(sA + r * LT + tperm(c0), c0 <= r ? acc[0] : 0.f, c0 + 1 <= r ? acc[1] : 0.f,
+               c0 + 2 <= r ? acc[2] : 0.f, c0 + 3 <= r ? acc[3] : 0.f);
+    } else {
+      const float br = sB[r];
+      if (ti == tj) {
+        float4 v;
+        v.x = c0 < r ? br * acc[0] : 0.f;
+        v.y = c0 + 1 < r ? br * acc[1] : 0.f;
+        v.z = c0 + 2 < r ? br * acc[2] : 0.f;
+        v.w = c0 + 3 < r ? br * acc[3] : 0.f;
+        *reinterpret_cast<float4*>(sLd + (16 * ti + lc) * LD + 4 * lg) = v;
+      } else {
+        st4_bf16(sLo + ((ti * (ti - 1) / 2 + tj) * 16 + lc) * 16 + 4 * lg, br * acc[0], br * acc[1], br * acc[2],
+                 br * acc[3]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // 3. D_b: lane (block lg, column lc) solves (I + L_bb) x = e_lc
+  if (wave == 0) {
+    const float* lb = sLd + 16 * lg * LD;
+    float x[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) x[m] = m == lc ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) s += lb[i * LD + m] * x[m];
+      if (i > lc) x[i] = -s;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sD[(16 * lg + i) * 16 + lc] = f2bf(x[i]);
+  }
+  __syncthreads();
+
+  // 4. W, one wave per 16-column tile (k16 products of 16 x 16 blocks; the B
+  // operands are accumulator tiles)
+  if (wave < NT) {
+    const int dt = wave;
+    auto blk = [&](const bf16_t* b) { return *reinterpret_cast<const shortx4*>(b + lc * 16 + 4 * lg); };
+    floatx4 xb[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * b + 4 * lg + i;
+        xb[b][i] = sB[r] * bf2f(sK[r * LQ + 16 * dt + lc]);
+      }
+    floatx4 w[4];
+    w[0] = mfma_k16(blk(sD), acc_to_b16(xb[0]), zero4());
+    const shortx4 w0 = acc_to_b16(w[0]);
+    w[1] = mfma_k16(blk(sD + 256), acc_to_b16(xb[1] - mfma_k16(blk(sLo), w0, zero4())), zero4());
+    const shortx4 w1 = acc_to_b16(w[1]);
+    w[2] = mfma_k16(blk(sD + 512),
+                    acc_to_b16(xb[2] - mfma_k16(blk(sLo + 512), w1, mfma_k16(blk(sLo + 256), w0, zero4()))), zero4());
+    const shortx4 w2 = acc_to_b16(w[2]);
+    w[3] = mfma_k16(blk(sD + 768),
+                    acc_to_b16(xb[3] - mfma_k16(blk(sLo + 1280), w2,
+                                                mfma_k16(blk(sLo + 1024), w1, mfma_k16(blk(sLo + 768), w0, zero4())))),
+                    zero4());
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      st4_bf16(sWt + (16 * dt + lc) * LT + tperm(16 * b + 4 * lg), w[b][0], w[b][1], w[b][2], w[b][3]);
+  }
+  __syncthreads();
+
+  // 5. P (from P^T = K^T W: lane holds P[16 dt + lc][16 et + 4 lg + i]) and
+  // R = Q - A W (lane holds R[16 rt + 4 lg + i][16 dt + lc]); A's row block rt
+  // reaches tokens <= 16 rt + 15 only
+  const size_t cb = (size_t)bh * nch + c;
+  bf16_t* Pc = Pg + cb * DK * DK;
+  bf16_t* Rc = Rg + cb * DK * kC;
+  constexpr int NPJ = NT * NT, NRJ = 4 * NT;
+  for (int jb = wave; jb < NPJ + NRJ; jb += NW) {
+    if (jb < NPJ) {
+      const int et = jb / NT, dt = jb - et * NT;
+      floatx4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        acc = mfma_k32(tok_frag(sK, LQ, 32 * kb, 16 * et, lane), ld_frag(sWt + (16 * dt + lc) * LT + 32 * kb + 8 * lg),
+                       acc);
+      st4_bf16(Pc + (size_t)(16 * dt + lc) * DK + 16 * et + 4 * lg, acc[0], acc[1], acc[2], acc[3]);
+    } else {
+      const int t = jb - NPJ, rt = t / NT, dt = t - rt * NT;
+      floatx4 acc = zero4();
+      for (int kb = 0; kb <= (rt >> 1); ++kb)
+        acc = mfma_k32(ld_frag(sA + (16 * rt + lc) * LT + 32 * kb + 8 * lg),
+                       ld_frag(sWt + (16 * dt + lc) * LT + 32 * kb + 8 * lg), acc);
+      float rv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rv[i] = bf2f(sQ[(16 * rt + 4 * lg + i) * LQ + 16 * dt + lc]) - acc[i];
+      st4_bf16(Rc + (size_t)(16 * dt + lc) * kC + tperm(16 * rt + 4 * lg), rv[0], rv[1], rv[2], rv[3]);
+    }
+  }
+}
+
+// One workgroup per (batch, head, DVS value columns), DK / 16 waves: wave w
+// keeps dS rows 16w .. 16w + 15 of the slice as DVS / 16 accumulator tiles.
+// Per chunk (last to first): write dSn (fp32, for the gradient pass), then
+// dS <- dS - P dS + R^T dO with P rows and R^T rows loaded straight into
+// registers (NS chunks ahead) and dS^T, the dO slice read from LDS (double
+// buffered, one barrier per chunk).
+template <int DK, int DVS>
+__global__ __launch_bounds__(DK * 4) void bwd_chain_mat(BackwardArgs a, const bf16_t* __restrict__ Pg,
+                                                        const bf16_t* __restrict__ Rg, float* __restrict__ dSc) {
+  constexpr int NTH = DK * 4, NJ = DVS / 16, LDT = DK + 16, LVO = DVS + 16, NS = 4;  // NS: chunks in flight (the prologue issues four)
+  constexpr int KP = DK >= 32 ? DK / 32 : 1;
+  constexpr int NVO = kC * DVS / 8, VPT = (NVO + NTH - 1) / NTH;
+  __shared__ __attribute__((aligned(16))) bf16_t sDt[2][DVS][LDT];
+  __shared__ __attribute__((aligned(16))) bf16_t sDO[2][kC][LVO];
+  const int dv = a.dv_, nsl = dv / DVS;
+  const int wid = xcd_remap_b(blockIdx.x, gridDim.x);
+  const int bh = wid / nsl, sl = wid - bh * nsl;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
+  const int Tn = a.T, nch = (Tn + kC - 1) / kC;
+  const int prow = 16 * wave + lc;  // the row of P and R^T this lane's fragments come from
+  const bf16_t* doh = reinterpret_cast<const bf16_t*>(a.dO) + (size_t)bh * Tn * dv + sl * DVS;
+
+  // register slots of NS chunks: P fragments, R^T fragments, the dO slice;
+  // every lane issues every load (clamped to valid rows and chunks), and
+  // slots are indexed at compile time only
+  u32x4 sp[NS][KP], sr[NS][2], so[NS][VPT];
+  auto issue = [&](int x, auto slotc) {
+    constexpr int S = decltype(slotc)::value;
+    const size_t cb = (size_t)bh * nch + x;
+    const bf16_t* pr = Pg + (cb * DK + prow) * DK;
+#pragma unroll
+    for (int kb = 0; kb < KP; ++kb) {
+      if constexpr (DK == 16) {
+        const uint2 h = *reinterpret_cast<const uint2*>(pr + 4 * lg);
+        sp[S][kb] = u32x4{h.x, h.y, 0u, 0u};
+      } else {
+        sp[S][kb] = *reinterpret_cast<const u32x4*>(pr + 32 * kb + 8 * lg);
+      }
+    }
+    const bf16_t* rr = Rg + (cb * DK + prow) * kC;
+    sr[S][0] = *reinterpret_cast<const u32x4*>(rr + 8 * lg);
+    sr[S][1] = *reinterpret_cast<const u32x4*>(rr + 32 + 8 * lg);
+    const int t0 = x * kC, nrow = min(kC, Tn - t0);
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int v = min(tid + NTH * j, NVO - 1);
+      const int r = min(v / (DVS / 8), nrow - 1);
+      so[S][j] = *reinterpret_cast<const u32x4*>(doh + (size_t)(t0 + r) * dv + (v % (DVS / 8)) * 8);
+    }
+  };
+  auto store_do = [&](int x, auto slotc, int buf) {
+    constexpr int S = decltype(slotc)::value;
+    const int nrow = min(kC, Tn - x * kC);
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int v = tid + NTH * j;
+      if (NVO % NTH != 0 && v >= NVO) continue;
+      const int r = v / (DVS / 8), c8 = (v % (DVS / 8)) * 8;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(&sDO[buf][r][c8]) = r < nrow ? so[S][j] : z;
+    }
+  };
+  floatx4 st[NJ];
+  auto put_dst = [&](int buf) {  // dS^T, bf16: lane writes 4 consecutive rows of column 16 jt + lc
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) st4_bf16(&sDt[buf][16 * jt + lc][16 * wave + 4 * lg], st[jt][0], st[jt][1], st[jt][2], st[jt][3]);
+  };
+  const int col0 = sl * DVS + lc;
+#pragma unroll
+  for (int jt = 0; jt < NJ; ++jt) {
+    st[jt] = zero4();
+    if (a.dST) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[jt][i] = a.dST[((size_t)bh * DK + 16 * wave + 4 * lg + i) * dv + col0 + 16 * jt];
+    }
+  }
+  issue(max(nch - 1, 0), std::integral_constant<int, 0>{});
+  issue(max(nch - 2, 0), std::integral_constant<int, 1>{});
+  issue(max(nch - 3, 0), std::integral_constant<int, 2>{});
+  issue(max(nch - 4, 0), std::integral_constant<int, 3>{});
+  put_dst(0);
+  store_do(nch - 1, std::integral_constant<int, 0>{}, 0);
+  lds_barrier();
+
+  auto body = [&](const int i, auto slotc) {
+    constexpr int S = decltype(slotc)::value, NXT = (S + 1) % NS, buf = S & 1;
+    const int x = nch - 1 - i;
+    float* out = dSc + (((size_t)bh * nch + x) * DK + 16 * wave + 4 * lg) * dv + col0;
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) out[(size_t)i2 * dv + 16 * jt] = st[jt][i2];
+    floatx4 cp[NJ], cr[NJ];
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) { cp[jt] = zero4(); cr[jt] = zero4(); }
+    if constexpr (DK == 16) {  // one 16-deep product
+      const shortx4 pa = words_to_shortx4(sp[S][0][0], sp[S][0][1]);
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt)
+        cp[jt] = mfma_k16(pa, *reinterpret_cast<const shortx4*>(&sDt[buf][16 * jt + lc][4 * lg]), cp[jt]);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KP; ++kb) {
+        const bf16x8 pa = __builtin_bit_cast(bf16x8, sp[S][kb]);
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) cp[jt] = mfma_k32(pa, ld_frag(&sDt[buf][16 * jt + lc][32 * kb + 8 * lg]), cp[jt]);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 ra = __builtin_bit_cast(bf16x8, sr[S][kb]);
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt) cr[jt] = mfma_k32(ra, tok_frag(&sDO[buf][0][0], LVO, 32 * kb, 16 * jt, lane), cr[jt]);
+    }
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) st[jt] = st[jt] - cp[jt] + cr[jt];
+    // the next chunk's dS^T and dO slice go to the other buffers (past the
+    // first chunk this writes unused data)
+    put_dst(buf ^ 1);
+    store_do(max(x - 1, 0), std::integral_constant<int, NXT>{}, buf ^ 1);
+    issue(max(x - NS, 0), slotc);
+    lds_barrier();
+  };
+  int i = 0;
+  for (; i + NS <= nch; i += NS) {
+    body(i, std::integral_constant<int, 0>{});
+    body(i + 1, std::integral_constant<int, 1>{});
+    body(i + 2, std::integral_constant<int, 2>{});
+    body(i + 3, std::integral_constant<int, 3>{});
+  }
+  if (i < nch) body(i, std::integral_constant<int, 0>{});
+  if (i + 1 < nch) body(i + 1, std::integral_constant<int, 1>{});
+  if (i + 2 < nch) body(i + 2, std::integral_constant<int, 2>{});
+  if (a.dS0) {
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) a.dS0[((size_t)bh * DK + 16 * wave + 4 * lg + i2) * dv + col0 + 16 * jt] = st[jt][i2];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Pass 3: one workgroup per (batch, head, chunk).  Phases (barriers between),
 // with LDS regions reused as operands die:
 //   A  stage Q, K; tril(Q K^T) and K K^T -> L, T (A and T are read by
@@ -720,17 +1093,34 @@ hipError_t launch_chain_dk(const BackwardArgs& a, float* dSc, hipStream_t st) {
   return hipGetLastError();
 }
 
+// bf16: P and R for every chunk, then the one-product chain
+template <int DK>
+hipError_t launch_chain_mat(const BackwardArgs& a, bf16_t* Pg, bf16_t* Rg, float* dSc, hipStream_t st) {
+  static_assert(TransLayout<DK>::total <= 80 * 1024, "two transition workgroups should fit a CU");
+  const long nchunks = (long)a.B * a.H * ((a.T + kC - 1) / kC);
+  hipLaunchKernelGGL((bwd_transition<DK>), dim3((unsigned)nchunks), dim3(kTransThreads), 0, st, a, Pg, Rg);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long bh = (long)a.B * a.H;
+  if (a.dv_ % 32 == 0)
+    hipLaunchKernelGGL((bwd_chain_mat<DK, 32>), dim3((unsigned)(bh * (a.dv_ / 32))), dim3(DK * 4), 0, st, a, Pg, Rg, dSc);
+  else
+    hipLaunchKernelGGL((bwd_chain_mat<DK, 16>), dim3((unsigned)(bh * (a.dv_ / 16))), dim3(DK * 4), 0, st, a, Pg, Rg, dSc);
+  return hipGetLastError();
+}
+
 template <class E>
-hipError_t launch_backward_e(const BackwardArgs& a, float* Sc, float* dSc, hipStream_t st) {
+hipError_t launch_backward_e(const BackwardArgs& a, float* Sc, float* dSc, bf16_t* Pg, bf16_t* Rg, hipStream_t st) {
   const long nchunks = (long)a.B * a.H * ((a.T + kC - 1) / kC);
   hipError_t e;
+  constexpr bool kB = sizeof(typename E::T) == 2;
   switch (a.dk_) {
-    case 16: e = launch_chain_dk<16, E>(a, dSc, st); break;
-    case 32: e = launch_chain_dk<32, E>(a, dSc, st); break;
-    case 64: e = launch_chain_dk<64, E>(a, dSc, st); break;
+    case 16: e = kB ? launch_chain_mat<16>(a, Pg, Rg, dSc, st) : launch_chain_dk<16, E>(a, dSc, st); break;
+    case 32: e = kB ? launch_chain_mat<32>(a, Pg, Rg, dSc, st) : launch_chain_dk<32, E>(a, dSc, st); break;
+    case 64: e = kB ? launch_chain_mat<64>(a, Pg, Rg, dSc, st) : launch_chain_dk<64, E>(a, dSc, st); break;
     case 128:
-      if constexpr (sizeof(typename E::T) == 2) {
-        e = launch_chain_dk<128, E>(a, dSc, st);
+      if constexpr (kB) {
+        e = launch_chain_mat<128>(a, Pg, Rg, dSc, st);
         break;
       }
       return hipErrorInvalidValue;
@@ -757,11 +1147,14 @@ __global__ __launch_bounds__(256) void zero_state(float* __restrict__ p, size_t 
 // of the workspace (the final state where a copy of S0 was put).
 bool pass1_pipelined(int bf16, const BackwardArgs& a) { return bf16 && a.dk_ == 128 && a.dv_ % 32 == 0; }
 
+// [Sc, dSc: fp32 nchunks x dk x dv][pipelined pass 1: final state, output]
+// [bf16: P nchunks x dk x dk, R^T nchunks x dk x 64]
 size_t delta_backward_workspace_bytes(int bf16, const BackwardArgs& a) {
   const size_t nchunks = (size_t)a.B * a.H * ((a.T + kC - 1) / kC);
   size_t n = 2 * nchunks * a.dk_ * a.dv_ * sizeof(float);
   if (pass1_pipelined(bf16, a))
     n += (size_t)a.B * a.H * a.dk_ * a.dv_ * sizeof(float) + (size_t)a.B * a.H * a.T * a.dv_ * sizeof(bf16_t);
+  if (bf16) n = (n + 255) / 256 * 256 + nchunks * a.dk_ * (a.dk_ + kC) * sizeof(bf16_t);
   return n;
 }
 
@@ -778,8 +1171,12 @@ hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, hipStream_t st
   }
   // pass 1: the state entering every chunk, from a forward kernel
   void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, delta_backward_workspace_bytes(bf16, a), st);
+  const size_t wsb = delta_backward_workspace_bytes(bf16, a);
+  hipError_t e = hipMallocAsync(&ws, wsb, st);
   if (e != hipSuccess) return e;
+  const size_t nchunks = (size_t)a.B * a.H * ((a.T + kC - 1) / kC);
+  bf16_t* Pg = bf16 ? reinterpret_cast<bf16_t*>(static_cast<char*>(ws) + wsb) - nchunks * a.dk_ * (a.dk_ + kC) : nullptr;
+  bf16_t* Rg = bf16 ? Pg + nchunks * a.dk_ * a.dk_ : nullptr;
   const size_t nst = (size_t)a.B * a.H * ((a.T + kC - 1) / kC) * a.dk_ * a.dv_;
   float* Sc = reinterpret_cast<float*>(ws);
   float* dSc = Sc + nst;
@@ -808,7 +1205,8 @@ hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, hipStream_t st
     e = launch_prefill_generic(PF_DELTA, bf16, a.dk_, f, st);
   }
   // passes 2 and 3
-  if (e == hipSuccess) e = bf16 ? launch_backward_e<BF16>(a, Sc, dSc, st) : launch_backward_e<F32>(a, Sc, dSc, st);
+  if (e == hipSuccess) e = bf16 ? launch_backward_e<BF16>(a, Sc, dSc, Pg, Rg, st)
+                              : launch_backward_e<F32>(a, Sc, dSc, Pg, Rg, st);
   const hipError_t fr = hipFreeAsync(ws, st);
   return e != hipSuccess ? e : fr;
 }
