@@ -633,13 +633,16 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
 
 // One workgroup per (batch, head, DVS value columns), DK / 16 waves: wave w
 // keeps dS rows 16w .. 16w + 15 of the slice as DVS / 16 accumulator tiles.
-// Per chunk (last to first): write dSn (fp32, for the gradient pass), then
+// Per chunk (last to first): write dSn for the gradient pass (bf16, the
+// precision that pass reads it in, in accumulator-tile order: tile (kt, jt)
+// of chunk c at ((c * dk/16 + kt) * dv/16 + jt) * 256, lane l's four rows
+// at 4l), then
 // dS <- dS - P dS + R^T dO with P rows and R^T rows loaded straight into
 // registers (NS chunks ahead) and dS^T, the dO slice read from LDS (double
 // buffered, one barrier per chunk).
 template <int DK, int DVS>
 __global__ __launch_bounds__(DK * 4) void bwd_chain_mat(BackwardArgs a, const bf16_t* __restrict__ Pg,
-                                                        const bf16_t* __restrict__ Rg, float* __restrict__ dSc) {
+                                                        const bf16_t* __restrict__ Rg, bf16_t* __restrict__ dSt) {
   constexpr int NTH = DK * 4, NJ = DVS / 16, LDT = DK + 16, LVO = DVS + 16, NS = 4;  // NS: chunks in flight (the prologue issues four)
   constexpr int KP = DK >= 32 ? DK / 32 : 1;
   constexpr int NVO = kC * DVS / 8, VPT = (NVO + NTH - 1) / NTH;
@@ -718,32 +721,49 @@ __global__ __launch_bounds__(DK * 4) void bwd_chain_mat(BackwardArgs a, const bf
   auto body = [&](const int i, auto slotc) {
     constexpr int S = decltype(slotc)::value, NXT = (S + 1) % NS, buf = S & 1;
     const int x = nch - 1 - i;
-    float* out = dSc + (((size_t)bh * nch + x) * DK + 16 * wave + 4 * lg) * dv + col0;
+    // every LDS fragment of the chunk first, then the products
+    bf16x8 fd[KP][NJ], fo[2][NJ];
 #pragma unroll
-    for (int jt = 0; jt < NJ; ++jt)
+    for (int kb = 0; kb < KP; ++kb)
 #pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) out[(size_t)i2 * dv + 16 * jt] = st[jt][i2];
+      for (int jt = 0; jt < NJ; ++jt) {
+        if constexpr (DK == 16) {
+          const shortx4 h = *reinterpret_cast<const shortx4*>(&sDt[buf][16 * jt + lc][4 * lg]);
+          fd[kb][jt] = __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(uint2, h).x, __builtin_bit_cast(uint2, h).y, 0u, 0u});
+        } else {
+          fd[kb][jt] = ld_frag(&sDt[buf][16 * jt + lc][32 * kb + 8 * lg]);
+        }
+      }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt) fo[kb][jt] = tok_frag(&sDO[buf][0][0], LVO, 32 * kb, 16 * jt, lane);
+    bf16_t* out = dSt + ((((size_t)bh * nch + x) * (DK / 16) + wave) * (dv / 16) + sl * NJ) * 256 + 4 * lane;
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) st4_bf16(out + 256 * jt, st[jt][0], st[jt][1], st[jt][2], st[jt][3]);
     floatx4 cp[NJ], cr[NJ];
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) { cp[jt] = zero4(); cr[jt] = zero4(); }
     if constexpr (DK == 16) {  // one 16-deep product
       const shortx4 pa = words_to_shortx4(sp[S][0][0], sp[S][0][1]);
 #pragma unroll
-      for (int jt = 0; jt < NJ; ++jt)
-        cp[jt] = mfma_k16(pa, *reinterpret_cast<const shortx4*>(&sDt[buf][16 * jt + lc][4 * lg]), cp[jt]);
+      for (int jt = 0; jt < NJ; ++jt) {
+        const u32x4 w = __builtin_bit_cast(u32x4, fd[0][jt]);
+        cp[jt] = mfma_k16(pa, words_to_shortx4(w[0], w[1]), cp[jt]);
+      }
     } else {
 #pragma unroll
       for (int kb = 0; kb < KP; ++kb) {
         const bf16x8 pa = __builtin_bit_cast(bf16x8, sp[S][kb]);
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) cp[jt] = mfma_k32(pa, ld_frag(&sDt[buf][16 * jt + lc][32 * kb + 8 * lg]), cp[jt]);
+        for (int jt = 0; jt < NJ; ++jt) cp[jt] = mfma_k32(pa, fd[kb][jt], cp[jt]);
       }
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const bf16x8 ra = __builtin_bit_cast(bf16x8, sr[S][kb]);
 #pragma unroll
-      for (int jt = 0; jt < NJ; ++jt) cr[jt] = mfma_k32(ra, tok_frag(&sDO[buf][0][0], LVO, 32 * kb, 16 * jt, lane), cr[jt]);
+      for (int jt = 0; jt < NJ; ++jt) cr[jt] = mfma_k32(ra, fo[kb][jt], cr[jt]);
     }
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) st[jt] = st[jt] - cp[jt] + cr[jt];
@@ -807,7 +827,12 @@ struct GradLayout {
   static constexpr int oW = oDB + kC * 4;  // phase-dependent work area
   // phases A, B
   static constexpr int aQ = oW, aK = aQ + ROWQ, aAt = aK + ROWQ, aTL = aAt + TRI;
-  static constexpr int endAB = aTL + FT;
+  // bf16 inputs: T and T^T (bf16, formed by block substitution), A^T, the
+  // blocks of L (off the diagonal bf16, on it fp32) and D_b = (I + L_bb)^-1;
+  // the fp32 T region aTL is not used then
+  static constexpr int aT = aTL + FT, aTt = aT + TRI, aAtt = aTt + TRI;
+  static constexpr int aLo = aAtt + TRI, aD = aLo + 6 * 256 * 2, aLd = aD + 4 * 256 * 2;
+  static constexpr int endAB = ES == 2 ? aLd + 4 * 16 * 20 * 4 : aTL + FT;
   // phases C, D: dO, dA, dA^T, bL, bL^T, K^T; then Q^T where bL was
   static constexpr int cDO = oW, cDA = cDO + ROWV, cDAt = cDA + TRI, cBL = cDAt + TRI, cBLt = cBL + TRI;
   static constexpr int dKt = cBLt + TRI, dQt = cBL;
@@ -847,13 +872,22 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
   const T* doh = reinterpret_cast<const T*>(a.dO) + (size_t)bh * Tn * DV;
   const T* bth = reinterpret_cast<const T*>(a.beta) + (size_t)bh * Tn;
   const float* S = Sc + (size_t)chunk * DK * DV;
+  // dSn: fp32 row-major (fp32 inputs), or bf16 in accumulator-tile order
+  // (bf16 inputs; written so by bwd_chain_mat)
   const float* dSn = dSc + (size_t)chunk * DK * DV;
+  const bf16_t* dSt = reinterpret_cast<const bf16_t*>(dSc) + (size_t)chunk * DK * DV;
 
   // ---- phase A ----
   T* sQ = reinterpret_cast<T*>(smem + L::aQ);
   T* sK = reinterpret_cast<T*>(smem + L::aK);
   T* sA = reinterpret_cast<T*>(smem + L::aAt);  // tril(Q K^T), row-major
   float* sTL = reinterpret_cast<float*>(smem + L::aTL);
+  bf16_t* sT = reinterpret_cast<bf16_t*>(smem + L::aT);
+  bf16_t* sTt = reinterpret_cast<bf16_t*>(smem + L::aTt);
+  bf16_t* sAtt = reinterpret_cast<bf16_t*>(smem + L::aAtt);
+  bf16_t* sLo = reinterpret_cast<bf16_t*>(smem + L::aLo);
+  bf16_t* sD = reinterpret_cast<bf16_t*>(smem + L::aD);
+  float* sLd = reinterpret_cast<float*>(smem + L::aLd);
   stage_rows<E, DK, NTH>(qh, DK, t0, nrow, sQ, LQ, nullptr, 0, tid);
   stage_rows<E, DK, NTH>(kh, DK, t0, nrow, sK, LQ, nullptr, 0, tid);
   if (tid < kC) {
@@ -862,7 +896,10 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
   }
   for (int i = tid; i < kC * kC; i += NTH) {  // tiles above the diagonal stay zero
     const int r = i >> 6, cc = i & 63;
-    if ((cc >> 4) > (r >> 4)) sA[r * LKT + cc] = E::cvt(0.f);
+    if ((cc >> 4) > (r >> 4)) {
+      sA[r * LKT + cc] = E::cvt(0.f);
+      if constexpr (kBf16) sAtt[cc * LKT + r] = E::cvt(0.f);
+    }
   }
   __syncthreads();
   for (int jb = wave; jb < 20; jb += NW) {
@@ -878,14 +915,68 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
       const int r = 16 * ti + 4 * lg + i;
       if (isA) {
         sA[r * LKT + cc] = E::cvt(cc <= r ? acc[i] : 0.f);
-      } else if (cc < r) {
-        sTL[cc * LTL + r] = sB[r] * acc[i];
-        sKK[r * LTL + cc] = acc[i];
+        if constexpr (kBf16) sAtt[cc * LKT + r] = E::cvt(cc <= r ? acc[i] : 0.f);
+      } else {
+        if (cc < r) sKK[r * LTL + cc] = acc[i];
+        if constexpr (kBf16) {
+          const float l = cc < r ? sB[r] * acc[i] : 0.f;
+          if (ti == tj) sLd[(16 * ti + 4 * lg + i) * 20 + lc] = l;
+          else sLo[((ti * (ti - 1) / 2 + tj) * 16 + 4 * lg + i) * 16 + lc] = f2bf(l);
+        } else if (cc < r) {
+          sTL[cc * LTL + r] = sB[r] * acc[i];
+        }
       }
     }
   }
   __syncthreads();
-  form_T<kBf16, NTH>(sTL, tid, wave, lane);
+  if constexpr (kBf16) {
+    // D_b: lane (block lg, column lc) solves (I + L_bb) x = e_lc
+    if (wave == 0) {
+      const float* lb = sLd + 16 * lg * 20;
+      float x[16];
+#pragma unroll
+      for (int m = 0; m < 16; ++m) x[m] = m == lc ? 1.f : 0.f;
+#pragma unroll
+      for (int i = 1; i < 16; ++i) {
+        float sacc = 0.f;
+#pragma unroll
+        for (int m = 0; m < i; ++m) sacc += lb[i * 20 + m] * x[m];
+        if (i > lc) x[i] = -sacc;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sD[(16 * lg + i) * 16 + lc] = f2bf(x[i]);
+    }
+    __syncthreads();
+    // T = (I + L)^-1 by block forward substitution on the identity's column
+    // tiles: T_ct,ct = D_ct, T_b,ct = -D_b sum_{ct<=j<b} L_bj T_j,ct; wave ct
+    // writes T (row-major) and T^T, zeros above the diagonal included
+    if (wave < 4) {
+      const int ct = wave;
+      auto blk = [&](const bf16_t* b) { return *reinterpret_cast<const shortx4*>(b + lc * 16 + 4 * lg); };
+      floatx4 tb[4];
+      shortx4 tb16[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (b < ct) {
+          tb[b] = zero4();
+        } else if (b == ct) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tb[b][i] = bf2f(sD[(16 * b + 4 * lg + i) * 16 + lc]);
+        } else {
+          floatx4 acc = zero4();
+          for (int j = ct; j < b; ++j) acc = mfma_k16(blk(sLo + (b * (b - 1) / 2 + j) * 256), tb16[j], acc);
+          tb[b] = -mfma_k16(blk(sD + 256 * b), acc_to_b16(acc), zero4());
+        }
+        tb16[b] = acc_to_b16(tb[b]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sT[(16 * b + 4 * lg + i) * LKT + 16 * ct + lc] = f2bf(tb[b][i]);
+        st4_bf16(sTt + (16 * ct + lc) * LKT + 16 * b + 4 * lg, tb[b][0], tb[b][1], tb[b][2], tb[b][3]);
+      }
+    }
+    __syncthreads();
+  } else {
+    form_T<kBf16, NTH>(sTL, tid, wave, lane);
+  }
 
   // ---- phase B: 16-column slices of dv, one per wave at a time ----
   for (int s = wave; s < NVT; s += NW) {
@@ -896,8 +987,18 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         Sv[kt][i] = S[(size_t)(16 * kt + 4 * lg + i) * DV + col];
-        dSv[kt][i] = dSn[(size_t)(16 * kt + 4 * lg + i) * DV + col];
+        if constexpr (!kBf16) dSv[kt][i] = dSn[(size_t)(16 * kt + 4 * lg + i) * DV + col];
       }
+    if constexpr (kBf16) {
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+        const uint2 w = *reinterpret_cast<const uint2*>(dSt + (kt * NVT + s) * 256 + 4 * lane);
+        dSv[kt][0] = bf2f((bf16_t)(w.x & 0xffffu));
+        dSv[kt][1] = bf2f((bf16_t)(w.x >> 16));
+        dSv[kt][2] = bf2f((bf16_t)(w.y & 0xffffu));
+        dSv[kt][3] = bf2f((bf16_t)(w.y >> 16));
+      }
+    }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -919,15 +1020,21 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
     }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      if constexpr (kBf16) ut[mt] = accB<kBf16>(zero4(), sTL + (16 * mt + lc) * LTL, xx, (mt | 1) + 1, lane);
-      else ut[mt] = accB<kBf16>(zero4(), sTL + (16 * mt + lc) * LTL, xx, mt + 1, lane);
-      const floatx4 d1 = accB_col<kBf16>(zero4(), sA + 16 * mt + lc, LKT, dOt, 4, lane);  // A^T dO
+      floatx4 d1;
+      if constexpr (kBf16) {
+        ut[mt] = accB<kBf16>(zero4(), sT + (16 * mt + lc) * LKT, xx, (mt | 1) + 1, lane);
+        d1 = accB<kBf16>(zero4(), sAtt + (16 * mt + lc) * LKT, dOt, 4, lane);  // A^T dO
+      } else {
+        ut[mt] = accB<kBf16>(zero4(), sTL + (16 * mt + lc) * LTL, xx, mt + 1, lane);
+        d1 = accB_col<kBf16>(zero4(), sA + 16 * mt + lc, LKT, dOt, 4, lane);  // A^T dO
+      }
       const floatx4 d2 = accB<kBf16>(zero4(), sK + (16 * mt + lc) * LQ, dSv, NKT, lane);
       du[mt] = d1 + d2;
     }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      dx[mt] = accB_col<kBf16>(zero4(), sTL + 16 * mt + lc, LTL, du, 4, lane);  // T^T du
+      if constexpr (kBf16) dx[mt] = accB<kBf16>(zero4(), sTt + (16 * mt + lc) * LKT, du, 4, lane);  // T^T du
+      else dx[mt] = accB_col<kBf16>(zero4(), sTL + 16 * mt + lc, LTL, du, 4, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * mt + 4 * lg + i;
@@ -1027,7 +1134,13 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
     for (int j = 0; j < NPT; ++j) {
       const int i = min(tid + NTH * j, NV4 - 1);
       bs[j] = reinterpret_cast<const float4*>(S)[i];
-      bd[j] = reinterpret_cast<const float4*>(dSn)[i];
+      if constexpr (kBf16) {  // lane-tile i: tile i / 64, lane i % 64 (its four rows of one column)
+        const uint2 w = *reinterpret_cast<const uint2*>(dSt + 4 * i);
+        bd[j] = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                            __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+      } else {
+        bd[j] = reinterpret_cast<const float4*>(dSn)[i];
+      }
     }
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
@@ -1035,9 +1148,15 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
       if (i >= NV4) continue;
       const int r = (4 * i) / DV, d = (4 * i) % DV;
       T* ps = sS + r * LS + d;
-      T* pd = sDS + r * LS + d;
       ps[0] = E::cvt(bs[j].x); ps[1] = E::cvt(bs[j].y); ps[2] = E::cvt(bs[j].z); ps[3] = E::cvt(bs[j].w);
-      pd[0] = E::cvt(bd[j].x); pd[1] = E::cvt(bd[j].y); pd[2] = E::cvt(bd[j].z); pd[3] = E::cvt(bd[j].w);
+      if constexpr (kBf16) {  // four rows of one column
+        const int tile = i >> 6, ln = i & 63, kt = tile / NVT, jt = tile - kt * NVT;
+        T* pd = sDS + (16 * kt + 4 * (ln >> 4)) * LS + 16 * jt + (ln & 15);
+        pd[0] = E::cvt(bd[j].x); pd[LS] = E::cvt(bd[j].y); pd[2 * LS] = E::cvt(bd[j].z); pd[3 * LS] = E::cvt(bd[j].w);
+      } else {
+        T* pd = sDS + r * LS + d;
+        pd[0] = E::cvt(bd[j].x); pd[1] = E::cvt(bd[j].y); pd[2] = E::cvt(bd[j].z); pd[3] = E::cvt(bd[j].w);
+      }
     }
   }
   __syncthreads();
@@ -1096,6 +1215,7 @@ hipError_t launch_chain_dk(const BackwardArgs& a, float* dSc, hipStream_t st) {
 // bf16: P and R for every chunk, then the one-product chain
 template <int DK>
 hipError_t launch_chain_mat(const BackwardArgs& a, bf16_t* Pg, bf16_t* Rg, float* dSc, hipStream_t st) {
+  bf16_t* dSt = reinterpret_cast<bf16_t*>(dSc);  // bf16 tile order (see bwd_chain_mat)
   static_assert(TransLayout<DK>::total <= 80 * 1024, "two transition workgroups should fit a CU");
   const long nchunks = (long)a.B * a.H * ((a.T + kC - 1) / kC);
   hipLaunchKernelGGL((bwd_transition<DK>), dim3((unsigned)nchunks), dim3(kTransThreads), 0, st, a, Pg, Rg);
@@ -1103,9 +1223,9 @@ hipError_t launch_chain_mat(const BackwardArgs& a, bf16_t* Pg, bf16_t* Rg, float
   if (e != hipSuccess) return e;
   const long bh = (long)a.B * a.H;
   if (a.dv_ % 32 == 0)
-    hipLaunchKernelGGL((bwd_chain_mat<DK, 32>), dim3((unsigned)(bh * (a.dv_ / 32))), dim3(DK * 4), 0, st, a, Pg, Rg, dSc);
+    hipLaunchKernelGGL((bwd_chain_mat<DK, 32>), dim3((unsigned)(bh * (a.dv_ / 32))), dim3(DK * 4), 0, st, a, Pg, Rg, dSt);
   else
-    hipLaunchKernelGGL((bwd_chain_mat<DK, 16>), dim3((unsigned)(bh * (a.dv_ / 16))), dim3(DK * 4), 0, st, a, Pg, Rg, dSc);
+    hipLaunchKernelGGL((bwd_chain_mat<DK, 16>), dim3((unsigned)(bh * (a.dv_ / 16))), dim3(DK * 4), 0, st, a, Pg, Rg, dSt);
   return hipGetLastError();
 }
 
