@@ -871,7 +871,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
   const T* vh = reinterpret_cast<const T*>(a.v) + (size_t)bh * Tn * DV;
   const T* doh = reinterpret_cast<const T*>(a.dO) + (size_t)bh * Tn * DV;
   const T* bth = reinterpret_cast<const T*>(a.beta) + (size_t)bh * Tn;
-  const float* S = Sc + (size_t)chunk * DK * DV;
+  const T* S = reinterpret_cast<const T*>(Sc) + (size_t)chunk * DK * DV;  // input type
   // dSn: fp32 row-major (fp32 inputs), or bf16 in accumulator-tile order
   // (bf16 inputs; written so by bwd_chain_mat)
   const float* dSn = dSc + (size_t)chunk * DK * DV;
@@ -986,7 +986,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
     for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        Sv[kt][i] = S[(size_t)(16 * kt + 4 * lg + i) * DV + col];
+        Sv[kt][i] = E::tof(S[(size_t)(16 * kt + 4 * lg + i) * DV + col]);
         if constexpr (!kBf16) dSv[kt][i] = dSn[(size_t)(16 * kt + 4 * lg + i) * DV + col];
       }
     if constexpr (kBf16) {
@@ -1129,11 +1129,14 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
   T* sDS = reinterpret_cast<T*>(smem + L::eDS);
   {  // S and dSn rows, fp32 -> operand type, 16-byte loads issued first
     constexpr int NV4 = DK * DV / 4, NPT = NV4 / NTH > 0 ? NV4 / NTH : 1;
-    float4 bs[NPT], bd[NPT];
+    constexpr int NVS = DK * DV / E::kVec, NPS = (NVS + NTH - 1) / NTH;  // 16-byte vectors of S
+    u32x4 bs[NPS];
+    float4 bd[NPT];
+#pragma unroll
+    for (int j = 0; j < NPS; ++j) bs[j] = reinterpret_cast<const u32x4*>(S)[min(tid + NTH * j, NVS - 1)];
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
       const int i = min(tid + NTH * j, NV4 - 1);
-      bs[j] = reinterpret_cast<const float4*>(S)[i];
       if constexpr (kBf16) {  // lane-tile i: tile i / 64, lane i % 64 (its four rows of one column)
         const uint2 w = *reinterpret_cast<const uint2*>(dSt + 4 * i);
         bd[j] = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
@@ -1147,8 +1150,6 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
       const int i = tid + NTH * j;
       if (i >= NV4) continue;
       const int r = (4 * i) / DV, d = (4 * i) % DV;
-      T* ps = sS + r * LS + d;
-      ps[0] = E::cvt(bs[j].x); ps[1] = E::cvt(bs[j].y); ps[2] = E::cvt(bs[j].z); ps[3] = E::cvt(bs[j].w);
       if constexpr (kBf16) {  // four rows of one column
         const int tile = i >> 6, ln = i & 63, kt = tile / NVT, jt = tile - kt * NVT;
         T* pd = sDS + (16 * kt + 4 * (ln >> 4)) * LS + 16 * jt + (ln & 15);
@@ -1157,6 +1158,13 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
         T* pd = sDS + r * LS + d;
         pd[0] = E::cvt(bd[j].x); pd[1] = E::cvt(bd[j].y); pd[2] = E::cvt(bd[j].z); pd[3] = E::cvt(bd[j].w);
       }
+    }
+#pragma unroll
+    for (int j = 0; j < NPS; ++j) {
+      const int i = tid + NTH * j;
+      if (NVS % NTH != 0 && i >= NVS) continue;
+      const int r = (E::kVec * i) / DV, d = (E::kVec * i) % DV;
+      *reinterpret_cast<u32x4*>(sS + r * LS + d) = bs[j];
     }
   }
   __syncthreads();

@@ -34,9 +34,9 @@ struct PrefillArgs {
   float* S;
   float* z;          // linear attention only
   int B, H, T, dv, use_init;
-  // backward pass only (generic kernel): when set, the state entering every
-  // chunk is written to Sc [B*H][ceil(T/64)][dk][dv] and neither o nor the
-  // final state is written
+  // backward pass only: when set, the state entering every chunk is written
+  // to Sc [B*H][ceil(T/64)][dk][dv] in the input type (generic kernel:
+  // neither o nor the final state is written then)
   float* Sc;
 };
 

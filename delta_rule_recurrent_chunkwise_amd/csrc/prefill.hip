@@ -213,11 +213,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = c * kC;
     if (a.Sc && chain) {  // the state entering chunk c, for the backward pass
-      float* sc = a.Sc + ((size_t)bh * nchunks + c) * DK * dv + sl * DVS;
+      // in the input type (the precision the gradient pass reads it in)
+      typename E::T* sc = reinterpret_cast<typename E::T*>(a.Sc) + ((size_t)bh * nchunks + c) * DK * dv + sl * DVS;
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[(size_t)(16 * kt + 4 * lg + i) * dv + 16 * cw + lc] = st[kt][i];
+        for (int i = 0; i < 4; ++i) sc[(size_t)(16 * kt + 4 * lg + i) * dv + 16 * cw + lc] = E::cvt(st[kt][i]);
     }
     __syncthreads();  // the previous chunk's readers of LDS are done
 

@@ -149,7 +149,7 @@ struct PipeArgs {
   float* S;
   int T, dv, use_init;
   int Tq;              // rows per head of q, k, k^: T, or T rounded up to 64 (gated)
-  float* Sc;           // if set: the state entering every chunk, [B*H][nch][dk][dv]
+  float* Sc;           // if set: the state entering every chunk, [B*H][nch][dk][dv] (bf16)
 };
 
 // Loads.  Each tile-loader wave owns whole tiles (Q, K, and, gated, K^) and
@@ -379,11 +379,13 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
           if constexpr (CAP) {  // the state entering chunk x, for the backward pass
             // row perm32(16t + 4lg + i) = 8lg + 32(t / 2) + 4(t % 2) + i: one
             // lane-dependent base, offsets uniform across the wave
-            float* scl = a.Sc + ((size_t)bh * nch + x) * kDK * dv + sl * kDVS + (size_t)(8 * lg) * dv + col;
+            // (bf16, the precision the gradient pass reads it in)
+            bf16_t* scl = reinterpret_cast<bf16_t*>(a.Sc) + ((size_t)bh * nch + x) * kDK * dv + sl * kDVS +
+                          (size_t)(8 * lg) * dv + col;
 #pragma unroll
             for (int t = 0; t < 8; ++t)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) scl[(size_t)(32 * (t >> 1) + 4 * (t & 1) + i) * dv] = st[t][i];
+              for (int i = 0; i < 4; ++i) scl[(size_t)(32 * (t >> 1) + 4 * (t & 1) + i) * dv] = f2bf(st[t][i]);
           }
           // Y = K S and O = Q S (shared S fragments), X = beta (V - Y); the
           // fragments of k-step kb+1 are loaded while kb computes.
