@@ -51,7 +51,12 @@
  *               the normaliser entering each chunk, or the chunk's decay
  *               (fp32);
  *             - deltanet_prefill_backward: 8 B*H*C*dk*dv bytes for the
- *               state entering and the gradient leaving every chunk.
+ *               state entering and the gradient leaving every chunk; with
+ *               bf16 inputs also 2 B*H*C*dk*(dk+64) bytes for every chunk's
+ *               P = W^T K and R^T = (Q - A W)^T (see that function), and,
+ *               when dk = 128 and dv % 32 == 0, 4 B*H*dk*dv + 2 B*H*T*dv
+ *               bytes that receive the forward pass's final state and
+ *               output.
  *           A failed allocation returns LA_ERR_LAUNCH.
  * Sizes.    B, H (or N, H) >= 1; T >= 0 for prefill, any length (the last
  *           64-token chunk may be partial).  T = 0 enqueues no work when
@@ -218,9 +223,12 @@ int gla_decode_step(const void *q, const void *k, const void *v, const void *g,
  * incoming state S and dSn the gradient of the state leaving it:
  *   du = A^T dO + K dSn, dX = T^T du, dV = diag(beta) dX,
  *   dQ = dO S^T + tril(dO u^T) K, dS = dSn + Q^T dO - K^T diag(beta) dX, ...
- * It recomputes the forward chunk states into a stream-ordered workspace of
- * 8 B*H*C*dk*dv bytes (C = ceil(T/64)); a failed allocation returns
- * LA_ERR_LAUNCH.  Sizes: dk, dv in {16, 32, 64, 128} for bf16, up to 64 for
+ * With W = T diag(beta) K the last one is dS = dSn - P dSn + R^T dO,
+ * P = W^T K, R = Q - A W; for bf16 inputs P and R are formed for all chunks
+ * at once and the walk over chunks is that one product per chunk.
+ * It recomputes the forward chunk states into a stream-ordered workspace
+ * (sizes under "Pointers" above; C = ceil(T/64)); a failed allocation
+ * returns LA_ERR_LAUNCH.  Sizes: dk, dv in {16, 32, 64, 128} for bf16, up to 64 for
  * float32.  T = 0 copies dST to dS0 (or zero-fills it).
  */
 int deltanet_prefill_backward(const void *q, const void *k, const void *v,
