@@ -75,8 +75,10 @@ ROW_PROFILES = [
      ["decode_kernel<128, 128, linattn::BF16, 4"]),
     ("delta_backward_B4_H16_T4096_d128.txt",
      "deltanet_prefill_backward B=4 H=16 T=4096 dk=dv=128 bf16: forward chunk states "
-     "(pipelined kernel with state capture), reverse chain, chunk-parallel gradients",
-     ["prefill_pipe<0, 32, true>", "bwd_chain<128, linattn::BF16, 32>", "bwd_grads<128, 128, linattn::BF16>"]),
+     "(pipelined kernel with state capture), transition pre-pass, reverse chain, "
+     "chunk-parallel gradients",
+     ["prefill_pipe<0, 32, true>", "bwd_transition<128>", "bwd_chain_mat<128, 32>",
+      "bwd_grads<128, 128, linattn::BF16>"]),
     ("prologue_B4_H16_T4096_d128.txt",
      "deltanet_prologue B=4 H=16 T=4096 dk=128 bf16, one beta logit per token shared by the heads",
      ["qk_prologue<128, linattn::BF16, true>", "beta_sigmoid<linattn::BF16>"]),
@@ -512,9 +514,10 @@ def bench_backward_row(la, workloads, torch, launches=5):
     per = th * 2 * (2 * w.dk + 2 * w.dv + 1) + th * 2 * (2 * w.dk + w.dv + 1)
     name, r = _row("deltanet_prefill_backward", f"deltanet_prefill_backward B={w.B} H={w.H} "
                    f"T={w.T} dk=dv={w.dk} bf16", us, med, per,
-                   "three passes: forward chunk states (pipelined kernel, states captured), reverse chain over "
-                   "chunks, chunk-parallel gradients; bytes are the inputs (q, k, v, beta, dO) "
-                   "and gradients (dq, dk, dv, dbeta) only")
+                   "four kernels: forward chunk states (pipelined kernel, states captured), "
+                   "chunk-parallel transition pre-pass (P = W^T K, R = Q - A W), reverse chain "
+                   "dS <- dS - P dS + R^T dO, chunk-parallel gradients; bytes are the inputs "
+                   "(q, k, v, beta, dO) and gradients (dq, dk, dv, dbeta) only")
     return {name: r}
 
 
