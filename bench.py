@@ -81,7 +81,7 @@ ROW_PROFILES = [
       "bwd_grads<128, 128, linattn::BF16>"]),
     ("prologue_B4_H16_T4096_d128.txt",
      "deltanet_prologue B=4 H=16 T=4096 dk=128 bf16, one beta logit per token shared by the heads",
-     ["qk_prologue<128, linattn::BF16, true>", "beta_sigmoid<linattn::BF16>"]),
+     ["qk_prologue<128, linattn::BF16, true>"]),
 ]
 
 
