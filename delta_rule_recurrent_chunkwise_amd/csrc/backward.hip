@@ -180,29 +180,33 @@ union Vec16U {
 template <class E, int D, int NTH = kThreads>
 __device__ __forceinline__ void stage_rows(const typename E::T* src, int sld, int t0, int nrow, typename E::T* dst,
                                            int ld, typename E::T* dstT, int ldT, int tid) {
+  typedef uint32_t w4 __attribute__((ext_vector_type(4)));
   constexpr int KV = E::kVec;
   constexpr int VPR = D / KV;  // 16-byte vectors per row
   constexpr int NV = kC * VPR;
   constexpr int NPT = (NV + NTH - 1) / NTH;
   const bool rows_fast = dstT != nullptr;
-  Vec16U<E> buf[NPT];
+  w4 buf[NPT];  // plain vectors: a union selected per lane would go through scratch memory
 #pragma unroll
   for (int j = 0; j < NPT; ++j) {
     const int i = min(tid + NTH * j, NV - 1);
     const int r = min(rows_fast ? i % kC : i / VPR, nrow - 1);
     const int vc = rows_fast ? i / kC : i % VPR;
-    buf[j].v = *reinterpret_cast<const Vec16*>(src + (size_t)(t0 + r) * sld + vc * KV);
+    buf[j] = *reinterpret_cast<const w4*>(src + (size_t)(t0 + r) * sld + vc * KV);
   }
+  const w4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int j = 0; j < NPT; ++j) {
     const int i = tid + NTH * j;
     if (NV % NTH != 0 && i >= NV) continue;
     const int r = rows_fast ? i % kC : i / VPR, d = (rows_fast ? i / kC : i % VPR) * KV;
-    if (r >= nrow) buf[j].v = Vec16{};
-    if (dst) *reinterpret_cast<Vec16*>(dst + r * ld + d) = buf[j].v;
+    const w4 w = r < nrow ? buf[j] : z;
+    if (dst) *reinterpret_cast<w4*>(dst + r * ld + d) = w;
     if (dstT) {
+      Vec16U<E> x;
+      x.v = __builtin_bit_cast(Vec16, w);
 #pragma unroll
-      for (int e = 0; e < KV; ++e) dstT[(d + e) * ldT + r] = buf[j].e[e];
+      for (int e = 0; e < KV; ++e) dstT[(d + e) * ldT + r] = x.e[e];
     }
   }
 }
@@ -837,7 +841,9 @@ struct GradLayout {
   static constexpr int cDO = oW, cDA = cDO + ROWV, cDAt = cDA + TRI, cBL = cDAt + TRI, cBLt = cBL + TRI;
   static constexpr int dKt = cBLt + TRI, dQt = cBL;
   static_assert(TQ <= 2 * TRI, "Q^T must fit where bL and its transpose were");
-  static constexpr int endCD = dKt + TQ;
+  // bf16: K and Q row-major after the four 64 x 64 tiles
+  static constexpr int dKr = cBLt + TRI, dQr = dKr + ROWQ;
+  static constexpr int endCD = ES == 2 ? dQr + ROWQ : dKt + TQ;
   // phase E: dO (kept), S, dSn
   static constexpr int eS = cDA, eDS = eS + ST;
   static constexpr int endE = eDS + ST;
@@ -1057,14 +1063,22 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
   T* sBL = reinterpret_cast<T*>(smem + L::cBL);
   T* sBLt = reinterpret_cast<T*>(smem + L::cBLt);
   stage_rows<E, DV, NTH>(doh, DV, t0, nrow, sDO, LV, nullptr, 0, tid);
+  // bf16: sDAt and sBLt hold dA and diag(beta) dL with their token columns
+  // permuted by tperm (A operands against the transpose reads of phase D);
+  // fp32: the transposes
   for (int i = tid; i < kC * kC; i += NTH) {  // tiles above the diagonal stay zero
     const int r = i >> 6, cc = i & 63;
     if ((cc >> 4) > (r >> 4)) {
       const T z = E::cvt(0.f);
       sDA[r * LKT + cc] = z;
-      sDAt[cc * LKT + r] = z;
       sBL[r * LKT + cc] = z;
-      sBLt[cc * LKT + r] = z;
+      if constexpr (kBf16) {
+        sDAt[r * LKT + tperm(cc)] = z;
+        sBLt[r * LKT + tperm(cc)] = z;
+      } else {
+        sDAt[cc * LKT + r] = z;
+        sBLt[cc * LKT + r] = z;
+      }
     }
   }
   __syncthreads();
@@ -1073,6 +1087,35 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
     const int t = isA ? jb : jb - 10;
     const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
     const int tj = t - ti * (ti + 1) / 2;
+    if constexpr (kBf16) {
+      // the transposed product: lane holds row r = 16 ti + lc, columns
+      // c0 .. c0 + 3 of dA = dO u^T (or of dX u^T), 8-byte stores
+      const floatx4 acc =
+          rowrow<kBf16>(zero4(), sU + (16 * tj + lc) * LV, (isA ? sDO : sDX) + (16 * ti + lc) * LV, DV, lane);
+      const int r = 16 * ti + lc, c0 = 16 * tj + 4 * lg;
+      if (isA) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = c0 + i <= r ? acc[i] : 0.f;
+        st4_bf16(reinterpret_cast<bf16_t*>(sDA) + r * LKT + c0, v[0], v[1], v[2], v[3]);
+        st4_bf16(reinterpret_cast<bf16_t*>(sDAt) + r * LKT + tperm(c0), v[0], v[1], v[2], v[3]);
+      } else {
+        float dl[4], p = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dl[i] = c0 + i < r ? -acc[i] : 0.f;
+          p += c0 + i < r ? dl[i] * sKK[r * LTL + c0 + i] : 0.f;  // rowsum(dL * K K^T)
+        }
+        p += __shfl_xor(p, 16);
+        p += __shfl_xor(p, 32);
+        if (lg == 0) atomicAdd(&sDB[r], p);
+        const float br = sB[r];
+        st4_bf16(reinterpret_cast<bf16_t*>(sBL) + r * LKT + c0, br * dl[0], br * dl[1], br * dl[2], br * dl[3]);
+        st4_bf16(reinterpret_cast<bf16_t*>(sBLt) + r * LKT + tperm(c0), br * dl[0], br * dl[1], br * dl[2],
+                 br * dl[3]);
+      }
+      continue;
+    }
     const floatx4 acc =
         rowrow<kBf16>(zero4(), (isA ? sDO : sDX) + (16 * ti + lc) * LV, sU + (16 * tj + lc) * LV, DV, lane);
     const int cc = 16 * tj + lc;
@@ -1098,12 +1141,44 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
   __syncthreads();
 
   // ---- phase D: each wave owns output tiles id = wave + 4 n of the 4 x NKT grid ----
+  constexpr int NTILE = 4 * NKT, NOWN = (NTILE + NW - 1) / NW;  // output tiles, per wave
+  floatx4 gq[NOWN], gk[NOWN];
+  if constexpr (kBf16) {
+    // K and Q row-major; every product over tokens reads them (and dA,
+    // diag(beta) dL) with the transpose read or against the permuted copies.
+    // Tiles are computed transposed: lane holds output row r = 16 ti + lc,
+    // columns 16 tk + 4 lg .. +3.
+    bf16_t* sKr = reinterpret_cast<bf16_t*>(smem + L::dKr);
+    bf16_t* sQr = reinterpret_cast<bf16_t*>(smem + L::dQr);
+    stage_rows<E, DK, NTH>(kh, DK, t0, nrow, reinterpret_cast<T*>(sKr), LQ, nullptr, 0, tid);
+    stage_rows<E, DK, NTH>(qh, DK, t0, nrow, reinterpret_cast<T*>(sQr), LQ, nullptr, 0, tid);
+    __syncthreads();
+    const bf16_t* bDA = reinterpret_cast<const bf16_t*>(sDA);
+    const bf16_t* bDAp = reinterpret_cast<const bf16_t*>(sDAt);
+    const bf16_t* bBL = reinterpret_cast<const bf16_t*>(sBL);
+    const bf16_t* bBLp = reinterpret_cast<const bf16_t*>(sBLt);
+#pragma unroll
+    for (int n = 0; n < NOWN; ++n) {
+      const int id = wave + NW * n, ti = id / NKT, tk = id - ti * NKT;
+      if (NTILE % NW != 0 && id >= NTILE) continue;
+      floatx4 xq = zero4(), xk = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = tok_frag(sKr, LQ, 32 * kb, 16 * tk, lane);
+        xq = mfma_k32(kf, ld_frag(bDAp + (16 * ti + lc) * LKT + 32 * kb + 8 * lg), xq);           // dA K
+        xk = mfma_k32(kf, ld_frag(bBLp + (16 * ti + lc) * LKT + 32 * kb + 8 * lg), xk);           // (b dL) K
+        xk = mfma_k32(kf, tok_frag(bBL, LKT, 32 * kb, 16 * ti, lane), xk);                        // (b dL)^T K
+        xk = mfma_k32(tok_frag(sQr, LQ, 32 * kb, 16 * tk, lane), tok_frag(bDA, LKT, 32 * kb, 16 * ti, lane), xk);  // dA^T Q
+      }
+      gq[n] = xq;
+      gk[n] = xk;
+    }
+    __syncthreads();
+  } else {
   T* sKt = reinterpret_cast<T*>(smem + L::dKt);
   T* sQt = reinterpret_cast<T*>(smem + L::dQt);
   stage_rows<E, DK, NTH>(kh, DK, t0, nrow, nullptr, 0, sKt, LKT, tid);
   __syncthreads();
-  constexpr int NTILE = 4 * NKT, NOWN = (NTILE + NW - 1) / NW;  // output tiles, per wave
-  floatx4 gq[NOWN], gk[NOWN];
 #pragma unroll
   for (int n = 0; n < NOWN; ++n) {
     const int id = wave + NW * n, ti = id / NKT, tk = id - ti * NKT;
@@ -1123,6 +1198,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
     gk[n] += rowrow<kBf16>(zero4(), sDAt + (16 * ti + lc) * LKT, sQt + (16 * tk + lc) * LKT, kC, lane);
   }
   __syncthreads();
+  }
 
   // ---- phase E ----
   T* sS = reinterpret_cast<T*>(smem + L::eS);
@@ -1174,6 +1250,20 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
   for (int n = 0; n < NOWN; ++n) {
     const int id = wave + NW * n, ti = id / NKT, tk = id - ti * NKT;
     if (NTILE % NW != 0 && id >= NTILE) continue;
+    if constexpr (kBf16) {  // transposed tiles, as gq and gk: row r = 16 ti + lc
+      const floatx4 q1 = rowrow<kBf16>(zero4(), sS + (16 * tk + lc) * LS, sDO + (16 * ti + lc) * LV, DV, lane);
+      const floatx4 k1 = rowrow<kBf16>(zero4(), sDS + (16 * tk + lc) * LS, sU + (16 * ti + lc) * LV, DV, lane);
+      const floatx4 k2 = rowrow<kBf16>(zero4(), sS + (16 * tk + lc) * LS, sDX + (16 * ti + lc) * LV, DV, lane);
+      const int r = 16 * ti + lc, d0 = 16 * tk + 4 * lg;
+      const float br = sB[r];
+      if (r < nrow) {
+        st4_bf16(reinterpret_cast<bf16_t*>(dqo) + (size_t)r * DK + d0, gq[n][0] + q1[0], gq[n][1] + q1[1],
+                 gq[n][2] + q1[2], gq[n][3] + q1[3]);
+        st4_bf16(reinterpret_cast<bf16_t*>(dko) + (size_t)r * DK + d0, gk[n][0] + k1[0] - br * k2[0],
+                 gk[n][1] + k1[1] - br * k2[1], gk[n][2] + k1[2] - br * k2[2], gk[n][3] + k1[3] - br * k2[3]);
+      }
+      continue;
+    }
     const floatx4 q1 = rowrow<kBf16>(zero4(), sDO + (16 * ti + lc) * LV, sS + (16 * tk + lc) * LS, DV, lane);
     const floatx4 k1 = rowrow<kBf16>(zero4(), sU + (16 * ti + lc) * LV, sDS + (16 * tk + lc) * LS, DV, lane);
     const floatx4 k2 = rowrow<kBf16>(zero4(), sDX + (16 * ti + lc) * LV, sS + (16 * tk + lc) * LS, DV, lane);
