@@ -877,7 +877,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
   const T* vh = reinterpret_cast<const T*>(a.v) + (size_t)bh * Tn * DV;
   const T* doh = reinterpret_cast<const T*>(a.dO) + (size_t)bh * Tn * DV;
   const T* bth = reinterpret_cast<const T*>(a.beta) + (size_t)bh * Tn;
-  const T* S = reinterpret_cast<const T*>(Sc) + (size_t)chunk * DK * DV;  // input type
+  // S: fp32 row-major (fp32 inputs), or bf16 in accumulator-tile order
+  const T* S = reinterpret_cast<const T*>(Sc) + (size_t)chunk * DK * DV;
   // dSn: fp32 row-major (fp32 inputs), or bf16 in accumulator-tile order
   // (bf16 inputs; written so by bwd_chain_mat)
   const float* dSn = dSc + (size_t)chunk * DK * DV;
@@ -992,17 +993,24 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
     for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        Sv[kt][i] = E::tof(S[(size_t)(16 * kt + 4 * lg + i) * DV + col]);
-        if constexpr (!kBf16) dSv[kt][i] = dSn[(size_t)(16 * kt + 4 * lg + i) * DV + col];
+        if constexpr (!kBf16) {
+          Sv[kt][i] = S[(size_t)(16 * kt + 4 * lg + i) * DV + col];
+          dSv[kt][i] = dSn[(size_t)(16 * kt + 4 * lg + i) * DV + col];
+        }
       }
     if constexpr (kBf16) {
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt) {
         const uint2 w = *reinterpret_cast<const uint2*>(dSt + (kt * NVT + s) * 256 + 4 * lane);
+        const uint2 v = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(S) + (kt * NVT + s) * 256 + 4 * lane);
         dSv[kt][0] = bf2f((bf16_t)(w.x & 0xffffu));
         dSv[kt][1] = bf2f((bf16_t)(w.x >> 16));
         dSv[kt][2] = bf2f((bf16_t)(w.y & 0xffffu));
         dSv[kt][3] = bf2f((bf16_t)(w.y >> 16));
+        Sv[kt][0] = bf2f((bf16_t)(v.x & 0xffffu));
+        Sv[kt][1] = bf2f((bf16_t)(v.x >> 16));
+        Sv[kt][2] = bf2f((bf16_t)(v.y & 0xffffu));
+        Sv[kt][3] = bf2f((bf16_t)(v.y >> 16));
       }
     }
 #pragma unroll
@@ -1203,44 +1211,48 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
   // ---- phase E ----
   T* sS = reinterpret_cast<T*>(smem + L::eS);
   T* sDS = reinterpret_cast<T*>(smem + L::eDS);
-  {  // S and dSn rows, fp32 -> operand type, 16-byte loads issued first
-    constexpr int NV4 = DK * DV / 4, NPT = NV4 / NTH > 0 ? NV4 / NTH : 1;
-    constexpr int NVS = DK * DV / E::kVec, NPS = (NVS + NTH - 1) / NTH;  // 16-byte vectors of S
-    u32x4 bs[NPS];
-    float4 bd[NPT];
+  if constexpr (kBf16) {
+    // S and dSn in accumulator-tile order: lane-tile i (tile i / 64, lane
+    // i % 64) holds four rows of one column; all loads first
+    constexpr int NLT = DK * DV / 4, NPT = (NLT + NTH - 1) / NTH;
+    uint2 bs[NPT], bd[NPT];
 #pragma unroll
-    for (int j = 0; j < NPS; ++j) bs[j] = reinterpret_cast<const u32x4*>(S)[min(tid + NTH * j, NVS - 1)];
+    for (int j = 0; j < NPT; ++j) {
+      const int i = min(tid + NTH * j, NLT - 1);
+      bs[j] = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(S) + 4 * i);
+      bd[j] = *reinterpret_cast<const uint2*>(dSt + 4 * i);
+    }
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      const int i = tid + NTH * j;
+      if (NLT % NTH != 0 && i >= NLT) continue;
+      const int tile = i >> 6, ln = i & 63, kt = tile / NVT, jt = tile - kt * NVT;
+      const int o = (16 * kt + 4 * (ln >> 4)) * LS + 16 * jt + (ln & 15);
+      bf16_t* ps = reinterpret_cast<bf16_t*>(sS) + o;
+      bf16_t* pd = reinterpret_cast<bf16_t*>(sDS) + o;
+      ps[0] = (bf16_t)(bs[j].x & 0xffffu); ps[LS] = (bf16_t)(bs[j].x >> 16);
+      ps[2 * LS] = (bf16_t)(bs[j].y & 0xffffu); ps[3 * LS] = (bf16_t)(bs[j].y >> 16);
+      pd[0] = (bf16_t)(bd[j].x & 0xffffu); pd[LS] = (bf16_t)(bd[j].x >> 16);
+      pd[2 * LS] = (bf16_t)(bd[j].y & 0xffffu); pd[3 * LS] = (bf16_t)(bd[j].y >> 16);
+    }
+  } else {  // fp32 rows
+    constexpr int NV4 = DK * DV / 4, NPT = NV4 / NTH > 0 ? NV4 / NTH : 1;
+    float4 bs[NPT], bd[NPT];
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
       const int i = min(tid + NTH * j, NV4 - 1);
-      if constexpr (kBf16) {  // lane-tile i: tile i / 64, lane i % 64 (its four rows of one column)
-        const uint2 w = *reinterpret_cast<const uint2*>(dSt + 4 * i);
-        bd[j] = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
-                            __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
-      } else {
-        bd[j] = reinterpret_cast<const float4*>(dSn)[i];
-      }
+      bs[j] = reinterpret_cast<const float4*>(S)[i];
+      bd[j] = reinterpret_cast<const float4*>(dSn)[i];
     }
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
       const int i = tid + NTH * j;
       if (i >= NV4) continue;
       const int r = (4 * i) / DV, d = (4 * i) % DV;
-      if constexpr (kBf16) {  // four rows of one column
-        const int tile = i >> 6, ln = i & 63, kt = tile / NVT, jt = tile - kt * NVT;
-        T* pd = sDS + (16 * kt + 4 * (ln >> 4)) * LS + 16 * jt + (ln & 15);
-        pd[0] = E::cvt(bd[j].x); pd[LS] = E::cvt(bd[j].y); pd[2 * LS] = E::cvt(bd[j].z); pd[3 * LS] = E::cvt(bd[j].w);
-      } else {
-        T* pd = sDS + r * LS + d;
-        pd[0] = E::cvt(bd[j].x); pd[1] = E::cvt(bd[j].y); pd[2] = E::cvt(bd[j].z); pd[3] = E::cvt(bd[j].w);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NPS; ++j) {
-      const int i = tid + NTH * j;
-      if (NVS % NTH != 0 && i >= NVS) continue;
-      const int r = (E::kVec * i) / DV, d = (E::kVec * i) % DV;
-      *reinterpret_cast<u32x4*>(sS + r * LS + d) = bs[j];
+      T* ps = sS + r * LS + d;
+      T* pd = sDS + r * LS + d;
+      ps[0] = E::cvt(bs[j].x); ps[1] = E::cvt(bs[j].y); ps[2] = E::cvt(bs[j].z); ps[3] = E::cvt(bs[j].w);
+      pd[0] = E::cvt(bd[j].x); pd[1] = E::cvt(bd[j].y); pd[2] = E::cvt(bd[j].z); pd[3] = E::cvt(bd[j].w);
     }
   }
   __syncthreads();

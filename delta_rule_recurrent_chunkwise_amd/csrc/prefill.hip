@@ -213,12 +213,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = c * kC;
     if (a.Sc && chain) {  // the state entering chunk c, for the backward pass
-      // in the input type (the precision the gradient pass reads it in)
-      typename E::T* sc = reinterpret_cast<typename E::T*>(a.Sc) + ((size_t)bh * nchunks + c) * DK * dv + sl * DVS;
+      // in the input type (the precision the gradient pass reads it in):
+      // fp32 row-major; bf16 in accumulator-tile order (tile (kt, jt) of the
+      // chunk at (kt * dv/16 + jt) * 256, lane l's four rows at 4l)
+      typename E::T* sc = reinterpret_cast<typename E::T*>(a.Sc) + ((size_t)bh * nchunks + c) * DK * dv;
+      if constexpr (sizeof(typename E::T) == 2) {
+        const int jt = (sl * DVS + 16 * cw) / 16;
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
+        for (int kt = 0; kt < NKT; ++kt)
+          *reinterpret_cast<uint2*>(sc + ((size_t)kt * (dv / 16) + jt) * 256 + 4 * lane) =
+              make_uint2(pack2(st[kt][0], st[kt][1]), pack2(st[kt][2], st[kt][3]));
+      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[(size_t)(16 * kt + 4 * lg + i) * dv + 16 * cw + lc] = E::cvt(st[kt][i]);
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[(size_t)(16 * kt + 4 * lg + i) * dv + sl * DVS + 16 * cw + lc] = st[kt][i];
+      }
     }
     __syncthreads();  // the previous chunk's readers of LDS are done
 

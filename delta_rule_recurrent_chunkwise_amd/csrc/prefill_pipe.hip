@@ -149,7 +149,7 @@ struct PipeArgs {
   float* S;
   int T, dv, use_init;
   int Tq;              // rows per head of q, k, k^: T, or T rounded up to 64 (gated)
-  float* Sc;           // if set: the state entering every chunk, [B*H][nch][dk][dv] (bf16)
+  float* Sc;           // if set: the state entering every chunk, bf16, [B*H][nch] x dk x dv in accumulator-tile order
 };
 
 // Loads.  Each tile-loader wave owns whole tiles (Q, K, and, gated, K^) and
@@ -379,13 +379,19 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
           if constexpr (CAP) {  // the state entering chunk x, for the backward pass
             // row perm32(16t + 4lg + i) = 8lg + 32(t / 2) + 4(t % 2) + i: one
             // lane-dependent base, offsets uniform across the wave
-            // (bf16, the precision the gradient pass reads it in)
-            bf16_t* scl = reinterpret_cast<bf16_t*>(a.Sc) + ((size_t)bh * nch + x) * kDK * dv + sl * kDVS +
-                          (size_t)(8 * lg) * dv + col;
+            // (bf16, the precision the gradient pass reads it in), in
+            // accumulator-tile order: tile (kt, jt) of chunk x at
+            // ((x * dk/16 + kt) * dv/16 + jt) * 256, lane l's four rows at 4l.
+            // Accumulator rows 16t + 4lg + i hold key channels 32(t/2) + 8lg +
+            // 4(t%2) + i: tile 2(t/2) + lg/2, lane group 2(lg%2) + t%2.
+            bf16_t* scb = reinterpret_cast<bf16_t*>(a.Sc) + ((size_t)bh * nch + x) * kDK * dv;
+            const int jt = sl * (kDVS / 16) + wave;
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) scl[(size_t)(32 * (t >> 1) + 4 * (t & 1) + i) * dv] = f2bf(st[t][i]);
+            for (int t = 0; t < 8; ++t) {
+              const int kt = 2 * (t >> 1) + (lg >> 1), lgt = 2 * (lg & 1) + (t & 1);
+              *reinterpret_cast<uint2*>(scb + ((size_t)kt * (dv / 16) + jt) * 256 + 4 * (16 * lgt + lc)) =
+                  make_uint2(pack2(st[t][0], st[t][1]), pack2(st[t][2], st[t][3]));
+            }
           }
           // Y = K S and O = Q S (shared S fragments), X = beta (V - Y); the
           // fragments of k-step kb+1 are loaded while kb computes.
