@@ -339,19 +339,24 @@ __global__ __launch_bounds__(256) void la_chunk_out(const bf16_t* __restrict__ q
   const int trow = 8 * lg + ((lane >> 2) & 3);
   const int tcol = 4 * (lane & 3);
   bf16_t* oc = o + ((size_t)bh * T + t0) * DV;
+  // the output tiles are formed transposed (operands swapped): lane (lc, lg)
+  // holds token r = 16 mt + lc, value columns 16 jt + 4 lg .. +3, so one
+  // scale per lane and one 8-byte store
+  const int r = 16 * mt + lc;
+  const float rs_r = GLA ? __expf(sg[GLA ? r : 0]) : sden[GLA ? 0 : r];  // decay of Q S_c, or the denominator
 #pragma unroll
   for (int jt = 0; jt < DV / 16; ++jt) {
     // phi(Q) S_c (a separate accumulator: the 16-deep and 32-deep opcodes
     // must not share one accumulation chain)
     floatx4 aqs = zero4();
     if constexpr (DK == 16) {
-      aqs = mfma_k16(*reinterpret_cast<const shortx4_t*>(&sq[16 * mt + lc][4 * lg]),
-                     ld_tr(&ss[4 * lg + ((lane >> 2) & 3)][16 * jt + tcol]), aqs);
+      aqs = mfma_k16(ld_tr(&ss[4 * lg + ((lane >> 2) & 3)][16 * jt + tcol]),
+                     *reinterpret_cast<const shortx4_t*>(&sq[16 * mt + lc][4 * lg]), aqs);
     } else {
 #pragma unroll
       for (int kb = 0; kb < DK / 32; ++kb) {
         const bf16x8 b = cat_tr(ld_tr(&ss[32 * kb + trow][16 * jt + tcol]), ld_tr(&ss[32 * kb + 4 + trow][16 * jt + tcol]));
-        aqs = mfma_k32(*reinterpret_cast<const bf16x8*>(&sq[16 * mt + lc][32 * kb + 8 * lg]), b, aqs);
+        aqs = mfma_k32(b, *reinterpret_cast<const bf16x8*>(&sq[16 * mt + lc][32 * kb + 8 * lg]), aqs);
       }
     }
     // tril(.) V over tokens 0 .. 16 mt + 15
@@ -360,14 +365,14 @@ __global__ __launch_bounds__(256) void la_chunk_out(const bf16_t* __restrict__ q
     for (int kb = 0; kb < 2; ++kb) {
       if (32 * kb > 16 * mt + 15) break;
       const bf16x8 b = cat_tr(ld_tr(&sv[32 * kb + trow][16 * jt + tcol]), ld_tr(&sv[32 * kb + 4 + trow][16 * jt + tcol]));
-      acc = mfma_k32(*reinterpret_cast<const bf16x8*>(&sa[16 * mt + lc][32 * kb + 8 * lg]), b, acc);
+      acc = mfma_k32(b, *reinterpret_cast<const bf16x8*>(&sa[16 * mt + lc][32 * kb + 8 * lg]), acc);
     }
+    float v4[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * mt + 4 * lg + i;
-      const float val = GLA ? acc[i] + aqs[i] * __expf(sg[GLA ? r : 0]) : (acc[i] + aqs[i]) / sden[r];
-      if (r < nrow) oc[(size_t)r * DV + 16 * jt + lc] = f2bf(val);
-    }
+    for (int i = 0; i < 4; ++i) v4[i] = GLA ? acc[i] + aqs[i] * rs_r : (acc[i] + aqs[i]) / rs_r;
+    if (r < nrow)
+      *reinterpret_cast<uint2*>(oc + (size_t)r * DV + 16 * jt + 4 * lg) =
+          make_uint2(pack2(v4[0], v4[1]), pack2(v4[2], v4[3]));
   }
 }
 
