@@ -53,6 +53,14 @@ def test_backward_ragged_and_many_heads(dtype, dk, dv):
         _check(B, H, T, dk, dv, dtype, 700 + T, True, True)
 
 
+@pytest.mark.parametrize("dk,dv", [(16, 16), (64, 32), (16, 128), (128, 16), (128, 128)])
+def test_backward_long_enough_for_the_chain_loop(dk, dv):
+    """Six chunks and a ragged tail (T = 327): the reverse chain's prefetch
+    ring runs its main loop (four chunks) and its tail, at every width of
+    the value slices (16 and 32 columns) and the 16-deep product (dk = 16)."""
+    _check(1, 2, 327, dk, dv, torch.bfloat16, 800 + dk + dv, True, True)
+
+
 def test_backward_of_empty_sequence():
     """T = 0: the initial state's gradient is the final state's."""
     dev = require_gpu()
