@@ -17,12 +17,16 @@
 //   dK = dA^T Q + u dSn^T - diag(beta) dX S^T + (diag(beta) dL) K + (diag(beta) dL)^T K
 //   dS = dSn + Q^T dO - K^T diag(beta) dX   (the gradient of the state entering)
 //
-// Three passes:
-//   1. the forward chunk recurrence (the generic prefill kernel) writes the
-//      state entering every chunk to a workspace (fp32);
-//   2. bwd_chain walks the chunks backwards, one workgroup per (batch, head,
-//      slice of value columns) -- the columns of dS are independent, as those
-//      of S are forward -- and writes dSn of every chunk to a workspace;
+// Passes:
+//   1. the forward chunk recurrence (the pipelined kernel for bf16 with
+//      dk = 128 and dv % 32 == 0, the generic one otherwise) writes the state
+//      entering every chunk to a workspace, in the input type;
+//   2. bf16: bwd_transition forms every chunk's P = W^T K and R = Q - A W at
+//      once, and bwd_chain_mat walks the chunks backwards with
+//      dS <- dS - P dS + R^T dO (see there); fp32: bwd_chain walks them with
+//      the formulas above.  One workgroup per (batch, head, slice of value
+//      columns) -- the columns of dS are independent, as those of S are
+//      forward -- and dSn of every chunk goes to a workspace;
 //   3. bwd_grads forms every chunk's dQ, dK, dV, dbeta at once, one workgroup
 //      per chunk, from its S and dSn.
 // Inputs and outputs have the input dtype; the products run on bf16 MFMA
@@ -36,8 +40,7 @@ namespace linattn {
 namespace {
 
 constexpr int kC = 64;
-constexpr int kThreads = 256;        // bwd_grads
-constexpr int kWaves = kThreads / 64;
+constexpr int kThreads = 256;        // default staging width
 constexpr int kChainThreads = 512;   // bwd_chain: 8 waves, so the products spread wider
 constexpr int kGradThreads = 512;    // bwd_grads: likewise
 constexpr int LTL = kC + 4;  // fp32 row stride of T and its transpose
