@@ -479,8 +479,11 @@ constexpr int kTransThreads = 512;
 //   3. D_b = (I + L_bb)^-1 (one lane per block column, fp32);
 //   4. W by block forward substitution, W_b = D_b (beta K_b - sum_{j<b} L_bj W_j),
 //      one wave per 16-column tile of W, stored as W^T (token columns permuted);
-//   5. P (row-major, dk x dk) and R^T (dk x 64, token columns permuted) to
-//      global memory.
+//   5. P and R^T (token columns permuted) to global memory, in the order the
+//      chain's MFMA fragments are read: P as [dk/16][dk/32][64 lanes][8],
+//      fragment (w, kb), lane (lc, lg) = P[16w + lc][32kb + 8lg .. +7]
+//      (dk = 16: [1][64][4], P[lc][4lg .. +3]); R^T as [dk/16][2][64][8]
+//      likewise.  A wave's store of one tile then covers 512 contiguous bytes.
 template <int DK>
 __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, bf16_t* __restrict__ Pg,
                                                                 bf16_t* __restrict__ Rg) {
@@ -623,7 +626,12 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
       for (int kb = 0; kb < 2; ++kb)
         acc = mfma_k32(tok_frag(sK, LQ, 32 * kb, 16 * et, lane), ld_frag(sWt + (16 * dt + lc) * LT + 32 * kb + 8 * lg),
                        acc);
-      st4_bf16(Pc + (size_t)(16 * dt + lc) * DK + 16 * et + 4 * lg, acc[0], acc[1], acc[2], acc[3]);
+      // P[16 dt + lc][16 et + 4 lg .. +3]: fragment (dt, et / 2), lane
+      // lc + 16 (2 (et % 2) + lg / 2), half lg % 2
+      const size_t o = DK == 16 ? ((size_t)dt * 64 + lc + 16 * lg) * 4
+                                : (((size_t)dt * (DK / 32) + (et >> 1)) * 64 + lc + 16 * (2 * (et & 1) + (lg >> 1))) * 8 +
+                                      4 * (lg & 1);
+      st4_bf16(Pc + o, acc[0], acc[1], acc[2], acc[3]);
     } else {
       const int t = jb - NPJ, rt = t / NT, dt = t - rt * NT;
       floatx4 acc = zero4();
@@ -633,7 +641,9 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
       float rv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) rv[i] = bf2f(sQ[(16 * rt + 4 * lg + i) * LQ + 16 * dt + lc]) - acc[i];
-      st4_bf16(Rc + (size_t)(16 * dt + lc) * kC + tperm(16 * rt + 4 * lg), rv[0], rv[1], rv[2], rv[3]);
+      // R^T[16 dt + lc][tperm(16 rt + 4 lg) .. +3]: fragment (dt, rt / 2),
+      // lane lc + 16 lg, half rt % 2
+      st4_bf16(Rc + (((size_t)dt * 2 + (rt >> 1)) * 64 + lc + 16 * lg) * 8 + 4 * (rt & 1), rv[0], rv[1], rv[2], rv[3]);
     }
   }
 }
@@ -644,9 +654,10 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
 // precision that pass reads it in, in accumulator-tile order: tile (kt, jt)
 // of chunk c at ((c * dk/16 + kt) * dv/16 + jt) * 256, lane l's four rows
 // at 4l), then
-// dS <- dS - P dS + R^T dO with P rows and R^T rows loaded straight into
-// registers (NS chunks ahead) and dS^T, the dO slice read from LDS (double
-// buffered, one barrier per chunk).
+// dS <- dS - P dS + R^T dO with the fragments of P and R^T loaded straight
+// into registers (NS chunks ahead; bwd_transition stores them in fragment
+// order, so a wave's load is 1 KB contiguous) and dS^T, the dO slice read
+// from LDS (double buffered, one barrier per chunk).
 template <int DK, int DVS>
 __global__ __launch_bounds__(DK * 4) void bwd_chain_mat(BackwardArgs a, const bf16_t* __restrict__ Pg,
                                                         const bf16_t* __restrict__ Rg, bf16_t* __restrict__ dSt) {
@@ -660,7 +671,6 @@ __global__ __launch_bounds__(DK * 4) void bwd_chain_mat(BackwardArgs a, const bf
   const int bh = wid / nsl, sl = wid - bh * nsl;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
   const int Tn = a.T, nch = (Tn + kC - 1) / kC;
-  const int prow = 16 * wave + lc;  // the row of P and R^T this lane's fragments come from
   const bf16_t* doh = reinterpret_cast<const bf16_t*>(a.dO) + (size_t)bh * Tn * dv + sl * DVS;
 
   // register slots of NS chunks: P fragments, R^T fragments, the dO slice;
@@ -670,19 +680,19 @@ __global__ __launch_bounds__(DK * 4) void bwd_chain_mat(BackwardArgs a, const bf
   auto issue = [&](int x, auto slotc) {
     constexpr int S = decltype(slotc)::value;
     const size_t cb = (size_t)bh * nch + x;
-    const bf16_t* pr = Pg + (cb * DK + prow) * DK;
+    // fragment (wave, kb) of P and of R^T: 64 lanes x 16 bytes, contiguous
 #pragma unroll
     for (int kb = 0; kb < KP; ++kb) {
       if constexpr (DK == 16) {
-        const uint2 h = *reinterpret_cast<const uint2*>(pr + 4 * lg);
+        const uint2 h = *reinterpret_cast<const uint2*>(Pg + cb * DK * DK + (size_t)lane * 4);
         sp[S][kb] = u32x4{h.x, h.y, 0u, 0u};
       } else {
-        sp[S][kb] = *reinterpret_cast<const u32x4*>(pr + 32 * kb + 8 * lg);
+        sp[S][kb] = *reinterpret_cast<const u32x4*>(Pg + cb * DK * DK + (((size_t)wave * KP + kb) * 64 + lane) * 8);
       }
     }
-    const bf16_t* rr = Rg + (cb * DK + prow) * kC;
-    sr[S][0] = *reinterpret_cast<const u32x4*>(rr + 8 * lg);
-    sr[S][1] = *reinterpret_cast<const u32x4*>(rr + 32 + 8 * lg);
+    const bf16_t* rr = Rg + cb * DK * kC + (size_t)wave * 2 * 64 * 8 + (size_t)lane * 8;
+    sr[S][0] = *reinterpret_cast<const u32x4*>(rr);
+    sr[S][1] = *reinterpret_cast<const u32x4*>(rr + 64 * 8);
     const int t0 = x * kC, nrow = min(kC, Tn - t0);
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
