@@ -48,7 +48,8 @@ const char* la_strerror(int code) {
              "dk and dv <= 64 for deltanet_prefill_backward)";
     case LA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch or a workspace allocation";
     case LA_ERR_ALIGN:
-      return "q, k and v (prefill; and dO, backward) and S (decode) must be 16-byte aligned";
+      return "q, k, v and o (prefill; and dO, dq, dk, dv, backward; q and k in and out, prologue) "
+             "and S (decode) must be 16-byte aligned";
     default: return "unknown error code";
   }
 }
@@ -60,7 +61,7 @@ int la_prefill(const void* q, const void* k, const void* v, void* o, float* S, f
   if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
   if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1, true)) return LA_ERR_SHAPE;
   if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return LA_ERR_ALIGN;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LA_ERR_ALIGN;
   linattn::PrefillArgs a{q, k, v, nullptr, nullptr, o, S, z, B, H, T, dv, use_initial_state ? 1 : 0};
   return launch_rc(linattn::launch_prefill(linattn::PF_LA, dtype == LA_DTYPE_BF16, dk, a,
                                            static_cast<hipStream_t>(stream)));
@@ -86,7 +87,7 @@ int deltanet_prefill(const void* q, const void* k, const void* v, const void* be
   if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1, true)) return LA_ERR_SHAPE;
   if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
   if (g && dtype == LA_DTYPE_F32 && dk > 64) return LA_ERR_UNSUPPORTED_DIM;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return LA_ERR_ALIGN;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LA_ERR_ALIGN;
   linattn::PrefillArgs a{q, k, v, beta, g, o, S, nullptr, B, H, T, dv, use_initial_state ? 1 : 0};
   return launch_rc(linattn::launch_prefill(g ? linattn::PF_GATED : linattn::PF_DELTA, dtype == LA_DTYPE_BF16, dk, a,
                                            static_cast<hipStream_t>(stream)));
@@ -112,7 +113,7 @@ int gated_deltanet_prefill(const void* q, const void* k, const void* v, const vo
   if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
   if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1, true)) return LA_ERR_SHAPE;
   if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return LA_ERR_ALIGN;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LA_ERR_ALIGN;
   linattn::PrefillArgs a{q, k, v, beta, g, o, S, nullptr, B, H, T, dv, use_initial_state ? 1 : 0};
   return launch_rc(linattn::launch_prefill(linattn::PF_SGATED, dtype == LA_DTYPE_BF16, dk, a,
                                            static_cast<hipStream_t>(stream)));
@@ -138,7 +139,7 @@ int gla_prefill(const void* q, const void* k, const void* v, const void* g, void
   if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
   if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1, true)) return LA_ERR_SHAPE;
   if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return LA_ERR_ALIGN;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LA_ERR_ALIGN;
   linattn::PrefillArgs a{q, k, v, nullptr, g, o, S, nullptr, B, H, T, dv, use_initial_state ? 1 : 0};
   return launch_rc(linattn::launch_prefill(linattn::PF_GLA, dtype == LA_DTYPE_BF16, dk, a,
                                            static_cast<hipStream_t>(stream)));
@@ -165,7 +166,9 @@ int deltanet_prefill_backward(const void* q, const void* k, const void* v, const
   if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1, true)) return LA_ERR_SHAPE;
   if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
   if (dtype == LA_DTYPE_F32 && (dk > 64 || dv > 64)) return LA_ERR_UNSUPPORTED_DIM;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO)) return LA_ERR_ALIGN;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(dq) || !aligned16(dk_out) ||
+      !aligned16(dv_out))
+    return LA_ERR_ALIGN;
   linattn::BackwardArgs a{q, k, v, beta, S0, dO, dST, dq, dk_out, dv_out, dbeta, dS0, B, H, T, dk, dv};
   return launch_rc(linattn::launch_delta_backward(dtype == LA_DTYPE_BF16, a, static_cast<hipStream_t>(stream)));
 }

@@ -1065,7 +1065,9 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * mt + 4 * lg + i;
-        if (r < nrow) reinterpret_cast<T*>(a.dv)[((size_t)bh * Tn + t0 + r) * DV + col] = E::cvt(sB[r] * dx[mt][i]);
+        if constexpr (!kBf16) {
+          if (r < nrow) reinterpret_cast<T*>(a.dv)[((size_t)bh * Tn + t0 + r) * DV + col] = E::cvt(sB[r] * dx[mt][i]);
+        }
         sU[r * LV + col] = E::cvt(ut[mt][i]);
         sDX[r * LV + col] = E::cvt(dx[mt][i]);
         float p = res[mt][i] * dx[mt][i];  // rowsum over this slice's 16 columns
@@ -1076,6 +1078,20 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
     }
   }
   __syncthreads();
+  if constexpr (kBf16) {  // dV = diag(beta) dX, from its rows in LDS with 16-byte stores
+    constexpr int NVD = kC * DV / 8;
+    for (int v = tid; v < NVD; v += NTH) {
+      const int r = v / (DV / 8), c8 = (v % (DV / 8)) * 8;
+      if (r >= nrow) continue;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(sDX) + r * LV + c8);
+      const float br = sB[r];
+      u32x4 y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        y[e] = pack2(br * __uint_as_float(x[e] << 16), br * __uint_as_float(x[e] & 0xffff0000u));
+      *reinterpret_cast<u32x4*>(reinterpret_cast<bf16_t*>(a.dv) + ((size_t)bh * Tn + t0 + r) * DV + c8) = y;
+    }
+  }
 
   // ---- phase C ----
   T* sDO = reinterpret_cast<T*>(smem + L::cDO);

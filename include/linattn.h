@@ -34,9 +34,11 @@
  *           beta, g and o.  The state S and normaliser z are always float32.
  *           bf16 outputs are rounded to nearest even.
  * Pointers. Device pointers (hipMalloc'd or equivalent), owned by the caller.
- *           q, k, v of the prefill entry points (and dO of the backward)
- *           and S of the decode entry points must be 16-byte aligned (they
- *           are read in 16-byte vectors).  o must not alias any input.  S (and z) are read and written.  The
+ *           q, k, v and o of the prefill entry points (and dO, dq, dk, dv
+ *           of the backward) and S of the decode entry points must be
+ *           16-byte aligned (they are read or written in vectors of up to
+ *           16 bytes); LA_ERR_ALIGN otherwise.  o must not alias any input.
+ *           S (and z) are read and written.  The
  *           library keeps no state between calls; calls are re-entrant.  It
  *           allocates device memory in three cases, each a stream-ordered
  *           workspace (hipMallocAsync on `stream`, released with

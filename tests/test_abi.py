@@ -115,6 +115,7 @@ def test_scalar_gated_entry_points_validate_like_the_others():
         assert fn(B=0) == SHAPE
         assert fn(dk=96) == DIM
         assert fn(q=MISALIGNED) == ALIGN
+        assert fn(o=MISALIGNED) == ALIGN
     for fn in (_gdn_decode, _gla_decode):
         assert fn(dt=5) == DTYPE
         assert fn(N=0) == SHAPE
@@ -150,6 +151,9 @@ def test_backward_validation():
     assert _bwd(dt=0, dv=128) == DIM
     assert _bwd(dO=MISALIGNED) == ALIGN
     assert _bwd(q=MISALIGNED) == ALIGN
+    for out in ("dq", "dk_", "dv_"):  # written in 8- and 16-byte vectors
+        assert _bwd(**{out: MISALIGNED}) == ALIGN
+    assert _bwd(db=MISALIGNED) != ALIGN  # dbeta is written element by element
 
 
 @pytest.mark.parametrize("missing", ["qi", "ki", "qo", "ko"])
@@ -227,6 +231,8 @@ def test_float32_gated_prefill_limited_to_dk_64():
 def test_misaligned_vector_pointers():
     assert _la_prefill(q=MISALIGNED) == ALIGN
     assert _dn_prefill(v=MISALIGNED) == ALIGN
+    assert _la_prefill(o=MISALIGNED) == ALIGN  # outputs are written in vectors too
+    assert _dn_prefill(o=MISALIGNED) == ALIGN
     assert _la_decode(S=MISALIGNED) == ALIGN
     assert _dn_decode(S=MISALIGNED) == ALIGN
 
