@@ -17,9 +17,9 @@ Functions (both follow the article "From GPT-2 to Kimi K3, explained"):
                      channel, g [B,H,T,dk]) applied to S before each read.
 ``gla_recurrent``    section "Gated Delta Net", the additive cache with a
                      forgetting factor: S <- a_t S + k_t^T v_t, o_t = q_t S.
-``delta_backward``   reverse-mode gradient of the (ungated) delta rule, token
-                     by token: dq, dk, dv, dbeta and dS0 for the loss
-                     sum do . o + sum dS_T * S_T.
+``delta_backward``   reverse-mode gradient of the delta rule, ungated or with
+                     either gate, token by token: dq, dk, dv, dbeta, dS0
+                     (and dg) for the loss sum do . o + sum dS_T * S_T.
 ``qk_prologue``      section "DeltaNet (Fast Weight Programmers)", the layer's
                      q, k = normalize(silu(.)) (and an optional scale).
 ``beta_sigmoid``     the same layer's beta = sigmoid(logits), broadcast over
@@ -64,8 +64,8 @@ def _bind(lib):
     lib.orc_delta_recurrent.restype = i
     lib.orc_gla_recurrent.argtypes = [i, i, i, i, i, d, d, d, d, i, d, d, d, i]
     lib.orc_gla_recurrent.restype = i
-    lib.orc_delta_backward.argtypes = [i, i, i, i, i, d, d, d, d, i, d, d, d,
-                                       d, d, d, d, d, i]
+    lib.orc_delta_backward.argtypes = [i, i, i, i, i, d, d, d, d, d, i, i, d, d, d,
+                                       d, d, d, d, d, d, i]
     lib.orc_delta_backward.restype = i
     lib.orc_qk_prologue.argtypes = [ctypes.c_long, i, d, i, i, ctypes.c_double, d]
     lib.orc_qk_prologue.restype = i
@@ -215,17 +215,28 @@ def gla_recurrent(q, k, v, g=None, S0=None, nthreads: int = 0, lib=None):
     return o, S
 
 
-def delta_backward(q, k, v, beta, dO, S0=None, dST=None, nthreads: int = 0, lib=None):
-    """Gradients of the delta rule for the loss sum(dO * o) + sum(dST * S_T).
-    q, k [B,H,T,dk]; v, dO [B,H,T,dv]; beta [B,H,T] (one dtype); S0 and dST
-    [B,H,dk,dv] or None.  Returns (dq, dk, dv, dbeta, dS0) as float64."""
+def delta_backward(q, k, v, beta, dO, S0=None, dST=None, g=None, nthreads: int = 0,
+                   lib=None):
+    """Gradients of the delta rule (g None) or the gated delta rule for the
+    loss sum(dO * o) + sum(dST * S_T).  q, k [B,H,T,dk]; v, dO [B,H,T,dv];
+    beta [B,H,T]; g log-decay, [B,H,T] per token or [B,H,T,dk] per key
+    channel (one dtype with the others); S0 and dST [B,H,dk,dv] or None.
+    Returns (dq, dk, dv, dbeta, dS0) as float64, and dg (g's shape) after
+    them when g is given."""
     lib = lib or load()
     B, H, T, dk = q.shape
     dv = v.shape[-1]
-    bufs = [_as_buffer(t) for t in (q, k, v, beta, dO)]
+    tensors = [q, k, v, beta, dO] + ([g] if g is not None else [])
+    bufs = [_as_buffer(t) for t in tensors]
     dts = {b[2] for b in bufs}
     if len(dts) != 1:
-        raise ValueError("q, k, v, beta and dO must share a dtype")
+        raise ValueError("q, k, v, beta, dO (and g) must share a dtype")
+    per_channel = 0
+    if g is not None:
+        if tuple(g.shape) == (B, H, T, dk):
+            per_channel = 1
+        elif tuple(g.shape) != (B, H, T):
+            raise ValueError(f"g must be [B,H,T] or [B,H,T,dk], got {tuple(g.shape)}")
     s0, s0p = _state64(S0, (B, H, dk, dv))
     dst, dstp = _state64(dST, (B, H, dk, dv))
     dq = np.empty((B, H, T, dk), np.float64)
@@ -233,13 +244,18 @@ def delta_backward(q, k, v, beta, dO, S0=None, dST=None, nthreads: int = 0, lib=
     dvv = np.empty((B, H, T, dv), np.float64)
     db = np.empty((B, H, T), np.float64)
     dS0 = np.empty((B, H, dk, dv), np.float64)
+    dg = np.empty(tuple(g.shape), np.float64) if g is not None else None
     rc = lib.orc_delta_backward(B, H, T, dk, dv, bufs[0][1], bufs[1][1], bufs[2][1],
-                                bufs[3][1], dts.pop(), s0p, bufs[4][1], dstp,
+                                bufs[3][1], bufs[5][1] if g is not None else None,
+                                per_channel, dts.pop(), s0p, bufs[4][1], dstp,
                                 dq.ctypes.data, dkk.ctypes.data, dvv.ctypes.data,
-                                db.ctypes.data, dS0.ctypes.data, int(nthreads))
+                                db.ctypes.data, dS0.ctypes.data,
+                                dg.ctypes.data if g is not None else None, int(nthreads))
     if rc != 0:
         raise MemoryError("oracle allocation failed")
-    return dq, dkk, dvv, db, dS0
+    if g is None:
+        return dq, dkk, dvv, db, dS0
+    return dq, dkk, dvv, db, dS0, dg
 
 
 def qk_prologue(x, apply_silu: bool = True, scale: float = 1.0, lib=None):

@@ -307,6 +307,14 @@ int orc_gla_recurrent(int B, int H, int T, int dk, int dv,
     return fail ? -1 : 0;
 }
 
+/* ga[i] = exp(g) of token tok (tok = bh * T + t) for key row i: one gate per
+ * token, or one per key channel; 1 without a gate */
+static void decay_row(const void *g, int per_channel, int dt, size_t tok, int dk, double *ga)
+{
+    for (int i = 0; i < dk; i++)
+        ga[i] = !g ? 1.0 : exp(rd(g, per_channel ? tok * (size_t)dk + i : tok, dt));
+}
+
 /*
  * Reverse-mode gradient of the ungated delta rule, one token at a time, for
  * the loss  sum_t do_t . o_t + sum dS_T * S_T  (do the output gradient, dS_T
@@ -321,18 +329,28 @@ int orc_gla_recurrent(int B, int H, int T, int dk, int dv,
  *   dbeta= du . (v - S^T k)
  *   dr   = -beta du                     (r = S^T k)
  *   dk  += S dr ;  dS += k dr^T         (the gradient of the state before t)
+ * With a gate g (the decays of sections "Gated Delta Net" and "KDA / Kimi
+ * Linear", as in orc_delta_recurrent: S_a = exp(g_t) S, one scalar per token,
+ * or row i of S times exp(g_t,i), one per key channel), the steps above run
+ * on the decayed state S_a in place of S, and then
+ *   dg   = sum of dS_a * S_a            (over the whole state per token, over
+ *                                        row i per key channel)
+ *   dS   = exp(g_t) dS_a                (row-wise per key channel)
+ * where dS_a is the gradient left after the last step above.
  * The states before every token are kept (recomputed forward), so memory is
  * T * dk * dv doubles per head: for small cases only.  S0 may be NULL (zero
- * start), dST may be NULL (no final-state gradient).  dO has the inputs'
- * dtype.  Outputs (float64): dq, dk [B,H,T,dk], dv [B,H,T,dv], dbeta [B,H,T],
- * dS0 [B,H,dk,dv] (any may be NULL).  Returns 0, or -1 on allocation failure.
+ * start), dST may be NULL (no final-state gradient), g may be NULL (no gate;
+ * dg is then not written).  dO has the inputs' dtype.  Outputs (float64): dq,
+ * dk [B,H,T,dk], dv [B,H,T,dv], dbeta [B,H,T], dS0 [B,H,dk,dv], dg with g's
+ * shape (any may be NULL).  Returns 0, or -1 on allocation failure.
  */
 int orc_delta_backward(int B, int H, int T, int dk, int dv,
                        const void *q, const void *k, const void *v,
-                       const void *beta, int dt, const double *S0,
+                       const void *beta, const void *g, int g_per_channel,
+                       int dt, const double *S0,
                        const void *dO, const double *dST,
                        double *dq, double *dkk, double *dvv, double *dbeta,
-                       double *dS0, int nthreads)
+                       double *dS0, double *dg, int nthreads)
 {
     int fail = 0;
     set_threads(nthreads);
@@ -346,10 +364,13 @@ int orc_delta_backward(int B, int H, int T, int dk, int dv,
         double *u = malloc(sizeof(double) * (size_t)dv);
         double *du = malloc(sizeof(double) * (size_t)dv);
         double *dov = malloc(sizeof(double) * (size_t)dv);
-        if (!Sall || !dS || !kt || !r || !u || !du || !dov) {
+        double *Sa = malloc(sizeof(double) * ss);
+        double *ga = malloc(sizeof(double) * (size_t)dk);
+        if (!Sall || !dS || !kt || !r || !u || !du || !dov || !Sa || !ga) {
 #pragma omp atomic write
             fail = 1;
             free(Sall); free(dS); free(kt); free(r); free(u); free(du); free(dov);
+            free(Sa); free(ga);
             continue;
         }
         const size_t sbase = (size_t)bh * ss;
@@ -357,32 +378,42 @@ int orc_delta_backward(int B, int H, int T, int dk, int dv,
         for (size_t i = 0; i < ss; i++)
             Sall[i] = S0 ? S0[sbase + i] : 0.0;
         for (int t = 0; t < T; t++) {
-            const double *S = Sall + (size_t)t * ss;
             double *Sn = Sall + (size_t)(t + 1) * ss;
             const size_t qk_row = ((size_t)bh * T + t) * dk;
             const size_t v_row = ((size_t)bh * T + t) * dv;
             const double b = rd(beta, (size_t)bh * T + t, dt);
+            /* the decayed state S_a (S itself without a gate) */
+            decay_row(g, g_per_channel, dt, (size_t)bh * T + t, dk, ga);
+            for (int i = 0; i < dk; i++) {
+                for (int j = 0; j < dv; j++)
+                    Sa[(size_t)i * dv + j] = ga[i] * Sall[(size_t)t * ss + (size_t)i * dv + j];
+            }
             for (int i = 0; i < dk; i++)
                 kt[i] = rd(k, qk_row + i, dt);
             for (int j = 0; j < dv; j++) {
                 r[j] = 0.0;
                 for (int i = 0; i < dk; i++)
-                    r[j] += S[(size_t)i * dv + j] * kt[i];
+                    r[j] += Sa[(size_t)i * dv + j] * kt[i];
                 u[j] = (rd(v, v_row + j, dt) - r[j]) * b;
             }
             for (int i = 0; i < dk; i++)
                 for (int j = 0; j < dv; j++)
-                    Sn[(size_t)i * dv + j] = S[(size_t)i * dv + j] + kt[i] * u[j];
+                    Sn[(size_t)i * dv + j] = Sa[(size_t)i * dv + j] + kt[i] * u[j];
         }
         /* backward */
         for (size_t i = 0; i < ss; i++)
             dS[i] = dST ? dST[sbase + i] : 0.0;
         for (int t = T - 1; t >= 0; t--) {
-            const double *S = Sall + (size_t)t * ss;        /* before token t */
+            const double *S = Sa;                           /* before token t, decayed */
             const double *Sn = Sall + (size_t)(t + 1) * ss; /* after token t */
             const size_t qk_row = ((size_t)bh * T + t) * dk;
             const size_t v_row = ((size_t)bh * T + t) * dv;
             const double b = rd(beta, (size_t)bh * T + t, dt);
+            decay_row(g, g_per_channel, dt, (size_t)bh * T + t, dk, ga);
+            for (int i = 0; i < dk; i++) {
+                for (int j = 0; j < dv; j++)
+                    Sa[(size_t)i * dv + j] = ga[i] * Sall[(size_t)t * ss + (size_t)i * dv + j];
+            }
             for (int i = 0; i < dk; i++)
                 kt[i] = rd(k, qk_row + i, dt);
             for (int j = 0; j < dv; j++)
@@ -426,14 +457,31 @@ int orc_delta_backward(int B, int H, int T, int dk, int dv,
                 if (dkk)
                     dkk[qk_row + i] = acc;
             }
-            /* the gradient of the state before token t: dS += k dr^T, dr = -b du */
+            /* the gradient of the decayed state: dS += k dr^T, dr = -b du */
             for (int i = 0; i < dk; i++)
                 for (int j = 0; j < dv; j++)
                     dS[(size_t)i * dv + j] -= b * kt[i] * du[j];
+            /* through the decay S_a = exp(g) S: dg, and the gradient of S */
+            if (g) {
+                double gsum = 0.0;
+                for (int i = 0; i < dk; i++) {
+                    double gi = 0.0;
+                    for (int j = 0; j < dv; j++)
+                        gi += dS[(size_t)i * dv + j] * Sa[(size_t)i * dv + j];
+                    if (g_per_channel && dg)
+                        dg[qk_row + i] = gi;
+                    gsum += gi;
+                    for (int j = 0; j < dv; j++)
+                        dS[(size_t)i * dv + j] *= ga[i];
+                }
+                if (!g_per_channel && dg)
+                    dg[(size_t)bh * T + t] = gsum;
+            }
         }
         if (dS0)
             memcpy(dS0 + sbase, dS, sizeof(double) * ss);
         free(Sall); free(dS); free(kt); free(r); free(u); free(du); free(dov);
+        free(Sa); free(ga);
     }
     return fail ? -1 : 0;
 }

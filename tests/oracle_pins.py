@@ -514,6 +514,105 @@ def pin_delta_backward_autograd(lib):
         _close(g, t.grad.numpy(), tol=1e-11, what=f"d{name} vs autograd")
 
 
+def _gated_loss(q, k, v, beta, g, S0, dO, dST, lib):
+    o, S = oracle.delta_recurrent(q, k, v, beta, g, S0, lib=lib)
+    return float(np.sum(o * dO) + np.sum(S * dST))
+
+
+def pin_gated_backward_finite_differences(lib):
+    """With either gate (one decay per token, one per key channel), every
+    gradient the backward returns, dg included, matches central differences
+    of the gated forward oracle's loss (float64)."""
+    rng = _rng(32)
+    B, H, T, dk, dv = 1, 2, 6, 3, 4
+    for per_channel in (False, True):
+        q, k, v, beta, g = _delta_inputs(rng, B, H, T, dk, dv, gated=True, gate_scale=0.5)
+        g = np.ascontiguousarray(g if per_channel else g[..., 0])
+        S0 = rng.standard_normal((B, H, dk, dv))
+        dO = rng.standard_normal((B, H, T, dv))
+        dST = rng.standard_normal((B, H, dk, dv))
+        grads = oracle.delta_backward(q, k, v, beta, dO, S0, dST, g=g, lib=lib)
+        args = dict(q=q, k=k, v=v, beta=beta, S0=S0, g=g)
+        h = 1e-6
+        for name, gr in zip(("q", "k", "v", "beta", "S0", "g"), grads):
+            x = args[name]
+            num = np.empty_like(x)
+            for idx in np.ndindex(x.shape):
+                saved = x[idx]
+                x[idx] = saved + h
+                lp = _gated_loss(q, k, v, beta, g, S0, dO, dST, lib)
+                x[idx] = saved - h
+                lm = _gated_loss(q, k, v, beta, g, S0, dO, dST, lib)
+                x[idx] = saved
+                num[idx] = (lp - lm) / (2 * h)
+            _close(gr, num, tol=1e-6,
+                   what=f"d{name} vs finite differences ({'channel' if per_channel else 'token'} gate)")
+
+
+def pin_gated_backward_autograd(lib):
+    """With a per-channel gate, the backward equals torch autograd through a
+    plain float64 loop (decay the key rows of S, read with k, correct with
+    beta (v - r), write k^T u, read with q) at a few dozen tokens."""
+    rng = _rng(33)
+    B, H, T, dk, dv = 1, 2, 40, 8, 6
+    q, k, v, beta, g = _delta_inputs(rng, B, H, T, dk, dv, gated=True, gate_scale=0.25)
+    S0 = rng.standard_normal((B, H, dk, dv))
+    dO = rng.standard_normal((B, H, T, dv))
+    dST = rng.standard_normal((B, H, dk, dv))
+    tq, tk, tv, tb, tS0, tg = (torch.tensor(x, dtype=torch.float64, requires_grad=True)
+                               for x in (q, k, v, beta, S0, g))
+    S = tS0
+    outs = []
+    for t in range(T):
+        S = torch.exp(tg[:, :, t])[..., :, None] * S
+        kt = tk[:, :, t]
+        r = (kt[..., :, None] * S).sum(-2)
+        u = tb[:, :, t, None] * (tv[:, :, t] - r)
+        S = S + kt[..., :, None] * u[..., None, :]
+        outs.append((tq[:, :, t][..., :, None] * S).sum(-2))
+    o = torch.stack(outs, 2)
+    loss = (o * torch.from_numpy(dO)).sum() + (S * torch.from_numpy(dST)).sum()
+    loss.backward()
+    grads = oracle.delta_backward(q, k, v, beta, dO, S0, dST, g=g, lib=lib)
+    for name, gr, t in zip(("q", "k", "v", "beta", "S0", "g"), grads, (tq, tk, tv, tb, tS0, tg)):
+        _close(gr, t.grad.numpy(), tol=1e-11, what=f"d{name} vs autograd (channel gate)")
+
+
+def pin_gated_backward_rescaling_identity(lib):
+    """One decay per token: dividing S_t by the cumulative decay Gamma_t
+    turns the gated rule into the ungated one with q_t scaled by Gamma_t and
+    v_t divided by it (the erase I - beta k k^T is scale free), and the final
+    state is Gamma_T times the rescaled one.  So the gradient of
+    G_t = log Gamma_t is q_t . dq_t - v_t . dv_t (plus dST . S_T at t = T),
+    and dg_t is the sum of those from t to the end.  With g = 0 both gates
+    give the ungated gradients; a per-channel gate with equal channels gives
+    the per-token one, and its dg summed over the channels."""
+    rng = _rng(34)
+    B, H, T, dk, dv = 2, 2, 50, 8, 5
+    q, k, v, beta, g = _delta_inputs(rng, B, H, T, dk, dv, gated=True, gate_scale=0.3)
+    gt = np.ascontiguousarray(g[..., 0])
+    S0 = rng.standard_normal((B, H, dk, dv))
+    dO = rng.standard_normal((B, H, T, dv))
+    dST = rng.standard_normal((B, H, dk, dv))
+    dq, dk_, dv_, db, dS0, dg = oracle.delta_backward(q, k, v, beta, dO, S0, dST, g=gt, lib=lib)
+    _, ST = oracle.delta_recurrent(q, k, v, beta, gt, S0, lib=lib)
+    dG = np.sum(q * dq, -1) - np.sum(v * dv_, -1)
+    dG[..., -1] += np.sum(dST * ST, axis=(-2, -1))
+    _close(dg, np.flip(np.cumsum(np.flip(dG, -1), -1), -1), tol=1e-10, what="dg vs rescaling identity")
+    # equal channels: the per-channel gate is the per-token one
+    gc = np.ascontiguousarray(np.repeat(gt[..., None], dk, -1))
+    ch = oracle.delta_backward(q, k, v, beta, dO, S0, dST, g=gc, lib=lib)
+    for name, a, b in zip(("q", "k", "v", "beta", "S0"), ch[:5], (dq, dk_, dv_, db, dS0)):
+        _close(a, b, tol=1e-12, what=f"d{name}: equal channels vs per-token gate")
+    _close(ch[5].sum(-1), dg, tol=1e-12, what="dg: channels summed vs per-token gate")
+    # zero gate: the ungated gradients, and dg = dG summed as above
+    ung = oracle.delta_backward(q, k, v, beta, dO, S0, dST, lib=lib)
+    for gz in (np.zeros_like(gt), np.zeros_like(g)):
+        z = oracle.delta_backward(q, k, v, beta, dO, S0, dST, g=gz, lib=lib)
+        for name, a, b in zip(("q", "k", "v", "beta", "S0"), z[:5], ung):
+            _close(a, b, tol=1e-12, what=f"d{name}: zero gate vs ungated")
+
+
 # --------------------------------------------------------------------------
 # The layer's prologue: q, k = normalize(silu(.)), beta = sigmoid(.)
 # --------------------------------------------------------------------------
@@ -640,6 +739,9 @@ ALL_PINS = [
     pin_gla_limits,
     pin_delta_backward_finite_differences,
     pin_delta_backward_autograd,
+    pin_gated_backward_finite_differences,
+    pin_gated_backward_autograd,
+    pin_gated_backward_rescaling_identity,
     pin_prologue_facts,
     pin_stored_precision_widening,
     pin_state_carry,

@@ -84,6 +84,16 @@ MUTANTS = {
     "bf16_widening_wrong_shift": (
         "uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;",
         "uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 15;"),
+    "gated_bwd_state_gradient_not_decayed": (
+        "dS[(size_t)i * dv + j] *= ga[i];", "dS[(size_t)i * dv + j] *= 1.0;"),
+    "gated_bwd_dg_against_undecayed_state": (
+        "gi += dS[(size_t)i * dv + j] * Sa[(size_t)i * dv + j];",
+        "gi += dS[(size_t)i * dv + j] * Sall[(size_t)t * ss + (size_t)i * dv + j];"),
+    "gated_bwd_dg_before_the_erase_term": (
+        "if (g) {\n                double gsum = 0.0;",
+        "if (g) {\n                for (int i = 0; i < dk; i++) for (int j = 0; j < dv; j++)\n"
+        "                    dS[(size_t)i * dv + j] += b * kt[i] * du[j];\n"
+        "                double gsum = 0.0;"),
 }
 
 
