@@ -19,7 +19,8 @@ import torch
 __all__ = [
     "la_prefill", "la_decode_step", "deltanet_prefill", "deltanet_decode_step",
     "gated_deltanet_prefill", "gated_deltanet_decode_step", "gla_prefill",
-    "gla_decode_step", "deltanet_prefill_backward", "deltanet_prologue", "la_strerror",
+    "gla_decode_step", "deltanet_prefill_backward", "gated_deltanet_prefill_backward",
+    "deltanet_prologue", "la_strerror",
     "library", "LIB_PATH",
     "EXPORTED_SYMBOLS",
     "LinAttnError",
@@ -29,7 +30,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblinattn.
 EXPORTED_SYMBOLS = ("la_prefill", "la_decode_step", "deltanet_prefill",
                     "deltanet_decode_step", "gated_deltanet_prefill",
                     "gated_deltanet_decode_step", "gla_prefill", "gla_decode_step",
-                    "deltanet_prefill_backward", "deltanet_prologue", "la_strerror")
+                    "deltanet_prefill_backward", "gated_deltanet_prefill_backward",
+                    "deltanet_prologue", "la_strerror")
 
 LA_DTYPE_F32, LA_DTYPE_BF16 = 0, 1
 _DTYPES = {torch.float32: LA_DTYPE_F32, torch.bfloat16: LA_DTYPE_BF16}
@@ -64,6 +66,7 @@ def library():
         lib.gla_prefill.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
         lib.gla_decode_step.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
         lib.deltanet_prefill_backward.argtypes = [P] * 12 + [I] * 6 + [P]
+        lib.gated_deltanet_prefill_backward.argtypes = [P] * 14 + [I] * 6 + [P]
         lib.deltanet_prologue.argtypes = [P] * 6 + [I] * 6 + [ctypes.c_float, I, P]
         for fn in EXPORTED_SYMBOLS[:-1]:
             getattr(lib, fn).restype = I
@@ -316,6 +319,35 @@ def deltanet_prefill_backward(q, k, v, beta, dO, S0=None, dST=None, want_dS0=Fal
         _stream(dev, stream))
     _check("deltanet_prefill_backward", rc)
     return dq, dkk, dvv, db, dS0
+
+
+def gated_deltanet_prefill_backward(q, k, v, beta, g, dO, S0=None, dST=None, want_dS0=False,
+                                    stream=None):
+    """Gradients of gated_deltanet_prefill (one log-decay per token) for the
+    loss sum(dO * o) + sum(dST * S_T): returns (dq, dk, dv, dbeta, dg, dS0),
+    dS0 None unless want_dS0.  g [B,H,T] in the inputs' dtype; the rest as
+    deltanet_prefill_backward."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev, dtype = _inputs("gated_deltanet_prefill_backward",
+                         dict(q=q, k=k, v=v, beta=beta, g=g, dO=dO),
+                         dict(q=(B, H, T, dk), k=(B, H, T, dk), v=(B, H, T, dv),
+                              beta=(B, H, T), g=(B, H, T), dO=(B, H, T, dv)))
+    for name, t in (("S0", S0), ("dST", dST)):
+        if t is not None:
+            _state("gated_deltanet_prefill_backward", name, t, (B, H, dk, dv), dev)
+    dq = torch.empty_like(q)
+    dkk = torch.empty_like(k)
+    dvv = torch.empty_like(v)
+    db = torch.empty_like(beta)
+    dg = torch.empty_like(g)
+    dS0 = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32) if want_dS0 else None
+    rc = library().gated_deltanet_prefill_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(dO), _ptr(dST),
+        _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(db), _ptr(dg), _ptr(dS0), B, H, T, dk, dv,
+        _DTYPES[dtype], _stream(dev, stream))
+    _check("gated_deltanet_prefill_backward", rc)
+    return dq, dkk, dvv, db, dg, dS0
 
 
 def deltanet_prologue(q, k, beta_logits=None, apply_silu=True, q_scale=1.0, out=None,

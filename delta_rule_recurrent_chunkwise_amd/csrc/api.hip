@@ -45,7 +45,7 @@ const char* la_strerror(int code) {
     case LA_ERR_UNSUPPORTED_DIM:
       return "unsupported head dimension: dk and dv must each be 16, 32, 64 or 128 "
              "(float32: dk <= 64 for deltanet_prefill with a per-channel gate, "
-             "dk and dv <= 64 for deltanet_prefill_backward)";
+             "dk and dv <= 64 for the backward entry points)";
     case LA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch or a workspace allocation";
     case LA_ERR_ALIGN:
       return "q, k, v and o (prefill; and dO, dq, dk, dv, backward; q and k in and out, prologue) "
@@ -170,6 +170,23 @@ int deltanet_prefill_backward(const void* q, const void* k, const void* v, const
       !aligned16(dv_out))
     return LA_ERR_ALIGN;
   linattn::BackwardArgs a{q, k, v, beta, S0, dO, dST, dq, dk_out, dv_out, dbeta, dS0, B, H, T, dk, dv};
+  return launch_rc(linattn::launch_delta_backward(dtype == LA_DTYPE_BF16, a, static_cast<hipStream_t>(stream)));
+}
+
+int gated_deltanet_prefill_backward(const void* q, const void* k, const void* v, const void* beta,
+                                    const void* g, const float* S0, const void* dO, const float* dST,
+                                    void* dq, void* dk_out, void* dv_out, void* dbeta, void* dg, float* dS0,
+                                    int B, int H, int T, int dk, int dv, int dtype, void* stream) {
+  if (T != 0 && (!q || !k || !v || !beta || !g || !dO || !dq || !dk_out || !dv_out || !dbeta || !dg))
+    return LA_ERR_NULL;
+  if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
+  if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1, true)) return LA_ERR_SHAPE;
+  if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
+  if (dtype == LA_DTYPE_F32 && (dk > 64 || dv > 64)) return LA_ERR_UNSUPPORTED_DIM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(dq) || !aligned16(dk_out) ||
+      !aligned16(dv_out))
+    return LA_ERR_ALIGN;
+  linattn::BackwardArgs a{q, k, v, beta, S0, dO, dST, dq, dk_out, dv_out, dbeta, dS0, B, H, T, dk, dv, g, dg};
   return launch_rc(linattn::launch_delta_backward(dtype == LA_DTYPE_BF16, a, static_cast<hipStream_t>(stream)));
 }
 

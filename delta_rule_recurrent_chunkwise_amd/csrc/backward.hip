@@ -50,6 +50,25 @@ __device__ __forceinline__ int xcd_remap_b(int bid, int n) {
   return (bid % 8) * (n / 8) + bid / 8;
 }
 
+// Gated rule (one log-decay g per token): G_r = g_t0 + ... + g_(t0+r), the
+// log-decay summed from the chunk start, r = 0..63 (rows past the end add
+// nothing, so they keep G of the last row).  Called by a whole wave; lane r
+// returns G_r.
+template <class E>
+__device__ __forceinline__ float chunk_logdecay(const typename E::T* gh, int t0, int nrow, int lane) {
+  float x = lane < nrow ? E::tof(gh[t0 + lane]) : 0.f;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+// exp(G_r - G_c) for c <= r (a decay ratio, at most 1), else 0
+__device__ __forceinline__ float decay_ratio(const float* sG, int r, int c) {
+  return c <= r ? __expf(sG[r] - sG[c]) : 0.f;
+}
+
 // T = (I + L)^-1 in the lower triangle (diagonal included) of sTL, from L
 // stored transposed in its strictly upper triangle (sTL[c][r] = L[r][c],
 // c < r).  Diagonal 16 x 16 blocks by forward substitution, one lane per
@@ -270,10 +289,15 @@ struct ChainLayout {
   static constexpr int oAt = oDOt + DVS * LKT * (int)sizeof(T);
   static constexpr int oTL = oAt + kC * LKT * (int)sizeof(T);
   static constexpr int oB = oTL + kC * LTL * 4;
-  static constexpr int total = oB + kC * 4;
+  static constexpr int oG = oB + kC * 4;  // gated: G_r
+  static constexpr int total = oG + kC * 4;
 };
 
-template <int DK, class E, int DVS>
+// GATE (one log-decay per token, G_r summed from the chunk start, decay
+// ratios exp(G_r - G_c) in A and L):
+//   du = A^T dO + diag(exp(G_C - G)) K dSn,
+//   dS = exp(G_C) dSn + Q^T diag(exp(G)) dO - K^T diag(beta exp(G)) dX.
+template <int DK, class E, int DVS, bool GATE>
 __global__ __launch_bounds__(kChainThreads) void bwd_chain(BackwardArgs a, float* __restrict__ dSc) {
   constexpr int NTH = kChainThreads, NW = NTH / 64;
   typedef ChainLayout<DK, E, DVS> L;
@@ -290,6 +314,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain(BackwardArgs a, float
   T* sA = reinterpret_cast<T*>(smem + L::oAt);  // tril(Q K^T), row-major
   float* sTL = reinterpret_cast<float*>(smem + L::oTL);
   float* sB = reinterpret_cast<float*>(smem + L::oB);
+  float* sG = reinterpret_cast<float*>(smem + L::oG);
 
   const int dv = a.dv_;
   const int nsl = dv / DVS;
@@ -341,13 +366,22 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain(BackwardArgs a, float
     pk.store(nrow, sK, LQ, sKt, LKT, tid);
     pdo.store(nrow, nullptr, 0, sDOt, LKT, tid);  // the dO slice, transposed
     if (tid < kC) sB[tid] = tid < nrow ? pb : 0.f;
+    if constexpr (GATE) {
+      if (wave == 0) sG[lane] = chunk_logdecay<E>(reinterpret_cast<const T*>(a.g) + (size_t)bh * Tn, t0, nrow, lane);
+    }
     prefetch(c > 0 ? c - 1 : 0);  // issued on every trip (the last one re-reads chunk 0)
     __syncthreads();
 
     floatx4 kds[4];
     if (chain) {  // K dSn while the other waves form the products
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) kds[mt] = accB<kBf16>(zero4(), sK + (16 * mt + lc) * LQ, st, NKT, lane);
+      for (int mt = 0; mt < 4; ++mt) {
+        kds[mt] = accB<kBf16>(zero4(), sK + (16 * mt + lc) * LQ, st, NKT, lane);
+        if constexpr (GATE) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) kds[mt][i] *= __expf(sG[63] - sG[16 * mt + 4 * lg + i]);
+        }
+      }
     } else {
       // jobs 0..9: tiles (i, j <= i) of tril(Q K^T); jobs 10..19: the same
       // tiles of K K^T -> L (strictly lower, rows scaled by beta), stored
@@ -357,9 +391,13 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain(BackwardArgs a, float
         const int t = isA ? jb : jb - 10;
         const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
         const int tj = t - ti * (ti + 1) / 2;
-        const floatx4 acc =
+        floatx4 acc =
             rowrow<kBf16>(zero4(), (isA ? sQ : sK) + (16 * ti + lc) * LQ, sK + (16 * tj + lc) * LQ, DK, lane);
         const int cc = 16 * tj + lc;
+        if constexpr (GATE) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] *= decay_ratio(sG, 16 * ti + 4 * lg + i, cc);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * ti + 4 * lg + i;
@@ -390,13 +428,22 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain(BackwardArgs a, float
       for (int mt = 0; mt < 4; ++mt) {
         dx[mt] = accB_col<kBf16>(zero4(), sTL + 16 * mt + lc, LTL, du, 4, lane);  // T^T du
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dx[mt][i] *= -sB[16 * mt + 4 * lg + i];  // -diag(beta) dX
+        for (int i = 0; i < 4; ++i) {  // -diag(beta) dX (gated: times exp(G_r))
+          const int r = 16 * mt + 4 * lg + i;
+          dx[mt][i] *= GATE ? -sB[r] * __expf(sG[r]) : -sB[r];
+        }
       }
+      floatx4 dOg[4];  // diag(exp(G)) dO
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dOg[t][i] = GATE ? dOt[t][i] * __expf(sG[16 * t + 4 * lg + i]) : dOt[t][i];
+      const float gc = GATE ? __expf(sG[63]) : 1.f;
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt) {
-        floatx4 g1 = accB<kBf16>(zero4(), sQt + (16 * kt + lc) * LKT, dOt, 4, lane);
+        floatx4 g1 = accB<kBf16>(zero4(), sQt + (16 * kt + lc) * LKT, dOg, 4, lane);
         floatx4 g2 = accB<kBf16>(zero4(), sKt + (16 * kt + lc) * LKT, dx, 4, lane);
-        st[kt] += g1 + g2;
+        st[kt] = gc * st[kt] + g1 + g2;
       }
     }
   }
@@ -467,7 +514,8 @@ struct TransLayout {
   static constexpr int oD = oLo + 6 * 256 * 2;    // D_b = (I + L_bb)^-1: bf16 [4][16][16]
   static constexpr int oLd = oD + 4 * 256 * 2;    // L_bb: fp32 [4][16][LD], strictly lower
   static constexpr int oB = oLd + 4 * 16 * LD * 4;
-  static constexpr int total = oB + kC * 4;
+  static constexpr int oG = oB + kC * 4;          // gated: G_r (fp32)
+  static constexpr int total = oG + kC * 4;
 };
 
 constexpr int kTransThreads = 512;
@@ -484,9 +532,14 @@ constexpr int kTransThreads = 512;
 //      fragment (w, kb), lane (lc, lg) = P[16w + lc][32kb + 8lg .. +7]
 //      (dk = 16: [1][64][4], P[lc][4lg .. +3]); R^T as [dk/16][2][64][8]
 //      likewise.  A wave's store of one tile then covers 512 contiguous bytes.
-template <int DK>
+// GATE (one log-decay per token, G_r summed from the chunk start): A and L
+// take the decay ratios exp(G_r - G_c), W solves (I + L) W = diag(beta
+// exp(G)) K, P = W^T diag(exp(G_C - G)) K and R = diag(exp(G)) Q - A W, and
+// exp(G_C) of the chunk goes to gC; the chain then takes
+// dS <- exp(G_C) dS - P dS + R^T dO.
+template <int DK, bool GATE>
 __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, bf16_t* __restrict__ Pg,
-                                                                bf16_t* __restrict__ Rg) {
+                                                                bf16_t* __restrict__ Rg, float* __restrict__ gC) {
   typedef TransLayout<DK> LY;
   constexpr int NTH = kTransThreads, NW = NTH / 64, LQ = LY::LQ, LT = LY::LT, LD = LY::LD, NT = DK / 16;
   __shared__ __attribute__((aligned(16))) char smem[LY::total];
@@ -498,6 +551,7 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
   bf16_t* sD = reinterpret_cast<bf16_t*>(smem + LY::oD);
   float* sLd = reinterpret_cast<float*>(smem + LY::oLd);
   float* sB = reinterpret_cast<float*>(smem + LY::oB);
+  float* sG = reinterpret_cast<float*>(smem + LY::oG);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
   const int Tn = a.T, nch = (Tn + kC - 1) / kC;
   const size_t chunk = blockIdx.x;
@@ -530,6 +584,13 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
     *reinterpret_cast<u32x4*>(sK + r * LQ + c8) = r < nrow ? bk[j] : z4;
   }
   if (tid < kC) sB[tid] = tid < nrow ? bt : 0.f;
+  if constexpr (GATE) {
+    if (wave == 0) {
+      const float G = chunk_logdecay<BF16>(reinterpret_cast<const bf16_t*>(a.g) + (size_t)bh * Tn, t0, nrow, lane);
+      sG[lane] = G;
+      if (lane == 63) gC[chunk] = __expf(G);
+    }
+  }
   __syncthreads();
 
   // 2. jobs 0..9: tiles (ti >= tj) of tril(Q K^T); 10..19: of L.  The
@@ -540,8 +601,12 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
     const int t = isA ? jb : jb - 10;
     const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
     const int tj = t - ti * (ti + 1) / 2;
-    const floatx4 acc = mm_rowrow_bf16(zero4(), sK + (16 * tj + lc) * LQ, (isA ? sQ : sK) + (16 * ti + lc) * LQ, DK, lane);
+    floatx4 acc = mm_rowrow_bf16(zero4(), sK + (16 * tj + lc) * LQ, (isA ? sQ : sK) + (16 * ti + lc) * LQ, DK, lane);
     const int r = 16 * ti + lc, c0 = 16 * tj + 4 * lg;
+    if constexpr (GATE) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= decay_ratio(sG, r, c0 + i);
+    }
     if (isA) {
       st4_bf16(sA + r * LT + tperm(c0), c0 <= r ? acc[0] : 0.f, c0 + 1 <= r ? acc[1] : 0.f,
                c0 + 2 <= r ? acc[2] : 0.f, c0 + 3 <= r ? acc[3] : 0.f);
@@ -592,6 +657,7 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * b + 4 * lg + i;
         xb[b][i] = sB[r] * bf2f(sK[r * LQ + 16 * dt + lc]);
+        if constexpr (GATE) xb[b][i] *= __expf(sG[r]);
       }
     floatx4 w[4];
     w[0] = mfma_k16(blk(sD), acc_to_b16(xb[0]), zero4());
@@ -610,6 +676,20 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
       st4_bf16(sWt + (16 * dt + lc) * LT + tperm(16 * b + 4 * lg), w[b][0], w[b][1], w[b][2], w[b][3]);
   }
   __syncthreads();
+  if constexpr (GATE) {  // K's rows times exp(G_C - G_r): P's operand
+    constexpr int NKV = kC * DK / 8;
+    for (int v = tid; v < NKV; v += NTH) {
+      const int r = v / (DK / 8), c8 = (v % (DK / 8)) * 8;
+      u32x4* p = reinterpret_cast<u32x4*>(sK + r * LQ + c8);
+      const u32x4 x = *p;
+      const float f = __expf(sG[63] - sG[r]);
+      u32x4 y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = pack2(f * __uint_as_float(x[e] << 16), f * __uint_as_float(x[e] & 0xffff0000u));
+      *p = y;
+    }
+    __syncthreads();
+  }
 
   // 5. P (from P^T = K^T W: lane holds P[16 dt + lc][16 et + 4 lg + i]) and
   // R = Q - A W (lane holds R[16 rt + 4 lg + i][16 dt + lc]); A's row block rt
@@ -640,7 +720,10 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
                        ld_frag(sWt + (16 * dt + lc) * LT + 32 * kb + 8 * lg), acc);
       float rv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rv[i] = bf2f(sQ[(16 * rt + 4 * lg + i) * LQ + 16 * dt + lc]) - acc[i];
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * lg + i;
+        rv[i] = bf2f(sQ[r * LQ + 16 * dt + lc]) * (GATE ? __expf(sG[r]) : 1.f) - acc[i];
+      }
       // R^T[16 dt + lc][tperm(16 rt + 4 lg) .. +3]: fragment (dt, rt / 2),
       // lane lc + 16 lg, half rt % 2
       st4_bf16(Rc + (((size_t)dt * 2 + (rt >> 1)) * 64 + lc + 16 * lg) * 8 + 4 * (rt & 1), rv[0], rv[1], rv[2], rv[3]);
@@ -658,9 +741,11 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
 // into registers (NS chunks ahead; bwd_transition stores them in fragment
 // order, so a wave's load is 1 KB contiguous) and dS^T, the dO slice read
 // from LDS (double buffered, one barrier per chunk).
-template <int DK, int DVS>
+// GATE: dS <- exp(G_C) dS - P dS + R^T dO, exp(G_C) of each chunk from gC.
+template <int DK, int DVS, bool GATE>
 __global__ __launch_bounds__(DK * 4) void bwd_chain_mat(BackwardArgs a, const bf16_t* __restrict__ Pg,
-                                                        const bf16_t* __restrict__ Rg, bf16_t* __restrict__ dSt) {
+                                                        const bf16_t* __restrict__ Rg, bf16_t* __restrict__ dSt,
+                                                        const float* __restrict__ gC) {
   constexpr int NTH = DK * 4, NJ = DVS / 16, LDT = DK + 16, LVO = DVS + 16, NS = 4;  // NS: chunks in flight (the prologue issues four)
   constexpr int KP = DK >= 32 ? DK / 32 : 1;
   constexpr int NVO = kC * DVS / 8, VPT = (NVO + NTH - 1) / NTH;
@@ -677,9 +762,11 @@ __global__ __launch_bounds__(DK * 4) void bwd_chain_mat(BackwardArgs a, const bf
   // every lane issues every load (clamped to valid rows and chunks), and
   // slots are indexed at compile time only
   u32x4 sp[NS][KP], sr[NS][2], so[NS][VPT];
+  float sgc[NS];
   auto issue = [&](int x, auto slotc) {
     constexpr int S = decltype(slotc)::value;
     const size_t cb = (size_t)bh * nch + x;
+    sgc[S] = GATE ? gC[cb] : 1.f;
     // fragment (wave, kb) of P and of R^T: 64 lanes x 16 bytes, contiguous
 #pragma unroll
     for (int kb = 0; kb < KP; ++kb) {
@@ -783,7 +870,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_chain_mat(BackwardArgs a, const bf
       for (int jt = 0; jt < NJ; ++jt) cr[jt] = mfma_k32(ra, fo[kb][jt], cr[jt]);
     }
 #pragma unroll
-    for (int jt = 0; jt < NJ; ++jt) st[jt] = st[jt] - cp[jt] + cr[jt];
+    for (int jt = 0; jt < NJ; ++jt) st[jt] = (GATE ? sgc[S] * st[jt] : st[jt]) - cp[jt] + cr[jt];
     // the next chunk's dS^T and dO slice go to the other buffers (past the
     // first chunk this writes unused data)
     put_dst(buf ^ 1);
@@ -824,7 +911,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_chain_mat(BackwardArgs a, const bf
 //   E  stage S, dSn rows; dQ += dO S^T, dK += u dSn^T - diag(beta) dX S^T;
 //      write dQ, dK, dbeta
 // ---------------------------------------------------------------------------
-template <int DK, int DV, class E>
+template <int DK, int DV, class E, bool GATE = false>
 struct GradLayout {
   typedef typename E::T T;
   static constexpr int ES = (int)sizeof(T);
@@ -841,7 +928,9 @@ struct GradLayout {
   static constexpr int oKK = oDX + ROWV;
   static constexpr int oB = oKK + FT;
   static constexpr int oDB = oB + kC * 4;
-  static constexpr int oW = oDB + kC * 4;  // phase-dependent work area
+  static constexpr int oG = oDB + kC * 4;   // gated: G_r
+  static constexpr int oDG = oG + kC * 4;   // gated: the gradient of G_r
+  static constexpr int oW = oDG + kC * 4;  // phase-dependent work area
   // phases A, B
   static constexpr int aQ = oW, aK = aQ + ROWQ, aAt = aK + ROWQ, aTL = aAt + TRI;
   // bf16 inputs: T and T^T (bf16, formed by block substitution), A^T, the
@@ -860,13 +949,36 @@ struct GradLayout {
   // phase E: dO (kept), S, dSn
   static constexpr int eS = cDA, eDS = eS + ST;
   static constexpr int endE = eDS + ST;
-  static constexpr int total = endAB > endCD ? (endAB > endE ? endAB : endE) : (endCD > endE ? endCD : endE);
+  static constexpr int endAll = endAB > endCD ? (endAB > endE ? endAB : endE) : (endCD > endE ? endCD : endE);
+  // gated: the strictly lower part of the ten lower 16 x 16 tiles of the
+  // gated A, kept from phase A to phase C: after everything (bf16), or
+  // where K^T is staged in phase D (fp32; no phase before D uses it)
+  static constexpr int oAg = ES == 2 ? endAll : dKt;
+  static constexpr int endAg = oAg + (GATE ? 10 * 256 * ES : 0);
+  static constexpr int total = endAll > endAg ? endAll : endAg;
+  static_assert(ES == 2 || dKt >= endAB, "fp32: the kept A tiles must not overlap phases A and B");
 };
 
-template <int DK, int DV, class E>
+// GATE (one log-decay per token, G_r summed from the chunk start): A, L and
+// their gradients take the decay ratios exp(G_r - G_c); X = diag(beta)(V -
+// diag(exp(G)) K S), du = A^T dO + diag(exp(G_C - G)) K dSn,
+// dQ = diag(exp(G)) dO S^T + dA K, dK = ... + diag(exp(G_C - G)) u dSn^T -
+// diag(beta exp(G)) dX S^T.  G enters the chunk at X (through exp(G_r) K S),
+// at A and L (through the ratios), at O (exp(G_r) Q S) and at the state
+// leaving it, so the gradient of G_r is
+//   - beta_r exp(G_r) (K S)_r . dX_r + sum_j (dA * A)_rj - sum_i (dA * A)_ir
+//   + k_r . (bL K - bL^T K)_r + exp(G_r) q_r . (dO S^T)_r
+//   - exp(G_C - G_r) k_r . (u dSn^T)_r
+// plus, on the last row, exp(G_C) <S, dSn> + sum_j exp(G_C - G_j) k_j .
+// (u dSn^T)_j (dA, A, bL with the ratios).  Pairs that cancel exactly (the
+// diagonal of dA * A, the last row's own k . (u dSn^T)) are left out, so
+// every term carries a decay and dg keeps its relative accuracy when the
+// decays are strong.  g_t enters G_r for r >= t of its own chunk only, so
+// dg_t = sum of dG_r over r >= t in the chunk.
+template <int DK, int DV, class E, bool GATE>
 __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const float* __restrict__ Sc,
                                                      const float* __restrict__ dSc) {
-  typedef GradLayout<DK, DV, E> L;
+  typedef GradLayout<DK, DV, E, GATE> L;
   typedef typename E::T T;
   constexpr bool kBf16 = sizeof(T) == 2;
   constexpr int NTH = kGradThreads, NW = NTH / 64;
@@ -879,6 +991,9 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
   float* sKK = reinterpret_cast<float*>(smem + L::oKK);
   float* sB = reinterpret_cast<float*>(smem + L::oB);
   float* sDB = reinterpret_cast<float*>(smem + L::oDB);
+  float* sG = reinterpret_cast<float*>(smem + L::oG);
+  float* sDG = reinterpret_cast<float*>(smem + L::oDG);
+  T* sAg = reinterpret_cast<T*>(smem + L::oAg);  // gated: [10][16][16], tile t = ti (ti + 1) / 2 + tj
 
   const int chunk = blockIdx.x;  // over B * H * nch
   const int Tn = a.T, nch = (Tn + kC - 1) / kC;
@@ -914,6 +1029,12 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
     sB[tid] = tid < nrow ? E::tof(bth[t0 + tid]) : 0.f;
     sDB[tid] = 0.f;
   }
+  if constexpr (GATE) {
+    if (wave == 0) {
+      sG[lane] = chunk_logdecay<E>(reinterpret_cast<const T*>(a.g) + (size_t)bh * Tn, t0, nrow, lane);
+      sDG[lane] = 0.f;
+    }
+  }
   for (int i = tid; i < kC * kC; i += NTH) {  // tiles above the diagonal stay zero
     const int r = i >> 6, cc = i & 63;
     if ((cc >> 4) > (r >> 4)) {
@@ -927,13 +1048,18 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
     const int t = isA ? jb : jb - 10;
     const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
     const int tj = t - ti * (ti + 1) / 2;
-    const floatx4 acc =
+    floatx4 acc =
         rowrow<kBf16>(zero4(), (isA ? sQ : sK) + (16 * ti + lc) * LQ, sK + (16 * tj + lc) * LQ, DK, lane);
     const int cc = 16 * tj + lc;
+    if constexpr (GATE) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= decay_ratio(sG, 16 * ti + 4 * lg + i, cc);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * ti + 4 * lg + i;
       if (isA) {
+        if constexpr (GATE) sAg[t * 256 + (4 * lg + i) * 16 + lc] = E::cvt(cc < r ? acc[i] : 0.f);
         sA[r * LKT + cc] = E::cvt(cc <= r ? acc[i] : 0.f);
         if constexpr (kBf16) sAtt[cc * LKT + r] = E::cvt(cc <= r ? acc[i] : 0.f);
       } else {
@@ -1037,10 +1163,25 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
         vt[mt][i] = r < nrow ? vx : 0.f;
         dOt[mt][i] = r < nrow ? ox : 0.f;
       }
-    floatx4 res[4], xx[4], ut[4], du[4], dx[4];
+    floatx4 res[4], xx[4], ut[4], du[4], dx[4], gy[4];  // gy: exp(G) K S (gated)
+    if constexpr (GATE) {  // exp(G_C) <S, dSn> over this slice, to the last row
+      float p = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p += Sv[kt][i] * dSv[kt][i];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) p += __shfl_xor(p, off, 64);
+      if (lane == 0) atomicAdd(&sDG[nrow - 1], __expf(sG[63]) * p);
+    }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const floatx4 y = accB<kBf16>(zero4(), sK + (16 * mt + lc) * LQ, Sv, NKT, lane);
+      floatx4 y = accB<kBf16>(zero4(), sK + (16 * mt + lc) * LQ, Sv, NKT, lane);
+      if constexpr (GATE) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] *= __expf(sG[16 * mt + 4 * lg + i]);
+        gy[mt] = y;
+      }
       res[mt] = vt[mt] - y;  // V - K S
 #pragma unroll
       for (int i = 0; i < 4; ++i) xx[mt][i] = sB[16 * mt + 4 * lg + i] * res[mt][i];
@@ -1055,7 +1196,11 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
         ut[mt] = accB<kBf16>(zero4(), sTL + (16 * mt + lc) * LTL, xx, mt + 1, lane);
         d1 = accB_col<kBf16>(zero4(), sA + 16 * mt + lc, LKT, dOt, 4, lane);  // A^T dO
       }
-      const floatx4 d2 = accB<kBf16>(zero4(), sK + (16 * mt + lc) * LQ, dSv, NKT, lane);
+      floatx4 d2 = accB<kBf16>(zero4(), sK + (16 * mt + lc) * LQ, dSv, NKT, lane);
+      if constexpr (GATE) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d2[i] *= __expf(sG[63] - sG[16 * mt + 4 * lg + i]);
+      }
       du[mt] = d1 + d2;
     }
 #pragma unroll
@@ -1074,6 +1219,12 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
 #pragma unroll
         for (int off = 1; off < 16; off <<= 1) p += __shfl_xor(p, off, 16);
         if (lc == 0) atomicAdd(&sDB[r], p);
+        if constexpr (GATE) {  // - beta_r exp(G_r) (K S)_r . dX_r
+          float pv = gy[mt][i] * sB[r] * dx[mt][i];
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) pv += __shfl_xor(pv, off, 16);
+          if (lc == 0) atomicAdd(&sDG[r], -pv);
+        }
       }
     }
   }
@@ -1130,10 +1281,37 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
       const floatx4 acc =
           rowrow<kBf16>(zero4(), sU + (16 * tj + lc) * LV, (isA ? sDO : sDX) + (16 * ti + lc) * LV, DV, lane);
       const int r = 16 * ti + lc, c0 = 16 * tj + 4 * lg;
+      float gm[4] = {1.f, 1.f, 1.f, 1.f};
+      if constexpr (GATE) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gm[i] = decay_ratio(sG, r, c0 + i);
+      }
       if (isA) {
         float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = c0 + i <= r ? acc[i] : 0.f;
+        for (int i = 0; i < 4; ++i) v[i] = c0 + i <= r ? acc[i] * gm[i] : 0.f;
+        if constexpr (GATE) {
+          // A's part of the gradient of G: row sums minus column sums of
+          // dA * A below the diagonal (on it the two cancel exactly)
+          const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(sAg) + t * 256 + lc * 16 + 4 * lg);
+          const float ag[4] = {bf2f((bf16_t)(w.x & 0xffffu)), bf2f((bf16_t)(w.x >> 16)), bf2f((bf16_t)(w.y & 0xffffu)),
+                               bf2f((bf16_t)(w.y >> 16))};
+          float m[4], rs = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {  // dA (without the ratios) times the gated A
+            m[i] = acc[i] * ag[i];
+            rs += m[i];
+          }
+          rs += __shfl_xor(rs, 16);
+          rs += __shfl_xor(rs, 32);
+          if (lg == 0) atomicAdd(&sDG[r], rs);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) m[i] += __shfl_xor(m[i], off, 16);
+            if (lc == 0) atomicAdd(&sDG[c0 + i], -m[i]);
+          }
+        }
         st4_bf16(reinterpret_cast<bf16_t*>(sDA) + r * LKT + c0, v[0], v[1], v[2], v[3]);
         st4_bf16(reinterpret_cast<bf16_t*>(sDAt) + r * LKT + tperm(c0), v[0], v[1], v[2], v[3]);
       } else {
@@ -1147,6 +1325,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
         p += __shfl_xor(p, 32);
         if (lg == 0) atomicAdd(&sDB[r], p);
         const float br = sB[r];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dl[i] *= gm[i];
         st4_bf16(reinterpret_cast<bf16_t*>(sBL) + r * LKT + c0, br * dl[0], br * dl[1], br * dl[2], br * dl[3]);
         st4_bf16(reinterpret_cast<bf16_t*>(sBLt) + r * LKT + tperm(c0), br * dl[0], br * dl[1], br * dl[2],
                  br * dl[3]);
@@ -1159,17 +1339,28 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * ti + 4 * lg + i;
+      const float gm = GATE ? decay_ratio(sG, r, cc) : 1.f;
       if (isA) {
-        const T x = E::cvt(cc <= r ? acc[i] : 0.f);
+        const T x = E::cvt(cc <= r ? acc[i] * gm : 0.f);
         sDA[r * LKT + cc] = x;
         sDAt[cc * LKT + r] = x;
+        if constexpr (GATE) {  // dA * A below the diagonal: + row sum, - column sum
+          float m = acc[i] * E::tof(sAg[t * 256 + (4 * lg + i) * 16 + lc]);  // dA times the gated A
+          float rs = m;
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) rs += __shfl_xor(rs, off, 16);
+          if (lc == 0) atomicAdd(&sDG[r], rs);
+          m += __shfl_xor(m, 16);
+          m += __shfl_xor(m, 32);
+          if (lg == 0) atomicAdd(&sDG[cc], -m);
+        }
       } else {
         const float dl = cc < r ? -acc[i] : 0.f;
         float p = cc < r ? dl * sKK[r * LTL + cc] : 0.f;  // rowsum(dL * K K^T)
 #pragma unroll
         for (int off = 1; off < 16; off <<= 1) p += __shfl_xor(p, off, 16);
         if (lc == 0) atomicAdd(&sDB[r], p);
-        const T x = E::cvt(sB[r] * dl);
+        const T x = E::cvt(sB[r] * dl * gm);
         sBL[r * LKT + cc] = x;
         sBLt[cc * LKT + r] = x;
       }
@@ -1198,14 +1389,28 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
     for (int n = 0; n < NOWN; ++n) {
       const int id = wave + NW * n, ti = id / NKT, tk = id - ti * NKT;
       if (NTILE % NW != 0 && id >= NTILE) continue;
-      floatx4 xq = zero4(), xk = zero4();
+      // gated: (b dL) K and (b dL)^T K kept apart (xk, xb) for the gradient of G
+      floatx4 xq = zero4(), xk = zero4(), xb = zero4(), xc = zero4();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 kf = tok_frag(sKr, LQ, 32 * kb, 16 * tk, lane);
         xq = mfma_k32(kf, ld_frag(bDAp + (16 * ti + lc) * LKT + 32 * kb + 8 * lg), xq);           // dA K
         xk = mfma_k32(kf, ld_frag(bBLp + (16 * ti + lc) * LKT + 32 * kb + 8 * lg), xk);           // (b dL) K
-        xk = mfma_k32(kf, tok_frag(bBL, LKT, 32 * kb, 16 * ti, lane), xk);                        // (b dL)^T K
-        xk = mfma_k32(tok_frag(sQr, LQ, 32 * kb, 16 * tk, lane), tok_frag(bDA, LKT, 32 * kb, 16 * ti, lane), xk);  // dA^T Q
+        if constexpr (GATE) xb = mfma_k32(kf, tok_frag(bBL, LKT, 32 * kb, 16 * ti, lane), xb);    // (b dL)^T K
+        else xk = mfma_k32(kf, tok_frag(bBL, LKT, 32 * kb, 16 * ti, lane), xk);
+        const bf16x8 qf = tok_frag(sQr, LQ, 32 * kb, 16 * tk, lane), af = tok_frag(bDA, LKT, 32 * kb, 16 * ti, lane);
+        if constexpr (GATE) xc = mfma_k32(qf, af, xc);  // dA^T Q
+        else xk = mfma_k32(qf, af, xk);
+      }
+      if constexpr (GATE) {  // k_r . (bL K - bL^T K)_r, four columns per lane
+        const int r = 16 * ti + lc, d0 = 16 * tk + 4 * lg;
+        float p = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p += bf2f(sKr[r * LQ + d0 + i]) * (xk[i] - xb[i]);
+        p += __shfl_xor(p, 16);
+        p += __shfl_xor(p, 32);
+        if (lg == 0) atomicAdd(&sDG[r], p);
+        xk += xb + xc;
       }
       gq[n] = xq;
       gk[n] = xk;
@@ -1221,9 +1426,19 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
     const int id = wave + NW * n, ti = id / NKT, tk = id - ti * NKT;
     if (NTILE % NW != 0 && id >= NTILE) continue;
     gq[n] = rowrow<kBf16>(zero4(), sDA + (16 * ti + lc) * LKT, sKt + (16 * tk + lc) * LKT, kC, lane);
-    floatx4 x = rowrow<kBf16>(zero4(), sBL + (16 * ti + lc) * LKT, sKt + (16 * tk + lc) * LKT, kC, lane);
-    x += rowrow<kBf16>(zero4(), sBLt + (16 * ti + lc) * LKT, sKt + (16 * tk + lc) * LKT, kC, lane);
-    gk[n] = x;
+    const floatx4 x = rowrow<kBf16>(zero4(), sBL + (16 * ti + lc) * LKT, sKt + (16 * tk + lc) * LKT, kC, lane);
+    const floatx4 xt = rowrow<kBf16>(zero4(), sBLt + (16 * ti + lc) * LKT, sKt + (16 * tk + lc) * LKT, kC, lane);
+    gk[n] = x + xt;
+    if constexpr (GATE) {  // k_r . (bL K - bL^T K)_r over the tile's 16 columns
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * ti + 4 * lg + i, d = 16 * tk + lc;
+        float p = r < nrow ? E::tof(sKt[d * LKT + r]) * (x[i] - xt[i]) : 0.f;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) p += __shfl_xor(p, off, 16);
+        if (lc == 0) atomicAdd(&sDG[r], p);
+      }
+    }
   }
   __syncthreads();  // bL is dead: Q^T goes in its place
   stage_rows<E, DK, NTH>(qh, DK, t0, nrow, nullptr, 0, sQt, LKT, tid);
@@ -1297,11 +1512,44 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
       const floatx4 k2 = rowrow<kBf16>(zero4(), sS + (16 * tk + lc) * LS, sDX + (16 * ti + lc) * LV, DV, lane);
       const int r = 16 * ti + lc, d0 = 16 * tk + 4 * lg;
       const float br = sB[r];
+      // gated: dO S^T and beta dX S^T times exp(G_r), u dSn^T times exp(G_C - G_r)
+      const float e1 = GATE ? __expf(sG[r]) : 1.f, e2 = GATE ? __expf(sG[63] - sG[r]) : 1.f;
+      float dq4[4], dk4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dq4[i] = gq[n][i] + e1 * q1[i];
+        dk4[i] = gk[n][i] + e2 * k1[i] - br * e1 * k2[i];
+      }
       if (r < nrow) {
-        st4_bf16(reinterpret_cast<bf16_t*>(dqo) + (size_t)r * DK + d0, gq[n][0] + q1[0], gq[n][1] + q1[1],
-                 gq[n][2] + q1[2], gq[n][3] + q1[3]);
-        st4_bf16(reinterpret_cast<bf16_t*>(dko) + (size_t)r * DK + d0, gk[n][0] + k1[0] - br * k2[0],
-                 gk[n][1] + k1[1] - br * k2[1], gk[n][2] + k1[2] - br * k2[2], gk[n][3] + k1[3] - br * k2[3]);
+        st4_bf16(reinterpret_cast<bf16_t*>(dqo) + (size_t)r * DK + d0, dq4[0], dq4[1], dq4[2], dq4[3]);
+        st4_bf16(reinterpret_cast<bf16_t*>(dko) + (size_t)r * DK + d0, dk4[0], dk4[1], dk4[2], dk4[3]);
+      }
+      if constexpr (GATE) {  // exp(G_r) q . (dO S^T) - exp(G_C - G_r) k . (u dSn^T), four columns
+        float p = 0.f, pk = 0.f;
+        if (r < nrow) {
+          const uint2 w = *reinterpret_cast<const uint2*>(qh + (size_t)(t0 + r) * DK + d0);
+          const uint2 x = *reinterpret_cast<const uint2*>(kh + (size_t)(t0 + r) * DK + d0);
+          const float qv[4] = {bf2f((bf16_t)(w.x & 0xffffu)), bf2f((bf16_t)(w.x >> 16)), bf2f((bf16_t)(w.y & 0xffffu)),
+                               bf2f((bf16_t)(w.y >> 16))};
+          const float kv[4] = {bf2f((bf16_t)(x.x & 0xffffu)), bf2f((bf16_t)(x.x >> 16)), bf2f((bf16_t)(x.y & 0xffffu)),
+                               bf2f((bf16_t)(x.y >> 16))};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p += qv[i] * q1[i];
+            pk += kv[i] * k1[i];
+          }
+          // on the last row (e2 = 1) the term cancels against its share of
+          // the chunk sum: both are left out
+          pk = r < nrow - 1 ? e2 * pk : 0.f;
+          p = e1 * p - pk;
+        }
+        p += __shfl_xor(p, 16);
+        p += __shfl_xor(p, 32);
+        if (lg == 0) atomicAdd(&sDG[r], p);
+        // the same k . (u dSn^T) terms summed over the chunk, on its last row
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) pk += __shfl_xor(pk, off, 64);
+        if (lane == 0) atomicAdd(&sDG[nrow - 1], pk);
       }
       continue;
     }
@@ -1311,75 +1559,110 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * ti + 4 * lg + i, d = 16 * tk + lc;
+      const float e1 = GATE ? __expf(sG[r]) : 1.f, e2 = GATE ? __expf(sG[63] - sG[r]) : 1.f;
+      const float dqv = gq[n][i] + e1 * q1[i];
       if (r < nrow) {
-        dqo[(size_t)r * DK + d] = E::cvt(gq[n][i] + q1[i]);
-        dko[(size_t)r * DK + d] = E::cvt(gk[n][i] + k1[i] - sB[r] * k2[i]);
+        dqo[(size_t)r * DK + d] = E::cvt(dqv);
+        dko[(size_t)r * DK + d] = E::cvt(gk[n][i] + e2 * k1[i] - sB[r] * e1 * k2[i]);
+      }
+      if constexpr (GATE) {  // exp(G_r) q . (dO S^T) - exp(G_C - G_r) k . (u dSn^T), 16 columns
+        float p = 0.f, pk = 0.f;
+        if (r < nrow) {  // the last row's own term and its share of the chunk sum cancel
+          pk = r < nrow - 1 ? e2 * E::tof(kh[(size_t)(t0 + r) * DK + d]) * k1[i] : 0.f;
+          p = e1 * E::tof(qh[(size_t)(t0 + r) * DK + d]) * q1[i] - pk;
+        }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) p += __shfl_xor(p, off, 16);
+        if (lc == 0) atomicAdd(&sDG[r], p);
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) pk += __shfl_xor(pk, off, 64);
+        if (lane == 0) atomicAdd(&sDG[nrow - 1], pk);
       }
     }
   }
   if (tid < nrow) reinterpret_cast<T*>(a.dbeta)[(size_t)bh * Tn + t0 + tid] = E::cvt(sDB[tid]);
+  if constexpr (GATE) {  // dg_t: the sums of dG_r over r >= t in the chunk
+    __syncthreads();
+    if (wave == 0) {
+      float x = lane < nrow ? sDG[lane] : 0.f;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_down(x, off, 64);
+        if (lane + off < 64) x += o;
+      }
+      if (lane < nrow) reinterpret_cast<T*>(a.dg)[(size_t)bh * Tn + t0 + lane] = E::cvt(x);
+    }
+  }
 }
 
-template <int DK, int DV, class E>
-hipError_t launch_grads(const BackwardArgs& a, const float* Sc, const float* dSc, long nchunks, hipStream_t st) {
-  static_assert(GradLayout<DK, DV, E>::total <= 160 * 1024, "backward gradient kernel exceeds the LDS of a CU");
-  hipLaunchKernelGGL((bwd_grads<DK, DV, E>), dim3((unsigned)nchunks), dim3(kGradThreads), 0, st, a, Sc, dSc);
+template <int DK, int DV, class E, bool GATE>
+hipError_t launch_grads(const BackwardArgs& a, const float* Sc, const float* dSc, long nchunks,
+                        hipStream_t st) {
+  static_assert(GradLayout<DK, DV, E, GATE>::total <= 160 * 1024, "backward gradient kernel exceeds the LDS of a CU");
+  hipLaunchKernelGGL((bwd_grads<DK, DV, E, GATE>), dim3((unsigned)nchunks), dim3(kGradThreads), 0, st, a, Sc, dSc);
   return hipGetLastError();
 }
 
-template <int DK, class E>
-hipError_t launch_grads_dk(const BackwardArgs& a, const float* Sc, const float* dSc, long nchunks, hipStream_t st) {
+template <int DK, class E, bool GATE>
+hipError_t launch_grads_dk(const BackwardArgs& a, const float* Sc, const float* dSc, long nchunks,
+                           hipStream_t st) {
   switch (a.dv_) {
-    case 16: return launch_grads<DK, 16, E>(a, Sc, dSc, nchunks, st);
-    case 32: return launch_grads<DK, 32, E>(a, Sc, dSc, nchunks, st);
-    case 64: return launch_grads<DK, 64, E>(a, Sc, dSc, nchunks, st);
+    case 16: return launch_grads<DK, 16, E, GATE>(a, Sc, dSc, nchunks, st);
+    case 32: return launch_grads<DK, 32, E, GATE>(a, Sc, dSc, nchunks, st);
+    case 64: return launch_grads<DK, 64, E, GATE>(a, Sc, dSc, nchunks, st);
     case 128:
-      if constexpr (sizeof(typename E::T) == 2) return launch_grads<DK, 128, E>(a, Sc, dSc, nchunks, st);
+      if constexpr (sizeof(typename E::T) == 2) return launch_grads<DK, 128, E, GATE>(a, Sc, dSc, nchunks, st);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int DK, class E>
+template <int DK, class E, bool GATE>
 hipError_t launch_chain_dk(const BackwardArgs& a, float* dSc, hipStream_t st) {
   const long bh = (long)a.B * a.H;
   if (a.dv_ % 32 == 0) {
-    hipLaunchKernelGGL((bwd_chain<DK, E, 32>), dim3((unsigned)(bh * (a.dv_ / 32))), dim3(kChainThreads), 0, st, a, dSc);
+    hipLaunchKernelGGL((bwd_chain<DK, E, 32, GATE>), dim3((unsigned)(bh * (a.dv_ / 32))), dim3(kChainThreads), 0, st,
+                       a, dSc);
   } else {
-    hipLaunchKernelGGL((bwd_chain<DK, E, 16>), dim3((unsigned)(bh * (a.dv_ / 16))), dim3(kChainThreads), 0, st, a, dSc);
+    hipLaunchKernelGGL((bwd_chain<DK, E, 16, GATE>), dim3((unsigned)(bh * (a.dv_ / 16))), dim3(kChainThreads), 0, st,
+                       a, dSc);
   }
   return hipGetLastError();
 }
 
 // bf16: P and R for every chunk, then the one-product chain
-template <int DK>
-hipError_t launch_chain_mat(const BackwardArgs& a, bf16_t* Pg, bf16_t* Rg, float* dSc, hipStream_t st) {
+template <int DK, bool GATE>
+hipError_t launch_chain_mat(const BackwardArgs& a, bf16_t* Pg, bf16_t* Rg, float* dSc, float* gC, hipStream_t st) {
   bf16_t* dSt = reinterpret_cast<bf16_t*>(dSc);  // bf16 tile order (see bwd_chain_mat)
   static_assert(TransLayout<DK>::total <= 80 * 1024, "two transition workgroups should fit a CU");
   const long nchunks = (long)a.B * a.H * ((a.T + kC - 1) / kC);
-  hipLaunchKernelGGL((bwd_transition<DK>), dim3((unsigned)nchunks), dim3(kTransThreads), 0, st, a, Pg, Rg);
+  hipLaunchKernelGGL((bwd_transition<DK, GATE>), dim3((unsigned)nchunks), dim3(kTransThreads), 0, st, a, Pg, Rg, gC);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long bh = (long)a.B * a.H;
   if (a.dv_ % 32 == 0)
-    hipLaunchKernelGGL((bwd_chain_mat<DK, 32>), dim3((unsigned)(bh * (a.dv_ / 32))), dim3(DK * 4), 0, st, a, Pg, Rg, dSt);
+    hipLaunchKernelGGL((bwd_chain_mat<DK, 32, GATE>), dim3((unsigned)(bh * (a.dv_ / 32))), dim3(DK * 4), 0, st, a, Pg,
+                       Rg, dSt, gC);
   else
-    hipLaunchKernelGGL((bwd_chain_mat<DK, 16>), dim3((unsigned)(bh * (a.dv_ / 16))), dim3(DK * 4), 0, st, a, Pg, Rg, dSt);
+    hipLaunchKernelGGL((bwd_chain_mat<DK, 16, GATE>), dim3((unsigned)(bh * (a.dv_ / 16))), dim3(DK * 4), 0, st, a, Pg,
+                       Rg, dSt, gC);
   return hipGetLastError();
 }
 
-template <class E>
-hipError_t launch_backward_e(const BackwardArgs& a, float* Sc, float* dSc, bf16_t* Pg, bf16_t* Rg, hipStream_t st) {
+// gC: exp(G_C) of every chunk (gated rule, bf16)
+template <class E, bool GATE>
+hipError_t launch_backward_e(const BackwardArgs& a, float* Sc, float* dSc, bf16_t* Pg, bf16_t* Rg, float* gC,
+                             hipStream_t st) {
   const long nchunks = (long)a.B * a.H * ((a.T + kC - 1) / kC);
   hipError_t e;
   constexpr bool kB = sizeof(typename E::T) == 2;
   switch (a.dk_) {
-    case 16: e = kB ? launch_chain_mat<16>(a, Pg, Rg, dSc, st) : launch_chain_dk<16, E>(a, dSc, st); break;
-    case 32: e = kB ? launch_chain_mat<32>(a, Pg, Rg, dSc, st) : launch_chain_dk<32, E>(a, dSc, st); break;
-    case 64: e = kB ? launch_chain_mat<64>(a, Pg, Rg, dSc, st) : launch_chain_dk<64, E>(a, dSc, st); break;
+    case 16: e = kB ? launch_chain_mat<16, GATE>(a, Pg, Rg, dSc, gC, st) : launch_chain_dk<16, E, GATE>(a, dSc, st); break;
+    case 32: e = kB ? launch_chain_mat<32, GATE>(a, Pg, Rg, dSc, gC, st) : launch_chain_dk<32, E, GATE>(a, dSc, st); break;
+    case 64: e = kB ? launch_chain_mat<64, GATE>(a, Pg, Rg, dSc, gC, st) : launch_chain_dk<64, E, GATE>(a, dSc, st); break;
     case 128:
       if constexpr (kB) {
-        e = launch_chain_mat<128>(a, Pg, Rg, dSc, st);
+        e = launch_chain_mat<128, GATE>(a, Pg, Rg, dSc, gC, st);
         break;
       }
       return hipErrorInvalidValue;
@@ -1387,11 +1670,11 @@ hipError_t launch_backward_e(const BackwardArgs& a, float* Sc, float* dSc, bf16_
   }
   if (e != hipSuccess) return e;
   switch (a.dk_) {
-    case 16: return launch_grads_dk<16, E>(a, Sc, dSc, nchunks, st);
-    case 32: return launch_grads_dk<32, E>(a, Sc, dSc, nchunks, st);
-    case 64: return launch_grads_dk<64, E>(a, Sc, dSc, nchunks, st);
+    case 16: return launch_grads_dk<16, E, GATE>(a, Sc, dSc, nchunks, st);
+    case 32: return launch_grads_dk<32, E, GATE>(a, Sc, dSc, nchunks, st);
+    case 64: return launch_grads_dk<64, E, GATE>(a, Sc, dSc, nchunks, st);
     case 128:
-      if constexpr (sizeof(typename E::T) == 2) return launch_grads_dk<128, E>(a, Sc, dSc, nchunks, st);
+      if constexpr (sizeof(typename E::T) == 2) return launch_grads_dk<128, E, GATE>(a, Sc, dSc, nchunks, st);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -1401,18 +1684,20 @@ __global__ __launch_bounds__(256) void zero_state(float* __restrict__ p, size_t 
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0.f;
 }
 
-// The pipelined forward kernel (bf16, dk = 128, dv % 32 == 0) writes an
-// output and a final state it does not skip; they go to scratch at the end
-// of the workspace (the final state where a copy of S0 was put).
-bool pass1_pipelined(int bf16, const BackwardArgs& a) { return bf16 && a.dk_ == 128 && a.dv_ % 32 == 0; }
+// The pipelined forward kernel (bf16, dk = 128, dv % 32 == 0, no gate)
+// writes an output and a final state it does not skip; they go to scratch
+// at the end of the workspace (the final state where a copy of S0 was put).
+bool pass1_pipelined(int bf16, const BackwardArgs& a) { return bf16 && !a.g && a.dk_ == 128 && a.dv_ % 32 == 0; }
 
-// [Sc, dSc: fp32 nchunks x dk x dv][pipelined pass 1: final state, output]
+// [Sc, dSc: fp32 nchunks x dk x dv]
+// [pipelined pass 1: final state, output | gated: gC, fp32 nchunks]
 // [bf16: P nchunks x dk x dk, R^T nchunks x dk x 64]
 size_t delta_backward_workspace_bytes(int bf16, const BackwardArgs& a) {
   const size_t nchunks = (size_t)a.B * a.H * ((a.T + kC - 1) / kC);
   size_t n = 2 * nchunks * a.dk_ * a.dv_ * sizeof(float);
   if (pass1_pipelined(bf16, a))
     n += (size_t)a.B * a.H * a.dk_ * a.dv_ * sizeof(float) + (size_t)a.B * a.H * a.T * a.dv_ * sizeof(bf16_t);
+  if (a.g) n += nchunks * sizeof(float);
   if (bf16) n = (n + 255) / 256 * 256 + nchunks * a.dk_ * (a.dk_ + kC) * sizeof(bf16_t);
   return n;
 }
@@ -1437,13 +1722,17 @@ hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, hipStream_t st
   bf16_t* Pg = bf16 ? reinterpret_cast<bf16_t*>(static_cast<char*>(ws) + wsb) - nchunks * a.dk_ * (a.dk_ + kC) : nullptr;
   bf16_t* Rg = bf16 ? Pg + nchunks * a.dk_ * a.dk_ : nullptr;
   const size_t nst = (size_t)a.B * a.H * ((a.T + kC - 1) / kC) * a.dk_ * a.dv_;
+  const size_t nS = (size_t)a.B * a.H * a.dk_ * a.dv_;
   float* Sc = reinterpret_cast<float*>(ws);
   float* dSc = Sc + nst;
+  float* s_scratch = dSc + nst;  // pipelined pass 1: the final state lands here
+  float* gC = a.g ? dSc + nst : nullptr;
   PrefillArgs f{};
   f.q = a.q;
   f.k = a.k;
   f.v = a.v;
   f.beta = a.beta;
+  f.g = a.g;
   f.S = const_cast<float*>(a.S0);
   f.B = a.B;
   f.H = a.H;
@@ -1451,21 +1740,28 @@ hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, hipStream_t st
   f.dv = a.dv_;
   f.use_init = a.S0 != nullptr;
   f.Sc = Sc;
-  if (pass1_pipelined(bf16, a)) {
-    float* s_scratch = dSc + nst;  // the final state lands here
-    bf16_t* o_scratch = reinterpret_cast<bf16_t*>(s_scratch + (size_t)a.B * a.H * a.dk_ * a.dv_);
-    if (a.S0)
-      e = hipMemcpyAsync(s_scratch, a.S0, (size_t)a.B * a.H * a.dk_ * a.dv_ * sizeof(float),
-                         hipMemcpyDeviceToDevice, st);
-    f.S = s_scratch;
-    f.o = o_scratch;
-    if (e == hipSuccess) e = launch_prefill_pipe(f, nullptr, st);
-  } else {
-    e = launch_prefill_generic(PF_DELTA, bf16, a.dk_, f, st);
+  if (a.S0 && pass1_pipelined(bf16, a))
+    e = hipMemcpyAsync(s_scratch, a.S0, nS * sizeof(float), hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess) {
+    if (a.g) {
+      e = launch_prefill_generic(PF_SGATED, bf16, a.dk_, f, st);
+    } else if (pass1_pipelined(bf16, a)) {
+      f.S = s_scratch;
+      f.o = reinterpret_cast<bf16_t*>(s_scratch + nS);
+      e = launch_prefill_pipe(f, nullptr, st);
+    } else {
+      e = launch_prefill_generic(PF_DELTA, bf16, a.dk_, f, st);
+    }
   }
   // passes 2 and 3
-  if (e == hipSuccess) e = bf16 ? launch_backward_e<BF16>(a, Sc, dSc, Pg, Rg, st)
-                              : launch_backward_e<F32>(a, Sc, dSc, Pg, Rg, st);
+  if (e == hipSuccess) {
+    if (a.g)
+      e = bf16 ? launch_backward_e<BF16, true>(a, Sc, dSc, Pg, Rg, gC, st)
+               : launch_backward_e<F32, true>(a, Sc, dSc, Pg, Rg, gC, st);
+    else
+      e = bf16 ? launch_backward_e<BF16, false>(a, Sc, dSc, Pg, Rg, gC, st)
+               : launch_backward_e<F32, false>(a, Sc, dSc, Pg, Rg, gC, st);
+  }
   const hipError_t fr = hipFreeAsync(ws, st);
   return e != hipSuccess ? e : fr;
 }

@@ -62,6 +62,8 @@ struct BackwardArgs {
   void* dbeta;
   float* dS0;        // gradient of the initial state or NULL
   int B, H, T, dk_, dv_;
+  const void* g;     // one log-decay per token [B,H,T] (gated rule) or NULL
+  void* dg;          // its gradient [B,H,T] (with g)
 };
 hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, hipStream_t st);
 // The layer prologue (prologue.hip): see deltanet_prologue.

@@ -40,7 +40,7 @@
  *           16 bytes); LA_ERR_ALIGN otherwise.  o must not alias any input.
  *           S (and z) are read and written.  The
  *           library keeps no state between calls; calls are re-entrant.  It
- *           allocates device memory in three cases, each a stream-ordered
+ *           allocates device memory in three cases (four entry points), each a stream-ordered
  *           workspace (hipMallocAsync on `stream`, released with
  *           hipFreeAsync after its kernels):
  *             - the gated deltanet_prefill with bf16 inputs, dk = 128 and
@@ -58,7 +58,9 @@
  *               P = W^T K and R^T = (Q - A W)^T (see that function), and,
  *               when dk = 128 and dv % 32 == 0, 4 B*H*dk*dv + 2 B*H*T*dv
  *               bytes that receive the forward pass's final state and
- *               output.
+ *               output; gated_deltanet_prefill_backward as well, with
+ *               4 B*H*C bytes (a decay per chunk) instead of those last
+ *               two.
  *           A failed allocation returns LA_ERR_LAUNCH.
  * Sizes.    B, H (or N, H) >= 1; T >= 0 for prefill, any length (the last
  *           64-token chunk may be partial).  T = 0 enqueues no work when
@@ -239,6 +241,35 @@ int deltanet_prefill_backward(const void *q, const void *k, const void *v,
                               void *dk_out, void *dv_out, void *dbeta,
                               float *dS0, int B, int H, int T, int dk, int dv,
                               int dtype, void *stream);
+
+/*
+ * gated_deltanet_prefill_backward -- gradients of gated_deltanet_prefill (one
+ * decay a_t = exp(g_t) per token, section "Gated Delta Net"), for the same
+ * loss as deltanet_prefill_backward, with the gate's gradient dg [B,H,T]
+ * (dtype) as well.  g [B,H,T] (dtype) is required; every other argument,
+ * size limit and error is as for deltanet_prefill_backward.  Per chunk, with
+ * G_r the log-decay summed from the chunk start and G_C its last value, the
+ * ungated formulas take the decay ratios exp(G_r - G_c) in A = tril(Q K^T)
+ * and L, exp(G_r) on the rows of K S, Q S and their gradients, and
+ * exp(G_C - G_r) on the rows of K dSn and u dSn^T; the chain becomes
+ * dS = exp(G_C) dSn - P dSn + R^T dO.  g_t enters only the log-decays G_r,
+ * r >= t, of its own chunk, so dg_t is the sum over those rows of the
+ * gradient of G_r, formed in the same chunk pass from the terms where G
+ * appears (K S and Q S, the ratios in A and L, the state leaving the
+ * chunk); each term carries its own decay, so dg keeps its relative
+ * accuracy when the decays are strong.
+ * The forward chunk states come from the generic kernel here (also for
+ * bf16, dk = 128); the workspace adds one float per chunk to that of
+ * deltanet_prefill_backward (and needs none of its pipelined-pass scratch).
+ */
+int gated_deltanet_prefill_backward(const void *q, const void *k,
+                                    const void *v, const void *beta,
+                                    const void *g, const float *S0,
+                                    const void *dO, const float *dST,
+                                    void *dq, void *dk_out, void *dv_out,
+                                    void *dbeta, void *dg, float *dS0, int B,
+                                    int H, int T, int dk, int dv, int dtype,
+                                    void *stream);
 
 /*
  * deltanet_prologue -- the steps just before the delta rule in the layer of

@@ -156,6 +156,30 @@ def test_backward_validation():
     assert _bwd(db=MISALIGNED) != ALIGN  # dbeta is written element by element
 
 
+def _gbwd(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, S0=None, dO=FAKE, dST=None, dq=FAKE,
+          dk_=FAKE, dv_=FAKE, db=FAKE, dg=FAKE, dS0=None, B=1, H=1, T=64, dk=64, dv=64, dt=1):
+    return la.library().gated_deltanet_prefill_backward(q, k, v, beta, g, S0, dO, dST, dq, dk_,
+                                                        dv_, db, dg, dS0, B, H, T, dk, dv, dt,
+                                                        None)
+
+
+@pytest.mark.parametrize("missing", ["q", "k", "v", "beta", "g", "dO", "dq", "dk_", "dv_", "db",
+                                     "dg"])
+def test_gated_backward_null_pointers(missing):
+    assert _gbwd(**{missing: None}) == NULL
+
+
+def test_gated_backward_validation():
+    assert _gbwd(dt=3) == DTYPE
+    assert _gbwd(T=-1) == SHAPE
+    assert _gbwd(dv=96) == DIM
+    assert _gbwd(dt=0, dk=128) == DIM   # float32: dk, dv <= 64, as without a gate
+    assert _gbwd(dO=MISALIGNED) == ALIGN
+    for out in ("dq", "dk_", "dv_"):
+        assert _gbwd(**{out: MISALIGNED}) == ALIGN
+    assert _gbwd(dg=MISALIGNED) != ALIGN  # dg is written element by element
+
+
 @pytest.mark.parametrize("missing", ["qi", "ki", "qo", "ko"])
 def test_prologue_null_pointers(missing):
     assert _pro(**{missing: None}) == NULL
