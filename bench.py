@@ -77,8 +77,14 @@ ROW_PROFILES = [
      "deltanet_prefill_backward B=4 H=16 T=4096 dk=dv=128 bf16: forward chunk states "
      "(pipelined kernel with state capture), transition pre-pass, reverse chain, "
      "chunk-parallel gradients",
-     ["prefill_pipe<0, 32, true>", "bwd_transition<128>", "bwd_chain_mat<128, 32>",
-      "bwd_grads<128, 128, linattn::BF16>"]),
+     ["prefill_pipe<0, 32, true>", "bwd_transition<128, false>", "bwd_chain_mat<128, 32, false>",
+      "bwd_grads<128, 128, linattn::BF16, false>"]),
+    ("gated_delta_backward_B4_H16_T4096_d128.txt",
+     "gated_deltanet_prefill_backward (one decay per token) B=4 H=16 T=4096 dk=dv=128 bf16: "
+     "forward chunk states (generic kernel), transition pre-pass, reverse chain, "
+     "chunk-parallel gradients with dg",
+     ["prefill_kernel<128, linattn::BF16, 4", "bwd_transition<128, true>",
+      "bwd_chain_mat<128, 32, true>", "bwd_grads<128, 128, linattn::BF16, true>"]),
     ("prologue_B4_H16_T4096_d128.txt",
      "deltanet_prologue B=4 H=16 T=4096 dk=128 bf16, one beta logit per token shared by the heads",
      ["qk_prologue<128, linattn::BF16, true>"]),
@@ -518,7 +524,24 @@ def bench_backward_row(la, workloads, torch, launches=5):
                    "chunk-parallel transition pre-pass (P = W^T K, R = Q - A W), reverse chain "
                    "dS <- dS - P dS + R^T dO, chunk-parallel gradients; bytes are the inputs "
                    "(q, k, v, beta, dO) and gradients (dq, dk, dv, dbeta) only")
-    return {name: r}
+    rows = {name: r}
+    gen = workloads.generator(98)
+    d["g"] = (-torch.nn.functional.softplus(torch.randn(w.B, w.H, w.T, generator=gen)) / 16.0
+              ).to(w.dtype).to(dev)
+
+    def run_g(d):
+        la.gated_deltanet_prefill_backward(d["q"], d["k"], d["v"], d["beta"], d["g"], d["dO"],
+                                           stream=stream)
+
+    us, med = _time_launches(torch, stream, run_g, [d], launches, warmup=1)
+    name, r = _row("gated_deltanet_prefill_backward", "gated_deltanet_prefill_backward (one decay "
+                   f"per token) B={w.B} H={w.H} T={w.T} dk=dv={w.dk} bf16", us, med,
+                   per + 2 * th * 2,
+                   "four kernels: forward chunk states (generic kernel, states captured), "
+                   "transition pre-pass with the decays, reverse chain with the chunk decay, "
+                   "chunk-parallel gradients and dg; bytes as above plus g in and dg out")
+    rows[name] = r
+    return rows
 
 
 def bench_token_gated_rows(la, workloads, torch, launches=20):
