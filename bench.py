@@ -81,9 +81,9 @@ ROW_PROFILES = [
       "bwd_grads<128, 128, linattn::BF16, false>"]),
     ("gated_delta_backward_B4_H16_T4096_d128.txt",
      "gated_deltanet_prefill_backward (one decay per token) B=4 H=16 T=4096 dk=dv=128 bf16: "
-     "forward chunk states (generic kernel), transition pre-pass, reverse chain, "
+     "forward chunk states (pipelined kernel with state capture), transition pre-pass, reverse chain, "
      "chunk-parallel gradients with dg",
-     ["prefill_kernel<128, linattn::BF16, 4", "bwd_transition<128, true>",
+     ["prefill_pipe<2, 32, true>", "bwd_transition<128, true>",
       "bwd_chain_mat<128, 32, true>", "bwd_grads<128, 128, linattn::BF16, true>"]),
     ("prologue_B4_H16_T4096_d128.txt",
      "deltanet_prologue B=4 H=16 T=4096 dk=128 bf16, one beta logit per token shared by the heads",
@@ -537,7 +537,7 @@ def bench_backward_row(la, workloads, torch, launches=5):
     name, r = _row("gated_deltanet_prefill_backward", "gated_deltanet_prefill_backward (one decay "
                    f"per token) B={w.B} H={w.H} T={w.T} dk=dv={w.dk} bf16", us, med,
                    per + 2 * th * 2,
-                   "four kernels: forward chunk states (generic kernel, states captured), "
+                   "four kernels: forward chunk states (pipelined kernel, states captured), "
                    "transition pre-pass with the decays, reverse chain with the chunk decay, "
                    "chunk-parallel gradients and dg; bytes as above plus g in and dg out")
     rows[name] = r

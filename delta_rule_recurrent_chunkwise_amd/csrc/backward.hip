@@ -1684,13 +1684,14 @@ __global__ __launch_bounds__(256) void zero_state(float* __restrict__ p, size_t 
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0.f;
 }
 
-// The pipelined forward kernel (bf16, dk = 128, dv % 32 == 0, no gate)
-// writes an output and a final state it does not skip; they go to scratch
-// at the end of the workspace (the final state where a copy of S0 was put).
-bool pass1_pipelined(int bf16, const BackwardArgs& a) { return bf16 && !a.g && a.dk_ == 128 && a.dv_ % 32 == 0; }
+// The pipelined forward kernels (bf16, dk = 128, dv % 32 == 0; ungated or
+// one decay per token) write an output and a final state they do not skip;
+// they go to scratch in the workspace (the final state where a copy of S0
+// was put).
+bool pass1_pipelined(int bf16, const BackwardArgs& a) { return bf16 && a.dk_ == 128 && a.dv_ % 32 == 0; }
 
 // [Sc, dSc: fp32 nchunks x dk x dv]
-// [pipelined pass 1: final state, output | gated: gC, fp32 nchunks]
+// [pipelined pass 1: final state, output][gated: gC, fp32 nchunks]
 // [bf16: P nchunks x dk x dk, R^T nchunks x dk x 64]
 size_t delta_backward_workspace_bytes(int bf16, const BackwardArgs& a) {
   const size_t nchunks = (size_t)a.B * a.H * ((a.T + kC - 1) / kC);
@@ -1726,7 +1727,10 @@ hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, hipStream_t st
   float* Sc = reinterpret_cast<float*>(ws);
   float* dSc = Sc + nst;
   float* s_scratch = dSc + nst;  // pipelined pass 1: the final state lands here
-  float* gC = a.g ? dSc + nst : nullptr;
+  bf16_t* o_scratch = reinterpret_cast<bf16_t*>(s_scratch + nS);
+  float* gC = !a.g ? nullptr
+          : pass1_pipelined(bf16, a) ? reinterpret_cast<float*>(o_scratch + (size_t)a.B * a.H * a.T * a.dv_)
+                                     : dSc + nst;
   PrefillArgs f{};
   f.q = a.q;
   f.k = a.k;
@@ -1743,12 +1747,12 @@ hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, hipStream_t st
   if (a.S0 && pass1_pipelined(bf16, a))
     e = hipMemcpyAsync(s_scratch, a.S0, nS * sizeof(float), hipMemcpyDeviceToDevice, st);
   if (e == hipSuccess) {
-    if (a.g) {
-      e = launch_prefill_generic(PF_SGATED, bf16, a.dk_, f, st);
-    } else if (pass1_pipelined(bf16, a)) {
+    if (pass1_pipelined(bf16, a)) {
       f.S = s_scratch;
-      f.o = reinterpret_cast<bf16_t*>(s_scratch + nS);
-      e = launch_prefill_pipe(f, nullptr, st);
+      f.o = o_scratch;
+      e = a.g ? launch_prefill_pipe_token(f, st) : launch_prefill_pipe(f, nullptr, st);
+    } else if (a.g) {
+      e = launch_prefill_generic(PF_SGATED, bf16, a.dk_, f, st);
     } else {
       e = launch_prefill_generic(PF_DELTA, bf16, a.dk_, f, st);
     }

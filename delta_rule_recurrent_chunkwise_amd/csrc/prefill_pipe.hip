@@ -869,7 +869,8 @@ hipError_t launch_prefill_pipe_token(const PrefillArgs& a, hipStream_t st) {
   p.dv = a.dv;
   p.use_init = a.use_init;
   p.Tq = a.T;
-  return launch_pipe_t<2>(p, (long)a.B * a.H, a.dv, st);
+  p.Sc = a.Sc;
+  return a.Sc ? launch_pipe_t<2, true>(p, (long)a.B * a.H, a.dv, st) : launch_pipe_t<2>(p, (long)a.B * a.H, a.dv, st);
 }
 
 }  // namespace linattn

@@ -58,9 +58,8 @@
  *               P = W^T K and R^T = (Q - A W)^T (see that function), and,
  *               when dk = 128 and dv % 32 == 0, 4 B*H*dk*dv + 2 B*H*T*dv
  *               bytes that receive the forward pass's final state and
- *               output; gated_deltanet_prefill_backward as well, with
- *               4 B*H*C bytes (a decay per chunk) instead of those last
- *               two.
+ *               output; gated_deltanet_prefill_backward as well, plus
+ *               4 B*H*C bytes (a decay per chunk).
  *           A failed allocation returns LA_ERR_LAUNCH.
  * Sizes.    B, H (or N, H) >= 1; T >= 0 for prefill, any length (the last
  *           64-token chunk may be partial).  T = 0 enqueues no work when
@@ -258,9 +257,8 @@ int deltanet_prefill_backward(const void *q, const void *k, const void *v,
  * appears (K S and Q S, the ratios in A and L, the state leaving the
  * chunk); each term carries its own decay, so dg keeps its relative
  * accuracy when the decays are strong.
- * The forward chunk states come from the generic kernel here (also for
- * bf16, dk = 128); the workspace adds one float per chunk to that of
- * deltanet_prefill_backward (and needs none of its pipelined-pass scratch).
+ * The workspace is that of deltanet_prefill_backward plus one float per
+ * chunk.
  */
 int gated_deltanet_prefill_backward(const void *q, const void *k,
                                     const void *v, const void *beta,
