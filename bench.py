@@ -693,13 +693,73 @@ def copy_probe(torch, nbytes=1 << 30, reps=5):
     return nbytes
 
 
+def host_cores():
+    """The host cores this process may use: its CPU affinity, capped by
+    OMP_NUM_THREADS where the environment sets it (a GPU machine gives each GPU's
+    job a share of its cores and says so there, whatever the affinity mask
+    shows)."""
+    n = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS")
+    if share and share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return n
+
+
+def parity_leg(la, workloads, oracle, torch):
+    """The oracle's results against the GPU's for every workload, as the
+    bench line's record of the achieved error: max|gpu - ref| / max|ref| of
+    o, S (and z) over whole tensors for the four prefill workloads, and for
+    the decode workload over the full state and every output after one
+    step."""
+    dev = torch.device("cuda:0")
+
+    def err(gpu, ref):
+        import numpy as np
+        g = gpu.detach().to("cpu", torch.float64).numpy()
+        r = np.asarray(ref, np.float64)
+        if not np.all(np.isfinite(g)):
+            return float("inf")
+        return float(np.max(np.abs(g - r)) / max(float(np.max(np.abs(r))), 1e-300))
+
+    out = {}
+    for w in workloads.WORKLOADS:
+        inp = workloads.make_workload(w)
+        d = {n: t.to(dev) for n, t in inp.items()}
+        tol = 1e-4 if w.dtype == torch.float32 else 2e-2
+        if w.kind == "la":
+            o, S, z = la.la_prefill(d["q"], d["k"], d["v"])
+            torch.cuda.synchronize()
+            ro, rS, rz = oracle.la_recurrent(inp["q"], inp["k"], inp["v"])
+            e = {"o": err(o, ro), "S": err(S, rS), "z": err(z, rz)}
+        elif w.kind in ("delta", "gated"):
+            o, S = la.deltanet_prefill(d["q"], d["k"], d["v"], d["beta"], g=d.get("g"))
+            torch.cuda.synchronize()
+            del d
+            ro, rS = oracle.delta_recurrent(inp["q"], inp["k"], inp["v"], inp["beta"],
+                                            inp.get("g"))
+            e = {"o": err(o, ro), "S": err(S, rS)}
+        else:
+            S = d["S0"].clone()
+            o = la.deltanet_decode_step(d["q"][0], d["k"][0], d["v"][0], d["beta"][0], S)
+            torch.cuda.synchronize()
+            ro, rS = oracle.delta_recurrent(inp["q"][0][:, :, None], inp["k"][0][:, :, None],
+                                            inp["v"][0][:, :, None],
+                                            inp["beta"][0][:, :, None], None, S0=inp["S0"])
+            e = {"o step 1": err(o, ro[:, :, 0]), "S step 1": err(S, rS)}
+        e["tol"] = tol
+        e["ok"] = all(v <= tol for k, v in e.items() if k != "tol")
+        out[w.name] = e
+        del inp
+    return out
+
+
 def cpu_baseline(workloads, oracle, torch, prefill_inp, w, decode_inp, wd, budget_s=10.0,
                  decode_budget_s=3.0):
     """The float64 oracle (as written, untuned) timed on the host cores: whole
     passes over the prefill workload, repeated until about `budget_s` seconds
     of work are done, and whole decode steps over all heads for about
     `decode_budget_s` seconds."""
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    cores = host_cores()
     x = {n: prefill_inp[n].contiguous() for n in ("q", "k", "v", "beta")}
     passes = 0
     t0 = time.perf_counter()
@@ -851,8 +911,11 @@ def main():
         if not args.no_rows:
             line["rows"] = bench_rows(la, workloads, torch)
         if not args.no_cpu_baseline:
+            # the CPU leg: the oracle, timed as the baseline, and its results
+            # against the GPU's for every workload
             import oracle
             line["cpu_baseline"] = cpu_baseline(workloads, oracle, torch, pinp, w, dinp, wd)
+            line["parity"] = parity_leg(la, workloads, oracle, torch)
     print(json.dumps(line), flush=True)
 
 

@@ -21,6 +21,9 @@ __all__ = [
     "gated_deltanet_prefill", "gated_deltanet_decode_step", "gla_prefill",
     "gla_decode_step", "deltanet_prefill_backward", "gated_deltanet_prefill_backward",
     "deltanet_prologue", "la_strerror",
+    "la_prefill_workspace_bytes", "deltanet_prefill_workspace_bytes",
+    "gla_prefill_workspace_bytes", "deltanet_prefill_backward_workspace_bytes",
+    "gated_deltanet_prefill_backward_workspace_bytes",
     "library", "LIB_PATH",
     "EXPORTED_SYMBOLS",
     "LinAttnError",
@@ -31,7 +34,13 @@ EXPORTED_SYMBOLS = ("la_prefill", "la_decode_step", "deltanet_prefill",
                     "deltanet_decode_step", "gated_deltanet_prefill",
                     "gated_deltanet_decode_step", "gla_prefill", "gla_decode_step",
                     "deltanet_prefill_backward", "gated_deltanet_prefill_backward",
-                    "deltanet_prologue", "la_strerror")
+                    "deltanet_prologue",
+                    "la_prefill_workspace_bytes", "deltanet_prefill_workspace_bytes",
+                    "gla_prefill_workspace_bytes",
+                    "deltanet_prefill_backward_workspace_bytes",
+                    "gated_deltanet_prefill_backward_workspace_bytes",
+                    "la_strerror")
+WORKSPACE_QUERIES = EXPORTED_SYMBOLS[11:16]
 
 LA_DTYPE_F32, LA_DTYPE_BF16 = 0, 1
 _DTYPES = {torch.float32: LA_DTYPE_F32, torch.bfloat16: LA_DTYPE_BF16}
@@ -56,20 +65,27 @@ def library():
                 f"{LIB_PATH} is missing: build it with "
                 "`python -m delta_rule_recurrent_chunkwise_amd.build`")
         lib = ctypes.CDLL(LIB_PATH)
-        P, I = ctypes.c_void_p, ctypes.c_int
-        lib.la_prefill.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+        P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        lib.la_prefill.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, Z, P]
         lib.la_decode_step.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
-        lib.deltanet_prefill.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+        lib.deltanet_prefill.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, Z, P]
         lib.deltanet_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
-        lib.gated_deltanet_prefill.argtypes = lib.deltanet_prefill.argtypes
+        lib.gated_deltanet_prefill.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
         lib.gated_deltanet_decode_step.argtypes = lib.deltanet_decode_step.argtypes
-        lib.gla_prefill.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+        lib.gla_prefill.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, Z, P]
         lib.gla_decode_step.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
-        lib.deltanet_prefill_backward.argtypes = [P] * 12 + [I] * 6 + [P]
-        lib.gated_deltanet_prefill_backward.argtypes = [P] * 14 + [I] * 6 + [P]
+        lib.deltanet_prefill_backward.argtypes = [P] * 12 + [I] * 6 + [P, Z, P]
+        lib.gated_deltanet_prefill_backward.argtypes = [P] * 14 + [I] * 6 + [P, Z, P]
         lib.deltanet_prologue.argtypes = [P] * 6 + [I] * 6 + [ctypes.c_float, I, P]
-        for fn in EXPORTED_SYMBOLS[:-1]:
+        for fn in EXPORTED_SYMBOLS[:11]:
             getattr(lib, fn).restype = I
+        lib.la_prefill_workspace_bytes.argtypes = [I] * 6
+        lib.deltanet_prefill_workspace_bytes.argtypes = [I] * 7
+        lib.gla_prefill_workspace_bytes.argtypes = [I] * 6
+        lib.deltanet_prefill_backward_workspace_bytes.argtypes = [I] * 6
+        lib.gated_deltanet_prefill_backward_workspace_bytes.argtypes = [I] * 6
+        for fn in WORKSPACE_QUERIES:
+            getattr(lib, fn).restype = Z
         lib.la_strerror.argtypes = [I]
         lib.la_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -78,6 +94,37 @@ def library():
 
 def la_strerror(code: int) -> str:
     return library().la_strerror(int(code)).decode()
+
+
+def _dt(dtype) -> int:
+    return dtype if isinstance(dtype, int) else _DTYPES[dtype]
+
+
+def la_prefill_workspace_bytes(B, H, T, dk, dv, dtype) -> int:
+    """Bytes of workspace la_prefill needs for these sizes (0: none)."""
+    return int(library().la_prefill_workspace_bytes(B, H, T, dk, dv, _dt(dtype)))
+
+
+def deltanet_prefill_workspace_bytes(gated, B, H, T, dk, dv, dtype) -> int:
+    """Bytes of workspace deltanet_prefill needs (gated: g given; 0: none)."""
+    return int(library().deltanet_prefill_workspace_bytes(int(bool(gated)), B, H, T, dk, dv,
+                                                          _dt(dtype)))
+
+
+def gla_prefill_workspace_bytes(B, H, T, dk, dv, dtype) -> int:
+    """Bytes of workspace gla_prefill needs for these sizes (0: none)."""
+    return int(library().gla_prefill_workspace_bytes(B, H, T, dk, dv, _dt(dtype)))
+
+
+def deltanet_prefill_backward_workspace_bytes(B, H, T, dk, dv, dtype) -> int:
+    """Bytes of workspace deltanet_prefill_backward needs."""
+    return int(library().deltanet_prefill_backward_workspace_bytes(B, H, T, dk, dv, _dt(dtype)))
+
+
+def gated_deltanet_prefill_backward_workspace_bytes(B, H, T, dk, dv, dtype) -> int:
+    """Bytes of workspace gated_deltanet_prefill_backward needs."""
+    return int(library().gated_deltanet_prefill_backward_workspace_bytes(B, H, T, dk, dv,
+                                                                         _dt(dtype)))
 
 
 def _check(fn: str, rc: int):
@@ -131,6 +178,22 @@ def _state(fn, name, t, shape, dev):
     return t
 
 
+def _workspace(nbytes, dev, workspace):
+    """(pointer, size) of a workspace of at least nbytes bytes: the caller's
+    uint8 tensor if given, else a fresh torch allocation (256-byte aligned)
+    that lives until the call returns; the library's kernels are enqueued on
+    the current stream, so torch's caching allocator reuses the block only
+    for work ordered after them."""
+    if nbytes == 0:
+        return None, 0, None
+    if workspace is None:
+        workspace = torch.empty(int(nbytes), device=dev, dtype=torch.uint8)
+    elif (not isinstance(workspace, torch.Tensor) or workspace.device != dev
+          or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(), workspace
+
+
 def _out(fn, o, shape, dev, dtype):
     if o is None:
         return torch.empty(shape, device=dev, dtype=dtype)
@@ -140,11 +203,14 @@ def _out(fn, o, shape, dev, dtype):
     return o
 
 
-def la_prefill(q, k, v, S=None, z=None, use_initial_state=False, o=None, stream=None):
+def la_prefill(q, k, v, S=None, z=None, use_initial_state=False, o=None, stream=None,
+               workspace=None):
     """ELU+1 linear attention with normaliser over q, k [B,H,T,dk], v [B,H,T,dv].
     Returns (o [B,H,T,dv], S [B,H,dk,dv] fp32, z [B,H,dk] fp32).  With
     use_initial_state the given S, z are the initial state; they are
-    overwritten with the final state."""
+    overwritten with the final state.  workspace: an optional device tensor
+    of at least la_prefill_workspace_bytes(...) bytes (allocated here if
+    None and one is needed)."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     dev, dtype = _inputs("la_prefill", dict(q=q, k=k, v=v),
@@ -154,9 +220,10 @@ def la_prefill(q, k, v, S=None, z=None, use_initial_state=False, o=None, stream=
     S = _state("la_prefill", "S", S, (B, H, dk, dv), dev)
     z = _state("la_prefill", "z", z, (B, H, dk), dev)
     o = _out("la_prefill", o, (B, H, T, dv), dev, dtype)
+    wp, wn, _keep = _workspace(la_prefill_workspace_bytes(B, H, T, dk, dv, dtype), dev, workspace)
     rc = library().la_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(S), _ptr(z),
                               int(bool(use_initial_state)), B, H, T, dk, dv,
-                              _DTYPES[dtype], _stream(dev, stream))
+                              _DTYPES[dtype], wp, wn, _stream(dev, stream))
     _check("la_prefill", rc)
     return o, S, z
 
@@ -178,7 +245,7 @@ def la_decode_step(q, k, v, S, z, o=None, stream=None):
 
 
 def deltanet_prefill(q, k, v, beta, g=None, S=None, use_initial_state=False, o=None,
-                     stream=None):
+                     stream=None, workspace=None):
     """Delta rule (g None) or per-key-channel gated delta rule (g = log-decay
     [B,H,T,dk]) over q, k [B,H,T,dk], v [B,H,T,dv], beta [B,H,T].
     Returns (o [B,H,T,dv], S [B,H,dk,dv] fp32)."""
@@ -191,9 +258,12 @@ def deltanet_prefill(q, k, v, beta, g=None, S=None, use_initial_state=False, o=N
         raise ValueError("deltanet_prefill: use_initial_state needs S")
     S = _state("deltanet_prefill", "S", S, (B, H, dk, dv), dev)
     o = _out("deltanet_prefill", o, (B, H, T, dv), dev, dtype)
+    wp, wn, _keep = _workspace(deltanet_prefill_workspace_bytes(g is not None, B, H, T, dk, dv, dtype),
+                               dev, workspace)
     rc = library().deltanet_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
                                     _ptr(o), _ptr(S), int(bool(use_initial_state)),
-                                    B, H, T, dk, dv, _DTYPES[dtype], _stream(dev, stream))
+                                    B, H, T, dk, dv, _DTYPES[dtype], wp, wn,
+                                    _stream(dev, stream))
     _check("deltanet_prefill", rc)
     return o, S
 
@@ -259,7 +329,8 @@ def gated_deltanet_decode_step(q, k, v, beta, g, S, o=None, stream=None):
     return o
 
 
-def gla_prefill(q, k, v, g=None, S=None, use_initial_state=False, o=None, stream=None):
+def gla_prefill(q, k, v, g=None, S=None, use_initial_state=False, o=None, stream=None,
+                workspace=None):
     """Gated linear attention S <- a S + k^T v, o = q S over q, k [B,H,T,dk],
     v [B,H,T,dv], g = log-decay [B,H,T] or None.
     Returns (o [B,H,T,dv], S [B,H,dk,dv] fp32)."""
@@ -272,9 +343,10 @@ def gla_prefill(q, k, v, g=None, S=None, use_initial_state=False, o=None, stream
         raise ValueError("gla_prefill: use_initial_state needs S")
     S = _state("gla_prefill", "S", S, (B, H, dk, dv), dev)
     o = _out("gla_prefill", o, (B, H, T, dv), dev, dtype)
+    wp, wn, _keep = _workspace(gla_prefill_workspace_bytes(B, H, T, dk, dv, dtype), dev, workspace)
     rc = library().gla_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(o), _ptr(S),
                                int(bool(use_initial_state)), B, H, T, dk, dv,
-                               _DTYPES[dtype], _stream(dev, stream))
+                               _DTYPES[dtype], wp, wn, _stream(dev, stream))
     _check("gla_prefill", rc)
     return o, S
 
@@ -295,7 +367,7 @@ def gla_decode_step(q, k, v, S, g=None, o=None, stream=None):
 
 
 def deltanet_prefill_backward(q, k, v, beta, dO, S0=None, dST=None, want_dS0=False,
-                              stream=None):
+                              stream=None, workspace=None):
     """Gradients of deltanet_prefill (no gate) for the loss
     sum(dO * o) + sum(dST * S_T): returns (dq, dk, dv, dbeta, dS0), dS0 None
     unless want_dS0.  q, k [B,H,T,dk]; v, dO [B,H,T,dv]; beta [B,H,T] (one
@@ -313,16 +385,18 @@ def deltanet_prefill_backward(q, k, v, beta, dO, S0=None, dST=None, want_dS0=Fal
     dvv = torch.empty_like(v)
     db = torch.empty_like(beta)
     dS0 = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32) if want_dS0 else None
+    wp, wn, _keep = _workspace(deltanet_prefill_backward_workspace_bytes(B, H, T, dk, dv, dtype),
+                               dev, workspace)
     rc = library().deltanet_prefill_backward(
         _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dST), _ptr(dq),
         _ptr(dkk), _ptr(dvv), _ptr(db), _ptr(dS0), B, H, T, dk, dv, _DTYPES[dtype],
-        _stream(dev, stream))
+        wp, wn, _stream(dev, stream))
     _check("deltanet_prefill_backward", rc)
     return dq, dkk, dvv, db, dS0
 
 
 def gated_deltanet_prefill_backward(q, k, v, beta, g, dO, S0=None, dST=None, want_dS0=False,
-                                    stream=None):
+                                    stream=None, workspace=None):
     """Gradients of gated_deltanet_prefill (one log-decay per token) for the
     loss sum(dO * o) + sum(dST * S_T): returns (dq, dk, dv, dbeta, dg, dS0),
     dS0 None unless want_dS0.  g [B,H,T] in the inputs' dtype; the rest as
@@ -342,10 +416,12 @@ def gated_deltanet_prefill_backward(q, k, v, beta, g, dO, S0=None, dST=None, wan
     db = torch.empty_like(beta)
     dg = torch.empty_like(g)
     dS0 = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32) if want_dS0 else None
+    wp, wn, _keep = _workspace(
+        gated_deltanet_prefill_backward_workspace_bytes(B, H, T, dk, dv, dtype), dev, workspace)
     rc = library().gated_deltanet_prefill_backward(
         _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(dO), _ptr(dST),
         _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(db), _ptr(dg), _ptr(dS0), B, H, T, dk, dv,
-        _DTYPES[dtype], _stream(dev, stream))
+        _DTYPES[dtype], wp, wn, _stream(dev, stream))
     _check("gated_deltanet_prefill_backward", rc)
     return dq, dkk, dvv, db, dg, dS0
 

@@ -30,6 +30,48 @@ bool sizes_ok(long long b, long long h, long long t, int dk, int dv, bool allow_
 
 int launch_rc(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH; }
 
+// A workspace is needed only when its size is not 0: then it must be given,
+// be at least that large, and start on a 256-byte boundary.
+int workspace_rc(size_t need, const void* ws, size_t have) {
+  if (need == 0) return LA_OK;
+  if (ws == nullptr || have < need) return LA_ERR_WORKSPACE;
+  if (((uintptr_t)ws & 255u) != 0) return LA_ERR_ALIGN;
+  return LA_OK;
+}
+
+// The checks every prefill entry point shares, in the order the header
+// documents them; LA_OK when the call may proceed to its workspace check.
+int prefill_args_rc(int dtype, int B, int H, int T, int dk, int dv) {
+  if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
+  if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1, true)) return LA_ERR_SHAPE;
+  if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
+  return LA_OK;
+}
+
+size_t prefill_ws(int mode, int B, int H, int T, int dk, int dv, int dtype) {
+  if (prefill_args_rc(dtype, B, H, T, dk, dv) != LA_OK) return 0;
+  linattn::PrefillArgs a{};
+  a.B = B;
+  a.H = H;
+  a.T = T;
+  a.dv = dv;
+  return linattn::prefill_workspace_bytes(mode, dtype == LA_DTYPE_BF16, dk, a);
+}
+
+size_t backward_ws(int gated, int B, int H, int T, int dk, int dv, int dtype) {
+  if (prefill_args_rc(dtype, B, H, T, dk, dv) != LA_OK) return 0;
+  if (dtype == LA_DTYPE_F32 && (dk > 64 || dv > 64)) return 0;  // not supported
+  linattn::BackwardArgs a{};
+  a.B = B;
+  a.H = H;
+  a.T = T;
+  a.dk_ = dk;
+  a.dv_ = dv;
+  static const char one = 0;
+  a.g = gated ? &one : nullptr;  // only its presence matters here
+  return linattn::delta_backward_workspace_bytes(dtype == LA_DTYPE_BF16, a);
+}
+
 }  // namespace
 
 extern "C" {
@@ -46,24 +88,31 @@ const char* la_strerror(int code) {
       return "unsupported head dimension: dk and dv must each be 16, 32, 64 or 128 "
              "(float32: dk <= 64 for deltanet_prefill with a per-channel gate, "
              "dk and dv <= 64 for the backward entry points)";
-    case LA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch or a workspace allocation";
+    case LA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case LA_ERR_WORKSPACE:
+      return "the workspace is NULL or smaller than the matching *_workspace_bytes() query returns";
     case LA_ERR_ALIGN:
       return "q, k, v and o (prefill; and dO, dq, dk, dv, backward; q and k in and out, prologue) "
-             "and S (decode) must be 16-byte aligned";
+             "and S (decode) must be 16-byte aligned, and a workspace 256-byte aligned";
     default: return "unknown error code";
   }
 }
 
+size_t la_prefill_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype) {
+  return prefill_ws(linattn::PF_LA, B, H, T, dk, dv, dtype);
+}
+
 int la_prefill(const void* q, const void* k, const void* v, void* o, float* S, float* z,
                int use_initial_state, int B, int H, int T, int dk, int dv, int dtype,
-               void* stream) {
+               void* workspace, size_t workspace_bytes, void* stream) {
   if (!S || !z || (T != 0 && (!q || !k || !v || !o))) return LA_ERR_NULL;
-  if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
-  if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1, true)) return LA_ERR_SHAPE;
-  if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
+  if (int rc = prefill_args_rc(dtype, B, H, T, dk, dv)) return rc;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LA_ERR_ALIGN;
+  if (int rc = workspace_rc(la_prefill_workspace_bytes(B, H, T, dk, dv, dtype), workspace,
+                            workspace_bytes))
+    return rc;
   linattn::PrefillArgs a{q, k, v, nullptr, nullptr, o, S, z, B, H, T, dv, use_initial_state ? 1 : 0};
-  return launch_rc(linattn::launch_prefill(linattn::PF_LA, dtype == LA_DTYPE_BF16, dk, a,
+  return launch_rc(linattn::launch_prefill(linattn::PF_LA, dtype == LA_DTYPE_BF16, dk, a, workspace,
                                            static_cast<hipStream_t>(stream)));
 }
 
@@ -79,18 +128,24 @@ int la_decode_step(const void* q, const void* k, const void* v, void* o, float* 
                                           static_cast<hipStream_t>(stream)));
 }
 
+size_t deltanet_prefill_workspace_bytes(int gated, int B, int H, int T, int dk, int dv, int dtype) {
+  return prefill_ws(gated ? linattn::PF_GATED : linattn::PF_DELTA, B, H, T, dk, dv, dtype);
+}
+
 int deltanet_prefill(const void* q, const void* k, const void* v, const void* beta,
                      const void* g, void* o, float* S, int use_initial_state, int B, int H,
-                     int T, int dk, int dv, int dtype, void* stream) {
+                     int T, int dk, int dv, int dtype, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   if (!S || (T != 0 && (!q || !k || !v || !beta || !o))) return LA_ERR_NULL;
-  if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
-  if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1, true)) return LA_ERR_SHAPE;
-  if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
+  if (int rc = prefill_args_rc(dtype, B, H, T, dk, dv)) return rc;
   if (g && dtype == LA_DTYPE_F32 && dk > 64) return LA_ERR_UNSUPPORTED_DIM;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LA_ERR_ALIGN;
+  if (int rc = workspace_rc(deltanet_prefill_workspace_bytes(g != nullptr, B, H, T, dk, dv, dtype),
+                            workspace, workspace_bytes))
+    return rc;
   linattn::PrefillArgs a{q, k, v, beta, g, o, S, nullptr, B, H, T, dv, use_initial_state ? 1 : 0};
   return launch_rc(linattn::launch_prefill(g ? linattn::PF_GATED : linattn::PF_DELTA, dtype == LA_DTYPE_BF16, dk, a,
-                                           static_cast<hipStream_t>(stream)));
+                                           workspace, static_cast<hipStream_t>(stream)));
 }
 
 int deltanet_decode_step(const void* q, const void* k, const void* v, const void* beta,
@@ -110,12 +165,10 @@ int gated_deltanet_prefill(const void* q, const void* k, const void* v, const vo
                            const void* g, void* o, float* S, int use_initial_state, int B,
                            int H, int T, int dk, int dv, int dtype, void* stream) {
   if (!S || (T != 0 && (!q || !k || !v || !beta || !g || !o))) return LA_ERR_NULL;
-  if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
-  if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1, true)) return LA_ERR_SHAPE;
-  if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
+  if (int rc = prefill_args_rc(dtype, B, H, T, dk, dv)) return rc;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LA_ERR_ALIGN;
   linattn::PrefillArgs a{q, k, v, beta, g, o, S, nullptr, B, H, T, dv, use_initial_state ? 1 : 0};
-  return launch_rc(linattn::launch_prefill(linattn::PF_SGATED, dtype == LA_DTYPE_BF16, dk, a,
+  return launch_rc(linattn::launch_prefill(linattn::PF_SGATED, dtype == LA_DTYPE_BF16, dk, a, nullptr,
                                            static_cast<hipStream_t>(stream)));
 }
 
@@ -132,16 +185,21 @@ int gated_deltanet_decode_step(const void* q, const void* k, const void* v, cons
                                           static_cast<hipStream_t>(stream)));
 }
 
+size_t gla_prefill_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype) {
+  return prefill_ws(linattn::PF_GLA, B, H, T, dk, dv, dtype);
+}
+
 int gla_prefill(const void* q, const void* k, const void* v, const void* g, void* o, float* S,
                 int use_initial_state, int B, int H, int T, int dk, int dv, int dtype,
-                void* stream) {
+                void* workspace, size_t workspace_bytes, void* stream) {
   if (!S || (T != 0 && (!q || !k || !v || !o))) return LA_ERR_NULL;
-  if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
-  if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1, true)) return LA_ERR_SHAPE;
-  if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
+  if (int rc = prefill_args_rc(dtype, B, H, T, dk, dv)) return rc;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LA_ERR_ALIGN;
+  if (int rc = workspace_rc(gla_prefill_workspace_bytes(B, H, T, dk, dv, dtype), workspace,
+                            workspace_bytes))
+    return rc;
   linattn::PrefillArgs a{q, k, v, nullptr, g, o, S, nullptr, B, H, T, dv, use_initial_state ? 1 : 0};
-  return launch_rc(linattn::launch_prefill(linattn::PF_GLA, dtype == LA_DTYPE_BF16, dk, a,
+  return launch_rc(linattn::launch_prefill(linattn::PF_GLA, dtype == LA_DTYPE_BF16, dk, a, workspace,
                                            static_cast<hipStream_t>(stream)));
 }
 
@@ -157,37 +215,46 @@ int gla_decode_step(const void* q, const void* k, const void* v, const void* g, 
                                           static_cast<hipStream_t>(stream)));
 }
 
+size_t deltanet_prefill_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype) {
+  return backward_ws(0, B, H, T, dk, dv, dtype);
+}
+
 int deltanet_prefill_backward(const void* q, const void* k, const void* v, const void* beta,
                               const float* S0, const void* dO, const float* dST, void* dq, void* dk_out,
                               void* dv_out, void* dbeta, float* dS0, int B, int H, int T, int dk,
-                              int dv, int dtype, void* stream) {
+                              int dv, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   if (T != 0 && (!q || !k || !v || !beta || !dO || !dq || !dk_out || !dv_out || !dbeta)) return LA_ERR_NULL;
-  if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
-  if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1, true)) return LA_ERR_SHAPE;
-  if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
+  if (int rc = prefill_args_rc(dtype, B, H, T, dk, dv)) return rc;
   if (dtype == LA_DTYPE_F32 && (dk > 64 || dv > 64)) return LA_ERR_UNSUPPORTED_DIM;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(dq) || !aligned16(dk_out) ||
       !aligned16(dv_out))
     return LA_ERR_ALIGN;
+  if (int rc = workspace_rc(backward_ws(0, B, H, T, dk, dv, dtype), workspace, workspace_bytes)) return rc;
   linattn::BackwardArgs a{q, k, v, beta, S0, dO, dST, dq, dk_out, dv_out, dbeta, dS0, B, H, T, dk, dv};
-  return launch_rc(linattn::launch_delta_backward(dtype == LA_DTYPE_BF16, a, static_cast<hipStream_t>(stream)));
+  return launch_rc(linattn::launch_delta_backward(dtype == LA_DTYPE_BF16, a, workspace,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+size_t gated_deltanet_prefill_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype) {
+  return backward_ws(1, B, H, T, dk, dv, dtype);
 }
 
 int gated_deltanet_prefill_backward(const void* q, const void* k, const void* v, const void* beta,
                                     const void* g, const float* S0, const void* dO, const float* dST,
                                     void* dq, void* dk_out, void* dv_out, void* dbeta, void* dg, float* dS0,
-                                    int B, int H, int T, int dk, int dv, int dtype, void* stream) {
+                                    int B, int H, int T, int dk, int dv, int dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
   if (T != 0 && (!q || !k || !v || !beta || !g || !dO || !dq || !dk_out || !dv_out || !dbeta || !dg))
     return LA_ERR_NULL;
-  if (!dtype_ok(dtype)) return LA_ERR_DTYPE;
-  if (!sizes_ok(B, H, T, dk > 0 ? dk : 1, dv > 0 ? dv : 1, true)) return LA_ERR_SHAPE;
-  if (!dim_ok(dk) || !dim_ok(dv)) return LA_ERR_UNSUPPORTED_DIM;
+  if (int rc = prefill_args_rc(dtype, B, H, T, dk, dv)) return rc;
   if (dtype == LA_DTYPE_F32 && (dk > 64 || dv > 64)) return LA_ERR_UNSUPPORTED_DIM;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(dq) || !aligned16(dk_out) ||
       !aligned16(dv_out))
     return LA_ERR_ALIGN;
+  if (int rc = workspace_rc(backward_ws(1, B, H, T, dk, dv, dtype), workspace, workspace_bytes)) return rc;
   linattn::BackwardArgs a{q, k, v, beta, S0, dO, dST, dq, dk_out, dv_out, dbeta, dS0, B, H, T, dk, dv, g, dg};
-  return launch_rc(linattn::launch_delta_backward(dtype == LA_DTYPE_BF16, a, static_cast<hipStream_t>(stream)));
+  return launch_rc(linattn::launch_delta_backward(dtype == LA_DTYPE_BF16, a, workspace,
+                                                  static_cast<hipStream_t>(stream)));
 }
 
 int deltanet_prologue(const void* q_in, const void* k_in, const void* beta_logits, void* q_out,

@@ -1684,28 +1684,27 @@ __global__ __launch_bounds__(256) void zero_state(float* __restrict__ p, size_t 
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0.f;
 }
 
-// The pipelined forward kernels (bf16, dk = 128, dv % 32 == 0; ungated or
-// one decay per token) write an output and a final state they do not skip;
-// they go to scratch in the workspace (the final state where a copy of S0
-// was put).
 bool pass1_pipelined(int bf16, const BackwardArgs& a) { return bf16 && a.dk_ == 128 && a.dv_ % 32 == 0; }
 
-// [Sc, dSc: fp32 nchunks x dk x dv]
-// [pipelined pass 1: final state, output][gated: gC, fp32 nchunks]
-// [bf16: P nchunks x dk x dk, R^T nchunks x dk x 64]
-size_t delta_backward_workspace_bytes(int bf16, const BackwardArgs& a) {
-  const size_t nchunks = (size_t)a.B * a.H * ((a.T + kC - 1) / kC);
-  size_t n = 2 * nchunks * a.dk_ * a.dv_ * sizeof(float);
-  if (pass1_pipelined(bf16, a))
-    n += (size_t)a.B * a.H * a.dk_ * a.dv_ * sizeof(float) + (size_t)a.B * a.H * a.T * a.dv_ * sizeof(bf16_t);
-  if (a.g) n += nchunks * sizeof(float);
-  if (bf16) n = (n + 255) / 256 * 256 + nchunks * a.dk_ * (a.dk_ + kC) * sizeof(bf16_t);
-  return n;
-}
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
 }  // namespace
 
-hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, hipStream_t st) {
+// Workspace layout, each region starting on a 256-byte boundary:
+//   Sc, dSc   fp32 [nchunks][dk][dv] each (the chunk states and their
+//             gradients; bf16 paths use the first half of each);
+//   gC        fp32 [nchunks] (gated rule only: the decay of every chunk);
+//   P, R^T    bf16 [nchunks][dk][dk] and [nchunks][dk][64] (bf16 only).
+size_t delta_backward_workspace_bytes(int bf16, const BackwardArgs& a) {
+  if (a.T == 0) return 0;
+  const size_t nchunks = (size_t)a.B * a.H * ((a.T + kC - 1) / kC);
+  size_t n = 2 * round256(nchunks * a.dk_ * a.dv_ * sizeof(float));
+  if (a.g) n += round256(nchunks * sizeof(float));
+  if (bf16) n += round256(nchunks * a.dk_ * (a.dk_ + kC) * sizeof(bf16_t));
+  return n;
+}
+
+hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, void* workspace, hipStream_t st) {
   if (a.T == 0) {  // no tokens: the state's gradient passes through
     if (!a.dS0) return hipSuccess;
     const size_t n = (size_t)a.B * a.H * a.dk_ * a.dv_;
@@ -1714,23 +1713,22 @@ hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, hipStream_t st
     hipLaunchKernelGGL(zero_state, dim3((unsigned)blocks), dim3(256), 0, st, a.dS0, n);
     return hipGetLastError();
   }
-  // pass 1: the state entering every chunk, from a forward kernel
-  void* ws = nullptr;
-  const size_t wsb = delta_backward_workspace_bytes(bf16, a);
-  hipError_t e = hipMallocAsync(&ws, wsb, st);
-  if (e != hipSuccess) return e;
   const size_t nchunks = (size_t)a.B * a.H * ((a.T + kC - 1) / kC);
-  bf16_t* Pg = bf16 ? reinterpret_cast<bf16_t*>(static_cast<char*>(ws) + wsb) - nchunks * a.dk_ * (a.dk_ + kC) : nullptr;
-  bf16_t* Rg = bf16 ? Pg + nchunks * a.dk_ * a.dk_ : nullptr;
-  const size_t nst = (size_t)a.B * a.H * ((a.T + kC - 1) / kC) * a.dk_ * a.dv_;
-  const size_t nS = (size_t)a.B * a.H * a.dk_ * a.dv_;
+  const size_t nst = nchunks * a.dk_ * a.dv_;
+  char* ws = static_cast<char*>(workspace);
   float* Sc = reinterpret_cast<float*>(ws);
-  float* dSc = Sc + nst;
-  float* s_scratch = dSc + nst;  // pipelined pass 1: the final state lands here
-  bf16_t* o_scratch = reinterpret_cast<bf16_t*>(s_scratch + nS);
-  float* gC = !a.g ? nullptr
-          : pass1_pipelined(bf16, a) ? reinterpret_cast<float*>(o_scratch + (size_t)a.B * a.H * a.T * a.dv_)
-                                     : dSc + nst;
+  ws += round256(nst * sizeof(float));
+  float* dSc = reinterpret_cast<float*>(ws);
+  ws += round256(nst * sizeof(float));
+  float* gC = nullptr;
+  if (a.g) {
+    gC = reinterpret_cast<float*>(ws);
+    ws += round256(nchunks * sizeof(float));
+  }
+  bf16_t* Pg = bf16 ? reinterpret_cast<bf16_t*>(ws) : nullptr;
+  bf16_t* Rg = bf16 ? Pg + nchunks * a.dk_ * a.dk_ : nullptr;
+  // pass 1: the state entering every chunk, from a forward kernel that
+  // writes only those (no output, no final state; S0 is only read)
   PrefillArgs f{};
   f.q = a.q;
   f.k = a.k;
@@ -1744,19 +1742,11 @@ hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, hipStream_t st
   f.dv = a.dv_;
   f.use_init = a.S0 != nullptr;
   f.Sc = Sc;
-  if (a.S0 && pass1_pipelined(bf16, a))
-    e = hipMemcpyAsync(s_scratch, a.S0, nS * sizeof(float), hipMemcpyDeviceToDevice, st);
-  if (e == hipSuccess) {
-    if (pass1_pipelined(bf16, a)) {
-      f.S = s_scratch;
-      f.o = o_scratch;
-      e = a.g ? launch_prefill_pipe_token(f, st) : launch_prefill_pipe(f, nullptr, st);
-    } else if (a.g) {
-      e = launch_prefill_generic(PF_SGATED, bf16, a.dk_, f, st);
-    } else {
-      e = launch_prefill_generic(PF_DELTA, bf16, a.dk_, f, st);
-    }
-  }
+  hipError_t e;
+  if (pass1_pipelined(bf16, a))
+    e = a.g ? launch_prefill_pipe_token(f, st) : launch_prefill_pipe(f, nullptr, st);
+  else
+    e = launch_prefill_generic(a.g ? PF_SGATED : PF_DELTA, bf16, a.dk_, f, st);
   // passes 2 and 3
   if (e == hipSuccess) {
     if (a.g)
@@ -1766,8 +1756,7 @@ hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, hipStream_t st
       e = bf16 ? launch_backward_e<BF16, false>(a, Sc, dSc, Pg, Rg, gC, st)
                : launch_backward_e<F32, false>(a, Sc, dSc, Pg, Rg, gC, st);
   }
-  const hipError_t fr = hipFreeAsync(ws, st);
-  return e != hipSuccess ? e : fr;
+  return e;
 }
 
 }  // namespace linattn

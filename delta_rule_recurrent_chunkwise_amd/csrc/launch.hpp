@@ -44,7 +44,12 @@ struct PrefillArgs {
 // hipErrorInvalidValue for a combination with no kernel.
 hipError_t launch_decode(int kind, int bf16, int dk, int dv, const DecodeArgs& a,
                          hipStream_t st);
-hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, hipStream_t st);
+// Device memory a prefill needs beyond its inputs and outputs (0 for most
+// paths), and the prefill itself with a workspace of at least that many
+// bytes, 256-byte aligned (may be NULL when the size is 0).
+size_t prefill_workspace_bytes(int mode, int bf16, int dk, const PrefillArgs& a);
+hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, void* workspace,
+                          hipStream_t st);
 // The generic prefill kernel only (used by the backward pass with a.Sc set).
 hipError_t launch_prefill_generic(int mode, int bf16, int dk, const PrefillArgs& a, hipStream_t st);
 // Gradient of the ungated delta rule (backward.hip): see deltanet_prefill_backward.
@@ -65,7 +70,8 @@ struct BackwardArgs {
   const void* g;     // one log-decay per token [B,H,T] (gated rule) or NULL
   void* dg;          // its gradient [B,H,T] (with g)
 };
-hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, hipStream_t st);
+size_t delta_backward_workspace_bytes(int bf16, const BackwardArgs& a);
+hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, void* workspace, hipStream_t st);
 // The layer prologue (prologue.hip): see deltanet_prologue.
 struct PrologueArgs {
   const void* q_in;

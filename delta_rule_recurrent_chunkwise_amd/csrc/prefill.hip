@@ -616,7 +616,18 @@ static hipError_t launch_prefill_e(int dk, const PrefillArgs& a, hipStream_t st)
   }
 }
 
-hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, hipStream_t st) {
+// The chunk-parallel linear-attention kernels (bf16) keep per-chunk states in
+// the workspace; the per-channel gated pipelined kernel reads the pre-pass's
+// decay-scaled q and k from it.  Every other path needs none.
+size_t prefill_workspace_bytes(int mode, int bf16, int dk, const PrefillArgs& a) {
+  if (a.T == 0 || !bf16) return 0;
+  if (mode == PF_LA || mode == PF_GLA) return la_par_workspace_bytes(dk, a);
+  if (mode == PF_GATED && dk == 128 && a.dv % 32 == 0) return gated_pipe_workspace_bytes(a);
+  return 0;
+}
+
+hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, void* workspace,
+                          hipStream_t st) {
   if (a.T == 0) {  // no tokens: the state passes through unchanged
     if (a.use_init) return hipSuccess;
     const size_t nbh = (size_t)a.B * a.H;
@@ -628,27 +639,15 @@ hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, hipS
     // Linear attention, chunk-parallel: the chunk-start states come from a
     // prefix over per-chunk phi(K)^T V (gated: decayed); then every chunk's
     // output is formed independently from its own start state.
-    void* ws = nullptr;
-    hipError_t e = hipMallocAsync(&ws, la_par_workspace_bytes(dk, a), st);
-    if (e != hipSuccess) return e;
-    e = launch_la_par_states(dk, a, ws, mode == PF_GLA, st);
-    if (e == hipSuccess) e = launch_la_par_outputs(dk, a, ws, mode == PF_GLA, st);
-    const hipError_t f = hipFreeAsync(ws, st);
-    return e != hipSuccess ? e : f;
+    hipError_t e = launch_la_par_states(dk, a, workspace, mode == PF_GLA, st);
+    if (e == hipSuccess) e = launch_la_par_outputs(dk, a, workspace, mode == PF_GLA, st);
+    return e;
   }
   if (bf16 && dk == 128 && a.dv % 32 == 0) {
     if (mode == PF_DELTA) return launch_prefill_pipe(a, nullptr, st);
     if (mode == PF_SGATED) return launch_prefill_pipe_token(a, st);
-    if (mode == PF_GATED) {
-      // the gate pre-pass writes Gam Q, Gam K, K / Gam and Gam_C to a
-      // stream-ordered workspace that is released after the main kernel
-      void* ws = nullptr;
-      hipError_t e = hipMallocAsync(&ws, gated_pipe_workspace_bytes(a), st);
-      if (e != hipSuccess) return e;
-      e = launch_prefill_pipe(a, ws, st);
-      const hipError_t f = hipFreeAsync(ws, st);
-      return e != hipSuccess ? e : f;
-    }
+    // the gate pre-pass writes Gam Q, Gam K, K / Gam and Gam_C to the workspace
+    if (mode == PF_GATED) return launch_prefill_pipe(a, workspace, st);
   }
   return launch_prefill_generic(mode, bf16, dk, a, st);
 }

@@ -150,6 +150,7 @@ struct PipeArgs {
   int T, dv, use_init;
   int Tq;              // rows per head of q, k, k^: T, or T rounded up to 64 (gated)
   float* Sc;           // if set: the state entering every chunk, bf16, [B*H][nch] x dk x dv in accumulator-tile order
+                       // (CAP kernels write only this: no output, no final state)
 };
 
 // Loads.  Each tile-loader wave owns whole tiles (Q, K, and, gated, K^) and
@@ -182,7 +183,8 @@ struct LoadPlan {
   }
 };
 
-// CAP: also write the state entering every chunk to a.Sc (backward pass).
+// CAP: write the state entering every chunk to a.Sc instead of the output
+// and the final state (backward pass).
 template <int GM, int DVS, bool CAP = false>
 __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
   constexpr bool GATED = GM == 1;  // per key channel, operands from the pre-pass
@@ -528,10 +530,12 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
             for (int i = 0; i < 4; ++i) sm.o[P][16 * mt + 4 * lg + i][col] = f2bf(ox[mt][i]);
         },
         std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    if constexpr (!CAP) {  // the backward pass needs only the chunk states
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+      for (int t = 0; t < 8; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Sh[(size_t)perm32(16 * t + 4 * lg + i) * dv + col] = st[t][i];
+        for (int i = 0; i < 4; ++i) Sh[(size_t)perm32(16 * t + 4 * lg + i) * dv + col] = st[t][i];
+    }
   } else if (wave == 6) {
     // ======================= D wave =======================
     // D_b = (I + L_bb)^-1 of chunk x (phase 1): lane (block lg, column lc)
@@ -710,7 +714,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
     };
     auto ph1 = [&](const int x, auto parity) {};
     auto ph2 = [&](const int x, auto parity) {
-      if (wave == 4 && x >= 1) store_o(x - 1, std::false_type{});
+      if (!CAP && wave == 4 && x >= 1) store_o(x - 1, std::false_type{});
     };
     // plain: Q of chunk x+1 and K of chunk x+2 are stored in phase 2 of x
     // (K(x+1) is read then, for L(x+1)); gated: K and K^ in phase 1, and
@@ -721,7 +725,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
     else if (LP::kThree && wave == 1) run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, LP::kThree ? 1 : 0>{});
     else if (LP::is_tile_wave(wave)) run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
     else run(ph1, ph2, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-    if (wave == 4) store_o(nch - 1, std::true_type{});
+    if (!CAP && wave == 4) store_o(nch - 1, std::true_type{});
   }
 }
 

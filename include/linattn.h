@@ -40,27 +40,30 @@
  *           16 bytes); LA_ERR_ALIGN otherwise.  o must not alias any input.
  *           S (and z) are read and written.  The
  *           library keeps no state between calls; calls are re-entrant.  It
- *           allocates device memory in three cases (four entry points), each a stream-ordered
- *           workspace (hipMallocAsync on `stream`, released with
- *           hipFreeAsync after its kernels):
- *             - the gated deltanet_prefill with bf16 inputs, dk = 128 and
- *               dv % 32 == 0: 384 B*H*C*dk + 4 B*H*C*dk bytes for the
- *               decay-scaled q and k, where C = ceil(T/64) is the number
- *               of 64-token chunks;
- *             - la_prefill and gla_prefill with bf16 inputs:
- *               6 B*H*C*dk*dv + 4 B*H*C*dk bytes for the per-chunk state
- *               increments (fp32), the state entering each chunk (bf16) and
- *               the normaliser entering each chunk, or the chunk's decay
- *               (fp32);
- *             - deltanet_prefill_backward: 8 B*H*C*dk*dv bytes for the
- *               state entering and the gradient leaving every chunk; with
- *               bf16 inputs also 2 B*H*C*dk*(dk+64) bytes for every chunk's
- *               P = W^T K and R^T = (Q - A W)^T (see that function), and,
- *               when dk = 128 and dv % 32 == 0, 4 B*H*dk*dv + 2 B*H*T*dv
- *               bytes that receive the forward pass's final state and
- *               output; gated_deltanet_prefill_backward as well, plus
- *               4 B*H*C bytes (a decay per chunk).
- *           A failed allocation returns LA_ERR_LAUNCH.
+ *           never allocates device memory: the five entry points that need
+ *           scratch memory on some paths (la_prefill, gla_prefill and
+ *           deltanet_prefill, and the two backward entry points) take a
+ *           caller-owned workspace pointer and its size in bytes, and each
+ *           has a *_workspace_bytes() query with the same sizes and dtype.
+ *           The query returns 0 where no workspace is needed (the workspace
+ *           may then be NULL), and 0 for arguments the call would reject.
+ *           A workspace must be at least the queried size (LA_ERR_WORKSPACE
+ *           otherwise) and 256-byte aligned (LA_ERR_ALIGN); its contents on
+ *           entry do not matter, and it must not be used by other work
+ *           until the call's kernels have finished on `stream`.  The sizes
+ *           (C = ceil(T/64) chunks, bf16 inputs unless stated):
+ *             - la_prefill, gla_prefill: 6 B*H*C*dk*dv + 4 B*H*C*dk (the
+ *               per-chunk state increments in fp32, the state entering
+ *               each chunk in bf16, the normaliser entering each chunk or
+ *               the chunk's decay); 0 for float32;
+ *             - deltanet_prefill with a per-channel gate, dk = 128 and
+ *               dv % 32 == 0: 384 B*H*C*dk + 4 B*H*C*dk (decay-scaled
+ *               copies of q and k); 0 otherwise;
+ *             - deltanet_prefill_backward: 8 B*H*C*dk*dv (the state
+ *               entering and the gradient leaving every chunk), plus
+ *               2 B*H*C*dk*(dk+64) with bf16 inputs (every chunk's P and
+ *               R^T); the gated backward adds 4 B*H*C; each region is
+ *               rounded up to 256 bytes.
  * Sizes.    B, H (or N, H) >= 1; T >= 0 for prefill, any length (the last
  *           64-token chunk may be partial).  T = 0 enqueues no work when
  *           use_initial_state is set and otherwise zero-fills S (and z);
@@ -70,12 +73,16 @@
  * Stream.   stream is a hipStream_t passed as void*; NULL is the null stream.
  *           Work is enqueued asynchronously; nothing synchronises the host.
  * Errors.   0 (LA_OK) or a negative code.  Arguments are validated before
- *           any HIP call, so a bad call has no effect on the device.  A
+ *           any HIP call, so a bad call has no effect on the device; the
+ *           order is pointers, dtype, shape, head dimensions, alignment,
+ *           workspace.  A
  *           kernel-launch failure returns LA_ERR_LAUNCH.  Numerical problems
  *           (NaN/Inf inputs) are not errors: they propagate to the outputs.
  */
 #ifndef LINATTN_H
 #define LINATTN_H
+
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -88,7 +95,10 @@ extern "C" {
 #define LA_ERR_UNSUPPORTED_DIM (-4) /* dk or dv not in {16, 32, 64, 128}     */
 #define LA_ERR_LAUNCH (-5)          /* the HIP runtime rejected a launch     */
 #define LA_ERR_ALIGN (-6)           /* a vector-accessed pointer is not      */
-                                    /* 16-byte aligned                       */
+                                    /* 16-byte aligned, or a workspace not   */
+                                    /* 256-byte aligned                      */
+#define LA_ERR_WORKSPACE (-7)       /* the workspace is NULL or smaller than */
+                                    /* its *_workspace_bytes() query         */
 
 #define LA_DTYPE_F32 0
 #define LA_DTYPE_BF16 1
@@ -107,10 +117,15 @@ extern "C" {
  * S [B,H,dk,dv], z [B,H,dk] in/out:   float32.  use_initial_state = 0: the
  *   incoming contents are ignored and the state starts at zero; otherwise
  *   they are the initial state.  On completion they hold the final state.
+ * workspace: la_prefill_workspace_bytes(B, H, T, dk, dv, dtype) bytes (see
+ *   "Pointers"); NULL when that is 0.
  */
+size_t la_prefill_workspace_bytes(int B, int H, int T, int dk, int dv,
+                                  int dtype);
 int la_prefill(const void *q, const void *k, const void *v, void *o, float *S,
                float *z, int use_initial_state, int B, int H, int T, int dk,
-               int dv, int dtype, void *stream);
+               int dv, int dtype, void *workspace, size_t workspace_bytes,
+               void *stream);
 
 /*
  * la_decode_step -- one new token per sequence, state updated in place.
@@ -142,11 +157,16 @@ int la_decode_step(const void *q, const void *k, const void *v, void *o,
  * q and k are used as given: no feature map, normalisation or scale.
  * q, k [B,H,T,dk], v [B,H,T,dv], beta [B,H,T], g [B,H,T,dk] or NULL (dtype).
  * o [B,H,T,dv] out (dtype).  S [B,H,dk,dv] float32 in/out as in la_prefill.
+ * workspace: deltanet_prefill_workspace_bytes(g != NULL, B, H, T, dk, dv,
+ *   dtype) bytes; NULL when that is 0 (always so without a gate).
  */
+size_t deltanet_prefill_workspace_bytes(int gated, int B, int H, int T,
+                                        int dk, int dv, int dtype);
 int deltanet_prefill(const void *q, const void *k, const void *v,
                      const void *beta, const void *g, void *o, float *S,
                      int use_initial_state, int B, int H, int T, int dk,
-                     int dv, int dtype, void *stream);
+                     int dv, int dtype, void *workspace,
+                     size_t workspace_bytes, void *stream);
 
 /*
  * deltanet_decode_step -- one new token per sequence, state updated in
@@ -198,10 +218,14 @@ int gated_deltanet_decode_step(const void *q, const void *k, const void *v,
  * chunk start and Gam = exp(G).
  * q, k [B,H,T,dk], v [B,H,T,dv], g [B,H,T] = log a or NULL (no decay), in
  * dtype; o [B,H,T,dv] out; S [B,H,dk,dv] float32 in/out as in la_prefill.
+ * workspace: gla_prefill_workspace_bytes(B, H, T, dk, dv, dtype) bytes.
  */
+size_t gla_prefill_workspace_bytes(int B, int H, int T, int dk, int dv,
+                                   int dtype);
 int gla_prefill(const void *q, const void *k, const void *v, const void *g,
                 void *o, float *S, int use_initial_state, int B, int H, int T,
-                int dk, int dv, int dtype, void *stream);
+                int dk, int dv, int dtype, void *workspace,
+                size_t workspace_bytes, void *stream);
 
 /*
  * gla_decode_step -- one token of gla_prefill, state updated in place:
@@ -229,17 +253,20 @@ int gla_decode_step(const void *q, const void *k, const void *v, const void *g,
  * With W = T diag(beta) K the last one is dS = dSn - P dSn + R^T dO,
  * P = W^T K, R = Q - A W; for bf16 inputs P and R are formed for all chunks
  * at once and the walk over chunks is that one product per chunk.
- * It recomputes the forward chunk states into a stream-ordered workspace
- * (sizes under "Pointers" above; C = ceil(T/64)); a failed allocation
- * returns LA_ERR_LAUNCH.  Sizes: dk, dv in {16, 32, 64, 128} for bf16, up to 64 for
- * float32.  T = 0 copies dST to dS0 (or zero-fills it).
+ * It recomputes the forward chunk states into the workspace of
+ * deltanet_prefill_backward_workspace_bytes(B, H, T, dk, dv, dtype) bytes
+ * (sizes under "Pointers" above).  Sizes: dk, dv in {16, 32, 64, 128} for
+ * bf16, up to 64 for float32.  T = 0 copies dST to dS0 (or zero-fills it).
  */
+size_t deltanet_prefill_backward_workspace_bytes(int B, int H, int T, int dk,
+                                                 int dv, int dtype);
 int deltanet_prefill_backward(const void *q, const void *k, const void *v,
                               const void *beta, const float *S0,
                               const void *dO, const float *dST, void *dq,
                               void *dk_out, void *dv_out, void *dbeta,
                               float *dS0, int B, int H, int T, int dk, int dv,
-                              int dtype, void *stream);
+                              int dtype, void *workspace,
+                              size_t workspace_bytes, void *stream);
 
 /*
  * gated_deltanet_prefill_backward -- gradients of gated_deltanet_prefill (one
@@ -257,9 +284,12 @@ int deltanet_prefill_backward(const void *q, const void *k, const void *v,
  * appears (K S and Q S, the ratios in A and L, the state leaving the
  * chunk); each term carries its own decay, so dg keeps its relative
  * accuracy when the decays are strong.
- * The workspace is that of deltanet_prefill_backward plus one float per
- * chunk.
+ * The workspace, of gated_deltanet_prefill_backward_workspace_bytes(...)
+ * bytes, is that of deltanet_prefill_backward plus one float per chunk.
  */
+size_t gated_deltanet_prefill_backward_workspace_bytes(int B, int H, int T,
+                                                       int dk, int dv,
+                                                       int dtype);
 int gated_deltanet_prefill_backward(const void *q, const void *k,
                                     const void *v, const void *beta,
                                     const void *g, const float *S0,
@@ -267,6 +297,7 @@ int gated_deltanet_prefill_backward(const void *q, const void *k,
                                     void *dq, void *dk_out, void *dv_out,
                                     void *dbeta, void *dg, float *dS0, int B,
                                     int H, int T, int dk, int dv, int dtype,
+                                    void *workspace, size_t workspace_bytes,
                                     void *stream);
 
 /*

@@ -1,5 +1,8 @@
 """Shared helpers for the GPU parity tests: tolerances and the comparison
 metric max|gpu - ref| / max|ref| (over the whole compared tensor)."""
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -32,7 +35,20 @@ def rel_err(gpu, ref) -> float:
     return float(np.max(diff)) / scale
 
 
+def _log_margin(what, err, tol):
+    """Append the achieved error to the JSON-lines file named by the
+    environment variable LINATTN_PARITY_LOG (if set), so a run records its
+    margins under the tolerance, not just pass/fail."""
+    path = os.environ.get("LINATTN_PARITY_LOG")
+    if not path:
+        return
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    with open(path, "a") as f:
+        f.write(json.dumps({"test": test, "what": what, "rel_err": err, "tol": tol}) + "\n")
+
+
 def assert_close(gpu, ref, tol, what):
     err = rel_err(gpu, ref)
     print(f"  {what}: rel err {err:.3e} (tol {tol:.0e})", flush=True)
+    _log_margin(what, err, tol)
     assert err <= tol, f"{what}: max|gpu-ref|/max|ref| = {err:.3e} > {tol:.1e}"

@@ -13,10 +13,11 @@ import delta_rule_recurrent_chunkwise_amd as la
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "linattn.h")
 
-OK, NULL, SHAPE, DTYPE, DIM, LAUNCH, ALIGN = 0, -1, -2, -3, -4, -5, -6
+OK, NULL, SHAPE, DTYPE, DIM, LAUNCH, ALIGN, WORKSPACE = 0, -1, -2, -3, -4, -5, -6, -7
 P = ctypes.c_void_p
-FAKE = P(0x1000)          # 16-byte aligned, never dereferenced
+FAKE = P(0x1000)          # 256-byte aligned, never dereferenced
 MISALIGNED = P(0x1002)
+BIG = 1 << 40             # a workspace size no call here needs more than
 
 
 def _declared_functions():
@@ -43,20 +44,20 @@ def test_error_codes_match_header():
     assert codes["LA_OK"] == OK and codes["LA_ERR_NULL"] == NULL
     assert codes["LA_ERR_SHAPE"] == SHAPE and codes["LA_ERR_DTYPE"] == DTYPE
     assert codes["LA_ERR_UNSUPPORTED_DIM"] == DIM and codes["LA_ERR_LAUNCH"] == LAUNCH
-    assert codes["LA_ERR_ALIGN"] == ALIGN
+    assert codes["LA_ERR_ALIGN"] == ALIGN and codes["LA_ERR_WORKSPACE"] == WORKSPACE
     assert codes["LA_DTYPE_F32"] == 0 and codes["LA_DTYPE_BF16"] == 1
 
 
 def test_strerror_is_static_text_for_every_code():
-    for code in (OK, NULL, SHAPE, DTYPE, DIM, LAUNCH, ALIGN, -99, 7):
+    for code in (OK, NULL, SHAPE, DTYPE, DIM, LAUNCH, ALIGN, WORKSPACE, -99, 7):
         msg = la.la_strerror(code)
         assert isinstance(msg, str) and msg
     assert la.la_strerror(-99) == "unknown error code"
 
 
 def _la_prefill(q=FAKE, k=FAKE, v=FAKE, o=FAKE, S=FAKE, z=FAKE, init=0, B=1, H=1, T=64,
-                dk=64, dv=64, dt=1):
-    return la.library().la_prefill(q, k, v, o, S, z, init, B, H, T, dk, dv, dt, None)
+                dk=64, dv=64, dt=1, ws=FAKE, wsn=BIG):
+    return la.library().la_prefill(q, k, v, o, S, z, init, B, H, T, dk, dv, dt, ws, wsn, None)
 
 
 def _la_decode(q=FAKE, k=FAKE, v=FAKE, o=FAKE, S=FAKE, z=FAKE, N=1, H=1, dk=64, dv=64, dt=1):
@@ -64,9 +65,9 @@ def _la_decode(q=FAKE, k=FAKE, v=FAKE, o=FAKE, S=FAKE, z=FAKE, N=1, H=1, dk=64, 
 
 
 def _dn_prefill(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=None, o=FAKE, S=FAKE, init=0, B=1, H=1,
-                T=64, dk=64, dv=64, dt=1):
+                T=64, dk=64, dv=64, dt=1, ws=FAKE, wsn=BIG):
     return la.library().deltanet_prefill(q, k, v, beta, g, o, S, init, B, H, T, dk, dv, dt,
-                                         None)
+                                         ws, wsn, None)
 
 
 def _dn_decode(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=None, o=FAKE, S=FAKE, N=1, H=1, dk=64,
@@ -87,8 +88,8 @@ def _gdn_decode(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, o=FAKE, S=FAKE, N=1, 
 
 
 def _gla_prefill(q=FAKE, k=FAKE, v=FAKE, g=FAKE, o=FAKE, S=FAKE, init=0, B=1, H=1, T=64,
-                 dk=64, dv=64, dt=1):
-    return la.library().gla_prefill(q, k, v, g, o, S, init, B, H, T, dk, dv, dt, None)
+                 dk=64, dv=64, dt=1, ws=FAKE, wsn=BIG):
+    return la.library().gla_prefill(q, k, v, g, o, S, init, B, H, T, dk, dv, dt, ws, wsn, None)
 
 
 def _gla_decode(q=FAKE, k=FAKE, v=FAKE, g=FAKE, o=FAKE, S=FAKE, N=1, H=1, dk=64, dv=64, dt=1):
@@ -127,9 +128,9 @@ def test_scalar_gated_entry_points_validate_like_the_others():
 
 
 def _bwd(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, S0=None, dO=FAKE, dST=None, dq=FAKE, dk_=FAKE,
-         dv_=FAKE, db=FAKE, dS0=None, B=1, H=1, T=64, dk=64, dv=64, dt=1):
+         dv_=FAKE, db=FAKE, dS0=None, B=1, H=1, T=64, dk=64, dv=64, dt=1, ws=FAKE, wsn=BIG):
     return la.library().deltanet_prefill_backward(q, k, v, beta, S0, dO, dST, dq, dk_, dv_, db,
-                                                  dS0, B, H, T, dk, dv, dt, None)
+                                                  dS0, B, H, T, dk, dv, dt, ws, wsn, None)
 
 
 def _pro(qi=FAKE, ki=FAKE, bl=None, qo=FAKE, ko=FAKE, bo=None, B=1, H=2, T=64, dk=64, bh=1,
@@ -157,10 +158,11 @@ def test_backward_validation():
 
 
 def _gbwd(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, S0=None, dO=FAKE, dST=None, dq=FAKE,
-          dk_=FAKE, dv_=FAKE, db=FAKE, dg=FAKE, dS0=None, B=1, H=1, T=64, dk=64, dv=64, dt=1):
+          dk_=FAKE, dv_=FAKE, db=FAKE, dg=FAKE, dS0=None, B=1, H=1, T=64, dk=64, dv=64, dt=1,
+          ws=FAKE, wsn=BIG):
     return la.library().gated_deltanet_prefill_backward(q, k, v, beta, g, S0, dO, dST, dq, dk_,
                                                         dv_, db, dg, dS0, B, H, T, dk, dv, dt,
-                                                        None)
+                                                        ws, wsn, None)
 
 
 @pytest.mark.parametrize("missing", ["q", "k", "v", "beta", "g", "dO", "dq", "dk_", "dv_", "db",
@@ -286,3 +288,89 @@ def test_peak_probe_library_loads_and_rejects_bad_arguments():
     assert lib.peak_probe_stream(FAKE, None, 1 << 15, 0, None) == -1      # copy needs dst
     assert lib.peak_probe_stream(FAKE, FAKE, (1 << 15) + 16, 0, None) == -1  # not whole tiles
     assert lib.peak_probe_stream(MISALIGNED, FAKE, 1 << 15, 1, None) == -1
+
+
+# ---------------------------------------------------------------------------
+# Workspaces: the library allocates nothing; the entry points that need scratch
+# memory take it from the caller and check it before any HIP call.
+# ---------------------------------------------------------------------------
+def _nch(T):
+    return (T + 63) // 64
+
+
+def test_workspace_queries_match_the_documented_sizes():
+    B, H, T = 2, 3, 130
+    C = _nch(T)
+    for dk, dv in ((16, 32), (64, 64), (128, 128)):
+        la_ws = 6 * B * H * C * dk * dv + 4 * B * H * C * dk
+        assert la.la_prefill_workspace_bytes(B, H, T, dk, dv, 1) == la_ws
+        assert la.gla_prefill_workspace_bytes(B, H, T, dk, dv, 1) == la_ws
+        assert la.la_prefill_workspace_bytes(B, H, T, dk, dv, 0) == 0    # float32: one kernel
+        assert la.deltanet_prefill_workspace_bytes(0, B, H, T, dk, dv, 1) == 0
+        assert la.deltanet_prefill_workspace_bytes(1, B, H, T, dk, dv, 0) == 0
+        gated = 384 * B * H * C * dk + 4 * B * H * C * dk if dk == 128 and dv % 32 == 0 else 0
+        assert la.deltanet_prefill_workspace_bytes(1, B, H, T, dk, dv, 1) == gated
+
+        def r(n):
+            return (n + 255) // 256 * 256
+        nst = B * H * C * dk * dv
+        bwd = 2 * r(4 * nst) + r(2 * B * H * C * dk * (dk + 64))
+        assert la.deltanet_prefill_backward_workspace_bytes(B, H, T, dk, dv, 1) == bwd
+        assert la.gated_deltanet_prefill_backward_workspace_bytes(B, H, T, dk, dv, 1) == \
+            bwd + r(4 * B * H * C)
+    assert la.deltanet_prefill_backward_workspace_bytes(B, H, T, 64, 64, 0) == 2 * 4 * B * H * C * 64 * 64
+
+
+def test_workspace_queries_are_zero_when_nothing_runs_or_the_call_is_invalid():
+    for q in (la.la_prefill_workspace_bytes, la.gla_prefill_workspace_bytes,
+              la.deltanet_prefill_backward_workspace_bytes,
+              la.gated_deltanet_prefill_backward_workspace_bytes):
+        assert q(1, 1, 0, 64, 64, 1) == 0          # T = 0
+        assert q(0, 1, 64, 64, 64, 1) == 0         # bad shape
+        assert q(1, 1, 64, 96, 64, 1) == 0         # bad dim
+        assert q(1, 1, 64, 64, 64, 5) == 0         # bad dtype
+    assert la.deltanet_prefill_backward_workspace_bytes(1, 1, 64, 128, 64, 0) == 0  # fp32 dk 128
+
+
+def test_missing_or_small_workspace_is_rejected_before_any_hip_call():
+    need = la.la_prefill_workspace_bytes(1, 1, 64, 64, 64, 1)
+    assert need > 0
+    assert _la_prefill(ws=None, wsn=0) == WORKSPACE
+    assert _la_prefill(ws=None, wsn=BIG) == WORKSPACE
+    assert _la_prefill(wsn=need - 1) == WORKSPACE
+    assert _la_prefill(ws=P(0x1010), wsn=BIG) == ALIGN          # 16- but not 256-byte aligned
+    assert _gla_prefill(ws=None, wsn=0) == WORKSPACE
+    assert _gla_prefill(wsn=la.gla_prefill_workspace_bytes(1, 1, 64, 64, 64, 1) - 1) == WORKSPACE
+    assert _dn_prefill(g=FAKE, dk=128, dv=128, ws=None, wsn=0) == WORKSPACE
+    assert _dn_prefill(g=FAKE, dk=128, dv=128,
+                       wsn=la.deltanet_prefill_workspace_bytes(1, 1, 1, 64, 128, 128, 1) - 1) == WORKSPACE
+    assert _bwd(ws=None, wsn=0) == WORKSPACE
+    assert _bwd(wsn=la.deltanet_prefill_backward_workspace_bytes(1, 1, 64, 64, 64, 1) - 1) == WORKSPACE
+    assert _gbwd(ws=None, wsn=0) == WORKSPACE
+    assert _gbwd(wsn=la.gated_deltanet_prefill_backward_workspace_bytes(1, 1, 64, 64, 64, 1) - 1) \
+        == WORKSPACE
+    # earlier checks win: a bad call is reported as such even without a workspace
+    assert _la_prefill(dt=7, ws=None, wsn=0) == DTYPE
+    assert _la_prefill(q=None, ws=None, wsn=0) == NULL
+    assert _la_prefill(q=MISALIGNED, ws=None, wsn=0) == ALIGN
+
+
+def test_paths_without_a_workspace_accept_none():
+    """No workspace is needed (or read) where the query returns 0: the
+    ungated delta rule and float32 linear attention reach their launch, which
+    cannot happen here, so only T = 0 (no HIP call) is run through."""
+    none = dict(q=None, k=None, v=None, o=None)
+    assert _la_prefill(T=0, init=1, ws=None, wsn=0, **none) == OK
+    assert _dn_prefill(T=0, init=1, beta=None, ws=None, wsn=0, **none) == OK
+    assert _gla_prefill(T=0, init=1, g=None, ws=None, wsn=0, **none) == OK
+
+
+def test_no_allocation_calls_in_the_library_sources():
+    """The library allocates no device memory: no hipMalloc / hipFree of any
+    kind appears in its sources."""
+    csrc = os.path.join(ROOT, "delta_rule_recurrent_chunkwise_amd", "csrc")
+    for name in os.listdir(csrc):
+        if name.endswith((".hip", ".hpp")) and name != "peak_probe.hip":
+            text = open(os.path.join(csrc, name)).read()
+            assert not re.search(r"hip(Malloc|Free|ExtMalloc|HostMalloc)", text), name
+

@@ -1,6 +1,8 @@
 """The five workloads at full size, in the launch configuration bench.py
-times, against the float64 oracle.  Where the oracle over the whole workload
-would take minutes, outputs are compared on sampled heads, which the oracle
+times, against the float64 oracle: full tensors for the prefills; for the
+decode workload the full state after step 1 and sampled (sequence, head)
+pairs after all 1010 steps.  The backward rows, whose oracle is a slower
+reverse recurrence, are compared on sampled heads, which the oracle
 recomputes independently (heads never interact)."""
 import numpy as np
 import pytest
@@ -48,7 +50,9 @@ def test_deltanet_workload_full():
     assert_close(S, S_ref, TOL[w.dtype], "S")
 
 
-def test_gated_workload_sampled_heads():
+def test_gated_workload_full():
+    """The per-key-channel gated workload (B=1 H=32 T=32768 d=128 bf16) on
+    every head: o and the final state against the oracle's full recurrence."""
     dev = require_gpu()
     w = W[3]
     print(f"workload {w.name}", flush=True)
@@ -56,11 +60,10 @@ def test_gated_workload_sampled_heads():
     d = _to(inp, dev)
     o, S = la.deltanet_prefill(d["q"], d["k"], d["v"], d["beta"], g=d["g"])
     torch.cuda.synchronize()
-    heads = [0, 5, 11, 18, 24, 31]
-    sub = {n: inp[n][:, heads].contiguous() for n in ("q", "k", "v", "beta", "g")}
-    o_ref, S_ref = oracle.delta_recurrent(sub["q"], sub["k"], sub["v"], sub["beta"], sub["g"])
-    assert_close(o[:, heads], o_ref, TOL[w.dtype], "o (sampled heads)")
-    assert_close(S[:, heads], S_ref, TOL[w.dtype], "S (sampled heads)")
+    del d
+    o_ref, S_ref = oracle.delta_recurrent(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"])
+    assert_close(o, o_ref, TOL[w.dtype], "o (all heads)")
+    assert_close(S, S_ref, TOL[w.dtype], "S (all heads)")
 
 
 def test_decode_workload():
@@ -104,9 +107,9 @@ def test_decode_workload():
     assert_close(o[n_idx, h_idx], o_ref[0, :, -1], TOL[w.dtype], "o of step 1010 (sampled)")
 
 
-def test_token_gate_at_the_gated_workload_shape_sampled_heads():
+def test_token_gate_at_the_gated_workload_shape_full():
     """gated_deltanet_prefill (one decay per token) at B=1 H=32 T=32768
-    d=128 bf16, the shape and launch its bench row times, on sampled heads."""
+    d=128 bf16, the shape and launch its bench row times, on every head."""
     dev = require_gpu()
     w = W[3]
     print("gated_deltanet_prefill at the gated workload's shape", flush=True)
@@ -114,11 +117,10 @@ def test_token_gate_at_the_gated_workload_shape_sampled_heads():
     d = _to(inp, dev)
     o, S = la.gated_deltanet_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"])
     torch.cuda.synchronize()
-    heads = [3, 17, 30]
-    sub = {n: inp[n][:, heads].contiguous() for n in ("q", "k", "v", "beta", "g")}
-    o_ref, S_ref = oracle.delta_recurrent(sub["q"], sub["k"], sub["v"], sub["beta"], sub["g"])
-    assert_close(o[:, heads], o_ref, TOL[w.dtype], "o (sampled heads)")
-    assert_close(S[:, heads], S_ref, TOL[w.dtype], "S (sampled heads)")
+    del d
+    o_ref, S_ref = oracle.delta_recurrent(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"])
+    assert_close(o, o_ref, TOL[w.dtype], "o (all heads)")
+    assert_close(S, S_ref, TOL[w.dtype], "S (all heads)")
 
 
 def test_gla_at_the_la_workload_shape():
@@ -151,4 +153,28 @@ def test_backward_at_the_deltanet_workload_shape_sampled_heads():
     ref = oracle.delta_backward(sub["q"], sub["k"], sub["v"], sub["beta"],
                                 dO[bi:bi + 1, heads].contiguous())
     for name, g, r in zip(("dq", "dk", "dv", "dbeta"), grads, ref):
+        assert_close(g[bi:bi + 1, heads], r, TOL[w.dtype], f"{name} (sampled heads)")
+
+
+def test_gated_backward_at_the_deltanet_workload_shape_sampled_heads():
+    """gated_deltanet_prefill_backward (one decay per token) at B=4 H=16
+    T=4096 d=128 bf16, the shape and launch its bench row times (pass 1 is
+    the pipelined per-token kernel with state capture over 64 chunks); the
+    oracle's gated reverse recurrence on two sampled heads, dg included."""
+    dev = require_gpu()
+    w = W[2]
+    print("gated_deltanet_prefill_backward at the delta-rule workload's shape", flush=True)
+    inp = workloads.make_delta(w.B, w.H, w.T, w.dk, w.dv, w.dtype, seed=97, gated="token")
+    gen = workloads.generator(98)
+    dO = torch.randn(w.B, w.H, w.T, w.dv, generator=gen).to(w.dtype)
+    d = _to(inp, dev)
+    grads = la.gated_deltanet_prefill_backward(d["q"], d["k"], d["v"], d["beta"], d["g"], dO.to(dev))
+    torch.cuda.synchronize()
+    bi, heads = 2, [5, 14]
+    sub = {n: inp[n][bi:bi + 1, heads].contiguous() for n in ("q", "k", "v", "beta", "g")}
+    ref = oracle.delta_backward(sub["q"], sub["k"], sub["v"], sub["beta"],
+                                dO[bi:bi + 1, heads].contiguous(), g=sub["g"])
+    names = ("dq", "dk", "dv", "dbeta", "dg")
+    ref = (ref[0], ref[1], ref[2], ref[3], ref[5])   # the oracle returns dS0 before dg
+    for name, g, r in zip(names, grads[:5], ref):
         assert_close(g[bi:bi + 1, heads], r, TOL[w.dtype], f"{name} (sampled heads)")
