@@ -23,7 +23,7 @@ __all__ = [
     "deltanet_prologue", "la_strerror",
     "la_prefill_workspace_bytes", "deltanet_prefill_workspace_bytes",
     "gla_prefill_workspace_bytes", "deltanet_prefill_backward_workspace_bytes",
-    "gated_deltanet_prefill_backward_workspace_bytes",
+    "gated_deltanet_prefill_backward_workspace_bytes", "la_prefill_noalloc",
     "library", "LIB_PATH",
     "EXPORTED_SYMBOLS",
     "LinAttnError",
@@ -39,8 +39,10 @@ EXPORTED_SYMBOLS = ("la_prefill", "la_decode_step", "deltanet_prefill",
                     "gla_prefill_workspace_bytes",
                     "deltanet_prefill_backward_workspace_bytes",
                     "gated_deltanet_prefill_backward_workspace_bytes",
+                    "la_prefill_noalloc",
                     "la_strerror")
 WORKSPACE_QUERIES = EXPORTED_SYMBOLS[11:16]
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 LA_DTYPE_F32, LA_DTYPE_BF16 = 0, 1
 _DTYPES = {torch.float32: LA_DTYPE_F32, torch.bfloat16: LA_DTYPE_BF16}
@@ -86,6 +88,8 @@ def library():
         lib.gated_deltanet_prefill_backward_workspace_bytes.argtypes = [I] * 6
         for fn in WORKSPACE_QUERIES:
             getattr(lib, fn).restype = Z
+        lib.la_prefill_noalloc.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+        lib.la_prefill_noalloc.restype = I
         lib.la_strerror.argtypes = [I]
         lib.la_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -225,6 +229,28 @@ def la_prefill(q, k, v, S=None, z=None, use_initial_state=False, o=None, stream=
                               int(bool(use_initial_state)), B, H, T, dk, dv,
                               _DTYPES[dtype], wp, wn, _stream(dev, stream))
     _check("la_prefill", rc)
+    return o, S, z
+
+
+def la_prefill_noalloc(q, k, v, o, S, z, use_initial_state=False, stream=None):
+    """la_prefill for callers that cannot allocate: o [B,H,T,dv], S [B,H,dk,dv]
+    and z [B,H,dk] (fp32) must be given, and nothing is allocated here or in
+    the library (its scratch is a fixed 64 MiB array per GPU).  Raises
+    LinAttnError (LA_ERR_SCRATCH_LIMIT) if the sizes need more scratch than
+    that.  Calls that may overlap on one GPU must not be made."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev, dtype = _inputs("la_prefill_noalloc", dict(q=q, k=k, v=v, o=o),
+                         dict(q=(B, H, T, dk), k=(B, H, T, dk), v=(B, H, T, dv),
+                              o=(B, H, T, dv)))
+    if S is None or z is None:
+        raise ValueError("la_prefill_noalloc: S and z must be given")
+    _state("la_prefill_noalloc", "S", S, (B, H, dk, dv), dev)
+    _state("la_prefill_noalloc", "z", z, (B, H, dk), dev)
+    rc = library().la_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(S), _ptr(z),
+                                      int(bool(use_initial_state)), B, H, T, dk, dv,
+                                      _DTYPES[dtype], _stream(dev, stream))
+    _check("la_prefill_noalloc", rc)
     return o, S, z
 
 

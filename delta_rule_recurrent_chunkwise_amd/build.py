@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "liblinattn.so")
-SOURCES = ["api.hip", "decode.hip", "prefill.hip", "prefill_pipe.hip", "la_par.hip", "backward.hip", "prologue.hip"]
+SOURCES = ["api.hip", "decode.hip", "prefill.hip", "prefill_pipe.hip", "la_par.hip", "backward.hip", "prologue.hip",
+           "noalloc.hip"]
 # the measurement harness's MFMA peak probe, a library of its own
 PROBE_PATH = os.path.join(HERE, "libpeak_probe.so")
 PROBE_SOURCE = "peak_probe.hip"

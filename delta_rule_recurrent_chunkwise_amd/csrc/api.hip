@@ -91,6 +91,9 @@ const char* la_strerror(int code) {
     case LA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     case LA_ERR_WORKSPACE:
       return "the workspace is NULL or smaller than the matching *_workspace_bytes() query returns";
+    case LA_ERR_SCRATCH_LIMIT:
+      return "la_prefill_noalloc: the call needs more scratch memory than the library's fixed "
+             "LA_NOALLOC_SCRATCH_BYTES (64 MiB) array holds; use la_prefill with a workspace";
     case LA_ERR_ALIGN:
       return "q, k, v and o (prefill; and dO, dq, dk, dv, backward; q and k in and out, prologue) "
              "and S (decode) must be 16-byte aligned, and a workspace 256-byte aligned";

@@ -99,6 +99,8 @@ extern "C" {
                                     /* 256-byte aligned                      */
 #define LA_ERR_WORKSPACE (-7)       /* the workspace is NULL or smaller than */
                                     /* its *_workspace_bytes() query         */
+#define LA_ERR_SCRATCH_LIMIT (-8)   /* la_prefill_noalloc: the call needs    */
+                                    /* more than its fixed scratch holds     */
 
 #define LA_DTYPE_F32 0
 #define LA_DTYPE_BF16 1
@@ -319,6 +321,30 @@ int deltanet_prologue(const void *q_in, const void *k_in,
                       void *beta_out, int B, int H, int T, int dk,
                       int beta_heads, int apply_silu, float q_scale, int dtype,
                       void *stream);
+
+/*
+ * la_prefill_noalloc -- la_prefill for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that
+ * forbid allocation): the same computation, arguments (minus the workspace)
+ * and errors, with the scratch memory that la_prefill takes as its
+ * workspace held instead in a fixed array in the library's device memory.
+ * Every GPU the library runs on holds its own array of
+ * LA_NOALLOC_SCRATCH_BYTES (64 MiB) until the process ends; its address is
+ * looked up on the first call on each device (the current device).  Nothing
+ * is allocated, by the library or by this call.
+ * Limit: la_prefill_workspace_bytes(B, H, T, dk, dv, dtype) must not exceed
+ * LA_NOALLOC_SCRATCH_BYTES, else LA_ERR_SCRATCH_LIMIT (checked before any
+ * HIP call).  With bf16 inputs that is 6 B*H*C*dk*dv + 4 B*H*C*dk bytes for
+ * C = ceil(T/64) chunks (38 MB at B=8, H=12, T=1024, dk = dv = 64); float32
+ * inputs need none.
+ * Calls on one GPU share its array, so calls that can overlap on one GPU
+ * (streams without ordering between them) race and must not be made; calls
+ * ordered on one stream are safe.  No state is carried between calls.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int la_prefill_noalloc(const void *q, const void *k, const void *v, void *o,
+                       float *S, float *z, int use_initial_state, int B,
+                       int H, int T, int dk, int dv, int dtype, void *stream);
 
 /* la_strerror -- a static, NUL-terminated description of an error code. */
 const char *la_strerror(int code);

@@ -374,3 +374,17 @@ def test_no_allocation_calls_in_the_library_sources():
             text = open(os.path.join(csrc, name)).read()
             assert not re.search(r"hip(Malloc|Free|ExtMalloc|HostMalloc)", text), name
 
+
+def test_noalloc_checks_its_limit_before_any_hip_call():
+    """la_prefill_noalloc validates like la_prefill and rejects sizes beyond
+    its fixed scratch with LA_ERR_SCRATCH_LIMIT, all before any HIP call."""
+    lib = la.library()
+
+    def call(q=FAKE, o=FAKE, S=FAKE, z=FAKE, B=1, H=1, T=64, dk=64, dv=64, dt=1):
+        return lib.la_prefill_noalloc(q, FAKE, FAKE, o, S, z, 0, B, H, T, dk, dv, dt, None)
+    assert _codes()["LA_ERR_SCRATCH_LIMIT"] == -8
+    assert call(B=8, H=12, T=4096) == -8          # 152 MB > 64 MiB
+    assert call(B=64, H=64, T=1 << 14, dk=128, dv=128) == -8
+    assert call(q=None) == NULL and call(S=None) == NULL and call(z=None) == NULL
+    assert call(dt=4) == DTYPE and call(B=0) == SHAPE and call(T=-1) == SHAPE
+    assert call(dk=96) == DIM and call(q=MISALIGNED) == ALIGN
