@@ -14,18 +14,23 @@ bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
 bool dtype_ok(int dt) { return dt == LA_DTYPE_F32 || dt == LA_DTYPE_BF16; }
 
-// Element counts must stay addressable and the grid within one dimension.
+// Element counts must stay addressable and the grid within one dimension:
+// B*H and the chunk count B*H*ceil(T/64) fit an int, and every tensor (T
+// rounded up to whole chunks) and the state hold fewer than 2^50 elements.
 // t = 0 is allowed where the caller says so (a prefill over no tokens).
+// Each bound is checked by division, so no product here can overflow.
 bool sizes_ok(long long b, long long h, long long t, int dk, int dv, bool allow_empty = false) {
-  const long long mx = (dk > dv ? dk : dv);
+  const long long lim = 1LL << 50;
+  const long long mx = (dk > dv ? dk : dv);  // callers pass dims >= 1
   if (b <= 0 || h <= 0 || t < (allow_empty ? 0 : 1)) return false;
-  if (b * h > INT_MAX) return false;
+  if (b > INT_MAX / h) return false;
+  const long long bh = b * h;
   if (t > INT_MAX - 64) return false;  // the chunk count rounds t up to 64
-  const long long tp = ((t + 63) / 64) * 64;
-  const long long elems = b * h * tp * mx;
-  const long long state = b * h * (long long)dk * dv;
-  if (b * h * (tp / 64) > INT_MAX) return false;  // one workgroup per chunk in some kernels
-  return (tp == 0 || elems / mx / tp == b * h) && elems < (1LL << 50) && state < (1LL << 50);
+  const long long nch = (t + 63) / 64;
+  if (nch > 0 && bh > INT_MAX / nch) return false;  // one workgroup per chunk in some kernels
+  const long long tp = nch * 64;
+  if (tp > 0 && bh * nch > lim / 64 / mx) return false;
+  return bh <= lim / ((long long)dk * dv);
 }
 
 int launch_rc(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH; }

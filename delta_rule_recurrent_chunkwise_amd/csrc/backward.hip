@@ -1686,24 +1686,9 @@ __global__ __launch_bounds__(256) void zero_state(float* __restrict__ p, size_t 
 
 bool pass1_pipelined(int bf16, const BackwardArgs& a) { return bf16 && a.dk_ == 128 && a.dv_ % 32 == 0; }
 
-size_t round256(size_t n) { return (n + 255) / 256 * 256; }
-
 }  // namespace
 
-// Workspace layout, each region starting on a 256-byte boundary:
-//   Sc, dSc   fp32 [nchunks][dk][dv] each (the chunk states and their
-//             gradients; bf16 paths use the first half of each);
-//   gC        fp32 [nchunks] (gated rule only: the decay of every chunk);
-//   P, R^T    bf16 [nchunks][dk][dk] and [nchunks][dk][64] (bf16 only).
-size_t delta_backward_workspace_bytes(int bf16, const BackwardArgs& a) {
-  if (a.T == 0) return 0;
-  const size_t nchunks = (size_t)a.B * a.H * ((a.T + kC - 1) / kC);
-  size_t n = 2 * round256(nchunks * a.dk_ * a.dv_ * sizeof(float));
-  if (a.g) n += round256(nchunks * sizeof(float));
-  if (bf16) n += round256(nchunks * a.dk_ * (a.dk_ + kC) * sizeof(bf16_t));
-  return n;
-}
-
+// Workspace layout: see delta_backward_workspace_bytes (launch.hpp).
 hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, void* workspace, hipStream_t st) {
   if (a.T == 0) {  // no tokens: the state's gradient passes through
     if (!a.dS0) return hipSuccess;
@@ -1717,13 +1702,13 @@ hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, void* workspac
   const size_t nst = nchunks * a.dk_ * a.dv_;
   char* ws = static_cast<char*>(workspace);
   float* Sc = reinterpret_cast<float*>(ws);
-  ws += round256(nst * sizeof(float));
+  ws += workspace_round256(nst * sizeof(float));
   float* dSc = reinterpret_cast<float*>(ws);
-  ws += round256(nst * sizeof(float));
+  ws += workspace_round256(nst * sizeof(float));
   float* gC = nullptr;
   if (a.g) {
     gC = reinterpret_cast<float*>(ws);
-    ws += round256(nchunks * sizeof(float));
+    ws += workspace_round256(nchunks * sizeof(float));
   }
   bf16_t* Pg = bf16 ? reinterpret_cast<bf16_t*>(ws) : nullptr;
   bf16_t* Rg = bf16 ? Pg + nchunks * a.dk_ * a.dk_ : nullptr;

@@ -453,12 +453,6 @@ hipError_t launch_states(int dk, const PrefillArgs& a, void* workspace, hipStrea
 
 }  // namespace
 
-// [dS: fp32 nchunks x dk x dv][dz, then z_c (or Gam_C): fp32 nchunks x dk][S_c: bf16 nchunks x dk x dv]
-size_t la_par_workspace_bytes(int dk, const PrefillArgs& a) {
-  const size_t nchunks = (size_t)a.B * a.H * ((a.T + kC - 1) / kC);
-  return nchunks * ((size_t)dk * a.dv + dk) * sizeof(float) + nchunks * dk * a.dv * sizeof(bf16_t);
-}
-
 hipError_t launch_la_par_states(int dk, const PrefillArgs& a, void* workspace, bool gla, hipStream_t st) {
   return gla ? launch_states<true>(dk, a, workspace, st) : launch_states<false>(dk, a, workspace, st);
 }

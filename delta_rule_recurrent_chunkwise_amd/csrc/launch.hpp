@@ -1,7 +1,11 @@
 // launch.hpp -- internal interface between the C-ABI entry points (api.hip)
-// and the kernel launchers (decode.hip, prefill.hip).
+// and the kernel launchers (decode.hip, prefill.hip, ...): argument structs,
+// launcher declarations, and the workspace sizes (host-only arithmetic, so
+// the validation in api.hip builds without the device compiler).
 #pragma once
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
 
 namespace linattn {
 
@@ -44,10 +48,8 @@ struct PrefillArgs {
 // hipErrorInvalidValue for a combination with no kernel.
 hipError_t launch_decode(int kind, int bf16, int dk, int dv, const DecodeArgs& a,
                          hipStream_t st);
-// Device memory a prefill needs beyond its inputs and outputs (0 for most
-// paths), and the prefill itself with a workspace of at least that many
-// bytes, 256-byte aligned (may be NULL when the size is 0).
-size_t prefill_workspace_bytes(int mode, int bf16, int dk, const PrefillArgs& a);
+// The prefill with a workspace of at least prefill_workspace_bytes() bytes,
+// 256-byte aligned (may be NULL when that is 0).
 hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, void* workspace,
                           hipStream_t st);
 // The generic prefill kernel only (used by the backward pass with a.Sc set).
@@ -70,7 +72,6 @@ struct BackwardArgs {
   const void* g;     // one log-decay per token [B,H,T] (gated rule) or NULL
   void* dg;          // its gradient [B,H,T] (with g)
 };
-size_t delta_backward_workspace_bytes(int bf16, const BackwardArgs& a);
 hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, void* workspace, hipStream_t st);
 // The layer prologue (prologue.hip): see deltanet_prologue.
 struct PrologueArgs {
@@ -87,7 +88,6 @@ hipError_t launch_prologue(int bf16, const PrologueArgs& a, hipStream_t st);
 // The software-pipelined delta-rule prefill for bf16, dk = 128, dv % 32 == 0:
 // plain (a.g == NULL, no workspace) or gated (needs a workspace of
 // gated_pipe_workspace_bytes(a) bytes).
-size_t gated_pipe_workspace_bytes(const PrefillArgs& a);
 hipError_t launch_prefill_pipe(const PrefillArgs& a, void* workspace, hipStream_t st);
 // ... and with one decay per token (a.g [B,H,T]; no workspace).
 hipError_t launch_prefill_pipe_token(const PrefillArgs& a, hipStream_t st);
@@ -97,9 +97,53 @@ hipError_t launch_prefill_pipe_token(const PrefillArgs& a, hipStream_t st);
 // exclusive prefix in place (the chunk-start states) and the final S, z.
 // gla: gated linear attention instead (no feature map or normaliser; a decay
 // per token).
-size_t la_par_workspace_bytes(int dk, const PrefillArgs& a);
 hipError_t launch_la_par_states(int dk, const PrefillArgs& a, void* workspace, bool gla, hipStream_t st);
 // ... then every chunk's output from its chunk-start state (bf16).
 hipError_t launch_la_par_outputs(int dk, const PrefillArgs& a, void* workspace, bool gla, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Workspace sizes (C = ceil(T/64) chunks per head)
+// ---------------------------------------------------------------------------
+inline size_t workspace_round256(size_t n) { return (n + 255) / 256 * 256; }
+inline size_t workspace_chunks(long B, long H, long T) { return (size_t)B * H * ((T + 63) / 64); }
+
+// Chunk-parallel linear attention: [dS: fp32 chunks x dk x dv][dz, then z_c
+// (or Gam_C): fp32 chunks x dk][S_c: bf16 chunks x dk x dv].
+inline size_t la_par_workspace_bytes(int dk, const PrefillArgs& a) {
+  const size_t n = workspace_chunks(a.B, a.H, a.T);
+  return n * ((size_t)dk * a.dv + dk) * sizeof(float) + n * dk * a.dv * sizeof(uint16_t);
+}
+
+// Per-channel gate pre-pass (dk = 128): Gam Q, Gam K, K / Gam in bf16 (64 rows
+// per chunk) and Gam_C in fp32.
+inline size_t gated_pipe_workspace_bytes(const PrefillArgs& a) {
+  const size_t n = workspace_chunks(a.B, a.H, a.T);
+  return 3 * n * 64 * 128 * sizeof(uint16_t) + n * 128 * sizeof(float);
+}
+
+// Device memory a prefill needs beyond its inputs and outputs (0 for most
+// paths): the chunk-parallel bf16 linear-attention kernels keep per-chunk
+// states; the per-channel gated pipelined kernel reads the pre-pass's
+// decay-scaled q and k.
+inline size_t prefill_workspace_bytes(int mode, int bf16, int dk, const PrefillArgs& a) {
+  if (a.T == 0 || !bf16) return 0;
+  if (mode == PF_LA || mode == PF_GLA) return la_par_workspace_bytes(dk, a);
+  if (mode == PF_GATED && dk == 128 && a.dv % 32 == 0) return gated_pipe_workspace_bytes(a);
+  return 0;
+}
+
+// Backward: each region starting on a 256-byte boundary,
+//   Sc, dSc   fp32 [chunks][dk][dv] each (the chunk states and their
+//             gradients; bf16 paths use the first half of each);
+//   gC        fp32 [chunks] (gated rule only: the decay of every chunk);
+//   P, R^T    bf16 [chunks][dk][dk] and [chunks][dk][64] (bf16 only).
+inline size_t delta_backward_workspace_bytes(int bf16, const BackwardArgs& a) {
+  if (a.T == 0) return 0;
+  const size_t n = workspace_chunks(a.B, a.H, a.T);
+  size_t w = 2 * workspace_round256(n * a.dk_ * a.dv_ * sizeof(float));
+  if (a.g) w += workspace_round256(n * sizeof(float));
+  if (bf16) w += workspace_round256(n * a.dk_ * (a.dk_ + 64) * sizeof(uint16_t));
+  return w;
+}
 
 }  // namespace linattn

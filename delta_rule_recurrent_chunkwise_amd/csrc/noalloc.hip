@@ -13,6 +13,7 @@
 // on one GPU (different streams without ordering between them) race on it.
 // The kernels write every scratch element they read in the same call, so the
 // previous call's contents need no clearing.
+#include <hip/hip_runtime.h>
 #include <mutex>
 #include <stdint.h>
 

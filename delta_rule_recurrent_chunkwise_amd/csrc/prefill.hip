@@ -619,13 +619,6 @@ static hipError_t launch_prefill_e(int dk, const PrefillArgs& a, hipStream_t st)
 // The chunk-parallel linear-attention kernels (bf16) keep per-chunk states in
 // the workspace; the per-channel gated pipelined kernel reads the pre-pass's
 // decay-scaled q and k from it.  Every other path needs none.
-size_t prefill_workspace_bytes(int mode, int bf16, int dk, const PrefillArgs& a) {
-  if (a.T == 0 || !bf16) return 0;
-  if (mode == PF_LA || mode == PF_GLA) return la_par_workspace_bytes(dk, a);
-  if (mode == PF_GATED && dk == 128 && a.dv % 32 == 0) return gated_pipe_workspace_bytes(a);
-  return 0;
-}
-
 hipError_t launch_prefill(int mode, int bf16, int dk, const PrefillArgs& a, void* workspace,
                           hipStream_t st) {
   if (a.T == 0) {  // no tokens: the state passes through unchanged

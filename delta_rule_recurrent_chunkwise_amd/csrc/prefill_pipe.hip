@@ -796,12 +796,6 @@ __global__ __launch_bounds__(256) void gate_prep(const bf16_t* __restrict__ q, c
 
 }  // namespace
 
-size_t gated_pipe_workspace_bytes(const PrefillArgs& a) {
-  const size_t nch = (size_t)(a.T + kC - 1) / kC;
-  const size_t n = (size_t)a.B * a.H * nch * kC * kDK;
-  return 3 * n * sizeof(bf16_t) + (size_t)a.B * a.H * nch * kDK * sizeof(float);
-}
-
 namespace {
 
 template <int GM, bool CAP = false>
