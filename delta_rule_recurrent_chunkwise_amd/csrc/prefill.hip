@@ -50,6 +50,10 @@ namespace linattn {
 
 constexpr int kC = 64;         // chunk length in tokens
 constexpr int kThreads = 256;  // 4 waves
+// Per-channel gate: the factored chunk form divides keys by the decay summed
+// from the chunk start; a chunk where that sum leaves [-kGateRange,
+// kGateRange] for some channel is computed token by token instead.
+constexpr float kGateRange = 64.f;
 constexpr int kWaves = kThreads / 64;
 
 // kGate: decay per key channel, decayed operands (K~, K^, Q~) staged;
@@ -114,6 +118,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   constexpr bool kSolve = ModeTraits<MODE>::kSolve;
 
   __shared__ __attribute__((aligned(16))) char smem[L::total];
+  __shared__ int sWide;  // per-channel gate: this chunk's decay leaves the factored form's range
   T* sQ = reinterpret_cast<T*>(smem + L::oQ);
   T* sK = reinterpret_cast<T*>(smem + L::oK);
   T* sKh = kGate ? reinterpret_cast<T*>(smem + L::oKh) : sK;
@@ -295,6 +300,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         gl[j] = run;
       }
       sPart[part * DK + d] = run;
+      if (tid == 0) sWide = 0;
       __syncthreads();
       float off = 0.f, tot = 0.f;
 #pragma unroll
@@ -303,19 +309,35 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         if (p < part) off += x;
         tot += x;
       }
+      // K / Gam must stay in the float range: a chunk in which some channel's
+      // summed log-decay leaves [-kGateRange, kGateRange] is walked token by
+      // token instead, on raw q, k and g staged in the same places
+      float mx = 0.f;
+#pragma unroll
+      for (int j = 0; j < TPP; ++j) mx = fmaxf(mx, fabsf(off + gl[j]));
+      if (!(mx <= kGateRange)) sWide = 1;  // also for NaN
+      __syncthreads();
+      const bool wide = sWide != 0;
       if (part == 0) sVec[d] = __expf(tot);
 #pragma unroll
       for (int j = 0; j < TPP; ++j) {
         const int r = part * TPP + j;
         const float G = off + gl[j];
-        const float eg = __expf(G), emg = __expf(-G), dec = __expf(tot - G);
         const bool in = t0 + r <= tlast;
         const float qv = in ? E::ld(qh + (size_t)(t0 + r) * DK + d) : 0.f;
         const float kv = in ? E::ld(kh + (size_t)(t0 + r) * DK + d) : 0.f;
-        sQ[r * LQ + d] = E::cvt(qv * eg);
-        sK[r * LQ + d] = E::cvt(kv * eg);
-        sKh[r * LQ + d] = E::cvt(kv * emg);
-        sKt[d * LKT + r] = E::cvt(kv * dec);
+        if (wide) {
+          const float gv = in ? E::ld(gh + (size_t)(t0 + r) * DK + d) : 0.f;
+          sQ[r * LQ + d] = E::cvt(qv);
+          sK[r * LQ + d] = E::cvt(kv);
+          sKh[r * LQ + d] = E::cvt(gv);
+        } else {
+          const float eg = __expf(G), emg = __expf(-G), dec = __expf(tot - G);
+          sQ[r * LQ + d] = E::cvt(qv * eg);
+          sK[r * LQ + d] = E::cvt(kv * eg);
+          sKh[r * LQ + d] = E::cvt(kv * emg);
+          sKt[d * LKT + r] = E::cvt(kv * dec);
+        }
       }
     }
     if (kGate) {
@@ -330,6 +352,43 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
       if (kSolve && tid < kC) sRow[tid] = t0 + tid <= tlast ? E::ld(bth + t0 + tid) : 0.f;
     }
     __syncthreads();
+    if (kGate && sWide) {
+      // the recurrence itself, token by token, S <- diag(a_t) S, u = beta_t
+      // (v_t - k_t S), S += k_t^T u, o_t = q_t S: lane (lc, lg) of a chain
+      // wave holds column 16cw + lc of rows (key channels) 16kt + 4lg + i;
+      // sums over channels are completed across the four lanes of a column
+      if (chain) {
+        for (int tau = 0; tau < kC; ++tau) {
+          float kk[NKT][4], qq[NKT][4];
+          float r = 0.f;
+#pragma unroll
+          for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int ch = 16 * kt + 4 * lg + i;
+              kk[kt][i] = E::tof(sK[tau * LQ + ch]);
+              qq[kt][i] = E::tof(sQ[tau * LQ + ch]);
+              st[kt][i] *= __expf(E::tof(sKh[tau * LQ + ch]));
+              r += kk[kt][i] * st[kt][i];
+            }
+          r += __shfl_xor(r, 16);
+          r += __shfl_xor(r, 32);
+          const float u = sRow[tau] * (E::tof(sVt[(16 * cw + lc) * LKT + tau]) - r);
+          float o = 0.f;
+#pragma unroll
+          for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              st[kt][i] += kk[kt][i] * u;
+              o += qq[kt][i] * st[kt][i];
+            }
+          o += __shfl_xor(o, 16);
+          o += __shfl_xor(o, 32);
+          if (lg == 0 && !a.Sc && t0 + tau <= tlast) oh[(size_t)(t0 + tau) * dv + 16 * cw + lc] = E::cvt(o);
+        }
+      }
+      continue;  // uniform over the workgroup
+    }
 
     // -------- chain waves: products with the incoming state; others: the
     // -------- chunk's pairwise products

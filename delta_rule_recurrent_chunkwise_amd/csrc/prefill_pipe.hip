@@ -150,7 +150,6 @@ struct PipeArgs {
   int T, dv, use_init;
   int Tq;              // rows per head of q, k, k^: T, or T rounded up to 64 (gated)
   float* Sc;           // if set: the state entering every chunk, bf16, [B*H][nch] x dk x dv in accumulator-tile order
-                       // (CAP kernels write only this: no output, no final state)
 };
 
 // Loads.  Each tile-loader wave owns whole tiles (Q, K, and, gated, K^) and
@@ -183,8 +182,10 @@ struct LoadPlan {
   }
 };
 
-// CAP: write the state entering every chunk to a.Sc instead of the output
-// and the final state (backward pass).
+// CAP: also write the state entering every chunk to a.Sc (backward pass,
+// which passes a.o = NULL: then neither the output nor the final state is
+// written; a run-time test, which kept the register allocation free of
+// spills where the compile-time one did not).
 template <int GM, int DVS, bool CAP = false>
 __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
   constexpr bool GATED = GM == 1;  // per key channel, operands from the pre-pass
@@ -374,10 +375,60 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
       }
     }
     floatx4 xx[4], ox[4];
+    // Per-channel gate, a chunk the pre-pass marked (Gam_C < 0): its decay
+    // leaves the range of the factored form, so it is walked token by token
+    // with the recurrence itself, S <- diag(a_t) S, u = beta_t (v_t - k_t S),
+    // S += k_t^T u, o_t = q_t S, on the raw q, k and g the pre-pass staged in
+    // its slots.  Lane (lc, lg) holds column col of rows 16t + 4lg + i, i.e.
+    // key channels perm32(16t + 4lg) + i; the sums over channels are
+    // completed across the four lanes that share a column.
+    auto token_walk = [&](auto parity) {
+      constexpr int P = decltype(parity)::value;
+      for (int tau = 0; tau < kC; ++tau) {
+        float kk[8][4], qq[8][4];
+        float r = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int c0 = perm32(16 * t + 4 * lg);
+          const uint2 kw = *reinterpret_cast<const uint2*>(&sm.k[GATED ? P : 0][tau][c0]);
+          const uint2 qw = *reinterpret_cast<const uint2*>(&sm.q[P][tau][c0]);
+          const uint2 gw = *reinterpret_cast<const uint2*>(&sm.kh[GATED ? P : 0][GATED ? tau : 0][c0]);
+          const uint32_t kv[2] = {kw.x, kw.y}, qv[2] = {qw.x, qw.y}, gv[2] = {gw.x, gw.y};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t sh = (i & 1) ? 16u : 0u;
+            kk[t][i] = bf2f((bf16_t)(kv[i >> 1] >> sh));
+            qq[t][i] = bf2f((bf16_t)(qv[i >> 1] >> sh));
+            st[t][i] *= __expf(bf2f((bf16_t)(gv[i >> 1] >> sh)));
+            r += kk[t][i] * st[t][i];
+          }
+        }
+        r += __shfl_xor(r, 16);
+        r += __shfl_xor(r, 32);
+        const float u = sm.beta[P][tau] * (bf2f(sm.v[P][tau][col]) - r);
+        float o = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            st[t][i] += kk[t][i] * u;
+            o += qq[t][i] * st[t][i];
+          }
+        o += __shfl_xor(o, 16);
+        o += __shfl_xor(o, 32);
+        if (lg == 0) sm.o[P][tau][col] = f2bf(o);
+      }
+    };
     run(
         [&](const int x, auto parity) {
           constexpr int P = decltype(parity)::value;
           if (x < 0) return;
+          if constexpr (GATED) {
+            if (sm.gc[P][0] < 0.f) {
+              token_walk(parity);
+              return;
+            }
+          }
           if constexpr (CAP) {  // the state entering chunk x, for the backward pass
             // row perm32(16t + 4lg + i) = 8lg + 32(t / 2) + 4(t % 2) + i: one
             // lane-dependent base, offsets uniform across the wave
@@ -443,6 +494,9 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
         [&](const int x, auto parity) {
           constexpr int P = decltype(parity)::value;
           if (x < 0) return;
+          if constexpr (GATED) {
+            if (sm.gc[P][0] < 0.f) return;  // walked token by token in phase 1
+          }
           auto fr16 = [&](const bf16_t* blk) {  // A operand of a transposed 16x16 block
             return ld_tr(blk + (4 * lg + ((lane >> 2) & 3)) * 16 + 4 * (lane & 3));
           };
@@ -530,7 +584,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
             for (int i = 0; i < 4; ++i) sm.o[P][16 * mt + 4 * lg + i][col] = f2bf(ox[mt][i]);
         },
         std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-    if constexpr (!CAP) {  // the backward pass needs only the chunk states
+    if (a.o != nullptr) {  // the backward pass (no output) needs only the chunk states
 #pragma unroll
       for (int t = 0; t < 8; ++t)
 #pragma unroll
@@ -714,7 +768,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
     };
     auto ph1 = [&](const int x, auto parity) {};
     auto ph2 = [&](const int x, auto parity) {
-      if (!CAP && wave == 4 && x >= 1) store_o(x - 1, std::false_type{});
+      if (a.o != nullptr && wave == 4 && x >= 1) store_o(x - 1, std::false_type{});
     };
     // plain: Q of chunk x+1 and K of chunk x+2 are stored in phase 2 of x
     // (K(x+1) is read then, for L(x+1)); gated: K and K^ in phase 1, and
@@ -725,7 +779,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
     else if (LP::kThree && wave == 1) run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, LP::kThree ? 1 : 0>{});
     else if (LP::is_tile_wave(wave)) run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
     else run(ph1, ph2, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-    if (!CAP && wave == 4) store_o(nch - 1, std::true_type{});
+    if (a.o != nullptr && wave == 4) store_o(nch - 1, std::true_type{});
   }
 }
 
@@ -737,11 +791,19 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
 // Inputs have T rows per head; the outputs have nch * 64, and rows past T
 // (a partial last chunk) get g = 0 and q = k = 0, so Gam_C is the decay
 // over the tokens that exist.
+// A chunk in which some |G_t| exceeds kGateRange (a channel decays by more
+// than e^-64 within it, so K / Gam would leave the float range) is not
+// scaled: its q, k and g are copied as they are into the Gam Q, Gam K and
+// K / Gam slots, and Gam_C is set to -1, which tells the main kernel to walk
+// that chunk token by token.
+constexpr float kGateRange = 64.f;
+
 __global__ __launch_bounds__(256) void gate_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                  const bf16_t* __restrict__ g, bf16_t* __restrict__ qt,
                                                  bf16_t* __restrict__ kt, bf16_t* __restrict__ kht,
                                                  float* __restrict__ gcum, int T, int nch) {
   __shared__ float2 part[4][64];
+  __shared__ int wide;
   const int chunk = blockIdx.x;  // over B*H*nch
   const int bh = chunk / nch, t0 = (chunk - bh * nch) * kC;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
@@ -762,6 +824,7 @@ __global__ __launch_bounds__(256) void gate_prep(const bf16_t* __restrict__ q, c
     gl[t] = run;
   }
   part[w][l] = run;
+  if (threadIdx.x == 0) wide = 0;
   __syncthreads();
   float2 off = make_float2(0.f, 0.f), tot = make_float2(0.f, 0.f);
 #pragma unroll
@@ -771,12 +834,32 @@ __global__ __launch_bounds__(256) void gate_prep(const bf16_t* __restrict__ q, c
     tot.x += x.x;
     tot.y += x.y;
   }
-  if (w == 0) reinterpret_cast<float2*>(gcum + (size_t)chunk * kDK)[l] = make_float2(__expf(tot.x), __expf(tot.y));
+  // does any channel leave [-kGateRange, kGateRange] within the chunk?
+  float mx = 0.f;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) mx = fmaxf(mx, fmaxf(fabsf(off.x + gl[t].x), fabsf(off.y + gl[t].y)));
+  if (!(mx <= kGateRange)) wide = 1;  // also for NaN
+  __syncthreads();
   const uint32_t* q2 = reinterpret_cast<const uint32_t*>(q + ibase);
   const uint32_t* k2 = reinterpret_cast<const uint32_t*>(k + ibase);
   uint32_t* qt2 = reinterpret_cast<uint32_t*>(qt + base);
   uint32_t* kt2 = reinterpret_cast<uint32_t*>(kt + base);
   uint32_t* kh2 = reinterpret_cast<uint32_t*>(kht + base);
+  if (wide) {  // uniform over the workgroup: raw q, k, g and the marker
+    if (w == 0) reinterpret_cast<float2*>(gcum + (size_t)chunk * kDK)[l] = make_float2(-1.f, -1.f);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int idx = (16 * w + t) * (kDK / 2) + l;
+      const int iidx = min(16 * w + t, nrow - 1) * (kDK / 2) + l;
+      const bool in = 16 * w + t < nrow;
+      const uint32_t qr = q2[iidx], kr = k2[iidx];  // in bounds for every lane
+      qt2[idx] = in ? qr : 0u;
+      kt2[idx] = in ? kr : 0u;
+      kh2[idx] = in ? gw[t] : 0u;
+    }
+    return;
+  }
+  if (w == 0) reinterpret_cast<float2*>(gcum + (size_t)chunk * kDK)[l] = make_float2(__expf(tot.x), __expf(tot.y));
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
     const int idx = (16 * w + t) * (kDK / 2) + l;

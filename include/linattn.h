@@ -152,10 +152,11 @@ int la_decode_step(const void *q, const void *k, const void *v, void *o,
  *   S_t = diag(a_t) S_{t-1} + beta_t k_t^T (v_t - k_t diag(a_t) S_{t-1}),
  * where g = log a (the log-decay, <= 0) is given per token and key channel.
  * The chunked gated form divides keys by the decay accumulated from the
- * start of their 64-token chunk, so the summed log-decay of any key channel
- * over one chunk must stay above about -87 (the float exponent range);
- * stronger decays overflow to Inf/NaN.  gated_deltanet_prefill has no such
- * limit.
+ * start of their 64-token chunk.  A chunk in which some key channel's summed
+ * log-decay leaves [-64, 64] (stronger decay, or growth where g > 0), where
+ * that division would leave the float range, is computed token by token
+ * with the recurrence itself instead: any finite g gives the recurrence's
+ * result, such chunks only take longer.
  * q and k are used as given: no feature map, normalisation or scale.
  * q, k [B,H,T,dk], v [B,H,T,dv], beta [B,H,T], g [B,H,T,dk] or NULL (dtype).
  * o [B,H,T,dv] out (dtype).  S [B,H,dk,dv] float32 in/out as in la_prefill.

@@ -23,10 +23,13 @@ def _pair(B, H, T, dk, dv, dtype, seed, init):
     S = d["S0"].clone() if init else torch.empty(B, H, dk, dv, device=dev)
     z = d["z0"].clone() if init else torch.empty(B, H, dk, device=dev)
     torch.cuda.synchronize()
-    before = torch.cuda.memory_allocated(dev)
+    # torch's count of allocation requests so far (frees, e.g. by garbage
+    # collection of earlier tests' tensors, do not change it)
+    before = torch.cuda.memory_stats(dev)["allocation.all.allocated"]
     la.la_prefill_noalloc(d["q"], d["k"], d["v"], o, S, z, use_initial_state=init)
     torch.cuda.synchronize()
-    assert torch.cuda.memory_allocated(dev) == before, "the call allocated through torch"
+    assert torch.cuda.memory_stats(dev)["allocation.all.allocated"] == before, \
+        "the call allocated through torch"
     return (o, S, z), (o_ref, S_ref, z_ref)
 
 
