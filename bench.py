@@ -621,6 +621,81 @@ def bench_token_gated_rows(la, workloads, torch, launches=20):
     return rows
 
 
+def bench_segmented_rows(la, workloads, torch, launches=10):
+    """The sequence-parallel chunk-state scan (prototype in
+    delta_rule_recurrent_chunkwise_amd/segmented.py) against the one-pass
+    prefill: at the gated workload's shape (per-channel and per-token gate,
+    B=1 H=32 T=32768) and with few heads (B=1 H=4 T=32768, no gate), for
+    several segment counts.  Each entry: the one-pass and segmented times per
+    call (HIP events around the whole call), the segmented call's steps, and
+    the segmented result's difference from the one-pass result."""
+    from delta_rule_recurrent_chunkwise_amd.segmented import (SegmentBuffers,
+                                                              segmented_delta_prefill)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    cases = [("per_channel_gate_B1_H32_T32768", 1, 32, True, False, (2, 4, 8)),
+             ("per_token_gate_B1_H32_T32768", 1, 32, "token", True, (2, 4, 8)),
+             ("no_gate_B1_H4_T32768", 1, 4, False, False, (2, 4, 8, 16, 32))]
+    T, d = 32768, 128
+    out = {}
+    for name, B, H, gated, token, seg_counts in cases:
+        inp = workloads.make_delta(B, H, T, d, d, torch.bfloat16, seed=70 + H, gated=gated)
+        x = {k: v.to(dev) for k, v in inp.items()}
+        del inp
+        g = x.get("g")
+        o1 = torch.empty_like(x["v"])
+        S1 = torch.empty(B, H, d, d, device=dev, dtype=torch.float32)
+
+        def one_pass(_):
+            if token:
+                la.gated_deltanet_prefill(x["q"], x["k"], x["v"], x["beta"], g, S=S1, o=o1,
+                                          stream=stream)
+            else:
+                la.deltanet_prefill(x["q"], x["k"], x["v"], x["beta"], g=g, S=S1, o=o1,
+                                    stream=stream)
+
+        us1, _ = _time_launches(torch, stream, one_pass, [None], launches, warmup=2)
+        entry = {"one_pass_us": us1, "segmented": {}}
+        for P in seg_counts:
+            buf = SegmentBuffers(B, H, T, d, d, P, torch.bfloat16, dev,
+                                 gated is not False and not token)
+            marks = []
+
+            def seg(_, rec=None):
+                segmented_delta_prefill(x["q"], x["k"], x["v"], x["beta"], P, g=g,
+                                        token_gate=token, buffers=buf, stream=stream,
+                                        timer=rec)
+
+            us, _ = _time_launches(torch, stream, seg, [None], launches, warmup=2)
+            # one more call with an event after every step
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+
+            def rec(step):
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                marks.append((step, e))
+
+            seg(None, rec)
+            torch.cuda.synchronize()
+            steps, prev = {}, ev0
+            for step, e in marks:
+                steps[step + "_us"] = prev.elapsed_time(e) * 1e3
+                prev = e
+            one_pass(None)
+            torch.cuda.synchronize()
+            o_diff = ((buf.o0.view_as(o1).float() - o1.float()).abs().max()
+                      / o1.float().abs().max()).item()
+            s_diff = ((buf.S - S1).abs().max() / S1.abs().max()).item()
+            entry["segmented"][f"P{P}"] = {"us": us, "speedup": us1 / us, "steps": steps,
+                                           "o_rel_diff": o_diff, "S_rel_diff": s_diff}
+            del buf
+        out[name] = entry
+        del x, o1, S1
+        torch.cuda.empty_cache()
+    return out
+
+
 def measured_peaks(torch, reps=5):
     """Rates this GPU sustains in the same run, from libpeak_probe.so (built
     with the library): a copy between two buffers (the prefill's pattern:
@@ -803,7 +878,7 @@ def main():
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the other rows (LA prefill, gated prefill, LA/gated decode)")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "copy", "rows", "token-rows",
-                                       "backward-row", "prologue-row"],
+                                       "backward-row", "prologue-row", "segmented"],
                     default="all",
                     help="run one part only (for profiler runs)")
     ap.add_argument("--summarize", metavar="DIR",
@@ -843,6 +918,9 @@ def main():
         return
     if args.only == "prologue-row":
         print(json.dumps(bench_prologue_row(la, workloads, torch)))
+        return
+    if args.only == "segmented":
+        print(json.dumps(bench_segmented_rows(la, workloads, torch)))
         return
     if args.only == "decode":
         wd, _, el = bench_decode(la, workloads, torch, args.decode_steps)
