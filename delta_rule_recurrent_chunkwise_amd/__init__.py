@@ -20,28 +20,28 @@ __all__ = [
     "la_prefill", "la_decode_step", "deltanet_prefill", "deltanet_decode_step",
     "gated_deltanet_prefill", "gated_deltanet_decode_step", "gla_prefill",
     "gla_decode_step", "deltanet_prefill_backward", "gated_deltanet_prefill_backward",
-    "deltanet_prologue", "la_strerror",
+    "kda_prefill_backward", "deltanet_prologue", "la_strerror",
     "la_prefill_workspace_bytes", "deltanet_prefill_workspace_bytes",
     "gla_prefill_workspace_bytes", "deltanet_prefill_backward_workspace_bytes",
-    "gated_deltanet_prefill_backward_workspace_bytes", "la_prefill_noalloc",
+    "gated_deltanet_prefill_backward_workspace_bytes", "kda_prefill_backward_workspace_bytes",
+    "la_prefill_noalloc",
     "library", "LIB_PATH",
     "EXPORTED_SYMBOLS",
     "LinAttnError",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblinattn.so")
-EXPORTED_SYMBOLS = ("la_prefill", "la_decode_step", "deltanet_prefill",
-                    "deltanet_decode_step", "gated_deltanet_prefill",
-                    "gated_deltanet_decode_step", "gla_prefill", "gla_decode_step",
-                    "deltanet_prefill_backward", "gated_deltanet_prefill_backward",
-                    "deltanet_prologue",
-                    "la_prefill_workspace_bytes", "deltanet_prefill_workspace_bytes",
-                    "gla_prefill_workspace_bytes",
-                    "deltanet_prefill_backward_workspace_bytes",
-                    "gated_deltanet_prefill_backward_workspace_bytes",
-                    "la_prefill_noalloc",
-                    "la_strerror")
-WORKSPACE_QUERIES = EXPORTED_SYMBOLS[11:16]
+COMPUTE_ENTRIES = ("la_prefill", "la_decode_step", "deltanet_prefill",
+                   "deltanet_decode_step", "gated_deltanet_prefill",
+                   "gated_deltanet_decode_step", "gla_prefill", "gla_decode_step",
+                   "deltanet_prefill_backward", "gated_deltanet_prefill_backward",
+                   "kda_prefill_backward", "deltanet_prologue")
+WORKSPACE_QUERIES = ("la_prefill_workspace_bytes", "deltanet_prefill_workspace_bytes",
+                     "gla_prefill_workspace_bytes",
+                     "deltanet_prefill_backward_workspace_bytes",
+                     "gated_deltanet_prefill_backward_workspace_bytes",
+                     "kda_prefill_backward_workspace_bytes")
+EXPORTED_SYMBOLS = COMPUTE_ENTRIES + WORKSPACE_QUERIES + ("la_prefill_noalloc", "la_strerror")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 LA_DTYPE_F32, LA_DTYPE_BF16 = 0, 1
@@ -78,14 +78,16 @@ def library():
         lib.gla_decode_step.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
         lib.deltanet_prefill_backward.argtypes = [P] * 12 + [I] * 6 + [P, Z, P]
         lib.gated_deltanet_prefill_backward.argtypes = [P] * 14 + [I] * 6 + [P, Z, P]
+        lib.kda_prefill_backward.argtypes = [P] * 14 + [I] * 6 + [P, Z, P]
         lib.deltanet_prologue.argtypes = [P] * 6 + [I] * 6 + [ctypes.c_float, I, P]
-        for fn in EXPORTED_SYMBOLS[:11]:
+        for fn in COMPUTE_ENTRIES:
             getattr(lib, fn).restype = I
         lib.la_prefill_workspace_bytes.argtypes = [I] * 6
         lib.deltanet_prefill_workspace_bytes.argtypes = [I] * 7
         lib.gla_prefill_workspace_bytes.argtypes = [I] * 6
         lib.deltanet_prefill_backward_workspace_bytes.argtypes = [I] * 6
         lib.gated_deltanet_prefill_backward_workspace_bytes.argtypes = [I] * 6
+        lib.kda_prefill_backward_workspace_bytes.argtypes = [I] * 6
         for fn in WORKSPACE_QUERIES:
             getattr(lib, fn).restype = Z
         lib.la_prefill_noalloc.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
@@ -129,6 +131,11 @@ def gated_deltanet_prefill_backward_workspace_bytes(B, H, T, dk, dv, dtype) -> i
     """Bytes of workspace gated_deltanet_prefill_backward needs."""
     return int(library().gated_deltanet_prefill_backward_workspace_bytes(B, H, T, dk, dv,
                                                                          _dt(dtype)))
+
+
+def kda_prefill_backward_workspace_bytes(B, H, T, dk, dv, dtype) -> int:
+    """Bytes of workspace kda_prefill_backward needs."""
+    return int(library().kda_prefill_backward_workspace_bytes(B, H, T, dk, dv, _dt(dtype)))
 
 
 def _check(fn: str, rc: int):
@@ -449,6 +456,36 @@ def gated_deltanet_prefill_backward(q, k, v, beta, g, dO, S0=None, dST=None, wan
         _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(db), _ptr(dg), _ptr(dS0), B, H, T, dk, dv,
         _DTYPES[dtype], wp, wn, _stream(dev, stream))
     _check("gated_deltanet_prefill_backward", rc)
+    return dq, dkk, dvv, db, dg, dS0
+
+
+def kda_prefill_backward(q, k, v, beta, g, dO, S0=None, dST=None, want_dS0=False,
+                         stream=None, workspace=None):
+    """Gradients of deltanet_prefill with a per-key-channel gate (g =
+    log-decay [B,H,T,dk]) for the loss sum(dO * o) + sum(dST * S_T): returns
+    (dq, dk, dv, dbeta, dg, dS0), dS0 None unless want_dS0.  bf16 inputs; the
+    rest as deltanet_prefill_backward."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev, dtype = _inputs("kda_prefill_backward", dict(q=q, k=k, v=v, beta=beta, g=g, dO=dO),
+                         dict(q=(B, H, T, dk), k=(B, H, T, dk), v=(B, H, T, dv),
+                              beta=(B, H, T), g=(B, H, T, dk), dO=(B, H, T, dv)))
+    for name, t in (("S0", S0), ("dST", dST)):
+        if t is not None:
+            _state("kda_prefill_backward", name, t, (B, H, dk, dv), dev)
+    dq = torch.empty_like(q)
+    dkk = torch.empty_like(k)
+    dvv = torch.empty_like(v)
+    db = torch.empty_like(beta)
+    dg = torch.empty_like(g)
+    dS0 = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32) if want_dS0 else None
+    wp, wn, _keep = _workspace(kda_prefill_backward_workspace_bytes(B, H, T, dk, dv, dtype), dev,
+                               workspace)
+    rc = library().kda_prefill_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(dO), _ptr(dST),
+        _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(db), _ptr(dg), _ptr(dS0), B, H, T, dk, dv,
+        _DTYPES[dtype], wp, wn, _stream(dev, stream))
+    _check("kda_prefill_backward", rc)
     return dq, dkk, dvv, db, dg, dS0
 
 

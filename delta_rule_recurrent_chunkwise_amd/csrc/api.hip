@@ -77,6 +77,18 @@ size_t backward_ws(int gated, int B, int H, int T, int dk, int dv, int dtype) {
   return linattn::delta_backward_workspace_bytes(dtype == LA_DTYPE_BF16, a);
 }
 
+size_t kda_ws(int B, int H, int T, int dk, int dv, int dtype) {
+  if (prefill_args_rc(dtype, B, H, T, dk, dv) != LA_OK) return 0;
+  if (dtype != LA_DTYPE_BF16) return 0;  // not supported
+  linattn::BackwardArgs a{};
+  a.B = B;
+  a.H = H;
+  a.T = T;
+  a.dk_ = dk;
+  a.dv_ = dv;
+  return linattn::kda_backward_workspace_bytes(a);
+}
+
 }  // namespace
 
 extern "C" {
@@ -263,6 +275,26 @@ int gated_deltanet_prefill_backward(const void* q, const void* k, const void* v,
   linattn::BackwardArgs a{q, k, v, beta, S0, dO, dST, dq, dk_out, dv_out, dbeta, dS0, B, H, T, dk, dv, g, dg};
   return launch_rc(linattn::launch_delta_backward(dtype == LA_DTYPE_BF16, a, workspace,
                                                   static_cast<hipStream_t>(stream)));
+}
+
+size_t kda_prefill_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype) {
+  return kda_ws(B, H, T, dk, dv, dtype);
+}
+
+int kda_prefill_backward(const void* q, const void* k, const void* v, const void* beta, const void* g,
+                         const float* S0, const void* dO, const float* dST, void* dq, void* dk_out, void* dv_out,
+                         void* dbeta, void* dg, float* dS0, int B, int H, int T, int dk, int dv, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (T != 0 && (!q || !k || !v || !beta || !g || !dO || !dq || !dk_out || !dv_out || !dbeta || !dg))
+    return LA_ERR_NULL;
+  if (int rc = prefill_args_rc(dtype, B, H, T, dk, dv)) return rc;
+  if (dtype != LA_DTYPE_BF16) return LA_ERR_UNSUPPORTED_DIM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(dq) || !aligned16(dk_out) ||
+      !aligned16(dv_out))
+    return LA_ERR_ALIGN;
+  if (int rc = workspace_rc(kda_ws(B, H, T, dk, dv, dtype), workspace, workspace_bytes)) return rc;
+  linattn::BackwardArgs a{q, k, v, beta, S0, dO, dST, dq, dk_out, dv_out, dbeta, dS0, B, H, T, dk, dv, g, dg};
+  return launch_rc(linattn::launch_kda_backward(a, workspace, static_cast<hipStream_t>(stream)));
 }
 
 int deltanet_prologue(const void* q_in, const void* k_in, const void* beta_logits, void* q_out,

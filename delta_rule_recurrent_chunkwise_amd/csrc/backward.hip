@@ -501,14 +501,32 @@ __device__ __forceinline__ void st4_bf16(bf16_t* p, float a0, float a1, float a2
   *reinterpret_cast<uint2*>(p) = make_uint2(pack2(a0, a1), pack2(a2, a3));
 }
 
-template <int DK>
+// Per-key-channel gate (KDA): the gate pre-pass's tiles (Q~ = Gam Q,
+// K~ = Gam K, K^ = K / Gam, bf16 [chunk][64][dk]; Gam_C fp32 [chunk][dk], -1
+// for a chunk walked token by token, whose tiles hold the raw q, k, g) and
+// the gradient pass's outputs (dQ~, dK~, dK^ fp32 [chunk][64][dk], and the
+// gradient of each chunk's log-decay through the state it leaves, fp32
+// [chunk][dk]).
+struct KdaPtrs {
+  const bf16_t* qt;
+  const bf16_t* kt;
+  const bf16_t* kht;
+  const float* gc;
+  float* dqt;
+  float* dkt;
+  float* dkh;
+  float* cc;
+};
+
+template <int DK, bool KDA = false>
 struct TransLayout {
   static constexpr int LQ = DK + 16;  // rows of Q, K
   static constexpr int LT = kC + 16;  // rows of A and W^T (token columns permuted by tperm)
   static constexpr int LD = 20;       // fp32 rows of a diagonal block of L
   static constexpr int oQ = 0;
   static constexpr int oK = oQ + kC * LQ * 2;
-  static constexpr int oA = oK + kC * LQ * 2;
+  static constexpr int oKh = oK + kC * LQ * 2;                  // KDA: K^ (and, walked, g)
+  static constexpr int oA = oKh + (KDA ? kC * LQ * 2 : 0);
   static constexpr int oWt = oA + kC * LT * 2;
   static constexpr int oLo = oWt + DK * LT * 2;   // L_bj, b > j: bf16 [6][16][16], row-major
   static constexpr int oD = oLo + 6 * 256 * 2;    // D_b = (I + L_bb)^-1: bf16 [4][16][16]
@@ -537,14 +555,27 @@ constexpr int kTransThreads = 512;
 // exp(G)) K, P = W^T diag(exp(G_C - G)) K and R = diag(exp(G)) Q - A W, and
 // exp(G_C) of the chunk goes to gC; the chain then takes
 // dS <- exp(G_C) dS - P dS + R^T dO.
-template <int DK, bool GATE>
+// KDA (a decay per key channel; the tiles of the gate pre-pass): A =
+// tril(Q~ K^^T), L = tril(diag(beta) K~ K^^T, -1), W solves (I + L) W =
+// diag(beta) K~, P = W^T (K^ diag(Gam_C)) and R = Q~ - A W; the chain takes
+// dS <- diag(Gam_C) dS - P dS + R^T dO.  A chunk walked token by token gets
+// its transition from the recurrence itself: X <- (I - beta k k^T) diag(a) X
+// from X = I over its tokens (the delta rule with v = 0 and the identity as
+// the state), R_t = q_t^T X_t and P = -X^T, and its Gam_C marker makes the
+// chain use 0 for the decay, so that the chain's step is dS <- X^T dS + R^T dO
+// (with P = I - X^T and a decay of 1, dS - P dS would leave the bf16
+// rounding of the operand dS behind where X is small).
+template <int DK, bool GATE, bool KDA = false>
 __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, bf16_t* __restrict__ Pg,
-                                                                bf16_t* __restrict__ Rg, float* __restrict__ gC) {
-  typedef TransLayout<DK> LY;
+                                                                bf16_t* __restrict__ Rg, float* __restrict__ gC,
+                                                                KdaPtrs kp = KdaPtrs{}) {
+  static_assert(!(GATE && KDA), "one gate kind at a time");
+  typedef TransLayout<DK, KDA> LY;
   constexpr int NTH = kTransThreads, NW = NTH / 64, LQ = LY::LQ, LT = LY::LT, LD = LY::LD, NT = DK / 16;
   __shared__ __attribute__((aligned(16))) char smem[LY::total];
   bf16_t* sQ = reinterpret_cast<bf16_t*>(smem + LY::oQ);
   bf16_t* sK = reinterpret_cast<bf16_t*>(smem + LY::oK);
+  bf16_t* sKh = reinterpret_cast<bf16_t*>(smem + LY::oKh);
   bf16_t* sA = reinterpret_cast<bf16_t*>(smem + LY::oA);
   bf16_t* sWt = reinterpret_cast<bf16_t*>(smem + LY::oWt);
   bf16_t* sLo = reinterpret_cast<bf16_t*>(smem + LY::oLo);
@@ -562,15 +593,24 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
   const bf16_t* bth = reinterpret_cast<const bf16_t*>(a.beta) + (size_t)bh * Tn;
 
   // 1. staging (rows past the end as zeros); A starts cleared, as its tiles
-  // above the diagonal are read as zeros
+  // above the diagonal are read as zeros.  KDA: Q~, K~, K^ from the gate
+  // pre-pass (64 rows per chunk, zero past the end).
   constexpr int NV = kC * DK / 8, VPT = (NV + NTH - 1) / NTH;
-  u32x4 bq[VPT], bk[VPT];
+  u32x4 bq[VPT], bk[VPT], bkh[KDA ? VPT : 1];
+  const bool walked = KDA && kp.gc[chunk * DK] < 0.f;
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
     const int v = min(tid + NTH * j, NV - 1);
-    const size_t off = (size_t)(t0 + min(v / (DK / 8), nrow - 1)) * DK + (v % (DK / 8)) * 8;
-    bq[j] = *reinterpret_cast<const u32x4*>(qh + off);
-    bk[j] = *reinterpret_cast<const u32x4*>(kh + off);
+    if constexpr (KDA) {
+      const size_t off = chunk * kC * DK + (size_t)v * 8;
+      bq[j] = *reinterpret_cast<const u32x4*>(kp.qt + off);
+      bk[j] = *reinterpret_cast<const u32x4*>(kp.kt + off);
+      bkh[j] = *reinterpret_cast<const u32x4*>(kp.kht + off);
+    } else {
+      const size_t off = (size_t)(t0 + min(v / (DK / 8), nrow - 1)) * DK + (v % (DK / 8)) * 8;
+      bq[j] = *reinterpret_cast<const u32x4*>(qh + off);
+      bk[j] = *reinterpret_cast<const u32x4*>(kh + off);
+    }
   }
   const float bt = bf2f(bth[t0 + min(tid & 63, nrow - 1)]);
   const u32x4 z4 = {0u, 0u, 0u, 0u};
@@ -582,6 +622,7 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
     const int r = v / (DK / 8), c8 = (v % (DK / 8)) * 8;
     *reinterpret_cast<u32x4*>(sQ + r * LQ + c8) = r < nrow ? bq[j] : z4;
     *reinterpret_cast<u32x4*>(sK + r * LQ + c8) = r < nrow ? bk[j] : z4;
+    if constexpr (KDA) *reinterpret_cast<u32x4*>(sKh + r * LQ + c8) = r < nrow ? bkh[j] : z4;
   }
   if (tid < kC) sB[tid] = tid < nrow ? bt : 0.f;
   if constexpr (GATE) {
@@ -592,6 +633,77 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
     }
   }
   __syncthreads();
+  const size_t cb = (size_t)bh * nch + c;
+  bf16_t* Pc = Pg + cb * DK * DK;
+  bf16_t* Rc = Rg + cb * DK * kC;
+  if constexpr (KDA) {
+    if (walked) {  // uniform over the workgroup: the transition by the recurrence
+      bf16_t* sR = sA;  // R, rows of LQ, where A and W^T would be
+      if (wave < NT) {
+        const int col = 16 * wave + lc;
+        float x[NT][4];  // X[16 t + 4 lg + i][col]
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[t][i] = 16 * t + 4 * lg + i == col ? 1.f : 0.f;
+        for (int tau = 0; tau < kC; ++tau) {
+          float kk[NT][4], qq[NT][4];
+          float r = 0.f;
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const int o = tau * LQ + 16 * t + 4 * lg;
+            const uint2 kw = *reinterpret_cast<const uint2*>(sK + o);
+            const uint2 qw = *reinterpret_cast<const uint2*>(sQ + o);
+            const uint2 gw = *reinterpret_cast<const uint2*>(sKh + o);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t kx = i < 2 ? kw.x : kw.y, qx = i < 2 ? qw.x : qw.y, gx = i < 2 ? gw.x : gw.y;
+              const int sh = (i & 1) * 16;
+              kk[t][i] = bf2f((bf16_t)(kx >> sh));
+              qq[t][i] = bf2f((bf16_t)(qx >> sh));
+              x[t][i] *= __expf(bf2f((bf16_t)(gx >> sh)));
+              r += kk[t][i] * x[t][i];
+            }
+          }
+          r += __shfl_xor(r, 16);
+          r += __shfl_xor(r, 32);
+          const float u = -sB[tau] * r;  // v = 0
+          float o = 0.f;
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              x[t][i] += kk[t][i] * u;
+              o += qq[t][i] * x[t][i];
+            }
+          o += __shfl_xor(o, 16);
+          o += __shfl_xor(o, 32);
+          if (lg == 0) sR[tau * LQ + col] = f2bf(o);
+        }
+        // P = -X^T: lane (column col of X) writes row col of P, in the
+        // fragment order of the product path below
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          float pv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pv[i] = -x[t][i];
+          const size_t o = DK == 16 ? ((size_t)lc + 16 * lg) * 4
+                                    : (((size_t)wave * (DK / 32) + (t >> 1)) * 64 + lc + 16 * (2 * (t & 1) + (lg >> 1))) * 8 +
+                                          4 * (lg & 1);
+          st4_bf16(Pc + o, pv[0], pv[1], pv[2], pv[3]);
+        }
+      }
+      __syncthreads();
+      for (int jb = wave; jb < 4 * NT; jb += NW) {  // R^T, as below
+        const int rt = jb / NT, dt = jb - rt * NT;
+        float rv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rv[i] = bf2f(sR[(16 * rt + 4 * lg + i) * LQ + 16 * dt + lc]);
+        st4_bf16(Rc + (((size_t)dt * 2 + (rt >> 1)) * 64 + lc + 16 * lg) * 8 + 4 * (rt & 1), rv[0], rv[1], rv[2], rv[3]);
+      }
+      return;
+    }
+  }
 
   // 2. jobs 0..9: tiles (ti >= tj) of tril(Q K^T); 10..19: of L.  The
   // transposed products, so that a lane holds row 16 ti + lc and the four
@@ -601,7 +713,8 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
     const int t = isA ? jb : jb - 10;
     const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
     const int tj = t - ti * (ti + 1) / 2;
-    floatx4 acc = mm_rowrow_bf16(zero4(), sK + (16 * tj + lc) * LQ, (isA ? sQ : sK) + (16 * ti + lc) * LQ, DK, lane);
+    floatx4 acc = mm_rowrow_bf16(zero4(), (KDA ? sKh : sK) + (16 * tj + lc) * LQ, (isA ? sQ : sK) + (16 * ti + lc) * LQ,
+                                 DK, lane);
     const int r = 16 * ti + lc, c0 = 16 * tj + 4 * lg;
     if constexpr (GATE) {
 #pragma unroll
@@ -690,13 +803,25 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
     }
     __syncthreads();
   }
+  if constexpr (KDA) {  // K^ diag(Gam_C): P's operand
+    constexpr int NKV = kC * DK / 8;
+    const float* gcc = kp.gc + chunk * DK;
+    for (int v = tid; v < NKV; v += NTH) {
+      const int r = v / (DK / 8), c8 = (v % (DK / 8)) * 8;
+      u32x4* p = reinterpret_cast<u32x4*>(sKh + r * LQ + c8);
+      const u32x4 x = *p;
+      u32x4 y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        y[e] = pack2(gcc[c8 + 2 * e] * __uint_as_float(x[e] << 16), gcc[c8 + 2 * e + 1] * __uint_as_float(x[e] & 0xffff0000u));
+      *p = y;
+    }
+    __syncthreads();
+  }
 
   // 5. P (from P^T = K^T W: lane holds P[16 dt + lc][16 et + 4 lg + i]) and
   // R = Q - A W (lane holds R[16 rt + 4 lg + i][16 dt + lc]); A's row block rt
   // reaches tokens <= 16 rt + 15 only
-  const size_t cb = (size_t)bh * nch + c;
-  bf16_t* Pc = Pg + cb * DK * DK;
-  bf16_t* Rc = Rg + cb * DK * kC;
   constexpr int NPJ = NT * NT, NRJ = 4 * NT;
   for (int jb = wave; jb < NPJ + NRJ; jb += NW) {
     if (jb < NPJ) {
@@ -704,8 +829,8 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
       floatx4 acc = zero4();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        acc = mfma_k32(tok_frag(sK, LQ, 32 * kb, 16 * et, lane), ld_frag(sWt + (16 * dt + lc) * LT + 32 * kb + 8 * lg),
-                       acc);
+        acc = mfma_k32(tok_frag(KDA ? sKh : sK, LQ, 32 * kb, 16 * et, lane),
+                       ld_frag(sWt + (16 * dt + lc) * LT + 32 * kb + 8 * lg), acc);
       // P[16 dt + lc][16 et + 4 lg .. +3]: fragment (dt, et / 2), lane
       // lc + 16 (2 (et % 2) + lg / 2), half lg % 2
       const size_t o = DK == 16 ? ((size_t)dt * 64 + lc + 16 * lg) * 4
@@ -742,7 +867,10 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
 // order, so a wave's load is 1 KB contiguous) and dS^T, the dO slice read
 // from LDS (double buffered, one barrier per chunk).
 // GATE: dS <- exp(G_C) dS - P dS + R^T dO, exp(G_C) of each chunk from gC.
-template <int DK, int DVS, bool GATE>
+// KDA: dS <- diag(Gam_C) dS - P dS + R^T dO, Gam_C per key channel from gC
+// ([chunk][dk]; the marker -1 of a chunk walked token by token stands for 0,
+// its P being minus the transposed transition).
+template <int DK, int DVS, bool GATE, bool KDA = false>
 __global__ __launch_bounds__(DK * 4) void bwd_chain_mat(BackwardArgs a, const bf16_t* __restrict__ Pg,
                                                         const bf16_t* __restrict__ Rg, bf16_t* __restrict__ dSt,
                                                         const float* __restrict__ gC) {
@@ -763,10 +891,15 @@ __global__ __launch_bounds__(DK * 4) void bwd_chain_mat(BackwardArgs a, const bf
   // slots are indexed at compile time only
   u32x4 sp[NS][KP], sr[NS][2], so[NS][VPT];
   float sgc[NS];
+  floatx4 sgk[KDA ? NS : 1];  // KDA: Gam_C of this wave's four rows
   auto issue = [&](int x, auto slotc) {
     constexpr int S = decltype(slotc)::value;
     const size_t cb = (size_t)bh * nch + x;
     sgc[S] = GATE ? gC[cb] : 1.f;
+    if constexpr (KDA) {
+      const float4 g4 = *reinterpret_cast<const float4*>(gC + cb * DK + 16 * wave + 4 * lg);
+      sgk[S] = floatx4{g4.x, g4.y, g4.z, g4.w};
+    }
     // fragment (wave, kb) of P and of R^T: 64 lanes x 16 bytes, contiguous
 #pragma unroll
     for (int kb = 0; kb < KP; ++kb) {
@@ -869,8 +1002,14 @@ __global__ __launch_bounds__(DK * 4) void bwd_chain_mat(BackwardArgs a, const bf
 #pragma unroll
       for (int jt = 0; jt < NJ; ++jt) cr[jt] = mfma_k32(ra, fo[kb][jt], cr[jt]);
     }
+    if constexpr (KDA) {
+      const floatx4 gk = sgk[S][0] < 0.f ? floatx4{0.f, 0.f, 0.f, 0.f} : sgk[S];
 #pragma unroll
-    for (int jt = 0; jt < NJ; ++jt) st[jt] = (GATE ? sgc[S] * st[jt] : st[jt]) - cp[jt] + cr[jt];
+      for (int jt = 0; jt < NJ; ++jt) st[jt] = gk * st[jt] - cp[jt] + cr[jt];
+    } else {
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt) st[jt] = (GATE ? sgc[S] * st[jt] : st[jt]) - cp[jt] + cr[jt];
+    }
     // the next chunk's dS^T and dO slice go to the other buffers (past the
     // first chunk this writes unused data)
     put_dst(buf ^ 1);
@@ -911,7 +1050,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_chain_mat(BackwardArgs a, const bf
 //   E  stage S, dSn rows; dQ += dO S^T, dK += u dSn^T - diag(beta) dX S^T;
 //      write dQ, dK, dbeta
 // ---------------------------------------------------------------------------
-template <int DK, int DV, class E, bool GATE = false>
+template <int DK, int DV, class E, bool GATE = false, bool KDA = false>
 struct GradLayout {
   typedef typename E::T T;
   static constexpr int ES = (int)sizeof(T);
@@ -930,7 +1069,9 @@ struct GradLayout {
   static constexpr int oDB = oB + kC * 4;
   static constexpr int oG = oDB + kC * 4;   // gated: G_r
   static constexpr int oDG = oG + kC * 4;   // gated: the gradient of G_r
-  static constexpr int oW = oDG + kC * 4;  // phase-dependent work area
+  static constexpr int oGC = oDG + kC * 4;  // KDA: Gam_C per key channel
+  static constexpr int oCC = oGC + (KDA ? DK * 4 : 0);  // KDA: the chunk decay's gradient per channel
+  static constexpr int oW = oCC + (KDA ? DK * 4 : 0);  // phase-dependent work area
   // phases A, B
   static constexpr int aQ = oW, aK = aQ + ROWQ, aAt = aK + ROWQ, aTL = aAt + TRI;
   // bf16 inputs: T and T^T (bf16, formed by block substitution), A^T, the
@@ -939,13 +1080,17 @@ struct GradLayout {
   static constexpr int aT = aTL + FT, aTt = aT + TRI, aAtt = aTt + TRI;
   static constexpr int aLo = aAtt + TRI, aD = aLo + 6 * 256 * 2, aLd = aD + 4 * 256 * 2;
   static constexpr int endAB = ES == 2 ? aLd + 4 * 16 * 20 * 4 : aTL + FT;
+  // KDA (bf16): K^ where the fp32 T region would be
+  static constexpr int aKh = aTL;
+  static_assert(!KDA || (ES == 2 && ROWQ <= FT), "KDA: K^ must fit the unused fp32 T region");
   // phases C, D: dO, dA, dA^T, bL, bL^T, K^T; then Q^T where bL was
   static constexpr int cDO = oW, cDA = cDO + ROWV, cDAt = cDA + TRI, cBL = cDAt + TRI, cBLt = cBL + TRI;
   static constexpr int dKt = cBLt + TRI, dQt = cBL;
   static_assert(TQ <= 2 * TRI, "Q^T must fit where bL and its transpose were");
   // bf16: K and Q row-major after the four 64 x 64 tiles
   static constexpr int dKr = cBLt + TRI, dQr = dKr + ROWQ;
-  static constexpr int endCD = ES == 2 ? dQr + ROWQ : dKt + TQ;
+  static constexpr int dKtr = dQr + ROWQ;  // KDA: K~ row-major as well
+  static constexpr int endCD = ES == 2 ? dKtr + (KDA ? ROWQ : 0) : dKt + TQ;
   // phase E: dO (kept), S, dSn
   static constexpr int eS = cDA, eDS = eS + ST;
   static constexpr int endE = eDS + ST;
@@ -975,10 +1120,21 @@ struct GradLayout {
 // every term carries a decay and dg keeps its relative accuracy when the
 // decays are strong.  g_t enters G_r for r >= t of its own chunk only, so
 // dg_t = sum of dG_r over r >= t in the chunk.
-template <int DK, int DV, class E, bool GATE>
+// KDA (bf16; a decay per key channel, the gate pre-pass's tiles): with
+// dSn' = diag(Gam_C) dSn, the formulas above with Q~ for Q, K~ for K on the
+// left of K S and of L (and W), K^ on the right of A and L and in the state
+// update, and dSn' for dSn; the gradients of the three tiles are kept apart,
+//   dQ~ = dO S^T + dA K^,  dK~ = (b dL) K^ - diag(beta) dX S^T,
+//   dK^ = dA^T Q~ + (b dL)^T K~ + u dSn'^T,
+// and go to the workspace with <S_i + (K^^T u)_i, dSn'_i> per channel i (the
+// gradient of the chunk's log-decay through Gam_C); kda_combine forms dq,
+// dk and dg from them.  A chunk walked token by token is left to
+// kda_walk_grads.
+template <int DK, int DV, class E, bool GATE, bool KDA = false>
 __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const float* __restrict__ Sc,
-                                                     const float* __restrict__ dSc) {
-  typedef GradLayout<DK, DV, E, GATE> L;
+                                                     const float* __restrict__ dSc, KdaPtrs kp = KdaPtrs{}) {
+  static_assert(!(GATE && KDA), "one gate kind at a time");
+  typedef GradLayout<DK, DV, E, GATE, KDA> L;
   typedef typename E::T T;
   constexpr bool kBf16 = sizeof(T) == 2;
   constexpr int NTH = kGradThreads, NW = NTH / 64;
@@ -994,8 +1150,14 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
   float* sG = reinterpret_cast<float*>(smem + L::oG);
   float* sDG = reinterpret_cast<float*>(smem + L::oDG);
   T* sAg = reinterpret_cast<T*>(smem + L::oAg);  // gated: [10][16][16], tile t = ti (ti + 1) / 2 + tj
+  float* sGC = reinterpret_cast<float*>(smem + L::oGC);
+  float* sCC = reinterpret_cast<float*>(smem + L::oCC);
 
   const int chunk = blockIdx.x;  // over B * H * nch
+  if constexpr (KDA) {
+    static_assert(sizeof(typename E::T) == 2, "KDA gradients: bf16 only");
+    if (kp.gc[(size_t)chunk * DK] < 0.f) return;  // walked token by token (uniform)
+  }
   const int Tn = a.T, nch = (Tn + kC - 1) / kC;
   const int bh = chunk / nch, c = chunk - bh * nch;
   const int t0 = c * kC, nrow = min(kC, Tn - t0);
@@ -1023,8 +1185,20 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
   bf16_t* sLo = reinterpret_cast<bf16_t*>(smem + L::aLo);
   bf16_t* sD = reinterpret_cast<bf16_t*>(smem + L::aD);
   float* sLd = reinterpret_cast<float*>(smem + L::aLd);
-  stage_rows<E, DK, NTH>(qh, DK, t0, nrow, sQ, LQ, nullptr, 0, tid);
-  stage_rows<E, DK, NTH>(kh, DK, t0, nrow, sK, LQ, nullptr, 0, tid);
+  T* sKh = reinterpret_cast<T*>(smem + L::aKh);
+  const size_t tile0 = (size_t)chunk * kC * DK;  // KDA: this chunk's rows of the pre-pass tiles
+  if constexpr (KDA) {
+    stage_rows<E, DK, NTH>(reinterpret_cast<const T*>(kp.qt + tile0), DK, 0, nrow, sQ, LQ, nullptr, 0, tid);
+    stage_rows<E, DK, NTH>(reinterpret_cast<const T*>(kp.kt + tile0), DK, 0, nrow, sK, LQ, nullptr, 0, tid);
+    stage_rows<E, DK, NTH>(reinterpret_cast<const T*>(kp.kht + tile0), DK, 0, nrow, sKh, LQ, nullptr, 0, tid);
+    for (int i = tid; i < DK; i += NTH) {
+      sGC[i] = kp.gc[(size_t)chunk * DK + i];
+      sCC[i] = 0.f;
+    }
+  } else {
+    stage_rows<E, DK, NTH>(qh, DK, t0, nrow, sQ, LQ, nullptr, 0, tid);
+    stage_rows<E, DK, NTH>(kh, DK, t0, nrow, sK, LQ, nullptr, 0, tid);
+  }
   if (tid < kC) {
     sB[tid] = tid < nrow ? E::tof(bth[t0 + tid]) : 0.f;
     sDB[tid] = 0.f;
@@ -1048,8 +1222,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
     const int t = isA ? jb : jb - 10;
     const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
     const int tj = t - ti * (ti + 1) / 2;
-    floatx4 acc =
-        rowrow<kBf16>(zero4(), (isA ? sQ : sK) + (16 * ti + lc) * LQ, sK + (16 * tj + lc) * LQ, DK, lane);
+    floatx4 acc = rowrow<kBf16>(zero4(), (isA ? sQ : sK) + (16 * ti + lc) * LQ, (KDA ? sKh : sK) + (16 * tj + lc) * LQ,
+                                DK, lane);
     const int cc = 16 * tj + lc;
     if constexpr (GATE) {
 #pragma unroll
@@ -1152,6 +1326,19 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
         Sv[kt][3] = bf2f((bf16_t)(v.y >> 16));
       }
     }
+    if constexpr (KDA) {  // dSn' = diag(Gam_C) dSn; <S_i, dSn'_i> over this slice, per channel
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ch = 16 * kt + 4 * lg + i;
+          dSv[kt][i] *= sGC[ch];
+          float p = Sv[kt][i] * dSv[kt][i];
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) p += __shfl_xor(p, off, 16);
+          if (lc == 0) atomicAdd(&sCC[ch], p);
+        }
+    }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -1196,7 +1383,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
         ut[mt] = accB<kBf16>(zero4(), sTL + (16 * mt + lc) * LTL, xx, mt + 1, lane);
         d1 = accB_col<kBf16>(zero4(), sA + 16 * mt + lc, LKT, dOt, 4, lane);  // A^T dO
       }
-      floatx4 d2 = accB<kBf16>(zero4(), sK + (16 * mt + lc) * LQ, dSv, NKT, lane);
+      floatx4 d2 = accB<kBf16>(zero4(), (KDA ? sKh : sK) + (16 * mt + lc) * LQ, dSv, NKT, lane);
       if constexpr (GATE) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) d2[i] *= __expf(sG[63] - sG[16 * mt + 4 * lg + i]);
@@ -1370,7 +1557,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
 
   // ---- phase D: each wave owns output tiles id = wave + 4 n of the 4 x NKT grid ----
   constexpr int NTILE = 4 * NKT, NOWN = (NTILE + NW - 1) / NW;  // output tiles, per wave
-  floatx4 gq[NOWN], gk[NOWN];
+  floatx4 gq[NOWN], gk[NOWN], gkh[KDA ? NOWN : 1];  // KDA: dK~ in gk, dK^ in gkh
   if constexpr (kBf16) {
     // K and Q row-major; every product over tokens reads them (and dA,
     // diag(beta) dL) with the transpose read or against the permuted copies.
@@ -1378,8 +1565,18 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
     // columns 16 tk + 4 lg .. +3.
     bf16_t* sKr = reinterpret_cast<bf16_t*>(smem + L::dKr);
     bf16_t* sQr = reinterpret_cast<bf16_t*>(smem + L::dQr);
-    stage_rows<E, DK, NTH>(kh, DK, t0, nrow, reinterpret_cast<T*>(sKr), LQ, nullptr, 0, tid);
-    stage_rows<E, DK, NTH>(qh, DK, t0, nrow, reinterpret_cast<T*>(sQr), LQ, nullptr, 0, tid);
+    bf16_t* sKtr = reinterpret_cast<bf16_t*>(smem + L::dKtr);  // KDA: K~ (sKr holds K^, sQr Q~)
+    if constexpr (KDA) {
+      stage_rows<E, DK, NTH>(reinterpret_cast<const T*>(kp.kht + tile0), DK, 0, nrow, reinterpret_cast<T*>(sKr), LQ,
+                             nullptr, 0, tid);
+      stage_rows<E, DK, NTH>(reinterpret_cast<const T*>(kp.qt + tile0), DK, 0, nrow, reinterpret_cast<T*>(sQr), LQ,
+                             nullptr, 0, tid);
+      stage_rows<E, DK, NTH>(reinterpret_cast<const T*>(kp.kt + tile0), DK, 0, nrow, reinterpret_cast<T*>(sKtr), LQ,
+                             nullptr, 0, tid);
+    } else {
+      stage_rows<E, DK, NTH>(kh, DK, t0, nrow, reinterpret_cast<T*>(sKr), LQ, nullptr, 0, tid);
+      stage_rows<E, DK, NTH>(qh, DK, t0, nrow, reinterpret_cast<T*>(sQr), LQ, nullptr, 0, tid);
+    }
     __syncthreads();
     const bf16_t* bDA = reinterpret_cast<const bf16_t*>(sDA);
     const bf16_t* bDAp = reinterpret_cast<const bf16_t*>(sDAt);
@@ -1396,10 +1593,15 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
         const bf16x8 kf = tok_frag(sKr, LQ, 32 * kb, 16 * tk, lane);
         xq = mfma_k32(kf, ld_frag(bDAp + (16 * ti + lc) * LKT + 32 * kb + 8 * lg), xq);           // dA K
         xk = mfma_k32(kf, ld_frag(bBLp + (16 * ti + lc) * LKT + 32 * kb + 8 * lg), xk);           // (b dL) K
-        if constexpr (GATE) xb = mfma_k32(kf, tok_frag(bBL, LKT, 32 * kb, 16 * ti, lane), xb);    // (b dL)^T K
-        else xk = mfma_k32(kf, tok_frag(bBL, LKT, 32 * kb, 16 * ti, lane), xk);
+        if constexpr (KDA) {
+          xb = mfma_k32(tok_frag(sKtr, LQ, 32 * kb, 16 * tk, lane), tok_frag(bBL, LKT, 32 * kb, 16 * ti, lane), xb);
+        } else if constexpr (GATE) {
+          xb = mfma_k32(kf, tok_frag(bBL, LKT, 32 * kb, 16 * ti, lane), xb);  // (b dL)^T K
+        } else {
+          xk = mfma_k32(kf, tok_frag(bBL, LKT, 32 * kb, 16 * ti, lane), xk);
+        }
         const bf16x8 qf = tok_frag(sQr, LQ, 32 * kb, 16 * tk, lane), af = tok_frag(bDA, LKT, 32 * kb, 16 * ti, lane);
-        if constexpr (GATE) xc = mfma_k32(qf, af, xc);  // dA^T Q
+        if constexpr (GATE || KDA) xc = mfma_k32(qf, af, xc);  // dA^T Q
         else xk = mfma_k32(qf, af, xk);
       }
       if constexpr (GATE) {  // k_r . (bL K - bL^T K)_r, four columns per lane
@@ -1414,6 +1616,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
       }
       gq[n] = xq;
       gk[n] = xk;
+      if constexpr (KDA) gkh[n] = xb + xc;
     }
     __syncthreads();
   } else {
@@ -1474,6 +1677,11 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
       const int o = (16 * kt + 4 * (ln >> 4)) * LS + 16 * jt + (ln & 15);
       bf16_t* ps = reinterpret_cast<bf16_t*>(sS) + o;
       bf16_t* pd = reinterpret_cast<bf16_t*>(sDS) + o;
+      if constexpr (KDA) {  // dSn' = diag(Gam_C) dSn: rows are key channels
+        const float* gr = sGC + 16 * kt + 4 * (ln >> 4);
+        bd[j] = make_uint2(pack2(gr[0] * bf2f((bf16_t)(bd[j].x & 0xffffu)), gr[1] * bf2f((bf16_t)(bd[j].x >> 16))),
+                           pack2(gr[2] * bf2f((bf16_t)(bd[j].y & 0xffffu)), gr[3] * bf2f((bf16_t)(bd[j].y >> 16))));
+      }
       ps[0] = (bf16_t)(bs[j].x & 0xffffu); ps[LS] = (bf16_t)(bs[j].x >> 16);
       ps[2 * LS] = (bf16_t)(bs[j].y & 0xffffu); ps[3 * LS] = (bf16_t)(bs[j].y >> 16);
       pd[0] = (bf16_t)(bd[j].x & 0xffffu); pd[LS] = (bf16_t)(bd[j].x >> 16);
@@ -1512,6 +1720,32 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
       const floatx4 k2 = rowrow<kBf16>(zero4(), sS + (16 * tk + lc) * LS, sDX + (16 * ti + lc) * LV, DV, lane);
       const int r = 16 * ti + lc, d0 = 16 * tk + 4 * lg;
       const float br = sB[r];
+      if constexpr (KDA) {
+        // dQ~, dK~, dK^ (fp32, rows of this chunk's tiles) for kda_combine;
+        // sum over tokens of K^ * (u dSn'^T) per channel for the decay's gradient
+        float p[4] = {0.f, 0.f, 0.f, 0.f};
+        if (r < nrow) {
+          const uint2 w = *reinterpret_cast<const uint2*>(kp.kht + tile0 + (size_t)r * DK + d0);
+          p[0] = bf2f((bf16_t)(w.x & 0xffffu)) * k1[0];
+          p[1] = bf2f((bf16_t)(w.x >> 16)) * k1[1];
+          p[2] = bf2f((bf16_t)(w.y & 0xffffu)) * k1[2];
+          p[3] = bf2f((bf16_t)(w.y >> 16)) * k1[3];
+          const size_t o = tile0 + (size_t)r * DK + d0;
+          *reinterpret_cast<float4*>(kp.dqt + o) =
+              make_float4(gq[n][0] + q1[0], gq[n][1] + q1[1], gq[n][2] + q1[2], gq[n][3] + q1[3]);
+          *reinterpret_cast<float4*>(kp.dkt + o) = make_float4(gk[n][0] - br * k2[0], gk[n][1] - br * k2[1],
+                                                               gk[n][2] - br * k2[2], gk[n][3] - br * k2[3]);
+          *reinterpret_cast<float4*>(kp.dkh + o) =
+              make_float4(gkh[n][0] + k1[0], gkh[n][1] + k1[1], gkh[n][2] + k1[2], gkh[n][3] + k1[3]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) p[i] += __shfl_xor(p[i], off, 16);
+          if (lc == 0) atomicAdd(&sCC[d0 + i], p[i]);
+        }
+        continue;
+      }
       // gated: dO S^T and beta dX S^T times exp(G_r), u dSn^T times exp(G_C - G_r)
       const float e1 = GATE ? __expf(sG[r]) : 1.f, e2 = GATE ? __expf(sG[63] - sG[r]) : 1.f;
       float dq4[4], dk4[4];
@@ -1581,6 +1815,10 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
     }
   }
   if (tid < nrow) reinterpret_cast<T*>(a.dbeta)[(size_t)bh * Tn + t0 + tid] = E::cvt(sDB[tid]);
+  if constexpr (KDA) {
+    __syncthreads();
+    for (int i = tid; i < DK; i += NTH) kp.cc[(size_t)chunk * DK + i] = sCC[i];
+  }
   if constexpr (GATE) {  // dg_t: the sums of dG_r over r >= t in the chunk
     __syncthreads();
     if (wave == 0) {
@@ -1592,6 +1830,256 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
       }
       if (lane < nrow) reinterpret_cast<T*>(a.dg)[(size_t)bh * Tn + t0 + lane] = E::cvt(x);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// KDA: dq, dk and dg of a chunk in the factored form from the gradients of
+// its tiles.  With G_t the log-decay summed from the chunk start (per key
+// channel, fp32, from g as the pre-pass forms it), Q~ = e^G q, K~ = e^G k,
+// K^ = e^-G k and Gam_C = e^(G_C):
+//   dq = e^G dQ~,  dk = e^G dK~ + e^-G dK^,
+//   dG_t = q e^G dQ~ + k e^G dK~ - k e^-G dK^ (elementwise), plus, on the
+//   chunk's last row, the decay's gradient through Gam_C from the gradient
+//   pass;
+// g_t enters G_r for r >= t of its own chunk only, so dg_t = sum of dG_r over
+// r >= t in the chunk.  One workgroup of 256 threads per chunk, thread (w, l)
+// on channels 2l, 2l+1 of TPS consecutive rows, as in the pre-pass; a chunk
+// walked token by token is left to kda_walk_grads.
+// ---------------------------------------------------------------------------
+template <int DK>
+__global__ __launch_bounds__(256) void kda_combine(BackwardArgs a, KdaPtrs kp) {
+  constexpr int NCOL = DK / 2, NSEG = 256 / NCOL, TPS = kC / NSEG;
+  __shared__ float2 part[NSEG][NCOL];
+  const int chunk = blockIdx.x;
+  if (kp.gc[(size_t)chunk * DK] < 0.f) return;  // walked (uniform)
+  const int Tn = a.T, nch = (Tn + kC - 1) / kC;
+  const int bh = chunk / nch, t0 = (chunk - bh * nch) * kC, nrow = min(kC, Tn - t0);
+  const int w = threadIdx.x / NCOL, l = threadIdx.x % NCOL;
+  const size_t ib = ((size_t)bh * Tn + t0) * DK;   // raw inputs and outputs
+  const size_t tb = (size_t)chunk * kC * DK;       // the tiles' gradients
+  const uint32_t* g2 = reinterpret_cast<const uint32_t*>(reinterpret_cast<const bf16_t*>(a.g) + ib);
+  float2 G[TPS];
+  float2 run = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int t = 0; t < TPS; ++t) {
+    const int r = TPS * w + t;
+    const uint32_t gv = r < nrow ? g2[r * NCOL + l] : 0u;
+    run.x += bf2f((bf16_t)(gv & 0xffffu));
+    run.y += bf2f((bf16_t)(gv >> 16));
+    G[t] = run;
+  }
+  part[w][l] = run;
+  __syncthreads();
+  float2 off = make_float2(0.f, 0.f);
+  for (int p = 0; p < w; ++p) {
+    off.x += part[p][l].x;
+    off.y += part[p][l].y;
+  }
+  __syncthreads();
+  const uint32_t* q2 = reinterpret_cast<const uint32_t*>(reinterpret_cast<const bf16_t*>(a.q) + ib);
+  const uint32_t* k2 = reinterpret_cast<const uint32_t*>(reinterpret_cast<const bf16_t*>(a.k) + ib);
+  uint32_t* dq2 = reinterpret_cast<uint32_t*>(reinterpret_cast<bf16_t*>(a.dq) + ib);
+  uint32_t* dk2 = reinterpret_cast<uint32_t*>(reinterpret_cast<bf16_t*>(a.dk) + ib);
+  uint32_t* dg2 = reinterpret_cast<uint32_t*>(reinterpret_cast<bf16_t*>(a.dg) + ib);
+  const float2 cc = reinterpret_cast<const float2*>(kp.cc + (size_t)chunk * DK)[l];
+  float2 dG[TPS];
+#pragma unroll
+  for (int t = 0; t < TPS; ++t) {
+    const int r = TPS * w + t;
+    dG[t] = make_float2(0.f, 0.f);
+    if (r >= nrow) continue;
+    const float G0 = off.x + G[t].x, G1 = off.y + G[t].y;
+    const float e0 = __expf(G0), e1 = __expf(G1), i0 = __expf(-G0), i1 = __expf(-G1);
+    const uint32_t qw = q2[r * NCOL + l], kw = k2[r * NCOL + l];
+    const float q0 = bf2f((bf16_t)(qw & 0xffffu)), q1 = bf2f((bf16_t)(qw >> 16));
+    const float k0 = bf2f((bf16_t)(kw & 0xffffu)), k1 = bf2f((bf16_t)(kw >> 16));
+    const float2 a1 = reinterpret_cast<const float2*>(kp.dqt + tb)[r * NCOL + l];
+    const float2 b1 = reinterpret_cast<const float2*>(kp.dkt + tb)[r * NCOL + l];
+    const float2 c1 = reinterpret_cast<const float2*>(kp.dkh + tb)[r * NCOL + l];
+    dq2[r * NCOL + l] = pack2(e0 * a1.x, e1 * a1.y);
+    dk2[r * NCOL + l] = pack2(e0 * b1.x + i0 * c1.x, e1 * b1.y + i1 * c1.y);
+    dG[t].x = q0 * e0 * a1.x + k0 * e0 * b1.x - k0 * i0 * c1.x;
+    dG[t].y = q1 * e1 * a1.y + k1 * e1 * b1.y - k1 * i1 * c1.y;
+    if (r == nrow - 1) {
+      dG[t].x += cc.x;
+      dG[t].y += cc.y;
+    }
+  }
+  // suffix sums: within the thread's rows, then the later row groups' totals
+  float2 suf = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int t = TPS - 1; t >= 0; --t) {
+    suf.x += dG[t].x;
+    suf.y += dG[t].y;
+    dG[t] = suf;
+  }
+  part[w][l] = suf;
+  __syncthreads();
+  float2 later = make_float2(0.f, 0.f);
+  for (int p = w + 1; p < NSEG; ++p) {
+    later.x += part[p][l].x;
+    later.y += part[p][l].y;
+  }
+#pragma unroll
+  for (int t = 0; t < TPS; ++t) {
+    const int r = TPS * w + t;
+    if (r < nrow) dg2[r * NCOL + l] = pack2(dG[t].x + later.x, dG[t].y + later.y);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// KDA, a chunk whose decay leaves the factored form's range: the gradients
+// by the recurrence itself, token by token and backwards.  Per token t, with
+// S' = diag(a_t) S_{t-1}, r = S'^T k_t, u = beta_t (v_t - r),
+// S_t = S' + k_t u^T, o_t = S_t^T q_t, and dS the gradient of S_t from the
+// tokens after it (dSn for the chunk's last token):
+//   dS += q_t dO_t^T;  dq_t = S_t dO_t;  du = dS^T k_t;
+//   dk_t = dS u - beta_t S' du;  dv_t = beta_t du;  dbeta_t = du . (v_t - r);
+//   dS' = dS - beta_t k_t du^T;  dg_t = rowsum(dS' * S');  dS <- diag(a_t) dS'.
+// S_{t-1} is formed again from the chunk's entry state for every t (64
+// dependent steps at most, no per-token states kept).  One workgroup per
+// chunk; wave w < dv/16 holds 16 value columns of S and dS (rows 16 kt +
+// 4 lg + i, column 16 w + lc); the sums over value columns go through LDS.
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ __launch_bounds__(512) void kda_walk_grads(BackwardArgs a, const bf16_t* __restrict__ Sc,
+                                                      const bf16_t* __restrict__ dSc, KdaPtrs kp) {
+  constexpr int NKT = DK / 16, NVW = DV / 16, LQ = DK + 8, LV = DV + 8, NRED = 3 * DK + 1;
+  __shared__ __attribute__((aligned(16))) bf16_t sq[kC][LQ];
+  __shared__ __attribute__((aligned(16))) bf16_t sk[kC][LQ];
+  __shared__ __attribute__((aligned(16))) float sa[kC][DK];  // e^g
+  __shared__ __attribute__((aligned(16))) bf16_t sv[kC][LV];
+  __shared__ __attribute__((aligned(16))) bf16_t sdo[kC][LV];
+  __shared__ float sb[kC];
+  __shared__ float red[NVW][NRED];
+  const size_t chunk = blockIdx.x;
+  if (!(kp.gc[chunk * DK] < 0.f)) return;  // factored chunks are done elsewhere (uniform)
+  const int Tn = a.T, nch = (Tn + kC - 1) / kC;
+  const int bh = (int)(chunk / nch), t0 = (int)(chunk - (size_t)bh * nch) * kC, nrow = min(kC, Tn - t0);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
+  // stage the chunk: raw q, k, g from the pre-pass's slots (zero past the end)
+  const size_t tb = chunk * kC * DK;
+  for (int i = tid; i < kC * DK; i += 512) {
+    const int r = i / DK, d = i - r * DK;
+    sq[r][d] = kp.qt[tb + i];
+    sk[r][d] = kp.kt[tb + i];
+    sa[r][d] = __expf(bf2f(kp.kht[tb + i]));
+  }
+  const bf16_t* vh = reinterpret_cast<const bf16_t*>(a.v) + ((size_t)bh * Tn + t0) * DV;
+  const bf16_t* doh = reinterpret_cast<const bf16_t*>(a.dO) + ((size_t)bh * Tn + t0) * DV;
+  for (int i = tid; i < kC * DV; i += 512) {
+    const int r = i / DV, d = i - r * DV;
+    sv[r][d] = r < nrow ? vh[(size_t)r * DV + d] : f2bf(0.f);
+    sdo[r][d] = r < nrow ? doh[(size_t)r * DV + d] : f2bf(0.f);
+  }
+  if (tid < kC) sb[tid] = tid < nrow ? bf2f(reinterpret_cast<const bf16_t*>(a.beta)[(size_t)bh * Tn + t0 + tid]) : 0.f;
+  __syncthreads();
+  const bool act = wave < NVW;
+  const int col = 16 * wave + lc;
+  float s0[NKT][4], ds[NKT][4];  // entry state and the running gradient (tile order in Sc, dSc)
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt) {
+    const size_t o = chunk * DK * DV + ((size_t)kt * NVW + (act ? wave : 0)) * 256 + 4 * lane;
+    const uint2 w0 = *reinterpret_cast<const uint2*>(Sc + o);
+    const uint2 w1 = *reinterpret_cast<const uint2*>(dSc + o);
+    s0[kt][0] = bf2f((bf16_t)(w0.x & 0xffffu));
+    s0[kt][1] = bf2f((bf16_t)(w0.x >> 16));
+    s0[kt][2] = bf2f((bf16_t)(w0.y & 0xffffu));
+    s0[kt][3] = bf2f((bf16_t)(w0.y >> 16));
+    ds[kt][0] = bf2f((bf16_t)(w1.x & 0xffffu));
+    ds[kt][1] = bf2f((bf16_t)(w1.x >> 16));
+    ds[kt][2] = bf2f((bf16_t)(w1.y & 0xffffu));
+    ds[kt][3] = bf2f((bf16_t)(w1.y >> 16));
+  }
+  // one forward step of token tau on x (a wave's 16 columns); returns r and
+  // leaves S' in sp when asked
+  auto step = [&](float (&x)[NKT][4], int tau, float (*sp)[4]) {
+    float r = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ch = 16 * kt + 4 * lg + i;
+        x[kt][i] *= sa[tau][ch];
+        if (sp) sp[kt][i] = x[kt][i];
+        r += bf2f(sk[tau][ch]) * x[kt][i];
+      }
+    r += __shfl_xor(r, 16);
+    r += __shfl_xor(r, 32);
+    const float u = sb[tau] * (bf2f(sv[tau][col]) - r);
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[kt][i] += bf2f(sk[tau][16 * kt + 4 * lg + i]) * u;
+    return r;
+  };
+  bf16_t* dqo = reinterpret_cast<bf16_t*>(a.dq) + ((size_t)bh * Tn + t0) * DK;
+  bf16_t* dko = reinterpret_cast<bf16_t*>(a.dk) + ((size_t)bh * Tn + t0) * DK;
+  bf16_t* dgo = reinterpret_cast<bf16_t*>(a.dg) + ((size_t)bh * Tn + t0) * DK;
+  bf16_t* dvo = reinterpret_cast<bf16_t*>(a.dv) + ((size_t)bh * Tn + t0) * DV;
+  for (int tau = nrow - 1; tau >= 0; --tau) {
+    if (act) {
+      float x[NKT][4], sp[NKT][4];
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[kt][i] = s0[kt][i];
+      for (int s2 = 0; s2 < tau; ++s2) step(x, s2, nullptr);
+      const float r = step(x, tau, sp);  // x = S_tau, sp = S'
+      const float u = sb[tau] * (bf2f(sv[tau][col]) - r);
+      const float dOj = bf2f(sdo[tau][col]);
+      float du = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ch = 16 * kt + 4 * lg + i;
+          ds[kt][i] += bf2f(sq[tau][ch]) * dOj;
+          du += bf2f(sk[tau][ch]) * ds[kt][i];
+        }
+      du += __shfl_xor(du, 16);
+      du += __shfl_xor(du, 32);
+      const float bt = sb[tau];
+      if (lg == 0) dvo[(size_t)tau * DV + col] = f2bf(bt * du);
+      float pb = lg == 0 ? du * (bf2f(sv[tau][col]) - r) : 0.f;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) pb += __shfl_xor(pb, off, 16);
+      if (lane == 0) red[wave][3 * DK] = pb;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ch = 16 * kt + 4 * lg + i;
+          float pk = ds[kt][i] * u - bt * sp[kt][i] * du;               // dk partial
+          const float dsp = ds[kt][i] - bt * bf2f(sk[tau][ch]) * du;    // dS'
+          float pg = dsp * sp[kt][i];                                   // dg partial
+          float p1 = x[kt][i] * dOj;                                    // dq partial
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) {
+            p1 += __shfl_xor(p1, off, 16);
+            pk += __shfl_xor(pk, off, 16);
+            pg += __shfl_xor(pg, off, 16);
+          }
+          if (lc == 0) {
+            red[wave][ch] = p1;
+            red[wave][DK + ch] = pk;
+            red[wave][2 * DK + ch] = pg;
+          }
+          ds[kt][i] = sa[tau][ch] * dsp;
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < NRED; i += 512) {
+      float t = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < NVW; ++w2) t += red[w2][i];
+      if (i < DK) dqo[(size_t)tau * DK + i] = f2bf(t);
+      else if (i < 2 * DK) dko[(size_t)tau * DK + i - DK] = f2bf(t);
+      else if (i < 3 * DK) dgo[(size_t)tau * DK + i - 2 * DK] = f2bf(t);
+      else reinterpret_cast<bf16_t*>(a.dbeta)[(size_t)bh * Tn + t0 + tau] = f2bf(t);
+    }
+    __syncthreads();
   }
 }
 
@@ -1680,6 +2168,52 @@ hipError_t launch_backward_e(const BackwardArgs& a, float* Sc, float* dSc, bf16_
   }
 }
 
+// KDA (bf16): the transition and chain with a decay per key channel, then
+// the gradients (factored chunks: bwd_grads and kda_combine; walked chunks:
+// kda_walk_grads; each kernel leaves the other kind of chunk alone)
+template <int DK, int DV>
+hipError_t launch_kda_grads(const BackwardArgs& a, const bf16_t* Sc, const bf16_t* dSt, const KdaPtrs& kp,
+                            long nchunks, hipStream_t st) {
+  static_assert(GradLayout<DK, DV, BF16, false, true>::total <= 160 * 1024,
+                "backward gradient kernel exceeds the LDS of a CU");
+  hipLaunchKernelGGL((bwd_grads<DK, DV, BF16, false, true>), dim3((unsigned)nchunks), dim3(kGradThreads), 0, st, a,
+                     reinterpret_cast<const float*>(Sc), reinterpret_cast<const float*>(dSt), kp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((kda_walk_grads<DK, DV>), dim3((unsigned)nchunks), dim3(512), 0, st, a, Sc, dSt, kp);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((kda_combine<DK>), dim3((unsigned)nchunks), dim3(256), 0, st, a, kp);
+  return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_kda_passes(const BackwardArgs& a, const bf16_t* Sc, bf16_t* dSt, bf16_t* Pg, bf16_t* Rg,
+                             const KdaPtrs& kp, hipStream_t st) {
+  static_assert(TransLayout<DK, true>::total <= 160 * 1024, "transition kernel exceeds the LDS of a CU");
+  const long nchunks = (long)a.B * a.H * ((a.T + kC - 1) / kC);
+  hipLaunchKernelGGL((bwd_transition<DK, false, true>), dim3((unsigned)nchunks), dim3(kTransThreads), 0, st, a, Pg, Rg,
+                     static_cast<float*>(nullptr), kp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long bh = (long)a.B * a.H;
+  if (a.dv_ % 32 == 0)
+    hipLaunchKernelGGL((bwd_chain_mat<DK, 32, false, true>), dim3((unsigned)(bh * (a.dv_ / 32))), dim3(DK * 4), 0, st,
+                       a, Pg, Rg, dSt, kp.gc);
+  else
+    hipLaunchKernelGGL((bwd_chain_mat<DK, 16, false, true>), dim3((unsigned)(bh * (a.dv_ / 16))), dim3(DK * 4), 0, st,
+                       a, Pg, Rg, dSt, kp.gc);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (a.dv_) {
+    case 16: return launch_kda_grads<DK, 16>(a, Sc, dSt, kp, nchunks, st);
+    case 32: return launch_kda_grads<DK, 32>(a, Sc, dSt, kp, nchunks, st);
+    case 64: return launch_kda_grads<DK, 64>(a, Sc, dSt, kp, nchunks, st);
+    case 128: return launch_kda_grads<DK, 128>(a, Sc, dSt, kp, nchunks, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 __global__ __launch_bounds__(256) void zero_state(float* __restrict__ p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0.f;
 }
@@ -1742,6 +2276,69 @@ hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, void* workspac
                : launch_backward_e<F32, false>(a, Sc, dSc, Pg, Rg, gC, st);
   }
   return e;
+}
+
+// Workspace layout: see kda_backward_workspace_bytes (launch.hpp).
+hipError_t launch_kda_backward(const BackwardArgs& a, void* workspace, hipStream_t st) {
+  if (a.T == 0) {  // no tokens: the state's gradient passes through
+    if (!a.dS0) return hipSuccess;
+    const size_t n = (size_t)a.B * a.H * a.dk_ * a.dv_;
+    if (a.dST) return hipMemcpyAsync(a.dS0, a.dST, n * sizeof(float), hipMemcpyDeviceToDevice, st);
+    const size_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+    hipLaunchKernelGGL(zero_state, dim3((unsigned)blocks), dim3(256), 0, st, a.dS0, n);
+    return hipGetLastError();
+  }
+  const size_t nchunks = workspace_chunks(a.B, a.H, a.T);
+  const size_t ntile = nchunks * kC * a.dk_;
+  char* ws = static_cast<char*>(workspace);
+  char* prep = ws;
+  ws += workspace_round256(gate_prep_bytes(a.dk_, a.B, a.H, a.T));
+  bf16_t* Sc = reinterpret_cast<bf16_t*>(ws);
+  ws += workspace_round256(nchunks * a.dk_ * a.dv_ * sizeof(bf16_t));
+  bf16_t* dSt = reinterpret_cast<bf16_t*>(ws);
+  ws += workspace_round256(nchunks * a.dk_ * a.dv_ * sizeof(bf16_t));
+  bf16_t* Pg = reinterpret_cast<bf16_t*>(ws);
+  bf16_t* Rg = Pg + nchunks * a.dk_ * a.dk_;
+  ws += workspace_round256(nchunks * a.dk_ * (a.dk_ + 64) * sizeof(bf16_t));
+  float* dqt = reinterpret_cast<float*>(ws);
+  KdaPtrs kp{};
+  kp.qt = reinterpret_cast<const bf16_t*>(prep);
+  kp.kt = kp.qt + ntile;
+  kp.kht = kp.kt + ntile;
+  kp.gc = reinterpret_cast<const float*>(kp.kht + ntile);
+  kp.dqt = dqt;
+  kp.dkt = dqt + ntile;
+  kp.dkh = dqt + 2 * ntile;
+  kp.cc = dqt + 3 * ntile;
+  // the gate pre-pass, then pass 1: the state entering every chunk (no
+  // output, no final state; S0 is only read)
+  PrefillArgs f{};
+  f.q = a.q;
+  f.k = a.k;
+  f.v = a.v;
+  f.beta = a.beta;
+  f.g = a.g;
+  f.S = const_cast<float*>(a.S0);
+  f.B = a.B;
+  f.H = a.H;
+  f.T = a.T;
+  f.dv = a.dv_;
+  f.use_init = a.S0 != nullptr;
+  f.Sc = reinterpret_cast<float*>(Sc);
+  hipError_t e = launch_gate_prep(a.dk_, f, prep, st);
+  if (e != hipSuccess) return e;
+  if (a.dk_ == 128 && a.dv_ % 32 == 0)
+    e = launch_prefill_pipe_prepped(f, prep, st);
+  else
+    e = launch_prefill_generic(PF_GATED, 1, a.dk_, f, st);
+  if (e != hipSuccess) return e;
+  switch (a.dk_) {
+    case 16: return launch_kda_passes<16>(a, Sc, dSt, Pg, Rg, kp, st);
+    case 32: return launch_kda_passes<32>(a, Sc, dSt, Pg, Rg, kp, st);
+    case 64: return launch_kda_passes<64>(a, Sc, dSt, Pg, Rg, kp, st);
+    case 128: return launch_kda_passes<128>(a, Sc, dSt, Pg, Rg, kp, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace linattn

@@ -73,6 +73,9 @@ struct BackwardArgs {
   void* dg;          // its gradient [B,H,T] (with g)
 };
 hipError_t launch_delta_backward(int bf16, const BackwardArgs& a, void* workspace, hipStream_t st);
+// Gradient of the per-key-channel gated rule (bf16; a.g [B,H,T,dk], a.dg
+// likewise): see kda_prefill_backward.
+hipError_t launch_kda_backward(const BackwardArgs& a, void* workspace, hipStream_t st);
 // The layer prologue (prologue.hip): see deltanet_prologue.
 struct PrologueArgs {
   const void* q_in;
@@ -89,6 +92,15 @@ hipError_t launch_prologue(int bf16, const PrologueArgs& a, hipStream_t st);
 // plain (a.g == NULL, no workspace) or gated (needs a workspace of
 // gated_pipe_workspace_bytes(a) bytes).
 hipError_t launch_prefill_pipe(const PrefillArgs& a, void* workspace, hipStream_t st);
+// The per-key-channel gate pre-pass (bf16, dk in {16, 32, 64, 128}): for
+// n = B*H*ceil(T/64) chunks, Gam Q, Gam K, K / Gam as bf16 [n][64][dk] each,
+// then Gam_C as fp32 [n][dk], into `workspace` (gate_prep_bytes); Gam_C = -1
+// in every channel marks a chunk whose decay leaves the factored form's
+// range, whose three tiles then hold the raw q, k and g.
+hipError_t launch_gate_prep(int dk, const PrefillArgs& a, void* workspace, hipStream_t st);
+// The pipelined gated kernel (dk = 128) on the pre-pass's output `prep`; with
+// a.Sc set it captures the chunk states (and writes neither o nor S).
+hipError_t launch_prefill_pipe_prepped(const PrefillArgs& a, const void* prep, hipStream_t st);
 // ... and with one decay per token (a.g [B,H,T]; no workspace).
 hipError_t launch_prefill_pipe_token(const PrefillArgs& a, hipStream_t st);
 
@@ -114,12 +126,13 @@ inline size_t la_par_workspace_bytes(int dk, const PrefillArgs& a) {
   return n * ((size_t)dk * a.dv + dk) * sizeof(float) + n * dk * a.dv * sizeof(uint16_t);
 }
 
-// Per-channel gate pre-pass (dk = 128): Gam Q, Gam K, K / Gam in bf16 (64 rows
-// per chunk) and Gam_C in fp32.
-inline size_t gated_pipe_workspace_bytes(const PrefillArgs& a) {
-  const size_t n = workspace_chunks(a.B, a.H, a.T);
-  return 3 * n * 64 * 128 * sizeof(uint16_t) + n * 128 * sizeof(float);
+// Per-channel gate pre-pass: Gam Q, Gam K, K / Gam in bf16 (64 rows per
+// chunk) and Gam_C in fp32.
+inline size_t gate_prep_bytes(int dk, long B, long H, long T) {
+  const size_t n = workspace_chunks(B, H, T);
+  return 3 * n * 64 * dk * sizeof(uint16_t) + n * dk * sizeof(float);
 }
+inline size_t gated_pipe_workspace_bytes(const PrefillArgs& a) { return gate_prep_bytes(128, a.B, a.H, a.T); }
 
 // Device memory a prefill needs beyond its inputs and outputs (0 for most
 // paths): the chunk-parallel bf16 linear-attention kernels keep per-chunk
@@ -143,6 +156,22 @@ inline size_t delta_backward_workspace_bytes(int bf16, const BackwardArgs& a) {
   size_t w = 2 * workspace_round256(n * a.dk_ * a.dv_ * sizeof(float));
   if (a.g) w += workspace_round256(n * sizeof(float));
   if (bf16) w += workspace_round256(n * a.dk_ * (a.dk_ + 64) * sizeof(uint16_t));
+  return w;
+}
+
+// Per-channel gated backward, each region on a 256-byte boundary:
+//   the gate pre-pass's tiles (gate_prep_bytes);
+//   Sc, dSc   bf16 [chunks][dk][dv] each;
+//   P, R^T    bf16 [chunks][dk][dk] and [chunks][dk][64];
+//   dQ~, dK~, dK^  fp32 [chunks][64][dk] each, then fp32 [chunks][dk] (the
+//             gradient of the chunk's decay through the state it leaves).
+inline size_t kda_backward_workspace_bytes(const BackwardArgs& a) {
+  if (a.T == 0) return 0;
+  const size_t n = workspace_chunks(a.B, a.H, a.T);
+  size_t w = workspace_round256(gate_prep_bytes(a.dk_, a.B, a.H, a.T));
+  w += 2 * workspace_round256(n * a.dk_ * a.dv_ * sizeof(uint16_t));
+  w += workspace_round256(n * a.dk_ * (a.dk_ + 64) * sizeof(uint16_t));
+  w += workspace_round256(n * (3 * 64 + 1) * a.dk_ * sizeof(float));
   return w;
 }
 

@@ -423,12 +423,6 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
         [&](const int x, auto parity) {
           constexpr int P = decltype(parity)::value;
           if (x < 0) return;
-          if constexpr (GATED) {
-            if (sm.gc[P][0] < 0.f) {
-              token_walk(parity);
-              return;
-            }
-          }
           if constexpr (CAP) {  // the state entering chunk x, for the backward pass
             // row perm32(16t + 4lg + i) = 8lg + 32(t / 2) + 4(t % 2) + i: one
             // lane-dependent base, offsets uniform across the wave
@@ -444,6 +438,12 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
               const int kt = 2 * (t >> 1) + (lg >> 1), lgt = 2 * (lg & 1) + (t & 1);
               *reinterpret_cast<uint2*>(scb + ((size_t)kt * (dv / 16) + jt) * 256 + 4 * (16 * lgt + lc)) =
                   make_uint2(pack2(st[t][0], st[t][1]), pack2(st[t][2], st[t][3]));
+            }
+          }
+          if constexpr (GATED) {
+            if (sm.gc[P][0] < 0.f) {
+              token_walk(parity);
+              return;
             }
           }
           // Y = K S and O = Q S (shared S fragments), X = beta (V - Y); the
@@ -787,38 +787,41 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
 // cumulative log-decay G_t = sum_{s<=t} g_s over the chunk (fp32), then
 // Gam Q, Gam K, K / Gam in bf16 and Gam_C = e^{G_63}.  One workgroup of 256
 // threads per chunk: thread (w, l) holds channels 2l, 2l+1 of tokens
-// 16w .. 16w+15; the four waves' partial sums are combined through LDS.
-// Inputs have T rows per head; the outputs have nch * 64, and rows past T
-// (a partial last chunk) get g = 0 and q = k = 0, so Gam_C is the decay
-// over the tokens that exist.
+// TPS w .. TPS w + TPS - 1 (TPS = 16 at dk = 128, fewer rows per thread and
+// more row groups at smaller dk); the row groups' partial sums are combined
+// through LDS.  Inputs have T rows per head; the outputs have nch * 64, and
+// rows past T (a partial last chunk) get g = 0 and q = k = 0, so Gam_C is the
+// decay over the tokens that exist.
 // A chunk in which some |G_t| exceeds kGateRange (a channel decays by more
 // than e^-64 within it, so K / Gam would leave the float range) is not
 // scaled: its q, k and g are copied as they are into the Gam Q, Gam K and
-// K / Gam slots, and Gam_C is set to -1, which tells the main kernel to walk
-// that chunk token by token.
+// K / Gam slots, and Gam_C is set to -1, which tells the main kernel (and the
+// backward pass) to walk that chunk token by token.
 constexpr float kGateRange = 64.f;
 
+template <int DK>
 __global__ __launch_bounds__(256) void gate_prep(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                  const bf16_t* __restrict__ g, bf16_t* __restrict__ qt,
                                                  bf16_t* __restrict__ kt, bf16_t* __restrict__ kht,
                                                  float* __restrict__ gcum, int T, int nch) {
-  __shared__ float2 part[4][64];
+  constexpr int NCOL = DK / 2, NSEG = 256 / NCOL, TPS = kC / NSEG;
+  __shared__ float2 part[NSEG][NCOL];
   __shared__ int wide;
   const int chunk = blockIdx.x;  // over B*H*nch
   const int bh = chunk / nch, t0 = (chunk - bh * nch) * kC;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const size_t base = (size_t)chunk * kC * kDK;                 // outputs
-  const size_t ibase = ((size_t)bh * T + t0) * kDK;             // inputs
+  const int w = threadIdx.x / NCOL, l = threadIdx.x % NCOL;
+  const size_t base = (size_t)chunk * kC * DK;                  // outputs
+  const size_t ibase = ((size_t)bh * T + t0) * DK;              // inputs
   const int nrow = min(kC, T - t0);                             // rows that exist
   const uint32_t* g2 = reinterpret_cast<const uint32_t*>(g + ibase);
-  uint32_t gw[16];
+  uint32_t gw[TPS];
 #pragma unroll
-  for (int t = 0; t < 16; ++t) gw[t] = g2[min(16 * w + t, nrow - 1) * (kDK / 2) + l];  // masked below
+  for (int t = 0; t < TPS; ++t) gw[t] = g2[min(TPS * w + t, nrow - 1) * NCOL + l];  // masked below
   float2 run = make_float2(0.f, 0.f);
-  float2 gl[16];
+  float2 gl[TPS];
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const uint32_t gv = 16 * w + t < nrow ? gw[t] : 0u;
+  for (int t = 0; t < TPS; ++t) {
+    const uint32_t gv = TPS * w + t < nrow ? gw[t] : 0u;
     run.x += bf2f((bf16_t)(gv & 0xffffu));
     run.y += bf2f((bf16_t)(gv >> 16));
     gl[t] = run;
@@ -828,7 +831,7 @@ __global__ __launch_bounds__(256) void gate_prep(const bf16_t* __restrict__ q, c
   __syncthreads();
   float2 off = make_float2(0.f, 0.f), tot = make_float2(0.f, 0.f);
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
+  for (int p = 0; p < NSEG; ++p) {
     const float2 x = part[p][l];
     if (p < w) { off.x += x.x; off.y += x.y; }
     tot.x += x.x;
@@ -837,7 +840,7 @@ __global__ __launch_bounds__(256) void gate_prep(const bf16_t* __restrict__ q, c
   // does any channel leave [-kGateRange, kGateRange] within the chunk?
   float mx = 0.f;
 #pragma unroll
-  for (int t = 0; t < 16; ++t) mx = fmaxf(mx, fmaxf(fabsf(off.x + gl[t].x), fabsf(off.y + gl[t].y)));
+  for (int t = 0; t < TPS; ++t) mx = fmaxf(mx, fmaxf(fabsf(off.x + gl[t].x), fabsf(off.y + gl[t].y)));
   if (!(mx <= kGateRange)) wide = 1;  // also for NaN
   __syncthreads();
   const uint32_t* q2 = reinterpret_cast<const uint32_t*>(q + ibase);
@@ -846,12 +849,12 @@ __global__ __launch_bounds__(256) void gate_prep(const bf16_t* __restrict__ q, c
   uint32_t* kt2 = reinterpret_cast<uint32_t*>(kt + base);
   uint32_t* kh2 = reinterpret_cast<uint32_t*>(kht + base);
   if (wide) {  // uniform over the workgroup: raw q, k, g and the marker
-    if (w == 0) reinterpret_cast<float2*>(gcum + (size_t)chunk * kDK)[l] = make_float2(-1.f, -1.f);
+    if (w == 0) reinterpret_cast<float2*>(gcum + (size_t)chunk * DK)[l] = make_float2(-1.f, -1.f);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int idx = (16 * w + t) * (kDK / 2) + l;
-      const int iidx = min(16 * w + t, nrow - 1) * (kDK / 2) + l;
-      const bool in = 16 * w + t < nrow;
+    for (int t = 0; t < TPS; ++t) {
+      const int idx = (TPS * w + t) * NCOL + l;
+      const int iidx = min(TPS * w + t, nrow - 1) * NCOL + l;
+      const bool in = TPS * w + t < nrow;
       const uint32_t qr = q2[iidx], kr = k2[iidx];  // in bounds for every lane
       qt2[idx] = in ? qr : 0u;
       kt2[idx] = in ? kr : 0u;
@@ -859,12 +862,12 @@ __global__ __launch_bounds__(256) void gate_prep(const bf16_t* __restrict__ q, c
     }
     return;
   }
-  if (w == 0) reinterpret_cast<float2*>(gcum + (size_t)chunk * kDK)[l] = make_float2(__expf(tot.x), __expf(tot.y));
+  if (w == 0) reinterpret_cast<float2*>(gcum + (size_t)chunk * DK)[l] = make_float2(__expf(tot.x), __expf(tot.y));
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const int idx = (16 * w + t) * (kDK / 2) + l;
-    const int iidx = min(16 * w + t, nrow - 1) * (kDK / 2) + l;
-    const bool in = 16 * w + t < nrow;
+  for (int t = 0; t < TPS; ++t) {
+    const int idx = (TPS * w + t) * NCOL + l;
+    const int iidx = min(TPS * w + t, nrow - 1) * NCOL + l;
+    const bool in = TPS * w + t < nrow;
     const uint32_t qr = q2[iidx], kr = k2[iidx];  // in bounds for every lane
     const uint32_t qw = in ? qr : 0u, kw = in ? kr : 0u;
     const float G0 = off.x + gl[t].x, G1 = off.y + gl[t].y;
@@ -899,8 +902,8 @@ hipError_t launch_pipe_t(const PipeArgs& p, long bh, int dv, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_prefill_pipe(const PrefillArgs& a, void* workspace, hipStream_t st) {
-  const long bh = (long)a.B * a.H;
+namespace {
+PipeArgs pipe_args(const PrefillArgs& a) {
   PipeArgs p{};
   p.v = reinterpret_cast<const bf16_t*>(a.v);
   p.beta = reinterpret_cast<const bf16_t*>(a.beta);
@@ -911,46 +914,62 @@ hipError_t launch_prefill_pipe(const PrefillArgs& a, void* workspace, hipStream_
   p.use_init = a.use_init;
   p.Tq = a.T;
   p.Sc = a.Sc;
-  if (a.g == nullptr) {
-    p.q = reinterpret_cast<const bf16_t*>(a.q);
-    p.k = reinterpret_cast<const bf16_t*>(a.k);
-    p.kh = nullptr;
-    p.gc = nullptr;
-    return a.Sc ? launch_pipe_t<0, true>(p, bh, a.dv, st) : launch_pipe_t<0>(p, bh, a.dv, st);
-  }
+  return p;
+}
+}  // namespace
+
+hipError_t launch_gate_prep(int dk, const PrefillArgs& a, void* workspace, hipStream_t st) {
   const int nch = (a.T + kC - 1) / kC;
-  const size_t n = (size_t)a.B * a.H * nch * kC * kDK;
+  const size_t n = (size_t)a.B * a.H * nch * kC * dk;
   bf16_t* qt = reinterpret_cast<bf16_t*>(workspace);
   bf16_t* kt = qt + n;
   bf16_t* kht = kt + n;
   float* gcum = reinterpret_cast<float*>(kht + n);
-  hipLaunchKernelGGL(gate_prep, dim3((unsigned)(a.B * a.H * nch)), dim3(256), 0, st,
-                     reinterpret_cast<const bf16_t*>(a.q), reinterpret_cast<const bf16_t*>(a.k),
-                     reinterpret_cast<const bf16_t*>(a.g), qt, kt, kht, gcum, a.T, nch);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  p.q = qt;
-  p.k = kt;
-  p.kh = kht;
-  p.gc = gcum;
+  const dim3 grid((unsigned)(a.B * a.H * nch)), block(256);
+  const bf16_t* q = reinterpret_cast<const bf16_t*>(a.q);
+  const bf16_t* k = reinterpret_cast<const bf16_t*>(a.k);
+  const bf16_t* g = reinterpret_cast<const bf16_t*>(a.g);
+  switch (dk) {
+    case 16: hipLaunchKernelGGL(gate_prep<16>, grid, block, 0, st, q, k, g, qt, kt, kht, gcum, a.T, nch); break;
+    case 32: hipLaunchKernelGGL(gate_prep<32>, grid, block, 0, st, q, k, g, qt, kt, kht, gcum, a.T, nch); break;
+    case 64: hipLaunchKernelGGL(gate_prep<64>, grid, block, 0, st, q, k, g, qt, kt, kht, gcum, a.T, nch); break;
+    case 128: hipLaunchKernelGGL(gate_prep<128>, grid, block, 0, st, q, k, g, qt, kt, kht, gcum, a.T, nch); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_pipe_prepped(const PrefillArgs& a, const void* prep, hipStream_t st) {
+  const int nch = (a.T + kC - 1) / kC;
+  const size_t n = (size_t)a.B * a.H * nch * kC * kDK;
+  PipeArgs p = pipe_args(a);
+  p.q = reinterpret_cast<const bf16_t*>(prep);
+  p.k = p.q + n;
+  p.kh = p.k + n;
+  p.gc = reinterpret_cast<const float*>(p.kh + n);
   p.Tq = nch * kC;
-  return launch_pipe_t<1>(p, bh, a.dv, st);
+  const long bh = (long)a.B * a.H;
+  return a.Sc ? launch_pipe_t<1, true>(p, bh, a.dv, st) : launch_pipe_t<1>(p, bh, a.dv, st);
+}
+
+hipError_t launch_prefill_pipe(const PrefillArgs& a, void* workspace, hipStream_t st) {
+  if (a.g == nullptr) {
+    PipeArgs p = pipe_args(a);
+    p.q = reinterpret_cast<const bf16_t*>(a.q);
+    p.k = reinterpret_cast<const bf16_t*>(a.k);
+    const long bh = (long)a.B * a.H;
+    return a.Sc ? launch_pipe_t<0, true>(p, bh, a.dv, st) : launch_pipe_t<0>(p, bh, a.dv, st);
+  }
+  const hipError_t e = launch_gate_prep(kDK, a, workspace, st);
+  if (e != hipSuccess) return e;
+  return launch_prefill_pipe_prepped(a, workspace, st);
 }
 
 hipError_t launch_prefill_pipe_token(const PrefillArgs& a, hipStream_t st) {
-  PipeArgs p{};
+  PipeArgs p = pipe_args(a);
   p.q = reinterpret_cast<const bf16_t*>(a.q);
   p.k = reinterpret_cast<const bf16_t*>(a.k);
   p.g = reinterpret_cast<const bf16_t*>(a.g);
-  p.v = reinterpret_cast<const bf16_t*>(a.v);
-  p.beta = reinterpret_cast<const bf16_t*>(a.beta);
-  p.o = reinterpret_cast<bf16_t*>(a.o);
-  p.S = a.S;
-  p.T = a.T;
-  p.dv = a.dv;
-  p.use_init = a.use_init;
-  p.Tq = a.T;
-  p.Sc = a.Sc;
   return a.Sc ? launch_pipe_t<2, true>(p, (long)a.B * a.H, a.dv, st) : launch_pipe_t<2>(p, (long)a.B * a.H, a.dv, st);
 }
 

@@ -40,9 +40,9 @@
  *           16 bytes); LA_ERR_ALIGN otherwise.  o must not alias any input.
  *           S (and z) are read and written.  The
  *           library keeps no state between calls; calls are re-entrant.  It
- *           never allocates device memory: the five entry points that need
+ *           never allocates device memory: the six entry points that need
  *           scratch memory on some paths (la_prefill, gla_prefill and
- *           deltanet_prefill, and the two backward entry points) take a
+ *           deltanet_prefill, and the three backward entry points) take a
  *           caller-owned workspace pointer and its size in bytes, and each
  *           has a *_workspace_bytes() query with the same sizes and dtype.
  *           The query returns 0 where no workspace is needed (the workspace
@@ -63,7 +63,13 @@
  *               entering and the gradient leaving every chunk), plus
  *               2 B*H*C*dk*(dk+64) with bf16 inputs (every chunk's P and
  *               R^T); the gated backward adds 4 B*H*C; each region is
- *               rounded up to 256 bytes.
+ *               rounded up to 256 bytes;
+ *             - kda_prefill_backward: 388 B*H*C*dk (the gate pre-pass's
+ *               copies and decays) + 4 B*H*C*dk*dv (the chunk states and
+ *               their gradients, bf16) + 2 B*H*C*dk*(dk+64) (P and R^T) +
+ *               772 B*H*C*dk (the gradients of the decay-scaled q and k,
+ *               fp32, and the decays' gradients), each region rounded up to
+ *               256 bytes.
  * Sizes.    B, H (or N, H) >= 1; T >= 0 for prefill, any length (the last
  *           64-token chunk may be partial).  T = 0 enqueues no work when
  *           use_initial_state is set and otherwise zero-fills S (and z);
@@ -302,6 +308,41 @@ int gated_deltanet_prefill_backward(const void *q, const void *k,
                                     int H, int T, int dk, int dv, int dtype,
                                     void *workspace, size_t workspace_bytes,
                                     void *stream);
+
+/*
+ * kda_prefill_backward -- gradients of deltanet_prefill with a per-key-channel
+ * gate (sections "Gated Delta Net" and "KDA / Kimi Linear": a decay
+ * a_t[i] = exp(g_t[i]) per key channel scales row i of the state before each
+ * read), for the same loss as deltanet_prefill_backward, with the gate's
+ * gradient dg [B,H,T,dk] (dtype) as well.  g [B,H,T,dk] (dtype) is required;
+ * q, k, v, beta, S0, dO, dST, dq, dk_out, dv_out, dbeta and dS0 are as for
+ * deltanet_prefill_backward.  bf16 only: LA_DTYPE_F32 returns
+ * LA_ERR_UNSUPPORTED_DIM; dk and dv each one of 16, 32, 64, 128.
+ * Per chunk, with G the log-decay summed from the chunk start per channel,
+ * Q~ = e^G q, K~ = e^G k, K^ = e^-G k and Gam_C = e^(G_C), the chunk form is
+ * the ungated one with K~ on the left of K S and of L, K^ on the right of A
+ * and L and in the state update S' = diag(Gam_C)(S + K^^T u); its backward is
+ * the ungated one in the same operands (the chain takes
+ * dS = diag(Gam_C) dSn - P dSn + R^T dO, P = W^T K^ diag(Gam_C), R = Q~ - A W,
+ * W = T diag(beta) K~), and the gradients of Q~, K~, K^ and Gam_C give dq,
+ * dk and dg (g_t enters the G_r, r >= t, of its own chunk).  A chunk in
+ * which some channel's summed log-decay leaves [-64, 64] (where K^ would
+ * leave the float range) is computed from the recurrence itself, token by
+ * token: its transition from the identity, its gradients backwards from its
+ * entry state; any finite g gives the recurrence's gradients, more slowly
+ * for such chunks.  The workspace, of
+ * kda_prefill_backward_workspace_bytes(...) bytes, is described under
+ * "Pointers".  T = 0 copies dST to dS0 (or zero-fills it).
+ */
+size_t kda_prefill_backward_workspace_bytes(int B, int H, int T, int dk, int dv,
+                                            int dtype);
+int kda_prefill_backward(const void *q, const void *k, const void *v,
+                         const void *beta, const void *g, const float *S0,
+                         const void *dO, const float *dST, void *dq,
+                         void *dk_out, void *dv_out, void *dbeta, void *dg,
+                         float *dS0, int B, int H, int T, int dk, int dv,
+                         int dtype, void *workspace, size_t workspace_bytes,
+                         void *stream);
 
 /*
  * deltanet_prologue -- the steps just before the delta rule in the layer of

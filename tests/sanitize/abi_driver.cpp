@@ -23,6 +23,7 @@ hipError_t launch_decode(int, int, int, int, const DecodeArgs&, hipStream_t) { +
 hipError_t launch_prefill(int, int, int, const PrefillArgs&, void*, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_prefill_generic(int, int, int, const PrefillArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_delta_backward(int, const BackwardArgs&, void*, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_kda_backward(const BackwardArgs&, void*, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_prologue(int, const PrologueArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_prefill_pipe(const PrefillArgs&, void*, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_prefill_pipe_token(const PrefillArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
@@ -105,6 +106,13 @@ int main() {
         n = g_launches;
         expect_ok(gated_deltanet_prefill_backward(F, F, F, F, F, nullptr, F, nullptr, F, F, F, F, F, nullptr, 2, 3, 130,
                                                   dk, dv, dt, F, gbws, nullptr), n, true);
+        if (dt == LA_DTYPE_BF16) {
+          const size_t kws = kda_prefill_backward_workspace_bytes(2, 3, 130, dk, dv, dt);
+          EXPECT(kws > 0);
+          n = g_launches;
+          expect_ok(kda_prefill_backward(F, F, F, F, F, nullptr, F, nullptr, F, F, F, F, F, nullptr, 2, 3, 130, dk, dv,
+                                         dt, F, kws, nullptr), n, true);
+        }
         n = g_launches;
         expect_ok(deltanet_prologue(F, F, F, F, F, F, 2, 3, 130, dk, 1, 1, 0.5f, dt, nullptr), n, true);
       }
@@ -145,7 +153,8 @@ int main() {
     (void)deltanet_prefill_workspace_bytes(gated, B, H, T, dk, dv, dt);
     (void)deltanet_prefill_backward_workspace_bytes(B, H, T, dk, dv, dt);
     (void)gated_deltanet_prefill_backward_workspace_bytes(B, H, T, dk, dv, dt);
-    int rc[11];
+    (void)kda_prefill_backward_workspace_bytes(B, H, T, dk, dv, dt);
+    int rc[12];
     rc[0] = la_prefill(p[0], p[1], p[2], p[3], (float*)p[4], (float*)p[5], gated, B, H, T, dk, dv, dt, ws, wsn, nullptr);
     rc[1] = la_decode_step(p[0], p[1], p[2], p[3], (float*)p[4], (float*)p[5], B, H, dk, dv, dt, nullptr);
     rc[2] = deltanet_prefill(p[0], p[1], p[2], p[3], gated ? p[6] : nullptr, p[4], (float*)p[5], gated, B, H, T, dk,
@@ -163,6 +172,8 @@ int main() {
                                             p[0], p[1], nullptr, B, H, T, dk, dv, dt, ws, wsn, nullptr);
     rc[10] = deltanet_prologue(p[0], p[1], p[2], p[3], p[4], p[5], B, H, T, dk, (int)(next() % 3), gated, 1.f, dt,
                                nullptr);
+    rc[11] = kda_prefill_backward(p[0], p[1], p[2], p[3], p[6], nullptr, p[4], nullptr, p[5], p[6], p[7], p[0], p[1],
+                                  nullptr, B, H, T, dk, dv, dt, ws, wsn, nullptr);
     for (int r : rc) EXPECT(r <= 0 && r >= LA_ERR_WORKSPACE);
   }
   for (int code = -10; code <= 2; ++code) EXPECT(la_strerror(code) != nullptr);

@@ -182,6 +182,32 @@ def test_gated_backward_validation():
     assert _gbwd(dg=MISALIGNED) != ALIGN  # dg is written element by element
 
 
+def _kbwd(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, S0=None, dO=FAKE, dST=None, dq=FAKE,
+          dk_=FAKE, dv_=FAKE, db=FAKE, dg=FAKE, dS0=None, B=1, H=1, T=64, dk=64, dv=64, dt=1,
+          ws=FAKE, wsn=BIG):
+    return la.library().kda_prefill_backward(q, k, v, beta, g, S0, dO, dST, dq, dk_, dv_, db, dg,
+                                             dS0, B, H, T, dk, dv, dt, ws, wsn, None)
+
+
+@pytest.mark.parametrize("missing", ["q", "k", "v", "beta", "g", "dO", "dq", "dk_", "dv_", "db",
+                                     "dg"])
+def test_kda_backward_null_pointers(missing):
+    assert _kbwd(**{missing: None}) == NULL
+
+
+def test_kda_backward_validation():
+    assert _kbwd(dt=3) == DTYPE
+    assert _kbwd(T=-1) == SHAPE
+    assert _kbwd(dk=96) == DIM
+    assert _kbwd(dt=0) == DIM           # bf16 only
+    assert _kbwd(dt=0, dk=16, dv=16) == DIM
+    assert _kbwd(dO=MISALIGNED) == ALIGN
+    for out in ("dq", "dk_", "dv_"):
+        assert _kbwd(**{out: MISALIGNED}) == ALIGN
+    assert _kbwd(ws=None, wsn=0) == WORKSPACE
+    assert _kbwd(wsn=la.kda_prefill_backward_workspace_bytes(1, 1, 64, 64, 64, 1) - 1) == WORKSPACE
+
+
 @pytest.mark.parametrize("missing", ["qi", "ki", "qo", "ko"])
 def test_prologue_null_pointers(missing):
     assert _pro(**{missing: None}) == NULL
@@ -318,13 +344,18 @@ def test_workspace_queries_match_the_documented_sizes():
         assert la.deltanet_prefill_backward_workspace_bytes(B, H, T, dk, dv, 1) == bwd
         assert la.gated_deltanet_prefill_backward_workspace_bytes(B, H, T, dk, dv, 1) == \
             bwd + r(4 * B * H * C)
+        kda = (r(388 * B * H * C * dk) + 2 * r(2 * nst) + r(2 * B * H * C * dk * (dk + 64))
+               + r(772 * B * H * C * dk))
+        assert la.kda_prefill_backward_workspace_bytes(B, H, T, dk, dv, 1) == kda
+        assert la.kda_prefill_backward_workspace_bytes(B, H, T, dk, dv, 0) == 0  # bf16 only
     assert la.deltanet_prefill_backward_workspace_bytes(B, H, T, 64, 64, 0) == 2 * 4 * B * H * C * 64 * 64
 
 
 def test_workspace_queries_are_zero_when_nothing_runs_or_the_call_is_invalid():
     for q in (la.la_prefill_workspace_bytes, la.gla_prefill_workspace_bytes,
               la.deltanet_prefill_backward_workspace_bytes,
-              la.gated_deltanet_prefill_backward_workspace_bytes):
+              la.gated_deltanet_prefill_backward_workspace_bytes,
+              la.kda_prefill_backward_workspace_bytes):
         assert q(1, 1, 0, 64, 64, 1) == 0          # T = 0
         assert q(0, 1, 64, 64, 64, 1) == 0         # bad shape
         assert q(1, 1, 64, 96, 64, 1) == 0         # bad dim
