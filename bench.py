@@ -45,11 +45,15 @@ DECODE_KERNEL = "decode_kernel<128, 128, linattn::BF16, 0"
 PREFILL_PROFILE = "prefill_pipe_delta_B4_H16_T4096_d128.txt"
 DECODE_PROFILE = "decode_kernel_delta_N256_H32_d128.txt"
 COPY_KERNEL = "copyBuffer"
-# (summary file, workload, kernel-name substrings) of the rows timed by bench_rows
+# (summary file, workload, kernels) of the rows timed by bench_rows: each
+# kernel is a name substring, or (substring, grid size in threads) where the
+# same kernel runs at several shapes in the traced run
+_KDA3 = 4 * 16 * 64   # chunks of the B=4 H=16 T=4096 rows
+_KDA4 = 1 * 32 * 512  # chunks of the B=1 H=32 T=32768 rows
 ROW_PROFILES = [
     ("prefill_pipe_gated_B1_H32_T32768_d128.txt",
      "gated deltanet_prefill B=1 H=32 T=32768 dk=dv=128 bf16: gate pre-pass + pipelined kernel",
-     ["gate_prep", "prefill_pipe<1, 16, false>"]),
+     [("gate_prep<128>", _KDA4 * 256), "prefill_pipe<1, 16, false>"]),
     ("la_par_B8_H12_T1024_d64.txt",
      "la_prefill B=8 H=12 T=1024 dk=dv=64 bf16: chunk states, state scan, chunk outputs",
      ["la_chunk_state<64, 64, false>", "la_state_scan<false>", "la_chunk_out<64, 64, false>"]),
@@ -77,14 +81,30 @@ ROW_PROFILES = [
      "deltanet_prefill_backward B=4 H=16 T=4096 dk=dv=128 bf16: forward chunk states "
      "(pipelined kernel with state capture), transition pre-pass, reverse chain, "
      "chunk-parallel gradients",
-     ["prefill_pipe<0, 32, true>", "bwd_transition<128, false>", "bwd_chain_mat<128, 32, false>",
-      "bwd_grads<128, 128, linattn::BF16, false>"]),
+     ["prefill_pipe<0, 32, true>", "bwd_transition<128, false, false>",
+      "bwd_chain_mat<128, 32, false, false>", "bwd_grads<128, 128, linattn::BF16, false, false>"]),
     ("gated_delta_backward_B4_H16_T4096_d128.txt",
      "gated_deltanet_prefill_backward (one decay per token) B=4 H=16 T=4096 dk=dv=128 bf16: "
      "forward chunk states (pipelined kernel with state capture), transition pre-pass, reverse chain, "
      "chunk-parallel gradients with dg",
-     ["prefill_pipe<2, 32, true>", "bwd_transition<128, true>",
-      "bwd_chain_mat<128, 32, true>", "bwd_grads<128, 128, linattn::BF16, true>"]),
+     ["prefill_pipe<2, 32, true>", "bwd_transition<128, true, false>",
+      "bwd_chain_mat<128, 32, true, false>", "bwd_grads<128, 128, linattn::BF16, true, false>"]),
+    ("kda_backward_B4_H16_T4096_d128.txt",
+     "kda_prefill_backward (a decay per key channel) B=4 H=16 T=4096 dk=dv=128 bf16: gate "
+     "pre-pass, forward chunk states (pipelined kernel with state capture), transition pre-pass, "
+     "reverse chain, gradients of the decay-scaled operands, token walk of out-of-range chunks "
+     "(none here: each workgroup exits), combination into dq, dk, dg",
+     [("gate_prep<128>", _KDA3 * 256), "prefill_pipe<1, 32, true>",
+      ("bwd_transition<128, false, true>", _KDA3 * 512), ("bwd_chain_mat<128, 32, false, true>", 64 * 4 * 512),
+      ("bwd_grads<128, 128, linattn::BF16, false, true>", _KDA3 * 512), ("kda_walk_grads<128, 128>", _KDA3 * 512),
+      ("kda_combine<128>", _KDA3 * 256)]),
+    ("kda_backward_B1_H32_T32768_d128.txt",
+     "kda_prefill_backward (a decay per key channel) B=1 H=32 T=32768 dk=dv=128 bf16, the gated "
+     "workload's decays: the same passes",
+     [("gate_prep<128>", _KDA4 * 256), "prefill_pipe<1, 16, true>",
+      ("bwd_transition<128, false, true>", _KDA4 * 512), ("bwd_chain_mat<128, 32, false, true>", 32 * 4 * 512),
+      ("bwd_grads<128, 128, linattn::BF16, false, true>", _KDA4 * 512), ("kda_walk_grads<128, 128>", _KDA4 * 512),
+      ("kda_combine<128>", _KDA4 * 256)]),
     ("prologue_B4_H16_T4096_d128.txt",
      "deltanet_prologue B=4 H=16 T=4096 dk=128 bf16, one beta logit per token shared by the heads",
      ["qk_prologue<128, linattn::BF16, true>"]),
@@ -282,19 +302,24 @@ def summarize(prof_dir):
         with open(os.path.join(PROFILES, fname), "w") as f:
             f.write("\n".join(lines) + "\n")
         print(f"wrote profiles/{fname}")
-    # the other rows: kernel-trace figures only (same trace run)
+    # the other rows: kernel-trace figures only (same trace run), from the
+    # per-dispatch records
+    dispatches = _csv_rows(os.path.join(prof_dir, "trace"), "kernel_trace.csv")
     for fname, wl, kernels in ROW_PROFILES:
         lines = [f"# rocprofv3 kernel-trace summary: {wl}",
                  "# $R is the repository root; the command runs committed files only.",
                  f"# command: {trace_cmd}", ""]
-        for kname in kernels:
-            row = [r for r in stats if kname in r["Name"]]
-            if len(row) != 1:
-                raise SystemExit(f"expected one kernel-trace row for '{kname}', found {len(row)}")
-            row = row[0]
-            lines += [f"kernel: {row['Name']}", f"calls: {row['Calls']}",
-                      f"average_ns: {float(row['AverageNs']):.0f}",
-                      f"min_ns: {float(row['MinNs']):.0f}", f"max_ns: {float(row['MaxNs']):.0f}", ""]
+        for spec in kernels:
+            kname, grid = spec if isinstance(spec, tuple) else (spec, None)
+            sel = [r for r in dispatches if kname in r["Kernel_Name"]
+                   and (grid is None or int(r["Grid_Size_X"]) == grid)]
+            names = {r["Kernel_Name"] for r in sel}
+            if len(names) != 1:
+                raise SystemExit(f"expected one kernel for '{kname}' (grid {grid}), found {len(names)}")
+            ns = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in sel]
+            lines += [f"kernel: {names.pop()}" + (f"   (grid {grid} threads)" if grid else ""),
+                      f"calls: {len(ns)}", f"average_ns: {sum(ns) / len(ns):.0f}",
+                      f"min_ns: {min(ns)}", f"max_ns: {max(ns)}", ""]
         with open(os.path.join(PROFILES, fname), "w") as f:
             f.write("\n".join(lines))
         print(f"wrote profiles/{fname}")
@@ -541,6 +566,40 @@ def bench_backward_row(la, workloads, torch, launches=5):
                    "transition pre-pass with the decays, reverse chain with the chunk decay, "
                    "chunk-parallel gradients and dg; bytes as above plus g in and dg out")
     rows[name] = r
+    # a decay per key channel, at the timed shape and at the gated workload's
+    for wk, seed in ((w, 99), (workloads.WORKLOADS[3], 100)):
+        if wk is not w:
+            inp = workloads.make_workload(wk)
+            d = {k: v.to(dev) for k, v in inp.items() if k != "S0"}
+            del inp
+            gen = workloads.generator(seed)
+            d["dO"] = torch.randn(wk.B, wk.H, wk.T, wk.dv, generator=gen).to(wk.dtype).to(dev)
+        else:
+            gen = workloads.generator(seed)
+            d["g"] = (-torch.nn.functional.softplus(torch.randn(w.B, w.H, w.T, w.dk, generator=gen))
+                      / 16.0).to(w.dtype).to(dev)
+        ws = torch.empty(la.kda_prefill_backward_workspace_bytes(wk.B, wk.H, wk.T, wk.dk, wk.dv,
+                                                                 wk.dtype),
+                         device=dev, dtype=torch.uint8)
+
+        def run_k(d):
+            la.kda_prefill_backward(d["q"], d["k"], d["v"], d["beta"], d["g"], d["dO"],
+                                    stream=stream, workspace=ws)
+
+        us, med = _time_launches(torch, stream, run_k, [d], launches, warmup=1)
+        thk = wk.B * wk.H * wk.T
+        perk = (thk * 2 * (2 * wk.dk + 2 * wk.dv + 1) + thk * 2 * (2 * wk.dk + wk.dv + 1)
+                + 2 * thk * 2 * wk.dk)
+        name, r = _row("kda_prefill_backward", "kda_prefill_backward (a decay per key channel) "
+                       f"B={wk.B} H={wk.H} T={wk.T} dk=dv={wk.dk} bf16", us, med, perk,
+                       "seven kernels: gate pre-pass, forward chunk states (pipelined kernel on "
+                       "the pre-pass's tiles, states captured), transition pre-pass, reverse "
+                       "chain with the per-channel chunk decay, chunk-parallel gradients of the "
+                       "decay-scaled operands, the out-of-range chunks' token walk (none here), "
+                       "and the combination into dq, dk, dg; bytes as the other backward rows "
+                       "plus g in and dg out [B,H,T,dk]")
+        rows[f"{name}_T{wk.T}"] = r
+        del ws
     return rows
 
 

@@ -503,19 +503,12 @@ __device__ __forceinline__ void st4_bf16(bf16_t* p, float a0, float a1, float a2
 
 // Per-key-channel gate (KDA): the gate pre-pass's tiles (Q~ = Gam Q,
 // K~ = Gam K, K^ = K / Gam, bf16 [chunk][64][dk]; Gam_C fp32 [chunk][dk], -1
-// for a chunk walked token by token, whose tiles hold the raw q, k, g) and
-// the gradient pass's outputs (dQ~, dK~, dK^ fp32 [chunk][64][dk], and the
-// gradient of each chunk's log-decay through the state it leaves, fp32
-// [chunk][dk]).
+// for a chunk walked token by token, whose tiles hold the raw q, k, g).
 struct KdaPtrs {
   const bf16_t* qt;
   const bf16_t* kt;
   const bf16_t* kht;
   const float* gc;
-  float* dqt;
-  float* dkt;
-  float* dkh;
-  float* cc;
 };
 
 template <int DK, bool KDA = false>
@@ -1125,10 +1118,15 @@ struct GradLayout {
 // left of K S and of L (and W), K^ on the right of A and L and in the state
 // update, and dSn' for dSn; the gradients of the three tiles are kept apart,
 //   dQ~ = dO S^T + dA K^,  dK~ = (b dL) K^ - diag(beta) dX S^T,
-//   dK^ = dA^T Q~ + (b dL)^T K~ + u dSn'^T,
-// and go to the workspace with <S_i + (K^^T u)_i, dSn'_i> per channel i (the
-// gradient of the chunk's log-decay through Gam_C); kda_combine forms dq,
-// dk and dg from them.  A chunk walked token by token is left to
+//   dK^ = dA^T Q~ + (b dL)^T K~ + u dSn'^T.
+// With G the log-decay summed from the chunk start (per channel, formed
+// again here from g), Q~ = e^G q, K~ = e^G k, K^ = e^-G k and
+// Gam_C = e^(G_C):  dq = e^G dQ~,  dk = e^G dK~ + e^-G dK^, and
+//   dG = q e^G dQ~ + k e^G dK~ - k e^-G dK^  (elementwise),
+// plus, on the chunk's last row, <S_i + (K^^T u)_i, dSn'_i> per channel i
+// (Gam_C's part).  g_t enters G_r for r >= t of its own chunk only, so
+// dg_t = sum of dG_r over r >= t; as the last row's term is in every such
+// sum, it is added to every row.  A chunk walked token by token is left to
 // kda_walk_grads.
 template <int DK, int DV, class E, bool GATE, bool KDA = false>
 __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const float* __restrict__ Sc,
@@ -1558,6 +1556,23 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
   // ---- phase D: each wave owns output tiles id = wave + 4 n of the 4 x NKT grid ----
   constexpr int NTILE = 4 * NKT, NOWN = (NTILE + NW - 1) / NW;  // output tiles, per wave
   floatx4 gq[NOWN], gk[NOWN], gkh[KDA ? NOWN : 1];  // KDA: dK~ in gk, dK^ in gkh
+  // KDA: this lane's g, q, k for its output tiles of phase E (row 16 ti + lc,
+  // channels d0 .. d0 + 3), loaded now so that phase D covers their latency
+  uint2 rg[KDA ? NOWN : 1], rq[KDA ? NOWN : 1], rk[KDA ? NOWN : 1];
+  if constexpr (KDA) {
+    const bf16_t* ghh = reinterpret_cast<const bf16_t*>(a.g) + ((size_t)bh * Tn + t0) * DK;
+#pragma unroll
+    for (int n = 0; n < NOWN; ++n) {
+      const int id = min(wave + NW * n, NTILE - 1), ti = id / NKT, tk = id - ti * NKT;
+      const size_t o = (size_t)min(16 * ti + lc, nrow - 1) * DK + 16 * tk + 4 * lg;  // in bounds for every lane
+      rg[n] = *reinterpret_cast<const uint2*>(ghh + o);
+      rq[n] = *reinterpret_cast<const uint2*>(qh + (size_t)t0 * DK + o);
+      rk[n] = *reinterpret_cast<const uint2*>(kh + (size_t)t0 * DK + o);
+    }
+  }
+  float gpre[KDA ? NOWN : 1][4], dsuf[KDA ? NOWN : 1][4];
+  float* sTotG = sKK;            // KDA, [4][DK]: per tile, the sum of its rows' g
+  float* sTotD = sKK + 4 * DK;   // KDA, [4][DK]: per tile, the sum of its rows' dG
   if constexpr (kBf16) {
     // K and Q row-major; every product over tokens reads them (and dA,
     // diag(beta) dL) with the transpose read or against the permuted copies.
@@ -1617,6 +1632,34 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
       gq[n] = xq;
       gk[n] = xk;
       if constexpr (KDA) gkh[n] = xb + xc;
+    }
+    if constexpr (KDA) {
+      // the log-decay G_r summed from the chunk start, per key channel, for
+      // this lane's rows and channels: a prefix over the tile's 16 rows by
+      // shuffles now, plus the totals of the tiles above (through LDS, in the
+      // K K^T region, free since phase C) in phase E
+#pragma unroll
+      for (int n = 0; n < NOWN; ++n) {
+        const int id = wave + NW * n, ti = id / NKT, tk = id - ti * NKT;
+        const bool own = NTILE % NW == 0 || id < NTILE;
+        const int r = 16 * ti + lc, d0 = 16 * tk + 4 * lg;
+        float x[4];
+        x[0] = bf2f((bf16_t)(rg[n].x & 0xffffu));
+        x[1] = bf2f((bf16_t)(rg[n].x >> 16));
+        x[2] = bf2f((bf16_t)(rg[n].y & 0xffffu));
+        x[3] = bf2f((bf16_t)(rg[n].y >> 16));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (r >= nrow) x[i] = 0.f;
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) {
+            const float y = __shfl_up(x[i], off, 16);  // every lane shuffles, then masks
+            if (lc >= off) x[i] += y;
+          }
+          gpre[n][i] = x[i];
+          if (own && lc == 15) sTotG[ti * DK + d0 + i] = x[i];
+        }
+      }
     }
     __syncthreads();
   } else {
@@ -1707,9 +1750,9 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
       pd[0] = E::cvt(bd[j].x); pd[1] = E::cvt(bd[j].y); pd[2] = E::cvt(bd[j].z); pd[3] = E::cvt(bd[j].w);
     }
   }
-  __syncthreads();
   T* dqo = reinterpret_cast<T*>(a.dq) + ((size_t)bh * Tn + t0) * DK;
   T* dko = reinterpret_cast<T*>(a.dk) + ((size_t)bh * Tn + t0) * DK;
+  __syncthreads();
 #pragma unroll
   for (int n = 0; n < NOWN; ++n) {
     const int id = wave + NW * n, ti = id / NKT, tk = id - ti * NKT;
@@ -1721,28 +1764,47 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
       const int r = 16 * ti + lc, d0 = 16 * tk + 4 * lg;
       const float br = sB[r];
       if constexpr (KDA) {
-        // dQ~, dK~, dK^ (fp32, rows of this chunk's tiles) for kda_combine;
-        // sum over tokens of K^ * (u dSn'^T) per channel for the decay's gradient
-        float p[4] = {0.f, 0.f, 0.f, 0.f};
+        // with Q~ = e^G q, K~ = e^G k, K^ = e^-G k (fp32 from the inputs):
+        //   dq = e^G dQ~,  dk = e^G dK~ + e^-G dK^,
+        //   dG = q e^G dQ~ + k e^G dK~ - k e^-G dK^;
+        // and the sum over tokens of K^ (u dSn'^T) per channel, the part of
+        // the decay's gradient through Gam_C that phase B did not form
+        float qv[4] = {0.f, 0.f, 0.f, 0.f}, kv[4] = {0.f, 0.f, 0.f, 0.f};
         if (r < nrow) {
-          const uint2 w = *reinterpret_cast<const uint2*>(kp.kht + tile0 + (size_t)r * DK + d0);
-          p[0] = bf2f((bf16_t)(w.x & 0xffffu)) * k1[0];
-          p[1] = bf2f((bf16_t)(w.x >> 16)) * k1[1];
-          p[2] = bf2f((bf16_t)(w.y & 0xffffu)) * k1[2];
-          p[3] = bf2f((bf16_t)(w.y >> 16)) * k1[3];
-          const size_t o = tile0 + (size_t)r * DK + d0;
-          *reinterpret_cast<float4*>(kp.dqt + o) =
-              make_float4(gq[n][0] + q1[0], gq[n][1] + q1[1], gq[n][2] + q1[2], gq[n][3] + q1[3]);
-          *reinterpret_cast<float4*>(kp.dkt + o) = make_float4(gk[n][0] - br * k2[0], gk[n][1] - br * k2[1],
-                                                               gk[n][2] - br * k2[2], gk[n][3] - br * k2[3]);
-          *reinterpret_cast<float4*>(kp.dkh + o) =
-              make_float4(gkh[n][0] + k1[0], gkh[n][1] + k1[1], gkh[n][2] + k1[2], gkh[n][3] + k1[3]);
+          qv[0] = bf2f((bf16_t)(rq[n].x & 0xffffu)); qv[1] = bf2f((bf16_t)(rq[n].x >> 16));
+          qv[2] = bf2f((bf16_t)(rq[n].y & 0xffffu)); qv[3] = bf2f((bf16_t)(rq[n].y >> 16));
+          kv[0] = bf2f((bf16_t)(rk[n].x & 0xffffu)); kv[1] = bf2f((bf16_t)(rk[n].x >> 16));
+          kv[2] = bf2f((bf16_t)(rk[n].y & 0xffffu)); kv[3] = bf2f((bf16_t)(rk[n].y >> 16));
+        }
+        float dq4[4], dk4[4], dG[4], p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float G = gpre[n][i];
+          for (int t2 = 0; t2 < ti; ++t2) G += sTotG[t2 * DK + d0 + i];
+          const float e = __expf(G), ie = __expf(-G);
+          const float dqt = gq[n][i] + q1[i], dkt = gk[n][i] - br * k2[i], dkh = gkh[n][i] + k1[i];
+          dq4[i] = e * dqt;
+          dk4[i] = e * dkt + ie * dkh;
+          dG[i] = qv[i] * e * dqt + kv[i] * e * dkt - kv[i] * ie * dkh;
+          p[i] = kv[i] * ie * k1[i];
+        }
+        if (r < nrow) {
+          st4_bf16(reinterpret_cast<bf16_t*>(dqo) + (size_t)r * DK + d0, dq4[0], dq4[1], dq4[2], dq4[3]);
+          st4_bf16(reinterpret_cast<bf16_t*>(dko) + (size_t)r * DK + d0, dk4[0], dk4[1], dk4[2], dk4[3]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
-          for (int off = 1; off < 16; off <<= 1) p[i] += __shfl_xor(p[i], off, 16);
-          if (lc == 0) atomicAdd(&sCC[d0 + i], p[i]);
+          for (int off = 1; off < 16; off <<= 1) {
+            p[i] += __shfl_xor(p[i], off, 16);
+            const float y = __shfl_down(dG[i], off, 16);  // suffix over the tile's rows
+            if (lc + off < 16) dG[i] += y;
+          }
+          if (lc == 0) {
+            atomicAdd(&sCC[d0 + i], p[i]);
+            sTotD[ti * DK + d0 + i] = dG[i];
+          }
+          dsuf[n][i] = dG[i];
         }
         continue;
       }
@@ -1815,9 +1877,22 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
     }
   }
   if (tid < nrow) reinterpret_cast<T*>(a.dbeta)[(size_t)bh * Tn + t0 + tid] = E::cvt(sDB[tid]);
-  if constexpr (KDA) {
+  if constexpr (KDA) {  // dg_t = sum of dG_r over r >= t, plus the decay's part through Gam_C
     __syncthreads();
-    for (int i = tid; i < DK; i += NTH) kp.cc[(size_t)chunk * DK + i] = sCC[i];
+    bf16_t* dgo = reinterpret_cast<bf16_t*>(a.dg) + ((size_t)bh * Tn + t0) * DK;
+#pragma unroll
+    for (int n = 0; n < NOWN; ++n) {
+      const int id = wave + NW * n, ti = id / NKT, tk = id - ti * NKT;
+      if (NTILE % NW != 0 && id >= NTILE) continue;
+      const int r = 16 * ti + lc, d0 = 16 * tk + 4 * lg;
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[i] = dsuf[n][i] + sCC[d0 + i];
+        for (int t2 = ti + 1; t2 < 4; ++t2) v[i] += sTotD[t2 * DK + d0 + i];
+      }
+      if (r < nrow) st4_bf16(dgo + (size_t)r * DK + d0, v[0], v[1], v[2], v[3]);
+    }
   }
   if constexpr (GATE) {  // dg_t: the sums of dG_r over r >= t in the chunk
     __syncthreads();
@@ -1830,101 +1905,6 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
       }
       if (lane < nrow) reinterpret_cast<T*>(a.dg)[(size_t)bh * Tn + t0 + lane] = E::cvt(x);
     }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// KDA: dq, dk and dg of a chunk in the factored form from the gradients of
-// its tiles.  With G_t the log-decay summed from the chunk start (per key
-// channel, fp32, from g as the pre-pass forms it), Q~ = e^G q, K~ = e^G k,
-// K^ = e^-G k and Gam_C = e^(G_C):
-//   dq = e^G dQ~,  dk = e^G dK~ + e^-G dK^,
-//   dG_t = q e^G dQ~ + k e^G dK~ - k e^-G dK^ (elementwise), plus, on the
-//   chunk's last row, the decay's gradient through Gam_C from the gradient
-//   pass;
-// g_t enters G_r for r >= t of its own chunk only, so dg_t = sum of dG_r over
-// r >= t in the chunk.  One workgroup of 256 threads per chunk, thread (w, l)
-// on channels 2l, 2l+1 of TPS consecutive rows, as in the pre-pass; a chunk
-// walked token by token is left to kda_walk_grads.
-// ---------------------------------------------------------------------------
-template <int DK>
-__global__ __launch_bounds__(256) void kda_combine(BackwardArgs a, KdaPtrs kp) {
-  constexpr int NCOL = DK / 2, NSEG = 256 / NCOL, TPS = kC / NSEG;
-  __shared__ float2 part[NSEG][NCOL];
-  const int chunk = blockIdx.x;
-  if (kp.gc[(size_t)chunk * DK] < 0.f) return;  // walked (uniform)
-  const int Tn = a.T, nch = (Tn + kC - 1) / kC;
-  const int bh = chunk / nch, t0 = (chunk - bh * nch) * kC, nrow = min(kC, Tn - t0);
-  const int w = threadIdx.x / NCOL, l = threadIdx.x % NCOL;
-  const size_t ib = ((size_t)bh * Tn + t0) * DK;   // raw inputs and outputs
-  const size_t tb = (size_t)chunk * kC * DK;       // the tiles' gradients
-  const uint32_t* g2 = reinterpret_cast<const uint32_t*>(reinterpret_cast<const bf16_t*>(a.g) + ib);
-  float2 G[TPS];
-  float2 run = make_float2(0.f, 0.f);
-#pragma unroll
-  for (int t = 0; t < TPS; ++t) {
-    const int r = TPS * w + t;
-    const uint32_t gv = r < nrow ? g2[r * NCOL + l] : 0u;
-    run.x += bf2f((bf16_t)(gv & 0xffffu));
-    run.y += bf2f((bf16_t)(gv >> 16));
-    G[t] = run;
-  }
-  part[w][l] = run;
-  __syncthreads();
-  float2 off = make_float2(0.f, 0.f);
-  for (int p = 0; p < w; ++p) {
-    off.x += part[p][l].x;
-    off.y += part[p][l].y;
-  }
-  __syncthreads();
-  const uint32_t* q2 = reinterpret_cast<const uint32_t*>(reinterpret_cast<const bf16_t*>(a.q) + ib);
-  const uint32_t* k2 = reinterpret_cast<const uint32_t*>(reinterpret_cast<const bf16_t*>(a.k) + ib);
-  uint32_t* dq2 = reinterpret_cast<uint32_t*>(reinterpret_cast<bf16_t*>(a.dq) + ib);
-  uint32_t* dk2 = reinterpret_cast<uint32_t*>(reinterpret_cast<bf16_t*>(a.dk) + ib);
-  uint32_t* dg2 = reinterpret_cast<uint32_t*>(reinterpret_cast<bf16_t*>(a.dg) + ib);
-  const float2 cc = reinterpret_cast<const float2*>(kp.cc + (size_t)chunk * DK)[l];
-  float2 dG[TPS];
-#pragma unroll
-  for (int t = 0; t < TPS; ++t) {
-    const int r = TPS * w + t;
-    dG[t] = make_float2(0.f, 0.f);
-    if (r >= nrow) continue;
-    const float G0 = off.x + G[t].x, G1 = off.y + G[t].y;
-    const float e0 = __expf(G0), e1 = __expf(G1), i0 = __expf(-G0), i1 = __expf(-G1);
-    const uint32_t qw = q2[r * NCOL + l], kw = k2[r * NCOL + l];
-    const float q0 = bf2f((bf16_t)(qw & 0xffffu)), q1 = bf2f((bf16_t)(qw >> 16));
-    const float k0 = bf2f((bf16_t)(kw & 0xffffu)), k1 = bf2f((bf16_t)(kw >> 16));
-    const float2 a1 = reinterpret_cast<const float2*>(kp.dqt + tb)[r * NCOL + l];
-    const float2 b1 = reinterpret_cast<const float2*>(kp.dkt + tb)[r * NCOL + l];
-    const float2 c1 = reinterpret_cast<const float2*>(kp.dkh + tb)[r * NCOL + l];
-    dq2[r * NCOL + l] = pack2(e0 * a1.x, e1 * a1.y);
-    dk2[r * NCOL + l] = pack2(e0 * b1.x + i0 * c1.x, e1 * b1.y + i1 * c1.y);
-    dG[t].x = q0 * e0 * a1.x + k0 * e0 * b1.x - k0 * i0 * c1.x;
-    dG[t].y = q1 * e1 * a1.y + k1 * e1 * b1.y - k1 * i1 * c1.y;
-    if (r == nrow - 1) {
-      dG[t].x += cc.x;
-      dG[t].y += cc.y;
-    }
-  }
-  // suffix sums: within the thread's rows, then the later row groups' totals
-  float2 suf = make_float2(0.f, 0.f);
-#pragma unroll
-  for (int t = TPS - 1; t >= 0; --t) {
-    suf.x += dG[t].x;
-    suf.y += dG[t].y;
-    dG[t] = suf;
-  }
-  part[w][l] = suf;
-  __syncthreads();
-  float2 later = make_float2(0.f, 0.f);
-  for (int p = w + 1; p < NSEG; ++p) {
-    later.x += part[p][l].x;
-    later.y += part[p][l].y;
-  }
-#pragma unroll
-  for (int t = 0; t < TPS; ++t) {
-    const int r = TPS * w + t;
-    if (r < nrow) dg2[r * NCOL + l] = pack2(dG[t].x + later.x, dG[t].y + later.y);
   }
 }
 
@@ -2169,8 +2149,8 @@ hipError_t launch_backward_e(const BackwardArgs& a, float* Sc, float* dSc, bf16_
 }
 
 // KDA (bf16): the transition and chain with a decay per key channel, then
-// the gradients (factored chunks: bwd_grads and kda_combine; walked chunks:
-// kda_walk_grads; each kernel leaves the other kind of chunk alone)
+// the gradients (factored chunks: bwd_grads; walked chunks: kda_walk_grads;
+// each kernel leaves the other kind of chunk alone)
 template <int DK, int DV>
 hipError_t launch_kda_grads(const BackwardArgs& a, const bf16_t* Sc, const bf16_t* dSt, const KdaPtrs& kp,
                             long nchunks, hipStream_t st) {
@@ -2181,9 +2161,6 @@ hipError_t launch_kda_grads(const BackwardArgs& a, const bf16_t* Sc, const bf16_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((kda_walk_grads<DK, DV>), dim3((unsigned)nchunks), dim3(512), 0, st, a, Sc, dSt, kp);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((kda_combine<DK>), dim3((unsigned)nchunks), dim3(256), 0, st, a, kp);
   return hipGetLastError();
 }
 
@@ -2299,17 +2276,11 @@ hipError_t launch_kda_backward(const BackwardArgs& a, void* workspace, hipStream
   ws += workspace_round256(nchunks * a.dk_ * a.dv_ * sizeof(bf16_t));
   bf16_t* Pg = reinterpret_cast<bf16_t*>(ws);
   bf16_t* Rg = Pg + nchunks * a.dk_ * a.dk_;
-  ws += workspace_round256(nchunks * a.dk_ * (a.dk_ + 64) * sizeof(bf16_t));
-  float* dqt = reinterpret_cast<float*>(ws);
   KdaPtrs kp{};
   kp.qt = reinterpret_cast<const bf16_t*>(prep);
   kp.kt = kp.qt + ntile;
   kp.kht = kp.kt + ntile;
   kp.gc = reinterpret_cast<const float*>(kp.kht + ntile);
-  kp.dqt = dqt;
-  kp.dkt = dqt + ntile;
-  kp.dkh = dqt + 2 * ntile;
-  kp.cc = dqt + 3 * ntile;
   // the gate pre-pass, then pass 1: the state entering every chunk (no
   // output, no final state; S0 is only read)
   PrefillArgs f{};

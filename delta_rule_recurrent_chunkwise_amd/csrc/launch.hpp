@@ -162,16 +162,13 @@ inline size_t delta_backward_workspace_bytes(int bf16, const BackwardArgs& a) {
 // Per-channel gated backward, each region on a 256-byte boundary:
 //   the gate pre-pass's tiles (gate_prep_bytes);
 //   Sc, dSc   bf16 [chunks][dk][dv] each;
-//   P, R^T    bf16 [chunks][dk][dk] and [chunks][dk][64];
-//   dQ~, dK~, dK^  fp32 [chunks][64][dk] each, then fp32 [chunks][dk] (the
-//             gradient of the chunk's decay through the state it leaves).
+//   P, R^T    bf16 [chunks][dk][dk] and [chunks][dk][64].
 inline size_t kda_backward_workspace_bytes(const BackwardArgs& a) {
   if (a.T == 0) return 0;
   const size_t n = workspace_chunks(a.B, a.H, a.T);
   size_t w = workspace_round256(gate_prep_bytes(a.dk_, a.B, a.H, a.T));
   w += 2 * workspace_round256(n * a.dk_ * a.dv_ * sizeof(uint16_t));
   w += workspace_round256(n * a.dk_ * (a.dk_ + 64) * sizeof(uint16_t));
-  w += workspace_round256(n * (3 * 64 + 1) * a.dk_ * sizeof(float));
   return w;
 }
 

@@ -66,10 +66,8 @@
  *               rounded up to 256 bytes;
  *             - kda_prefill_backward: 388 B*H*C*dk (the gate pre-pass's
  *               copies and decays) + 4 B*H*C*dk*dv (the chunk states and
- *               their gradients, bf16) + 2 B*H*C*dk*(dk+64) (P and R^T) +
- *               772 B*H*C*dk (the gradients of the decay-scaled q and k,
- *               fp32, and the decays' gradients), each region rounded up to
- *               256 bytes.
+ *               their gradients, bf16) + 2 B*H*C*dk*(dk+64) (P and R^T),
+ *               each region rounded up to 256 bytes.
  * Sizes.    B, H (or N, H) >= 1; T >= 0 for prefill, any length (the last
  *           64-token chunk may be partial).  T = 0 enqueues no work when
  *           use_initial_state is set and otherwise zero-fills S (and z);

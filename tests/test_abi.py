@@ -344,8 +344,7 @@ def test_workspace_queries_match_the_documented_sizes():
         assert la.deltanet_prefill_backward_workspace_bytes(B, H, T, dk, dv, 1) == bwd
         assert la.gated_deltanet_prefill_backward_workspace_bytes(B, H, T, dk, dv, 1) == \
             bwd + r(4 * B * H * C)
-        kda = (r(388 * B * H * C * dk) + 2 * r(2 * nst) + r(2 * B * H * C * dk * (dk + 64))
-               + r(772 * B * H * C * dk))
+        kda = r(388 * B * H * C * dk) + 2 * r(2 * nst) + r(2 * B * H * C * dk * (dk + 64))
         assert la.kda_prefill_backward_workspace_bytes(B, H, T, dk, dv, 1) == kda
         assert la.kda_prefill_backward_workspace_bytes(B, H, T, dk, dv, 0) == 0  # bf16 only
     assert la.deltanet_prefill_backward_workspace_bytes(B, H, T, 64, 64, 0) == 2 * 4 * B * H * C * 64 * 64
