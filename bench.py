@@ -92,19 +92,17 @@ ROW_PROFILES = [
     ("kda_backward_B4_H16_T4096_d128.txt",
      "kda_prefill_backward (a decay per key channel) B=4 H=16 T=4096 dk=dv=128 bf16: gate "
      "pre-pass, forward chunk states (pipelined kernel with state capture), transition pre-pass, "
-     "reverse chain, gradients of the decay-scaled operands, token walk of out-of-range chunks "
-     "(none here: each workgroup exits), combination into dq, dk, dg",
+     "reverse chain, gradients (dq, dk, dg formed in the same kernel), token walk of "
+     "out-of-range chunks (none here: each workgroup exits)",
      [("gate_prep<128>", _KDA3 * 256), "prefill_pipe<1, 32, true>",
       ("bwd_transition<128, false, true>", _KDA3 * 512), ("bwd_chain_mat<128, 32, false, true>", 64 * 4 * 512),
-      ("bwd_grads<128, 128, linattn::BF16, false, true>", _KDA3 * 512), ("kda_walk_grads<128, 128>", _KDA3 * 512),
-      ("kda_combine<128>", _KDA3 * 256)]),
+      ("bwd_grads<128, 128, linattn::BF16, false, true>", _KDA3 * 512), ("kda_walk_grads<128, 128>", _KDA3 * 512)]),
     ("kda_backward_B1_H32_T32768_d128.txt",
      "kda_prefill_backward (a decay per key channel) B=1 H=32 T=32768 dk=dv=128 bf16, the gated "
      "workload's decays: the same passes",
      [("gate_prep<128>", _KDA4 * 256), "prefill_pipe<1, 16, true>",
       ("bwd_transition<128, false, true>", _KDA4 * 512), ("bwd_chain_mat<128, 32, false, true>", 32 * 4 * 512),
-      ("bwd_grads<128, 128, linattn::BF16, false, true>", _KDA4 * 512), ("kda_walk_grads<128, 128>", _KDA4 * 512),
-      ("kda_combine<128>", _KDA4 * 256)]),
+      ("bwd_grads<128, 128, linattn::BF16, false, true>", _KDA4 * 512), ("kda_walk_grads<128, 128>", _KDA4 * 512)]),
     ("prologue_B4_H16_T4096_d128.txt",
      "deltanet_prologue B=4 H=16 T=4096 dk=128 bf16, one beta logit per token shared by the heads",
      ["qk_prologue<128, linattn::BF16, true>"]),
@@ -592,12 +590,11 @@ def bench_backward_row(la, workloads, torch, launches=5):
                 + 2 * thk * 2 * wk.dk)
         name, r = _row("kda_prefill_backward", "kda_prefill_backward (a decay per key channel) "
                        f"B={wk.B} H={wk.H} T={wk.T} dk=dv={wk.dk} bf16", us, med, perk,
-                       "seven kernels: gate pre-pass, forward chunk states (pipelined kernel on "
+                       "six kernels: gate pre-pass, forward chunk states (pipelined kernel on "
                        "the pre-pass's tiles, states captured), transition pre-pass, reverse "
-                       "chain with the per-channel chunk decay, chunk-parallel gradients of the "
-                       "decay-scaled operands, the out-of-range chunks' token walk (none here), "
-                       "and the combination into dq, dk, dg; bytes as the other backward rows "
-                       "plus g in and dg out [B,H,T,dk]")
+                       "chain with the per-channel chunk decay, chunk-parallel gradients (dq, "
+                       "dk, dg included), the out-of-range chunks' token walk (none here); "
+                       "bytes as the other backward rows plus g in and dg out [B,H,T,dk]")
         rows[f"{name}_T{wk.T}"] = r
         del ws
     return rows
