@@ -1014,7 +1014,8 @@ def main():
                      "kernel": PREFILL_KERNEL,
                      "algorithmic_bytes_per_launch": pbytes,
                      "avg_launch_us": avg_kernel_s * 1e6,
-                     "median_launch_us": kms[len(kms) // 2] * 1e3},
+                     "median_launch_us": kms[len(kms) // 2] * 1e3,
+                     "min_launch_us": kms[0] * 1e3},
         "mfma": {"achieved": pflops / avg_kernel_s / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
                  "unit": "TFLOP/s", "frac": pflops / avg_kernel_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                  "algorithmic_flops_per_launch": pflops,

@@ -1172,6 +1172,21 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
   const float* dSn = dSc + (size_t)chunk * DK * DV;
   const bf16_t* dSt = reinterpret_cast<const bf16_t*>(dSc) + (size_t)chunk * DK * DV;
 
+  // Ungated, bf16, dv = 128 (eight 16-column slices, one per wave): this
+  // wave's slice of S and dSn, loaded now (in flight with phase A's loads),
+  // read by phase B and staged into LDS for phase E without a second load.
+  // (The gated kernels have no registers to spare for it; with a
+  // per-channel decay it measured no gain.)
+  constexpr bool kHold = kBf16 && !GATE && !KDA && NVT == NW;
+  uint2 hS[kHold ? NKT : 1], hD[kHold ? NKT : 1];
+  if constexpr (kHold) {
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+      hD[kt] = *reinterpret_cast<const uint2*>(dSt + (kt * NVT + wave) * 256 + 4 * lane);
+      hS[kt] = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(S) + (kt * NVT + wave) * 256 + 4 * lane);
+    }
+  }
+
   // ---- phase A ----
   T* sQ = reinterpret_cast<T*>(smem + L::aQ);
   T* sK = reinterpret_cast<T*>(smem + L::aK);
@@ -1312,8 +1327,10 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
     if constexpr (kBf16) {
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt) {
-        const uint2 w = *reinterpret_cast<const uint2*>(dSt + (kt * NVT + s) * 256 + 4 * lane);
-        const uint2 v = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(S) + (kt * NVT + s) * 256 + 4 * lane);
+        const uint2 w = kHold ? hD[kHold ? kt : 0]
+                              : *reinterpret_cast<const uint2*>(dSt + (kt * NVT + s) * 256 + 4 * lane);
+        const uint2 v = kHold ? hS[kHold ? kt : 0]
+                              : *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(S) + (kt * NVT + s) * 256 + 4 * lane);
         dSv[kt][0] = bf2f((bf16_t)(w.x & 0xffffu));
         dSv[kt][1] = bf2f((bf16_t)(w.x >> 16));
         dSv[kt][2] = bf2f((bf16_t)(w.y & 0xffffu));
@@ -1708,9 +1725,14 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
     uint2 bs[NPT], bd[NPT];
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
-      const int i = min(tid + NTH * j, NLT - 1);
-      bs[j] = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(S) + 4 * i);
-      bd[j] = *reinterpret_cast<const uint2*>(dSt + 4 * i);
+      if constexpr (kHold) {  // lane-tile tid + NTH j is tile (j, wave), lane `lane`: the held words
+        bs[j] = hS[kHold ? j : 0];
+        bd[j] = hD[kHold ? j : 0];
+      } else {
+        const int i = min(tid + NTH * j, NLT - 1);
+        bs[j] = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(S) + 4 * i);
+        bd[j] = *reinterpret_cast<const uint2*>(dSt + 4 * i);
+      }
     }
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
