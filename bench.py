@@ -228,6 +228,51 @@ def _prefill_counter_lines(prof_dir, kname, avg_ns):
     return out
 
 
+# The segmented row's kernels, from a trace run of its own (the passes run the
+# plain pipelined kernel at the grid of the timed prefill, which they would
+# otherwise share a summary with).
+SEGMENTED_TRACE_CMD = ("cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d "
+                       "$R/gpurun_out/prof/trace_segmented -o trace -- python3 $R/bench.py "
+                       "--only segmented-row")
+SEGMENTED_PROFILES = [
+    ("segmented_B1_H4_T32768_d128.txt",
+     "deltanet_prefill_segmented B=1 H=4 T=32768 dk=dv=128 bf16, no gate, 16 segments of 2048 "
+     "tokens: start states and zeros, the two passes (pipelined kernel over 64 segment-heads; "
+     "value pass and transition pass, two calls each), the scan, the fix-up; and the one-pass "
+     "kernel on the same inputs",
+     ["seg_prepare", "prefill_pipe<0, 32, false>", "seg_mfrag<128>", "seg_scan<128>",
+      "seg_fixup<128, 128>", "prefill_pipe<0, 16, false>"]),
+    ("segmented_per_channel_gate_B1_H4_T32768_d128.txt",
+     "deltanet_prefill_segmented B=1 H=4 T=32768 dk=dv=128 bf16, a decay per key channel, 16 "
+     "segments: the gate pre-pass (once for both passes; the one-pass call runs it too, same "
+     "grid), the two gated passes, and the one-pass gated kernel",
+     ["gate_prep<128>", "prefill_pipe<1, 32, false>", "prefill_pipe<1, 16, false>"]),
+]
+
+
+def _trace_summaries(dispatches, profiles, trace_cmd):
+    """Per-kernel kernel-trace figures (calls, average, min, max) from
+    per-dispatch records, one summary file per entry of `profiles`."""
+    for fname, wl, kernels in profiles:
+        lines = [f"# rocprofv3 kernel-trace summary: {wl}",
+                 "# $R is the repository root; the command runs committed files only.",
+                 f"# command: {trace_cmd}", ""]
+        for spec in kernels:
+            kname, grid = spec if isinstance(spec, tuple) else (spec, None)
+            sel = [r for r in dispatches if kname in r["Kernel_Name"]
+                   and (grid is None or int(r["Grid_Size_X"]) == grid)]
+            names = {r["Kernel_Name"] for r in sel}
+            if len(names) != 1:
+                raise SystemExit(f"expected one kernel for '{kname}' (grid {grid}), found {len(names)}")
+            ns = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in sel]
+            lines += [f"kernel: {names.pop()}" + (f"   (grid {grid} threads)" if grid else ""),
+                      f"calls: {len(ns)}", f"average_ns: {sum(ns) / len(ns):.0f}",
+                      f"min_ns: {min(ns)}", f"max_ns: {max(ns)}", ""]
+        with open(os.path.join(PROFILES, fname), "w") as f:
+            f.write("\n".join(lines))
+        print(f"wrote profiles/{fname}")
+
+
 def summarize(prof_dir):
     """Write the rocprofv3 summaries in profiles/ from the raw output of the
     profiling commands listed in each summary (run from /tmp, repo at $R):
@@ -302,25 +347,11 @@ def summarize(prof_dir):
         print(f"wrote profiles/{fname}")
     # the other rows: kernel-trace figures only (same trace run), from the
     # per-dispatch records
-    dispatches = _csv_rows(os.path.join(prof_dir, "trace"), "kernel_trace.csv")
-    for fname, wl, kernels in ROW_PROFILES:
-        lines = [f"# rocprofv3 kernel-trace summary: {wl}",
-                 "# $R is the repository root; the command runs committed files only.",
-                 f"# command: {trace_cmd}", ""]
-        for spec in kernels:
-            kname, grid = spec if isinstance(spec, tuple) else (spec, None)
-            sel = [r for r in dispatches if kname in r["Kernel_Name"]
-                   and (grid is None or int(r["Grid_Size_X"]) == grid)]
-            names = {r["Kernel_Name"] for r in sel}
-            if len(names) != 1:
-                raise SystemExit(f"expected one kernel for '{kname}' (grid {grid}), found {len(names)}")
-            ns = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in sel]
-            lines += [f"kernel: {names.pop()}" + (f"   (grid {grid} threads)" if grid else ""),
-                      f"calls: {len(ns)}", f"average_ns: {sum(ns) / len(ns):.0f}",
-                      f"min_ns: {min(ns)}", f"max_ns: {max(ns)}", ""]
-        with open(os.path.join(PROFILES, fname), "w") as f:
-            f.write("\n".join(lines))
-        print(f"wrote profiles/{fname}")
+    _trace_summaries(_csv_rows(os.path.join(prof_dir, "trace"), "kernel_trace.csv"), ROW_PROFILES,
+                     trace_cmd)
+    if os.path.isdir(os.path.join(prof_dir, "trace_segmented")):
+        _trace_summaries(_csv_rows(os.path.join(prof_dir, "trace_segmented"), "kernel_trace.csv"),
+                         SEGMENTED_PROFILES, SEGMENTED_TRACE_CMD)
 
 
 def bench_prefill(la, workloads, torch, steps, warmup, copies=3):
@@ -677,77 +708,123 @@ def bench_token_gated_rows(la, workloads, torch, launches=20):
     return rows
 
 
-def bench_segmented_rows(la, workloads, torch, launches=10):
-    """The sequence-parallel chunk-state scan (prototype in
-    delta_rule_recurrent_chunkwise_amd/segmented.py) against the one-pass
-    prefill: at the gated workload's shape (per-channel and per-token gate,
-    B=1 H=32 T=32768) and with few heads (B=1 H=4 T=32768, no gate), for
-    several segment counts.  Each entry: the one-pass and segmented times per
-    call (HIP events around the whole call), the segmented call's steps, and
-    the segmented result's difference from the one-pass result."""
-    from delta_rule_recurrent_chunkwise_amd.segmented import (SegmentBuffers,
-                                                              segmented_delta_prefill)
+def bench_segmented_row(la, workloads, torch, launches=20):
+    """deltanet_prefill_segmented at the shape it is for, B=1 H=4 T=32768
+    d=128 (the automatic count: 16 segments of 2048 tokens), without a gate
+    and with a decay per key channel, next to the one-pass entry point on the
+    same inputs.  The roofline figure uses the operation's algorithmic bytes
+    (those of the one-pass prefill): the segmented call moves more, but the
+    row reports what the caller gets.  Timed by HIP events around each call
+    on the stream the kernels run on; profiled on its own (the passes run the
+    plain pipelined kernel at the grid of the timed prefill)."""
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
-    cases = [("per_channel_gate_B1_H32_T32768", 1, 32, True, False, (2, 4, 8)),
-             ("per_token_gate_B1_H32_T32768", 1, 32, "token", True, (2, 4, 8)),
-             ("no_gate_B1_H4_T32768", 1, 4, False, False, (2, 4, 8, 16, 32))]
+    B, H, T, d = 1, 4, 32768, 128
+    P = la.deltanet_prefill_segments(B, H, T, d, d)
+    nbytes, _ = prefill_algorithmic(B, H, T, d, d)
+    rows = {}
+    for name, gate in (("segmented_no_gate", None), ("segmented_per_channel_gate", "channel")):
+        gen = {None: False, "channel": True}[gate]
+        sets = []
+        for s in range(2):
+            inp = workloads.make_delta(B, H, T, d, d, torch.bfloat16, seed=90 + s, gated=gen)
+            sets.append({k: v.to(dev) for k, v in inp.items()})
+        o = torch.empty_like(sets[0]["v"])
+        S = torch.empty(B, H, d, d, device=dev, dtype=torch.float32)
+        ws1 = torch.empty(max(la.deltanet_prefill_workspace_bytes(gate is not None, B, H, T, d, d,
+                                                                  torch.bfloat16), 1),
+                          device=dev, dtype=torch.uint8)
+        ws = torch.empty(la.deltanet_prefill_segmented_workspace_bytes(gate, B, H, T, d, d,
+                                                                        torch.bfloat16, P),
+                         device=dev, dtype=torch.uint8)
+
+        def one(x):
+            la.deltanet_prefill(x["q"], x["k"], x["v"], x["beta"], g=x.get("g"), S=S, o=o,
+                                stream=stream, workspace=ws1)
+
+        def seg(x):
+            la.deltanet_prefill_segmented(x["q"], x["k"], x["v"], x["beta"], g=x.get("g"), gate=gate,
+                                          S=S, o=o, segments=P, stream=stream, workspace=ws)
+
+        us1, med1 = _time_launches(torch, stream, one, sets, launches)
+        us, med = _time_launches(torch, stream, seg, sets, launches)
+        wl = (f"deltanet_prefill_segmented B={B} H={H} T={T} dk=dv={d} bf16, {P} segments"
+              + (", a decay per key channel" if gate else ""))
+        _, r = _row(name, wl, us, med, nbytes)
+        r["segments"] = P
+        r["one_pass_avg_launch_us"] = us1
+        r["one_pass_median_launch_us"] = med1
+        r["speedup_over_one_pass"] = us1 / us
+        rows[name] = r
+        del sets, o, S, ws, ws1
+        torch.cuda.empty_cache()
+    return rows
+
+
+def bench_segmented_rows(la, workloads, torch, launches=10):
+    """deltanet_prefill_segmented (the sequence-parallel chunk-state scan)
+    against the one-pass prefill at the same shape: few heads with a long
+    sequence (B=1, H=4/8/16, T=32768, d=128; no gate, a decay per key
+    channel, one decay per token), where it is meant to win, and the gated
+    workload's shape (B=1 H=32 T=32768), where the automatic count declines
+    it.  Each entry: the one-pass time and, per segment count, the segmented
+    time per call (HIP events around the whole call on the stream the kernels
+    run on), the speedup, and the difference from the one-pass result."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
     T, d = 32768, 128
+    cases = [("no_gate_B1_H4_T32768", 4, None, (0, 4, 8, 16, 32)),
+             ("per_channel_gate_B1_H4_T32768", 4, "channel", (0, 8, 16)),
+             ("per_token_gate_B1_H4_T32768", 4, "token", (0, 8, 16)),
+             ("no_gate_B1_H8_T32768", 8, None, (0, 4, 16)),
+             ("no_gate_B1_H16_T32768", 16, None, (0, 2, 8)),
+             ("per_channel_gate_B1_H32_T32768", 32, "channel", (0, 2, 4))]
     out = {}
-    for name, B, H, gated, token, seg_counts in cases:
-        inp = workloads.make_delta(B, H, T, d, d, torch.bfloat16, seed=70 + H, gated=gated)
+    for name, H, gate, seg_counts in cases:
+        gen = {None: False, "channel": True, "token": "token"}[gate]
+        inp = workloads.make_delta(1, H, T, d, d, torch.bfloat16, seed=70 + H, gated=gen)
         x = {k: v.to(dev) for k, v in inp.items()}
         del inp
         g = x.get("g")
         o1 = torch.empty_like(x["v"])
-        S1 = torch.empty(B, H, d, d, device=dev, dtype=torch.float32)
+        S1 = torch.empty(1, H, d, d, device=dev, dtype=torch.float32)
+        ws1 = torch.empty(max(la.deltanet_prefill_workspace_bytes(gate == "channel", 1, H, T, d, d,
+                                                                  torch.bfloat16), 1),
+                          device=dev, dtype=torch.uint8)
 
         def one_pass(_):
-            if token:
+            if gate == "token":
                 la.gated_deltanet_prefill(x["q"], x["k"], x["v"], x["beta"], g, S=S1, o=o1,
                                           stream=stream)
             else:
                 la.deltanet_prefill(x["q"], x["k"], x["v"], x["beta"], g=g, S=S1, o=o1,
-                                    stream=stream)
+                                    stream=stream, workspace=ws1)
 
         us1, _ = _time_launches(torch, stream, one_pass, [None], launches, warmup=2)
-        entry = {"one_pass_us": us1, "segmented": {}}
+        one_pass(None)
+        entry = {"one_pass_us": us1, "auto_segments": la.deltanet_prefill_segments(1, H, T, d, d),
+                 "segmented": {}}
+        o2 = torch.empty_like(o1)
+        S2 = torch.empty_like(S1)
         for P in seg_counts:
-            buf = SegmentBuffers(B, H, T, d, d, P, torch.bfloat16, dev,
-                                 gated is not False and not token)
-            marks = []
+            ws = torch.empty(max(la.deltanet_prefill_segmented_workspace_bytes(
+                gate, 1, H, T, d, d, torch.bfloat16, P), 1), device=dev, dtype=torch.uint8)
 
-            def seg(_, rec=None):
-                segmented_delta_prefill(x["q"], x["k"], x["v"], x["beta"], P, g=g,
-                                        token_gate=token, buffers=buf, stream=stream,
-                                        timer=rec)
+            def seg(_):
+                la.deltanet_prefill_segmented(x["q"], x["k"], x["v"], x["beta"], g=g, gate=gate,
+                                              S=S2, o=o2, segments=P, stream=stream, workspace=ws)
 
             us, _ = _time_launches(torch, stream, seg, [None], launches, warmup=2)
-            # one more call with an event after every step
-            ev0 = torch.cuda.Event(enable_timing=True)
-            ev0.record(stream)
-
-            def rec(step):
-                e = torch.cuda.Event(enable_timing=True)
-                e.record(stream)
-                marks.append((step, e))
-
-            seg(None, rec)
+            seg(None)
             torch.cuda.synchronize()
-            steps, prev = {}, ev0
-            for step, e in marks:
-                steps[step + "_us"] = prev.elapsed_time(e) * 1e3
-                prev = e
-            one_pass(None)
-            torch.cuda.synchronize()
-            o_diff = ((buf.o0.view_as(o1).float() - o1.float()).abs().max()
-                      / o1.float().abs().max()).item()
-            s_diff = ((buf.S - S1).abs().max() / S1.abs().max()).item()
-            entry["segmented"][f"P{P}"] = {"us": us, "speedup": us1 / us, "steps": steps,
-                                           "o_rel_diff": o_diff, "S_rel_diff": s_diff}
-            del buf
+            o_diff = ((o2.float() - o1.float()).abs().max() / o1.float().abs().max()).item()
+            s_diff = ((S2 - S1).abs().max() / S1.abs().max()).item()
+            key = f"P{P}" if P else f"auto(P{entry['auto_segments']})"
+            entry["segmented"][key] = {"us": us, "speedup": us1 / us, "o_rel_diff": o_diff,
+                                       "S_rel_diff": s_diff}
+            del ws
         out[name] = entry
-        del x, o1, S1
+        del x, o1, S1, o2, S2, ws1
         torch.cuda.empty_cache()
     return out
 
@@ -934,7 +1011,8 @@ def main():
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the other rows (LA prefill, gated prefill, LA/gated decode)")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "copy", "rows", "token-rows",
-                                       "backward-row", "prologue-row", "segmented"],
+                                       "backward-row", "prologue-row", "segmented",
+                                       "segmented-row"],
                     default="all",
                     help="run one part only (for profiler runs)")
     ap.add_argument("--summarize", metavar="DIR",
@@ -977,6 +1055,9 @@ def main():
         return
     if args.only == "segmented":
         print(json.dumps(bench_segmented_rows(la, workloads, torch)))
+        return
+    if args.only == "segmented-row":
+        print(json.dumps(bench_segmented_row(la, workloads, torch)))
         return
     if args.only == "decode":
         wd, _, el = bench_decode(la, workloads, torch, args.decode_steps)

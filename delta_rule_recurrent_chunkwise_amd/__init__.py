@@ -20,7 +20,8 @@ __all__ = [
     "la_prefill", "la_decode_step", "deltanet_prefill", "deltanet_decode_step",
     "gated_deltanet_prefill", "gated_deltanet_decode_step", "gla_prefill",
     "gla_decode_step", "deltanet_prefill_backward", "gated_deltanet_prefill_backward",
-    "kda_prefill_backward", "deltanet_prologue", "la_strerror",
+    "kda_prefill_backward", "deltanet_prologue", "deltanet_prefill_segmented",
+    "deltanet_prefill_segments", "deltanet_prefill_segmented_workspace_bytes", "la_strerror",
     "la_prefill_workspace_bytes", "deltanet_prefill_workspace_bytes",
     "gla_prefill_workspace_bytes", "deltanet_prefill_backward_workspace_bytes",
     "gated_deltanet_prefill_backward_workspace_bytes", "kda_prefill_backward_workspace_bytes",
@@ -35,13 +36,15 @@ COMPUTE_ENTRIES = ("la_prefill", "la_decode_step", "deltanet_prefill",
                    "deltanet_decode_step", "gated_deltanet_prefill",
                    "gated_deltanet_decode_step", "gla_prefill", "gla_decode_step",
                    "deltanet_prefill_backward", "gated_deltanet_prefill_backward",
-                   "kda_prefill_backward", "deltanet_prologue")
+                   "kda_prefill_backward", "deltanet_prologue", "deltanet_prefill_segmented")
 WORKSPACE_QUERIES = ("la_prefill_workspace_bytes", "deltanet_prefill_workspace_bytes",
                      "gla_prefill_workspace_bytes",
                      "deltanet_prefill_backward_workspace_bytes",
                      "gated_deltanet_prefill_backward_workspace_bytes",
-                     "kda_prefill_backward_workspace_bytes")
-EXPORTED_SYMBOLS = COMPUTE_ENTRIES + WORKSPACE_QUERIES + ("la_prefill_noalloc", "la_strerror")
+                     "kda_prefill_backward_workspace_bytes",
+                     "deltanet_prefill_segmented_workspace_bytes")
+EXPORTED_SYMBOLS = COMPUTE_ENTRIES + WORKSPACE_QUERIES + ("deltanet_prefill_segments",
+                                                          "la_prefill_noalloc", "la_strerror")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 LA_DTYPE_F32, LA_DTYPE_BF16 = 0, 1
@@ -80,6 +83,7 @@ def library():
         lib.gated_deltanet_prefill_backward.argtypes = [P] * 14 + [I] * 6 + [P, Z, P]
         lib.kda_prefill_backward.argtypes = [P] * 14 + [I] * 6 + [P, Z, P]
         lib.deltanet_prologue.argtypes = [P] * 6 + [I] * 6 + [ctypes.c_float, I, P]
+        lib.deltanet_prefill_segmented.argtypes = [P] * 5 + [I, P, P] + [I] * 8 + [P, Z, P]
         for fn in COMPUTE_ENTRIES:
             getattr(lib, fn).restype = I
         lib.la_prefill_workspace_bytes.argtypes = [I] * 6
@@ -88,6 +92,9 @@ def library():
         lib.deltanet_prefill_backward_workspace_bytes.argtypes = [I] * 6
         lib.gated_deltanet_prefill_backward_workspace_bytes.argtypes = [I] * 6
         lib.kda_prefill_backward_workspace_bytes.argtypes = [I] * 6
+        lib.deltanet_prefill_segmented_workspace_bytes.argtypes = [I] * 8
+        lib.deltanet_prefill_segments.argtypes = [I] * 5
+        lib.deltanet_prefill_segments.restype = I
         for fn in WORKSPACE_QUERIES:
             getattr(lib, fn).restype = Z
         lib.la_prefill_noalloc.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
@@ -339,6 +346,56 @@ def gated_deltanet_prefill(q, k, v, beta, g, S=None, use_initial_state=False, o=
                                           B, H, T, dk, dv, _DTYPES[dtype],
                                           _stream(dev, stream))
     _check("gated_deltanet_prefill", rc)
+    return o, S
+
+
+_SEG_GATES = {None: 0, "channel": 1, "token": 2}
+
+
+def deltanet_prefill_segments(B, H, T, dk, dv) -> int:
+    """The segment count deltanet_prefill_segmented picks for segments=0
+    (1: one pass over the whole sequence; 0: invalid sizes)."""
+    return int(library().deltanet_prefill_segments(B, H, T, dk, dv))
+
+
+def deltanet_prefill_segmented_workspace_bytes(gate, B, H, T, dk, dv, dtype, segments=0) -> int:
+    """Bytes of workspace deltanet_prefill_segmented needs; gate is None,
+    "channel" (g [B,H,T,dk]) or "token" (g [B,H,T])."""
+    return int(library().deltanet_prefill_segmented_workspace_bytes(
+        _SEG_GATES[gate], B, H, T, dk, dv, _dt(dtype), int(segments)))
+
+
+def deltanet_prefill_segmented(q, k, v, beta, g=None, gate=None, S=None, use_initial_state=False,
+                               segments=0, o=None, stream=None, workspace=None):
+    """The delta rule of deltanet_prefill (gate None or "channel": g [B,H,T,dk])
+    or gated_deltanet_prefill (gate "token": g [B,H,T]) with each head's
+    sequence processed as `segments` segments side by side (0: the library
+    chooses; 1: one pass).  q, k [B,H,T,dk], v [B,H,T,dv], beta [B,H,T], bf16.
+    Returns (o [B,H,T,dv], S [B,H,dk,dv] fp32)."""
+    fn = "deltanet_prefill_segmented"
+    if gate not in _SEG_GATES:
+        raise ValueError(f"{fn}: gate must be None, 'channel' or 'token'")
+    if (g is None) != (gate is None):
+        raise ValueError(f"{fn}: g must be given exactly when gate is")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    gshape = (B, H, T, dk) if gate == "channel" else (B, H, T)
+    dev, dtype = _inputs(fn, dict(q=q, k=k, v=v, beta=beta, g=g),
+                         dict(q=(B, H, T, dk), k=(B, H, T, dk), v=(B, H, T, dv),
+                              beta=(B, H, T), g=gshape))
+    if use_initial_state and S is None:
+        raise ValueError(f"{fn}: use_initial_state needs S")
+    S = _state(fn, "S", S, (B, H, dk, dv), dev)
+    o = _out(fn, o, (B, H, T, dv), dev, dtype)
+    wp, wn, _keep = _workspace(
+        deltanet_prefill_segmented_workspace_bytes(gate, B, H, T, dk, dv, dtype, segments),
+        dev, workspace)
+    rc = library().deltanet_prefill_segmented(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                                              _SEG_GATES[gate], _ptr(o), _ptr(S),
+                                              int(bool(use_initial_state)), B, H, T, dk, dv,
+                                              _DTYPES[dtype], int(segments), wp, wn,
+                                              _stream(dev, stream))
+    _check(fn, rc)
     return o, S
 
 

@@ -19,6 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "liblinattn.so")
 SOURCES = ["api.hip", "decode.hip", "prefill.hip", "prefill_pipe.hip", "la_par.hip", "backward.hip", "prologue.hip",
+           "segmented.hip",
            "noalloc.hip"]
 # the measurement harness's MFMA peak probe, a library of its own
 PROBE_PATH = os.path.join(HERE, "libpeak_probe.so")

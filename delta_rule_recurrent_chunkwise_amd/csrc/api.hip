@@ -89,6 +89,47 @@ size_t kda_ws(int B, int H, int T, int dk, int dv, int dtype) {
   return linattn::kda_backward_workspace_bytes(a);
 }
 
+// Segmented prefill: the prefill mode of a gate kind (-1 for none valid).
+int seg_mode(int gate) {
+  return gate == 0 ? linattn::PF_DELTA : gate == 1 ? linattn::PF_GATED : gate == 2 ? linattn::PF_SGATED : -1;
+}
+
+// The segment count a call uses (0: chosen by the library); 0 when the
+// arguments are invalid for it.  Every check here precedes any HIP call.
+int seg_count(int B, int H, int T, int dv, int segments) {
+  if (segments < 0) return 0;
+  if (segments == 0) return linattn::segmented_auto_segments(B, H, T, dv);
+  return segments;
+}
+
+// The checks of deltanet_prefill_segmented after its pointers: LA_OK when
+// the call may proceed to its alignment and workspace checks.
+int seg_args_rc(int gate, int dtype, int B, int H, int T, int dk, int dv, int P) {
+  if (int rc = prefill_args_rc(dtype, B, H, T, dk, dv)) return rc;
+  if (seg_mode(gate) < 0 || P < 1) return LA_ERR_SHAPE;
+  if (P > 1) {
+    if (T % P != 0) return LA_ERR_SHAPE;
+    if ((long long)H * P > INT_MAX || !sizes_ok(B, (long long)H * P, T / P, dk, dv, true)) return LA_ERR_SHAPE;
+    if ((T / P + 255) / 256 > 65535) return LA_ERR_SHAPE;  // the fix-up's grid
+  }
+  if (dtype != LA_DTYPE_BF16) return LA_ERR_UNSUPPORTED_DIM;
+  return LA_OK;
+}
+
+size_t seg_ws(int gate, int B, int H, int T, int dk, int dv, int dtype, int segments) {
+  if (prefill_args_rc(dtype, B, H, T, dk, dv) != LA_OK) return 0;
+  const int P = seg_count(B, H, T, dv, segments);
+  if (P == 0 || seg_args_rc(gate, dtype, B, H, T, dk, dv, P) != LA_OK) return 0;
+  if (P == 1) return gate == 1 ? prefill_ws(linattn::PF_GATED, B, H, T, dk, dv, dtype) : 0;
+  if (T == 0) return 0;
+  linattn::PrefillArgs a{};
+  a.B = B;
+  a.H = H;
+  a.T = T;
+  a.dv = dv;
+  return linattn::segmented_layout(seg_mode(gate), dk, a, P).total;
+}
+
 }  // namespace
 
 extern "C" {
@@ -104,7 +145,8 @@ const char* la_strerror(int code) {
     case LA_ERR_UNSUPPORTED_DIM:
       return "unsupported head dimension: dk and dv must each be 16, 32, 64 or 128 "
              "(float32: dk <= 64 for deltanet_prefill with a per-channel gate, "
-             "dk and dv <= 64 for the backward entry points)";
+             "dk and dv <= 64 for the backward entry points; "
+             "bf16 only for kda_prefill_backward and deltanet_prefill_segmented)";
     case LA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     case LA_ERR_WORKSPACE:
       return "the workspace is NULL or smaller than the matching *_workspace_bytes() query returns";
@@ -295,6 +337,37 @@ int kda_prefill_backward(const void* q, const void* k, const void* v, const void
   if (int rc = workspace_rc(kda_ws(B, H, T, dk, dv, dtype), workspace, workspace_bytes)) return rc;
   linattn::BackwardArgs a{q, k, v, beta, S0, dO, dST, dq, dk_out, dv_out, dbeta, dS0, B, H, T, dk, dv, g, dg};
   return launch_rc(linattn::launch_kda_backward(a, workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t deltanet_prefill_segmented_workspace_bytes(int gate, int B, int H, int T, int dk, int dv,
+                                                  int dtype, int segments) {
+  return seg_ws(gate, B, H, T, dk, dv, dtype, segments);
+}
+
+int deltanet_prefill_segments(int B, int H, int T, int dk, int dv) {
+  if (prefill_args_rc(LA_DTYPE_BF16, B, H, T, dk, dv) != LA_OK) return 0;
+  return linattn::segmented_auto_segments(B, H, T, dv);
+}
+
+int deltanet_prefill_segmented(const void* q, const void* k, const void* v, const void* beta,
+                               const void* g, int gate, void* o, float* S, int use_initial_state,
+                               int B, int H, int T, int dk, int dv, int dtype, int segments,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!S || (T != 0 && (!q || !k || !v || !beta || !o))) return LA_ERR_NULL;
+  if (gate != 0 && T != 0 && !g) return LA_ERR_NULL;
+  if (int rc = prefill_args_rc(dtype, B, H, T, dk, dv)) return rc;
+  if (gate == 0 && g) return LA_ERR_SHAPE;
+  const int P = seg_count(B, H, T, dv, segments);
+  if (P == 0) return LA_ERR_SHAPE;
+  if (int rc = seg_args_rc(gate, dtype, B, H, T, dk, dv, P)) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LA_ERR_ALIGN;
+  if (int rc = workspace_rc(seg_ws(gate, B, H, T, dk, dv, dtype, segments), workspace, workspace_bytes))
+    return rc;
+  const int mode = seg_mode(gate);
+  linattn::PrefillArgs a{q, k, v, beta, g, o, S, nullptr, B, H, T, dv, use_initial_state ? 1 : 0};
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (P == 1 || T == 0) return launch_rc(linattn::launch_prefill(mode, 1, dk, a, workspace, st));
+  return launch_rc(linattn::launch_segmented(mode, dk, a, P, workspace, st));
 }
 
 int deltanet_prologue(const void* q_in, const void* k_in, const void* beta_logits, void* q_out,

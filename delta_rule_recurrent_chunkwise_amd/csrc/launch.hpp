@@ -113,6 +113,15 @@ hipError_t launch_la_par_states(int dk, const PrefillArgs& a, void* workspace, b
 // ... then every chunk's output from its chunk-start state (bf16).
 hipError_t launch_la_par_outputs(int dk, const PrefillArgs& a, void* workspace, bool gla, hipStream_t st);
 
+// The delta rule (mode PF_DELTA, PF_GATED or PF_SGATED, bf16) over each
+// head's sequence cut into P >= 2 segments of T / P tokens that run side by
+// side (segmented.hip): a pass from the caller's state over every segment, a
+// pass from the identity with v = 0 (each segment's transition), a scan of the
+// segments' incoming states, and a fix-up of the outputs.  The workspace is
+// segmented_layout(...).total bytes, 256-byte aligned.
+hipError_t launch_segmented(int mode, int dk, const PrefillArgs& a, int P, void* workspace,
+                            hipStream_t st);
+
 // ---------------------------------------------------------------------------
 // Workspace sizes (C = ceil(T/64) chunks per head)
 // ---------------------------------------------------------------------------
@@ -143,6 +152,64 @@ inline size_t prefill_workspace_bytes(int mode, int bf16, int dk, const PrefillA
   if (mode == PF_LA || mode == PF_GLA) return la_par_workspace_bytes(dk, a);
   if (mode == PF_GATED && dk == 128 && a.dv % 32 == 0) return gated_pipe_workspace_bytes(a);
   return 0;
+}
+
+// Segmented prefill with P segments (segment-heads n = B*H*P, Tp = T/P), each
+// region on a 256-byte boundary:
+//   Sz   fp32 [n][dk][dv]   every segment's final state from its own start
+//   M    fp32 [n][dk][dk]   every segment's transition (from the identity)
+//   oB   bf16 [n][Tp][dk]   the transition pass's outputs (rows M_t^T q_t)
+//   v0   bf16 [n][Tp][dk]   zeros: the transition pass's values
+//   F    bf16 [B*H][P-1][2][ceil(dk/32)][dv/16][64][8]: the incoming state of
+//        segments 1 .. P-1 as bf16 high and low parts, in MFMA B-operand order
+//   MF   bf16 [n][dk/16][2][ceil(dk/32)][64][8]: the transitions as high and
+//        low parts, in MFMA A-operand order
+//   prep the two passes' own workspace (the per-channel gate's pre-pass).
+struct SegmentedLayout {
+  size_t sz, m, ob, v0, f, mf, prep, total;
+};
+inline SegmentedLayout segmented_layout(int mode, int dk, const PrefillArgs& a, int P) {
+  SegmentedLayout L{};
+  const size_t n = (size_t)a.B * a.H * P, tp = (size_t)(a.T / P);
+  const size_t k32 = (size_t)(dk + 31) / 32;
+  PrefillArgs av = a, at = a;
+  av.H = at.H = a.H * P;
+  av.T = at.T = a.T / P;
+  at.dv = dk;
+  const size_t prep = prefill_workspace_bytes(mode, 1, dk, av) > prefill_workspace_bytes(mode, 1, dk, at)
+                          ? prefill_workspace_bytes(mode, 1, dk, av)
+                          : prefill_workspace_bytes(mode, 1, dk, at);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at_ = off;
+    off += workspace_round256(bytes);
+    return at_;
+  };
+  L.sz = take(n * dk * a.dv * sizeof(float));
+  L.m = take(n * dk * dk * sizeof(float));
+  L.ob = take(n * tp * dk * sizeof(uint16_t));
+  L.v0 = take(n * tp * dk * sizeof(uint16_t));
+  L.f = take((size_t)a.B * a.H * (P - 1) * 2 * k32 * (a.dv / 16) * 512 * sizeof(uint16_t));
+  L.mf = take(n * (dk / 16) * 2 * k32 * 512 * sizeof(uint16_t));
+  L.prep = take(prep);
+  L.total = off;
+  return L;
+}
+
+// The segment count chosen when the caller asks for it to be chosen: the
+// largest power of two P <= 64 for which one pass over the segments (as
+// B*H*P heads of 32 value columns per workgroup) still fits one wave of
+// workgroups on the 256 compute units, with at least 512 tokens per segment
+// and T % P == 0; 1 (one pass over the whole sequence) when that P is below 4,
+// since the two passes then cost more than the idle compute units.
+inline int segmented_auto_segments(int B, int H, int T, int dv) {
+  const long long units = (long long)B * H * (((long long)dv + 31) / 32);
+  int best = 1;
+  for (int P = 2; P <= 64; P *= 2) {
+    if (units * P > 256 || T % P != 0 || T / P < 512) break;
+    best = P;
+  }
+  return best >= 4 ? best : 1;
 }
 
 // Backward: each region starting on a 256-byte boundary,

@@ -40,9 +40,10 @@
  *           16 bytes); LA_ERR_ALIGN otherwise.  o must not alias any input.
  *           S (and z) are read and written.  The
  *           library keeps no state between calls; calls are re-entrant.  It
- *           never allocates device memory: the six entry points that need
- *           scratch memory on some paths (la_prefill, gla_prefill and
- *           deltanet_prefill, and the three backward entry points) take a
+ *           never allocates device memory: the seven entry points that need
+ *           scratch memory on some paths (la_prefill, gla_prefill,
+ *           deltanet_prefill, deltanet_prefill_segmented and the three
+ *           backward entry points) take a
  *           caller-owned workspace pointer and its size in bytes, and each
  *           has a *_workspace_bytes() query with the same sizes and dtype.
  *           The query returns 0 where no workspace is needed (the workspace
@@ -67,7 +68,8 @@
  *             - kda_prefill_backward: 388 B*H*C*dk (the gate pre-pass's
  *               copies and decays) + 4 B*H*C*dk*dv (the chunk states and
  *               their gradients, bf16) + 2 B*H*C*dk*(dk+64) (P and R^T),
- *               each region rounded up to 256 bytes.
+ *               each region rounded up to 256 bytes;
+ *             - deltanet_prefill_segmented: see its declaration.
  * Sizes.    B, H (or N, H) >= 1; T >= 0 for prefill, any length (the last
  *           64-token chunk may be partial).  T = 0 enqueues no work when
  *           use_initial_state is set and otherwise zero-fills S (and z);
@@ -361,6 +363,69 @@ int deltanet_prologue(const void *q_in, const void *k_in,
                       void *beta_out, int B, int H, int T, int dk,
                       int beta_heads, int apply_silu, float q_scale, int dtype,
                       void *stream);
+
+/*
+ * deltanet_prefill_segmented -- the delta rule of deltanet_prefill (gate 0:
+ * none; gate 1: a decay per key channel, g [B,H,T,dk]) or of
+ * gated_deltanet_prefill (gate 2: one decay per token, g [B,H,T]), with each
+ * head's sequence cut into P segments of T / P tokens that are processed side
+ * by side: the sequence-parallel chunk-state scan, for calls with few heads
+ * and long sequences, where one pass over the whole sequence leaves most of
+ * the GPU idle.  Article "From GPT-2 to Kimi K3, explained", section "DeltaNet
+ * (Parallelizing Linear Transformers with Delta Rule)": each chunk continues
+ * from the state the previous one leaves; since a run of tokens maps its
+ * incoming state affinely, S_out = M S_in + S_z, and each output likewise,
+ * o_t = o_t(from zero) + (M_t^T q_t)^T S_in, the segments' passes need not
+ * wait for each other:
+ *   1. every segment from its start state (segment 0 from S when
+ *      use_initial_state is set, the others from zero), outputs into o;
+ *   2. every segment from the identity with v = 0: its transition M (and the
+ *      rows M_t^T q_t);
+ *   3. the segments' incoming states by a scan with float32 accumulation
+ *      (the products take about 16 significant bits of each operand, as a
+ *      bf16 high and low part): S_in[1] = S_z[0],
+ *      S_in[p+1] = M[p] S_in[p] + S_z[p], and the final state
+ *      M[P-1] S_in[P-1] + S_z[P-1] into S;
+ *   4. o += (M_t^T q_t)^T S_in[p] for every token of segment p >= 1.
+ * The result is the recurrence's up to rounding (S_in enters step 4 with
+ * about 16 significant bits).  Arguments, layouts and errors as
+ * deltanet_prefill (gate 1), gated_deltanet_prefill (gate 2), plus:
+ *   gate      0, 1 or 2 as above; g must be NULL exactly when gate is 0
+ *             (LA_ERR_NULL for a missing g, LA_ERR_SHAPE for a g with gate
+ *             0 or a gate outside 0..2);
+ *   segments  P; 0 lets the library choose (deltanet_prefill_segments), 1
+ *             is one pass over the whole sequence (deltanet_prefill or
+ *             gated_deltanet_prefill).  P >= 2 must divide T
+ *             (LA_ERR_SHAPE otherwise);
+ *   dtype     LA_DTYPE_BF16 only (LA_ERR_UNSUPPORTED_DIM for float32).
+ * workspace: deltanet_prefill_segmented_workspace_bytes(gate, B, H, T, dk,
+ *   dv, dtype, segments) bytes, for P >= 2 (n = B*H*P segment-heads, each
+ *   region rounded up to 256 bytes): 4 n dk dv (every segment's state from
+ *   its start) + 4 n dk dk (transitions) + 4 B*H*T*dk (the transition pass's
+ *   outputs and its zero values, bf16) + 128 B*H*(P-1)*ceil(dk/32)*dv (the
+ *   incoming states as bf16 high and low parts) + 128 n dk ceil(dk/32) (the
+ *   transitions likewise) + what the two passes need
+ *   over B x H*P heads of T/P tokens (deltanet_prefill's workspace for a
+ *   per-channel gate); for P = 1 the one-pass entry point's.
+ */
+size_t deltanet_prefill_segmented_workspace_bytes(int gate, int B, int H,
+                                                  int T, int dk, int dv,
+                                                  int dtype, int segments);
+int deltanet_prefill_segmented(const void *q, const void *k, const void *v,
+                               const void *beta, const void *g, int gate,
+                               void *o, float *S, int use_initial_state, int B,
+                               int H, int T, int dk, int dv, int dtype,
+                               int segments, void *workspace,
+                               size_t workspace_bytes, void *stream);
+/*
+ * deltanet_prefill_segments -- the P that deltanet_prefill_segmented uses
+ * for segments = 0: the largest power of two up to 64 for which one pass
+ * over B*H*P heads (32 value columns per workgroup) still fits on the
+ * MI355X's 256 compute units at once, with T % P == 0 and at least 512 tokens
+ * per segment; 1 when that is below 4 (two passes over the sequence then cost
+ * more than the idle units).  0 for arguments the call would reject.
+ */
+int deltanet_prefill_segments(int B, int H, int T, int dk, int dv);
 
 /*
  * la_prefill_noalloc -- la_prefill for callers that cannot allocate device

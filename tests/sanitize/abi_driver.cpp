@@ -29,6 +29,7 @@ hipError_t launch_prefill_pipe(const PrefillArgs&, void*, hipStream_t) { ++g_lau
 hipError_t launch_prefill_pipe_token(const PrefillArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_la_par_states(int, const PrefillArgs&, void*, bool, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_la_par_outputs(int, const PrefillArgs&, void*, bool, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_segmented(int, int, const PrefillArgs&, int, void*, hipStream_t) { ++g_launches; return hipSuccess; }
 }  // namespace linattn
 
 static int failures = 0;
@@ -115,6 +116,17 @@ int main() {
         }
         n = g_launches;
         expect_ok(deltanet_prologue(F, F, F, F, F, F, 2, 3, 130, dk, 1, 1, 0.5f, dt, nullptr), n, true);
+        if (dt == LA_DTYPE_BF16) {
+          for (int gate = 0; gate < 3; ++gate)
+            for (int segs : {0, 1, 2, 5, 10}) {
+              const size_t sws = deltanet_prefill_segmented_workspace_bytes(gate, 2, 3, 130, dk, dv, dt, segs);
+              EXPECT(segs < 2 || sws > 0);
+              n = g_launches;
+              expect_ok(deltanet_prefill_segmented(F, F, F, F, gate ? F : nullptr, gate, F, (float*)F, 1, 2, 3, 130,
+                                                   dk, dv, dt, segs, F, sws, nullptr),
+                        n, true);
+            }
+        }
       }
   // T = 0 with the initial state kept: valid with NULL token arrays and no
   // workspace (the launcher then enqueues nothing)
@@ -138,6 +150,16 @@ int main() {
          LA_ERR_UNSUPPORTED_DIM);
   EXPECT(deltanet_prefill_backward(F, F, F, F, nullptr, F, nullptr, F, F, F, F, nullptr, 1, 1, 64, 64, 64, 1,
                                    nullptr, 0, nullptr) == LA_ERR_WORKSPACE);
+  EXPECT(deltanet_prefill_segmented(F, F, F, F, nullptr, 1, F, (float*)F, 0, 1, 1, 64, 64, 64, 1, 2, F, BIG,
+                                    nullptr) == LA_ERR_NULL);
+  EXPECT(deltanet_prefill_segmented(F, F, F, F, F, 0, F, (float*)F, 0, 1, 1, 64, 64, 64, 1, 2, F, BIG, nullptr) ==
+         LA_ERR_SHAPE);
+  EXPECT(deltanet_prefill_segmented(F, F, F, F, nullptr, 0, F, (float*)F, 0, 1, 1, 64, 64, 64, 1, 3, F, BIG,
+                                    nullptr) == LA_ERR_SHAPE);
+  EXPECT(deltanet_prefill_segmented(F, F, F, F, nullptr, 0, F, (float*)F, 0, 1, 1, 64, 64, 64, 0, 2, F, BIG,
+                                    nullptr) == LA_ERR_UNSUPPORTED_DIM);
+  EXPECT(deltanet_prefill_segmented(F, F, F, F, nullptr, 0, F, (float*)F, 0, 1, 1, 64, 64, 64, 1, 2, nullptr, 0,
+                                    nullptr) == LA_ERR_WORKSPACE);
   EXPECT(g_launches == before);
 
   // ---- a seeded sweep over extreme arguments: any outcome, no UB ----
@@ -154,7 +176,10 @@ int main() {
     (void)deltanet_prefill_backward_workspace_bytes(B, H, T, dk, dv, dt);
     (void)gated_deltanet_prefill_backward_workspace_bytes(B, H, T, dk, dv, dt);
     (void)kda_prefill_backward_workspace_bytes(B, H, T, dk, dv, dt);
-    int rc[12];
+    const int segs = pick_int(), gate = (int)(next() % 5) - 1;
+    (void)deltanet_prefill_segmented_workspace_bytes(gate, B, H, T, dk, dv, dt, segs);
+    (void)deltanet_prefill_segments(B, H, T, dk, dv);
+    int rc[13];
     rc[0] = la_prefill(p[0], p[1], p[2], p[3], (float*)p[4], (float*)p[5], gated, B, H, T, dk, dv, dt, ws, wsn, nullptr);
     rc[1] = la_decode_step(p[0], p[1], p[2], p[3], (float*)p[4], (float*)p[5], B, H, dk, dv, dt, nullptr);
     rc[2] = deltanet_prefill(p[0], p[1], p[2], p[3], gated ? p[6] : nullptr, p[4], (float*)p[5], gated, B, H, T, dk,
@@ -174,6 +199,8 @@ int main() {
                                nullptr);
     rc[11] = kda_prefill_backward(p[0], p[1], p[2], p[3], p[6], nullptr, p[4], nullptr, p[5], p[6], p[7], p[0], p[1],
                                   nullptr, B, H, T, dk, dv, dt, ws, wsn, nullptr);
+    rc[12] = deltanet_prefill_segmented(p[0], p[1], p[2], p[3], gated ? p[6] : nullptr, gate, p[4], (float*)p[5],
+                                        gated, B, H, T, dk, dv, dt, segs, ws, wsn, nullptr);
     for (int r : rc) EXPECT(r <= 0 && r >= LA_ERR_WORKSPACE);
   }
   for (int code = -10; code <= 2; ++code) EXPECT(la_strerror(code) != nullptr);

@@ -418,3 +418,79 @@ def test_noalloc_checks_its_limit_before_any_hip_call():
     assert call(q=None) == NULL and call(S=None) == NULL and call(z=None) == NULL
     assert call(dt=4) == DTYPE and call(B=0) == SHAPE and call(T=-1) == SHAPE
     assert call(dk=96) == DIM and call(q=MISALIGNED) == ALIGN
+
+
+def _seg(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=None, gate=0, o=FAKE, S=FAKE, init=0, B=1, H=1,
+         T=1024, dk=64, dv=64, dt=1, segs=4, ws=FAKE, wsn=BIG):
+    return la.library().deltanet_prefill_segmented(q, k, v, beta, g, gate, o, S, init, B, H, T, dk,
+                                                   dv, dt, segs, ws, wsn, None)
+
+
+@pytest.mark.parametrize("missing", ["q", "k", "v", "beta", "o", "S"])
+def test_segmented_null_pointers(missing):
+    assert _seg(**{missing: None}) == NULL
+    assert _seg(g=FAKE, gate=1, **{missing: None}) == NULL
+
+
+def test_segmented_validation():
+    assert _seg(gate=1) == NULL                   # a gate without g
+    assert _seg(gate=2) == NULL
+    assert _seg(g=FAKE) == SHAPE                  # g without a gate
+    assert _seg(g=FAKE, gate=3) == SHAPE
+    assert _seg(g=FAKE, gate=-1) == SHAPE
+    assert _seg(dt=3) == DTYPE
+    assert _seg(B=0) == SHAPE
+    assert _seg(segs=-1) == SHAPE
+    assert _seg(segs=3) == SHAPE                  # 1024 % 3 != 0
+    assert _seg(segs=2048) == SHAPE               # more segments than tokens
+    assert _seg(dk=96) == DIM
+    assert _seg(dt=0) == DIM                      # bf16 only
+    assert _seg(dt=0, segs=1) == DIM
+    for p in ("q", "k", "v", "o"):
+        assert _seg(**{p: MISALIGNED}) == ALIGN
+    need = la.deltanet_prefill_segmented_workspace_bytes(None, 1, 1, 1024, 64, 64, 1, 4)
+    assert need > 0
+    assert _seg(ws=None, wsn=0) == WORKSPACE
+    assert _seg(wsn=need - 1) == WORKSPACE
+    assert _seg(ws=P(0x1010)) == ALIGN
+
+
+def test_segmented_workspace_formula():
+    def r(n):
+        return (n + 255) // 256 * 256
+
+    for B, H, T, dk, dv, P in ((1, 4, 32768, 128, 128, 16), (2, 3, 1000, 64, 32, 8),
+                               (1, 1, 96, 16, 128, 3), (3, 2, 640, 128, 64, 5)):
+        n, Tp, k32 = B * H * P, T // P, (dk + 31) // 32
+        base = (r(4 * n * dk * dv) + r(4 * n * dk * dk) + 2 * r(2 * n * Tp * dk)
+                + r(128 * B * H * (P - 1) * k32 * dv) + r(128 * n * dk * k32))
+        for gate in (None, "token"):
+            assert la.deltanet_prefill_segmented_workspace_bytes(gate, B, H, T, dk, dv, 1, P) == base
+        prep = max(la.deltanet_prefill_workspace_bytes(True, B, H * P, Tp, dk, dv, 1),
+                   la.deltanet_prefill_workspace_bytes(True, B, H * P, Tp, dk, dk, 1))
+        assert la.deltanet_prefill_segmented_workspace_bytes("channel", B, H, T, dk, dv, 1, P) == \
+            base + r(prep)
+        assert la.deltanet_prefill_segmented_workspace_bytes(None, B, H, T, dk, dv, 0, P) == 0
+    # one segment: the one-pass entry points' workspace
+    assert la.deltanet_prefill_segmented_workspace_bytes(None, 1, 32, 4096, 128, 128, 1, 1) == 0
+    assert la.deltanet_prefill_segmented_workspace_bytes("channel", 1, 32, 4096, 128, 128, 1, 1) == \
+        la.deltanet_prefill_workspace_bytes(True, 1, 32, 4096, 128, 128, 1)
+    assert la.deltanet_prefill_segmented_workspace_bytes(None, 1, 1, 0, 64, 64, 1, 4) == 0  # T = 0
+    assert la.deltanet_prefill_segmented_workspace_bytes(None, 1, 1, 100, 64, 64, 1, 3) == 0  # 100 % 3
+
+
+def test_segment_count_rule():
+    """The automatic segment count: the largest power of two P <= 64 with
+    B*H*P*ceil(dv/32) <= 256, T % P == 0 and T/P >= 512, else 1 when below 4."""
+    seg = la.deltanet_prefill_segments
+    assert seg(1, 4, 32768, 128, 128) == 16
+    assert seg(1, 8, 32768, 128, 128) == 8
+    assert seg(1, 16, 32768, 128, 128) == 4
+    assert seg(1, 32, 32768, 128, 128) == 1      # two segments would not pay
+    assert seg(4, 16, 4096, 128, 128) == 1
+    assert seg(1, 4, 4096, 128, 128) == 8        # T / 16 = 256 tokens is too short
+    assert seg(1, 1, 65536, 64, 16) == 64
+    assert seg(2, 3, 3000, 128, 128) == 4        # T / 8 = 375 is too short
+    assert seg(1, 1, 100, 64, 64) == 1
+    assert seg(0, 1, 100, 64, 64) == 0           # invalid
+    assert seg(1, 1, 100, 96, 64) == 0
