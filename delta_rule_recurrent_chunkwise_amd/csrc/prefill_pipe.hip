@@ -532,10 +532,18 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
           // K^T fragments (K^ when gated): row 16t + c of the A operand is key
           // channel perm32(16t + c); its k-elements are the tokens of u's pairing.
           const bf16_t(*kt)[kLQ] = GATED ? sm.kh[GATED ? P : 0] : sm.k[kidx(x)];
-          const int trow = 4 * lg + ((lane >> 2) & 3);
+          // one lane base per chunk; every fragment is a compile-time offset
+          // from it (an immediate of the read).  The empty asm makes the base
+          // opaque: otherwise the compiler kept one loop-invariant address per
+          // fragment in a register and rebuilt all 32 from the chunk's buffer
+          // offset in every iteration (two vector operations each).
+          uint32_t ktb = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const bf16_t*)
+              &kt[4 * lg + ((lane >> 2) & 3)][8 * (lane & 3)];
+          asm volatile("" : "+v"(ktb));
+          const bf16_t* ktl = (const bf16_t*)(__attribute__((address_space(3))) const bf16_t*)(uintptr_t)ktb;
           auto kt_frag = [&](int t, int tok0) {
-            const int cc = 32 * (t >> 1) + 4 * (t & 1) + 8 * (lane & 3);
-            return cat_tr(ld_tr(&kt[tok0 + trow][cc]), ld_tr(&kt[tok0 + 16 + trow][cc]));
+            const int cc = 32 * (t >> 1) + 4 * (t & 1);
+            return cat_tr(ld_tr(ktl + tok0 * kLQ + cc), ld_tr(ktl + (tok0 + 16) * kLQ + cc));
           };
           bf16x8 fkt[2][8];
 #pragma unroll
