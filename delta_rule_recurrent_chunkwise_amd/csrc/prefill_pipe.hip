@@ -74,6 +74,24 @@ constexpr int kLR = 20;         // fp32 row stride inside a diagonal block of L
 constexpr int kLB = 16 * kLR + 16;  // fp32 stride between diagonal blocks
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer access for the loader and output waves: a resource whose base is
+// the chunk's first row and whose size ends at the chunk's last row that
+// exists.  A 16-byte access then needs only its lane's offset (loop-invariant,
+// with compile-time parts folded into the instruction's immediate) and no
+// per-access address arithmetic; accesses past the size read zeros and write
+// nothing (the hardware's range check on the vector offset).  0x00020000 is
+// the resource's fourth word for gfx9-family targets.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, off, 0, 0);
+}
 typedef short shortx4_t __attribute__((ext_vector_type(4)));
 
 // DVS: value columns per workgroup (32, or 16 when there are too few
@@ -240,16 +258,18 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
   auto issue_loads = [&](auto kindc, int chunk, auto& dst, uint32_t* bdst) {
     constexpr int KIND = decltype(kindc)::value;
     if constexpr (KIND == 1) {
-      const bf16_t* const pq = qh;  // register copies: a select among captured
-      const bf16_t* const pk = kh;  // references would go through memory
-      const bf16_t* const pkh = khh;
+      // rows of the chunk that exist (chunk <= nch - 1: at least one); rows
+      // past them read zeros, which get beta = 0 where they are staged
+      const int rows = min(qlast + 1 - chunk * kC, kC);
+      const uint32_t nb = (uint32_t)rows * kDK * 2;
+      const size_t cb = (size_t)chunk * kC * kDK;
+      const rsrc_t r0 = buf_rsrc(qh + cb, nb), r1 = buf_rsrc(kh + cb, nb);
+      const rsrc_t r2 = GATED ? buf_rsrc(khh + cb, nb) : r1;
 #pragma unroll
       for (int j = 0; j < LP::NT; ++j) {
         const int t = LP::tile_of(wave, j);
-        const bf16_t* base = t == 0 ? pq : (t == 1 ? pk : pkh);
         const int vv = LP::vec_of(wave, lane, j);
-        const int row = min(chunk * kC + (vv >> 4), qlast);
-        dst[j] = *reinterpret_cast<const u32x4*>(base + (size_t)row * kDK + (vv & 15) * 8);
+        dst[j] = buf_load16(t == 0 ? r0 : (t == 1 ? r1 : r2), (uint32_t)((vv >> 4) * kDK + (vv & 15) * 8) * 2);
       }
     } else if constexpr (KIND == 2) {  // wave 7
 #pragma unroll
@@ -765,13 +785,16 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
     // one place where rows past the end are skipped.
     const int sw = tid - 256;  // 0..63 on wave 4
     auto store_o = [&](int chunk, auto tailc) {
+      // the resource ends at the last element of the slice's last row that
+      // exists, so rows past the end are not written (and the tail skips them)
+      const int rows = min(Tn - chunk * kC, kC);
+      const rsrc_t ro = buf_rsrc(oh + (size_t)chunk * kC * dv, (uint32_t)((rows - 1) * dv + kDVS) * 2);
 #pragma unroll
       for (int j = 0; j < kC * VPRV / 64; ++j) {
         const int vi = sw + 64 * j;
         const int r = vi / VPRV, c8 = (vi % VPRV) * 8;
         if (decltype(tailc)::value && chunk * kC + r > tlast) continue;
-        *reinterpret_cast<u32x4*>(oh + (size_t)(chunk * kC + r) * dv + c8) =
-            *reinterpret_cast<const u32x4*>(&sm.o[chunk & 1][r][c8]);
+        buf_store16(ro, (uint32_t)(r * dv + c8) * 2, *reinterpret_cast<const u32x4*>(&sm.o[chunk & 1][r][c8]));
       }
     };
     auto ph1 = [&](const int x, auto parity) {};
