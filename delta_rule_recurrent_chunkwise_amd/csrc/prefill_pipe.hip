@@ -394,6 +394,12 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
         for (int i = 0; i < 4; ++i) st[t][i] = Sh[(size_t)perm32(16 * t + 4 * lg + i) * dv + col];
       }
     }
+    // Without the per-channel gate ox[mt] holds the output tile transposed
+    // (the output products take their operands in swapped order): lane
+    // (lc, lg) has token 16mt + lc, value columns 16wave + 4lg .. +3, one
+    // 8-byte LDS store instead of four 2-byte ones.  The per-channel gated
+    // kernel keeps the untransposed tile (the swap made it spill).
+    constexpr bool kOT = !GATED;
     floatx4 xx[4], ox[4];
     // Per-channel gate, a chunk the pre-pass marked (Gam_C < 0): its decay
     // leaves the range of the factored form, so it is walked token by token
@@ -491,7 +497,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
               y[mt] = mfma_k32(fk[kb & 1][mt], b, y[mt]);
-              ox[mt] = mfma_k32(fq[kb & 1][mt], b, ox[mt]);
+              ox[mt] = kOT ? mfma_k32(b, fq[kb & 1][mt], ox[mt]) : mfma_k32(fq[kb & 1][mt], b, ox[mt]);
             }
           }
 #pragma unroll
@@ -503,7 +509,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
             if constexpr (TOKG) {  // rows of K S and Q S decay by exp(G_r)
               const float4 dc = *reinterpret_cast<const float4*>(&sm.gs[TOKG ? P : 0][1][16 * mt + 4 * lg]);
               y[mt][0] *= dc.x; y[mt][1] *= dc.y; y[mt][2] *= dc.z; y[mt][3] *= dc.w;
-              ox[mt][0] *= dc.x; ox[mt][1] *= dc.y; ox[mt][2] *= dc.z; ox[mt][3] *= dc.w;
+              ox[mt] *= sm.gs[TOKG ? P : 0][1][16 * mt + lc];  // the lane's token
             }
             xx[mt][0] = bt.x * (bf2f((bf16_t)vw[0]) - y[mt][0]);
             xx[mt][1] = bt.y * (bf2f((bf16_t)vw[1]) - y[mt][1]);
@@ -571,10 +577,17 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
           const bf16x8 u01 = acc_pair_to_b(ut[0], ut[1]);
           const bf16x8 u23 = acc_pair_to_b(ut[2], ut[3]);
           // O += tril(Q K^T) u
-          ox[0] = mfma_k32(fa[0], u01, ox[0]);
-          ox[1] = mfma_k32(fa[1], u01, ox[1]);
-          ox[2] = mfma_k32(fa[3], u23, mfma_k32(fa[2], u01, ox[2]));
-          ox[3] = mfma_k32(fa[5], u23, mfma_k32(fa[4], u01, ox[3]));
+          if constexpr (kOT) {
+            ox[0] = mfma_k32(u01, fa[0], ox[0]);
+            ox[1] = mfma_k32(u01, fa[1], ox[1]);
+            ox[2] = mfma_k32(u23, fa[3], mfma_k32(u01, fa[2], ox[2]));
+            ox[3] = mfma_k32(u23, fa[5], mfma_k32(u01, fa[4], ox[3]));
+          } else {
+            ox[0] = mfma_k32(fa[0], u01, ox[0]);
+            ox[1] = mfma_k32(fa[1], u01, ox[1]);
+            ox[2] = mfma_k32(fa[3], u23, mfma_k32(fa[2], u01, ox[2]));
+            ox[3] = mfma_k32(fa[5], u23, mfma_k32(fa[4], u01, ox[3]));
+          }
 #pragma unroll
           for (int t = 0; t < 8; ++t) fkt[1][t] = kt_frag(t, 32);
           // S += K^T u (per-token gate: rows of u decay by exp(G_C - G_r))
@@ -606,10 +619,17 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
               st[t][3] *= gv.w;
             }
           }
+          if constexpr (kOT) {
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < 4; ++mt)
+              *reinterpret_cast<uint2*>(&sm.o[P][16 * mt + lc][16 * wave + 4 * lg]) =
+                  make_uint2(pack2(ox[mt][0], ox[mt][1]), pack2(ox[mt][2], ox[mt][3]));
+          } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sm.o[P][16 * mt + 4 * lg + i][col] = f2bf(ox[mt][i]);
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sm.o[P][16 * mt + 4 * lg + i][col] = f2bf(ox[mt][i]);
+          }
         },
         std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
     if (a.o != nullptr) {  // the backward pass (no output) needs only the chunk states
