@@ -1265,16 +1265,18 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
   if constexpr (kBf16) {
     // D_b: lane (block lg, column lc) solves (I + L_bb) x = e_lc
     if (wave == 0) {
+      // right-looking: once x_m is known it is folded into the partial sums
+      // of every later row, so one multiply-add separates x_m from x_{m+1}
+      // (x_m = 0 for m < lc, x_lc = 1)
       const float* lb = sLd + 16 * lg * 20;
-      float x[16];
+      float x[16], ps[16];
 #pragma unroll
-      for (int m = 0; m < 16; ++m) x[m] = m == lc ? 1.f : 0.f;
+      for (int i = 0; i < 16; ++i) ps[i] = 0.f;
 #pragma unroll
-      for (int i = 1; i < 16; ++i) {
-        float sacc = 0.f;
+      for (int m = 0; m < 16; ++m) {
+        x[m] = m < lc ? 0.f : (m == lc ? 1.f : -ps[m]);
 #pragma unroll
-        for (int m = 0; m < i; ++m) sacc += lb[i * 20 + m] * x[m];
-        if (i > lc) x[i] = -sacc;
+        for (int i = m + 1; i < 16; ++i) ps[i] += lb[i * 20 + m] * x[m];
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) sD[(16 * lg + i) * 16 + lc] = f2bf(x[i]);
@@ -1286,6 +1288,16 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
     if (wave < 4) {
       const int ct = wave;
       auto blk = [&](const bf16_t* b) { return *reinterpret_cast<const shortx4*>(b + lc * 16 + 4 * lg); };
+      // every block first: the stores of T below would otherwise keep each
+      // read in the chain behind them
+      shortx4 fl[6], fd[4];
+#pragma unroll
+      for (int i = 0; i < 6; ++i) fl[i] = blk(sLo + i * 256);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) fd[b] = blk(sD + 256 * b);
+      float dct[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dct[i] = bf2f(sD[(16 * ct + 4 * lg + i) * 16 + lc]);
       floatx4 tb[4];
       shortx4 tb16[4];
 #pragma unroll
@@ -1294,11 +1306,13 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
           tb[b] = zero4();
         } else if (b == ct) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) tb[b][i] = bf2f(sD[(16 * b + 4 * lg + i) * 16 + lc]);
+          for (int i = 0; i < 4; ++i) tb[b][i] = dct[i];
         } else {
           floatx4 acc = zero4();
-          for (int j = ct; j < b; ++j) acc = mfma_k16(blk(sLo + (b * (b - 1) / 2 + j) * 256), tb16[j], acc);
-          tb[b] = -mfma_k16(blk(sD + 256 * b), acc_to_b16(acc), zero4());
+#pragma unroll
+          for (int j = 0; j < b; ++j)
+            if (j >= ct) acc = mfma_k16(fl[b * (b - 1) / 2 + j], tb16[j], acc);
+          tb[b] = -mfma_k16(fd[b], acc_to_b16(acc), zero4());
         }
         tb16[b] = acc_to_b16(tb[b]);
 #pragma unroll
