@@ -80,14 +80,16 @@ __device__ void form_T(float* sTL, int tid, int wave, int lane) {
   if (wave == NTH / 64 - 1) {
     const int b0 = 16 * lg;
     float tv[16];
+    // right-looking: once tv[m] is known it is folded into the partial sums of
+    // every later row, so one multiply-add separates tv[m] from tv[m+1]
+    float ps[16];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) tv[m] = m == lc ? 1.f : 0.f;
+    for (int i = 0; i < 16; ++i) ps[i] = 0.f;
 #pragma unroll
-    for (int i = 1; i < 16; ++i) {
-      float s = 0.f;
+    for (int m = 0; m < 16; ++m) {
+      tv[m] = m < lc ? 0.f : (m == lc ? 1.f : -ps[m]);
 #pragma unroll
-      for (int m = 0; m < i; ++m) s += sTL[(b0 + m) * LTL + b0 + i] * tv[m];
-      if (i > lc) tv[i] = -s;
+      for (int i = m + 1; i < 16; ++i) ps[i] += sTL[(b0 + m) * LTL + b0 + i] * tv[m];
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -734,17 +736,18 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
   __syncthreads();
 
   // 3. D_b: lane (block lg, column lc) solves (I + L_bb) x = e_lc
+  // (right-looking: once x_m is known it is folded into the partial sums of
+  // every later row, so one multiply-add separates x_m from x_{m+1})
   if (wave == 0) {
     const float* lb = sLd + 16 * lg * LD;
-    float x[16];
+    float x[16], ps[16];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) x[m] = m == lc ? 1.f : 0.f;
+    for (int i = 0; i < 16; ++i) ps[i] = 0.f;
 #pragma unroll
-    for (int i = 1; i < 16; ++i) {
-      float s = 0.f;
+    for (int m = 0; m < 16; ++m) {
+      x[m] = m < lc ? 0.f : (m == lc ? 1.f : -ps[m]);
 #pragma unroll
-      for (int m = 0; m < i; ++m) s += lb[i * LD + m] * x[m];
-      if (i > lc) x[i] = -s;
+      for (int i = m + 1; i < 16; ++i) ps[i] += lb[i * LD + m] * x[m];
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) sD[(16 * lg + i) * 16 + lc] = f2bf(x[i]);

@@ -500,14 +500,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
       if (wave == kWaves - 1) {
         const int b0 = 16 * lg;
         float tv[16];
+        // right-looking: once tv[m] is known it is folded into the partial sums of
+        // every later row, so one multiply-add separates tv[m] from tv[m+1]
+        float ps[16];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) tv[m] = m == lc ? 1.f : 0.f;
+        for (int i = 0; i < 16; ++i) ps[i] = 0.f;
 #pragma unroll
-        for (int i = 1; i < 16; ++i) {
-          float s = 0.f;
+        for (int m = 0; m < 16; ++m) {
+          tv[m] = m < lc ? 0.f : (m == lc ? 1.f : -ps[m]);
 #pragma unroll
-          for (int m = 0; m < i; ++m) s += sTL[(b0 + m) * LTL + b0 + i] * tv[m];
-          if (i > lc) tv[i] = -s;
+          for (int i = m + 1; i < 16; ++i) ps[i] += sTL[(b0 + m) * LTL + b0 + i] * tv[m];
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i)
