@@ -228,6 +228,45 @@ def _prefill_counter_lines(prof_dir, kname, avg_ns):
     return out
 
 
+# Rows whose summaries also carry HBM counters, each from FETCH_SIZE and
+# WRITE_SIZE runs of their own (bench.py --only MODE): (summary file, mode,
+# kernels of one call, the call's algorithmic bytes).
+ROW_COUNTERS = [
+    ("prefill_pipe_gated_B1_H32_T32768_d128.txt", "gated-row",
+     ["gate_prep<128>", "prefill_pipe<1, 16, false>"], lambda: gated_algorithmic(1, 32, 32768, 128, 128)),
+    ("la_par_B8_H12_T1024_d64.txt", "la-rows",
+     ["la_chunk_state<64, 64, false>", "la_state_scan<false>", "la_chunk_out<64, 64, false>"],
+     lambda: la_algorithmic(8, 12, 1024, 64, 64, 2)),
+]
+
+
+def _row_counter_lines(prof_dir, mode, kernels, alg, cal):
+    """HBM bytes of each kernel of one call (FETCH_SIZE and WRITE_SIZE per
+    dispatch, scaled by the copy calibration) and their sum against the
+    call's algorithmic bytes."""
+    cmd = ("cd /tmp && rocprofv3 --pmc {c} -f csv -d $R/gpurun_out/prof/pmc_{c}_{m} -o pmc "
+           "-- python3 $R/bench.py --only {m}")
+    out = ["## HBM counters, one run per counter",
+           f"#   {cmd.format(c='FETCH_SIZE', m=mode)}",
+           f"#   {cmd.format(c='WRITE_SIZE', m=mode)}",
+           f"#   calibration: scale {cal['FETCH_SIZE'][1]:.4f} (fetch), {cal['WRITE_SIZE'][1]:.4f} (write), "
+           "from the copy runs of the headline summary"]
+    total = 0.0
+    for k in kernels:
+        f_kib, n = _counter_mean(os.path.join(prof_dir, f"pmc_FETCH_SIZE_{mode}"), "FETCH_SIZE", k)
+        w_kib, _ = _counter_mean(os.path.join(prof_dir, f"pmc_WRITE_SIZE_{mode}"), "WRITE_SIZE", k)
+        rd = f_kib * 1024.0 * cal["FETCH_SIZE"][1]
+        wr = w_kib * 1024.0 * cal["WRITE_SIZE"][1]
+        total += rd + wr
+        out += [f"counters: {k}   (dispatches {n})",
+                f"  hbm_read_bytes_per_launch: {rd:.0f}",
+                f"  hbm_write_bytes_per_launch: {wr:.0f}"]
+    out += [f"hbm_bytes_per_call: {total:.0f}",
+            f"algorithmic_bytes_per_call: {alg}",
+            f"traffic_over_algorithmic: {total / alg:.3f}", ""]
+    return out
+
+
 # The segmented row's kernels, from a trace run of its own (the passes run the
 # plain pipelined kernel at the grid of the timed prefill, which they would
 # otherwise share a summary with).
@@ -349,6 +388,12 @@ def summarize(prof_dir):
     # per-dispatch records
     _trace_summaries(_csv_rows(os.path.join(prof_dir, "trace"), "kernel_trace.csv"), ROW_PROFILES,
                      trace_cmd)
+    for fname, mode, kernels, alg in ROW_COUNTERS:
+        if not os.path.isdir(os.path.join(prof_dir, f"pmc_FETCH_SIZE_{mode}")):
+            continue
+        with open(os.path.join(PROFILES, fname), "a") as f:
+            f.write("\n".join(_row_counter_lines(prof_dir, mode, kernels, alg(), cal)))
+        print(f"added counters to profiles/{fname}")
     if os.path.isdir(os.path.join(prof_dir, "trace_segmented")):
         _trace_summaries(_csv_rows(os.path.join(prof_dir, "trace_segmented"), "kernel_trace.csv"),
                          SEGMENTED_PROFILES, SEGMENTED_TRACE_CMD)
@@ -442,18 +487,29 @@ def _row(name, workload, us, med_us, nbytes, note=None):
     return name, r
 
 
-def bench_rows(la, workloads, torch, launches=20):
-    """The remaining rows of the path, each timed on its own workload: linear
-    attention prefill (fp32 and bf16), the gated delta-rule prefill, and the
-    linear-attention and gated decode steps at the decode workload's shape."""
+def la_algorithmic(B, H, T, dk, dv, elem_bytes):
+    """Bytes a linear-attention prefill must move: q, k, v in and o out, and
+    the final state S and normaliser z (fp32)."""
+    return B * H * (T * 2 * (dk + dv) * elem_bytes + (dk * dv + dk) * 4)
+
+
+def gated_algorithmic(B, H, T, dk, dv):
+    """Bytes the per-channel gated delta-rule prefill must move (bf16): q, k,
+    g (one log-decay per key channel), v and beta in, o out, and the final
+    fp32 state."""
+    return B * H * (T * 2 * (3 * dk + 2 * dv + 1) + dk * dv * 4)
+
+
+def bench_la_rows(la, workloads, torch, launches=20):
+    """The linear-attention prefill rows (fp32 and bf16), each on its own
+    workload, with several input copies cycled."""
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     rows = {}
     W = workloads.WORKLOADS
     for w in (W[0], W[1]):
         inp = workloads.make_workload(w)
-        per = w.B * w.H * (w.T * 2 * (w.dk + w.dv) * (4 if w.dtype == torch.float32 else 2)
-                           + (w.dk * w.dv + w.dk) * 4)
+        per = la_algorithmic(w.B, w.H, w.T, w.dk, w.dv, 4 if w.dtype == torch.float32 else 2)
         copies = max(1, min(8, -(-600_000_000 // per)))
         sets = []
         for _ in range(copies):
@@ -472,7 +528,14 @@ def bench_rows(la, workloads, torch, launches=20):
                        "latency-bound: one 64-token chunk" if w.T == 64 else None)
         rows[f"{name}_{w.name}"] = r
         del sets
-    w = W[3]
+    return rows
+
+
+def bench_gated_row(la, workloads, torch, launches=20):
+    """The per-channel gated delta-rule prefill on the gated workload."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    w = workloads.WORKLOADS[3]
     inp = workloads.make_workload(w)
     d = {k: v.to(dev) for k, v in inp.items()}
     d["o"] = torch.empty_like(d["v"])
@@ -484,13 +547,22 @@ def bench_rows(la, workloads, torch, launches=20):
                             stream=stream)
 
     us, med = _time_launches(torch, stream, run_g, [d], max(3, launches // 4), warmup=1)
-    per = w.B * w.H * (w.T * 2 * (3 * w.dk + 2 * w.dv + 1) + w.dk * w.dv * 4)
+    per = gated_algorithmic(w.B, w.H, w.T, w.dk, w.dv)
     name, r = _row("deltanet_prefill_gated", f"deltanet_prefill (gated) {w.name}", us, med, per,
                    "gate pre-pass, then a serial chain over 512 chunks; 32 heads x 8 value "
                    "slices of 16 = 256 workgroups")
-    rows[name] = r
-    del d
-    wd = W[4]
+    return {name: r}
+
+
+def bench_rows(la, workloads, torch, launches=20):
+    """The remaining rows of the path, each timed on its own workload: linear
+    attention prefill (fp32 and bf16), the gated delta-rule prefill, and the
+    linear-attention and gated decode steps at the decode workload's shape."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    rows = bench_la_rows(la, workloads, torch, launches)
+    rows.update(bench_gated_row(la, workloads, torch, launches))
+    wd = workloads.WORKLOADS[4]
     N, H, dk, dv = wd.B, wd.H, wd.dk, wd.dv
     li = workloads.make_la_decode(N, H, dk, dv, wd.dtype, seed=77)
     d = {k: v.to(dev) for k, v in li.items()}
@@ -1012,7 +1084,7 @@ def main():
                     help="skip the other rows (LA prefill, gated prefill, LA/gated decode)")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "copy", "rows", "token-rows",
                                        "backward-row", "prologue-row", "segmented",
-                                       "segmented-row"],
+                                       "segmented-row", "la-rows", "gated-row"],
                     default="all",
                     help="run one part only (for profiler runs)")
     ap.add_argument("--summarize", metavar="DIR",
@@ -1043,6 +1115,12 @@ def main():
         return
     if args.only == "rows":
         print(json.dumps(bench_rows(la, workloads, torch)))
+        return
+    if args.only == "la-rows":
+        print(json.dumps(bench_la_rows(la, workloads, torch)))
+        return
+    if args.only == "gated-row":
+        print(json.dumps(bench_gated_row(la, workloads, torch)))
         return
     if args.only == "token-rows":
         print(json.dumps(bench_token_gated_rows(la, workloads, torch)))
