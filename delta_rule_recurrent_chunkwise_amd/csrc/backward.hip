@@ -243,13 +243,16 @@ template <class E, int D, bool RF, int NTH>
 struct RowTile {
   typedef typename E::T T;
   static constexpr int KV = E::kVec, VPR = D / KV, NV = kC * VPR, NPT = (NV + NTH - 1) / NTH;
-  Vec16U<E> buf[NPT];
+  typedef uint32_t w4 __attribute__((ext_vector_type(4)));
+  // plain vectors: an array of unions went through scratch memory, whose
+  // accesses the compiler then waited for between the loads
+  w4 buf[NPT];
   __device__ __forceinline__ void load(const T* src, int sld, int t0, int nrow, int tid) {
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
       const int i = min(tid + NTH * j, NV - 1);
       const int r = min(RF ? i % kC : i / VPR, nrow - 1);
-      buf[j].v = *reinterpret_cast<const Vec16*>(src + (size_t)(t0 + r) * sld + (RF ? i / kC : i % VPR) * KV);
+      buf[j] = *reinterpret_cast<const w4*>(src + (size_t)(t0 + r) * sld + (RF ? i / kC : i % VPR) * KV);
     }
   }
   __device__ __forceinline__ void store(int nrow, T* dst, int ld, T* dstT, int ldT, int tid) {
@@ -258,10 +261,12 @@ struct RowTile {
       const int i = tid + NTH * j;
       if (NV % NTH != 0 && i >= NV) continue;
       const int r = RF ? i % kC : i / VPR, d = (RF ? i / kC : i % VPR) * KV;
-      Vec16U<E> x = buf[j];
-      if (r >= nrow) x.v = Vec16{};
-      if (dst) *reinterpret_cast<Vec16*>(dst + r * ld + d) = x.v;
-      if (dstT) {
+      const w4 z = {0u, 0u, 0u, 0u};
+      const w4 w = r < nrow ? buf[j] : z;
+      if (dst) *reinterpret_cast<w4*>(dst + r * ld + d) = w;
+      if (dstT) {  // elements through one local union, as in stage_rows
+        Vec16U<E> x;
+        x.v = __builtin_bit_cast(Vec16, w);
 #pragma unroll
         for (int e = 0; e < KV; ++e) dstT[(d + e) * ldT + r] = x.e[e];
       }
@@ -1176,19 +1181,17 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
   const bf16_t* dSt = reinterpret_cast<const bf16_t*>(dSc) + (size_t)chunk * DK * DV;
 
   // Ungated, bf16, dv = 128 (eight 16-column slices, one per wave): this
-  // wave's slice of S and dSn, loaded now (in flight with phase A's loads),
-  // read by phase B and staged into LDS for phase E without a second load.
-  // (The gated kernels have no registers to spare for it; with a
-  // per-channel decay it measured no gain.)
+  // wave's slice of S and dSn, loaded with phase A's loads (after them, so
+  // that storing the staged tiles does not wait for these), read by phase B
+  // and staged into LDS for phase E without a second load.  (The gated
+  // kernels have no registers to spare for it; with a per-channel decay it
+  // measured no gain.)
   constexpr bool kHold = kBf16 && !GATE && !KDA && NVT == NW;
   uint2 hS[kHold ? NKT : 1], hD[kHold ? NKT : 1];
-  if constexpr (kHold) {
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-      hD[kt] = *reinterpret_cast<const uint2*>(dSt + (kt * NVT + wave) * 256 + 4 * lane);
-      hS[kt] = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(S) + (kt * NVT + wave) * 256 + 4 * lane);
-    }
-  }
+  // and (the same kernels) the V and dO entries phase B reads, rows 16mt +
+  // 4lg + i of column 16 wave + lc: loaded at the start, they arrive while
+  // phase A runs instead of holding up phase B's first product
+  T hV[kHold ? 16 : 1], hO[kHold ? 16 : 1];
 
   // ---- phase A ----
   T* sQ = reinterpret_cast<T*>(smem + L::aQ);
@@ -1203,20 +1206,51 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
   float* sLd = reinterpret_cast<float*>(smem + L::aLd);
   T* sKh = reinterpret_cast<T*>(smem + L::aKh);
   const size_t tile0 = (size_t)chunk * kC * DK;  // KDA: this chunk's rows of the pre-pass tiles
+  // Every staging load is issued before any of them is stored (one round
+  // trip to memory instead of one per tile), and every lane issues each of
+  // them: a load under a per-lane condition would make the compiler wait
+  // for all outstanding loads.
+  static_assert(DK <= NTH, "one Gam_C entry per thread");
+  RowTile<E, DK, false, NTH> tq, tk, tkh;
+  float gcv = 0.f;
   if constexpr (KDA) {
-    stage_rows<E, DK, NTH>(reinterpret_cast<const T*>(kp.qt + tile0), DK, 0, nrow, sQ, LQ, nullptr, 0, tid);
-    stage_rows<E, DK, NTH>(reinterpret_cast<const T*>(kp.kt + tile0), DK, 0, nrow, sK, LQ, nullptr, 0, tid);
-    stage_rows<E, DK, NTH>(reinterpret_cast<const T*>(kp.kht + tile0), DK, 0, nrow, sKh, LQ, nullptr, 0, tid);
-    for (int i = tid; i < DK; i += NTH) {
-      sGC[i] = kp.gc[(size_t)chunk * DK + i];
-      sCC[i] = 0.f;
-    }
+    tq.load(reinterpret_cast<const T*>(kp.qt + tile0), DK, 0, nrow, tid);
+    tk.load(reinterpret_cast<const T*>(kp.kt + tile0), DK, 0, nrow, tid);
+    tkh.load(reinterpret_cast<const T*>(kp.kht + tile0), DK, 0, nrow, tid);
+    gcv = kp.gc[(size_t)chunk * DK + tid % DK];
   } else {
-    stage_rows<E, DK, NTH>(qh, DK, t0, nrow, sQ, LQ, nullptr, 0, tid);
-    stage_rows<E, DK, NTH>(kh, DK, t0, nrow, sK, LQ, nullptr, 0, tid);
+    tq.load(qh, DK, t0, nrow, tid);
+    tk.load(kh, DK, t0, nrow, tid);
+  }
+  const T btv = bth[t0 + min(lane, nrow - 1)];
+  // keep the early S and dSn loads behind these in the issue order (the
+  // scheduler would otherwise hoist them), so that the stores below wait
+  // for the tiles only
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kHold) {
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+      hD[kt] = *reinterpret_cast<const uint2*>(dSt + (kt * NVT + wave) * 256 + 4 * lane);
+      hS[kt] = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(S) + (kt * NVT + wave) * 256 + 4 * lane);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int rr = min(16 * (e >> 2) + 4 * lg + (e & 3), nrow - 1);  // rows past the end: zeroed in phase B
+      hV[e] = vh[(size_t)(t0 + rr) * DV + 16 * wave + lc];
+      hO[e] = doh[(size_t)(t0 + rr) * DV + 16 * wave + lc];
+    }
+  }
+  tq.store(nrow, sQ, LQ, nullptr, 0, tid);
+  tk.store(nrow, sK, LQ, nullptr, 0, tid);
+  if constexpr (KDA) {
+    tkh.store(nrow, sKh, LQ, nullptr, 0, tid);
+    if (tid < DK) {
+      sGC[tid] = gcv;
+      sCC[tid] = 0.f;
+    }
   }
   if (tid < kC) {
-    sB[tid] = tid < nrow ? E::tof(bth[t0 + tid]) : 0.f;
+    sB[tid] = tid < nrow ? E::tof(btv) : 0.f;
     sDB[tid] = 0.f;
   }
   if constexpr (GATE) {
@@ -1377,8 +1411,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * mt + 4 * lg + i;
         const int rr = min(r, nrow - 1);  // every lane loads; rows past the end are zeroed
-        const float vx = E::tof(vh[(size_t)(t0 + rr) * DV + col]);
-        const float ox = E::tof(doh[(size_t)(t0 + rr) * DV + col]);
+        const float vx = E::tof(kHold ? hV[kHold ? 4 * mt + i : 0] : vh[(size_t)(t0 + rr) * DV + col]);
+        const float ox = E::tof(kHold ? hO[kHold ? 4 * mt + i : 0] : doh[(size_t)(t0 + rr) * DV + col]);
         vt[mt][i] = r < nrow ? vx : 0.f;
         dOt[mt][i] = r < nrow ? ox : 0.f;
       }
@@ -1448,6 +1482,9 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
     }
   }
   __syncthreads();
+  // phase C's dO tile, requested before the dV stores go out
+  RowTile<E, DV, false, NTH> tdo;
+  tdo.load(doh, DV, t0, nrow, tid);
   if constexpr (kBf16) {  // dV = diag(beta) dX, from its rows in LDS with 16-byte stores
     constexpr int NVD = kC * DV / 8;
     for (int v = tid; v < NVD; v += NTH) {
@@ -1469,7 +1506,20 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
   T* sDAt = reinterpret_cast<T*>(smem + L::cDAt);
   T* sBL = reinterpret_cast<T*>(smem + L::cBL);
   T* sBLt = reinterpret_cast<T*>(smem + L::cBLt);
-  stage_rows<E, DV, NTH>(doh, DV, t0, nrow, sDO, LV, nullptr, 0, tid);
+  tdo.store(nrow, sDO, LV, nullptr, 0, tid);
+  // bf16: phase D's row-major K and Q tiles (KDA: K^, Q~ and K~), requested
+  // now so that phase C covers their latency
+  RowTile<E, DK, false, NTH> tdk, tdq, tdk2;
+  if constexpr (kBf16) {
+    if constexpr (KDA) {
+      tdk.load(reinterpret_cast<const T*>(kp.kht + tile0), DK, 0, nrow, tid);
+      tdq.load(reinterpret_cast<const T*>(kp.qt + tile0), DK, 0, nrow, tid);
+      tdk2.load(reinterpret_cast<const T*>(kp.kt + tile0), DK, 0, nrow, tid);
+    } else {
+      tdk.load(kh, DK, t0, nrow, tid);
+      tdq.load(qh, DK, t0, nrow, tid);
+    }
+  }
   // bf16: sDAt and sBLt hold dA and diag(beta) dL with their token columns
   // permuted by tperm (A operands against the transpose reads of phase D);
   // fp32: the transposes
@@ -1615,17 +1665,9 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
     bf16_t* sKr = reinterpret_cast<bf16_t*>(smem + L::dKr);
     bf16_t* sQr = reinterpret_cast<bf16_t*>(smem + L::dQr);
     bf16_t* sKtr = reinterpret_cast<bf16_t*>(smem + L::dKtr);  // KDA: K~ (sKr holds K^, sQr Q~)
-    if constexpr (KDA) {
-      stage_rows<E, DK, NTH>(reinterpret_cast<const T*>(kp.kht + tile0), DK, 0, nrow, reinterpret_cast<T*>(sKr), LQ,
-                             nullptr, 0, tid);
-      stage_rows<E, DK, NTH>(reinterpret_cast<const T*>(kp.qt + tile0), DK, 0, nrow, reinterpret_cast<T*>(sQr), LQ,
-                             nullptr, 0, tid);
-      stage_rows<E, DK, NTH>(reinterpret_cast<const T*>(kp.kt + tile0), DK, 0, nrow, reinterpret_cast<T*>(sKtr), LQ,
-                             nullptr, 0, tid);
-    } else {
-      stage_rows<E, DK, NTH>(kh, DK, t0, nrow, reinterpret_cast<T*>(sKr), LQ, nullptr, 0, tid);
-      stage_rows<E, DK, NTH>(qh, DK, t0, nrow, reinterpret_cast<T*>(sQr), LQ, nullptr, 0, tid);
-    }
+    tdk.store(nrow, reinterpret_cast<T*>(sKr), LQ, nullptr, 0, tid);
+    tdq.store(nrow, reinterpret_cast<T*>(sQr), LQ, nullptr, 0, tid);
+    if constexpr (KDA) tdk2.store(nrow, reinterpret_cast<T*>(sKtr), LQ, nullptr, 0, tid);
     __syncthreads();
     const bf16_t* bDA = reinterpret_cast<const bf16_t*>(sDA);
     const bf16_t* bDAp = reinterpret_cast<const bf16_t*>(sDAt);
