@@ -868,6 +868,18 @@ __global__ __launch_bounds__(256) void gate_prep(const bf16_t* __restrict__ q, c
   uint32_t gw[TPS];
 #pragma unroll
   for (int t = 0; t < TPS; ++t) gw[t] = g2[min(TPS * w + t, nrow - 1) * NCOL + l];  // masked below
+  // every q and k load of the thread too, in flight with g's: the compiler
+  // cannot move a load above a store to the outputs, so loads next to the
+  // stores below would each wait for the previous row's round trip
+  const uint32_t* q2 = reinterpret_cast<const uint32_t*>(q + ibase);
+  const uint32_t* k2 = reinterpret_cast<const uint32_t*>(k + ibase);
+  uint32_t qv[TPS], kv[TPS];
+#pragma unroll
+  for (int t = 0; t < TPS; ++t) {
+    const int iidx = min(TPS * w + t, nrow - 1) * NCOL + l;  // in bounds for every lane
+    qv[t] = q2[iidx];
+    kv[t] = k2[iidx];
+  }
   float2 run = make_float2(0.f, 0.f);
   float2 gl[TPS];
 #pragma unroll
@@ -894,8 +906,6 @@ __global__ __launch_bounds__(256) void gate_prep(const bf16_t* __restrict__ q, c
   for (int t = 0; t < TPS; ++t) mx = fmaxf(mx, fmaxf(fabsf(off.x + gl[t].x), fabsf(off.y + gl[t].y)));
   if (!(mx <= kGateRange)) wide = 1;  // also for NaN
   __syncthreads();
-  const uint32_t* q2 = reinterpret_cast<const uint32_t*>(q + ibase);
-  const uint32_t* k2 = reinterpret_cast<const uint32_t*>(k + ibase);
   uint32_t* qt2 = reinterpret_cast<uint32_t*>(qt + base);
   uint32_t* kt2 = reinterpret_cast<uint32_t*>(kt + base);
   uint32_t* kh2 = reinterpret_cast<uint32_t*>(kht + base);
@@ -904,11 +914,9 @@ __global__ __launch_bounds__(256) void gate_prep(const bf16_t* __restrict__ q, c
 #pragma unroll
     for (int t = 0; t < TPS; ++t) {
       const int idx = (TPS * w + t) * NCOL + l;
-      const int iidx = min(TPS * w + t, nrow - 1) * NCOL + l;
       const bool in = TPS * w + t < nrow;
-      const uint32_t qr = q2[iidx], kr = k2[iidx];  // in bounds for every lane
-      qt2[idx] = in ? qr : 0u;
-      kt2[idx] = in ? kr : 0u;
+      qt2[idx] = in ? qv[t] : 0u;
+      kt2[idx] = in ? kv[t] : 0u;
       kh2[idx] = in ? gw[t] : 0u;
     }
     return;
@@ -917,10 +925,8 @@ __global__ __launch_bounds__(256) void gate_prep(const bf16_t* __restrict__ q, c
 #pragma unroll
   for (int t = 0; t < TPS; ++t) {
     const int idx = (TPS * w + t) * NCOL + l;
-    const int iidx = min(TPS * w + t, nrow - 1) * NCOL + l;
     const bool in = TPS * w + t < nrow;
-    const uint32_t qr = q2[iidx], kr = k2[iidx];  // in bounds for every lane
-    const uint32_t qw = in ? qr : 0u, kw = in ? kr : 0u;
+    const uint32_t qw = in ? qv[t] : 0u, kw = in ? kv[t] : 0u;
     const float G0 = off.x + gl[t].x, G1 = off.y + gl[t].y;
     const float e0 = __expf(G0), e1 = __expf(G1), r0 = __expf(-G0), r1 = __expf(-G1);
     const float q0 = bf2f((bf16_t)(qw & 0xffffu)), q1 = bf2f((bf16_t)(qw >> 16));
