@@ -1400,8 +1400,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
           const int ch = 16 * kt + 4 * lg + i;
           dSv[kt][i] *= sGC[ch];
           float p = Sv[kt][i] * dSv[kt][i];
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) p += __shfl_xor(p, off, 16);
+          p = sum16(p);
           if (lc == 0) atomicAdd(&sCC[ch], p);
         }
     }
@@ -1469,13 +1468,11 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
         sU[r * LV + col] = E::cvt(ut[mt][i]);
         sDX[r * LV + col] = E::cvt(dx[mt][i]);
         float p = res[mt][i] * dx[mt][i];  // rowsum over this slice's 16 columns
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) p += __shfl_xor(p, off, 16);
+        p = sum16(p);
         if (lc == 0) atomicAdd(&sDB[r], p);
         if constexpr (GATE) {  // - beta_r exp(G_r) (K S)_r . dX_r
           float pv = gy[mt][i] * sB[r] * dx[mt][i];
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) pv += __shfl_xor(pv, off, 16);
+          pv = sum16(pv);
           if (lc == 0) atomicAdd(&sDG[r], -pv);
         }
       }
@@ -1576,8 +1573,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
           if (lg == 0) atomicAdd(&sDG[r], rs);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) m[i] += __shfl_xor(m[i], off, 16);
+            m[i] = sum16(m[i]);
             if (lc == 0) atomicAdd(&sDG[c0 + i], -m[i]);
           }
         }
@@ -1616,8 +1612,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
         if constexpr (GATE) {  // dA * A below the diagonal: + row sum, - column sum
           float m = acc[i] * E::tof(sAg[t * 256 + (4 * lg + i) * 16 + lc]);  // dA times the gated A
           float rs = m;
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) rs += __shfl_xor(rs, off, 16);
+          rs = sum16(rs);
           if (lc == 0) atomicAdd(&sDG[r], rs);
           m += __shfl_xor(m, 16);
           m += __shfl_xor(m, 32);
@@ -1626,8 +1621,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
       } else {
         const float dl = cc < r ? -acc[i] : 0.f;
         float p = cc < r ? dl * sKK[r * LTL + cc] : 0.f;  // rowsum(dL * K K^T)
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) p += __shfl_xor(p, off, 16);
+        p = sum16(p);
         if (lc == 0) atomicAdd(&sDB[r], p);
         const T x = E::cvt(sB[r] * dl * gm);
         sBL[r * LKT + cc] = x;
@@ -1727,11 +1721,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (r >= nrow) x[i] = 0.f;
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) {
-            const float y = __shfl_up(x[i], off, 16);  // every lane shuffles, then masks
-            if (lc >= off) x[i] += y;
-          }
+          x[i] = scan16_up(x[i]);
           gpre[n][i] = x[i];
           if (own && lc == 15) sTotG[ti * DK + d0 + i] = x[i];
         }
@@ -1756,8 +1746,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * ti + 4 * lg + i, d = 16 * tk + lc;
         float p = r < nrow ? E::tof(sKt[d * LKT + r]) * (x[i] - xt[i]) : 0.f;
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) p += __shfl_xor(p, off, 16);
+        p = sum16(p);
         if (lc == 0) atomicAdd(&sDG[r], p);
       }
     }
@@ -1875,12 +1864,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) {
-            p[i] += __shfl_xor(p[i], off, 16);
-            const float y = __shfl_down(dG[i], off, 16);  // suffix over the tile's rows
-            if (lc + off < 16) dG[i] += y;
-          }
+          p[i] = sum16(p[i]);
+          dG[i] = scan16_down(dG[i]);  // suffix over the tile's rows
           if (lc == 0) {
             atomicAdd(&sCC[d0 + i], p[i]);
             sTotD[ti * DK + d0 + i] = dG[i];
@@ -1948,8 +1933,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
           pk = r < nrow - 1 ? e2 * E::tof(kh[(size_t)(t0 + r) * DK + d]) * k1[i] : 0.f;
           p = e1 * E::tof(qh[(size_t)(t0 + r) * DK + d]) * q1[i] - pk;
         }
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) p += __shfl_xor(p, off, 16);
+        p = sum16(p);
         if (lc == 0) atomicAdd(&sDG[r], p);
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) pk += __shfl_xor(pk, off, 64);
@@ -2104,8 +2088,7 @@ __global__ __launch_bounds__(512) void kda_walk_grads(BackwardArgs a, const bf16
       const float bt = sb[tau];
       if (lg == 0) dvo[(size_t)tau * DV + col] = f2bf(bt * du);
       float pb = lg == 0 ? du * (bf2f(sv[tau][col]) - r) : 0.f;
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) pb += __shfl_xor(pb, off, 16);
+      pb = sum16(pb);
       if (lane == 0) red[wave][3 * DK] = pb;
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
@@ -2116,12 +2099,9 @@ __global__ __launch_bounds__(512) void kda_walk_grads(BackwardArgs a, const bf16
           const float dsp = ds[kt][i] - bt * bf2f(sk[tau][ch]) * du;    // dS'
           float pg = dsp * sp[kt][i];                                   // dg partial
           float p1 = x[kt][i] * dOj;                                    // dq partial
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) {
-            p1 += __shfl_xor(p1, off, 16);
-            pk += __shfl_xor(pk, off, 16);
-            pg += __shfl_xor(pg, off, 16);
-          }
+          p1 = sum16(p1);
+          pk = sum16(pk);
+          pg = sum16(pg);
           if (lc == 0) {
             red[wave][ch] = p1;
             red[wave][DK + ch] = pk;

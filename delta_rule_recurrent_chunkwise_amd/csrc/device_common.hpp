@@ -61,6 +61,43 @@ struct alignas(16) Vec16 {
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
+// Sum over each row of 16 lanes, returned to every lane of the row, with
+// DPP moves (VALU operands) instead of LDS permutes.  quad_perm [1,0,3,2]
+// and [2,3,0,1] pair lanes i, i^1 and then i, i^2; row_half_mirror pairs
+// every lane of quad 0 with one of quad 1 (and 2 with 3), row_mirror every
+// lane of one half-row with one of the other.  These are the pairs of an xor
+// butterfly with offsets 1, 2, 4, 8, so the additions are the butterfly's,
+// in its order.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum16(float x) {
+  x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f32<0x141>(x);  // row_half_mirror
+  x += dpp_f32<0x140>(x);  // row_mirror
+  return x;
+}
+// Inclusive scans over each row of 16 lanes by DPP row shifts (a lane with
+// no source lane in its row reads 0): scan16_up gives lane c the sum over
+// lanes 0..c, scan16_down the sum over lanes c..15.  The additions and their
+// order are those of the shuffle scans with offsets 1, 2, 4, 8.
+__device__ __forceinline__ float scan16_up(float x) {
+  x += dpp_f32<0x111>(x);  // row_shr:1
+  x += dpp_f32<0x112>(x);  // row_shr:2
+  x += dpp_f32<0x114>(x);  // row_shr:4
+  x += dpp_f32<0x118>(x);  // row_shr:8
+  return x;
+}
+__device__ __forceinline__ float scan16_down(float x) {
+  x += dpp_f32<0x101>(x);  // row_shl:1
+  x += dpp_f32<0x102>(x);  // row_shl:2
+  x += dpp_f32<0x104>(x);  // row_shl:4
+  x += dpp_f32<0x108>(x);  // row_shl:8
+  return x;
+}
+
 // ---------------------------------------------------------------------------
 // Raw MFMA instructions
 // ---------------------------------------------------------------------------

@@ -328,8 +328,7 @@ __global__ __launch_bounds__(256) void la_chunk_out(const bf16_t* __restrict__ q
     float x = rs[i];
 #pragma unroll
     for (int c = lc; c < DK; c += 16) x += bf2f(sq[r][c]) * sz[c];
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 16);
+    x = sum16(x);
     if (lc == 0) sden[r] = x;
   }
   // one wave wrote its own score rows and denominators: wave-local ordering
