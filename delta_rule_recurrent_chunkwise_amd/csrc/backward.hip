@@ -665,8 +665,7 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
               r += kk[t][i] * x[t][i];
             }
           }
-          r += __shfl_xor(r, 16);
-          r += __shfl_xor(r, 32);
+          r = xsum32(xsum16(r));
           const float u = -sB[tau] * r;  // v = 0
           float o = 0.f;
 #pragma unroll
@@ -676,8 +675,7 @@ __global__ __launch_bounds__(kTransThreads) void bwd_transition(BackwardArgs a, 
               x[t][i] += kk[t][i] * u;
               o += qq[t][i] * x[t][i];
             }
-          o += __shfl_xor(o, 16);
-          o += __shfl_xor(o, 32);
+          o = xsum32(xsum16(o));
           if (lg == 0) sR[tau * LQ + col] = f2bf(o);
         }
         // P = -X^T: lane (column col of X) writes row col of P, in the
@@ -1422,8 +1420,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
       for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) p += Sv[kt][i] * dSv[kt][i];
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) p += __shfl_xor(p, off, 64);
+      p = sum64(p);
       if (lane == 0) atomicAdd(&sDG[nrow - 1], __expf(sG[63]) * p);
     }
 #pragma unroll
@@ -1568,8 +1565,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
             m[i] = acc[i] * ag[i];
             rs += m[i];
           }
-          rs += __shfl_xor(rs, 16);
-          rs += __shfl_xor(rs, 32);
+          rs = xsum32(xsum16(rs));
           if (lg == 0) atomicAdd(&sDG[r], rs);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -1586,8 +1582,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
           dl[i] = c0 + i < r ? -acc[i] : 0.f;
           p += c0 + i < r ? dl[i] * sKK[r * LTL + c0 + i] : 0.f;  // rowsum(dL * K K^T)
         }
-        p += __shfl_xor(p, 16);
-        p += __shfl_xor(p, 32);
+        p = xsum32(xsum16(p));
         if (lg == 0) atomicAdd(&sDB[r], p);
         const float br = sB[r];
 #pragma unroll
@@ -1614,8 +1609,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
           float rs = m;
           rs = sum16(rs);
           if (lc == 0) atomicAdd(&sDG[r], rs);
-          m += __shfl_xor(m, 16);
-          m += __shfl_xor(m, 32);
+          m = xsum32(xsum16(m));
           if (lg == 0) atomicAdd(&sDG[cc], -m);
         }
       } else {
@@ -1694,8 +1688,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
         float p = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) p += bf2f(sKr[r * LQ + d0 + i]) * (xk[i] - xb[i]);
-        p += __shfl_xor(p, 16);
-        p += __shfl_xor(p, 32);
+        p = xsum32(xsum16(p));
         if (lg == 0) atomicAdd(&sDG[r], p);
         xk += xb + xc;
       }
@@ -1905,12 +1898,10 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
           pk = r < nrow - 1 ? e2 * pk : 0.f;
           p = e1 * p - pk;
         }
-        p += __shfl_xor(p, 16);
-        p += __shfl_xor(p, 32);
+        p = xsum32(xsum16(p));
         if (lg == 0) atomicAdd(&sDG[r], p);
         // the same k . (u dSn^T) terms summed over the chunk, on its last row
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) pk += __shfl_xor(pk, off, 64);
+        pk = sum64(pk);
         if (lane == 0) atomicAdd(&sDG[nrow - 1], pk);
       }
       continue;
@@ -1935,8 +1926,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
         }
         p = sum16(p);
         if (lc == 0) atomicAdd(&sDG[r], p);
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) pk += __shfl_xor(pk, off, 64);
+        pk = sum64(pk);
         if (lane == 0) atomicAdd(&sDG[nrow - 1], pk);
       }
     }
@@ -2050,8 +2040,7 @@ __global__ __launch_bounds__(512) void kda_walk_grads(BackwardArgs a, const bf16
         if (sp) sp[kt][i] = x[kt][i];
         r += bf2f(sk[tau][ch]) * x[kt][i];
       }
-    r += __shfl_xor(r, 16);
-    r += __shfl_xor(r, 32);
+    r = xsum32(xsum16(r));
     const float u = sb[tau] * (bf2f(sv[tau][col]) - r);
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt)
@@ -2083,8 +2072,7 @@ __global__ __launch_bounds__(512) void kda_walk_grads(BackwardArgs a, const bf16
           ds[kt][i] += bf2f(sq[tau][ch]) * dOj;
           du += bf2f(sk[tau][ch]) * ds[kt][i];
         }
-      du += __shfl_xor(du, 16);
-      du += __shfl_xor(du, 32);
+      du = xsum32(xsum16(du));
       const float bt = sb[tau];
       if (lg == 0) dvo[(size_t)tau * DV + col] = f2bf(bt * du);
       float pb = lg == 0 ? du * (bf2f(sv[tau][col]) - r) : 0.f;

@@ -79,6 +79,23 @@ __device__ __forceinline__ float sum16(float x) {
   x += dpp_f32<0x140>(x);  // row_mirror
   return x;
 }
+// Sums of lanes l and l^16 (xsum16) and of lanes l and l^32 (xsum32), by
+// v_permlane16_swap / v_permlane32_swap (VALU, no LDS).  Given one value
+// twice, the 16-lane swap returns rows (0, 0, 2, 2) and (1, 1, 3, 3) of it,
+// the 32-lane swap the lower half twice and the upper half twice (checked on
+// the hardware), so the sum of the two results is the pair's sum in every
+// lane, the same operands as a shuffle by 16 or 32 would add.
+__device__ __forceinline__ float xsum16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xsum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Sum over the whole wave in every lane: the butterfly's pairs, in its order.
+__device__ __forceinline__ float sum64(float x) { return xsum32(xsum16(sum16(x))); }
+
 // Inclusive scans over each row of 16 lanes by DPP row shifts (a lane with
 // no source lane in its row reads 0): scan16_up gives lane c the sum over
 // lanes 0..c, scan16_down the sum over lanes c..15.  The additions and their

@@ -371,8 +371,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
               st[kt][i] *= __expf(E::tof(sKh[tau * LQ + ch]));
               r += kk[kt][i] * st[kt][i];
             }
-          r += __shfl_xor(r, 16);
-          r += __shfl_xor(r, 32);
+          r = xsum32(xsum16(r));
           const float u = sRow[tau] * (E::tof(sVt[(16 * cw + lc) * LKT + tau]) - r);
           float o = 0.f;
 #pragma unroll
@@ -382,8 +381,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
               st[kt][i] += kk[kt][i] * u;
               o += qq[kt][i] * st[kt][i];
             }
-          o += __shfl_xor(o, 16);
-          o += __shfl_xor(o, 32);
+          o = xsum32(xsum16(o));
           if (lg == 0 && !a.Sc && t0 + tau <= tlast) oh[(size_t)(t0 + tau) * dv + 16 * cw + lc] = E::cvt(o);
         }
       }

@@ -429,8 +429,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
             r += kk[t][i] * st[t][i];
           }
         }
-        r += __shfl_xor(r, 16);
-        r += __shfl_xor(r, 32);
+        r = xsum32(xsum16(r));
         const float u = sm.beta[P][tau] * (bf2f(sm.v[P][tau][col]) - r);
         float o = 0.f;
 #pragma unroll
@@ -440,8 +439,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
             st[t][i] += kk[t][i] * u;
             o += qq[t][i] * st[t][i];
           }
-        o += __shfl_xor(o, 16);
-        o += __shfl_xor(o, 32);
+        o = xsum32(xsum16(o));
         if (lg == 0) sm.o[P][tau][col] = f2bf(o);
       }
     };
