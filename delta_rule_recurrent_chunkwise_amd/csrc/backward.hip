@@ -56,13 +56,7 @@ __device__ __forceinline__ int xcd_remap_b(int bid, int n) {
 // returns G_r.
 template <class E>
 __device__ __forceinline__ float chunk_logdecay(const typename E::T* gh, int t0, int nrow, int lane) {
-  float x = lane < nrow ? E::tof(gh[t0 + lane]) : 0.f;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  return x;
+  return scan64_up(lane < nrow ? E::tof(gh[t0 + lane]) : 0.f);
 }
 // exp(G_r - G_c) for c <= r (a decay ratio, at most 1), else 0
 __device__ __forceinline__ float decay_ratio(const float* sG, int r, int c) {

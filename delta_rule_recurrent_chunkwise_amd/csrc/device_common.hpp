@@ -114,6 +114,20 @@ __device__ __forceinline__ float scan16_down(float x) {
   x += dpp_f32<0x108>(x);  // row_shl:8
   return x;
 }
+// Inclusive prefix over the whole wave: the row scans above, then
+// row_bcast:15 adds the last lane of rows 0 and 2 to rows 1 and 3, and
+// row_bcast:31 adds lane 31 to rows 2 and 3 (rows left out by the row mask
+// add 0).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_f32_rows(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ float scan64_up(float x) {
+  x = scan16_up(x);
+  x += dpp_f32_rows<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_f32_rows<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
 
 // ---------------------------------------------------------------------------
 // Raw MFMA instructions

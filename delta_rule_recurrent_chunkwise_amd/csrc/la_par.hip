@@ -49,13 +49,7 @@ __device__ __forceinline__ void load_vecs(u32x4 (&buf)[(N + 255) / 256], const b
 // Wave 0 of a chunk's workgroup: G_t = sum_{s<=t} g_s over the chunk (lane =
 // token; tokens past the end and a missing gate count as 0).
 __device__ __forceinline__ float chunk_log_decay(const bf16_t* gc, int lane, int nrow) {
-  float x = (gc && lane < nrow) ? bf2f(gc[min(lane, nrow - 1)]) : 0.f;
-#pragma unroll
-  for (int off = 1; off < kC; off <<= 1) {
-    const float y = __shfl_up(x, off, kC);
-    if (lane >= off) x += y;
-  }
-  return x;
+  return scan64_up((gc && lane < nrow) ? bf2f(gc[min(lane, nrow - 1)]) : 0.f);
 }
 
 __device__ __forceinline__ shortx4_t ld_tr(const bf16_t* p) {
@@ -97,7 +91,7 @@ __global__ __launch_bounds__(256) void la_chunk_state(const bf16_t* __restrict__
   if constexpr (GLA) {
     if (wave == 0) {
       const float G = chunk_log_decay(g ? g + (size_t)bh * T + t0 : nullptr, lane, nrow);
-      const float gC = __shfl(G, kC - 1, kC);
+      const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), kC - 1));
       sw[lane] = __expf(gC - G);
       if (lane == 0) dz[chunk] = __expf(gC);
     }

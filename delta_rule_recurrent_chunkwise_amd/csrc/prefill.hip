@@ -274,13 +274,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
       if (kSolve && tid < kC) sRow[tid] = t0 + tid <= tlast ? preb : 0.f;
       if (kScal && tid < kC) {
         // wave 0 (one lane per token): G_t = sum_{s<=t} g_s over the chunk
-        float x = t0 + tid <= tlast ? preg : 0.f;
-#pragma unroll
-        for (int off = 1; off < kC; off <<= 1) {
-          const float y = __shfl_up(x, off, kC);
-          if (lane >= off) x += y;
-        }
-        sG[tid] = x;
+        sG[tid] = scan64_up(t0 + tid <= tlast ? preg : 0.f);
       }
       if (c + 1 < nchunks) prefetch(c + 1);
     }

@@ -308,13 +308,8 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
       if constexpr (TOKG) {
         // G_t = sum_{s<=t} g_s over the chunk (lane = token), then the
         // factors exp(G_t) and exp(G_63 - G_t), both at most 1
-        float x = in ? bf2f((bf16_t)bsrc[1]) : 0.f;
-#pragma unroll
-        for (int off = 1; off < kC; off <<= 1) {
-          const float y = __shfl_up(x, off, kC);
-          if (lane >= off) x += y;
-        }
-        const float gC = __shfl(x, kC - 1, kC);
+        const float x = scan64_up(in ? bf2f((bf16_t)bsrc[1]) : 0.f);
+        const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), kC - 1));
         sm.gs[TOKG ? buf : 0][0][lane] = x;
         sm.gs[TOKG ? buf : 0][1][lane] = __expf(x);
         sm.gs[TOKG ? buf : 0][2][lane] = __expf(gC - x);
