@@ -42,7 +42,9 @@
 //   loaders      write chunk x+1 to LDS in phase 1 of iteration x and issue
 //                the global loads of chunk x+3 into the freed registers.
 // Chunk y lives in LDS buffer y & 1: it is written in phase 1 of iteration
-// y-1 and last read in phase 2 of iteration y.
+// y-1 and last read in phase 2 of iteration y.  (Tiles stored two chunks
+// ahead in phase 2 take three buffers, or two if not read in phase 2 of their
+// own chunk; a tile read only in phase 1 and stored in phase 2 takes one.)
 //
 // Index conventions.  Q, K (and K^) and the v slice are stored row-major
 // (tokens x channels).  The chain's 32-deep MFMA pairs two accumulator
@@ -104,13 +106,18 @@ struct __attribute__((aligned(16))) Smem2 {
   static constexpr bool TOKG = GM == 2;
   static constexpr int kLV = DVS + 16;  // bf16 row stride of the v slice
   static constexpr int kLO = DVS + 8;   // bf16 row stride of the output tile
-  static constexpr int NKH = GATED ? 2 : 1;
+  // Buffers per tile (see the loader schedule).  Gated with 16-column
+  // slices (three tile waves): Q stored in phase 2 for the next chunk (one
+  // buffer), Gam K and K / Gam two chunks ahead in phase 2 (two and three).
+  static constexpr bool kShift = GATED && DVS == 16;
+  static constexpr int NQB = kShift ? 1 : 2;
+  static constexpr int NKH = GATED ? (kShift ? 3 : 2) : 1;
   static constexpr int RKH = GATED ? kC : 1;
-  static constexpr int NKB = GATED ? 2 : 3;  // K buffers (see the loader schedule)
+  static constexpr int NKB = GATED ? 2 : 3;
   // K first: its buffer is chosen at run time, and fragment offsets from one
   // base register stay within the 16-bit immediate of the LDS instructions
   bf16_t k[NKB][kC][kLQ];     // K (gated: Gam K)
-  bf16_t q[2][kC][kLQ];       // Q (gated: Gam Q)
+  bf16_t q[NQB][kC][kLQ];     // Q (gated: Gam Q)
   bf16_t kh[NKH][RKH][kLQ];   // gated: K / Gam
   bf16_t a[kC][kLT];          // tril(Q K^T), token columns permuted
   bf16_t lb[2][6][16][16];    // L_bj (b > j), transposed
@@ -119,7 +126,7 @@ struct __attribute__((aligned(16))) Smem2 {
   bf16_t o[2][kC][kLO];       // output tile of chunk c in buffer c & 1
   float l[4 * kLB];           // diagonal blocks of L (strictly lower parts)
   float beta[2][kC];
-  float gc[NKH][kDK];         // gated: Gam_C per key channel
+  float gc[GATED ? 2 : 1][kDK];  // gated: Gam_C per key channel, chunk c in buffer c & 1
   // per-token decay of chunk c in buffer c & 1: G_t, exp(G_t), exp(G_63 - G_t)
   float gs[TOKG ? 2 : 1][3][TOKG ? kC : 1];
 };
@@ -176,11 +183,13 @@ struct PipeArgs {
 // Gam_C.  Every lane issues every load of its slots: a per-lane condition
 // around a load would make the compiler wait for all outstanding loads.
 //   plain:            wave 4 Q, wave 5 K; two register slots.
-//   gated, 16 cols:   wave 1 (no chain work) Q, wave 4 K, wave 5 K^; two slots.
+//   gated, 16 cols:   wave 1 (no chain work) Q, wave 4 K, wave 5 K^; two slots;
+//                     K and K^ are stored two chunks ahead, in phase 2.
 //   gated, 32 cols:   wave 4 Q + half of K^, wave 5 K + the other half; one
 //                     slot (96 registers).
 // With two slots the loads of chunk y are issued in iteration y-3 and stored
-// in iteration y-1; with one, issued in iteration y-2.
+// in iteration y-1 (y-4 and y-2 for a tile stored two chunks ahead); with
+// one, issued in iteration y-2.
 template <bool GATED, int DVS>
 struct LoadPlan {
   static constexpr bool kThree = GATED && DVS == 16;           // three tile waves
@@ -209,6 +218,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
   constexpr bool GATED = GM == 1;  // per key channel, operands from the pre-pass
   constexpr bool TOKG = GM == 2;   // one decay per token
   typedef Smem2<GM, DVS> Sm;
+  constexpr bool kShift = Sm::kShift;  // gated, 16 columns: one Q buffer, K^ chunk c in buffer c % 3
   constexpr int kDVS = DVS;
   constexpr int NCW = DVS / 16;        // chain waves
   constexpr int VPRV = DVS / 8;        // 16-byte vectors per row of the v slice
@@ -290,7 +300,8 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
 #pragma unroll
       for (int j = 0; j < LP::NT; ++j) {
         const int t = LP::tile_of(wave, j);
-        bf16_t(*tile)[kLQ] = t == 0 ? sm.q[buf] : (t == 1 ? sm.k[kbi] : sm.kh[GATED ? buf : 0]);
+        bf16_t(*tile)[kLQ] = t == 0 ? sm.q[kShift ? 0 : buf]
+                                    : (t == 1 ? sm.k[kbi] : sm.kh[GATED ? (kShift ? chunk % 3 : buf) : 0]);
         const int vv = LP::vec_of(wave, lane, j);
         *reinterpret_cast<u32x4*>(&tile[vv >> 4][(vv & 15) * 8]) = src[j];
       }
@@ -403,7 +414,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
     // its slots.  Lane (lc, lg) holds column col of rows 16t + 4lg + i, i.e.
     // key channels perm32(16t + 4lg) + i; the sums over channels are
     // completed across the four lanes that share a column.
-    auto token_walk = [&](auto parity) {
+    auto token_walk = [&](const int x, auto parity) {
       constexpr int P = decltype(parity)::value;
       for (int tau = 0; tau < kC; ++tau) {
         float kk[8][4], qq[8][4];
@@ -412,8 +423,8 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
         for (int t = 0; t < 8; ++t) {
           const int c0 = perm32(16 * t + 4 * lg);
           const uint2 kw = *reinterpret_cast<const uint2*>(&sm.k[GATED ? P : 0][tau][c0]);
-          const uint2 qw = *reinterpret_cast<const uint2*>(&sm.q[P][tau][c0]);
-          const uint2 gw = *reinterpret_cast<const uint2*>(&sm.kh[GATED ? P : 0][GATED ? tau : 0][c0]);
+          const uint2 qw = *reinterpret_cast<const uint2*>(&sm.q[kShift ? 0 : P][tau][c0]);
+          const uint2 gw = *reinterpret_cast<const uint2*>(&sm.kh[GATED ? (kShift ? x % 3 : P) : 0][GATED ? tau : 0][c0]);
           const uint32_t kv[2] = {kw.x, kw.y}, qv[2] = {qw.x, qw.y}, gv[2] = {gw.x, gw.y};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -461,7 +472,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
           }
           if constexpr (GATED) {
             if (sm.gc[P][0] < 0.f) {
-              token_walk(parity);
+              token_walk(x, parity);
               return;
             }
           }
@@ -475,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) {
             fk[0][mt] = ld_frag(&kx[16 * mt + lc][8 * lg]);
-            fq[0][mt] = ld_frag(&sm.q[P][16 * mt + lc][8 * lg]);
+            fq[0][mt] = ld_frag(&sm.q[kShift ? 0 : P][16 * mt + lc][8 * lg]);
           }
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
@@ -483,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
 #pragma unroll
               for (int mt = 0; mt < 4; ++mt) {
                 fk[(kb + 1) & 1][mt] = ld_frag(&kx[16 * mt + lc][32 * (kb + 1) + 8 * lg]);
-                fq[(kb + 1) & 1][mt] = ld_frag(&sm.q[P][16 * mt + lc][32 * (kb + 1) + 8 * lg]);
+                fq[(kb + 1) & 1][mt] = ld_frag(&sm.q[kShift ? 0 : P][16 * mt + lc][32 * (kb + 1) + 8 * lg]);
               }
             }
             const bf16x8 b = acc_pair_to_b(st[2 * kb], st[2 * kb + 1]);
@@ -550,7 +561,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
               zero4());
           // K^T fragments (K^ when gated): row 16t + c of the A operand is key
           // channel perm32(16t + c); its k-elements are the tokens of u's pairing.
-          const bf16_t(*kt)[kLQ] = GATED ? sm.kh[GATED ? P : 0] : sm.k[kidx(x)];
+          const bf16_t(*kt)[kLQ] = GATED ? sm.kh[GATED ? (kShift ? x % 3 : P) : 0] : sm.k[kidx(x)];
           // one lane base per chunk; every fragment is a compile-time offset
           // from it (an immediate of the read).  The empty asm makes the base
           // opaque: otherwise the compiler kept one loop-invariant address per
@@ -684,12 +695,12 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
           [&](const int x, auto parity) {
             constexpr int P = decltype(parity)::value;
             if (x < 0) return;
-            const bf16_t(*rt)[kLQ] = GATED ? sm.kh[GATED ? P : 0] : sm.k[kidx(x)];
+            const bf16_t(*rt)[kLQ] = GATED ? sm.kh[GATED ? (kShift ? x % 3 : P) : 0] : sm.k[kidx(x)];
 #pragma unroll
             for (int i = I0; i <= I1; ++i) {
               bf16x8 fq[4], fb[4][4];
 #pragma unroll
-              for (int kb = 0; kb < 4; ++kb) fq[kb] = ld_frag(&sm.q[P][16 * i + lc][32 * kb + 8 * lg]);
+              for (int kb = 0; kb < 4; ++kb) fq[kb] = ld_frag(&sm.q[kShift ? 0 : P][16 * i + lc][32 * kb + 8 * lg]);
 #pragma unroll
               for (int j = 0; j <= i; ++j)
 #pragma unroll
@@ -724,7 +735,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
           [&](const int x, auto parity) {
             constexpr int nb = 1 - decltype(parity)::value;  // buffer of chunk x+1
             if (x + 1 >= nch) return;
-            const bf16_t(*rt)[kLQ] = GATED ? sm.kh[GATED ? nb : 0] : sm.k[kidx(x + 1)];
+            const bf16_t(*rt)[kLQ] = GATED ? sm.kh[GATED ? (kShift ? (x + 1) % 3 : nb) : 0] : sm.k[kidx(x + 1)];
 #pragma unroll
             for (int i = I0; i <= I1; ++i) {
               bf16x8 fl[4], fb[4][4];
@@ -821,7 +832,8 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
     if (!GATED && wave == 4) run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, GATED ? 0 : 1>{});
     else if (!GATED && wave == 5) run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, GATED ? 0 : 2>{});
     else if (LP::kThree && wave == 1) run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, LP::kThree ? 1 : 0>{});
-    else if (LP::is_tile_wave(wave)) run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+    else if (LP::is_tile_wave(wave))  // gated K and K^: two chunks ahead in phase 2 (16 columns), else phase 1
+      run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, kShift ? 2 : 0>{});
     else run(ph1, ph2, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
     if (a.o != nullptr && wave == 4) store_o(nch - 1, std::true_type{});
   }
