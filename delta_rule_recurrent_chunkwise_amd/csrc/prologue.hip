@@ -82,7 +82,9 @@ __global__ __launch_bounds__(256) void qk_prologue(const typename E::T* q_in,
 #pragma unroll
     for (int e = 0; e < KV; ++e) {
       const float xv = E::tof(x[j].e[e]);
-      y[e] = SILU ? xv / (1.f + __expf(-xv)) : xv;
+      // x / (1 + e^-x) with the hardware reciprocal (about 1 ulp) in place
+      // of an IEEE division, about ten instructions per element
+      y[e] = SILU ? xv * __builtin_amdgcn_rcpf(1.f + __expf(-xv)) : xv;
       ss += y[e] * y[e];
     }
 #pragma unroll
