@@ -336,7 +336,9 @@ __global__ __launch_bounds__(256) void la_chunk_out(const bf16_t* __restrict__ q
   // holds token r = 16 mt + lc, value columns 16 jt + 4 lg .. +3, so one
   // scale per lane and one 8-byte store
   const int r = 16 * mt + lc;
-  const float rs_r = GLA ? __expf(sg[GLA ? r : 0]) : sden[GLA ? 0 : r];  // decay of Q S_c, or the denominator
+  // decay of Q S_c, or the reciprocal of the denominator (one division per
+  // lane instead of one per output element)
+  const float rs_r = GLA ? __expf(sg[GLA ? r : 0]) : 1.f / sden[GLA ? 0 : r];
 #pragma unroll
   for (int jt = 0; jt < DV / 16; ++jt) {
     // phi(Q) S_c (a separate accumulator: the 16-deep and 32-deep opcodes
@@ -362,7 +364,7 @@ __global__ __launch_bounds__(256) void la_chunk_out(const bf16_t* __restrict__ q
     }
     float v4[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v4[i] = GLA ? acc[i] + aqs[i] * rs_r : (acc[i] + aqs[i]) / rs_r;
+    for (int i = 0; i < 4; ++i) v4[i] = GLA ? acc[i] + aqs[i] * rs_r : (acc[i] + aqs[i]) * rs_r;
     if (r < nrow)
       *reinterpret_cast<uint2*>(oc + (size_t)r * DV + 16 * jt + 4 * lg) =
           make_uint2(pack2(v4[0], v4[1]), pack2(v4[2], v4[3]));

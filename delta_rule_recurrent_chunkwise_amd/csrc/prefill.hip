@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   T* sVt = reinterpret_cast<T*>(smem + L::oVt);
   T* sA = reinterpret_cast<T*>(smem + L::oA);
   float* sTL = reinterpret_cast<float*>(smem + L::oTL);
-  float* sRow = reinterpret_cast<float*>(smem + L::oRow);  // beta (delta) / den (LA)
+  float* sRow = reinterpret_cast<float*>(smem + L::oRow);  // beta (delta rule), or 1 / den (LA)
   float* sVec = reinterpret_cast<float*>(smem + L::oVec);  // Gam_C (gated) / z (LA)
   float* sPart = reinterpret_cast<float*>(smem + L::oPart);
   float* sG = reinterpret_cast<float*>(smem + L::oG);  // per-token modes: G_t
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         }
         // every lane has read z (sVec) before it is updated: one wave, LDS
         // operations in program order
-        sRow[lane] = den0 + den1;
+        sRow[lane] = 1.f / (den0 + den1);  // reciprocal: one division per row
 #pragma unroll
         for (int h = 0; h * 64 < DK; ++h)
           if (lane + 64 * h < DK) sVec[lane + 64 * h] += zs[h];
@@ -581,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * mt + 4 * lg + i;
           float val = ox[mt][i];
-          if (MODE == PF_LA) val = val / sRow[r];
+          if (MODE == PF_LA) val = val * sRow[r];
           if (!a.Sc && t0 + r <= tlast) oh[(size_t)(t0 + r) * dv + 16 * cw + lc] = E::cvt(val);
         }
       }
