@@ -209,7 +209,7 @@ def _prefill_counter_lines(prof_dir, kname, avg_ns):
     cycles = m["GRBM_GUI_ACTIVE"] / 8.0
     flops = m["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0
     alg_flops = prefill_algorithmic(4, 16, 4096, 128, 128)[1]
-    cmd = ("cd /tmp && rocprofv3 --pmc {cs} -f csv -d $R/gpurun_out/prof/pmc_{t}_prefill -o pmc "
+    cmd = ("cd /tmp && rocprofv3 --pmc {cs} -f csv -d $OUT/pmc_{t}_prefill -o pmc "
            "-- python3 $R/bench.py --only prefill --steps 5 --warmup 1 --decode-steps 20")
     out = ["", "## MFMA and LDS counters, one run per set"]
     out += [f"#   {cmd.format(cs=' '.join(cs), t=t)}" for t, cs in PREFILL_SQ_SETS.items()]
@@ -244,7 +244,7 @@ def _row_counter_lines(prof_dir, mode, kernels, alg, cal):
     """HBM bytes of each kernel of one call (FETCH_SIZE and WRITE_SIZE per
     dispatch, scaled by the copy calibration) and their sum against the
     call's algorithmic bytes."""
-    cmd = ("cd /tmp && rocprofv3 --pmc {c} -f csv -d $R/gpurun_out/prof/pmc_{c}_{m} -o pmc "
+    cmd = ("cd /tmp && rocprofv3 --pmc {c} -f csv -d $OUT/pmc_{c}_{m} -o pmc "
            "-- python3 $R/bench.py --only {m}")
     out = ["## HBM counters, one run per counter",
            f"#   {cmd.format(c='FETCH_SIZE', m=mode)}",
@@ -271,7 +271,7 @@ def _row_counter_lines(prof_dir, mode, kernels, alg, cal):
 # plain pipelined kernel at the grid of the timed prefill, which they would
 # otherwise share a summary with).
 SEGMENTED_TRACE_CMD = ("cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d "
-                       "$R/gpurun_out/prof/trace_segmented -o trace -- python3 $R/bench.py "
+                       "$OUT/trace_segmented -o trace -- python3 $R/bench.py "
                        "--only segmented-row")
 SEGMENTED_PROFILES = [
     ("segmented_B1_H4_T32768_d128.txt",
@@ -294,7 +294,7 @@ def _trace_summaries(dispatches, profiles, trace_cmd):
     per-dispatch records, one summary file per entry of `profiles`."""
     for fname, wl, kernels in profiles:
         lines = [f"# rocprofv3 kernel-trace summary: {wl}",
-                 "# $R is the repository root; the command runs committed files only.",
+                 "# $R is the repository root, $OUT the directory the raw rocprofv3 output goes to; the command runs committed files only.",
                  f"# command: {trace_cmd}", ""]
         for spec in kernels:
             kname, grid = spec if isinstance(spec, tuple) else (spec, None)
@@ -330,9 +330,9 @@ def summarize(prof_dir):
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         kib, _ = _counter_mean(os.path.join(prof_dir, f"pmc_{c}_copy"), c, COPY_KERNEL)
         cal[c] = (kib, copy_bytes / (kib * 1024.0))
-    trace_cmd = ("cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/prof/trace "
+    trace_cmd = ("cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d $OUT/trace "
                  "-o trace -- python3 $R/bench.py --no-cpu-baseline")
-    pmc_cmd = ("cd /tmp && rocprofv3 --pmc {c} -f csv -d $R/gpurun_out/prof/pmc_{c}_{m} -o pmc "
+    pmc_cmd = ("cd /tmp && rocprofv3 --pmc {c} -f csv -d $OUT/pmc_{c}_{m} -o pmc "
                "-- python3 $R/bench.py --only {m} --steps 5 --warmup 1 --decode-steps 20")
     jobs = [("prefill", PREFILL_KERNEL, PREFILL_PROFILE, PREFILL_SOURCES,
              "deltanet_prefill B=4 H=16 T=4096 dk=dv=128, bf16 q/k/v/beta/o, fp32 state",
@@ -353,7 +353,7 @@ def summarize(prof_dir):
         lines = [
             f"# rocprofv3 summary: {row['Name']}",
             f"# workload: {wl}",
-            "# $R is the repository root; every command runs committed files only.",
+            "# $R is the repository root, $OUT the directory the raw rocprofv3 output goes to; every command runs committed files only.",
             f"kernel_sources: {' '.join(srcs)}",
             f"kernel_sources_sha256: {sources_digest(srcs)}",
             "",
@@ -975,9 +975,9 @@ def copy_probe(torch, nbytes=1 << 30, reps=5):
 
 def host_cores():
     """The host cores this process may use: its CPU affinity, capped by
-    OMP_NUM_THREADS where the environment sets it (a GPU machine gives each GPU's
-    job a share of its cores and says so there, whatever the affinity mask
-    shows)."""
+    OMP_NUM_THREADS where the environment sets it (a shared multi-GPU host
+    gives each GPU's job a share of its cores and says so there, whatever
+    the affinity mask shows)."""
     n = len(os.sched_getaffinity(0))
     share = os.environ.get("OMP_NUM_THREADS")
     if share and share.isdigit() and int(share) > 0:
