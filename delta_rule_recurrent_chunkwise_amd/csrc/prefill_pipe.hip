@@ -212,13 +212,16 @@ struct LoadPlan {
 // CAP: also write the state entering every chunk to a.Sc (backward pass,
 // which passes a.o = NULL: then neither the output nor the final state is
 // written; a run-time test, which kept the register allocation free of
-// spills where the compile-time one did not).
+// spills where the compile-time one did not).  The output itself is not
+// formed under CAP (compile time): no Q tiles, no Q S, no tril(Q K^T), no
+// O += tril(Q K^T) u; the state needs K, V and beta only.
 template <int GM, int DVS, bool CAP = false>
 __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
   constexpr bool GATED = GM == 1;  // per key channel, operands from the pre-pass
   constexpr bool TOKG = GM == 2;   // one decay per token
   typedef Smem2<GM, DVS> Sm;
   constexpr bool kShift = Sm::kShift;  // gated, 16 columns: one Q buffer, K^ chunk c in buffer c % 3
+  constexpr bool kOut = !CAP;          // the output is formed (not when only the chunk states are wanted)
   constexpr int kDVS = DVS;
   constexpr int NCW = DVS / 16;        // chain waves
   constexpr int VPRV = DVS / 8;        // 16-byte vectors per row of the v slice
@@ -445,8 +448,10 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
             st[t][i] += kk[t][i] * u;
             o += qq[t][i] * st[t][i];
           }
-        o = xsum32(xsum16(o));
-        if (lg == 0) sm.o[P][tau][col] = f2bf(o);
+        if constexpr (kOut) {
+          o = xsum32(xsum16(o));
+          if (lg == 0) sm.o[P][tau][col] = f2bf(o);
+        }
       }
     };
     run(
@@ -486,7 +491,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) {
             fk[0][mt] = ld_frag(&kx[16 * mt + lc][8 * lg]);
-            fq[0][mt] = ld_frag(&sm.q[kShift ? 0 : P][16 * mt + lc][8 * lg]);
+            if constexpr (kOut) fq[0][mt] = ld_frag(&sm.q[kShift ? 0 : P][16 * mt + lc][8 * lg]);
           }
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
@@ -494,14 +499,16 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
 #pragma unroll
               for (int mt = 0; mt < 4; ++mt) {
                 fk[(kb + 1) & 1][mt] = ld_frag(&kx[16 * mt + lc][32 * (kb + 1) + 8 * lg]);
-                fq[(kb + 1) & 1][mt] = ld_frag(&sm.q[kShift ? 0 : P][16 * mt + lc][32 * (kb + 1) + 8 * lg]);
+                if constexpr (kOut)
+                  fq[(kb + 1) & 1][mt] = ld_frag(&sm.q[kShift ? 0 : P][16 * mt + lc][32 * (kb + 1) + 8 * lg]);
               }
             }
             const bf16x8 b = acc_pair_to_b(st[2 * kb], st[2 * kb + 1]);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
               y[mt] = mfma_k32(fk[kb & 1][mt], b, y[mt]);
-              ox[mt] = kOT ? mfma_k32(b, fq[kb & 1][mt], ox[mt]) : mfma_k32(fq[kb & 1][mt], b, ox[mt]);
+              if constexpr (kOut)
+                ox[mt] = kOT ? mfma_k32(b, fq[kb & 1][mt], ox[mt]) : mfma_k32(fq[kb & 1][mt], b, ox[mt]);
             }
           }
 #pragma unroll
@@ -513,7 +520,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
             if constexpr (TOKG) {  // rows of K S and Q S decay by exp(G_r)
               const float4 dc = *reinterpret_cast<const float4*>(&sm.gs[TOKG ? P : 0][1][16 * mt + 4 * lg]);
               y[mt][0] *= dc.x; y[mt][1] *= dc.y; y[mt][2] *= dc.z; y[mt][3] *= dc.w;
-              ox[mt] *= sm.gs[TOKG ? P : 0][1][16 * mt + lc];  // the lane's token
+              if constexpr (kOut) ox[mt] *= sm.gs[TOKG ? P : 0][1][16 * mt + lc];  // the lane's token
             }
             xx[mt][0] = bt.x * (bf2f((bf16_t)vw[0]) - y[mt][0]);
             xx[mt][1] = bt.y * (bf2f((bf16_t)vw[1]) - y[mt][1]);
@@ -536,12 +543,14 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
 #pragma unroll
           for (int i = 0; i < 6; ++i) fl[i] = fr16(&sm.lb[P][i][0][0]);
           bf16x8 fa[6];
-          fa[0] = ld_frag(&sm.a[lc][8 * lg]);
-          fa[1] = ld_frag(&sm.a[16 + lc][8 * lg]);
-          fa[2] = ld_frag(&sm.a[32 + lc][8 * lg]);
-          fa[3] = ld_frag(&sm.a[32 + lc][32 + 8 * lg]);
-          fa[4] = ld_frag(&sm.a[48 + lc][8 * lg]);
-          fa[5] = ld_frag(&sm.a[48 + lc][32 + 8 * lg]);
+          if constexpr (kOut) {
+            fa[0] = ld_frag(&sm.a[lc][8 * lg]);
+            fa[1] = ld_frag(&sm.a[16 + lc][8 * lg]);
+            fa[2] = ld_frag(&sm.a[32 + lc][8 * lg]);
+            fa[3] = ld_frag(&sm.a[32 + lc][32 + 8 * lg]);
+            fa[4] = ld_frag(&sm.a[48 + lc][8 * lg]);
+            fa[5] = ld_frag(&sm.a[48 + lc][32 + 8 * lg]);
+          }
           if constexpr (TOKG) {  // S <- exp(G_C) S before K^T u is added
             const float eC = sm.gs[TOKG ? P : 0][1][kC - 1];
 #pragma unroll
@@ -581,7 +590,8 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
           const bf16x8 u01 = acc_pair_to_b(ut[0], ut[1]);
           const bf16x8 u23 = acc_pair_to_b(ut[2], ut[3]);
           // O += tril(Q K^T) u
-          if constexpr (kOT) {
+          if constexpr (!kOut) {
+          } else if constexpr (kOT) {
             ox[0] = mfma_k32(u01, fa[0], ox[0]);
             ox[1] = mfma_k32(u01, fa[1], ox[1]);
             ox[2] = mfma_k32(u23, fa[3], mfma_k32(u01, fa[2], ox[2]));
@@ -623,7 +633,8 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
               st[t][3] *= gv.w;
             }
           }
-          if constexpr (kOT) {
+          if constexpr (!kOut) {
+          } else if constexpr (kOT) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
               *reinterpret_cast<uint2*>(&sm.o[P][16 * mt + lc][16 * wave + 4 * lg]) =
@@ -694,7 +705,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
       run(
           [&](const int x, auto parity) {
             constexpr int P = decltype(parity)::value;
-            if (x < 0) return;
+            if (x < 0 || !kOut) return;  // tril(Q K^T) serves the output only
             const bf16_t(*rt)[kLQ] = GATED ? sm.kh[GATED ? (kShift ? x % 3 : P) : 0] : sm.k[kidx(x)];
 #pragma unroll
             for (int i = I0; i <= I1; ++i) {
@@ -823,19 +834,20 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe(PipeArgs a) {
     };
     auto ph1 = [&](const int x, auto parity) {};
     auto ph2 = [&](const int x, auto parity) {
-      if (a.o != nullptr && wave == 4 && x >= 1) store_o(x - 1, std::false_type{});
+      if (kOut && a.o != nullptr && wave == 4 && x >= 1) store_o(x - 1, std::false_type{});
     };
     // plain: Q of chunk x+1 and K of chunk x+2 are stored in phase 2 of x
     // (K(x+1) is read then, for L(x+1)); gated: K and K^ in phase 1, and
     // Q of chunk x+1 in phase 2 where a wave of its own loads it (16-column
     // slices)
-    if (!GATED && wave == 4) run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, GATED ? 0 : 1>{});
+    if (!GATED && wave == 4) run(ph1, ph2, std::integral_constant<int, kOut ? 1 : 0>{}, std::integral_constant<int, GATED ? 0 : 1>{});
     else if (!GATED && wave == 5) run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, GATED ? 0 : 2>{});
-    else if (LP::kThree && wave == 1) run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, LP::kThree ? 1 : 0>{});
+    else if (LP::kThree && wave == 1)  // Q only: none without the output
+      run(ph1, ph2, std::integral_constant<int, kOut ? 1 : 0>{}, std::integral_constant<int, LP::kThree ? 1 : 0>{});
     else if (LP::is_tile_wave(wave))  // gated K and K^: two chunks ahead in phase 2 (16 columns), else phase 1
       run(ph1, ph2, std::integral_constant<int, 1>{}, std::integral_constant<int, kShift ? 2 : 0>{});
     else run(ph1, ph2, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-    if (a.o != nullptr && wave == 4) store_o(nch - 1, std::true_type{});
+    if (kOut && a.o != nullptr && wave == 4) store_o(nch - 1, std::true_type{});
   }
 }
 
