@@ -237,6 +237,10 @@ ROW_COUNTERS = [
     ("la_par_B8_H12_T1024_d64.txt", "la-rows",
      ["la_chunk_state<64, 64, false>", "la_state_scan<false>", "la_chunk_out<64, 64, false>"],
      lambda: la_algorithmic(8, 12, 1024, 64, 64, 2)),
+    ("delta_backward_B4_H16_T4096_d128.txt", "backward-row",
+     ["prefill_pipe<0, 32, true>", "bwd_transition<128, false, false>", "bwd_chain_mat<128, 32, false, false>",
+      "bwd_grads<128, 128, linattn::BF16, false, false>"],
+     lambda: backward_algorithmic(4, 16, 4096, 128, 128)),
 ]
 
 
@@ -493,6 +497,13 @@ def la_algorithmic(B, H, T, dk, dv, elem_bytes):
     return B * H * (T * 2 * (dk + dv) * elem_bytes + (dk * dv + dk) * 4)
 
 
+def backward_algorithmic(B, H, T, dk, dv):
+    """Bytes the delta rule's backward must move (bf16): q, k, v, dO and beta
+    in; dq, dk, dv and dbeta out."""
+    th = B * H * T
+    return th * 2 * (2 * dk + 2 * dv + 1) + th * 2 * (2 * dk + dv + 1)
+
+
 def gated_algorithmic(B, H, T, dk, dv):
     """Bytes the per-channel gated delta-rule prefill must move (bf16): q, k,
     g (one log-decay per key channel), v and beta in, o out, and the final
@@ -643,7 +654,7 @@ def bench_backward_row(la, workloads, torch, launches=5):
 
     us, med = _time_launches(torch, stream, run, [d], launches, warmup=1)
     th = w.B * w.H * w.T
-    per = th * 2 * (2 * w.dk + 2 * w.dv + 1) + th * 2 * (2 * w.dk + w.dv + 1)
+    per = backward_algorithmic(w.B, w.H, w.T, w.dk, w.dv)
     name, r = _row("deltanet_prefill_backward", f"deltanet_prefill_backward B={w.B} H={w.H} "
                    f"T={w.T} dk=dv={w.dk} bf16", us, med, per,
                    "four kernels: forward chunk states (pipelined kernel, states captured), "
