@@ -1172,13 +1172,13 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
   const float* dSn = dSc + (size_t)chunk * DK * DV;
   const bf16_t* dSt = reinterpret_cast<const bf16_t*>(dSc) + (size_t)chunk * DK * DV;
 
-  // Ungated, bf16, dv = 128 (eight 16-column slices, one per wave): this
-  // wave's slice of S and dSn, loaded with phase A's loads (after them, so
-  // that storing the staged tiles does not wait for these), read by phase B
-  // and staged into LDS for phase E without a second load.  (The gated
-  // kernels have no registers to spare for it; with a per-channel decay it
-  // measured no gain.)
-  constexpr bool kHold = kBf16 && !GATE && !KDA && NVT == NW;
+  // bf16, dv = 128 (eight 16-column slices, one per wave), no per-channel
+  // decay: this wave's slice of S and dSn, loaded with phase A's loads
+  // (after them, so that storing the staged tiles does not wait for these),
+  // read by phase B and staged into LDS for phase E without a second load.
+  // (With a per-channel decay the kernel has no registers to spare for it
+  // and measured no gain.)
+  constexpr bool kHold = kBf16 && !KDA && NVT == NW;
   uint2 hS[kHold ? NKT : 1], hD[kHold ? NKT : 1];
   // and (the same kernels) the V and dO entries phase B reads, rows 16mt +
   // 4lg + i of column 16 wave + lc: loaded at the start, they arrive while
