@@ -1031,10 +1031,12 @@ __global__ __launch_bounds__(DK * 4) void bwd_chain_mat(BackwardArgs a, const bf
 // ---------------------------------------------------------------------------
 // Pass 3: one workgroup per (batch, head, chunk).  Phases (barriers between),
 // with LDS regions reused as operands die:
-//   A  stage Q, K; tril(Q K^T) and K K^T -> L, T (A and T are read by
+//   A  stage Q, K; tril(Q K^T) and K K^T -> L; bf16: the blocks of L and
+//      D_b = (I + L_bb)^-1, also transposed; fp32: T (A and T are read by
 //      columns where their transposes are needed)
 //   B  per 16-column slice of dv (one wave each): X, u, du, dX from S and
-//      dSn held as accumulator tiles; write dV; rowsum((V - K S) * dX) into
+//      dSn held as accumulator tiles (bf16: u and dX by block forward and
+//      back substitution with those blocks, fp32: products with T); write dV; rowsum((V - K S) * dX) into
 //      dbeta; u and dX rows to LDS
 //   C  stage dO; dA = tril(dO u^T), dL = -tril(dX u^T, -1) (+ its rowsum
 //      against K K^T into dbeta), both also transposed
@@ -1067,10 +1069,10 @@ struct GradLayout {
   static constexpr int oW = oCC + (KDA ? DK * 4 : 0);  // phase-dependent work area
   // phases A, B
   static constexpr int aQ = oW, aK = aQ + ROWQ, aAt = aK + ROWQ, aTL = aAt + TRI;
-  // bf16 inputs: T and T^T (bf16, formed by block substitution), A^T, the
-  // blocks of L (off the diagonal bf16, on it fp32) and D_b = (I + L_bb)^-1;
-  // the fp32 T region aTL is not used then
-  static constexpr int aT = aTL + FT, aTt = aT + TRI, aAtt = aTt + TRI;
+  // bf16 inputs: the blocks of L (off the diagonal bf16, on it fp32) and
+  // D_b = (I + L_bb)^-1, the bf16 ones also transposed, and A^T; the fp32 T
+  // region aTL is not used then
+  static constexpr int aLoT = aTL + FT, aDT = aLoT + 6 * 256 * 2, aAtt = aDT + 4 * 256 * 2;
   static constexpr int aLo = aAtt + TRI, aD = aLo + 6 * 256 * 2, aLd = aD + 4 * 256 * 2;
   static constexpr int endAB = ES == 2 ? aLd + 4 * 16 * 20 * 4 : aTL + FT;
   // KDA (bf16): K^ where the fp32 T region would be
@@ -1190,8 +1192,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
   T* sK = reinterpret_cast<T*>(smem + L::aK);
   T* sA = reinterpret_cast<T*>(smem + L::aAt);  // tril(Q K^T), row-major
   float* sTL = reinterpret_cast<float*>(smem + L::aTL);
-  bf16_t* sT = reinterpret_cast<bf16_t*>(smem + L::aT);
-  bf16_t* sTt = reinterpret_cast<bf16_t*>(smem + L::aTt);
+  bf16_t* sLoT = reinterpret_cast<bf16_t*>(smem + L::aLoT);
+  bf16_t* sDT = reinterpret_cast<bf16_t*>(smem + L::aDT);
   bf16_t* sAtt = reinterpret_cast<bf16_t*>(smem + L::aAtt);
   bf16_t* sLo = reinterpret_cast<bf16_t*>(smem + L::aLo);
   bf16_t* sD = reinterpret_cast<bf16_t*>(smem + L::aD);
@@ -1289,6 +1291,13 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
         }
       }
     }
+    if constexpr (kBf16) {
+      if (!isA && ti != tj) {  // L_ti,tj transposed: row lc of it is column cc of the block
+        const float* bt = sB + 16 * ti + 4 * lg;
+        st4_bf16(sLoT + ((ti * (ti - 1) / 2 + tj) * 16 + lc) * 16 + 4 * lg, bt[0] * acc[0], bt[1] * acc[1],
+                 bt[2] * acc[2], bt[3] * acc[3]);
+      }
+    }
   }
   __syncthreads();
   if constexpr (kBf16) {
@@ -1309,50 +1318,15 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) sD[(16 * lg + i) * 16 + lc] = f2bf(x[i]);
-    }
-    __syncthreads();
-    // T = (I + L)^-1 by block forward substitution on the identity's column
-    // tiles: T_ct,ct = D_ct, T_b,ct = -D_b sum_{ct<=j<b} L_bj T_j,ct; wave ct
-    // writes T (row-major) and T^T, zeros above the diagonal included
-    if (wave < 4) {
-      const int ct = wave;
-      auto blk = [&](const bf16_t* b) { return *reinterpret_cast<const shortx4*>(b + lc * 16 + 4 * lg); };
-      // every block first: the stores of T below would otherwise keep each
-      // read in the chain behind them
-      shortx4 fl[6], fd[4];
 #pragma unroll
-      for (int i = 0; i < 6; ++i) fl[i] = blk(sLo + i * 256);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) fd[b] = blk(sD + 256 * b);
-      float dct[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dct[i] = bf2f(sD[(16 * ct + 4 * lg + i) * 16 + lc]);
-      floatx4 tb[4];
-      shortx4 tb16[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        if (b < ct) {
-          tb[b] = zero4();
-        } else if (b == ct) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) tb[b][i] = dct[i];
-        } else {
-          floatx4 acc = zero4();
-#pragma unroll
-          for (int j = 0; j < b; ++j)
-            if (j >= ct) acc = mfma_k16(fl[b * (b - 1) / 2 + j], tb16[j], acc);
-          tb[b] = -mfma_k16(fd[b], acc_to_b16(acc), zero4());
-        }
-        tb16[b] = acc_to_b16(tb[b]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sT[(16 * b + 4 * lg + i) * LKT + 16 * ct + lc] = f2bf(tb[b][i]);
-        st4_bf16(sTt + (16 * ct + lc) * LKT + 16 * b + 4 * lg, tb[b][0], tb[b][1], tb[b][2], tb[b][3]);
-      }
+      for (int i = 0; i < 16; i += 4) st4_bf16(sDT + (16 * lg + lc) * 16 + i, x[i], x[i + 1], x[i + 2], x[i + 3]);
     }
     __syncthreads();
   } else {
     form_T<kBf16, NTH>(sTL, tid, wave, lane);
   }
+  // an A operand from a 16 x 16 bf16 block stored row-major
+  auto blk16 = [&](const bf16_t* b) { return *reinterpret_cast<const shortx4*>(b + lc * 16 + 4 * lg); };
 
   // ---- phase B: 16-column slices of dv, one per wave at a time ----
   for (int s = wave; s < NVT; s += NW) {
@@ -1429,11 +1403,27 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
 #pragma unroll
       for (int i = 0; i < 4; ++i) xx[mt][i] = sB[16 * mt + 4 * lg + i] * res[mt][i];
     }
+    if constexpr (kBf16) {
+      // u = (I + L)^-1 X by block forward substitution, as in the forward:
+      // u_b = D_b (X_b - sum_{j<b} L_bj u_j)
+      shortx4 ub[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        floatx4 acc = xx[b];
+        if (b > 0) {
+          floatx4 t = zero4();
+#pragma unroll
+          for (int j = 0; j < b; ++j) t = mfma_k16(blk16(sLo + (b * (b - 1) / 2 + j) * 256), ub[j], t);
+          acc = xx[b] - t;
+        }
+        ut[b] = mfma_k16(blk16(sD + 256 * b), acc_to_b16(acc), zero4());
+        ub[b] = acc_to_b16(ut[b]);
+      }
+    }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       floatx4 d1;
       if constexpr (kBf16) {
-        ut[mt] = accB<kBf16>(zero4(), sT + (16 * mt + lc) * LKT, xx, (mt | 1) + 1, lane);
         d1 = accB<kBf16>(zero4(), sAtt + (16 * mt + lc) * LKT, dOt, 4, lane);  // A^T dO
       } else {
         ut[mt] = accB<kBf16>(zero4(), sTL + (16 * mt + lc) * LTL, xx, mt + 1, lane);
@@ -1446,10 +1436,26 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grads(BackwardArgs a, const 
       }
       du[mt] = d1 + d2;
     }
+    if constexpr (kBf16) {
+      // dX = (I + L)^-T du by block back substitution:
+      // dX_b = D_b^T (du_b - sum_{j>b} L_jb^T dX_j)
+      shortx4 xb[4];
+#pragma unroll
+      for (int b = 3; b >= 0; --b) {
+        floatx4 acc = du[b];
+        if (b < 3) {
+          floatx4 t = zero4();
+#pragma unroll
+          for (int j = b + 1; j < 4; ++j) t = mfma_k16(blk16(sLoT + (j * (j - 1) / 2 + b) * 256), xb[j], t);
+          acc = du[b] - t;
+        }
+        dx[b] = mfma_k16(blk16(sDT + 256 * b), acc_to_b16(acc), zero4());
+        xb[b] = acc_to_b16(dx[b]);
+      }
+    }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      if constexpr (kBf16) dx[mt] = accB<kBf16>(zero4(), sTt + (16 * mt + lc) * LKT, du, 4, lane);  // T^T du
-      else dx[mt] = accB_col<kBf16>(zero4(), sTL + 16 * mt + lc, LTL, du, 4, lane);
+      if constexpr (!kBf16) dx[mt] = accB_col<kBf16>(zero4(), sTL + 16 * mt + lc, LTL, du, 4, lane);  // T^T du
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * mt + 4 * lg + i;
