@@ -109,8 +109,9 @@ int seg_args_rc(int gate, int dtype, int B, int H, int T, int dk, int dv, int P)
   if (seg_mode(gate) < 0 || P < 1) return LA_ERR_SHAPE;
   if (P > 1) {
     if (T % P != 0) return LA_ERR_SHAPE;
+    // (this also bounds the fix-up's one-dimensional grid, B*H*(P-1) times
+    // ceil(T/P / 256) blocks, below 2^31)
     if ((long long)H * P > INT_MAX || !sizes_ok(B, (long long)H * P, T / P, dk, dv, true)) return LA_ERR_SHAPE;
-    if ((T / P + 255) / 256 > 65535) return LA_ERR_SHAPE;  // the fix-up's grid
   }
   if (dtype != LA_DTYPE_BF16) return LA_ERR_UNSUPPORTED_DIM;
   return LA_OK;

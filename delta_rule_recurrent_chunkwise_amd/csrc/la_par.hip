@@ -170,8 +170,8 @@ template <bool GLA>
 __global__ __launch_bounds__(256) void la_state_scan(const float* __restrict__ dS, float* __restrict__ dz,
                                                      bf16_t* __restrict__ Sb, float* S, float* z, int nch,
                                                      int dkdv, int dk, int use_init) {
-  const long bh = blockIdx.y;
-  const int e = blockIdx.x * 256 + threadIdx.x;
+  const long bh = blockIdx.x;  // heads in the first grid dimension (the second is limited to 65535)
+  const int e = blockIdx.y * 256 + threadIdx.x;
   if (e >= dkdv + dk) return;
   const float* gam = GLA ? dz + (size_t)bh * nch : nullptr;
   const bool isz = e >= dkdv;
@@ -441,7 +441,7 @@ hipError_t launch_states(int dk, const PrefillArgs& a, void* workspace, hipStrea
   const int nz = GLA ? 0 : dk;  // gated linear attention has no normaliser
   const int n = dk * a.dv + nz;
   bf16_t* Sb = reinterpret_cast<bf16_t*>(dz + (size_t)nchunks * dk);
-  hipLaunchKernelGGL((la_state_scan<GLA>), dim3((unsigned)((n + 255) / 256), (unsigned)(a.B * a.H)), dim3(256),
+  hipLaunchKernelGGL((la_state_scan<GLA>), dim3((unsigned)(a.B * a.H), (unsigned)((n + 255) / 256)), dim3(256),
                      0, st, dS, dz, Sb, a.S, a.z, nch, dk * a.dv, nz, a.use_init);
   return hipGetLastError();
 }

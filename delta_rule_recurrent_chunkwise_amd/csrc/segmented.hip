@@ -244,13 +244,18 @@ __global__ __launch_bounds__(64 * kFixWaves) void seg_fixup(const bf16_t* __rest
   __shared__ uint4 smem[NF > NSTAGE ? NF : NSTAGE];
   uint4* sb = smem;
   float(*stage)[16][SP] = reinterpret_cast<float(*)[16][SP]>(smem);
-  const int f = blockIdx.x, bh = f / (P - 1), p = f % (P - 1) + 1;
+  // one flat index (a grid's second dimension is limited to 65535 blocks):
+  // the row blocks of one segment are consecutive, so they share its
+  // fragments in L2
+  const int nrb = (Tp + kFixRows - 1) / kFixRows;
+  const int f = (int)(blockIdx.x / nrb), rb = (int)(blockIdx.x - (unsigned)f * nrb);
+  const int bh = f / (P - 1), p = f % (P - 1) + 1;
   const size_t sh = (size_t)bh * P + p;  // segment-head index
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 15, g = lane >> 4;
 
   // A operands: rows r0 + 16rt + c of oB (a row past the segment re-reads
   // the last one and is not stored); requested before the fragments are staged
-  const int r0 = blockIdx.y * kFixRows + 32 * w;
+  const int r0 = rb * kFixRows + 32 * w;
   bf16x8 fa[2][K32];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
@@ -328,7 +333,7 @@ hipError_t launch_scan(const float* M, uint4* MF, const float* Sz, uint4* F, flo
 template <int DK, int DV>
 hipError_t launch_fixup_t(const bf16_t* oB, const uint4* F, bf16_t* o, int BH, int P, int Tp,
                           hipStream_t st) {
-  const dim3 grid(BH * (P - 1), (Tp + kFixRows - 1) / kFixRows);
+  const dim3 grid((unsigned)((long)BH * (P - 1) * ((Tp + kFixRows - 1) / kFixRows)));
   hipLaunchKernelGGL((seg_fixup<DK, DV>), grid, dim3(64 * kFixWaves), 0, st, oB, F, o, P, Tp);
   return hipGetLastError();
 }

@@ -118,3 +118,83 @@ def test_decode_state_past_2_31_elements():
     assert_close(S.reshape(-1, POOL, D, D)[-1:], S_ref, TOL[BF], "S (last heads, past 2^31 elements)")
     del o, S
     _free()
+
+
+# Grids: a launch's second and third dimensions are limited to 65535 blocks,
+# so every count that grows with the input is in the first.
+
+@pytest.mark.parametrize("gated", [False, True], ids=["la", "gla"])
+def test_linear_attention_past_65535_heads(gated):
+    """The chunk-parallel (bf16) linear-attention kernels over 65,600 heads of
+    130 tokens (a ragged third chunk): the state scan runs one block row per
+    head."""
+    dev = require_gpu()
+    d, T, reps = 16, 130, 8200
+    print(f"{'gla' if gated else 'la'}_prefill: B={reps} H={POOL} T={T} d={d}", flush=True)
+    assert reps * POOL > 65535
+    if gated:
+        inp = workloads.make_gla(1, POOL, T, d, d, BF, seed=75)
+        names = ("q", "k", "v", "g")
+    else:
+        inp = workloads.make_la(1, POOL, T, d, d, BF, seed=75)
+        names = ("q", "k", "v")
+    x = {n: inp[n].to(dev).expand(reps, *inp[n].shape[1:]).contiguous() for n in names}
+    if gated:
+        o, S = la.gla_prefill(x["q"], x["k"], x["v"], x["g"])
+        o_ref, S_ref = oracle.gla_recurrent(inp["q"], inp["k"], inp["v"], inp["g"])
+    else:
+        o, S, z = la.la_prefill(x["q"], x["k"], x["v"])
+        o_ref, S_ref, z_ref = oracle.la_recurrent(inp["q"], inp["k"], inp["v"])
+        assert _same_copies(z, POOL), "z differs between copies of one head"
+        assert_close(z[-1:], z_ref, TOL[BF], "z (last batch)")
+    torch.cuda.synchronize()
+    assert _same_copies(o, POOL), "o differs between copies of one head"
+    assert _same_copies(S, POOL), "S differs between copies of one head"
+    assert_close(o[-1:], o_ref, TOL[BF], "o (last batch)")
+    assert_close(S[-1:], S_ref, TOL[BF], "S (last batch)")
+    del x, o, S
+    _free()
+
+
+def test_segmented_past_65535_fixup_blocks():
+    """Two segments of 2^24 + 64 tokens each (d = 16): the output fix-up has
+    65,537 blocks of 256 rows per segment.  beta = 0 except on the last chunk
+    of each segment, so the state is exactly zero until the first of them,
+    then the state S1 it leaves is carried unchanged to the second: every
+    output of segment 0 before its last chunk is exactly 0, every output of
+    segment 1 before its last chunk is q_t S1 (all 16.8 million compared),
+    and the two active chunks follow the oracle."""
+    dev = require_gpu()
+    d, Tp = 16, 2**24 + 64
+    T = 2 * Tp
+    print(f"deltanet_prefill_segmented: T={T} in 2 segments, d={d}", flush=True)
+    assert (Tp + 255) // 256 > 65535
+    pool = workloads.make_delta(1, 1, 64, d, d, BF, seed=76)
+    act = [workloads.make_delta(1, 1, 64, d, d, BF, seed=77 + i) for i in range(2)]
+    ins = {}
+    for n in ("q", "k", "v"):
+        t = torch.empty(1, 1, T, d, dtype=BF, device=dev)
+        for s in range(2):
+            a0 = s * Tp
+            t[0, 0, a0:a0 + Tp - 64] = pool[n][0, 0].to(dev).unsqueeze(0).expand((Tp - 64) // 64, 64, d).reshape(-1, d)
+            t[0, 0, a0 + Tp - 64:a0 + Tp] = act[s][n][0, 0].to(dev)
+        ins[n] = t
+    beta = torch.zeros(1, 1, T, dtype=BF, device=dev)
+    for s in range(2):
+        beta[0, 0, (s + 1) * Tp - 64:(s + 1) * Tp] = act[s]["beta"][0, 0].to(dev)
+    o, S = la.deltanet_prefill_segmented(ins["q"], ins["k"], ins["v"], beta, segments=2)
+    torch.cuda.synchronize()
+    o0_ref, S1 = oracle.delta_recurrent(act[0]["q"], act[0]["k"], act[0]["v"], act[0]["beta"])
+    o1_ref, S_ref = oracle.delta_recurrent(act[1]["q"], act[1]["k"], act[1]["v"], act[1]["beta"], S0=S1)
+    nz = int(torch.count_nonzero(o[0, 0, :Tp - 64]))
+    assert nz == 0, f"{nz} nonzero outputs where the state is exactly zero"
+    assert_close(o[:, :, Tp - 64:Tp], o0_ref, TOL[BF], "o (segment 0, last chunk)")
+    S1d = torch.as_tensor(S1, dtype=torch.float32).reshape(d, d).to(dev)
+    ref = ins["q"][0, 0, Tp:T - 64].float() @ S1d
+    err = float((o[0, 0, Tp:T - 64].float() - ref).abs().max() / ref.abs().max())
+    print(f"  o (segment 1, {Tp - 64} tokens against q S1): rel err {err:.3e} (tol {TOL[BF]:g})", flush=True)
+    assert err <= TOL[BF]
+    assert_close(o[:, :, T - 64:], o1_ref, TOL[BF], "o (segment 1, last chunk)")
+    assert_close(S, S_ref, TOL[BF], "S")
+    del ins, beta, o, S, ref
+    _free()
