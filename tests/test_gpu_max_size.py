@@ -198,3 +198,30 @@ def test_segmented_past_65535_fixup_blocks():
     assert_close(S, S_ref, TOL[BF], "S")
     del ins, beta, o, S, ref
     _free()
+
+
+@pytest.mark.parametrize("gate", ["channel", "token"])
+def test_gated_prefill_past_2_31_elements_across_heads(gate):
+    """The gated prefills over more than 2^31 elements per token tensor: a
+    decay per key channel (its pre-pass writes three scaled copies of q and k
+    into the workspace) and one per token."""
+    dev = require_gpu()
+    T = 64
+    reps = 2**31 // (POOL * T * D) + 32
+    print(f"gated prefill ({gate}) across heads: B={reps} H={POOL} T={T} d={D}", flush=True)
+    inp = workloads.make_delta(1, POOL, T, D, D, BF, seed=79, gated=True if gate == "channel" else "token")
+    x = {n: inp[n].to(dev).expand(reps, *inp[n].shape[1:]).contiguous() for n in ("q", "k", "v", "beta", "g")}
+    assert x["q"].numel() > 2**31
+    if gate == "channel":
+        o, S = la.deltanet_prefill(x["q"], x["k"], x["v"], x["beta"], g=x["g"])
+    else:
+        o, S = la.gated_deltanet_prefill(x["q"], x["k"], x["v"], x["beta"], x["g"])
+    torch.cuda.synchronize()
+    del x
+    assert _same_copies(o, POOL), "o differs between copies of one head"
+    assert _same_copies(S, POOL), "S differs between copies of one head"
+    o_ref, S_ref = oracle.delta_recurrent(inp["q"], inp["k"], inp["v"], inp["beta"], g=inp["g"])
+    assert_close(o[-1:], o_ref, TOL[BF], "o (last batch, past 2^31 elements)")
+    assert_close(S[-1:], S_ref, TOL[BF], "S (last batch, past 2^31 elements)")
+    del o, S
+    _free()
