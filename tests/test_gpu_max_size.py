@@ -225,3 +225,31 @@ def test_gated_prefill_past_2_31_elements_across_heads(gate):
     assert_close(S[-1:], S_ref, TOL[BF], "S (last batch, past 2^31 elements)")
     del o, S
     _free()
+
+
+def test_backward_past_2_31_elements_across_heads():
+    """deltanet_prefill_backward over more than 2^31 elements per token
+    tensor (its workspace holds the chunk states, P, R^T and dSn of about a
+    million chunks): every copy of a pool head gets the same gradients, and
+    the pool's gradients follow the oracle's reverse recurrence."""
+    dev = require_gpu()
+    T = 64
+    reps = 2**31 // (POOL * T * D) + 32
+    print(f"deltanet_prefill_backward across heads: B={reps} H={POOL} T={T} d={D}", flush=True)
+    inp = workloads.make_delta(1, POOL, T, D, D, BF, seed=80)
+    dO = torch.randn(1, POOL, T, D, generator=workloads.generator(81)).to(BF)
+    x = {n: inp[n].to(dev).expand(reps, *inp[n].shape[1:]).contiguous() for n in ("q", "k", "v", "beta")}
+    dOd = dO.to(dev).expand(reps, POOL, T, D).contiguous()
+    assert dOd.numel() > 2**31
+    grads = la.deltanet_prefill_backward(x["q"], x["k"], x["v"], x["beta"], dOd)
+    torch.cuda.synchronize()
+    del x, dOd
+    ref = oracle.delta_backward(inp["q"], inp["k"], inp["v"], inp["beta"], dO)
+    for name, g, r in zip(("dq", "dk", "dv", "dbeta"), grads, ref):
+        if g.dim() == 3:
+            assert bool(torch.equal(g, g[:1].expand_as(g))), f"{name} differs between copies of one head"
+        else:
+            assert _same_copies(g, POOL), f"{name} differs between copies of one head"
+        assert_close(g[-1:], r, TOL[BF], f"{name} (last batch, past 2^31 elements)")
+    del grads
+    _free()
