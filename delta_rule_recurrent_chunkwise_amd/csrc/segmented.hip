@@ -244,11 +244,12 @@ __global__ __launch_bounds__(64 * kFixWaves) void seg_fixup(const bf16_t* __rest
   __shared__ uint4 smem[NF > NSTAGE ? NF : NSTAGE];
   uint4* sb = smem;
   float(*stage)[16][SP] = reinterpret_cast<float(*)[16][SP]>(smem);
-  // one flat index (a grid's second dimension is limited to 65535 blocks):
-  // the row blocks of one segment are consecutive, so they share its
-  // fragments in L2
+  // one flat index (a grid's second dimension is limited to 65535 blocks),
+  // segment fastest: consecutive blocks take the same rows of every segment
+  // (1.3 us faster per call than a segment's row blocks in a row)
   const int nrb = (Tp + kFixRows - 1) / kFixRows;
-  const int f = (int)(blockIdx.x / nrb), rb = (int)(blockIdx.x - (unsigned)f * nrb);
+  const int nf = (int)(gridDim.x / nrb);
+  const int rb = (int)(blockIdx.x / nf), f = (int)(blockIdx.x - (unsigned)rb * nf);
   const int bh = f / (P - 1), p = f % (P - 1) + 1;
   const size_t sh = (size_t)bh * P + p;  // segment-head index
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 15, g = lane >> 4;
